@@ -1,0 +1,346 @@
+"""Plain CPU oracle for the W4A16 weight-only linear layer.
+
+TEST INFRASTRUCTURE. Only ``tests/``, ``__graft_entry__.smoke()`` and the
+``cpu_baseline`` leg of ``bench.py`` may import or call this module. The product
+path (the HIP library and its Python binding) never touches it, and it shares
+no code with that path: its own converters, its own quantiser, its own
+implementation of the packed device layout.
+
+What it computes, and where the method is stated:
+
+* The format. Weights are kept as small integers with a scale, and usually a
+  zero-point, per group; the kernel unpacks them and rebuilds approximate
+  FP16/BF16 values just before the multiply, while activations stay 16-bit and
+  accumulation stays in higher precision ("Weight-Only Quantisation", klaylearn
+  glossary: the definition paragraphs and the first FAQ answer; "Weight-Only
+  Quantization Explained", multigrid.ai: "What W4A16 actually names").
+* The quantiser. Round-to-nearest of w/scale ("Quantization Is Not a Zip File",
+  zhuai.tech, section 3 "The core idea: local structure, not global rounding"),
+  applied per group of 32/64/128 consecutive weights ("Block locality" in that
+  same section), with an asymmetric zero-point and the reconstruction
+  (q - zero) * scale ("Comparison of Quantization Methods: INT8 vs GPTQ vs AWQ
+  vs GGUF", instagit, "Practical Code Examples", the zero-point example).
+* The metadata width. 4 + 20/group bits per weight: a 16-bit scale and a 4-bit
+  zero per group, which gives the 4.156 bits/weight printed for group 128
+  ("Weight-Only Quantization Explained", "The memory arithmetic").
+
+Readings where the pages are silent (each also listed in the design notes):
+  * range includes zero: lo = min(0, min w), hi = max(0, max w);
+  * scale s = fp16_rne((hi - lo) / 15) computed in fp32; a zero scale becomes
+    the smallest positive fp16 (2**-24);
+  * zero z = clamp(rint(-lo / s), 0, 15); code q = clamp(rint(w / s) + z, 0, 15);
+    rint rounds half to even; every quantiser operation is IEEE fp32 (the
+    precision the kernel takes the same integer decision in);
+  * dequantised weight w_hat = s * (q - z) is exact in fp64 here;
+  * y = x @ w_hat^T accumulated in fp64.
+
+Weights must be finite with |w| < 2**18 so that the fp16 scale is finite.
+"""
+from __future__ import annotations
+
+import numpy as np
+
+# ---------------------------------------------------------------------------
+# 16-bit float conversions, bit level (round to nearest, ties to even).
+# The pages name fp16/bf16 as the activation and reconstruction types
+# ("Weight-Only Quantisation", definition); the instagit page's
+# "Implementation Architecture" lists bit-level float converters as the first
+# building block. Written out here from the IEEE 754 binary16 / bfloat16
+# definitions, not taken from any library.
+# ---------------------------------------------------------------------------
+
+
+def _rne_shift_right(v: np.ndarray, s: np.ndarray) -> np.ndarray:
+    """Round the non-negative integers v / 2**s to nearest, ties to even (s >= 1)."""
+    v = v.astype(np.uint64)
+    s = s.astype(np.uint64)
+    q = v >> s
+    rem = v - (q << s)
+    half = np.left_shift(np.uint64(1), s - np.uint64(1))
+    up = (rem > half) | ((rem == half) & ((q & np.uint64(1)) == 1))
+    return q + up.astype(np.uint64)
+
+
+def f32_to_f16_bits(a) -> np.ndarray:
+    """IEEE binary32 -> binary16 bits, RNE, subnormals kept, overflow -> inf."""
+    a = np.ascontiguousarray(a, dtype=np.float32)
+    u = a.view(np.uint32).astype(np.uint64)
+    sign = (u >> np.uint64(31)) << np.uint64(15)
+    exp = ((u >> np.uint64(23)) & np.uint64(0xFF)).astype(np.int64)
+    man = u & np.uint64(0x7FFFFF)
+    out = np.zeros(a.shape, dtype=np.uint64)
+
+    is_nan = (exp == 255) & (man != 0)
+    is_inf = (exp == 255) & (man == 0)
+    finite = exp < 255
+    e = exp - 127                      # unbiased exponent of a normal fp32 value
+    sig = man | np.uint64(1 << 23)     # 24-bit significand, value = sig * 2**(e-23)
+
+    # Result is a normal fp16 (or rounds up to inf): exponent field e + 15 in [1, 30].
+    normal = finite & (exp > 0) & (e >= -14)
+    # value in units of 2**(e-10): keep 11 significant bits
+    r = _rne_shift_right(sig, np.full(sig.shape, 13))          # 11 or 12 bits after rounding
+    carry = r >> np.uint64(11)                                  # 1 if rounding overflowed to 2**11
+    r_n = np.where(carry == 1, r >> np.uint64(1), r)
+    e_n = e + carry.astype(np.int64)
+    h_norm = (((e_n + 15).astype(np.uint64)) << np.uint64(10)) | (r_n & np.uint64(0x3FF))
+    h_norm = np.where(e_n > 15, np.uint64(0x7C00), h_norm)     # overflow -> inf
+
+    # Result is subnormal (or zero): value in units of 2**-24 is sig * 2**(e-23+24).
+    sub = finite & (exp > 0) & (e < -14)
+    shift = np.clip(-(e + 1), 1, 40)                            # e+1 <= -14  ->  shift >= 14
+    h_sub = np.where(shift >= 26, np.uint64(0), _rne_shift_right(sig, shift))
+    # (a result of 1024 units is the smallest normal, 0x0400, which is the same bits)
+
+    out = np.where(normal, h_norm, out)
+    out = np.where(sub, h_sub, out)
+    # fp32 zeros and fp32 subnormals (exp == 0) are below 2**-126: they round to zero.
+    out = np.where(is_inf, np.uint64(0x7C00), out)
+    out = np.where(is_nan, np.uint64(0x7E00), out)
+    return (out | sign).astype(np.uint16)
+
+
+def f16_bits_to_f64(h) -> np.ndarray:
+    """binary16 bits -> exact float64 value."""
+    h = np.asarray(h, dtype=np.uint16).astype(np.int64)
+    sign = np.where((h >> 15) & 1, -1.0, 1.0)
+    exp = (h >> 10) & 0x1F
+    man = h & 0x3FF
+    mag = np.where(exp == 0, np.ldexp(man.astype(np.float64), -24),
+                   np.ldexp((man + 1024).astype(np.float64), (exp - 25).astype(np.int64)))
+    mag = np.where(exp == 31, np.where(man == 0, np.inf, np.nan), mag)
+    return sign * mag
+
+
+def f16_bits_to_f32(h) -> np.ndarray:
+    """binary16 bits -> float32 (exact: every binary16 value is a binary32 value)."""
+    return f16_bits_to_f64(h).astype(np.float32)
+
+
+def f32_to_bf16_bits(a) -> np.ndarray:
+    """IEEE binary32 -> bfloat16 bits, RNE (the upper 16 bits, rounded)."""
+    a = np.ascontiguousarray(a, dtype=np.float32)
+    u = a.view(np.uint32).astype(np.uint64)
+    is_nan = ((u >> np.uint64(23)) & np.uint64(0xFF) == 0xFF) & ((u & np.uint64(0x7FFFFF)) != 0)
+    upper = u >> np.uint64(16)
+    rem = u & np.uint64(0xFFFF)
+    up = (rem > 0x8000) | ((rem == 0x8000) & ((upper & np.uint64(1)) == 1))
+    r = upper + up.astype(np.uint64)          # carries into the exponent, max finite -> inf
+    r = np.where(is_nan, upper | np.uint64(0x40), r)
+    return r.astype(np.uint16)
+
+
+def bf16_bits_to_f64(b) -> np.ndarray:
+    """bfloat16 bits -> exact float64 value (bf16 is the top half of a binary32)."""
+    b = np.asarray(b, dtype=np.uint16).astype(np.uint32) << np.uint32(16)
+    with np.errstate(invalid="ignore"):
+        return b.view(np.float32).astype(np.float64)
+
+
+def act_bits_to_f64(bits, dtype: str) -> np.ndarray:
+    if dtype == "f16":
+        return f16_bits_to_f64(bits)
+    if dtype == "bf16":
+        return bf16_bits_to_f64(bits)
+    raise ValueError(dtype)
+
+
+def out_round_bits(y64, dtype: str) -> np.ndarray:
+    """Round fp64 results to the output type as the kernel does: to fp32 first, then RNE."""
+    y32 = np.asarray(y64, dtype=np.float64).astype(np.float32)
+    return f32_to_f16_bits(y32) if dtype == "f16" else f32_to_bf16_bits(y32)
+
+
+# ---------------------------------------------------------------------------
+# Byte accounting ("Weight-Only Quantization Explained", "The memory
+# arithmetic": 4.156 bits per weight at group 128, 26.0 GB vs 6.75 GB for 13e9
+# weights; "Quantization Is Not a Zip File", section 2: 2N / 1N / 0.5N bytes).
+# ---------------------------------------------------------------------------
+
+
+def bits_per_weight(group: int, scale_bits: int = 16, zero_bits: int = 4, code_bits: int = 4) -> float:
+    """Storage per weight: the code plus the group's scale and zero spread over the group."""
+    return code_bits + (scale_bits + zero_bits) / group
+
+
+def packed_bytes(N: int, K: int, group: int):
+    """(qweight, scales, zeros) byte counts: one nibble per weight, one fp16 scale and
+    one 4-bit zero per (group, output column)."""
+    G = K // group
+    return (N * K) // 2, 2 * G * N, (G * N) // 2
+
+
+def model_bytes(n_weights: float, bits: float) -> float:
+    return n_weights * bits / 8
+
+
+# ---------------------------------------------------------------------------
+# Groupwise asymmetric round-to-nearest quantiser.
+# Rounding step: "Quantization Is Not a Zip File", section 3 (q = round(w/scale),
+# w_hat = scale * q). Groups of 32/64/128 along K with their own scale: same
+# section, "Block locality". Zero-point and (q - zero) * scale reconstruction:
+# instagit comparison page, "Practical Code Examples" (asymmetric example).
+# ---------------------------------------------------------------------------
+
+F16_MIN_SUBNORMAL_BITS = np.uint16(0x0001)   # 2**-24
+
+
+def quantize_groupwise(w, group: int):
+    """Quantise fp32 weights w [N][K] in groups of `group` consecutive k.
+
+    Returns (codes u8 [N][K], scale_bits u16 [G][N], zeros u8 [G][N]).
+    Every step is an IEEE binary32 operation (division, never a reciprocal).
+    """
+    w = np.ascontiguousarray(w, dtype=np.float32)
+    N, K = w.shape
+    if group not in (32, 64, 128) or K % group != 0:
+        raise ValueError("group must be 32/64/128 and divide K")
+    if not np.all(np.isfinite(w)) or np.max(np.abs(w), initial=0.0) >= 2.0 ** 18:
+        raise ValueError("weights must be finite with |w| < 2**18")
+    G = K // group
+    wg = w.reshape(N, G, group)
+    zero = np.float32(0.0)
+    # 1. range of the group, widened to include zero
+    lo = np.minimum(wg.min(axis=2), zero)                       # [N][G] fp32
+    hi = np.maximum(wg.max(axis=2), zero)
+    # 2. scale: fp32 (hi - lo) / 15, rounded once to fp16; zero -> smallest subnormal
+    s32 = (hi - lo) / np.float32(15.0)
+    s_bits = f32_to_f16_bits(s32)
+    s_bits = np.where(s_bits == 0, F16_MIN_SUBNORMAL_BITS, s_bits).astype(np.uint16)
+    s = f16_bits_to_f32(s_bits)                                  # exact widening
+    # 3. zero-point: the code that reconstructs to (about) lo
+    z = np.clip(np.rint(-lo / s), 0, 15).astype(np.int32)
+    # 4. codes: round(w / s) + z, clamped to the 4-bit range
+    r = np.rint(wg / s[:, :, None]).astype(np.int32)
+    q = np.clip(r + z[:, :, None], 0, 15).astype(np.uint8)
+    return (q.reshape(N, K), np.ascontiguousarray(s_bits.T), np.ascontiguousarray(z.T.astype(np.uint8)))
+
+
+def dequantize(codes, scale_bits, zeros, group: int) -> np.ndarray:
+    """w_hat [N][K] = s * (q - z), exact in fp64."""
+    codes = np.asarray(codes, dtype=np.uint8)
+    N, K = codes.shape
+    G = K // group
+    s = f16_bits_to_f64(scale_bits).T                           # [N][G]
+    z = np.asarray(zeros, dtype=np.int64).T                     # [N][G]
+    d = codes.reshape(N, G, group).astype(np.int64) - z[:, :, None]
+    return (d.astype(np.float64) * s[:, :, None]).reshape(N, K)
+
+
+# ---------------------------------------------------------------------------
+# Packing. The pages require the data to stay packed until the kernel
+# ("Quantization Is Not a Zip File", section 8) and say the packing layout is
+# one of the things that decides speed ("Weight-Only Quantisation",
+# definition). The layouts themselves are this library's own; the device
+# layout is written out here independently from its specification:
+#
+#   qweight: rows in blocks of 64 (the last block may hold fewer, rows_b =
+#   min(64, N - 64 b)), K in chunks of 32. Record (n, c) is 16 bytes at byte
+#   offset 64*b*(K/2) + c*rows_b*16 + r*16 (b = n // 64, r = n % 64,
+#   c = k // 32). Dword j = (k % 32) // 8 of the record holds k = 32c + 8j + i,
+#   i = 0..7, in nibble p = i // 2 + 4 * (i % 2) (even k in the low half-word,
+#   odd k in the high half-word). Dwords are little-endian.
+#   scales: fp16 bits [G][N]. zeros: u32 [G][N/8], nibble n % 8 of word n // 8.
+# ---------------------------------------------------------------------------
+
+
+def _device_nibble_index(N: int, K: int) -> np.ndarray:
+    """Nibble position in the packed qweight stream of every (n, k), shape [N][K]."""
+    n = np.arange(N, dtype=np.int64)[:, None]
+    k = np.arange(K, dtype=np.int64)[None, :]
+    b = n // 64
+    r = n % 64
+    rows_b = np.minimum(64, N - 64 * b)
+    c = k // 32
+    j = (k % 32) // 8
+    i = k % 8
+    p = i // 2 + 4 * (i % 2)
+    byte_off = 64 * b * (K // 2) + c * rows_b * 16 + r * 16
+    dword = byte_off // 4 + j
+    return dword * 8 + p
+
+
+def pack_device(codes) -> np.ndarray:
+    """codes u8 [N][K] -> packed qweight bytes (uint8, N*K/2) in the device layout."""
+    codes = np.asarray(codes, dtype=np.uint8)
+    N, K = codes.shape
+    if N % 8 or K % 32:
+        raise ValueError("N % 8 == 0 and K % 32 == 0 required")
+    nib = np.empty(N * K, dtype=np.uint8)
+    nib[_device_nibble_index(N, K).ravel()] = codes.ravel()
+    # nibble t sits in byte t // 2, low nibble when t is even (little-endian dwords)
+    return (nib[0::2] | (nib[1::2] << 4)).astype(np.uint8)
+
+
+def unpack_device(qweight, N: int, K: int) -> np.ndarray:
+    """Inverse of pack_device: packed bytes -> codes u8 [N][K]."""
+    qb = np.asarray(qweight, dtype=np.uint8).ravel()
+    nib = np.empty(2 * qb.size, dtype=np.uint8)
+    nib[0::2] = qb & 0xF
+    nib[1::2] = qb >> 4
+    return nib[_device_nibble_index(N, K)]
+
+
+def pack_zeros(zeros) -> np.ndarray:
+    """zeros u8 [G][N] -> u32 [G][N/8], nibble n % 8 of word n // 8."""
+    z = np.asarray(zeros, dtype=np.uint32)
+    G, N = z.shape
+    zz = z.reshape(G, N // 8, 8)
+    word = np.zeros((G, N // 8), dtype=np.uint32)
+    for t in range(8):
+        word |= zz[:, :, t] << np.uint32(4 * t)
+    return word
+
+
+def unpack_zeros(words, G: int, N: int) -> np.ndarray:
+    w = np.asarray(words, dtype=np.uint32).reshape(G, N // 8)
+    out = np.empty((G, N // 8, 8), dtype=np.uint8)
+    for t in range(8):
+        out[:, :, t] = (w >> np.uint32(4 * t)) & np.uint32(0xF)
+    return out.reshape(G, N)
+
+
+def quantize_and_pack(w, group: int):
+    """Full offline step: (qweight bytes, scale bits [G][N], zero words [G][N/8], codes, zeros)."""
+    codes, s_bits, zeros = quantize_groupwise(w, group)
+    return pack_device(codes), s_bits, pack_zeros(zeros), codes, zeros
+
+
+# ---------------------------------------------------------------------------
+# The product. Activations stay 16-bit and the multiply is an ordinary
+# floating-point one against the rebuilt weights ("Weight-Only Quantization
+# Explained", "What W4A16 actually names" and "What it costs"). Here the
+# accumulation is fp64 (exact products of fp16/bf16 and s*(q-z)).
+# ---------------------------------------------------------------------------
+
+
+def linear_ref(x_bits, x_dtype: str, w_hat):
+    """y_ref [M][N] = x @ w_hat^T and A [M][N] = |x| @ |w_hat|^T, both fp64."""
+    x = act_bits_to_f64(x_bits, x_dtype)
+    if x.ndim == 1:
+        x = x[None, :]
+    w_hat = np.asarray(w_hat, dtype=np.float64)
+    y = x @ w_hat.T
+    a = np.abs(x) @ np.abs(w_hat).T
+    return y, a
+
+
+def linear_ref_rows(x_bits, x_dtype: str, codes, scale_bits, zeros, group: int, cols=None):
+    """Same as linear_ref but dequantises only the requested output columns n."""
+    codes = np.asarray(codes)
+    if cols is not None:
+        codes = codes[cols]
+        scale_bits = np.asarray(scale_bits)[:, cols]
+        zeros = np.asarray(zeros)[:, cols]
+    w_hat = dequantize(codes, scale_bits, zeros, group)
+    return linear_ref(x_bits, x_dtype, w_hat)
+
+
+TOL_REL = 2e-3
+TOL_ABS = 1e-5
+
+
+def error_ratio(y_gpu, y_ref, a) -> np.ndarray:
+    """|y - y_ref| / (2e-3 * sum|x*w_hat| + 1e-5); the acceptance bar is <= 1."""
+    y_gpu = np.asarray(y_gpu, dtype=np.float64)
+    return np.abs(y_gpu - y_ref) / (TOL_REL * a + TOL_ABS)

@@ -1,0 +1,329 @@
+"""Pins for the CPU oracle: each check ties it to something other than itself
+(values printed on the pages, IEEE 754 facts, a library routine for a special
+case, brute force, exact rational arithmetic)."""
+import json
+import os
+from fractions import Fraction
+
+import numpy as np
+import pytest
+import torch
+
+from oracle import w4a16_ref as ref
+
+# ---------------------------------------------------------------------------
+# 16-bit conversions
+# ---------------------------------------------------------------------------
+
+
+def _all_finite_f16():
+    b = np.arange(65536, dtype=np.uint32).astype(np.uint16)
+    f = b.view(np.float16)
+    return b[np.isfinite(f)]
+
+
+def test_f16_widening_matches_numpy_for_every_pattern():
+    b = np.arange(65536, dtype=np.uint32).astype(np.uint16)
+    ours = ref.f16_bits_to_f64(b)
+    lib = b.view(np.float16).astype(np.float64)
+    nan = np.isnan(lib)
+    assert np.array_equal(np.isnan(ours), nan)
+    assert np.array_equal(ours[~nan], lib[~nan])
+
+
+def test_f16_narrowing_roundtrips_every_finite_value():
+    b = _all_finite_f16()
+    f32 = b.view(np.float16).astype(np.float32)
+    assert np.array_equal(ref.f32_to_f16_bits(f32), b)
+
+
+def test_f16_narrowing_midpoints_and_neighbours_match_numpy():
+    # midpoints between consecutive non-negative finite fp16 values are exact in fp32
+    b = np.arange(0, 0x7C00, dtype=np.uint32).astype(np.uint16)
+    lo = b.view(np.float16).astype(np.float64)
+    hi = (b + 1).astype(np.uint16).view(np.float16).astype(np.float64)
+    hi[-1] = 65520.0  # the rounding boundary above the largest finite value
+    mid = ((lo + hi) / 2).astype(np.float32)
+    cases = [mid, np.nextafter(mid, np.float32(np.inf)), np.nextafter(mid, np.float32(0))]
+    x = np.concatenate(cases)
+    x = np.concatenate([x, -x])
+    assert np.array_equal(ref.f32_to_f16_bits(x), x.astype(np.float16).view(np.uint16))
+
+
+def test_f16_narrowing_random_patterns_match_numpy():
+    rng = np.random.default_rng(7)
+    u = rng.integers(0, 2**32, size=2_000_000, dtype=np.uint64).astype(np.uint32)
+    x = u.view(np.float32)
+    x = x[~np.isnan(x)]
+    with np.errstate(over="ignore"):
+        lib = x.astype(np.float16).view(np.uint16)
+    assert np.array_equal(ref.f32_to_f16_bits(x), lib)
+
+
+def test_f16_ieee_special_cases():
+    # closed forms from the binary16 definition
+    cases = [
+        (0.0, 0x0000), (-0.0, 0x8000), (1.0, 0x3C00), (-2.0, 0xC000),
+        (65504.0, 0x7BFF), (65519.0, 0x7BFF), (65520.0, 0x7C00), (1e9, 0x7C00),
+        (2.0**-24, 0x0001), (2.0**-25, 0x0000),            # tie -> even (zero)
+        (3 * 2.0**-25, 0x0002),                            # tie between 1 and 2 units -> 2
+        (2.0**-14, 0x0400), (1.0 + 2.0**-11, 0x3C00),      # tie -> even
+        (1.0 + 3 * 2.0**-11, 0x3C02), (float("inf"), 0x7C00), (float("-inf"), 0xFC00),
+    ]
+    for v, bits in cases:
+        assert int(ref.f32_to_f16_bits(np.array([v], np.float32))[0]) == bits, v
+    assert int(ref.f32_to_f16_bits(np.array([np.nan], np.float32))[0]) & 0x7C00 == 0x7C00
+
+
+def test_bf16_narrowing_matches_torch():
+    rng = np.random.default_rng(11)
+    u = rng.integers(0, 2**32, size=2_000_000, dtype=np.uint64).astype(np.uint32)
+    x = u.view(np.float32)
+    x = x[~np.isnan(x)]
+    lib = torch.from_numpy(x).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    assert np.array_equal(ref.f32_to_bf16_bits(x), lib)
+    # exact ties
+    t = (np.arange(1, 1 << 16, dtype=np.uint32) << 16) | np.uint32(0x8000)
+    t = t[((t >> 23) & 0xFF) != 0xFF].view(np.float32)
+    lib = torch.from_numpy(t).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    assert np.array_equal(ref.f32_to_bf16_bits(t), lib)
+
+
+def test_bf16_widening_every_pattern():
+    b = np.arange(65536, dtype=np.uint32).astype(np.uint16)
+    ours = ref.bf16_bits_to_f64(b)
+    lib = torch.from_numpy(b.view(np.int16)).view(torch.bfloat16).double().numpy()
+    nan = np.isnan(lib)
+    assert np.array_equal(np.isnan(ours), nan)
+    assert np.array_equal(ours[~nan], lib[~nan])
+
+
+# ---------------------------------------------------------------------------
+# Byte accounting: values printed on the pages
+# ---------------------------------------------------------------------------
+
+
+def test_sizing_matches_printed_values(golden_dir):
+    g = json.load(open(os.path.join(golden_dir, "memory_arithmetic.json")))
+    bpw = ref.bits_per_weight(128)
+    assert bpw == 4.15625
+    assert round(bpw, 3) == g["bits_per_weight_g128_printed"]
+    n13 = g["params_13b"]
+    assert ref.model_bytes(n13, 16) / 1e9 == g["fp16_weight_bytes_13b_printed_GB"]
+    assert round(ref.model_bytes(n13, bpw) / 1e9, 2) == g["w4_weight_bytes_13b_printed_GB"]
+    assert round(ref.model_bytes(n13, g["bits_per_weight_g128_printed"]) / 1e9, 2) == \
+        g["w4_weight_bytes_13b_printed_GB"]
+    saved = ref.model_bytes(n13, 16) - ref.model_bytes(n13, bpw)
+    assert round(saved / 1e9, 1) == g["saved_13b_printed_GB"]
+    assert round(g["hidden_13b"] * 2 / 1e3, 1) == g["one_token_activation_fp16_printed_kB"]
+    assert round(g["hidden_13b"] * 1 / 1e3, 1) == g["one_token_activation_int8_printed_kB"]
+    n70 = g["params_70b"]
+    assert ref.model_bytes(n70, 16) / 1e9 == g["bf16_weight_bytes_70b_printed_GB"]
+    assert ref.model_bytes(n70, 4) / 1e9 == g["int4_weight_bytes_70b_printed_GB"]
+
+
+@pytest.mark.parametrize("N,K,group", [(4096, 4096, 128), (8192, 28672, 32), (5120, 13824, 128),
+                                       (15360, 5120, 64)])
+def test_packed_bytes_equal_bits_per_weight(N, K, group):
+    q, s, z = ref.packed_bytes(N, K, group)
+    assert (q + s + z) * 8 == N * K * ref.bits_per_weight(group)
+    assert q * 8 == 4 * N * K
+
+
+# ---------------------------------------------------------------------------
+# Quantiser
+# ---------------------------------------------------------------------------
+
+
+def _exact_w_hat(codes, s_bits, zeros, group):
+    return ref.dequantize(codes, s_bits, zeros, group)
+
+
+@pytest.mark.parametrize("group", [32, 64, 128])
+def test_quantizer_codes_are_nearest_grid_points(group):
+    rng = np.random.default_rng(group)
+    w = (rng.standard_normal((24, 4 * group)) * 0.02).astype(np.float32)
+    w[3] = np.abs(w[3])          # one-signed rows
+    w[4] = -np.abs(w[4])
+    w[5, :group] = 0.25          # constant group
+    codes, s_bits, zeros = ref.quantize_groupwise(w, group)
+    N, K = w.shape
+    G = K // group
+    s = ref.f16_bits_to_f64(s_bits).T                     # [N][G]
+    z = zeros.T.astype(np.int64)
+    w64 = w.astype(np.float64).reshape(N, G, group)
+    grid = (np.arange(16)[None, None, None, :] - z[:, :, None, None]) * s[:, :, None, None]
+    dist = np.abs(w64[..., None] - grid)                  # [N][G][g][16]
+    best = dist.min(axis=-1)
+    got = np.take_along_axis(dist, codes.reshape(N, G, group, 1).astype(np.int64), axis=-1)[..., 0]
+    assert np.all(got <= best + 2.0**-20 * np.abs(w64) + 1e-30)
+
+
+def test_quantizer_exact_ties_round_to_even():
+    s = 2.0**-6
+    j = np.arange(-8, 7)                           # (j + 1/2) s lies strictly inside the grid
+    vals = np.concatenate([[-8 * s, 7 * s], (j + 0.5) * s, np.zeros(128 - 2 - j.size)])
+    w = vals.astype(np.float32)[None, :]
+    codes, s_bits, zeros = ref.quantize_groupwise(w, 128)
+    assert ref.f16_bits_to_f64(s_bits)[0, 0] == s
+    assert zeros[0, 0] == 8
+    d = codes[0, 2:2 + j.size].astype(np.int64) - 8
+    want = np.where(j % 2 == 0, j, j + 1)          # the even one of j, j+1
+    assert np.array_equal(d, want)
+
+
+@pytest.mark.parametrize("group", [32, 64, 128])
+def test_round_trip_error_within_half_scale(group):
+    rng = np.random.default_rng(100 + group)
+    w = (rng.standard_t(4, size=(64, 8 * group)) * 0.02).astype(np.float32)
+    codes, s_bits, zeros = ref.quantize_groupwise(w, group)
+    w_hat = _exact_w_hat(codes, s_bits, zeros, group)
+    N, K = w.shape
+    G = K // group
+    s = np.repeat(ref.f16_bits_to_f64(s_bits).T, group, axis=1)
+    err = np.abs(w.astype(np.float64) - w_hat)
+    inner = (codes > 0) & (codes < 15)
+    assert np.all(err[inner] <= 0.5 * s[inner] + 2.0**-24 * np.abs(w[inner]))
+    # clamped codes: half a step plus the fp16 rounding of the scale over 15 steps
+    wg = w.astype(np.float64).reshape(N, G, group)
+    s_real = (np.maximum(wg.max(2), 0) - np.minimum(wg.min(2), 0)) / 15
+    s_real = np.repeat(s_real, group, axis=1)
+    bound = 0.5 * s + 15 * np.abs(s_real - s) + 2.0**-20 * np.abs(w).max()
+    assert np.all(err <= bound)
+
+
+@pytest.mark.parametrize("group", [32, 64, 128])
+def test_lattice_weights_are_reproduced_exactly(group):
+    rng = np.random.default_rng(200 + group)
+    N, G = 40, 6
+    q = rng.integers(0, 16, size=(N, G, group))
+    q[:, :, 0] = 0
+    q[:, :, 1] = 15
+    q = np.take_along_axis(q, rng.permuted(np.tile(np.arange(group), (N, G, 1)), axis=2), axis=2)
+    z = rng.integers(0, 16, size=(N, G))
+    e = rng.integers(-20, -2, size=(N, G))
+    s = np.ldexp(1.0, e)
+    W = ((q - z[:, :, None]) * s[:, :, None]).reshape(N, G * group).astype(np.float32)
+    codes, s_bits, zeros = ref.quantize_groupwise(W, group)
+    assert np.array_equal(codes.reshape(N, G, group), q.astype(np.uint8))
+    assert np.array_equal(ref.f16_bits_to_f64(s_bits).T, s)
+    assert np.array_equal(zeros.T, z.astype(np.uint8))
+    assert np.array_equal(_exact_w_hat(codes, s_bits, zeros, group), W.astype(np.float64))
+
+
+def test_degenerate_groups():
+    w = np.zeros((8, 96), dtype=np.float32)
+    w[1, :32] = 1e-12                                    # range underflows fp16
+    w[2, :32] = 0.5                                      # constant positive group
+    w[3, :32] = -0.5                                     # constant negative group
+    codes, s_bits, zeros = ref.quantize_groupwise(w, 32)
+    assert s_bits[0, 0] == 0x0001 and zeros[0, 0] == 0 and codes[0, 0] == 0
+    assert s_bits[0, 1] == 0x0001 and np.all(codes[1, :32] == 0)
+    w_hat = ref.dequantize(codes, s_bits, zeros, 32)
+    assert np.all(w_hat[0] == 0.0)
+    assert np.all(w_hat[4:] == 0.0)
+    assert zeros[0, 2] == 0 and np.all(codes[2, :32] == 15)
+    assert zeros[0, 3] == 15 and np.all(codes[3, :32] == 0)
+    s2 = ref.f16_bits_to_f64(s_bits[0, 2])
+    assert abs(w_hat[2, 0] - 0.5) <= 15 * abs(0.5 / 15 - s2) + 1e-12
+
+
+def test_quantizer_rejects_bad_input():
+    with pytest.raises(ValueError):
+        ref.quantize_groupwise(np.zeros((8, 100), np.float32), 32)
+    with pytest.raises(ValueError):
+        ref.quantize_groupwise(np.full((8, 32), np.inf, np.float32), 32)
+
+
+# ---------------------------------------------------------------------------
+# Dequantisation and product
+# ---------------------------------------------------------------------------
+
+
+def _frac_f16(bits):
+    v = ref.f16_bits_to_f64(np.uint16(bits))
+    return Fraction(float(v))
+
+
+@pytest.mark.parametrize("M,N,K,group,dtype", [(1, 8, 32, 32, "f16"), (3, 16, 256, 64, "f16"),
+                                               (2, 16, 128, 128, "bf16")])
+def test_product_matches_exact_rational_sum(M, N, K, group, dtype):
+    rng = np.random.default_rng(M * 1000 + N + K)
+    w = (rng.standard_normal((N, K)) * 0.02).astype(np.float32)
+    x32 = rng.standard_normal((M, K)).astype(np.float32)
+    xb = x32.astype(np.float16).view(np.uint16) if dtype == "f16" else \
+        torch.from_numpy(x32).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    codes, s_bits, zeros = ref.quantize_groupwise(w, group)
+    y, a = ref.linear_ref_rows(xb, dtype, codes, s_bits, zeros, group)
+    xv = ref.act_bits_to_f64(xb, dtype)
+    for m in range(M):
+        for n in range(N):
+            acc = Fraction(0)
+            acc_abs = Fraction(0)
+            for k in range(K):
+                g = k // group
+                wk = _frac_f16(s_bits[g, n]) * (int(codes[n, k]) - int(zeros[g, n]))
+                term = Fraction(float(xv[m, k])) * wk
+                acc += term
+                acc_abs += abs(term)
+            assert abs(Fraction(float(y[m, n])) - acc) <= K * Fraction(2) ** -53 * acc_abs
+            assert abs(Fraction(float(a[m, n])) - acc_abs) <= K * Fraction(2) ** -53 * acc_abs
+
+
+def test_one_hot_activation_selects_a_dequantised_weight():
+    rng = np.random.default_rng(5)
+    w = (rng.standard_normal((16, 128)) * 0.02).astype(np.float32)
+    codes, s_bits, zeros = ref.quantize_groupwise(w, 64)
+    w_hat = ref.dequantize(codes, s_bits, zeros, 64)
+    for k in (0, 63, 64, 127):
+        x = np.zeros((1, 128), dtype=np.float16)
+        x[0, k] = 1.0
+        y, a = ref.linear_ref(x.view(np.uint16), "f16", w_hat)
+        assert np.array_equal(y[0], w_hat[:, k])
+        assert np.array_equal(a[0], np.abs(w_hat[:, k]))
+
+
+def test_error_ratio_bar():
+    y_ref = np.array([[1.0, 0.0]])
+    a = np.array([[10.0, 0.0]])
+    r = ref.error_ratio(np.array([[1.0 + 0.02001, 1e-5]]), y_ref, a)
+    assert np.allclose(r, [[1.0, 1.0]], rtol=1e-9)
+
+
+# ---------------------------------------------------------------------------
+# Layouts
+# ---------------------------------------------------------------------------
+
+
+@pytest.mark.parametrize("N,K", [(64, 32), (72, 64), (200, 96), (8, 32), (136, 256)])
+def test_device_layout_is_a_permutation(N, K):
+    idx = ref._device_nibble_index(N, K).ravel()
+    assert np.array_equal(np.sort(idx), np.arange(N * K))
+
+
+def test_device_layout_worked_example(golden_dir):
+    g = json.load(open(os.path.join(golden_dir, "device_layout_example.json")))
+    N, K = g["N"], g["K"]
+    for p in g["positions"]:
+        codes = np.zeros((N, K), dtype=np.uint8)
+        codes[p["n"], p["k"]] = 0xA
+        packed = ref.pack_device(codes)
+        nz = np.nonzero(packed)[0]
+        assert list(nz) == [p["byte"]], p
+        assert packed[p["byte"]] == (0xA0 if p["high_nibble"] else 0x0A), p
+
+
+@pytest.mark.parametrize("N,K", [(72, 64), (200, 96), (4096, 128)])
+def test_device_layout_round_trip(N, K):
+    rng = np.random.default_rng(N + K)
+    codes = rng.integers(0, 16, size=(N, K), dtype=np.uint8)
+    packed = ref.pack_device(codes)
+    assert packed.size == N * K // 2
+    assert np.array_equal(ref.unpack_device(packed, N, K), codes)
+
+
+def test_zero_packing_by_hand():
+    z = np.array([[1, 2, 3, 4, 5, 6, 7, 8, 15, 0, 0, 0, 0, 0, 0, 9]], dtype=np.uint8)
+    words = ref.pack_zeros(z)
+    assert words.tolist() == [[0x87654321, 0x9000000F]]
+    assert np.array_equal(ref.unpack_zeros(words, 1, 16), z)
