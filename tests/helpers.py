@@ -1,0 +1,70 @@
+"""Shared helpers for the GPU parity tests: seeded inputs -> oracle -> HIP path."""
+from __future__ import annotations
+
+import numpy as np
+
+from oracle import w4a16_ref as ref
+
+_CACHE = {}
+
+
+def lib():
+    import w4a16_weight_only_dequant_amd as w4
+    return w4
+
+
+def oracle_pack(w: np.ndarray, group: int):
+    codes, s_bits, zeros = ref.quantize_groupwise(w, group)
+    return {
+        "codes": codes,
+        "s_bits": s_bits,
+        "zeros": zeros,
+        "qweight": ref.pack_device(codes),
+        "zero_words": ref.pack_zeros(zeros),
+    }
+
+
+def gpu_pack(w: np.ndarray, group: int):
+    import torch
+    wt = torch.from_numpy(w).cuda()
+    pw = lib().pack(wt, group)
+    torch.cuda.synchronize()
+    del wt
+    return pw
+
+
+def prepared(key, make_w, group):
+    """Weights, oracle quantisation and the GPU-packed weight, cached per key."""
+    if key not in _CACHE:
+        w = make_w()
+        o = oracle_pack(w, group)
+        pw = gpu_pack(w, group)
+        _CACHE[key] = (w, o, pw)
+    return _CACHE[key]
+
+
+def drop(key):
+    _CACHE.pop(key, None)
+
+
+def to_device_bits(x_bits: np.ndarray, dtype: str):
+    import torch
+    t = torch.from_numpy(np.ascontiguousarray(x_bits).view(np.int16)).cuda()
+    return t.view(torch.float16 if dtype == "f16" else torch.bfloat16)
+
+
+def y_to_f64(y) -> np.ndarray:
+    return y.float().cpu().numpy().astype(np.float64)
+
+
+def check_against_oracle(y_gpu, x_bits, dtype, o, group, cols=None):
+    """Assert |y - y_ref| <= 2e-3 * sum|x w_hat| + 1e-5 element-wise; return the max ratio."""
+    y = y_to_f64(y_gpu)
+    if cols is not None:
+        y = y[:, cols]
+    y_ref, a = ref.linear_ref_rows(x_bits, dtype, o["codes"], o["s_bits"], o["zeros"], group, cols)
+    r = ref.error_ratio(y, y_ref, a)
+    worst = float(r.max()) if r.size else 0.0
+    assert np.all(np.isfinite(y)), "non-finite output"
+    assert worst <= 1.0, f"max error ratio {worst:.3g} (> 1) at {np.unravel_index(np.argmax(r), r.shape)}"
+    return worst

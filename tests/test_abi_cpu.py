@@ -1,0 +1,109 @@
+"""C ABI checks that need no GPU: the library loads, exports every declared
+symbol, sizes buffers by the closed form, and rejects bad arguments before
+touching the device."""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "w4a16.h")
+
+
+def _declared():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(w4a16_[a-z0-9_]+)\s*\(", text)))
+
+
+@pytest.fixture(scope="module")
+def w4():
+    import w4a16_weight_only_dequant_amd as w4
+    return w4
+
+
+def test_library_exports_every_declared_symbol(w4):
+    lib = ctypes.CDLL(w4.LIB_PATH)
+    names = _declared()
+    assert len(names) >= 10
+    for name in names:
+        assert hasattr(lib, name), name
+    assert set(names) == set(w4.EXPORTED)
+
+
+def test_status_strings_and_version(w4):
+    lib = w4.raw()
+    assert lib.w4a16_layout_version() == 1
+    for code in range(5):
+        assert lib.w4a16_status_string(code)
+    assert lib.w4a16_status_string(99) == b"unknown status"
+
+
+@pytest.mark.parametrize("N,K,group", [(4096, 4096, 128), (8192, 28672, 32), (5120, 13824, 128), (72, 96, 32)])
+def test_packed_bytes_closed_form(w4, N, K, group):
+    G = K // group
+    assert w4.packed_bytes(N, K, group) == (N * K // 2, 2 * G * N, G * N // 2)
+
+
+@pytest.mark.parametrize("N,K,group", [(100, 128, 128), (4, 128, 128), (64, 100, 32), (64, 128, 16),
+                                       (64, 64, 128), (64, 0, 32)])
+def test_bad_shapes_rejected(w4, N, K, group):
+    with pytest.raises(w4.W4A16Error) as e:
+        w4.packed_bytes(N, K, group)
+    assert e.value.status == 1
+
+
+def test_workspace_sizes_monotone_and_bounded(w4):
+    for M in (1, 2, 8, 16, 64, 2048):
+        b = w4.workspace_bytes(M, 4096, 4096, 128)
+        assert 0 <= b <= 64 * M * 4096 * 4 + (1 << 16)
+
+
+def test_compute_calls_validate_before_device(w4):
+    lib = w4.raw()
+    ws = ctypes.c_size_t(0)
+    fake = ctypes.c_void_p(1 << 20)   # never dereferenced: every call below fails validation first
+    # NULL x
+    assert lib.w4a16_gemv(None, 0, fake, fake, fake, fake, 1, 64, 128, 128, None, 0, None) == 1
+    # bad dtype
+    assert lib.w4a16_gemm(fake, 7, fake, fake, fake, ctypes.c_void_p(1 << 30), 1, 64, 128, 128, None, 0, None) == 1
+    # M > 8 on the GEMV entry point
+    assert lib.w4a16_gemv(fake, 0, fake, fake, fake, fake, 9, 64, 128, 128, None, 0, None) == 1
+    # misaligned pointer
+    assert lib.w4a16_linear(ctypes.c_void_p((1 << 20) + 2), 0, fake, fake, fake, ctypes.c_void_p(1 << 30),
+                            1, 64, 128, 128, None, 0, None) == 1
+    # y overlapping x
+    assert lib.w4a16_gemm(fake, 0, ctypes.c_void_p(1 << 30), ctypes.c_void_p(1 << 31), ctypes.c_void_p(1 << 32),
+                          fake, 4, 64, 128, 128, None, 0, None) == 1
+    # group / shape
+    assert lib.w4a16_gemv(fake, 0, fake, fake, fake, fake, 1, 64, 128, 48, None, 0, None) == 1
+    assert lib.w4a16_pack(None, 64, 128, 128, fake, fake, fake, None) == 1
+    assert lib.w4a16_unpack(fake, fake, fake, 60, 128, 128, fake, fake, fake, None) == 1
+    assert lib.w4a16_workspace_bytes(0, 64, 128, 128, ctypes.byref(ws)) == 1
+
+
+def test_missing_workspace_reported(w4):
+    lib = w4.raw()
+    shapes = [(M, N, K, g) for M in (1, 4, 16, 64, 256) for (N, K, g) in
+              ((4096, 4096, 128), (8192, 28672, 32), (15360, 5120, 128))]
+    needy = [s for s in shapes if w4.workspace_bytes(*s) > 0]
+    if not needy:
+        pytest.skip("no shape needs a workspace in this build")
+    M, N, K, g = needy[0]
+    need = w4.workspace_bytes(M, N, K, g)
+    a = [ctypes.c_void_p((1 << 34) + i * (1 << 30)) for i in range(5)]
+    st = lib.w4a16_gemm(a[0], 0, a[1], a[2], a[3], a[4], M, N, K, g, None, 0, None)
+    assert st == 4
+    st = lib.w4a16_gemm(a[0], 0, a[1], a[2], a[3], a[4], M, N, K, g, ctypes.c_void_p(1 << 40), need - 1, None)
+    assert st == 4
+
+
+def test_product_path_never_touches_the_oracle():
+    pkg = os.path.join(ROOT, "w4a16_weight_only_dequant_amd")
+    for dirpath, _, files in os.walk(pkg):
+        for f in files:
+            if f.endswith((".py", ".hip", ".hpp", ".cpp", ".h")):
+                text = open(os.path.join(dirpath, f)).read()
+                assert "oracle" not in text.lower().replace("oracle/", ""), f
+                assert "w4a16_ref" not in text, f

@@ -1,0 +1,7 @@
+"""MI355X (gfx950) W4A16 weight-only linear layer.
+
+The compute lives in libw4a16.so (hand-written HIP kernels behind a C ABI,
+include/w4a16.h); this package is its thin Python binding.
+"""
+from ._lib import (EXPORTED, LIB_PATH, PackedWeight, W4A16Error, Workspace, device_supported,  # noqa: F401
+                   gemm, gemv, gemv_max_m, linear, pack, packed_bytes, raw, unpack, workspace_bytes)

@@ -1,0 +1,216 @@
+"""ctypes binding of libw4a16.so (the gfx950 HIP library).
+
+Argument marshalling only: every step of the linear layer runs in the HIP
+kernels behind the C ABI declared in include/w4a16.h. PyTorch supplies device
+memory and the current HIP stream. If the shared library is missing this
+module raises at import time; there is no fallback path.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+# W4A16_LIB may name another build of the same library (e.g. a tuning variant)
+LIB_PATH = os.environ.get("W4A16_LIB") or os.path.join(_HERE, "libw4a16.so")
+
+W4A16_OK = 0
+W4A16_F16 = 0
+W4A16_BF16 = 1
+
+if not os.path.exists(LIB_PATH):
+    raise ImportError(
+        f"{LIB_PATH} is missing: build it with `python -c 'import __graft_entry__ as g; g.build()'` "
+        "(hipcc, gfx950). There is no CPU fallback.")
+
+_lib = ctypes.CDLL(LIB_PATH)
+
+_i64 = ctypes.c_int64
+_i32 = ctypes.c_int32
+_sz = ctypes.c_size_t
+_vp = ctypes.c_void_p
+_szp = ctypes.POINTER(ctypes.c_size_t)
+
+_SIGS = {
+    "w4a16_status_string": (ctypes.c_char_p, [ctypes.c_int]),
+    "w4a16_layout_version": (ctypes.c_int, []),
+    "w4a16_gemv_max_m": (_i32, []),
+    "w4a16_device_supported": (ctypes.c_int, [ctypes.c_int]),
+    "w4a16_packed_bytes": (ctypes.c_int, [_i64, _i64, _i32, _szp, _szp, _szp]),
+    "w4a16_workspace_bytes": (ctypes.c_int, [_i64, _i64, _i64, _i32, _szp]),
+    "w4a16_pack": (ctypes.c_int, [_vp, _i64, _i64, _i32, _vp, _vp, _vp, _vp]),
+    "w4a16_unpack": (ctypes.c_int, [_vp, _vp, _vp, _i64, _i64, _i32, _vp, _vp, _vp, _vp]),
+    "w4a16_gemv": (ctypes.c_int, [_vp, _i32, _vp, _vp, _vp, _vp, _i64, _i64, _i64, _i32, _vp, _sz, _vp]),
+    "w4a16_gemm": (ctypes.c_int, [_vp, _i32, _vp, _vp, _vp, _vp, _i64, _i64, _i64, _i32, _vp, _sz, _vp]),
+    "w4a16_linear": (ctypes.c_int, [_vp, _i32, _vp, _vp, _vp, _vp, _i64, _i64, _i64, _i32, _vp, _sz, _vp]),
+}
+
+EXPORTED = tuple(_SIGS)
+
+for _name, (_res, _args) in _SIGS.items():
+    _f = getattr(_lib, _name)
+    _f.restype = _res
+    _f.argtypes = _args
+
+
+class W4A16Error(RuntimeError):
+    def __init__(self, fn: str, status: int):
+        msg = _lib.w4a16_status_string(status).decode()
+        super().__init__(f"{fn} failed: {msg} (status {status})")
+        self.status = status
+
+
+def _check(fn: str, status: int):
+    if status != W4A16_OK:
+        raise W4A16Error(fn, status)
+
+
+def raw():
+    """The ctypes handle, for tests of the C ABI itself."""
+    return _lib
+
+
+def _stream_ptr(stream=None) -> int:
+    s = stream if stream is not None else torch.cuda.current_stream()
+    return s.cuda_stream
+
+
+def _dtype_code(t: torch.Tensor) -> int:
+    if t.dtype == torch.float16:
+        return W4A16_F16
+    if t.dtype == torch.bfloat16:
+        return W4A16_BF16
+    raise TypeError(f"activations must be float16 or bfloat16, got {t.dtype}")
+
+
+def packed_bytes(N: int, K: int, group: int):
+    q, s, z = _sz(), _sz(), _sz()
+    _check("w4a16_packed_bytes", _lib.w4a16_packed_bytes(N, K, group, ctypes.byref(q), ctypes.byref(s),
+                                                         ctypes.byref(z)))
+    return q.value, s.value, z.value
+
+
+def workspace_bytes(M: int, N: int, K: int, group: int) -> int:
+    b = _sz()
+    _check("w4a16_workspace_bytes", _lib.w4a16_workspace_bytes(M, N, K, group, ctypes.byref(b)))
+    return b.value
+
+
+def device_supported(device: int = 0) -> bool:
+    st = _lib.w4a16_device_supported(device)
+    if st not in (0, 2):
+        _check("w4a16_device_supported", st)
+    return st == 0
+
+
+def gemv_max_m() -> int:
+    return int(_lib.w4a16_gemv_max_m())
+
+
+class PackedWeight:
+    """Packed W4A16 weight of an N x K linear layer, resident in device memory."""
+
+    def __init__(self, qweight, scales, zeros, N, K, group):
+        self.qweight = qweight    # uint8 [N*K/2], device layout
+        self.scales = scales      # float16 [G][N]
+        self.zeros = zeros        # int32 [G][N/8] (4-bit zeros, 8 per word)
+        self.N, self.K, self.group = N, K, group
+
+    def nbytes(self) -> int:
+        return self.qweight.numel() + 2 * self.scales.numel() + 4 * self.zeros.numel()
+
+
+def pack(w: torch.Tensor, group: int, stream=None) -> PackedWeight:
+    """Quantise fp32 weights [N][K] (device) and pack them (w4a16_pack)."""
+    if w.dtype != torch.float32 or w.dim() != 2 or not w.is_cuda:
+        raise TypeError("w must be a 2-D float32 CUDA tensor [N][K]")
+    w = w.contiguous()
+    N, K = w.shape
+    qb, sb, zb = packed_bytes(N, K, group)
+    G = K // group
+    dev = w.device
+    qweight = torch.empty(qb, dtype=torch.uint8, device=dev)
+    scales = torch.empty((G, N), dtype=torch.float16, device=dev)
+    zeros = torch.empty((G, N // 8), dtype=torch.int32, device=dev)
+    assert scales.numel() * 2 == sb and zeros.numel() * 4 == zb
+    _check("w4a16_pack", _lib.w4a16_pack(w.data_ptr(), N, K, group, qweight.data_ptr(), scales.data_ptr(),
+                                         zeros.data_ptr(), _stream_ptr(stream)))
+    return PackedWeight(qweight, scales, zeros, N, K, group)
+
+
+def unpack(pw: PackedWeight, stream=None):
+    """Canonical view (codes u8 [N][K], scale bits int16 [G][N], zeros u8 [G][N])."""
+    N, K, group = pw.N, pw.K, pw.group
+    G = K // group
+    dev = pw.qweight.device
+    codes = torch.empty((N, K), dtype=torch.uint8, device=dev)
+    s_out = torch.empty((G, N), dtype=torch.int16, device=dev)
+    z_out = torch.empty((G, N), dtype=torch.uint8, device=dev)
+    _check("w4a16_unpack", _lib.w4a16_unpack(pw.qweight.data_ptr(), pw.scales.data_ptr(), pw.zeros.data_ptr(),
+                                             N, K, group, codes.data_ptr(), s_out.data_ptr(),
+                                             z_out.data_ptr(), _stream_ptr(stream)))
+    return codes, s_out, z_out
+
+
+class Workspace:
+    """Zero-initialised device workspace for split-K partial sums and counters.
+
+    The library leaves the counters at zero after every completed call, so one
+    buffer can be reused by consecutive calls on one stream.
+    """
+
+    def __init__(self, device=None):
+        self.device = torch.device(device) if device is not None else torch.device("cuda")
+        self.buf = None
+
+    def get(self, nbytes: int):
+        if nbytes == 0:
+            return None
+        if self.buf is None or self.buf.numel() < nbytes:
+            self.buf = torch.zeros(max(nbytes, 1 << 20), dtype=torch.uint8, device=self.device)
+        return self.buf
+
+
+_workspaces = {}
+
+
+def _default_workspace(device) -> Workspace:
+    key = (device.type, device.index)
+    ws = _workspaces.get(key)
+    if ws is None:
+        ws = _workspaces[key] = Workspace(device)
+    return ws
+
+
+def _call(fn_name: str, x: torch.Tensor, pw: PackedWeight, out=None, workspace=None, stream=None):
+    if x.dim() != 2 or x.shape[1] != pw.K or not x.is_cuda:
+        raise ValueError(f"x must be a CUDA tensor [M][{pw.K}]")
+    x = x.contiguous()
+    M = x.shape[0]
+    y = out if out is not None else torch.empty((M, pw.N), dtype=x.dtype, device=x.device)
+    nbytes = workspace_bytes(M, pw.N, pw.K, pw.group)
+    ws = (workspace or _default_workspace(x.device)).get(nbytes)
+    ws_ptr = ws.data_ptr() if ws is not None else None
+    ws_len = ws.numel() if ws is not None else 0
+    fn = getattr(_lib, fn_name)
+    _check(fn_name, fn(x.data_ptr(), _dtype_code(x), pw.qweight.data_ptr(), pw.scales.data_ptr(),
+                       pw.zeros.data_ptr(), y.data_ptr(), M, pw.N, pw.K, pw.group, ws_ptr, ws_len,
+                       _stream_ptr(stream)))
+    return y
+
+
+def gemv(x, pw, out=None, workspace=None, stream=None):
+    """Decode GEMV (M <= 8): y = x @ w_hat^T."""
+    return _call("w4a16_gemv", x, pw, out, workspace, stream)
+
+
+def gemm(x, pw, out=None, workspace=None, stream=None):
+    """MFMA GEMM (any M): y = x @ w_hat^T."""
+    return _call("w4a16_gemm", x, pw, out, workspace, stream)
+
+
+def linear(x, pw, out=None, workspace=None, stream=None):
+    """Default path, dispatching on M."""
+    return _call("w4a16_linear", x, pw, out, workspace, stream)

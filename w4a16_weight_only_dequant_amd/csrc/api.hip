@@ -1,0 +1,236 @@
+// C ABI of the gfx950 W4A16 library: argument checks, workspace sizing,
+// device check and dispatch on M. Declarations and contracts: include/w4a16.h.
+#include <hip/hip_runtime.h>
+
+#include <atomic>
+#include <cstdlib>
+#include <cstring>
+#include <mutex>
+
+#include "../../include/w4a16.h"
+#include "w4a16_internal.hpp"
+
+using namespace w4a16;
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+// 0 = not queried yet, 1 = gfx950, 2 = other device
+std::atomic<int> g_device_kind[kMaxDevices];
+
+int env_int(const char *name, int fallback) {
+    const char *v = std::getenv(name);
+    if (!v || !*v) return fallback;
+    char *end = nullptr;
+    long r = std::strtol(v, &end, 10);
+    return (end && *end == 0) ? (int)r : fallback;
+}
+
+// Largest M routed to the GEMV kernel by w4a16_linear (the GEMV kernel itself
+// accepts M <= 8).
+int gemv_max_m() {
+    static const int v = [] {
+        int m = env_int("W4A16_GEMV_MAX_M", 2);
+        return m < 0 ? 0 : (m > 8 ? 8 : m);
+    }();
+    return v;
+}
+
+bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+bool shape_ok(int64_t N, int64_t K, int32_t group) {
+    if (group != 32 && group != 64 && group != 128) return false;
+    if (N < 8 || N % 8 != 0) return false;
+    if (K < group || K % group != 0) return false;
+    // 32-bit index limits of the kernels
+    if (N > (1LL << 30) || K > (1LL << 30) || (N / 8) * K > (1LL << 31)) return false;
+    return true;
+}
+
+struct Range {
+    uintptr_t lo, hi;
+};
+bool overlap(Range a, Range b) { return a.lo < b.hi && b.lo < a.hi; }
+Range range_of(const void *p, size_t bytes) {
+    uintptr_t lo = reinterpret_cast<uintptr_t>(p);
+    return Range{lo, lo + bytes};
+}
+
+w4a16_status check_device() {
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return W4A16_ERR_HIP;
+    return w4a16_device_supported(dev);
+}
+
+// Argument checks shared by gemv / gemm / linear.
+w4a16_status check_linear(const void *x, int32_t dtype, const void *qweight, const void *scales,
+                          const void *zeros, void *y, int64_t M, int64_t N, int64_t K, int32_t group,
+                          void *workspace, size_t workspace_bytes, size_t need) {
+    if (!x || !qweight || !scales || !zeros || !y) return W4A16_ERR_INVALID_ARG;
+    if (dtype != W4A16_F16 && dtype != W4A16_BF16) return W4A16_ERR_INVALID_ARG;
+    if (M < 1 || M > (1LL << 24) || !shape_ok(N, K, group)) return W4A16_ERR_INVALID_ARG;
+    if (!aligned16(x) || !aligned16(qweight) || !aligned16(scales) || !aligned16(zeros) ||
+        !aligned16(y))
+        return W4A16_ERR_INVALID_ARG;
+    const int64_t G = K / group;
+    const Range ry = range_of(y, (size_t)(M * N * 2));
+    if (overlap(ry, range_of(x, (size_t)(M * K * 2))) ||
+        overlap(ry, range_of(qweight, (size_t)(N * K / 2))) ||
+        overlap(ry, range_of(scales, (size_t)(G * N * 2))) ||
+        overlap(ry, range_of(zeros, (size_t)(G * N / 2))))
+        return W4A16_ERR_INVALID_ARG;
+    if (need > 0) {
+        if (!workspace || workspace_bytes < need) return W4A16_ERR_WORKSPACE;
+        if (!aligned16(workspace)) return W4A16_ERR_INVALID_ARG;
+        if (overlap(ry, range_of(workspace, need))) return W4A16_ERR_INVALID_ARG;
+    }
+    return W4A16_OK;
+}
+
+// Largest LDS allocation of one workgroup on the current device (cached per device).
+std::atomic<int> g_max_lds[kMaxDevices];
+size_t max_lds_per_block() {
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return 64 * 1024;
+    int v = g_max_lds[dev].load(std::memory_order_acquire);
+    if (v == 0) {
+        if (hipDeviceGetAttribute(&v, hipDeviceAttributeMaxSharedMemoryPerBlock, dev) != hipSuccess || v <= 0)
+            v = 64 * 1024;
+        g_max_lds[dev].store(v, std::memory_order_release);
+    }
+    return (size_t)v;
+}
+
+// The GEMV stages all activations of the call in LDS; it takes M <= 8 and
+// M * K small enough for one workgroup's LDS.
+bool gemv_fits(int64_t M, int64_t K, int32_t dtype) {
+    if (M < 1 || M > 8) return false;
+    return gemv_lds_bytes(M, K, dtype == W4A16_BF16) + kGemvStaticLds <= max_lds_per_block();
+}
+
+size_t gemm_need(int64_t M, int64_t N, int64_t K, int32_t group) {
+    GemmPlan p = gemm_plan(M, N, K, group);
+    return p.k_splits > 1 ? p.counter_bytes + p.partial_bytes : 0;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char *w4a16_status_string(int status) {
+    switch (status) {
+        case W4A16_OK: return "ok";
+        case W4A16_ERR_INVALID_ARG: return "invalid argument";
+        case W4A16_ERR_UNSUPPORTED: return "device is not a gfx950";
+        case W4A16_ERR_HIP: return "HIP runtime error";
+        case W4A16_ERR_WORKSPACE: return "workspace missing or too small";
+        default: return "unknown status";
+    }
+}
+
+int w4a16_layout_version(void) { return W4A16_LAYOUT_VERSION; }
+
+int32_t w4a16_gemv_max_m(void) { return gemv_max_m(); }
+
+w4a16_status w4a16_device_supported(int device) {
+    if (device < 0) return W4A16_ERR_INVALID_ARG;
+    if (device < kMaxDevices) {
+        int k = g_device_kind[device].load(std::memory_order_acquire);
+        if (k == 1) return W4A16_OK;
+        if (k == 2) return W4A16_ERR_UNSUPPORTED;
+    }
+    hipDeviceProp_t prop;
+    if (hipGetDeviceProperties(&prop, device) != hipSuccess) return W4A16_ERR_HIP;
+    const bool ok = std::strncmp(prop.gcnArchName, "gfx950", 6) == 0;
+    if (device < kMaxDevices) g_device_kind[device].store(ok ? 1 : 2, std::memory_order_release);
+    return ok ? W4A16_OK : W4A16_ERR_UNSUPPORTED;
+}
+
+w4a16_status w4a16_packed_bytes(int64_t N, int64_t K, int32_t group, size_t *qweight_bytes,
+                                size_t *scales_bytes, size_t *zeros_bytes) {
+    if (!shape_ok(N, K, group)) return W4A16_ERR_INVALID_ARG;
+    const int64_t G = K / group;
+    if (qweight_bytes) *qweight_bytes = (size_t)(N * K / 2);
+    if (scales_bytes) *scales_bytes = (size_t)(2 * G * N);
+    if (zeros_bytes) *zeros_bytes = (size_t)(G * N / 2);
+    return W4A16_OK;
+}
+
+w4a16_status w4a16_workspace_bytes(int64_t M, int64_t N, int64_t K, int32_t group, size_t *bytes) {
+    if (!bytes || M < 1 || M > (1LL << 24) || !shape_ok(N, K, group)) return W4A16_ERR_INVALID_ARG;
+    *bytes = gemm_need(M, N, K, group);
+    return W4A16_OK;
+}
+
+w4a16_status w4a16_pack(const float *w, int64_t N, int64_t K, int32_t group, void *qweight,
+                        void *scales, void *zeros, void *stream) {
+    if (!w || !qweight || !scales || !zeros || !shape_ok(N, K, group)) return W4A16_ERR_INVALID_ARG;
+    if (!aligned16(w) || !aligned16(qweight) || !aligned16(scales) || !aligned16(zeros))
+        return W4A16_ERR_INVALID_ARG;
+    if ((int64_t)(K / group) * N > (1LL << 31)) return W4A16_ERR_INVALID_ARG;
+    w4a16_status st = check_device();
+    if (st != W4A16_OK) return st;
+    hipError_t e = launch_pack(w, (int)N, (int)K, group, qweight, scales, zeros,
+                               reinterpret_cast<hipStream_t>(stream));
+    return e == hipSuccess ? W4A16_OK : W4A16_ERR_HIP;
+}
+
+w4a16_status w4a16_unpack(const void *qweight, const void *scales, const void *zeros, int64_t N,
+                          int64_t K, int32_t group, uint8_t *codes, uint16_t *scales_out,
+                          uint8_t *zeros_out, void *stream) {
+    if (!qweight || !scales || !zeros || !codes || !scales_out || !zeros_out ||
+        !shape_ok(N, K, group))
+        return W4A16_ERR_INVALID_ARG;
+    if (!aligned16(qweight) || !aligned16(codes)) return W4A16_ERR_INVALID_ARG;
+    w4a16_status st = check_device();
+    if (st != W4A16_OK) return st;
+    hipError_t e = launch_unpack(qweight, scales, zeros, (int)N, (int)K, group, codes, scales_out,
+                                 zeros_out, reinterpret_cast<hipStream_t>(stream));
+    return e == hipSuccess ? W4A16_OK : W4A16_ERR_HIP;
+}
+
+w4a16_status w4a16_gemv(const void *x, int32_t dtype, const void *qweight, const void *scales,
+                        const void *zeros, void *y, int64_t M, int64_t N, int64_t K, int32_t group,
+                        void *workspace, size_t workspace_bytes, void *stream) {
+    (void)workspace;
+    (void)workspace_bytes;
+    if (M > 8) return W4A16_ERR_INVALID_ARG;
+    w4a16_status st = check_linear(x, dtype, qweight, scales, zeros, y, M, N, K, group, nullptr, 0, 0);
+    if (st != W4A16_OK) return st;
+    st = check_device();
+    if (st != W4A16_OK) return st;
+    if (!gemv_fits(M, K, dtype)) return W4A16_ERR_INVALID_ARG;
+    GemvPlan plan = gemv_plan(M, N, K, group);
+    hipError_t e = launch_gemv(x, dtype == W4A16_BF16, qweight, scales, zeros, y, (int)M, (int)N,
+                               (int)K, group, plan, reinterpret_cast<hipStream_t>(stream));
+    return e == hipSuccess ? W4A16_OK : W4A16_ERR_HIP;
+}
+
+w4a16_status w4a16_gemm(const void *x, int32_t dtype, const void *qweight, const void *scales,
+                        const void *zeros, void *y, int64_t M, int64_t N, int64_t K, int32_t group,
+                        void *workspace, size_t workspace_bytes, void *stream) {
+    const size_t need = (M >= 1 && M <= (1LL << 24) && shape_ok(N, K, group))
+                            ? gemm_need(M, N, K, group) : 0;
+    w4a16_status st = check_linear(x, dtype, qweight, scales, zeros, y, M, N, K, group, workspace,
+                                   workspace_bytes, need);
+    if (st != W4A16_OK) return st;
+    st = check_device();
+    if (st != W4A16_OK) return st;
+    GemmPlan plan = gemm_plan(M, N, K, group);
+    hipError_t e = launch_gemm(x, dtype == W4A16_BF16, qweight, scales, zeros, y, (int)M, (int)N,
+                               (int)K, group, plan, workspace, reinterpret_cast<hipStream_t>(stream));
+    return e == hipSuccess ? W4A16_OK : W4A16_ERR_HIP;
+}
+
+w4a16_status w4a16_linear(const void *x, int32_t dtype, const void *qweight, const void *scales,
+                          const void *zeros, void *y, int64_t M, int64_t N, int64_t K, int32_t group,
+                          void *workspace, size_t workspace_bytes, void *stream) {
+    if (M >= 1 && M <= gemv_max_m() && shape_ok(N, K, group) &&
+        (dtype == W4A16_F16 || dtype == W4A16_BF16) && gemv_fits(M, K, dtype))
+        return w4a16_gemv(x, dtype, qweight, scales, zeros, y, M, N, K, group, workspace,
+                          workspace_bytes, stream);
+    return w4a16_gemm(x, dtype, qweight, scales, zeros, y, M, N, K, group, workspace,
+                      workspace_bytes, stream);
+}
+
+}  // extern "C"

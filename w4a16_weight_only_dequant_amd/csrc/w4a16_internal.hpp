@@ -1,0 +1,102 @@
+// Internal declarations shared by the kernels and the C ABI of the gfx950
+// W4A16 library. Not installed; the public interface is include/w4a16.h.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+#include <stddef.h>
+
+namespace w4a16 {
+
+// Packed device layout: rows in blocks of 64, K in chunks of 32 weights; one
+// 16-byte record (4 dwords of 8 nibbles) per (row, chunk).
+constexpr int kRowBlock = 64;
+constexpr int kChunk = 32;
+
+// Workspace layout: a fixed region of arrival counters first, then fp32
+// partial sums. The counter region has the same size for every shape, so a
+// workspace reused across shapes never finds old partial sums where a later
+// call's counters live.
+constexpr size_t kCounterRegion = 64 * 1024;
+constexpr int kMaxCounters = (int)(kCounterRegion / sizeof(unsigned));
+
+typedef _Float16 half2_t __attribute__((ext_vector_type(2)));
+typedef __bf16 bf162_t __attribute__((ext_vector_type(2)));
+
+__host__ __device__ inline int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
+__host__ __device__ inline size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
+
+// Host-side plan for one GEMV launch: one workgroup per 16 output rows, each
+// with `waves` waves that split K (no cross-workgroup reduction).
+struct GemvPlan {
+    int row_blocks;   // workgroups = ceil(N / 16)
+    int waves;        // waves per workgroup (1..16)
+};
+
+GemvPlan gemv_plan(int64_t M, int64_t N, int64_t K, int32_t group);
+// Dynamic LDS of one GEMV workgroup (staged activations, bf16 chunk sums).
+size_t gemv_lds_bytes(int64_t M, int64_t K, bool bf16);
+// Static LDS of one GEMV workgroup (cross-wave reduction buffer).
+constexpr size_t kGemvStaticLds = 16 * 8 * 16 * sizeof(float);
+
+// Plan for the matrix-core kernels.
+struct GemmPlan {
+    int kind;               // 0 = skinny (M <= 64, weights streamed to registers), 1 = tiled
+    int k_splits;
+    int m_tiles;
+    int n_tiles;
+    size_t counter_bytes;
+    size_t partial_bytes;
+};
+
+GemmPlan gemm_plan(int64_t M, int64_t N, int64_t K, int32_t group);
+
+hipError_t launch_pack(const float *w, int N, int K, int group, void *qweight,
+                       void *scales, void *zeros, hipStream_t stream);
+hipError_t launch_unpack(const void *qweight, const void *scales, const void *zeros,
+                         int N, int K, int group, uint8_t *codes, uint16_t *scales_out,
+                         uint8_t *zeros_out, hipStream_t stream);
+hipError_t launch_gemv(const void *x, bool bf16, const void *qweight, const void *scales,
+                       const void *zeros, void *y, int M, int N, int K, int group,
+                       const GemvPlan &plan, hipStream_t stream);
+hipError_t launch_gemm(const void *x, bool bf16, const void *qweight, const void *scales,
+                       const void *zeros, void *y, int M, int N, int K, int group,
+                       const GemmPlan &plan, void *workspace, hipStream_t stream);
+
+// Deterministic split-K hand-off used by the GEMV and the skinny GEMM: every
+// workgroup stores its fp32 partial tile with agent-scope stores, then
+// announces itself on a per-tile counter; the last arrival sums the partials
+// in slice order and resets the counter to zero for the next call.
+__device__ inline void store_partial(float *p, float v) {
+    __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ inline float load_partial(const float *p) {
+    return __hip_atomic_load(const_cast<float *>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+// Returns true in every lane of the calling wave when this wave's workgroup is
+// the last of `total` arrivals on *counter. Must be called by one whole wave
+// after it has issued all of its partial stores.
+__device__ inline bool arrive_last(unsigned *counter, unsigned total) {
+    unsigned old = 0;
+    if ((threadIdx.x & 63) == 0)
+        old = __hip_atomic_fetch_add(counter, 1u, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
+    old = __shfl(old, 0, 64);
+    bool last = (old == total - 1);
+    if (last) {
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+        if ((threadIdx.x & 63) == 0)
+            __hip_atomic_store(counter, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+    return last;
+}
+
+__device__ inline uint16_t f32_to_f16_bits(float v) {
+    _Float16 h = (_Float16)v;
+    return __builtin_bit_cast(uint16_t, h);
+}
+__device__ inline uint16_t f32_to_bf16_bits(float v) {
+    __bf16 h = (__bf16)v;
+    return __builtin_bit_cast(uint16_t, h);
+}
+
+}  // namespace w4a16
