@@ -164,8 +164,8 @@ def bits_per_weight(group: int, scale_bits: int = 16, zero_bits: int = 4, code_b
 
 
 def packed_bytes(N: int, K: int, group: int):
-    """(qweight, scales, zeros) byte counts: one nibble per weight, one fp16 scale and
-    one 4-bit zero per (group, output column)."""
+    """(qweight, scales, zeros) algorithmic byte counts: one nibble per weight, one fp16
+    scale and one 4-bit zero per (group, output column)."""
     G = K // group
     return (N * K) // 2, 2 * G * N, (G * N) // 2
 
@@ -234,13 +234,23 @@ def dequantize(codes, scale_bits, zeros, group: int) -> np.ndarray:
 # definition). The layouts themselves are this library's own; the device
 # layout is written out here independently from its specification:
 #
-#   qweight: rows in blocks of 64 (the last block may hold fewer, rows_b =
-#   min(64, N - 64 b)), K in chunks of 32. Record (n, c) is 16 bytes at byte
-#   offset 64*b*(K/2) + c*rows_b*16 + r*16 (b = n // 64, r = n % 64,
-#   c = k // 32). Dword j = (k % 32) // 8 of the record holds k = 32c + 8j + i,
-#   i = 0..7, in nibble p = i // 2 + 4 * (i % 2) (even k in the low half-word,
-#   odd k in the high half-word). Dwords are little-endian.
-#   scales: fp16 bits [G][N]. zeros: u32 [G][N/8], nibble n % 8 of word n // 8.
+#   qweight: rows in blocks of 16 (the last block may hold fewer rows,
+#   rows_b = min(16, N - 16 b)); K in chunks of 32 weights (C = K/32 chunks)
+#   and columns of 4 chunks (the last column may hold fewer, nc = min(4,
+#   C - 4t)). A chunk of one row is 4 dwords; dword d = (k % 32) // 8 holds
+#   k = 32c + 8d + i, i = 0..7, in nibble p = i // 2 + 4 * (i % 2) (even k in
+#   the low half-word, odd k in the high half-word). Byte offset of dword d of
+#   chunk c = 4t + j of row n = 16b + r:
+#       16*b*(K/2) + t*rows_b*64 + d*(rows_b*nc*4) + r*(nc*4) + j*4.
+#   So for a full column the 16 rows x 4 dword positions form one contiguous
+#   KiB in which the 16 bytes at d*256 + r*16 are dword d of the column's four
+#   chunks of row r. Dwords are little-endian.
+#   Metadata per column (GPC = 128/group groups per column, T = ceil(C/4)
+#   columns; a short last column keeps its unused group slots, filled with 0):
+#   scales: fp16 bits [T][N][GPC] (group g = GPC*t + e is element e).
+#   zeros: u32 words [T][N*GPC/8]; the GPC zero-points of row n in column t are
+#   nibbles GPC*(n % (8/GPC)) + e of word n // (8/GPC).
+#   At group 128 (GPC = 1) these are the plain [G][N] and [G][N/8] layouts.
 # ---------------------------------------------------------------------------
 
 
@@ -248,15 +258,19 @@ def _device_nibble_index(N: int, K: int) -> np.ndarray:
     """Nibble position in the packed qweight stream of every (n, k), shape [N][K]."""
     n = np.arange(N, dtype=np.int64)[:, None]
     k = np.arange(K, dtype=np.int64)[None, :]
-    b = n // 64
-    r = n % 64
-    rows_b = np.minimum(64, N - 64 * b)
+    C = K // 32
+    b = n // 16
+    r = n % 16
+    rows_b = np.minimum(16, N - 16 * b)
     c = k // 32
-    j = (k % 32) // 8
+    t = c // 4
+    j = c % 4
+    nc = np.minimum(4, C - 4 * t)
+    d = (k % 32) // 8
     i = k % 8
     p = i // 2 + 4 * (i % 2)
-    byte_off = 64 * b * (K // 2) + c * rows_b * 16 + r * 16
-    dword = byte_off // 4 + j
+    byte_off = 16 * b * (K // 2) + t * rows_b * 64 + d * (rows_b * nc * 4) + r * (nc * 4) + j * 4
+    dword = byte_off // 4
     return dword * 8 + p
 
 
@@ -282,7 +296,7 @@ def unpack_device(qweight, N: int, K: int) -> np.ndarray:
 
 
 def pack_zeros(zeros) -> np.ndarray:
-    """zeros u8 [G][N] -> u32 [G][N/8], nibble n % 8 of word n // 8."""
+    """zeros u8 [G][N] -> u32 [G][N/8], nibble n % 8 of word n // 8 (canonical form)."""
     z = np.asarray(zeros, dtype=np.uint32)
     G, N = z.shape
     zz = z.reshape(G, N // 8, 8)
@@ -300,10 +314,53 @@ def unpack_zeros(words, G: int, N: int) -> np.ndarray:
     return out.reshape(G, N)
 
 
+def _padded_groups(G: int, group: int) -> int:
+    """Group slots of the per-column metadata layout: T columns of 128/group groups."""
+    gpc = 128 // group
+    return -(-G // gpc) * gpc
+
+
+def pack_scales_device(scale_bits, group: int) -> np.ndarray:
+    """scale bits [G][N] -> device order [T][N][GPC] (uint16), unused slots 0."""
+    s = np.asarray(scale_bits, dtype=np.uint16)
+    G, N = s.shape
+    gpc = 128 // group
+    Gp = _padded_groups(G, group)
+    full = np.zeros((Gp, N), dtype=np.uint16)
+    full[:G] = s
+    return np.ascontiguousarray(full.reshape(Gp // gpc, gpc, N).transpose(0, 2, 1))
+
+
+def pack_zeros_device(zeros, group: int) -> np.ndarray:
+    """zero-points u8 [G][N] -> device words [T][N*GPC/8] (uint32), unused slots 0.
+
+    The GPC nibbles of (column t, row n) are consecutive: nibble index
+    n*GPC + e within the column, eight nibbles per little-endian word."""
+    z = np.asarray(zeros, dtype=np.uint32)
+    G, N = z.shape
+    gpc = 128 // group
+    Gp = _padded_groups(G, group)
+    full = np.zeros((Gp, N), dtype=np.uint32)
+    full[:G] = z
+    nib = full.reshape(Gp // gpc, gpc, N).transpose(0, 2, 1).reshape(Gp // gpc, N * gpc)
+    nib = nib.reshape(Gp // gpc, N * gpc // 8, 8)
+    word = np.zeros(nib.shape[:2], dtype=np.uint32)
+    for t in range(8):
+        word |= nib[:, :, t] << np.uint32(4 * t)
+    return word
+
+
+def device_meta_bytes(N: int, K: int, group: int):
+    """(scales, zeros) byte counts of the per-column metadata layout."""
+    Gp = _padded_groups(K // group, group)
+    return 2 * Gp * N, Gp * N // 2
+
+
 def quantize_and_pack(w, group: int):
-    """Full offline step: (qweight bytes, scale bits [G][N], zero words [G][N/8], codes, zeros)."""
+    """Full offline step: (qweight bytes, device scales, device zero words, codes, scale bits, zeros)."""
     codes, s_bits, zeros = quantize_groupwise(w, group)
-    return pack_device(codes), s_bits, pack_zeros(zeros), codes, zeros
+    return (pack_device(codes), pack_scales_device(s_bits, group), pack_zeros_device(zeros, group),
+            codes, s_bits, zeros)
 
 
 # ---------------------------------------------------------------------------

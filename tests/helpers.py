@@ -20,7 +20,8 @@ def oracle_pack(w: np.ndarray, group: int):
         "s_bits": s_bits,
         "zeros": zeros,
         "qweight": ref.pack_device(codes),
-        "zero_words": ref.pack_zeros(zeros),
+        "scales_dev": ref.pack_scales_device(s_bits, group).ravel(),
+        "zeros_dev": ref.pack_zeros_device(zeros, group).ravel(),
     }
 
 

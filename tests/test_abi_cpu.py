@@ -40,10 +40,17 @@ def test_status_strings_and_version(w4):
     assert lib.w4a16_status_string(99) == b"unknown status"
 
 
-@pytest.mark.parametrize("N,K,group", [(4096, 4096, 128), (8192, 28672, 32), (5120, 13824, 128), (72, 96, 32)])
+@pytest.mark.parametrize("N,K,group", [(4096, 4096, 128), (8192, 28672, 32), (5120, 13824, 128), (72, 96, 32),
+                                       (72, 192, 64), (72, 160, 32)])
 def test_packed_bytes_closed_form(w4, N, K, group):
     G = K // group
-    assert w4.packed_bytes(N, K, group) == (N * K // 2, 2 * G * N, G * N // 2)
+    q, s, z = w4.packed_bytes(N, K, group)
+    assert q == N * K // 2
+    # metadata per 128-weight column: 128/group slots; exact 2GN / GN/2 when K % 128 == 0
+    slots = -(-K // 128) * (128 // group)
+    assert (s, z) == (2 * slots * N, slots * N // 2)
+    if K % 128 == 0:
+        assert (s, z) == (2 * G * N, G * N // 2)
 
 
 @pytest.mark.parametrize("N,K,group", [(100, 128, 128), (4, 128, 128), (64, 100, 32), (64, 128, 16),

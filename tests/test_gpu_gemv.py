@@ -17,10 +17,11 @@ def _run(fn, x_bits, dtype, pw):
     return y
 
 
-def gemv_accepts(M, K, dtype):
-    """The GEMV stages the activations in one workgroup's LDS (160 KiB on gfx950)."""
-    lds = M * K * 2 + (M * (K // 32) * 4 if dtype == "bf16" else 0) + 16 * 8 * 16 * 4
-    return M <= 8 and lds <= 160 * 1024
+def gemv_accepts(M, K, dtype, group=32):
+    """The GEMV stages activations and group metadata in one workgroup's LDS
+    (160 KiB on gfx950); conservative bound incl. the per-wave rounding of slices."""
+    lds = M * K * 2 * (1.0 + (64 / 256 if dtype == "bf16" else 0.0)) + (K // group) * 40 + 16 * 1024
+    return M <= 8 and lds <= 150 * 1024
 
 
 SMALL = [(8, 32, 32), (72, 64, 32), (200, 96, 32), (136, 256, 64), (64, 384, 128), (328, 640, 128),
@@ -31,6 +32,8 @@ SMALL = [(8, 32, 32), (72, 64, 32), (200, 96, 32), (136, 256, 64), (64, 384, 128
 @pytest.mark.parametrize("dtype", ["f16", "bf16"])
 @pytest.mark.parametrize("M", [1, 2, 3, 8])
 def test_gemv_small_shapes(N, K, group, dtype, M):
+    if not gemv_accepts(M, K, dtype, group):
+        pytest.skip("activations of this call exceed the GEMV's LDS stage")
     w, o, pw = H.prepared(("small", N, K, group), lambda: wl.random_weights(N + K, N, K), group)
     x = wl.random_activations(N * 31 + K + M, M, K, dtype)
     y = _run(H.lib().gemv, x, dtype, pw)
@@ -92,7 +95,7 @@ def test_gemv_full_size_configs(cfg, mat):
     group = wlc.group
     w, o, pw = H.prepared((cfg, mat), lambda: wl.weights(cfg, mat), group)
     for M in wlc.ms:
-        if not gemv_accepts(M, wlc.matrices[mat].K, wlc.dtype):
+        if not gemv_accepts(M, wlc.matrices[mat].K, wlc.dtype, group):
             continue
         x = wl.activations(cfg, mat, M)
         y = _run(H.lib().gemv, x, wlc.dtype, pw)

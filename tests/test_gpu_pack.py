@@ -17,9 +17,9 @@ def _check_packed(o, pw):
     qw = pw.qweight.cpu().numpy()
     assert np.array_equal(qw, o["qweight"]), f"qweight differs at {np.count_nonzero(qw != o['qweight'])} bytes"
     s = pw.scales.cpu().view(torch.int16).numpy().view(np.uint16)
-    assert np.array_equal(s, o["s_bits"]), "scales differ"
+    assert np.array_equal(s, o["scales_dev"]), "scales differ"
     z = pw.zeros.cpu().numpy().view(np.uint32)
-    assert np.array_equal(z, o["zero_words"]), "zeros differ"
+    assert np.array_equal(z, o["zeros_dev"]), "zeros differ"
     codes, s_out, z_out = H.lib().unpack(pw)
     torch.cuda.synchronize()
     assert np.array_equal(codes.cpu().numpy(), o["codes"])

@@ -327,3 +327,27 @@ def test_zero_packing_by_hand():
     words = ref.pack_zeros(z)
     assert words.tolist() == [[0x87654321, 0x9000000F]]
     assert np.array_equal(ref.unpack_zeros(words, 1, 16), z)
+
+
+def test_device_metadata_layout_by_hand():
+    # group 32: 4 groups per column; N = 8 rows, K = 160 -> G = 5 groups, 2 columns
+    G, N = 5, 8
+    s_bits = (np.arange(G * N, dtype=np.uint16).reshape(G, N) + 1)
+    z = (np.arange(G * N, dtype=np.uint8).reshape(G, N) % 16)
+    ds = ref.pack_scales_device(s_bits, 32)
+    assert ds.shape == (2, 8, 4)
+    assert ds[0, 3].tolist() == [s_bits[0, 3], s_bits[1, 3], s_bits[2, 3], s_bits[3, 3]]
+    assert ds[1, 7].tolist() == [s_bits[4, 7], 0, 0, 0]
+    dz = ref.pack_zeros_device(z, 32)
+    assert dz.shape == (2, 4)
+    # column 0, rows 2 and 3 share word 1: nibbles (row 2: groups 0..3, row 3: groups 0..3)
+    want = 0
+    for e, (row, g) in enumerate([(2, 0), (2, 1), (2, 2), (2, 3), (3, 0), (3, 1), (3, 2), (3, 3)]):
+        want |= int(z[g, row]) << (4 * e)
+    assert int(dz[0, 1]) == want
+    # group 128 keeps the canonical [G][N] / [G][N/8] forms
+    z128 = (np.arange(3 * 16, dtype=np.uint8).reshape(3, 16) % 16)
+    assert np.array_equal(ref.pack_zeros_device(z128, 128), ref.pack_zeros(z128))
+    s128 = np.arange(3 * 16, dtype=np.uint16).reshape(3, 16)
+    assert np.array_equal(ref.pack_scales_device(s128, 128).reshape(3, 16), s128)
+    assert ref.device_meta_bytes(8, 160, 32) == (2 * 8 * 8, 8 * 8 // 2)

@@ -114,8 +114,8 @@ class PackedWeight:
 
     def __init__(self, qweight, scales, zeros, N, K, group):
         self.qweight = qweight    # uint8 [N*K/2], device layout
-        self.scales = scales      # float16 [G][N]
-        self.zeros = zeros        # int32 [G][N/8] (4-bit zeros, 8 per word)
+        self.scales = scales      # float16, per 128-weight column: [T][N][128/group]
+        self.zeros = zeros        # int32, per column: [T][N*128/group/8] (4-bit zero-points)
         self.N, self.K, self.group = N, K, group
 
     def nbytes(self) -> int:
@@ -129,12 +129,10 @@ def pack(w: torch.Tensor, group: int, stream=None) -> PackedWeight:
     w = w.contiguous()
     N, K = w.shape
     qb, sb, zb = packed_bytes(N, K, group)
-    G = K // group
     dev = w.device
     qweight = torch.empty(qb, dtype=torch.uint8, device=dev)
-    scales = torch.empty((G, N), dtype=torch.float16, device=dev)
-    zeros = torch.empty((G, N // 8), dtype=torch.int32, device=dev)
-    assert scales.numel() * 2 == sb and zeros.numel() * 4 == zb
+    scales = torch.empty(sb // 2, dtype=torch.float16, device=dev)
+    zeros = torch.empty(zb // 4, dtype=torch.int32, device=dev)
     _check("w4a16_pack", _lib.w4a16_pack(w.data_ptr(), N, K, group, qweight.data_ptr(), scales.data_ptr(),
                                          zeros.data_ptr(), _stream_ptr(stream)))
     return PackedWeight(qweight, scales, zeros, N, K, group)

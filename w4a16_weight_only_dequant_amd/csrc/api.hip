@@ -47,6 +47,17 @@ bool shape_ok(int64_t N, int64_t K, int32_t group) {
     return true;
 }
 
+// Byte sizes of the packed buffers: codes, then scales and zero-points per
+// 128-weight column (128/group slots per column; a short last column keeps its
+// unused slots).
+void meta_bytes(int64_t N, int64_t K, int32_t group, size_t *q, size_t *sb, size_t *zb) {
+    const int64_t gpc = 128 / group;
+    const int64_t T = (K / 32 + 3) / 4;
+    *q = (size_t)(N * K / 2);
+    *sb = (size_t)(2 * T * N * gpc);
+    *zb = (size_t)(T * N * gpc / 2);
+}
+
 struct Range {
     uintptr_t lo, hi;
 };
@@ -72,12 +83,11 @@ w4a16_status check_linear(const void *x, int32_t dtype, const void *qweight, con
     if (!aligned16(x) || !aligned16(qweight) || !aligned16(scales) || !aligned16(zeros) ||
         !aligned16(y))
         return W4A16_ERR_INVALID_ARG;
-    const int64_t G = K / group;
+    size_t qb, sb, zb;
+    meta_bytes(N, K, group, &qb, &sb, &zb);
     const Range ry = range_of(y, (size_t)(M * N * 2));
-    if (overlap(ry, range_of(x, (size_t)(M * K * 2))) ||
-        overlap(ry, range_of(qweight, (size_t)(N * K / 2))) ||
-        overlap(ry, range_of(scales, (size_t)(G * N * 2))) ||
-        overlap(ry, range_of(zeros, (size_t)(G * N / 2))))
+    if (overlap(ry, range_of(x, (size_t)(M * K * 2))) || overlap(ry, range_of(qweight, qb)) ||
+        overlap(ry, range_of(scales, sb)) || overlap(ry, range_of(zeros, zb)))
         return W4A16_ERR_INVALID_ARG;
     if (need > 0) {
         if (!workspace || workspace_bytes < need) return W4A16_ERR_WORKSPACE;
@@ -103,9 +113,10 @@ size_t max_lds_per_block() {
 
 // The GEMV stages all activations of the call in LDS; it takes M <= 8 and
 // M * K small enough for one workgroup's LDS.
-bool gemv_fits(int64_t M, int64_t K, int32_t dtype) {
+bool gemv_fits(int64_t M, int64_t N, int64_t K, int32_t group, int32_t dtype) {
     if (M < 1 || M > 8) return false;
-    return gemv_lds_bytes(M, K, dtype == W4A16_BF16) + kGemvStaticLds <= max_lds_per_block();
+    const GemvPlan p = gemv_plan(M, N, K, group);
+    return gemv_lds_bytes(M, K, dtype == W4A16_BF16, p.waves, group) + kGemvStaticLds <= max_lds_per_block();
 }
 
 size_t gemm_need(int64_t M, int64_t N, int64_t K, int32_t group) {
@@ -149,10 +160,11 @@ w4a16_status w4a16_device_supported(int device) {
 w4a16_status w4a16_packed_bytes(int64_t N, int64_t K, int32_t group, size_t *qweight_bytes,
                                 size_t *scales_bytes, size_t *zeros_bytes) {
     if (!shape_ok(N, K, group)) return W4A16_ERR_INVALID_ARG;
-    const int64_t G = K / group;
-    if (qweight_bytes) *qweight_bytes = (size_t)(N * K / 2);
-    if (scales_bytes) *scales_bytes = (size_t)(2 * G * N);
-    if (zeros_bytes) *zeros_bytes = (size_t)(G * N / 2);
+    size_t q, sb, zb;
+    meta_bytes(N, K, group, &q, &sb, &zb);
+    if (qweight_bytes) *qweight_bytes = q;
+    if (scales_bytes) *scales_bytes = sb;
+    if (zeros_bytes) *zeros_bytes = zb;
     return W4A16_OK;
 }
 
@@ -167,7 +179,7 @@ w4a16_status w4a16_pack(const float *w, int64_t N, int64_t K, int32_t group, voi
     if (!w || !qweight || !scales || !zeros || !shape_ok(N, K, group)) return W4A16_ERR_INVALID_ARG;
     if (!aligned16(w) || !aligned16(qweight) || !aligned16(scales) || !aligned16(zeros))
         return W4A16_ERR_INVALID_ARG;
-    if ((int64_t)(K / group) * N > (1LL << 31)) return W4A16_ERR_INVALID_ARG;
+    if (((K / 32 + 3) / 4) * N > (1LL << 31)) return W4A16_ERR_INVALID_ARG;
     w4a16_status st = check_device();
     if (st != W4A16_OK) return st;
     hipError_t e = launch_pack(w, (int)N, (int)K, group, qweight, scales, zeros,
@@ -199,7 +211,7 @@ w4a16_status w4a16_gemv(const void *x, int32_t dtype, const void *qweight, const
     if (st != W4A16_OK) return st;
     st = check_device();
     if (st != W4A16_OK) return st;
-    if (!gemv_fits(M, K, dtype)) return W4A16_ERR_INVALID_ARG;
+    if (!gemv_fits(M, N, K, group, dtype)) return W4A16_ERR_INVALID_ARG;
     GemvPlan plan = gemv_plan(M, N, K, group);
     hipError_t e = launch_gemv(x, dtype == W4A16_BF16, qweight, scales, zeros, y, (int)M, (int)N,
                                (int)K, group, plan, reinterpret_cast<hipStream_t>(stream));
@@ -226,7 +238,7 @@ w4a16_status w4a16_linear(const void *x, int32_t dtype, const void *qweight, con
                           const void *zeros, void *y, int64_t M, int64_t N, int64_t K, int32_t group,
                           void *workspace, size_t workspace_bytes, void *stream) {
     if (M >= 1 && M <= gemv_max_m() && shape_ok(N, K, group) &&
-        (dtype == W4A16_F16 || dtype == W4A16_BF16) && gemv_fits(M, K, dtype))
+        (dtype == W4A16_F16 || dtype == W4A16_BF16) && gemv_fits(M, N, K, group, dtype))
         return w4a16_gemv(x, dtype, qweight, scales, zeros, y, M, N, K, group, workspace,
                           workspace_bytes, stream);
     return w4a16_gemm(x, dtype, qweight, scales, zeros, y, M, N, K, group, workspace,

@@ -1,0 +1,90 @@
+// Device helpers shared by the small-M kernels (the dot-product GEMV and the
+// matrix-core skinny GEMM): unpacking 4-bit codes and the per-wave K-slice.
+//
+// Both kernels give a workgroup one block of 16 output rows and all of K; its
+// waves split K into contiguous slices of 128-weight columns. A wave stages
+// the activations of its own slice in its own LDS region (no workgroup
+// barrier: a wave reads only what it wrote), issuing those loads before its
+// first weight loads.
+#pragma once
+
+#include "w4a16_internal.hpp"
+
+namespace w4a16 {
+
+constexpr int kColumn = kChunk * kColChunks;   // 128 weights of K per column
+
+// A 32-bit constant materialised in a VGPR. VOP3 instructions (v_and_or_b32)
+// cannot take two literal operands on gfx9, so the masks and magic numbers of
+// the unpack live in registers, which lets (d & mask) | magic issue as one
+// v_and_or_b32 instead of a v_and + v_or pair.
+__device__ inline uint32_t vconst(uint32_t c) {
+    uint32_t r;
+    asm("v_mov_b32 %0, %1" : "=v"(r) : "i"(c));
+    return r;
+}
+
+__device__ inline uint32_t and_or(uint32_t a, uint32_t mask, uint32_t bits) { return (a & mask) | bits; }
+
+struct UnpackConsts {
+    uint32_t lo_mask, hi_mask, f16_magic, bf16_magic;
+};
+
+__device__ inline UnpackConsts unpack_consts() {
+    return UnpackConsts{vconst(0x000F000Fu), vconst(0x00F000F0u), vconst(0x64006400u), vconst(0x43004300u)};
+}
+
+// One dword (8 codes of one k-slice, even k in the low half-word) -> four
+// fp16 pairs (k0,k1) (k2,k3) (k4,k5) (k6,k7) holding q - z exactly.
+// (d & 0x000F000F) | 0x64006400 is (1024+q0, 1024+q1); (d & 0x00F000F0) |
+// 0x64006400 is (1024+16 q2, 1024+16 q3); subtracting (1024+z), or scaling by
+// 1/16 and subtracting (64+z), leaves small integers, so every step is exact.
+__device__ inline void unpack_f16(uint32_t d, uint32_t z, const UnpackConsts &uc, uint32_t (&t)[4]) {
+    const half2_t a = __builtin_bit_cast(half2_t, (0xE400u | z) * 0x00010001u);         // -(1024+z)
+    const half2_t b = __builtin_bit_cast(half2_t, (0xD400u + 16u * z) * 0x00010001u);   // -(64+z)
+    const half2_t sixteenth = {(_Float16)0.0625f, (_Float16)0.0625f};
+    const uint32_t d8 = d >> 8;
+    const half2_t h0 = __builtin_bit_cast(half2_t, and_or(d, uc.lo_mask, uc.f16_magic));
+    const half2_t h1 = __builtin_bit_cast(half2_t, and_or(d, uc.hi_mask, uc.f16_magic));
+    const half2_t h2 = __builtin_bit_cast(half2_t, and_or(d8, uc.lo_mask, uc.f16_magic));
+    const half2_t h3 = __builtin_bit_cast(half2_t, and_or(d8, uc.hi_mask, uc.f16_magic));
+    t[0] = __builtin_bit_cast(uint32_t, h0 + a);
+    t[1] = __builtin_bit_cast(uint32_t, __builtin_elementwise_fma(h1, sixteenth, b));
+    t[2] = __builtin_bit_cast(uint32_t, h2 + a);
+    t[3] = __builtin_bit_cast(uint32_t, __builtin_elementwise_fma(h3, sixteenth, b));
+}
+
+// One dword -> four bf16 pairs holding 128 + q (exact: 7 mantissa bits).
+__device__ inline void unpack_bf16_magic(uint32_t d, const UnpackConsts &uc, uint32_t (&t)[4]) {
+    t[0] = and_or(d, uc.lo_mask, uc.bf16_magic);
+    t[1] = and_or(d >> 4, uc.lo_mask, uc.bf16_magic);
+    t[2] = and_or(d >> 8, uc.lo_mask, uc.bf16_magic);
+    t[3] = and_or(d >> 12, uc.lo_mask, uc.bf16_magic);
+}
+
+// The K-slice of one wave, in columns [t_begin, t_end); t_full ends the run of
+// full (4-chunk) columns; the last column of K may be partial.
+struct Slice {
+    int C;          // chunks along K
+    int T;          // columns along K
+    int t_begin, t_end, t_full;
+    int c_lo, c_hi;   // chunk range of the slice
+    int g_lo, g_hi;   // group range of the slice
+};
+
+template <int GROUP>
+__device__ inline Slice wave_slice(int K, int wave, int waves) {
+    Slice sl;
+    sl.C = K / kChunk;
+    sl.T = (sl.C + kColChunks - 1) / kColChunks;
+    sl.t_begin = (int)(((int64_t)wave * sl.T) / waves);
+    sl.t_end = (int)(((int64_t)(wave + 1) * sl.T) / waves);
+    sl.t_full = min(sl.t_end, sl.C / kColChunks);
+    sl.c_lo = sl.t_begin * kColChunks;
+    sl.c_hi = min(sl.t_end * kColChunks, sl.C);
+    sl.g_lo = sl.c_lo * kChunk / GROUP;
+    sl.g_hi = (sl.c_hi * kChunk + GROUP - 1) / GROUP;
+    return sl;
+}
+
+}  // namespace w4a16

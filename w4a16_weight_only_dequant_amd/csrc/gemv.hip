@@ -1,69 +1,42 @@
 // Decode GEMV for the W4A16 linear layer, y[m][n] = sum_k x[m][k] * w_hat[n][k],
-// for small M (1..8).
+// for small M (1..8), with fp16/bf16 dot products and fp32 accumulation.
 //
 // At small batch each weight is read once per token and used for only M
-// multiply-adds, so the kernel is bound by the weight stream from HBM
+// multiply-adds, so the weight stream from HBM is the bottleneck
 // ("Weight-Only Quantisation", first two FAQ answers; "Weight-Only
 // Quantization Explained", "Where it stops being the right answer"). The
 // weights stay packed until they reach registers ("Quantization Is Not a Zip
 // File", section 8) and are rebuilt as 16-bit values just before the multiply
 // ("Weight-Only Quantisation", definition).
 //
-// Mapping (gfx950, wave64). A workgroup owns 16 output rows and all of K; its
-// W waves split K into contiguous slices of 128-weight columns. Inside a wave,
-// lane (r, s) = (lane / 4, lane % 4) handles row r and chunk s of every
-// column, so one wave load is four 256-byte runs of 16-byte records (16 rows x
-// 4 chunks). Because a workgroup covers all of K, no partial sum ever leaves
-// the workgroup: the four chunk lanes of a row meet through DPP (quad
-// shuffles), the waves through LDS, always in the same order, so results are
-// deterministic and no cross-workgroup synchronisation (or L2 writeback) is
-// needed. Narrow N still fills the chip because the waves per workgroup grow
-// as N shrinks. The activations of the workgroup are staged once in LDS; for
-// bf16 the stage also stores each 32-weight chunk's activation sum.
+// Mapping (gfx950, wave64). A workgroup owns one block of 16 output rows and
+// all of K; its waves split K into slices of 128-weight columns. Lane
+// l = 16 s + r holds, for every column, dword s of the column's four chunks of
+// row r (one 16-byte load per lane; one contiguous KiB per wave), together with
+// row r's scales and zero-points of that column (one small load each, from the
+// per-column metadata layout). The activations of the slice are staged in the
+// wave's own LDS region. The four lanes of a row meet through cross-lane shuffles at
+// the end, the waves through LDS, always in the same order, so results are
+// deterministic and no partial sum leaves the workgroup.
 //
-// Unpack, fp16 activations: for a dword d holding k0..k7 (even k in the low
-// half-word), (d & 0x000F000F) | 0x64006400 is the fp16 pair (1024+q0, 1024+q1)
-// and (d & 0x00F000F0) | 0x64006400 is (1024+16 q2, 1024+16 q3); subtracting
-// (1024+z), or scaling by 1/16 and subtracting (64+z), gives q - z exactly,
-// and v_dot2_f32_f16 multiplies by the fp16 activation pair with fp32
-// accumulation. The group's scale multiplies the fp32 chunk sum.
-// bf16 activations: ((d >> 4i) & 0x000F000F) | 0x43004300 is the bf16 pair
-// (128+q, 128+q'); the chunk sum of x*(128+q) minus (128+z) times the chunk
-// sum of x is the chunk sum of x*(q-z) (both sums in fp32).
+// fp16 activations: each dword unpacks to four exact (q - z) fp16 pairs and
+// v_dot2_f32_f16 multiplies them with the activation pairs, accumulating in
+// fp32; the group scale multiplies the fp32 group sum. bf16 activations: the
+// dword unpacks to bf16 pairs (128 + q); the sum of x*(128+q) over the
+// dword's 8 weights minus (128 + z) times the sum of those 8 activations is
+// the sum of x*(q - z), both in fp32.
 #include <stdlib.h>
 
-#include "w4a16_internal.hpp"
+#include "decode_common.hpp"
 
 namespace w4a16 {
 namespace {
 
-constexpr int kRowsPerWave = 16;
-constexpr int kChunkLanes = 4;
 constexpr int kMaxWaves = 16;
 #ifndef W4A16_GEMV_PREFETCH
 #define W4A16_GEMV_PREFETCH 6
 #endif
 constexpr int kPrefetch = W4A16_GEMV_PREFETCH;   // columns in flight ahead of the one computing
-
-// A 32-bit constant materialised in a VGPR. VOP3 instructions (v_and_or_b32)
-// cannot take two literal operands on gfx9, so the masks and magic numbers of
-// the unpack live in registers, which lets (d & mask) | magic issue as one
-// v_and_or_b32 instead of a v_and + v_or pair.
-__device__ inline uint32_t vconst(uint32_t c) {
-    uint32_t r;
-    asm("v_mov_b32 %0, %1" : "=v"(r) : "i"(c));
-    return r;
-}
-
-struct UnpackConsts {
-    uint32_t lo_mask, hi_mask, f16_magic, bf16_magic;
-};
-
-__device__ inline UnpackConsts unpack_consts() {
-    return UnpackConsts{vconst(0x000F000Fu), vconst(0x00F000F0u), vconst(0x64006400u), vconst(0x43004300u)};
-}
-
-__device__ inline uint32_t and_or(uint32_t a, uint32_t mask, uint32_t bits) { return (a & mask) | bits; }
 
 template <bool BF>
 __device__ inline float dot_pair(uint32_t w, uint32_t x, float acc) {
@@ -75,92 +48,71 @@ __device__ inline float dot_pair(uint32_t w, uint32_t x, float acc) {
                                       __builtin_bit_cast(half2_t, x), acc, false);
 }
 
-// One record (32 weights of one row, one group) -> 16 activation-ready pairs.
-// fp16: the pairs are q - z exactly. bf16: the pairs are 128 + q.
-template <bool BF>
-__device__ inline void unpack_record(const uint4 &rec, uint32_t z, const UnpackConsts &uc,
-                                     uint32_t (&t)[16]) {
-    const uint32_t dws[4] = {rec.x, rec.y, rec.z, rec.w};
-    if constexpr (BF) {
-        (void)z;
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            const uint32_t d = dws[j];
-            t[4 * j + 0] = and_or(d, uc.lo_mask, uc.bf16_magic);
-            t[4 * j + 1] = and_or(d >> 4, uc.lo_mask, uc.bf16_magic);
-            t[4 * j + 2] = and_or(d >> 8, uc.lo_mask, uc.bf16_magic);
-            t[4 * j + 3] = and_or(d >> 12, uc.lo_mask, uc.bf16_magic);
-        }
-    } else {
-        const half2_t a = __builtin_bit_cast(half2_t, (0xE400u | z) * 0x00010001u);          // -(1024+z)
-        const half2_t b = __builtin_bit_cast(half2_t, (0xD400u + 16u * z) * 0x00010001u);    // -(64+z)
-        const half2_t sixteenth = {(_Float16)0.0625f, (_Float16)0.0625f};
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            const uint32_t d = dws[j];
-            const uint32_t d8 = d >> 8;
-            half2_t h0 = __builtin_bit_cast(half2_t, and_or(d, uc.lo_mask, uc.f16_magic));
-            half2_t h1 = __builtin_bit_cast(half2_t, and_or(d, uc.hi_mask, uc.f16_magic));
-            half2_t h2 = __builtin_bit_cast(half2_t, and_or(d8, uc.lo_mask, uc.f16_magic));
-            half2_t h3 = __builtin_bit_cast(half2_t, and_or(d8, uc.hi_mask, uc.f16_magic));
-            t[4 * j + 0] = __builtin_bit_cast(uint32_t, h0 + a);
-            t[4 * j + 1] = __builtin_bit_cast(uint32_t, __builtin_elementwise_fma(h1, sixteenth, b));
-            t[4 * j + 2] = __builtin_bit_cast(uint32_t, h2 + a);
-            t[4 * j + 3] = __builtin_bit_cast(uint32_t, __builtin_elementwise_fma(h3, sixteenth, b));
-        }
-    }
+// LDS bytes of one wave: activations [MT][xcols*128] (16-bit) and, for bf16,
+// their sums over every 8 consecutive k ([MT][xcols*16] fp32).
+__host__ __device__ inline size_t wave_lds_bytes(int MT, int xcols, bool bf16, int group) {
+    (void)group;
+    return (size_t)MT * xcols * 256 + (bf16 ? (size_t)MT * xcols * 64 : 0);
 }
 
+// The scales of one row in one column (GPC fp16 values) as raw bits.
+template <int GPC> struct ColScales;
+template <> struct ColScales<1> { uint16_t v; __device__ float get(int) const { return (float)__builtin_bit_cast(_Float16, v); } };
+template <> struct ColScales<2> { uint32_t v; __device__ float get(int e) const { return (float)__builtin_bit_cast(_Float16, (uint16_t)(v >> (16 * e))); } };
+template <> struct ColScales<4> { uint2 v; __device__ float get(int e) const { const uint32_t h = e < 2 ? v.x : v.y; return (float)__builtin_bit_cast(_Float16, (uint16_t)(h >> (16 * (e & 1)))); } };
+
 template <int GROUP, int MT, bool BF>
-__global__ __launch_bounds__(1024) void gemv_kernel(const uint16_t *__restrict__ x,
-                                                    const uint4 *__restrict__ qw,
-                                                    const uint16_t *__restrict__ scales,
-                                                    const uint32_t *__restrict__ zeros,
-                                                    uint16_t *__restrict__ y, int N, int K) {
-    // LDS image of the activations: x[m][k] as 16-bit values, then (bf16 only)
-    // the fp32 sum of every 32-weight chunk of every row, [MT][K/32].
+__global__ __launch_bounds__(1024) __attribute__((amdgpu_waves_per_eu(1, 4))) void gemv_kernel(
+    const uint16_t *__restrict__ x, const uint4 *__restrict__ qw, const uint16_t *__restrict__ scales,
+    const uint32_t *__restrict__ zeros, uint16_t *__restrict__ y, int N, int K, int xcols) {
+    constexpr int CPG = GROUP / kChunk;   // chunks per group (1, 2, 4)
+    constexpr int PF = MT == 1 ? kPrefetch : (MT == 2 ? 4 : (MT <= 4 ? 3 : 2));
     extern __shared__ __align__(16) unsigned char smem[];
-    uint4 *xs16 = reinterpret_cast<uint4 *>(smem);
-    float *xsum = reinterpret_cast<float *>(smem + (size_t)MT * K * 2);
-    __shared__ float red[kMaxWaves][MT][kRowsPerWave];
+    __shared__ float red[kMaxWaves][MT][kRowBlock];
 
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int waves = blockDim.x >> 6;
-    const int r = lane >> 2;          // row within the workgroup's 16
-    const int s = lane & 3;           // chunk within a 128-weight column
-    const int n0 = blockIdx.x * kRowsPerWave;
-    const int rows = min(kRowsPerWave, N - n0);
-    const bool row_ok = r < rows;
-    const int n = n0 + (row_ok ? r : 0);
+    const int r = lane & 15;          // row within the block
+    const int s = lane >> 4;          // dword position: k-slice [8s, 8s+8) of each chunk
+    const int b = blockIdx.x;
+    const int n0 = b * kRowBlock;
+    const int rows = min(kRowBlock, N - n0);
+    const int rl = r < rows ? r : r - rows;   // lanes past a short last block re-read a valid row
 
-    // this wave's slice of 128-weight columns
-    const int C = K / kChunk;                 // chunks along K
-    const int T = (C + kChunkLanes - 1) / kChunkLanes;
-    const int t_begin = (int)(((int64_t)wave * T) / waves);
-    const int t_end = (int)(((int64_t)(wave + 1) * T) / waves);
+    constexpr int GPC = kColumn / GROUP;   // groups per column (4, 2, 1)
+    const Slice sl = wave_slice<GROUP>(K, wave, waves);
+    const int nchunks = sl.c_hi - sl.c_lo;
 
-    // record (n, chunk c) sits at uint4 index rb*2K + c*rows_b + (n % 64)
-    const int rb = n / kRowBlock;
-    const int rows_b = min(kRowBlock, N - rb * kRowBlock);
-    const uint4 *rec_base = qw + (int64_t)rb * 2 * K + (n % kRowBlock);
-    const uint16_t *sc_base = scales + n;
-    const uint32_t *zp_base = zeros + (n >> 3);
-    const int zshift = 4 * (n & 7);
+    // this wave's LDS region
+    unsigned char *wbase = smem + (size_t)wave * wave_lds_bytes(MT, xcols, BF, GROUP);
+    uint4 *xw = reinterpret_cast<uint4 *>(wbase);                                        // [MT][xcols*16]
+    float *xsw = reinterpret_cast<float *>(wbase + (size_t)MT * xcols * 256);           // [MT][xcols*16]
+
+    // weights: block base, full column t at t*4*rows uint4, lane at s*rows + rl
+    const uint4 *qw_b = qw + (size_t)b * (K / 2);
+    const uint32_t lane_rec = (uint32_t)(s * rows + rl);
+    const uint32_t col_rec = (uint32_t)(kColChunks * rows);
     const UnpackConsts uc = unpack_consts();
+    // per-column metadata of row n: GPC scales at (t*N + n)*GPC, GPC zero
+    // nibbles starting at nibble (t*N + n)*GPC of the zero words
+    const int n = n0 + rl;
+    const ColScales<GPC> *sc_row = reinterpret_cast<const ColScales<GPC> *>(scales) + n;
+    const uint32_t *zp_row = zeros + (n * GPC) / 8;
+    const int zshift = 4 * ((n * GPC) % 8);
 
     struct Buf {
         uint4 rec;
-        uint32_t sc, zw;
+        ColScales<GPC> sc;
+        uint32_t zw;
     };
-    // This lane's chunk of column t, clamped into range: a clamped lane
-    // re-reads a valid record and its result is dropped in compute_col.
-    auto load_col = [&](int t, Buf &b) {
-        const int c = min(t * kChunkLanes + s, C - 1);
-        const uint32_t g = (uint32_t)(c * kChunk) / GROUP;
-        b.rec = rec_base[(uint32_t)c * (uint32_t)rows_b];
-        b.sc = sc_base[(size_t)g * (uint32_t)N];
-        b.zw = zp_base[(size_t)g * (uint32_t)(N / 8)];
+    auto load_meta = [&](int t, Buf &u) {
+        u.sc = sc_row[(size_t)t * N];
+        u.zw = zp_row[(size_t)t * (N * GPC / 8)];
+    };
+    auto load_col = [&](int t, Buf &u) {
+        u.rec = qw_b[(uint32_t)t * col_rec + lane_rec];
+        load_meta(t, u);
         // keep the prefetch where it is: the scheduler may not sink these
         // loads towards their use (which would serialise the stream)
         __builtin_amdgcn_sched_barrier(0);
@@ -169,84 +121,141 @@ __global__ __launch_bounds__(1024) void gemv_kernel(const uint16_t *__restrict__
     float acc[MT];
 #pragma unroll
     for (int m = 0; m < MT; ++m) acc[m] = 0.0f;
+    Buf ring[PF + 1];
 
-    auto compute_col = [&](int t, const Buf &b) {
-        const int c = t * kChunkLanes + s;
-        if (c < C) {
-            const uint32_t z = (b.zw >> zshift) & 0xFu;
-            uint32_t w[16];
-            unpack_record<BF>(b.rec, z, uc, w);
-            const float sc = (float)__builtin_bit_cast(_Float16, (uint16_t)b.sc);
-#pragma unroll
-            for (int m = 0; m < MT; ++m) {
-                const uint4 *xp = xs16 + ((size_t)m * K + (size_t)c * kChunk) / 8;
-                float p = 0.0f;
-#pragma unroll
-                for (int j = 0; j < 4; ++j) {
-                    const uint4 xv = xp[j];
-                    p = dot_pair<BF>(w[4 * j + 0], xv.x, p);
-                    p = dot_pair<BF>(w[4 * j + 1], xv.y, p);
-                    p = dot_pair<BF>(w[4 * j + 2], xv.z, p);
-                    p = dot_pair<BF>(w[4 * j + 3], xv.w, p);
-                }
-                if constexpr (BF) p = fmaf(-(float)(128u + z), xsum[(size_t)m * C + c], p);
-                acc[m] = fmaf(sc, p, acc[m]);
+    // 1. stage: activation loads first, weight prefetch right behind them,
+    // then the LDS stores (vector-memory counters retire in
+    // order, so the stores wait for the stage loads only)
+    {
+        const uint4 *xg = reinterpret_cast<const uint4 *>(x);
+        const int per_m = nchunks * 4;                 // uint4 of one activation row in the slice
+        const int xtotal = MT * per_m;
+        auto xsrc = [&](int i) {
+            i = max(min(i, xtotal - 1), 0);
+            const int m = i / per_m;
+            return xg[(size_t)m * (K / 8) + sl.c_lo * 4 + (i - m * per_m)];
+        };
+        auto xdst = [&](int i, const uint4 &v) {
+            if (i < xtotal) {
+                const int m = i / per_m;
+                xw[(size_t)m * xcols * 16 + (i - m * per_m)] = v;
             }
+        };
+        for (int base = 0; base < xtotal; base += 8 * 64) {
+            const uint4 v0 = xsrc(base + 0 * 64 + lane), v1 = xsrc(base + 1 * 64 + lane);
+            const uint4 v2 = xsrc(base + 2 * 64 + lane), v3 = xsrc(base + 3 * 64 + lane);
+            const uint4 v4 = xsrc(base + 4 * 64 + lane), v5 = xsrc(base + 5 * 64 + lane);
+            const uint4 v6 = xsrc(base + 6 * 64 + lane), v7 = xsrc(base + 7 * 64 + lane);
+            if (base == 0) {
+#pragma unroll
+                for (int i = 0; i < PF; ++i)
+                    if (sl.t_begin + i < sl.t_full) load_col(sl.t_begin + i, ring[i]);
+            }
+            xdst(base + 0 * 64 + lane, v0); xdst(base + 1 * 64 + lane, v1);
+            xdst(base + 2 * 64 + lane, v2); xdst(base + 3 * 64 + lane, v3);
+            xdst(base + 4 * 64 + lane, v4); xdst(base + 5 * 64 + lane, v5);
+            xdst(base + 6 * 64 + lane, v6); xdst(base + 7 * 64 + lane, v7);
+        }
+        if constexpr (BF) {
+            // sum of every 8 activations (one k-slice of one chunk)
+            for (int i = lane; i < MT * nchunks * 4; i += 64) {
+                const int m = i / (nchunks * 4), q = i - m * (nchunks * 4);
+                const uint4 v = xw[(size_t)m * xcols * 16 + q];
+                float sum = 0.0f;
+                sum = dot_pair<true>(v.x, 0x3F803F80u, sum);
+                sum = dot_pair<true>(v.y, 0x3F803F80u, sum);
+                sum = dot_pair<true>(v.z, 0x3F803F80u, sum);
+                sum = dot_pair<true>(v.w, 0x3F803F80u, sum);
+                xsw[(size_t)m * xcols * 16 + q] = sum;
+            }
+        }
+        // every LDS store above precedes every LDS read below (same wave, in order)
+        __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+    }
+
+    // one dword of chunk c (this lane's k-slice), group e of the column: adds
+    // its dot product to p
+    auto dword_dot = [&](int c, uint32_t d, uint32_t z, float (&p)[MT]) {
+        uint32_t w[4];
+        if constexpr (BF)
+            unpack_bf16_magic(d, uc, w);
+        else
+            unpack_f16(d, z, uc, w);
+        const int q = (c - sl.c_lo) * 4 + s;   // uint4 index of this k-slice in the wave's x
+#pragma unroll
+        for (int m = 0; m < MT; ++m) {
+            const uint4 xv = xw[(size_t)m * xcols * 16 + q];
+            float t = dot_pair<BF>(w[0], xv.x, 0.0f);
+            t = dot_pair<BF>(w[1], xv.y, t);
+            t = dot_pair<BF>(w[2], xv.z, t);
+            t = dot_pair<BF>(w[3], xv.w, t);
+            if constexpr (BF) t = fmaf(-(float)(128u + z), xsw[(size_t)m * xcols * 16 + q], t);
+            p[m] += t;
+        }
+    };
+    auto close_group = [&](float sc, float (&p)[MT]) {
+#pragma unroll
+        for (int m = 0; m < MT; ++m) {
+            acc[m] = fmaf(sc, p[m], acc[m]);
+            p[m] = 0.0f;
+        }
+    };
+    auto compute_col = [&](int t, const Buf &u) {
+        const uint32_t dws[4] = {u.rec.x, u.rec.y, u.rec.z, u.rec.w};
+        float p[MT];
+#pragma unroll
+        for (int m = 0; m < MT; ++m) p[m] = 0.0f;
+#pragma unroll
+        for (int j = 0; j < kColChunks; ++j) {
+            const int e = j / CPG;
+            const uint32_t z = (u.zw >> (zshift + 4 * e)) & 0xFu;
+            dword_dot(t * kColChunks + j, dws[j], z, p);
+            if ((j + 1) % CPG == 0) close_group(u.sc.get(e), p);
         }
     };
 
-    // 1. start the weight stream before anything else
-    Buf ring[kPrefetch + 1];
+    // 2. stream the full columns: column t computes while t+1..t+PF are in
+    // flight. The ring is indexed by compile-time positions (the loop is
+    // unrolled by the ring size), so no register with a load in flight is
+    // ever copied, and the loop body has no lane-dependent branch.
+    int t = sl.t_begin;
+    for (; t + PF + 1 <= sl.t_full; t += PF + 1) {
 #pragma unroll
-    for (int i = 0; i < kPrefetch; ++i)
-        if (t_begin + i < t_end) load_col(t_begin + i, ring[i]);
-
-    // 2. stage the activations (and the bf16 chunk sums) in LDS
-    {
-        const int per_row = K / 8;                 // uint4 per activation row
-        const uint4 *xg = reinterpret_cast<const uint4 *>(x);
-        for (int i = threadIdx.x; i < MT * per_row; i += blockDim.x) xs16[i] = xg[i];
-        if constexpr (BF) {
-            __syncthreads();
-            for (int i = threadIdx.x; i < MT * C; i += blockDim.x) {
-                const uint4 *xp = xs16 + (size_t)i * 4;   // chunk i of the [MT][C] grid
-                float sum = 0.0f;
-#pragma unroll
-                for (int j = 0; j < 4; ++j) {
-                    const uint4 v = xp[j];
-                    sum = dot_pair<true>(v.x, 0x3F803F80u, sum);
-                    sum = dot_pair<true>(v.y, 0x3F803F80u, sum);
-                    sum = dot_pair<true>(v.z, 0x3F803F80u, sum);
-                    sum = dot_pair<true>(v.w, 0x3F803F80u, sum);
-                }
-                xsum[i] = sum;
-            }
-        }
-        __syncthreads();
-    }
-
-    // 3. stream: column t computes while t+1..t+kPrefetch are in flight. The
-    // ring is indexed by compile-time positions (the loop is unrolled by the
-    // ring size), so no register with a load in flight is ever copied.
-    int t = t_begin;
-    for (; t + kPrefetch + 1 <= t_end; t += kPrefetch + 1) {
-#pragma unroll
-        for (int i = 0; i <= kPrefetch; ++i) {
-            const int tl = t + i + kPrefetch;
-            if (tl < t_end) load_col(tl, ring[(i + kPrefetch) % (kPrefetch + 1)]);
+        for (int i = 0; i <= PF; ++i) {
+            load_col(min(t + i + PF, sl.t_full - 1), ring[(i + PF) % (PF + 1)]);
             compute_col(t + i, ring[i]);
         }
     }
 #pragma unroll
-    for (int i = 0; i <= kPrefetch; ++i)
-        if (t + i < t_end) compute_col(t + i, ring[i]);
+    for (int i = 0; i <= PF; ++i)
+        if (t + i < sl.t_full) compute_col(t + i, ring[i]);
 
-    // 4. reduce: the four chunk lanes of a row (DPP quad shuffles), then the waves
+    // 3. the partial last column of K (K % 128 != 0): nc < 4 chunks, each
+    // lane's nc dwords are consecutive; its metadata has the usual layout
+    if (sl.t_end > sl.t_full) {
+        const int tl = sl.t_end - 1;
+        const int nc = sl.C - tl * kColChunks;
+        const uint32_t *col = reinterpret_cast<const uint32_t *>(qw_b) + (size_t)tl * rows * 16 +
+                              (size_t)s * rows * nc + (size_t)rl * nc;
+        Buf u;
+        load_meta(tl, u);
+        float p[MT];
+#pragma unroll
+        for (int m = 0; m < MT; ++m) p[m] = 0.0f;
+        for (int j = 0; j < nc; ++j) {
+            const int e = j / CPG;
+            const uint32_t z = (u.zw >> (zshift + 4 * e)) & 0xFu;
+            dword_dot(tl * kColChunks + j, col[j], z, p);
+            if ((j + 1) % CPG == 0 || j == nc - 1) close_group(u.sc.get(e), p);
+        }
+    }
+
+    // 4. reduce: the four k-slice lanes of a row, then the waves (fixed order)
 #pragma unroll
     for (int m = 0; m < MT; ++m) {
         float v = acc[m];
-        v += __shfl_xor(v, 1, 64);
-        v += __shfl_xor(v, 2, 64);
+        v += __shfl_xor(v, 16, 64);
+        v += __shfl_xor(v, 32, 64);
         acc[m] = v;
     }
     if (s == 0) {
@@ -254,9 +263,9 @@ __global__ __launch_bounds__(1024) void gemv_kernel(const uint16_t *__restrict__
         for (int m = 0; m < MT; ++m) red[wave][m][r] = acc[m];
     }
     __syncthreads();
-    for (int i = threadIdx.x; i < MT * kRowsPerWave; i += blockDim.x) {
-        const int m = i / kRowsPerWave;
-        const int rr = i % kRowsPerWave;
+    for (int i = threadIdx.x; i < MT * kRowBlock; i += blockDim.x) {
+        const int m = i / kRowBlock;
+        const int rr = i % kRowBlock;
         if (rr < rows) {
             float v = red[0][m][rr];
             for (int w = 1; w < waves; ++w) v += red[w][m][rr];
@@ -268,7 +277,8 @@ __global__ __launch_bounds__(1024) void gemv_kernel(const uint16_t *__restrict__
 template <int GROUP, bool BF, int MT>
 hipError_t launch_one(const void *x, const void *qw, const void *sc, const void *zp, void *y, int N,
                       int K, const GemvPlan &plan, hipStream_t stream) {
-    const size_t lds = gemv_lds_bytes(MT, K, BF);
+    const int xcols = gemv_xcols(K, plan.waves);
+    const size_t lds = wave_lds_bytes(MT, xcols, BF, GROUP) * plan.waves;
     auto kern = gemv_kernel<GROUP, MT, BF>;
     if (lds > 48 * 1024) {
         hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(kern),
@@ -278,7 +288,7 @@ hipError_t launch_one(const void *x, const void *qw, const void *sc, const void 
     hipLaunchKernelGGL(kern, dim3(plan.row_blocks), dim3(64 * plan.waves), lds, stream,
                        reinterpret_cast<const uint16_t *>(x), reinterpret_cast<const uint4 *>(qw),
                        reinterpret_cast<const uint16_t *>(sc), reinterpret_cast<const uint32_t *>(zp),
-                       reinterpret_cast<uint16_t *>(y), N, K);
+                       reinterpret_cast<uint16_t *>(y), N, K, xcols);
     return hipGetLastError();
 }
 
@@ -299,8 +309,13 @@ hipError_t launch_m(int M, const void *x, const void *qw, const void *sc, const 
 
 }  // namespace
 
-size_t gemv_lds_bytes(int64_t M, int64_t K, bool bf16) {
-    return (size_t)M * K * 2 + (bf16 ? (size_t)M * (K / kChunk) * 4 : 0);
+int gemv_xcols(int64_t K, int waves) {
+    const int64_t T = ceil_div(K / kChunk, kColChunks);
+    return (int)ceil_div(T, waves);
+}
+
+size_t gemv_lds_bytes(int64_t M, int64_t K, bool bf16, int waves, int group) {
+    return wave_lds_bytes((int)M, gemv_xcols(K, waves), bf16, group) * waves;
 }
 
 GemvPlan gemv_plan(int64_t M, int64_t N, int64_t K, int32_t group) {
@@ -311,11 +326,13 @@ GemvPlan gemv_plan(int64_t M, int64_t N, int64_t K, int32_t group) {
         return v ? atoi(v) : 0;
     }();
     GemvPlan p{};
-    p.row_blocks = (int)ceil_div(N, kRowsPerWave);
-    const int64_t columns = ceil_div(K / kChunk, kChunkLanes);
-    // about 16 resident waves per CU over 256 CUs, at least 2 columns per wave
-    int64_t w = ceil_div(4096, p.row_blocks);
-    if (w > columns / 2) w = columns / 2;
+    p.row_blocks = (int)ceil_div(N, kRowBlock);
+    const int64_t columns = ceil_div(K / kChunk, kColChunks);
+    // four waves per workgroup measured best for the decode shapes; more when
+    // the slices would be long (large K), never more waves than columns
+    int64_t w = 4;
+    if (columns > 4 * 32) w = ceil_div(columns, 32);
+    if (w > columns) w = columns;
     if (forced_waves > 0) w = forced_waves;
     if (w > kMaxWaves) w = kMaxWaves;
     if (w < 1) w = 1;

@@ -8,10 +8,30 @@
 
 namespace w4a16 {
 
-// Packed device layout: rows in blocks of 64, K in chunks of 32 weights; one
-// 16-byte record (4 dwords of 8 nibbles) per (row, chunk).
-constexpr int kRowBlock = 64;
+// Packed device layout. Rows come in blocks of 16 (the last block may hold
+// fewer, rows_b = min(16, N - 16 b)); K comes in chunks of 32 weights
+// (C = K / 32) grouped in columns of 4 chunks (the last column may hold fewer,
+// nc = min(4, C - 4 t)). A chunk of one row is 4 dwords of 8 nibbles; dword d
+// holds k = 32 c + 8 d + i (i = 0..7) in nibble i/2 + 4 (i%2), even k in the
+// low half-word. Inside column t of block b the dwords are ordered
+// [d][row][chunk], so for a full column the 16 bytes at d*256 + r*16 are
+// dword d of the column's 4 chunks of row r, and the whole column (16 rows)
+// is one contiguous KiB: a wave loads it with one 16-byte load per lane, and
+// each lane then holds one 8-weight k-slice of four consecutive chunks, which
+// is exactly the B operand of four 16x16x32 MFMAs (one chunk each).
+constexpr int kRowBlock = 16;
 constexpr int kChunk = 32;
+constexpr int kColChunks = 4;
+
+__host__ __device__ inline int64_t dword_offset(int n, int c, int d, int N, int K) {
+    const int b = n / kRowBlock, r = n % kRowBlock;
+    const int rows_b = (N - b * kRowBlock) < kRowBlock ? (N - b * kRowBlock) : kRowBlock;
+    const int C = K / kChunk;
+    const int t = c / kColChunks, j = c % kColChunks;
+    const int nc = (C - t * kColChunks) < kColChunks ? (C - t * kColChunks) : kColChunks;
+    return (int64_t)b * kRowBlock * (K / 8) + (int64_t)t * rows_b * 16 + (int64_t)d * rows_b * nc +
+           (int64_t)r * nc + j;
+}
 
 // Workspace layout: a fixed region of arrival counters first, then fp32
 // partial sums. The counter region has the same size for every shape, so a
@@ -34,8 +54,9 @@ struct GemvPlan {
 };
 
 GemvPlan gemv_plan(int64_t M, int64_t N, int64_t K, int32_t group);
-// Dynamic LDS of one GEMV workgroup (staged activations, bf16 chunk sums).
-size_t gemv_lds_bytes(int64_t M, int64_t K, bool bf16);
+// Dynamic LDS of one GEMV workgroup (per-wave activations, bf16 sums, metadata).
+size_t gemv_lds_bytes(int64_t M, int64_t K, bool bf16, int waves, int group);
+int gemv_xcols(int64_t K, int waves);
 // Static LDS of one GEMV workgroup (cross-wave reduction buffer).
 constexpr size_t kGemvStaticLds = 16 * 8 * 16 * sizeof(float);
 
