@@ -397,7 +397,28 @@ TOL_REL = 2e-3
 TOL_ABS = 1e-5
 
 
-def error_ratio(y_gpu, y_ref, a) -> np.ndarray:
-    """|y - y_ref| / (2e-3 * sum|x*w_hat| + 1e-5); the acceptance bar is <= 1."""
+def out_half_ulp(y64, dtype: str) -> np.ndarray:
+    """Half the spacing of the output format (fp16: 11 significant bits, bf16:
+    8) at |y|, subnormal range included: the largest error of rounding an exact
+    value once, to nearest, into that format."""
+    p, emin = (11, -14) if dtype == "f16" else (8, -126)
+    mag = np.abs(np.asarray(y64, dtype=np.float64))
+    _, ex = np.frexp(mag)                       # mag = f * 2**ex, f in [0.5, 1)
+    e = np.where(mag > 0, np.maximum(ex - 1, emin), emin)
+    return np.ldexp(1.0, (e - p).astype(np.int64))
+
+
+def error_ratio(y_gpu, y_ref, a, out_dtype: str | None = None) -> np.ndarray:
+    """|y - y_ref| / (2e-3 * sum|x*w_hat| + 1e-5 [+ half an output ulp]); the
+    acceptance bar is <= 1.
+
+    With out_dtype, the budget also holds the one rounding of the result to the
+    output type (fp32 -> fp16/bf16, to nearest even) that every implementation
+    must make: for bf16 that rounding alone reaches 2**-8 relative, more than
+    2e-3, so a correctly rounded exact result could otherwise fail when
+    |y| is close to sum|x*w_hat| (short K)."""
     y_gpu = np.asarray(y_gpu, dtype=np.float64)
-    return np.abs(y_gpu - y_ref) / (TOL_REL * a + TOL_ABS)
+    budget = TOL_REL * a + TOL_ABS
+    if out_dtype is not None:
+        budget = budget + out_half_ulp(np.maximum(np.abs(y_gpu), np.abs(y_ref)), out_dtype)
+    return np.abs(y_gpu - y_ref) / budget

@@ -59,12 +59,13 @@ def y_to_f64(y) -> np.ndarray:
 
 
 def check_against_oracle(y_gpu, x_bits, dtype, o, group, cols=None):
-    """Assert |y - y_ref| <= 2e-3 * sum|x w_hat| + 1e-5 element-wise; return the max ratio."""
+    """Assert |y - y_ref| <= 2e-3 * sum|x w_hat| + 1e-5 (+ the one rounding to
+    the output type) element-wise; return the max ratio."""
     y = y_to_f64(y_gpu)
     if cols is not None:
         y = y[:, cols]
     y_ref, a = ref.linear_ref_rows(x_bits, dtype, o["codes"], o["s_bits"], o["zeros"], group, cols)
-    r = ref.error_ratio(y, y_ref, a)
+    r = ref.error_ratio(y, y_ref, a, dtype)
     worst = float(r.max()) if r.size else 0.0
     assert np.all(np.isfinite(y)), "non-finite output"
     assert worst <= 1.0, f"max error ratio {worst:.3g} (> 1) at {np.unravel_index(np.argmax(r), r.shape)}"

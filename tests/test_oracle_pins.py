@@ -288,6 +288,41 @@ def test_error_ratio_bar():
     a = np.array([[10.0, 0.0]])
     r = ref.error_ratio(np.array([[1.0 + 0.02001, 1e-5]]), y_ref, a)
     assert np.allclose(r, [[1.0, 1.0]], rtol=1e-9)
+    # with the output rounding: half an ulp of the format at |y| joins the budget
+    r16 = ref.error_ratio(np.array([[1.0 + 0.02001 + 2.0 ** -11]]), np.array([[1.0]]), np.array([[10.0]]), "f16")
+    rbf = ref.error_ratio(np.array([[1.0 + 0.02001 + 2.0 ** -8]]), np.array([[1.0]]), np.array([[10.0]]), "bf16")
+    assert np.allclose(r16, 1.0, rtol=1e-6) and np.allclose(rbf, 1.0, rtol=1e-6)
+
+
+def test_out_half_ulp_fp16_matches_numpy_spacing():
+    """Half the fp16 spacing at every positive finite fp16 value below the
+    largest (subnormals included)."""
+    v = np.arange(1, 0x7BFF, dtype=np.uint16).view(np.float16)
+    want = np.spacing(v).astype(np.float64) / 2
+    assert np.array_equal(ref.out_half_ulp(v.astype(np.float64), "f16"), want)
+    assert ref.out_half_ulp(0.0, "f16") == 2.0 ** -25
+
+
+def test_out_half_ulp_bf16_is_half_the_gap_to_the_next_value():
+    """bf16: half the distance from a value to its successor (bit pattern + 1), for
+    every positive finite bf16 value below the largest."""
+    bits = np.arange(1, 0x7F7F, dtype=np.uint32).astype(np.uint16)
+    v = ref.bf16_bits_to_f64(bits)
+    gap = ref.bf16_bits_to_f64((bits + 1).astype(np.uint16)) - v
+    assert np.array_equal(ref.out_half_ulp(v, "bf16"), gap / 2)
+
+
+def test_exactly_rounded_bf16_result_needs_the_rounding_term():
+    """A short-K product whose |y| is close to sum|x*w_hat|: the exact result
+    rounded once to bf16 is off the 2e-3 bar on its own, inside it once the
+    rounding is counted."""
+    x = np.array([[1.0, 1.0]], dtype=np.float64)
+    w_hat = np.array([[0.5, 0.50390625 + 2.0 ** -10]])      # y = A, just past a bf16 midpoint
+    y = x @ w_hat.T
+    a = np.abs(x) @ np.abs(w_hat).T
+    y_bf = ref.bf16_bits_to_f64(ref.f32_to_bf16_bits(y.astype(np.float32)))
+    assert ref.error_ratio(y_bf, y, a)[0, 0] > 1.0
+    assert ref.error_ratio(y_bf, y, a, "bf16")[0, 0] <= 1.0
 
 
 # ---------------------------------------------------------------------------
