@@ -153,10 +153,10 @@ def unpack(pw: PackedWeight, stream=None):
 
 
 class Workspace:
-    """Zero-initialised device workspace for split-K partial sums and counters.
+    """Device workspace handed to the compute calls.
 
-    The library leaves the counters at zero after every completed call, so one
-    buffer can be reused by consecutive calls on one stream.
+    The calls take a workspace argument sized by w4a16_workspace_bytes; the
+    current kernels need none (0 bytes), so no buffer is allocated then.
     """
 
     def __init__(self, device=None):

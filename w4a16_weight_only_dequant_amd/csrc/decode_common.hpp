@@ -87,4 +87,10 @@ __device__ inline Slice wave_slice(int K, int wave, int waves) {
     return sl;
 }
 
+// The scales of one row in one column (GPC fp16 values) as raw bits.
+template <int GPC> struct ColScales;
+template <> struct ColScales<1> { uint16_t v; __device__ float get(int) const { return (float)__builtin_bit_cast(_Float16, v); } };
+template <> struct ColScales<2> { uint32_t v; __device__ float get(int e) const { return (float)__builtin_bit_cast(_Float16, (uint16_t)(v >> (16 * e))); } };
+template <> struct ColScales<4> { uint2 v; __device__ float get(int e) const { const uint32_t h = e < 2 ? v.x : v.y; return (float)__builtin_bit_cast(_Float16, (uint16_t)(h >> (16 * (e & 1)))); } };
+
 }  // namespace w4a16

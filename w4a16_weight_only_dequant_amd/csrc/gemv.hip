@@ -55,12 +55,6 @@ __host__ __device__ inline size_t wave_lds_bytes(int MT, int xcols, bool bf16, i
     return (size_t)MT * xcols * 256 + (bf16 ? (size_t)MT * xcols * 64 : 0);
 }
 
-// The scales of one row in one column (GPC fp16 values) as raw bits.
-template <int GPC> struct ColScales;
-template <> struct ColScales<1> { uint16_t v; __device__ float get(int) const { return (float)__builtin_bit_cast(_Float16, v); } };
-template <> struct ColScales<2> { uint32_t v; __device__ float get(int e) const { return (float)__builtin_bit_cast(_Float16, (uint16_t)(v >> (16 * e))); } };
-template <> struct ColScales<4> { uint2 v; __device__ float get(int e) const { const uint32_t h = e < 2 ? v.x : v.y; return (float)__builtin_bit_cast(_Float16, (uint16_t)(h >> (16 * (e & 1)))); } };
-
 template <int GROUP, int MT, bool BF>
 __global__ __launch_bounds__(1024) __attribute__((amdgpu_waves_per_eu(1, 4))) void gemv_kernel(
     const uint16_t *__restrict__ x, const uint4 *__restrict__ qw, const uint16_t *__restrict__ scales,

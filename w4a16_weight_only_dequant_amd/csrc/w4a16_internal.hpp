@@ -33,13 +33,6 @@ __host__ __device__ inline int64_t dword_offset(int n, int c, int d, int N, int 
            (int64_t)r * nc + j;
 }
 
-// Workspace layout: a fixed region of arrival counters first, then fp32
-// partial sums. The counter region has the same size for every shape, so a
-// workspace reused across shapes never finds old partial sums where a later
-// call's counters live.
-constexpr size_t kCounterRegion = 64 * 1024;
-constexpr int kMaxCounters = (int)(kCounterRegion / sizeof(unsigned));
-
 typedef _Float16 half2_t __attribute__((ext_vector_type(2)));
 typedef __bf16 bf162_t __attribute__((ext_vector_type(2)));
 
@@ -60,14 +53,16 @@ int gemv_xcols(int64_t K, int waves);
 // Static LDS of one GEMV workgroup (cross-wave reduction buffer).
 constexpr size_t kGemvStaticLds = 16 * 8 * 16 * sizeof(float);
 
-// Plan for the matrix-core kernels.
+// Plan for the matrix-core kernels: kind 0 streams the weights through
+// registers for M <= kSkinnyMaxM (one 16-row MFMA tile of activations),
+// kind 1 is the LDS-tiled GEMM for everything larger.
+constexpr int kSkinnyMaxM = 16;
+enum { kTile64x256 = 0, kTile128x256 = 1, kTile256x256 = 2 };
 struct GemmPlan {
-    int kind;               // 0 = skinny (M <= 64, weights streamed to registers), 1 = tiled
-    int k_splits;
-    int m_tiles;
-    int n_tiles;
-    size_t counter_bytes;
-    size_t partial_bytes;
+    int kind;          // 0 = skinny, 1 = tiled
+    int waves;         // skinny: waves per workgroup (split K)
+    int rows_per_wg;   // skinny: 16-row blocks per workgroup (1, 2, 4)
+    int tile;          // tiled: one of kTile*
 };
 
 GemmPlan gemm_plan(int64_t M, int64_t N, int64_t K, int32_t group);
@@ -82,34 +77,11 @@ hipError_t launch_gemv(const void *x, bool bf16, const void *qweight, const void
                        const GemvPlan &plan, hipStream_t stream);
 hipError_t launch_gemm(const void *x, bool bf16, const void *qweight, const void *scales,
                        const void *zeros, void *y, int M, int N, int K, int group,
-                       const GemmPlan &plan, void *workspace, hipStream_t stream);
-
-// Deterministic split-K hand-off used by the GEMV and the skinny GEMM: every
-// workgroup stores its fp32 partial tile with agent-scope stores, then
-// announces itself on a per-tile counter; the last arrival sums the partials
-// in slice order and resets the counter to zero for the next call.
-__device__ inline void store_partial(float *p, float v) {
-    __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-__device__ inline float load_partial(const float *p) {
-    return __hip_atomic_load(const_cast<float *>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-// Returns true in every lane of the calling wave when this wave's workgroup is
-// the last of `total` arrivals on *counter. Must be called by one whole wave
-// after it has issued all of its partial stores.
-__device__ inline bool arrive_last(unsigned *counter, unsigned total) {
-    unsigned old = 0;
-    if ((threadIdx.x & 63) == 0)
-        old = __hip_atomic_fetch_add(counter, 1u, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
-    old = __shfl(old, 0, 64);
-    bool last = (old == total - 1);
-    if (last) {
-        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
-        if ((threadIdx.x & 63) == 0)
-            __hip_atomic_store(counter, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    }
-    return last;
-}
+                       const GemmPlan &plan, hipStream_t stream);
+hipError_t launch_prefill(const void *x, bool bf16, const void *qweight, const void *scales,
+                          const void *zeros, void *y, int M, int N, int K, int group,
+                          const GemmPlan &plan, hipStream_t stream);
+int prefill_tile(int64_t M);
 
 __device__ inline uint16_t f32_to_f16_bits(float v) {
     _Float16 h = (_Float16)v;
