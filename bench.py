@@ -1,19 +1,24 @@
 #!/usr/bin/env python3
 """Benchmark of the gfx950 W4A16 linear layer.
 
-Default workload: the decode layer set of a 13B-class model at M = 1 (q, k, v,
-o: 5120x5120; up, gate: K=5120, N=13824; down: K=13824, N=5120; group 128,
-fp16 activations). One step = one token through all seven W4A16 linear layers
-(seven w4a16_linear calls, which dispatch to the GEMV kernel at M = 1). Inputs
-are synthetic and seeded; the packed weights are rotated over enough copies to
-exceed the 256 MB last-level cache, so every step streams its weights from HBM.
+Headline workload (default): the decode layer set of a 13B-class model at
+M = 1 -- q, k, v, o (K = N = 5120), up and gate (K = 5120, N = 13824), down
+(K = 13824, N = 5120), group 128, fp16 activations. One step = one token
+through all seven layers (seven w4a16_linear calls, dispatched to the decode
+GEMV at M = 1). Second leg: the prefill GEMM, M = 2048, K = 5120, N = 13824,
+group 128, bf16 activations (w4a16_linear dispatches to the tiled MFMA kernel).
 
-Prints one JSON line. `value` is achieved HBM GB/s over the step (algorithmic
-bytes: packed weights + scales + zeros + activations read + outputs written,
-divided by wall time per step). `roofline` gives the GEMV kernel's own rate
-from HIP events around each launch, against the 8 TB/s HBM3E peak.
-`cpu_baseline` times the CPU oracle (dequantise + fp64 product) on a bounded
-sample of the same workload.
+Inputs are synthetic and seeded; packed weights are rotated over enough copies
+to exceed the 256 MB last-level cache, so every launch streams its weights
+from HBM. Launches are replayed from HIP graphs.
+
+Prints one JSON line. `value` is achieved HBM GB/s of the headline step
+(algorithmic bytes -- packed weights + scales + zeros + activations read +
+outputs written -- over wall time per step). `roofline` is the decode GEMV
+kernel's own rate: algorithmic bytes of its launches over their average
+duration from HIP events on the launch stream. `prefill` carries the M = 2048
+GEMM's TFLOP/s against the dense bf16 MFMA peak. `cpu_baseline` times the CPU
+oracle (dequantise + fp64 product) on a bounded sample of the headline workload.
 """
 from __future__ import annotations
 
@@ -27,9 +32,17 @@ import time
 ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
-HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, 8 TB/s
-MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16/fp16 MFMA
+HBM_PEAK_GBS = 8000.0           # MI355X HBM3E, 8 TB/s
+MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 / fp16 MFMA
 MALL_BYTES = 256 << 20
+WORKLOAD_IDS = {"gemv_4096": 1, "decode_13b_layer": 2, "fused_qkv": 3, "prefill": 4, "ffn_down_70b": 5}
+
+# sources each kernel is built from (for matching stored counter results)
+KERNEL_SOURCES = {
+    "gemv": ["gemv.hip", "decode_common.hpp", "w4a16_internal.hpp"],
+    "skinny": ["gemm.hip", "decode_common.hpp", "w4a16_internal.hpp"],
+    "prefill": ["prefill.hip", "decode_common.hpp", "w4a16_internal.hpp"],
+}
 
 
 def parse():
@@ -37,19 +50,20 @@ def parse():
     p.add_argument("--gpus", type=int, default=1)
     p.add_argument("--steps", type=int, default=200)
     p.add_argument("--warmup", type=int, default=20)
-    p.add_argument("--workload", default="decode_13b_layer",
-                   choices=["decode_13b_layer", "gemv_4096", "fused_qkv", "prefill", "ffn_down_70b"])
+    p.add_argument("--workload", default="decode_13b_layer", choices=list(WORKLOAD_IDS))
     p.add_argument("--m", type=int, default=0, help="batch rows (default: the workload's first M)")
+    p.add_argument("--no-prefill", action="store_true", help="skip the M=2048 prefill leg")
+    p.add_argument("--prefill-reps", type=int, default=20)
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-seconds", type=float, default=15.0)
     p.add_argument("--copy-calibration", action="store_true",
-                   help="also run a plain device copy of known size (for counter scaling)")
+                   help="also run an elementwise kernel that reads and writes 256 MiB (counter scaling)")
     return p.parse_args()
 
 
-def kernel_source_hash(files):
+def kernel_source_hash(kind):
     h = hashlib.sha256()
-    for f in files:
+    for f in KERNEL_SOURCES[kind]:
         with open(os.path.join(ROOT, "w4a16_weight_only_dequant_amd", "csrc", f), "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()[:16]
@@ -60,84 +74,162 @@ def algorithmic_bytes(M, N, K, group):
     return N * K // 2 + 2 * G * N + G * N // 2 + 2 * M * K + 2 * M * N
 
 
+def kernel_kind(w4, M):
+    if M <= w4.gemv_max_m():
+        return "gemv"
+    return "skinny" if M <= 16 else "prefill"
+
+
+def stored_traffic(workload, M, kind):
+    """HBM bytes per step from committed counter runs, if taken on these sources."""
+    tfile = os.path.join(ROOT, "profiles", f"traffic_{workload}_m{M}.json")
+    if not os.path.exists(tfile):
+        return None
+    t = json.load(open(tfile))
+    if t.get("kernel_source_sha") != kernel_source_hash(kind):
+        return None
+    return t.get("traffic_bytes_per_launch_set")
+
+
+class Workload:
+    """Packed weights, activations and outputs of one configuration, with
+    enough rotated copies of the weights to defeat the 256 MB MALL."""
+
+    def __init__(self, cfg_id, M, dev):
+        import numpy as np
+        import torch
+
+        import w4a16_weight_only_dequant_amd as w4
+        import workloads as wl
+        self.w4, self.torch = w4, torch
+        self.cfg = wl.WORKLOADS[cfg_id]
+        self.M, self.group, self.dtype = M, self.cfg.group, self.cfg.dtype
+        tdt = torch.float16 if self.dtype == "f16" else torch.bfloat16
+        self.mats = list(self.cfg.matrices)
+        packed, self.xs, self.ys = [], [], []
+        for mi, mat in enumerate(self.mats):
+            w = torch.from_numpy(wl.weights(cfg_id, mi)).to(dev)
+            packed.append(w4.pack(w, self.group))
+            del w
+            xb = wl.activations(cfg_id, mi, M)
+            self.xs.append(torch.from_numpy(xb.view(np.int16)).to(dev).view(tdt))
+            self.ys.append(torch.empty((M, mat.N), dtype=tdt, device=dev))
+        torch.cuda.synchronize()
+        set_bytes = sum(p.nbytes() for p in packed)
+        self.copies = max(1, -(-3 * MALL_BYTES // set_bytes))
+        self.sets = [packed]
+        for _ in range(self.copies - 1):
+            self.sets.append([w4.PackedWeight(p.qweight.clone(), p.scales.clone(), p.zeros.clone(), p.N, p.K,
+                                              p.group) for p in packed])
+        self.ws = w4.Workspace(dev)
+        self.bytes = [algorithmic_bytes(M, m.N, m.K, self.group) for m in self.mats]
+        self.flops = [2 * M * m.N * m.K for m in self.mats]
+
+    def launch(self, c, j):
+        self.w4.linear(self.xs[j], self.sets[c][j], out=self.ys[j], workspace=self.ws)
+
+    def step(self, c):
+        for j in range(len(self.mats)):
+            self.launch(c, j)
+
+    def graphs(self, dev):
+        """One graph per weight copy holding one step; one graph per matrix
+        holding that matrix's launch on every copy (per-kernel timing)."""
+        torch = self.torch
+        for c in range(min(2, self.copies)):
+            self.step(c)
+        torch.cuda.synchronize()
+        cap = torch.cuda.Stream(device=dev)
+        self.step_graphs, self.mat_graphs = [], []
+        with torch.cuda.stream(cap):
+            for c in range(self.copies):
+                g = torch.cuda.CUDAGraph()
+                with torch.cuda.graph(g, stream=cap):
+                    self.step(c)
+                self.step_graphs.append(g)
+            for j in range(len(self.mats)):
+                g = torch.cuda.CUDAGraph()
+                with torch.cuda.graph(g, stream=cap):
+                    for c in range(self.copies):
+                        self.launch(c, j)
+                self.mat_graphs.append(g)
+        torch.cuda.synchronize()
+
+    def per_kernel_ms(self, reps):
+        """Average duration of one launch per matrix: HIP events on the
+        replay stream around back-to-back launches (the gap between two
+        dependent launches is included)."""
+        torch = self.torch
+        out = []
+        for j in range(len(self.mats)):
+            a0 = torch.cuda.Event(enable_timing=True)
+            a1 = torch.cuda.Event(enable_timing=True)
+            self.mat_graphs[j].replay()
+            a0.record()
+            for _ in range(reps):
+                self.mat_graphs[j].replay()
+            a1.record()
+            torch.cuda.synchronize()
+            out.append(a0.elapsed_time(a1) / (reps * self.copies))
+        return out
+
+
+def cpu_oracle_baseline(cfg_id, M, seconds):
+    """The oracle as it stands, timed on the host: dequantise + fp64 product,
+    matrix by matrix, until about `seconds` of CPU work is done."""
+    import workloads as wl
+    from oracle import w4a16_ref as ref
+    try:
+        from threadpoolctl import threadpool_info
+        blas_threads = max([p.get("num_threads", 1) for p in threadpool_info()
+                            if p.get("user_api") == "blas"] or [1])
+    except Exception:   # threadpoolctl missing: report the affinity count
+        blas_threads = len(os.sched_getaffinity(0))
+    cfg = wl.WORKLOADS[cfg_id]
+    mats = list(cfg.matrices)
+    done_bytes, t_cpu, names, mi = 0, 0.0, [], 0
+    while t_cpu < seconds and mi < 2 * len(mats):
+        j = mi % len(mats)
+        codes, s_bits, zeros = ref.quantize_groupwise(wl.weights(cfg_id, j), cfg.group)   # offline, untimed
+        xb = wl.activations(cfg_id, j, M)
+        t1 = time.perf_counter()
+        w_hat = ref.dequantize(codes, s_bits, zeros, cfg.group)
+        ref.linear_ref(xb, cfg.dtype, w_hat)
+        t_cpu += time.perf_counter() - t1
+        done_bytes += algorithmic_bytes(M, mats[j].N, mats[j].K, cfg.group)
+        names.append(mats[j].name)
+        mi += 1
+        del w_hat, codes
+    return {"value": round(done_bytes / t_cpu / 1e9, 3), "unit": "GB/s", "cores": blas_threads,
+            "kind": "oracle",
+            "sample": f"dequantise (numpy, one thread) + fp64 product and |x||w| product (BLAS, "
+                      f"{blas_threads} threads) of matrices {','.join(names)} at M={M}: "
+                      f"{done_bytes / 1e6:.0f} MB of the workload's algorithmic bytes in {t_cpu:.1f} s"}
+
+
 def main():
     args = parse()
     if args.gpus != 1:
-        print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1",
+        print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1 "
+                                   "(the multi-GPU sharding of the layer is described, not built)",
                           "n_gpus": args.gpus}))
         sys.exit(2)
 
-    import numpy as np
     import torch
 
     import w4a16_weight_only_dequant_amd as w4
-    import workloads as wl
 
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     dev = torch.device("cuda:0")
     assert w4.device_supported(0), "cuda:0 is not a gfx950"
 
-    cfg_id = {"gemv_4096": 1, "decode_13b_layer": 2, "fused_qkv": 3, "prefill": 4, "ffn_down_70b": 5}[args.workload]
-    wcfg = wl.WORKLOADS[cfg_id]
-    M = args.m or wcfg.ms[0]
-    group = wcfg.group
-    dtype = wcfg.dtype
-    tdt = torch.float16 if dtype == "f16" else torch.bfloat16
-
-    # ---- setup: pack every matrix once, then rotate copies past the MALL ----
-    packed, xs, ys, mats = [], [], [], []
-    for mi, mat in enumerate(wcfg.matrices):
-        w = torch.from_numpy(wl.weights(cfg_id, mi)).to(dev)
-        packed.append(w4.pack(w, group))
-        del w
-        xb = wl.activations(cfg_id, mi, M)
-        xs.append(torch.from_numpy(xb.view(np.int16)).to(dev).view(tdt))
-        ys.append(torch.empty((M, mat.N), dtype=tdt, device=dev))
-        mats.append(mat)
-    torch.cuda.synchronize()
-    set_bytes = sum(p.nbytes() for p in packed)
-    copies = max(1, -(-3 * MALL_BYTES // set_bytes))
-    sets = [packed]
-    for _ in range(copies - 1):
-        sets.append([w4.PackedWeight(p.qweight.clone(), p.scales.clone(), p.zeros.clone(), p.N, p.K, p.group)
-                     for p in packed])
-    ws = w4.Workspace(dev)
-    step_bytes = sum(algorithmic_bytes(M, m.N, m.K, group) for m in mats)
-    step_flops = sum(2 * M * m.N * m.K for m in mats)
-
-    def step(i, events=None):
-        s = sets[i % copies]
-        for j, pw in enumerate(s):
-            if events is not None:
-                events[j][0].record()
-            w4.linear(xs[j], pw, out=ys[j], workspace=ws)
-            if events is not None:
-                events[j][1].record()
-
-    # eager warm-up (allocates the workspace), then HIP graphs: one graph per
-    # weight copy holding one step, and one graph per matrix holding one launch
-    # on every copy (for the per-kernel timing). Graph replay keeps the GPU fed
-    # without per-launch host overhead.
-    for i in range(2):
-        step(i)
-    torch.cuda.synchronize()
-    cap = torch.cuda.Stream(device=dev)
-    step_graphs, mat_graphs = [], []
-    with torch.cuda.stream(cap):
-        for c in range(copies):
-            g = torch.cuda.CUDAGraph()
-            with torch.cuda.graph(g, stream=cap):
-                step(c)
-            step_graphs.append(g)
-        for j, m in enumerate(mats):
-            g = torch.cuda.CUDAGraph()
-            with torch.cuda.graph(g, stream=cap):
-                for c in range(copies):
-                    w4.linear(xs[j], sets[c][j], out=ys[j], workspace=ws)
-            mat_graphs.append(g)
-    torch.cuda.synchronize()
+    import workloads as wl
+    cfg_id = WORKLOAD_IDS[args.workload]
+    M = args.m or wl.WORKLOADS[cfg_id].ms[0]
+    wk = Workload(cfg_id, M, dev)
+    wk.graphs(dev)
     for i in range(args.warmup):
-        step_graphs[i % copies].replay()
+        wk.step_graphs[i % wk.copies].replay()
     torch.cuda.synchronize()
 
     # ---- timed region: exactly K steps, bracketed by synchronisation ----
@@ -147,86 +239,70 @@ def main():
     t0 = time.perf_counter()
     e0.record()
     for i in range(args.steps):
-        step_graphs[i % copies].replay()
+        wk.step_graphs[i % wk.copies].replay()
     e1.record()
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     ms_per_step = wall * 1e3 / args.steps
     gpu_ms_per_step = e0.elapsed_time(e1) / args.steps
+    step_bytes, step_flops = sum(wk.bytes), sum(wk.flops)
 
-    # ---- per-kernel timing: HIP events on the launch stream around each
-    # matrix's graph (one launch per weight copy, back to back) ----
-    n_mat = len(mats)
-    reps = max(1, args.steps // (copies * 4))
-    per_mat_ms = np.zeros(n_mat)
-    for j in range(n_mat):
-        a0 = torch.cuda.Event(enable_timing=True)
-        a1 = torch.cuda.Event(enable_timing=True)
-        mat_graphs[j].replay()
-        a0.record()
-        for _ in range(reps):
-            mat_graphs[j].replay()
-        a1.record()
-        torch.cuda.synchronize()
-        per_mat_ms[j] = a0.elapsed_time(a1) / (reps * copies)
-    kernel_ms_step = float(per_mat_ms.sum())
-
-    value = step_bytes / (ms_per_step * 1e-3) / 1e9
-    achieved = step_bytes / (kernel_ms_step * 1e-3) / 1e9
-
-    uses_gemv = M <= w4.gemv_max_m()
-    bound = "hbm" if uses_gemv or M <= 64 else "mfma"
-    if bound == "hbm":
-        roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                "frac": round(achieved / HBM_PEAK_GBS, 4)}
-    else:
-        tf = step_flops / (kernel_ms_step * 1e-3) / 1e12
+    # ---- the dominant kernel's own rate ----
+    per_ms = wk.per_kernel_ms(max(1, args.steps // (wk.copies * 4)))
+    kernel_ms = float(sum(per_ms))
+    kind = kernel_kind(w4, M)
+    if kind == "prefill":
+        tf = step_flops / (kernel_ms * 1e-3) / 1e12
         roof = {"bound": "mfma", "achieved": round(tf, 1), "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
                 "frac": round(tf / MFMA_BF16_PEAK_TFLOPS, 4)}
-    kernel_file = "gemv.hip" if uses_gemv else "gemm.hip"
-    src_hash = kernel_source_hash([kernel_file, "w4a16_internal.hpp"])
-    roof["kernel"] = "gemv_kernel" if uses_gemv else "gemm_kernel"
-    roof["kernel_source_sha"] = src_hash
-    roof["traffic"] = None
-    tfile = os.path.join(ROOT, "profiles", f"traffic_{args.workload}_m{M}.json")
-    if os.path.exists(tfile):
-        t = json.load(open(tfile))
-        if t.get("kernel_source_sha") == src_hash:
-            roof["traffic"] = t.get("traffic_bytes_per_step")
-    roof["units_per_launch"] = {m.name: {"weights": m.N * m.K, "bytes": algorithmic_bytes(M, m.N, m.K, group),
-                                         "kernel_us": round(float(per_mat_ms[j]) * 1e3, 2)}
-                                for j, m in enumerate(mats)}
+    else:
+        gbs = step_bytes / (kernel_ms * 1e-3) / 1e9
+        roof = {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": round(gbs / HBM_PEAK_GBS, 4)}
+    roof["traffic"] = stored_traffic(args.workload, M, kind)
+    roof["kernel"] = {"gemv": "gemv_kernel", "skinny": "skinny_kernel", "prefill": "prefill_kernel"}[kind]
+    roof["kernel_source_sha"] = kernel_source_hash(kind)
+    roof["timing"] = "HIP events on the replay stream around back-to-back launches of one matrix"
+    roof["units_per_launch"] = {m.name: {"weights": m.N * m.K, "bytes": wk.bytes[j],
+                                         "kernel_us": round(per_ms[j] * 1e3, 2)}
+                                for j, m in enumerate(wk.mats)}
+    del wk
+    torch.cuda.empty_cache()
+
+    # ---- prefill leg: M = 2048 GEMM (MFMA) ----
+    prefill = None
+    if not args.no_prefill and args.workload != "prefill":
+        pk = Workload(WORKLOAD_IDS["prefill"], wl.WORKLOADS[WORKLOAD_IDS["prefill"]].ms[0], dev)
+        pk.graphs(dev)
+        pms = pk.per_kernel_ms(max(1, args.prefill_reps // pk.copies))
+        pkind = kernel_kind(w4, pk.M)
+        tf = pk.flops[0] / (pms[0] * 1e-3) / 1e12
+        prefill = {"workload": "prefill", "M": pk.M, "N": pk.mats[0].N, "K": pk.mats[0].K, "group": pk.group,
+                   "dtype": pk.dtype, "kernel": "prefill_kernel" if pkind == "prefill" else pkind,
+                   "kernel_us": round(pms[0] * 1e3, 2), "tflops": round(tf, 1),
+                   "roofline": {"bound": "mfma", "achieved": round(tf, 1), "peak": MFMA_BF16_PEAK_TFLOPS,
+                                "unit": "TFLOP/s", "frac": round(tf / MFMA_BF16_PEAK_TFLOPS, 4),
+                                "traffic": stored_traffic("prefill", pk.M, pkind),
+                                "kernel_source_sha": kernel_source_hash(pkind)},
+                   "tokens_per_s": round(pk.M / (pms[0] * 1e-3), 1)}
+        del pk
+        torch.cuda.empty_cache()
 
     if args.copy_calibration:
-        a = torch.empty(1 << 28, dtype=torch.uint8, device=dev)   # 256 MiB
+        # an elementwise kernel of known traffic (reads 256 MiB, writes 256 MiB):
+        # counter bytes of this launch give the scale factor for the others
+        a = torch.ones(1 << 26, dtype=torch.float32, device=dev)
         b = torch.empty_like(a)
         for _ in range(3):
-            b.copy_(a)
+            torch.mul(a, 2.0, out=b)
         torch.cuda.synchronize()
+        del a, b
 
-    # ---- CPU oracle baseline on a bounded sample ----
     cpu = None
     if not args.no_cpu_baseline:
-        from oracle import w4a16_ref as ref
-        cores = len(os.sched_getaffinity(0))
-        done_bytes, t_cpu, names = 0, 0.0, []
-        mi = 0
-        while t_cpu < args.cpu_seconds and mi < 2 * n_mat:
-            j = mi % n_mat
-            codes, s_bits, zeros = ref.quantize_groupwise(wl.weights(cfg_id, j), group)   # offline, untimed
-            xb = wl.activations(cfg_id, j, M)
-            t1 = time.perf_counter()
-            w_hat = ref.dequantize(codes, s_bits, zeros, group)
-            ref.linear_ref(xb, dtype, w_hat)
-            t_cpu += time.perf_counter() - t1
-            done_bytes += algorithmic_bytes(M, mats[j].N, mats[j].K, group)
-            names.append(mats[j].name)
-            mi += 1
-            del w_hat, codes
-        cpu = {"value": round(done_bytes / t_cpu / 1e9, 3), "unit": "GB/s", "cores": cores, "kind": "oracle",
-               "sample": f"dequantise + fp64 product (numpy) for matrices {','.join(names)} at M={M}, "
-                         f"{t_cpu:.1f} s; threads = host affinity count (BLAS), dequantise single-threaded"}
+        cpu = cpu_oracle_baseline(cfg_id, M, args.cpu_seconds)
 
+    value = step_bytes / (ms_per_step * 1e-3) / 1e9
     out = {
         "metric": "W4A16 GEMV achieved HBM GB/s (% peak) at M=1; GEMM TFLOP/s (% MFMA) at M=2048",
         "value": round(value, 1),
@@ -239,16 +315,15 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": dtype,
+        "dtype": wl.WORKLOADS[cfg_id].dtype,
         "data": "synthetic",
-        "config": {"workload": args.workload, "M": M, "group": group,
-                   "matrices": [[m.name, m.N, m.K] for m in mats],
-                   "bytes_per_step": step_bytes, "flops_per_step": step_flops,
-                   "weight_copies_rotated": copies},
+        "config": {"workload": args.workload, "M": M, "group": wl.WORKLOADS[cfg_id].group,
+                   "matrices": [[m.name, m.N, m.K] for m in wl.WORKLOADS[cfg_id].matrices],
+                   "bytes_per_step": step_bytes, "flops_per_step": step_flops},
         "pct_hbm_peak": round(value / HBM_PEAK_GBS * 100, 2),
         "tokens_per_s": round(M / (ms_per_step * 1e-3), 1),
-        "tflops": round(step_flops / (ms_per_step * 1e-3) / 1e12, 3),
         "roofline": roof,
+        "prefill": prefill,
         "cpu_baseline": cpu,
     }
     print(json.dumps(out))

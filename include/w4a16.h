@@ -24,19 +24,31 @@
  * packed until the kernel consumes it ("Quantization Is Not a Zip File",
  * section 8).
  *
- * Layout (all little-endian, row-major, contiguous):
+ * Layout (all little-endian, contiguous). C = K/32 chunks of 32 weights along
+ * K, grouped into T = ceil(C/4) columns of 128 weights (the last column holds
+ * nc = C - 4(T-1) chunks when K % 128 != 0). Rows come in blocks of 16 (the
+ * last block holds rows_b = N - 16b when N % 16 == 8).
  *   w        fp32 [N][K]            input of w4a16_pack (PyTorch Linear order)
- *   qweight  N*K/2 bytes            rows in blocks of 64 (the last block holds
- *            rows_b = min(64, N - 64b) rows), K in chunks of 32: the 16-byte
- *            record of (row n, chunk c) starts at byte
- *              64*b*(K/2) + c*rows_b*16 + r*16,   b = n/64, r = n%64, c = k/32.
- *            Dword j = (k%32)/8 of a record holds k = 32c + 8j + i (i = 0..7)
- *            in nibble i/2 + 4*(i%2): even k in the low half-word, odd k in the
- *            high half-word.
- *   scales   fp16 [G][N]            G = K / group
- *   zeros    uint32 [G][N/8]        nibble n%8 of word n/8 holds z[g][n]
- *   x        fp16 or bf16 [M][K]
- *   y        same type as x, [M][N]; fp32 accumulation, rounded once (RNE)
+ *   qweight  N*K/2 bytes            block b occupies bytes [8Kb, 8K(b+1));
+ *            inside it, column t starts at byte 64*rows_b*t. Dword d (0..3) of
+ *            chunk c = 4t + j of row r = n%16 sits at byte
+ *              8Kb + 64*rows_b*t + 4*(d*rows_b*nc + r*nc + j)
+ *            (nc = 4 for a full column). It holds k = 32c + 8d + i (i = 0..7)
+ *            in nibble i/2 + 4*(i%2): even k in the low half-word, odd k in
+ *            the high half-word. A full column of a full block is one
+ *            contiguous KiB in which the 16 bytes at 256d + 16r are dword d of
+ *            the column's four chunks of row r.
+ *   scales   fp16 [T][N][128/group] the group scales of row n in column t, in
+ *                                   k order (slots past K hold 0)
+ *   zeros    uint32 [T][N*128/group/8]  4-bit zero-points in the same order:
+ *                                   entry (t, n, e) is nibble (n*128/group + e)
+ *                                   of column t's words (slots past K hold 0)
+ *            For K % 128 == 0 both have the canonical sizes 2*G*N and G*N/2
+ *            bytes (G = K/group), and at group 128 they are exactly [G][N]
+ *            and [G][N/8].
+ *   x        fp16 or bf16 [M][K], row-major
+ *   y        same type as x, [M][N], row-major; fp32 accumulation, rounded
+ *            once to the output type (round to nearest even)
  *
  * Ownership: the caller owns every buffer; no call allocates or frees device
  * memory. Every pointer passed to a compute call is a device pointer. Calls
@@ -50,8 +62,8 @@
  * device query that failed).
  *
  * Preconditions shared by the compute calls:
- *   M >= 1, N >= 8, N % 8 == 0, group in {32, 64, 128}, K >= group,
- *   K % group == 0; pointers non-NULL and 16-byte aligned; y does not overlap
+ *   1 <= M <= 2^24, M*K < 2^34, N >= 8, N % 8 == 0, group in {32, 64, 128},
+ *   K >= group, K % group == 0; pointers non-NULL and 16-byte aligned; y does not overlap
  *   any input; the current device is a gfx950 (w4a16_device_supported).
  *   Weights given to w4a16_pack are finite with |w| < 2^18.
  */
@@ -65,7 +77,7 @@
 extern "C" {
 #endif
 
-#define W4A16_LAYOUT_VERSION 1
+#define W4A16_LAYOUT_VERSION 2
 
 typedef enum {
     W4A16_OK = 0,
@@ -93,18 +105,21 @@ int w4a16_layout_version(void);
  * device packed kernel (this call), default path (w4a16_linear). */
 w4a16_status w4a16_device_supported(int device);
 
-/* Byte sizes of the packed buffers for an N x K weight matrix:
- * qweight N*K/2, scales 2*G*N, zeros G*N/2 (4 + 20/group bits per weight, the
- * 4.156 bits/weight at group 128 of "Weight-Only Quantization Explained",
- * "The memory arithmetic"). Host-only; any out-pointer may be NULL. */
+/* Byte sizes of the packed buffers for an N x K weight matrix: qweight
+ * N*K/2, scales 2*T*N*(128/group), zeros T*N*(128/group)/2 with
+ * T = ceil(K/128). For K % 128 == 0 these are 2*G*N and G*N/2: 4 + 20/group
+ * bits per weight, the 4.156 bits/weight at group 128 of "Weight-Only
+ * Quantization Explained", "The memory arithmetic". Host-only; any
+ * out-pointer may be NULL. */
 w4a16_status w4a16_packed_bytes(int64_t N, int64_t K, int32_t group,
                                 size_t *qweight_bytes, size_t *scales_bytes,
                                 size_t *zeros_bytes);
 
 /* Workspace bytes a w4a16_gemv / w4a16_gemm / w4a16_linear call of this shape
- * needs (split-K partial sums and arrival counters). Host-only. The workspace
- * must be zero-filled once before its first use; every completed call leaves
- * its counters at zero again. One workspace serves one call at a time. */
+ * needs. Host-only. The current kernels reduce inside each workgroup and need
+ * none (0 bytes; the compute calls then accept a NULL workspace); the argument
+ * stays in the interface so that a kernel needing scratch memory can be added
+ * without changing it. */
 w4a16_status w4a16_workspace_bytes(int64_t M, int64_t N, int64_t K, int32_t group,
                                    size_t *bytes);
 
@@ -122,15 +137,22 @@ w4a16_status w4a16_unpack(const void *qweight, const void *scales, const void *z
 
 /* Decode GEMV: y [M][N] = x [M][K] . w_hat^T for small M (1 <= M <= 8).
  * One pass over the packed weights: 128-bit loads, in-register unpack, fp16
- * or bf16 dot products with fp32 accumulation, per-group scale, split-K with a
- * deterministic in-kernel reduction. Returns W4A16_ERR_INVALID_ARG for M > 8. */
+ * or bf16 dot products with fp32 accumulation, per-group scale; the waves of
+ * a workgroup split K and meet in LDS in a fixed order (deterministic). The
+ * activations are staged in LDS: returns W4A16_ERR_INVALID_ARG for M > 8 or
+ * when M*K does not fit (w4a16_gemm has no such limit). */
 w4a16_status w4a16_gemv(const void *x, int32_t dtype, const void *qweight,
                         const void *scales, const void *zeros, void *y,
                         int64_t M, int64_t N, int64_t K, int32_t group,
                         void *workspace, size_t workspace_bytes, void *stream);
 
-/* Matrix-core GEMM for any M >= 1: packed weight tiles are dequantised in
- * registers/LDS to fp16/bf16 and fed to MFMA with fp32 accumulation. */
+/* Matrix-core GEMM for any M >= 1 (M*K < 2^34). M <= 16: the packed weights
+ * stream through registers as in the GEMV, and each unpacked dword feeds one
+ * 16x16x32 MFMA (exact integers q - z, group scale on the fp32 sums). Larger M:
+ * weight tiles are dequantised once per workgroup into LDS as 16-bit
+ * s*(q - z) (one rounding) and fed to 32x32x16 MFMAs with fp32 accumulation
+ * ("Weight-Only Quantisation", the FAQ answers on batch size: at prefill the
+ * layer is compute bound and the dequantisation is on the critical path). */
 w4a16_status w4a16_gemm(const void *x, int32_t dtype, const void *qweight,
                         const void *scales, const void *zeros, void *y,
                         int64_t M, int64_t N, int64_t K, int32_t group,

@@ -34,7 +34,7 @@ def test_library_exports_every_declared_symbol(w4):
 
 def test_status_strings_and_version(w4):
     lib = w4.raw()
-    assert lib.w4a16_layout_version() == 1
+    assert lib.w4a16_layout_version() == 2
     for code in range(5):
         assert lib.w4a16_status_string(code)
     assert lib.w4a16_status_string(99) == b"unknown status"

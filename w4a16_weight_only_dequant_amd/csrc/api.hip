@@ -80,6 +80,7 @@ w4a16_status check_linear(const void *x, int32_t dtype, const void *qweight, con
     if (!x || !qweight || !scales || !zeros || !y) return W4A16_ERR_INVALID_ARG;
     if (dtype != W4A16_F16 && dtype != W4A16_BF16) return W4A16_ERR_INVALID_ARG;
     if (M < 1 || M > (1LL << 24) || !shape_ok(N, K, group)) return W4A16_ERR_INVALID_ARG;
+    if (M * K >= (1LL << 34)) return W4A16_ERR_INVALID_ARG;   // 32-bit activation indices (in 16-byte units)
     if (!aligned16(x) || !aligned16(qweight) || !aligned16(scales) || !aligned16(zeros) ||
         !aligned16(y))
         return W4A16_ERR_INVALID_ARG;
