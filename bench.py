@@ -74,10 +74,11 @@ def algorithmic_bytes(M, N, K, group):
     return N * K // 2 + 2 * G * N + G * N // 2 + 2 * M * K + 2 * M * N
 
 
-def kernel_kind(w4, M):
-    if M <= w4.gemv_max_m():
-        return "gemv"
-    return "skinny" if M <= 16 else "prefill"
+def kernel_kind(w4, M, N, K, group, dtype):
+    """Kernel w4a16_linear uses for this shape (as the library reports it)."""
+    import torch
+    k = w4.linear_kernel(M, N, K, group, torch.bfloat16 if dtype == "bf16" else torch.float16)
+    return {"gemv": "gemv", "small_batch": "skinny", "tiled": "prefill"}[k]
 
 
 def stored_traffic(workload, M, kind):
@@ -247,23 +248,38 @@ def main():
     gpu_ms_per_step = e0.elapsed_time(e1) / args.steps
     step_bytes, step_flops = sum(wk.bytes), sum(wk.flops)
 
-    # ---- the dominant kernel's own rate ----
+    # ---- the dominant kernel's own rate: the kernel with the most time in
+    # the step, its algorithmic bytes (or flops) over its launches' durations
     per_ms = wk.per_kernel_ms(max(1, args.steps // (wk.copies * 4)))
-    kernel_ms = float(sum(per_ms))
-    kind = kernel_kind(w4, M)
-    if kind == "prefill":
-        tf = step_flops / (kernel_ms * 1e-3) / 1e12
-        roof = {"bound": "mfma", "achieved": round(tf, 1), "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
-                "frac": round(tf / MFMA_BF16_PEAK_TFLOPS, 4)}
-    else:
-        gbs = step_bytes / (kernel_ms * 1e-3) / 1e9
-        roof = {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+    kinds = [kernel_kind(w4, M, m.N, m.K, wk.group, wk.dtype) for m in wk.mats]
+    by_kind = {}
+    for j, k in enumerate(kinds):
+        e = by_kind.setdefault(k, {"ms": 0.0, "bytes": 0, "flops": 0, "launches": 0})
+        e["ms"] += per_ms[j]
+        e["bytes"] += wk.bytes[j]
+        e["flops"] += wk.flops[j]
+        e["launches"] += 1
+    names = {"gemv": "gemv_kernel", "skinny": "skinny_kernel", "prefill": "prefill_kernel"}
+
+    def roofline(kind, e):
+        if kind == "prefill":
+            tf = e["flops"] / (e["ms"] * 1e-3) / 1e12
+            return {"bound": "mfma", "achieved": round(tf, 1), "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                    "frac": round(tf / MFMA_BF16_PEAK_TFLOPS, 4)}
+        gbs = e["bytes"] / (e["ms"] * 1e-3) / 1e9
+        return {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                 "frac": round(gbs / HBM_PEAK_GBS, 4)}
+
+    kind = max(by_kind, key=lambda k: by_kind[k]["ms"])
+    roof = roofline(kind, by_kind[kind])
     roof["traffic"] = stored_traffic(args.workload, M, kind)
-    roof["kernel"] = {"gemv": "gemv_kernel", "skinny": "skinny_kernel", "prefill": "prefill_kernel"}[kind]
+    roof["kernel"] = names[kind]
+    roof["launches_per_step"] = by_kind[kind]["launches"]
     roof["kernel_source_sha"] = kernel_source_hash(kind)
     roof["timing"] = "HIP events on the replay stream around back-to-back launches of one matrix"
-    roof["units_per_launch"] = {m.name: {"weights": m.N * m.K, "bytes": wk.bytes[j],
+    roof["by_kernel"] = {names[k]: dict(roofline(k, e), launches=e["launches"], us=round(e["ms"] * 1e3, 2))
+                         for k, e in by_kind.items()}
+    roof["units_per_launch"] = {m.name: {"kernel": names[kinds[j]], "weights": m.N * m.K, "bytes": wk.bytes[j],
                                          "kernel_us": round(per_ms[j] * 1e3, 2)}
                                 for j, m in enumerate(wk.mats)}
     del wk
@@ -275,7 +291,7 @@ def main():
         pk = Workload(WORKLOAD_IDS["prefill"], wl.WORKLOADS[WORKLOAD_IDS["prefill"]].ms[0], dev)
         pk.graphs(dev)
         pms = pk.per_kernel_ms(max(1, args.prefill_reps // pk.copies))
-        pkind = kernel_kind(w4, pk.M)
+        pkind = kernel_kind(w4, pk.M, pk.mats[0].N, pk.mats[0].K, pk.group, pk.dtype)
         tf = pk.flops[0] / (pms[0] * 1e-3) / 1e12
         prefill = {"workload": "prefill", "M": pk.M, "N": pk.mats[0].N, "K": pk.mats[0].K, "group": pk.group,
                    "dtype": pk.dtype, "kernel": "prefill_kernel" if pkind == "prefill" else pkind,

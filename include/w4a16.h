@@ -146,9 +146,10 @@ w4a16_status w4a16_gemv(const void *x, int32_t dtype, const void *qweight,
                         int64_t M, int64_t N, int64_t K, int32_t group,
                         void *workspace, size_t workspace_bytes, void *stream);
 
-/* Matrix-core GEMM for any M >= 1 (M*K < 2^34). M <= 16: the packed weights
+/* Matrix-core GEMM for any M >= 1 (M*K < 2^34). M <= 256: the packed weights
  * stream through registers as in the GEMV, and each unpacked dword feeds one
- * 16x16x32 MFMA (exact integers q - z, group scale on the fp32 sums). Larger M:
+ * 16x16x32 MFMA per 16-row tile of x (exact integers q - z, group scale on the
+ * fp32 sums; one workgroup per tile and group of row blocks). Larger M:
  * weight tiles are dequantised once per workgroup into LDS as 16-bit
  * s*(q - z) (one rounding) and fed to 32x32x16 MFMAs with fp32 accumulation
  * ("Weight-Only Quantisation", the FAQ answers on batch size: at prefill the
@@ -167,8 +168,14 @@ w4a16_status w4a16_linear(const void *x, int32_t dtype, const void *qweight,
                           int64_t M, int64_t N, int64_t K, int32_t group,
                           void *workspace, size_t workspace_bytes, void *stream);
 
-/* Largest M that w4a16_linear sends to the GEMV kernel. */
+/* Largest M that w4a16_linear may send to the GEMV kernel. */
 int32_t w4a16_gemv_max_m(void);
+
+/* The kernel w4a16_linear picks for this shape on the current device:
+ * 0 = decode GEMV, 1 = small-batch matrix-core kernel (M <= 256),
+ * 2 = tiled matrix-core GEMM; -1 for arguments w4a16_linear would reject.
+ * Host-only (queries the device's LDS size once). */
+int32_t w4a16_linear_kernel(int64_t M, int64_t N, int64_t K, int32_t group, int32_t dtype);
 
 #ifdef __cplusplus
 }

@@ -1,7 +1,8 @@
 """GPU parity of the matrix-core kernels (w4a16_gemm): the small-batch kernel
-(M <= 16, weights streamed through registers) and the LDS-tiled kernel
-(larger M, three tile shapes). Every output within 2e-3 * sum|x * w_hat| + 1e-5
-of the fp64 oracle, plus exact special cases."""
+(M <= 256, weights streamed through registers, x in 16-row tiles) and the
+LDS-tiled kernel (larger M, three tile shapes). Every output within
+2e-3 * sum|x * w_hat| + 1e-5 (+ the output rounding) of the fp64 oracle, plus
+exact special cases."""
 import numpy as np
 import pytest
 
@@ -24,8 +25,8 @@ def _gemm(x_bits, dtype, pw):
 # last 16-row block (N % 16 = 8) and N not a multiple of the 256-wide tile.
 SHAPES = [(8, 32, 32), (72, 160, 32), (200, 96, 32), (136, 256, 64), (264, 320, 64), (328, 640, 128),
           (1000, 1024, 64), (4104, 4096, 128), (520, 8192, 32)]
-SKINNY_M = [1, 2, 5, 16]
-TILED_M = [17, 37, 64, 100, 256, 300]
+SKINNY_M = [1, 2, 5, 16, 17, 37, 64, 100, 256]
+TILED_M = [257, 300, 520]
 
 
 def _small(N, K, group):
@@ -36,7 +37,7 @@ def _small(N, K, group):
 @pytest.mark.parametrize("dtype", ["f16", "bf16"])
 @pytest.mark.parametrize("M", SKINNY_M + TILED_M)
 def test_gemm_small_shapes(N, K, group, dtype, M):
-    if N * K >= 4096 * 4096 and M in (5, 17, 64, 256):
+    if N * K >= 4096 * 4096 and M in (5, 17, 64, 100, 256, 520):
         pytest.skip("covered by the other batch sizes at this shape")
     w, o, pw = _small(N, K, group)
     x = wl.random_activations(N * 31 + K + M, M, K, dtype)
@@ -46,7 +47,7 @@ def test_gemm_small_shapes(N, K, group, dtype, M):
 
 
 @pytest.mark.parametrize("dtype", ["f16", "bf16"])
-@pytest.mark.parametrize("M", [4, 40, 130])
+@pytest.mark.parametrize("M", [4, 40, 130, 300])
 @pytest.mark.parametrize("N,K,group", [(72, 256, 32), (264, 320, 64), (4104, 4096, 128)])
 def test_gemm_one_hot_is_exact(N, K, group, dtype, M):
     """Row m of x = e_{k_m} selects one dequantised weight per output:
@@ -115,10 +116,10 @@ def test_linear_dispatch_matches_kernels():
     import torch
     N, K, group = 1000, 1024, 64
     w, o, pw = _small(N, K, group)
-    for M in (1, 2, 3, 16, 17, 300):
+    for M in (1, 2, 3, 16, 17, 256, 257, 300):
         x = H.to_device_bits(wl.random_activations(M, M, K, "f16"), "f16")
         y = H.lib().linear(x, pw)
-        ref_fn = H.lib().gemv if M <= H.lib().gemv_max_m() else H.lib().gemm
+        ref_fn = H.lib().gemv if H.lib().linear_kernel(M, N, K, group) == "gemv" else H.lib().gemm
         torch.cuda.synchronize()
         assert torch.equal(y.view(torch.int16), ref_fn(x, pw).view(torch.int16)), M
 

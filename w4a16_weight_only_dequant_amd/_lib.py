@@ -37,6 +37,7 @@ _SIGS = {
     "w4a16_status_string": (ctypes.c_char_p, [ctypes.c_int]),
     "w4a16_layout_version": (ctypes.c_int, []),
     "w4a16_gemv_max_m": (_i32, []),
+    "w4a16_linear_kernel": (_i32, [_i64, _i64, _i64, _i32, _i32]),
     "w4a16_device_supported": (ctypes.c_int, [ctypes.c_int]),
     "w4a16_packed_bytes": (ctypes.c_int, [_i64, _i64, _i32, _szp, _szp, _szp]),
     "w4a16_workspace_bytes": (ctypes.c_int, [_i64, _i64, _i64, _i32, _szp]),
@@ -107,6 +108,17 @@ def device_supported(device: int = 0) -> bool:
 
 def gemv_max_m() -> int:
     return int(_lib.w4a16_gemv_max_m())
+
+
+LINEAR_KERNELS = ("gemv", "small_batch", "tiled")
+
+
+def linear_kernel(M: int, N: int, K: int, group: int, dtype=torch.float16) -> str:
+    """Name of the kernel w4a16_linear uses for this shape (needs a device)."""
+    code = int(_lib.w4a16_linear_kernel(M, N, K, group, W4A16_BF16 if dtype == torch.bfloat16 else W4A16_F16))
+    if code < 0:
+        raise ValueError("w4a16_linear rejects this shape")
+    return LINEAR_KERNELS[code]
 
 
 class PackedWeight:

@@ -27,10 +27,10 @@ int env_int(const char *name, int fallback) {
 }
 
 // Largest M routed to the GEMV kernel by w4a16_linear (the GEMV kernel itself
-// accepts M <= 8).
+// accepts M <= 8). Measured: from M = 2 on the matrix-core kernel is faster.
 int gemv_max_m() {
     static const int v = [] {
-        int m = env_int("W4A16_GEMV_MAX_M", 2);
+        int m = env_int("W4A16_GEMV_MAX_M", 1);
         return m < 0 ? 0 : (m > 8 ? 8 : m);
     }();
     return v;
@@ -120,6 +120,15 @@ bool gemv_fits(int64_t M, int64_t N, int64_t K, int32_t group, int32_t dtype) {
     return gemv_lds_bytes(M, K, dtype == W4A16_BF16, p.waves, group) + kGemvStaticLds <= max_lds_per_block();
 }
 
+// w4a16_linear's choice for M <= gemv_max_m(): the dot-product GEMV for
+// matrices of fewer than 768 row blocks of 16 (its workgroups then hide their
+// latency better), the matrix-core kernel (four row blocks per workgroup) for
+// wider ones; both measured on the decode shapes.
+bool prefer_gemv(int64_t M, int64_t N, int64_t K, int32_t group, int32_t dtype) {
+    return M >= 1 && M <= gemv_max_m() && ceil_div(N, kRowBlock) < 768 && shape_ok(N, K, group) &&
+           (dtype == W4A16_F16 || dtype == W4A16_BF16) && gemv_fits(M, N, K, group, dtype);
+}
+
 size_t gemm_need(int64_t M, int64_t N, int64_t K, int32_t group) {
     (void)M; (void)N; (void)K; (void)group;
     return 0;   // no kernel of this library needs scratch memory
@@ -143,6 +152,13 @@ const char *w4a16_status_string(int status) {
 int w4a16_layout_version(void) { return W4A16_LAYOUT_VERSION; }
 
 int32_t w4a16_gemv_max_m(void) { return gemv_max_m(); }
+
+int32_t w4a16_linear_kernel(int64_t M, int64_t N, int64_t K, int32_t group, int32_t dtype) {
+    if (M < 1 || M > (1LL << 24) || !shape_ok(N, K, group) || (dtype != W4A16_F16 && dtype != W4A16_BF16))
+        return -1;
+    if (prefer_gemv(M, N, K, group, dtype)) return 0;
+    return gemm_plan(M, N, K, group).kind == 0 ? 1 : 2;
+}
 
 w4a16_status w4a16_device_supported(int device) {
     if (device < 0) return W4A16_ERR_INVALID_ARG;
@@ -238,8 +254,7 @@ w4a16_status w4a16_gemm(const void *x, int32_t dtype, const void *qweight, const
 w4a16_status w4a16_linear(const void *x, int32_t dtype, const void *qweight, const void *scales,
                           const void *zeros, void *y, int64_t M, int64_t N, int64_t K, int32_t group,
                           void *workspace, size_t workspace_bytes, void *stream) {
-    if (M >= 1 && M <= gemv_max_m() && shape_ok(N, K, group) &&
-        (dtype == W4A16_F16 || dtype == W4A16_BF16) && gemv_fits(M, N, K, group, dtype))
+    if (prefer_gemv(M, N, K, group, dtype))
         return w4a16_gemv(x, dtype, qweight, scales, zeros, y, M, N, K, group, workspace,
                           workspace_bytes, stream);
     return w4a16_gemm(x, dtype, qweight, scales, zeros, y, M, N, K, group, workspace,

@@ -1,5 +1,5 @@
-// Matrix-core (MFMA) path of the W4A16 linear layer for small batches
-// (1 <= M <= 16): y[m][n] = sum_k x[m][k] * w_hat[n][k].
+// Matrix-core (MFMA) path of the W4A16 linear layer for small and medium
+// batches: y[m][n] = sum_k x[m][k] * w_hat[n][k], x taken 16 rows at a time.
 //
 // Up to a batch of a few dozen tokens the layer still reads every weight once
 // per call and does little arithmetic per byte, so it stays bound by the
@@ -51,7 +51,7 @@ __device__ inline f4_t mfma16x16x32(const uint4 &a, const uint4 &b, f4_t c) {
 template <int GROUP, int R, bool BF>
 __global__ __launch_bounds__(64 * kSkinnyMaxWaves) void skinny_kernel(
     const uint16_t *__restrict__ x, const uint4 *__restrict__ qw, const uint16_t *__restrict__ scales,
-    const uint32_t *__restrict__ zeros, uint16_t *__restrict__ y, int M, int N, int K) {
+    const uint32_t *__restrict__ zeros, uint16_t *__restrict__ y, int M, int N, int K, int mtiles) {
     constexpr int CPG = GROUP / kChunk;    // chunks per group (1, 2, 4)
     constexpr int GPC = kColumn / GROUP;   // groups per column (4, 2, 1)
     constexpr int PF = R == 1 ? 4 : (R == 2 ? 3 : 2);   // columns in flight ahead of the one computing
@@ -64,6 +64,14 @@ __global__ __launch_bounds__(64 * kSkinnyMaxWaves) void skinny_kernel(
     const int s = lane >> 4;
     const int nblocks = (N + kRowBlock - 1) / kRowBlock;
     const Slice sl = wave_slice<GROUP>(K, wave, waves);
+    // workgroup = (group of R row blocks, 16-row tile of x); the x tiles of one
+    // weight group are neighbours in launch order, so they share its stream
+    // through the caches
+    const int mtile = blockIdx.x % mtiles;
+    const int wg = blockIdx.x / mtiles;
+    const int M_loc = min(16, M - 16 * mtile);
+    x += (size_t)16 * mtile * K;
+    y += (size_t)16 * mtile * N;
 
     // per row block i of this workgroup: packed base, lane record, metadata
     // row; a workgroup past the last block repeats the last one (not stored)
@@ -74,7 +82,7 @@ __global__ __launch_bounds__(64 * kSkinnyMaxWaves) void skinny_kernel(
     int zshift[R];
 #pragma unroll
     for (int i = 0; i < R; ++i) {
-        const int b = min(blockIdx.x * R + i, nblocks - 1);
+        const int b = min(wg * R + i, nblocks - 1);
         const int rows = min(kRowBlock, N - b * kRowBlock);
         const int rl = r < rows ? r : r - rows;   // lanes past a short block re-read a valid row
         qw_b[i] = qw + (size_t)b * (K / 2);
@@ -87,7 +95,7 @@ __global__ __launch_bounds__(64 * kSkinnyMaxWaves) void skinny_kernel(
     }
     // A operand rows: lane row r, clamped to the last real row of x (rows of
     // the 16-row tile past M produce outputs that are never stored)
-    const uint4 *xrow = reinterpret_cast<const uint4 *>(x) + (size_t)min(r, M - 1) * (K / 8) + s;
+    const uint4 *xrow = reinterpret_cast<const uint4 *>(x) + (size_t)min(r, M_loc - 1) * (K / 8) + s;
     const UnpackConsts uc = unpack_consts();
     const uint4 ones = make_uint4(0x3F803F80u, 0x3F803F80u, 0x3F803F80u, 0x3F803F80u);   // bf16 1.0
 
@@ -200,8 +208,8 @@ __global__ __launch_bounds__(64 * kSkinnyMaxWaves) void skinny_kernel(
     __syncthreads();
     for (int o = threadIdx.x; o < R * 256; o += blockDim.x) {
         const int i = o / 256, m = (o / 16) % 16, rr = o % 16;
-        const int b = blockIdx.x * R + i;
-        if (b >= nblocks || m >= M) continue;
+        const int b = wg * R + i;
+        if (b >= nblocks || m >= M_loc) continue;
         const int rows = min(kRowBlock, N - b * kRowBlock);
         if (rr >= rows) continue;
         const int src = 16 * (m / 4) + rr, v = m % 4;
@@ -217,10 +225,11 @@ hipError_t launch_skinny(const void *x, const void *qw, const void *sc, const vo
     const int nblocks = (int)ceil_div(N, kRowBlock);
     const dim3 block(64 * plan.waves);
     auto args = [&](auto kern, int R) {
-        hipLaunchKernelGGL(kern, dim3((unsigned)ceil_div(nblocks, R)), block, 0, stream,
+        const int mtiles = (int)ceil_div(M, 16);
+        hipLaunchKernelGGL(kern, dim3((unsigned)(ceil_div(nblocks, R) * mtiles)), block, 0, stream,
                            reinterpret_cast<const uint16_t *>(x), reinterpret_cast<const uint4 *>(qw),
                            reinterpret_cast<const uint16_t *>(sc), reinterpret_cast<const uint32_t *>(zp),
-                           reinterpret_cast<uint16_t *>(y), M, N, K);
+                           reinterpret_cast<uint16_t *>(y), M, N, K, mtiles);
     };
     switch (plan.rows_per_wg) {
         case 1: args(skinny_kernel<GROUP, 1, BF>, 1); break;
@@ -241,28 +250,32 @@ GemmPlan gemm_plan(int64_t M, int64_t N, int64_t K, int32_t group) {
         const char *v = getenv("W4A16_SKINNY_R");
         return v ? atoi(v) : 0;
     }();
+    static const int skinny_max = [] {
+        const char *v = getenv("W4A16_SKINNY_MAX_M");
+        return v ? atoi(v) : kSkinnyMaxM;
+    }();
     GemmPlan p{};
-    if (M <= kSkinnyMaxM) {
+    if (M <= skinny_max) {
         p.kind = 0;
         const int64_t columns = ceil_div(K / kChunk, kColChunks);
         int64_t w = 4;
-        if (columns > 4 * 32) w = ceil_div(columns, 32);
+        if (columns > 4 * 64) w = ceil_div(columns, 64);
         if (w > columns) w = columns;
         if (forced_waves > 0) w = forced_waves;
-        // four 16-row blocks per workgroup share each activation fragment
-        // (measured best at group 128 / 64); at group 32 the extra metadata
-        // registers of four blocks spill, two is the measured best there
-        int rpw = group >= 64 ? 4 : 2;
+        // row blocks per workgroup: more share each activation fragment, fewer
+        // make more workgroups; measured best: four for wide matrices (>= 768
+        // blocks; at group 32 four spill), two from 320 blocks, else one
+        const int64_t nblocks = ceil_div(N, kRowBlock);
+        int rpw = (nblocks >= 768 && group >= 64) ? 4 : (nblocks >= 320 ? 2 : 1);
         if (forced_r == 1 || forced_r == 2 || forced_r == 4) rpw = forced_r;
         if (w > kSkinnyMaxWaves) w = kSkinnyMaxWaves;
         if (w < 1) w = 1;
         p.waves = (int)w;
         p.rows_per_wg = rpw;
-        (void)N;
         return p;
     }
     p.kind = 1;
-    p.tile = prefill_tile(M);
+    p.tile = prefill_tile(M, N);
     return p;
 }
 

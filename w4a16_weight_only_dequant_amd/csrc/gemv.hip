@@ -322,10 +322,11 @@ GemvPlan gemv_plan(int64_t M, int64_t N, int64_t K, int32_t group) {
     GemvPlan p{};
     p.row_blocks = (int)ceil_div(N, kRowBlock);
     const int64_t columns = ceil_div(K / kChunk, kColChunks);
-    // four waves per workgroup measured best for the decode shapes; more when
-    // the slices would be long (large K), never more waves than columns
+    // four waves per workgroup measured best for the decode shapes, also for
+    // K = 28672 (56 columns per wave); more only for still longer K, never
+    // more waves than columns
     int64_t w = 4;
-    if (columns > 4 * 32) w = ceil_div(columns, 32);
+    if (columns > 4 * 64) w = ceil_div(columns, 64);
     if (w > columns) w = columns;
     if (forced_waves > 0) w = forced_waves;
     if (w > kMaxWaves) w = kMaxWaves;

@@ -348,15 +348,29 @@ hipError_t launch_group(int tile, const void *x, const void *qw, const void *sc,
 
 }  // namespace
 
-int prefill_tile(int64_t M) {
+int prefill_tile(int64_t M, int64_t N) {
     static const int forced = [] {
         const char *v = getenv("W4A16_PREFILL_TILE");
         return v ? atoi(v) : -1;
     }();
     if (forced >= 0 && forced <= kTile256x256) return forced;
-    if (M <= 64) return kTile64x256;
-    if (M <= 128) return kTile128x256;
-    return kTile256x256;
+    // time ~ rounds of workgroups over the 256 CUs x time of one tile; the
+    // relative tile times (0.62, 0.67, 1.0 for 64, 128, 256 rows) were
+    // measured at K = 5120
+    static const int rows[3] = {64, 128, 256};
+    static const double tile_time[3] = {0.62, 0.67, 1.0};
+    const int64_t n_tiles = ceil_div(N, 256);
+    int best = kTile256x256;
+    double best_cost = 1e300;
+    for (int t = 0; t < 3; ++t) {
+        const int64_t tiles = ceil_div(M, rows[t]) * n_tiles;
+        const double cost = (double)ceil_div(tiles, 256) * tile_time[t];
+        if (cost < best_cost - 1e-9) {
+            best_cost = cost;
+            best = t;
+        }
+    }
+    return best;
 }
 
 hipError_t launch_prefill(const void *x, bool bf16, const void *qweight, const void *scales, const void *zeros,

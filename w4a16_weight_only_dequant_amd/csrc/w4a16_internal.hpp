@@ -54,9 +54,9 @@ int gemv_xcols(int64_t K, int waves);
 constexpr size_t kGemvStaticLds = 16 * 8 * 16 * sizeof(float);
 
 // Plan for the matrix-core kernels: kind 0 streams the weights through
-// registers for M <= kSkinnyMaxM (one 16-row MFMA tile of activations),
-// kind 1 is the LDS-tiled GEMM for everything larger.
-constexpr int kSkinnyMaxM = 16;
+// registers for M <= kSkinnyMaxM (16-row MFMA tiles of activations, one per
+// workgroup), kind 1 is the LDS-tiled GEMM for everything larger.
+constexpr int kSkinnyMaxM = 256;   // measured crossover to the tiled kernel
 enum { kTile64x256 = 0, kTile128x256 = 1, kTile256x256 = 2 };
 struct GemmPlan {
     int kind;          // 0 = skinny, 1 = tiled
@@ -81,7 +81,7 @@ hipError_t launch_gemm(const void *x, bool bf16, const void *qweight, const void
 hipError_t launch_prefill(const void *x, bool bf16, const void *qweight, const void *scales,
                           const void *zeros, void *y, int M, int N, int K, int group,
                           const GemmPlan &plan, hipStream_t stream);
-int prefill_tile(int64_t M);
+int prefill_tile(int64_t M, int64_t N);
 
 __device__ inline uint16_t f32_to_f16_bits(float v) {
     _Float16 h = (_Float16)v;
