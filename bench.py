@@ -17,7 +17,9 @@ Prints one JSON line. `value` is achieved HBM GB/s of the headline step
 outputs written -- over wall time per step). `roofline` is the decode GEMV
 kernel's own rate: algorithmic bytes of its launches over their average
 duration from HIP events on the launch stream. `prefill` carries the M = 2048
-GEMM's TFLOP/s against the dense bf16 MFMA peak. `cpu_baseline` times the CPU
+GEMM's TFLOP/s against the dense bf16 MFMA peak. `grouped_step` times the same
+seven layers with q/k/v and gate/up each in one launch (w4a16_linear_group);
+`value` stays the seven-launch step. `cpu_baseline` times the CPU
 oracle (dequantise + fp64 product) on a bounded sample of the headline workload.
 """
 from __future__ import annotations
@@ -53,7 +55,7 @@ def parse():
     p.add_argument("--workload", default="decode_13b_layer", choices=list(WORKLOAD_IDS))
     p.add_argument("--m", type=int, default=0, help="batch rows (default: the workload's first M)")
     p.add_argument("--no-prefill", action="store_true", help="skip the M=2048 prefill leg")
-    p.add_argument("--prefill-reps", type=int, default=20)
+    p.add_argument("--prefill-reps", type=int, default=60)
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-seconds", type=float, default=15.0)
     p.add_argument("--copy-calibration", action="store_true",
@@ -132,6 +134,39 @@ class Workload:
     def step(self, c):
         for j in range(len(self.mats)):
             self.launch(c, j)
+
+    def step_grouped(self, c, groups):
+        """One step with the layers of each group in one launch."""
+        for g in groups:
+            if len(g) == 1:
+                self.launch(c, g[0])
+            else:
+                self.w4.linear_group([self.xs[j] for j in g], [self.sets[c][j] for j in g],
+                                     outs=[self.ys[j] for j in g], workspace=self.ws)
+
+    def time_grouped(self, dev, groups, steps, warmup):
+        """Wall time per step of the grouped step (one HIP graph per weight copy)."""
+        torch = self.torch
+        for c in range(min(2, self.copies)):
+            self.step_grouped(c, groups)
+        torch.cuda.synchronize()
+        cap = torch.cuda.Stream(device=dev)
+        graphs = []
+        with torch.cuda.stream(cap):
+            for c in range(self.copies):
+                g = torch.cuda.CUDAGraph()
+                with torch.cuda.graph(g, stream=cap):
+                    self.step_grouped(c, groups)
+                graphs.append(g)
+        torch.cuda.synchronize()
+        for i in range(warmup):
+            graphs[i % self.copies].replay()
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for i in range(steps):
+            graphs[i % self.copies].replay()
+        torch.cuda.synchronize()
+        return (time.perf_counter() - t0) * 1e3 / steps
 
     def graphs(self, dev):
         """One graph per weight copy holding one step; one graph per matrix
@@ -282,6 +317,19 @@ def main():
     roof["units_per_launch"] = {m.name: {"kernel": names[kinds[j]], "weights": m.N * m.K, "bytes": wk.bytes[j],
                                          "kernel_us": round(per_ms[j] * 1e3, 2)}
                                 for j, m in enumerate(wk.mats)}
+    # ---- the same step with the independent layers of one token grouped in
+    # one launch each (w4a16_linear_group): q, k, v share their input in a
+    # model, so do gate and up; o and down each follow a dependency
+    grouped = None
+    if args.workload == "decode_13b_layer":
+        names_idx = {m.name: j for j, m in enumerate(wk.mats)}
+        groups = [[names_idx[n] for n in g] for g in (("q", "k", "v"), ("o",), ("up", "gate"), ("down",))]
+        g_ms = wk.time_grouped(dev, groups, args.steps, args.warmup)
+        g_val = step_bytes / (g_ms * 1e-3) / 1e9
+        grouped = {"ms_per_step": round(g_ms, 5), "value": round(g_val, 1), "unit": "GB/s",
+                   "pct_hbm_peak": round(g_val / HBM_PEAK_GBS * 100, 2), "launches_per_step": len(groups),
+                   "groups": [[wk.mats[j].name for j in g] for g in groups],
+                   "tokens_per_s": round(M / (g_ms * 1e-3), 1)}
     del wk
     torch.cuda.empty_cache()
 
@@ -339,6 +387,7 @@ def main():
         "pct_hbm_peak": round(value / HBM_PEAK_GBS * 100, 2),
         "tokens_per_s": round(M / (ms_per_step * 1e-3), 1),
         "roofline": roof,
+        "grouped_step": grouped,
         "prefill": prefill,
         "cpu_baseline": cpu,
     }

@@ -168,6 +168,25 @@ w4a16_status w4a16_linear(const void *x, int32_t dtype, const void *qweight,
                           int64_t M, int64_t N, int64_t K, int32_t group,
                           void *workspace, size_t workspace_bytes, void *stream);
 
+/* Several independent linear layers of the same M, K, group and activation
+ * type in one launch: y[p] = x[p] . w_hat[p]^T for p < count (1..8), problem p
+ * with N[p] output rows. The arrays x, qweight, scales, zeros, y and N are
+ * host arrays of `count` entries (device pointers / sizes); x[p] may be the
+ * same pointer for several p (q/k/v or gate/up of one token batch). Every
+ * problem must pass w4a16_linear's checks, and no y[p] may overlap any buffer
+ * of any problem. For M <= 256 all problems run in one launch of the
+ * small-batch matrix-core kernel, which pays the fixed cost of a launch (the
+ * ramp-up and drain that dominate small decode layers) once; for larger M it
+ * enqueues one tiled GEMM per problem. Results are bit-identical to
+ * w4a16_gemm on each problem. This fuses the launches, not the math: the
+ * pages' dual-output decode variant ("Quantization Is Not a Zip File", section
+ * 2, paired gate/up projections) is the special case of two problems sharing x. */
+w4a16_status w4a16_linear_group(int32_t count, const void *const *x, int32_t dtype,
+                                const void *const *qweight, const void *const *scales,
+                                const void *const *zeros, void *const *y, int64_t M,
+                                const int64_t *N, int64_t K, int32_t group,
+                                void *workspace, size_t workspace_bytes, void *stream);
+
 /* Largest M that w4a16_linear may send to the GEMV kernel. */
 int32_t w4a16_gemv_max_m(void);
 

@@ -90,6 +90,29 @@ def test_compute_calls_validate_before_device(w4):
     assert lib.w4a16_workspace_bytes(0, 64, 128, 128, ctypes.byref(ws)) == 1
 
 
+def test_grouped_call_validates_before_device(w4):
+    lib = w4.raw()
+
+
+    def arr(*v):
+        return (ctypes.c_void_p * len(v))(*v)
+
+    a, b, c, d = (1 << 20), (1 << 24), (1 << 28), (1 << 32)
+    ok_y = arr(1 << 36, 1 << 37)
+    Ns = (ctypes.c_int64 * 2)(64, 64)
+    args = lambda count, x, y, N, M=1: (count, x, 0, arr(b, b + (1 << 22)), arr(c, c + (1 << 22)),  # noqa: E731
+                                        arr(d, d + (1 << 22)), y, M, N, 128, 128, None, 0, None)
+    # count out of range
+    assert lib.w4a16_linear_group(*args(0, arr(a, a), ok_y, Ns)) == 1
+    assert lib.w4a16_linear_group(*args(9, arr(a, a), ok_y, Ns)) == 1
+    # one problem with a bad N
+    assert lib.w4a16_linear_group(*args(2, arr(a, a), ok_y, (ctypes.c_int64 * 2)(64, 60))) == 1
+    # the output of problem 1 overlapping the activations of problem 0
+    assert lib.w4a16_linear_group(*args(2, arr(a, a + (1 << 22)), arr(1 << 36, a), Ns)) == 1
+    # NULL arrays
+    assert lib.w4a16_linear_group(2, None, 0, None, None, None, None, 1, Ns, 128, 128, None, 0, None) == 1
+
+
 def test_missing_workspace_reported(w4):
     lib = w4.raw()
     shapes = [(M, N, K, g) for M in (1, 4, 16, 64, 256) for (N, K, g) in

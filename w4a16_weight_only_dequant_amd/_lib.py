@@ -32,6 +32,8 @@ _i32 = ctypes.c_int32
 _sz = ctypes.c_size_t
 _vp = ctypes.c_void_p
 _szp = ctypes.POINTER(ctypes.c_size_t)
+_vpp = ctypes.POINTER(ctypes.c_void_p)
+_i64p = ctypes.POINTER(ctypes.c_int64)
 
 _SIGS = {
     "w4a16_status_string": (ctypes.c_char_p, [ctypes.c_int]),
@@ -46,6 +48,8 @@ _SIGS = {
     "w4a16_gemv": (ctypes.c_int, [_vp, _i32, _vp, _vp, _vp, _vp, _i64, _i64, _i64, _i32, _vp, _sz, _vp]),
     "w4a16_gemm": (ctypes.c_int, [_vp, _i32, _vp, _vp, _vp, _vp, _i64, _i64, _i64, _i32, _vp, _sz, _vp]),
     "w4a16_linear": (ctypes.c_int, [_vp, _i32, _vp, _vp, _vp, _vp, _i64, _i64, _i64, _i32, _vp, _sz, _vp]),
+    "w4a16_linear_group": (ctypes.c_int, [_i32, _vpp, _i32, _vpp, _vpp, _vpp, _vpp, _i64, _i64p, _i64, _i32,
+                                          _vp, _sz, _vp]),
 }
 
 EXPORTED = tuple(_SIGS)
@@ -219,6 +223,34 @@ def gemv(x, pw, out=None, workspace=None, stream=None):
 def gemm(x, pw, out=None, workspace=None, stream=None):
     """MFMA GEMM (any M): y = x @ w_hat^T."""
     return _call("w4a16_gemm", x, pw, out, workspace, stream)
+
+
+def linear_group(xs, pws, outs=None, workspace=None, stream=None):
+    """Several layers of the same M, K, group and type in one launch (w4a16_linear_group).
+
+    xs: list of CUDA tensors [M][K] (entries may be the same tensor); pws: list of
+    PackedWeight; returns the list of outputs [M][N_p]."""
+    count = len(pws)
+    if count != len(xs) or count < 1:
+        raise ValueError("need one x per packed weight")
+    xs = [x.contiguous() for x in xs]
+    M, K, group = xs[0].shape[0], pws[0].K, pws[0].group
+    for x, pw in zip(xs, pws):
+        if x.dim() != 2 or not x.is_cuda or x.shape != (M, K) or x.dtype != xs[0].dtype:
+            raise ValueError("every x must be a CUDA tensor [M][K] of one type")
+        if pw.K != K or pw.group != group:
+            raise ValueError("every weight must share K and group")
+    ys = outs if outs is not None else [torch.empty((M, pw.N), dtype=xs[0].dtype, device=xs[0].device)
+                                        for pw in pws]
+    arr = lambda vals: (ctypes.c_void_p * count)(*vals)  # noqa: E731
+    nbytes = workspace_bytes(M, max(pw.N for pw in pws), K, group)
+    ws = (workspace or _default_workspace(xs[0].device)).get(nbytes)
+    _check("w4a16_linear_group", _lib.w4a16_linear_group(
+        count, arr([x.data_ptr() for x in xs]), _dtype_code(xs[0]), arr([p.qweight.data_ptr() for p in pws]),
+        arr([p.scales.data_ptr() for p in pws]), arr([p.zeros.data_ptr() for p in pws]),
+        arr([y.data_ptr() for y in ys]), M, (ctypes.c_int64 * count)(*[p.N for p in pws]), K, group,
+        ws.data_ptr() if ws is not None else None, ws.numel() if ws is not None else 0, _stream_ptr(stream)))
+    return ys
 
 
 def linear(x, pw, out=None, workspace=None, stream=None):

@@ -251,6 +251,58 @@ w4a16_status w4a16_gemm(const void *x, int32_t dtype, const void *qweight, const
     return e == hipSuccess ? W4A16_OK : W4A16_ERR_HIP;
 }
 
+w4a16_status w4a16_linear_group(int32_t count, const void *const *x, int32_t dtype, const void *const *qweight,
+                                const void *const *scales, const void *const *zeros, void *const *y, int64_t M,
+                                const int64_t *N, int64_t K, int32_t group, void *workspace,
+                                size_t workspace_bytes, void *stream) {
+    if (count < 1 || count > kMaxGroup || !x || !qweight || !scales || !zeros || !y || !N)
+        return W4A16_ERR_INVALID_ARG;
+    int64_t n_total = 0;
+    for (int p = 0; p < count; ++p) {
+        const w4a16_status st = check_linear(x[p], dtype, qweight[p], scales[p], zeros[p], y[p], M, N[p], K,
+                                             group, workspace, workspace_bytes, 0);
+        if (st != W4A16_OK) return st;
+        n_total += N[p];
+    }
+    // no output may overlap any other problem's buffers either
+    for (int p = 0; p < count; ++p) {
+        const Range ry = range_of(y[p], (size_t)(M * N[p] * 2));
+        for (int q = 0; q < count; ++q) {
+            if (q == p) continue;
+            size_t qb, sb, zb;
+            meta_bytes(N[q], K, group, &qb, &sb, &zb);
+            if (overlap(ry, range_of(x[q], (size_t)(M * K * 2))) || overlap(ry, range_of(qweight[q], qb)) ||
+                overlap(ry, range_of(scales[q], sb)) || overlap(ry, range_of(zeros[q], zb)) ||
+                overlap(ry, range_of(y[q], (size_t)(M * N[q] * 2))))
+                return W4A16_ERR_INVALID_ARG;
+        }
+    }
+    w4a16_status st = check_device();
+    if (st != W4A16_OK) return st;
+    const GemmPlan plan = gemm_plan(M, n_total, K, group);
+    if (plan.kind != 0) {   // large M: one tiled launch per problem
+        for (int p = 0; p < count; ++p) {
+            st = w4a16_gemm(x[p], dtype, qweight[p], scales[p], zeros[p], y[p], M, N[p], K, group, workspace,
+                            workspace_bytes, stream);
+            if (st != W4A16_OK) return st;
+        }
+        return W4A16_OK;
+    }
+    GroupTable tab{};
+    tab.count = count;
+    for (int p = 0; p < count; ++p) {
+        tab.x[p] = x[p];
+        tab.qweight[p] = qweight[p];
+        tab.scales[p] = scales[p];
+        tab.zeros[p] = zeros[p];
+        tab.y[p] = y[p];
+        tab.N[p] = (int)N[p];
+    }
+    hipError_t e = launch_gemm_group(tab, dtype == W4A16_BF16, (int)M, (int)K, group, plan,
+                                     reinterpret_cast<hipStream_t>(stream));
+    return e == hipSuccess ? W4A16_OK : W4A16_ERR_HIP;
+}
+
 w4a16_status w4a16_linear(const void *x, int32_t dtype, const void *qweight, const void *scales,
                           const void *zeros, void *y, int64_t M, int64_t N, int64_t K, int32_t group,
                           void *workspace, size_t workspace_bytes, void *stream) {

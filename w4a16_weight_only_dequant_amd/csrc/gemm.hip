@@ -48,10 +48,12 @@ __device__ inline f4_t mfma16x16x32(const uint4 &a, const uint4 &b, f4_t c) {
                                                        c, 0, 0, 0);
 }
 
+// The body of one workgroup; `id` is its index within its problem.
 template <int GROUP, int R, bool BF>
-__global__ __launch_bounds__(64 * kSkinnyMaxWaves) void skinny_kernel(
-    const uint16_t *__restrict__ x, const uint4 *__restrict__ qw, const uint16_t *__restrict__ scales,
-    const uint32_t *__restrict__ zeros, uint16_t *__restrict__ y, int M, int N, int K, int mtiles) {
+__device__ __forceinline__ void skinny_body(const uint16_t *__restrict__ x, const uint4 *__restrict__ qw,
+                                            const uint16_t *__restrict__ scales,
+                                            const uint32_t *__restrict__ zeros, uint16_t *__restrict__ y,
+                                            int M, int N, int K, int mtiles, int id) {
     constexpr int CPG = GROUP / kChunk;    // chunks per group (1, 2, 4)
     constexpr int GPC = kColumn / GROUP;   // groups per column (4, 2, 1)
     constexpr int PF = R == 1 ? 4 : (R == 2 ? 3 : 2);   // columns in flight ahead of the one computing
@@ -67,8 +69,8 @@ __global__ __launch_bounds__(64 * kSkinnyMaxWaves) void skinny_kernel(
     // workgroup = (group of R row blocks, 16-row tile of x); the x tiles of one
     // weight group are neighbours in launch order, so they share its stream
     // through the caches
-    const int mtile = blockIdx.x % mtiles;
-    const int wg = blockIdx.x / mtiles;
+    const int mtile = id % mtiles;
+    const int wg = id / mtiles;
     const int M_loc = min(16, M - 16 * mtile);
     x += (size_t)16 * mtile * K;
     y += (size_t)16 * mtile * N;
@@ -219,6 +221,47 @@ __global__ __launch_bounds__(64 * kSkinnyMaxWaves) void skinny_kernel(
     }
 }
 
+template <int GROUP, int R, bool BF>
+__global__ __launch_bounds__(64 * kSkinnyMaxWaves) void skinny_kernel(
+    const uint16_t *__restrict__ x, const uint4 *__restrict__ qw, const uint16_t *__restrict__ scales,
+    const uint32_t *__restrict__ zeros, uint16_t *__restrict__ y, int M, int N, int K, int mtiles) {
+    skinny_body<GROUP, R, BF>(x, qw, scales, zeros, y, M, N, K, mtiles, blockIdx.x);
+}
+
+// Several independent problems (same M, K, group and type) in one launch:
+// workgroups [first[p], first[p+1]) belong to problem p.
+template <int GROUP, int R, bool BF>
+__global__ __launch_bounds__(64 * kSkinnyMaxWaves) void skinny_group_kernel(GroupTable tab, int M, int K,
+                                                                            int mtiles) {
+    int p = 0;
+    while (p + 1 < tab.count && (int)blockIdx.x >= tab.first[p + 1]) ++p;   // uniform
+    skinny_body<GROUP, R, BF>(reinterpret_cast<const uint16_t *>(tab.x[p]),
+                              reinterpret_cast<const uint4 *>(tab.qweight[p]),
+                              reinterpret_cast<const uint16_t *>(tab.scales[p]),
+                              reinterpret_cast<const uint32_t *>(tab.zeros[p]),
+                              reinterpret_cast<uint16_t *>(tab.y[p]), M, tab.N[p], K, mtiles,
+                              (int)blockIdx.x - tab.first[p]);
+}
+
+template <int GROUP, bool BF>
+hipError_t launch_skinny_group(GroupTable tab, int M, int K, const GemmPlan &plan, hipStream_t stream) {
+    const int mtiles = (int)ceil_div(M, 16);
+    const int R = plan.rows_per_wg;
+    int total = 0;
+    for (int p = 0; p < tab.count; ++p) {
+        tab.first[p] = total;
+        total += (int)ceil_div(ceil_div(tab.N[p], kRowBlock), R) * mtiles;
+    }
+    tab.first[tab.count] = total;
+    const dim3 grid((unsigned)total), block(64 * plan.waves);
+    switch (R) {
+        case 1: hipLaunchKernelGGL((skinny_group_kernel<GROUP, 1, BF>), grid, block, 0, stream, tab, M, K, mtiles); break;
+        case 2: hipLaunchKernelGGL((skinny_group_kernel<GROUP, 2, BF>), grid, block, 0, stream, tab, M, K, mtiles); break;
+        default: hipLaunchKernelGGL((skinny_group_kernel<GROUP, 4, BF>), grid, block, 0, stream, tab, M, K, mtiles); break;
+    }
+    return hipGetLastError();
+}
+
 template <int GROUP, bool BF>
 hipError_t launch_skinny(const void *x, const void *qw, const void *sc, const void *zp, void *y, int M, int N,
                          int K, const GemmPlan &plan, hipStream_t stream) {
@@ -293,6 +336,22 @@ hipError_t launch_gemm(const void *x, bool bf16, const void *qweight, const void
         case 32: return launch_skinny<32, false>(x, qweight, scales, zeros, y, M, N, K, plan, stream);
         case 64: return launch_skinny<64, false>(x, qweight, scales, zeros, y, M, N, K, plan, stream);
         default: return launch_skinny<128, false>(x, qweight, scales, zeros, y, M, N, K, plan, stream);
+    }
+}
+
+hipError_t launch_gemm_group(const GroupTable &tab, bool bf16, int M, int K, int group, const GemmPlan &plan,
+                             hipStream_t stream) {
+    if (bf16) {
+        switch (group) {
+            case 32: return launch_skinny_group<32, true>(tab, M, K, plan, stream);
+            case 64: return launch_skinny_group<64, true>(tab, M, K, plan, stream);
+            default: return launch_skinny_group<128, true>(tab, M, K, plan, stream);
+        }
+    }
+    switch (group) {
+        case 32: return launch_skinny_group<32, false>(tab, M, K, plan, stream);
+        case 64: return launch_skinny_group<64, false>(tab, M, K, plan, stream);
+        default: return launch_skinny_group<128, false>(tab, M, K, plan, stream);
     }
 }
 

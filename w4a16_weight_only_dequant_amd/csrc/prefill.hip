@@ -12,14 +12,15 @@
 // 16-bit values right before the multiply).
 //
 // Tiling (gfx950, wave64): a workgroup computes a BM x BN tile of y with
-// WM x WN waves, each owning a (BM/WM) x (BN/WN) sub-tile as 32x32 blocks of
+// WM x WN waves (4, or 8 for the 256 x 256 tile: two per SIMD), each owning a
+// (BM/WM) x (BN/WN) sub-tile as 32x32 blocks of
 // v_mfma_f32_32x32x16 accumulators (fp32). K advances in steps of 64 through
 // two LDS buffers: while the waves multiply out of one buffer they write the
 // next step's activations and dequantised weights into the other, and the
 // global loads for the step after that are already in flight. Both LDS tiles
 // are [row][64 k] 16-bit with the eight 16-byte units of a row XOR-swizzled
-// by (row % 8), so the MFMA operand reads (32 rows, same k) and the tile
-// writes are free of bank conflicts. The packed weights arrive one 128-weight
+// (swz below), so the MFMA operand reads (32 rows, same k) and the tile writes
+// are free of bank conflicts. The packed weights arrive one 128-weight
 // column at a time (16-byte records, one KiB per 16 rows) and serve two steps.
 #include <stdlib.h>
 
@@ -58,19 +59,32 @@ __device__ inline f16_t mfma32x32x16(const uint4 &a, const uint4 &b, f16_t c) {
 __device__ inline int swz(int row, int unit) { return row * kUnits + (unit ^ (row & 7) ^ ((row >> 3) & 1)); }
 
 // One dword of codes (k = 0..7 of a slice, even k in the low half-word) ->
-// eight bf16 values s*(q - z) in k order. (q - z) is exact, s*(q - z) is exact
-// in fp32 (11 + 5 significant bits) and is rounded once, to nearest even.
-// The byte mask lives in a register so that the compiler keeps the two masked
-// words and converts their bytes directly (v_cvt_f32_ubyte0..3).
-__device__ inline uint4 dequant_bf16(uint32_t d, float s, float nsz, uint32_t byte_mask) {
-    const uint32_t lo = d & byte_mask;          // bytes: k0 k4 k1 k5
-    const uint32_t hi = (d >> 4) & byte_mask;   // bytes: k2 k6 k3 k7
-    auto f = [&](uint32_t w, int byte) { return fmaf(s, (float)((w >> (8 * byte)) & 0xFFu), nsz); };
+// eight bf16 values s*(q - z) in k order. The magic-number unpack gives the
+// exact fp16 values 1024 + q (low nibble of a byte) and 1024 + 16 q (high
+// nibble); one fma with an fp16 operand (v_fma_mix_f32) then forms
+// s*(1024+q) - s*(1024+z) = s*(q - z), or (s/16)*(1024+16q) - s*(64+z), where
+// every product and both constants are exact in fp32 (at most 22 significant
+// bits), so the fma returns s*(q - z) exactly (15 significant bits at most) and
+// the conversion to bf16 is its one rounding, to nearest even.
+struct DequantBf16 {
+    float s, c_lo, s16, c_hi;   // s, -s*(1024+z), s/16, -s*(64+z)
+};
+__device__ inline DequantBf16 dequant_bf16_consts(float s, uint32_t z) {
+    return DequantBf16{s, -s * (float)(1024u + z), s * 0.0625f, -s * (float)(64u + z)};
+}
+__device__ inline uint4 dequant_bf16(uint32_t d, const DequantBf16 &c, const UnpackConsts &uc) {
+    const uint32_t d8 = d >> 8;
+    const half2_t h0 = __builtin_bit_cast(half2_t, and_or(d, uc.lo_mask, uc.f16_magic));    // k0, k1
+    const half2_t h1 = __builtin_bit_cast(half2_t, and_or(d, uc.hi_mask, uc.f16_magic));    // k2, k3 (x16)
+    const half2_t h2 = __builtin_bit_cast(half2_t, and_or(d8, uc.lo_mask, uc.f16_magic));   // k4, k5
+    const half2_t h3 = __builtin_bit_cast(half2_t, and_or(d8, uc.hi_mask, uc.f16_magic));   // k6, k7 (x16)
+    auto lo = [&](_Float16 h) { return fmaf(c.s, (float)h, c.c_lo); };
+    auto hi = [&](_Float16 h) { return fmaf(c.s16, (float)h, c.c_hi); };
     auto pk = [](float a, float b) {
         return __builtin_bit_cast(uint32_t, __builtin_convertvector(float2_t{a, b}, bf162_t));
     };
-    return make_uint4(pk(f(lo, 0), f(lo, 2)), pk(f(hi, 0), f(hi, 2)), pk(f(lo, 1), f(lo, 3)),
-                      pk(f(hi, 1), f(hi, 3)));
+    return make_uint4(pk(lo(h0.x), lo(h0.y)), pk(hi(h1.x), hi(h1.y)), pk(lo(h2.x), lo(h2.y)),
+                      pk(hi(h3.x), hi(h3.y)));
 }
 
 // Same for fp16: exact (q - z) pairs, then one fp16 multiply by s.
@@ -85,7 +99,7 @@ __device__ inline uint4 dequant_f16(uint32_t d, uint32_t z, _Float16 sh, const U
 }
 
 template <int BM, int BN, int WM, int WN, int GROUP, bool BF>
-__global__ __launch_bounds__(64 * WM * WN) __attribute__((amdgpu_waves_per_eu(1, 1))) void prefill_kernel(
+__global__ __launch_bounds__(64 * WM * WN) __attribute__((amdgpu_waves_per_eu(WM * WN / 4, WM * WN / 4))) void prefill_kernel(
     const uint16_t *__restrict__ x, const uint4 *__restrict__ qw, const uint16_t *__restrict__ scales,
     const uint32_t *__restrict__ zeros, uint16_t *__restrict__ y, int M, int N, int K, int m_tiles,
     int n_tiles) {
@@ -174,7 +188,6 @@ __global__ __launch_bounds__(64 * WM * WN) __attribute__((amdgpu_waves_per_eu(1,
     // dequantise half h (chunks 2h, 2h+1) of weight record i into LDS;
     // chunks past K (partial last column) have zero codes and zero scale
     const UnpackConsts uc = unpack_consts();
-    const uint32_t byte_mask = vconst(0x0F0F0F0Fu);
     auto store_w_rec = [&](const WCol &u, int i, int h, uint4 *wbuf) __attribute__((always_inline)) {
 #pragma unroll
         for (int jj = 0; jj < 2; ++jj) {
@@ -184,7 +197,7 @@ __global__ __launch_bounds__(64 * WM * WN) __attribute__((amdgpu_waves_per_eu(1,
             const float s = u.sc[i].get(e);
             uint4 v;
             if constexpr (BF)
-                v = dequant_bf16(dw, s, -s * (float)z, byte_mask);
+                v = dequant_bf16(dw, dequant_bf16_consts(s, z), uc);
             else
                 v = dequant_f16(dw, z, (_Float16)s, uc);
             wbuf[swz(wrow[i], 4 * jj + d)] = v;
@@ -242,10 +255,18 @@ __global__ __launch_bounds__(64 * WM * WN) __attribute__((amdgpu_waves_per_eu(1,
 #pragma unroll
             for (int b = 0; b < TN; ++b) b_[b] = wb[swz(wn * (BN / WN) + 32 * b + rsel, 2 * kk + khalf)];
         };
+        // one wave per SIMD: fragment reads run one sub-step ahead; two waves
+        // per SIMD: read just before use (the other wave covers the latency,
+        // and the registers are needed for its accumulators)
+        constexpr bool kAhead = WM * WN == 4;
         read(0, af[0], bfr[0]);
 #pragma unroll
         for (int kk = 0; kk < kStepK / 16; ++kk) {
-            if (kk + 1 < kStepK / 16) read(kk + 1, af[(kk + 1) & 1], bfr[(kk + 1) & 1]);
+            if constexpr (kAhead) {
+                if (kk + 1 < kStepK / 16) read(kk + 1, af[(kk + 1) & 1], bfr[(kk + 1) & 1]);
+            } else if (kk > 0) {
+                read(kk, af[kk & 1], bfr[kk & 1]);
+            }
             if (kk < WREC) store_w_rec(u, kk, h, wdst);
 #pragma unroll
             for (int i = kk; i < XREC; i += kStepK / 16) {
@@ -342,6 +363,7 @@ hipError_t launch_group(int tile, const void *x, const void *qw, const void *sc,
     switch (tile) {
         case kTile64x256: return launch_tile<64, 256, 1, 4, GROUP, BF>(x, qw, sc, zp, y, M, N, K, stream);
         case kTile128x256: return launch_tile<128, 256, 2, 2, GROUP, BF>(x, qw, sc, zp, y, M, N, K, stream);
+        case kTile256x256w8: return launch_tile<256, 256, 2, 4, GROUP, BF>(x, qw, sc, zp, y, M, N, K, stream);
         default: return launch_tile<256, 256, 2, 2, GROUP, BF>(x, qw, sc, zp, y, M, N, K, stream);
     }
 }
@@ -353,21 +375,24 @@ int prefill_tile(int64_t M, int64_t N) {
         const char *v = getenv("W4A16_PREFILL_TILE");
         return v ? atoi(v) : -1;
     }();
-    if (forced >= 0 && forced <= kTile256x256) return forced;
+    if (forced >= 0 && forced <= kTile256x256w8) return forced;
     // time ~ rounds of workgroups over the 256 CUs x time of one tile; the
     // relative tile times (0.62, 0.67, 1.0 for 64, 128, 256 rows) were
     // measured at K = 5120
+    // (the 256-row tile runs with eight waves, two per SIMD: 4-7% faster than
+    // four at K = 5120, M = 2048)
+    static const int kinds[3] = {kTile64x256, kTile128x256, kTile256x256w8};
     static const int rows[3] = {64, 128, 256};
     static const double tile_time[3] = {0.62, 0.67, 1.0};
     const int64_t n_tiles = ceil_div(N, 256);
-    int best = kTile256x256;
+    int best = kTile256x256w8;
     double best_cost = 1e300;
     for (int t = 0; t < 3; ++t) {
         const int64_t tiles = ceil_div(M, rows[t]) * n_tiles;
         const double cost = (double)ceil_div(tiles, 256) * tile_time[t];
         if (cost < best_cost - 1e-9) {
             best_cost = cost;
-            best = t;
+            best = kinds[t];
         }
     }
     return best;

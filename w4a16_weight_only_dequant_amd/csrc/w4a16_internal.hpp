@@ -57,7 +57,7 @@ constexpr size_t kGemvStaticLds = 16 * 8 * 16 * sizeof(float);
 // registers for M <= kSkinnyMaxM (16-row MFMA tiles of activations, one per
 // workgroup), kind 1 is the LDS-tiled GEMM for everything larger.
 constexpr int kSkinnyMaxM = 256;   // measured crossover to the tiled kernel
-enum { kTile64x256 = 0, kTile128x256 = 1, kTile256x256 = 2 };
+enum { kTile64x256 = 0, kTile128x256 = 1, kTile256x256 = 2, kTile256x256w8 = 3 };
 struct GemmPlan {
     int kind;          // 0 = skinny, 1 = tiled
     int waves;         // skinny: waves per workgroup (split K)
@@ -66,6 +66,21 @@ struct GemmPlan {
 };
 
 GemmPlan gemm_plan(int64_t M, int64_t N, int64_t K, int32_t group);
+
+// Problems of one grouped launch (kernel argument, passed by value).
+constexpr int kMaxGroup = 8;
+struct GroupTable {
+    const void *x[kMaxGroup];
+    const void *qweight[kMaxGroup];
+    const void *scales[kMaxGroup];
+    const void *zeros[kMaxGroup];
+    void *y[kMaxGroup];
+    int N[kMaxGroup];
+    int first[kMaxGroup + 1];   // first workgroup of each problem (set by the launcher)
+    int count;
+};
+hipError_t launch_gemm_group(const GroupTable &tab, bool bf16, int M, int K, int group, const GemmPlan &plan,
+                             hipStream_t stream);
 
 hipError_t launch_pack(const float *w, int N, int K, int group, void *qweight,
                        void *scales, void *zeros, hipStream_t stream);
