@@ -17,12 +17,24 @@ What it computes, and where the method is stated:
 * The quantiser. Round-to-nearest of w/scale ("Quantization Is Not a Zip File",
   zhuai.tech, section 3 "The core idea: local structure, not global rounding"),
   applied per group of 32/64/128 consecutive weights ("Block locality" in that
-  same section), with an asymmetric zero-point and the reconstruction
+  same section; 256 as well, the super-block size the K-quant row of the table
+  in that page's "How to read common GGUF quantization names" gives), with an asymmetric zero-point and the reconstruction
   (q - zero) * scale ("Comparison of Quantization Methods: INT8 vs GPTQ vs AWQ
   vs GGUF", instagit, "Practical Code Examples", the zero-point example).
 * The metadata width. 4 + 20/group bits per weight: a 16-bit scale and a 4-bit
   zero per group, which gives the 4.156 bits/weight printed for group 128
   ("Weight-Only Quantization Explained", "The memory arithmetic").
+
+* The symmetric variants. No zero-point: q = round(w / s) clamped to the signed
+  range [-2**(b-1), 2**(b-1) - 1] and w_hat = q * s, with s = max|w| / (2**(b-1) - 1)
+  (the symmetric INT8 scheme of the instagit comparison page, "INT8: Symmetric
+  Integer Quantization" and "Practical Code Examples", applied per group as the
+  "Classic blocks" row of the zhuai.tech table in "How to read common GGUF
+  quantization names" does: integer codes plus one scale per block; INT8 or
+  INT4 weights with FP16/BF16 activations are both weight-only schemes:
+  "Weight-Only Quantisation", definition). 4-bit (sym4) and 8-bit (sym8, W8A16)
+  codes are stored offset by 2**(b-1), so the shared reconstruction
+  s * (code - zero) holds with a fixed zero of 8 or 128 that is never stored.
 
 Readings where the pages are silent (each also listed in the design notes):
   * range includes zero: lo = min(0, min w), hi = max(0, max w);
@@ -31,6 +43,9 @@ Readings where the pages are silent (each also listed in the design notes):
   * zero z = clamp(rint(-lo / s), 0, 15); code q = clamp(rint(w / s) + z, 0, 15);
     rint rounds half to even; every quantiser operation is IEEE fp32 (the
     precision the kernel takes the same integer decision in);
+  * symmetric: s = fp16_rne(max|w| / qmax) in fp32 (qmax = 7 or 127, zero
+    scale -> 2**-24), code = clamp(rint(w / s), -qmax-1, qmax) + qmax + 1;
+  * groups of 32, 64, 128 or 256 consecutive weights along K;
   * dequantised weight w_hat = s * (q - z) is exact in fp64 here;
   * y = x @ w_hat^T accumulated in fp64.
 
@@ -163,11 +178,26 @@ def bits_per_weight(group: int, scale_bits: int = 16, zero_bits: int = 4, code_b
     return code_bits + (scale_bits + zero_bits) / group
 
 
-def packed_bytes(N: int, K: int, group: int):
-    """(qweight, scales, zeros) algorithmic byte counts: one nibble per weight, one fp16
-    scale and one 4-bit zero per (group, output column)."""
+FORMATS = ("asym4", "sym4", "sym8")
+
+
+def code_bits(fmt: str) -> int:
+    if fmt not in FORMATS:
+        raise ValueError(fmt)
+    return 8 if fmt == "sym8" else 4
+
+
+def format_bits_per_weight(group: int, fmt: str = "asym4") -> float:
+    """Storage per weight of a format: the code, the fp16 scale, and the 4-bit
+    zero-point only where the format stores one."""
+    return bits_per_weight(group, code_bits=code_bits(fmt), zero_bits=4 if fmt == "asym4" else 0)
+
+
+def packed_bytes(N: int, K: int, group: int, fmt: str = "asym4"):
+    """(qweight, scales, zeros) algorithmic byte counts: one code per weight, one fp16
+    scale per (group, output column), and for asym4 one 4-bit zero per (group, column)."""
     G = K // group
-    return (N * K) // 2, 2 * G * N, (G * N) // 2
+    return (N * K * code_bits(fmt)) // 8, 2 * G * N, (G * N) // 2 if fmt == "asym4" else 0
 
 
 def model_bytes(n_weights: float, bits: float) -> float:
@@ -185,20 +215,29 @@ def model_bytes(n_weights: float, bits: float) -> float:
 F16_MIN_SUBNORMAL_BITS = np.uint16(0x0001)   # 2**-24
 
 
-def quantize_groupwise(w, group: int):
+GROUPS = (32, 64, 128, 256)
+
+
+def quantize_groupwise(w, group: int, fmt: str = "asym4"):
     """Quantise fp32 weights w [N][K] in groups of `group` consecutive k.
 
-    Returns (codes u8 [N][K], scale_bits u16 [G][N], zeros u8 [G][N]).
-    Every step is an IEEE binary32 operation (division, never a reciprocal).
+    Returns (codes u8 [N][K], scale_bits u16 [G][N], zeros u8 [G][N]); for the
+    symmetric formats the zeros are the fixed offset (8 or 128), not stored on
+    the device. Every step is an IEEE binary32 operation (division, never a
+    reciprocal).
     """
     w = np.ascontiguousarray(w, dtype=np.float32)
     N, K = w.shape
-    if group not in (32, 64, 128) or K % group != 0:
-        raise ValueError("group must be 32/64/128 and divide K")
+    if group not in GROUPS or K % group != 0:
+        raise ValueError("group must be 32/64/128/256 and divide K")
+    if fmt not in FORMATS:
+        raise ValueError(f"unknown format {fmt}")
     if not np.all(np.isfinite(w)) or np.max(np.abs(w), initial=0.0) >= 2.0 ** 18:
         raise ValueError("weights must be finite with |w| < 2**18")
     G = K // group
     wg = w.reshape(N, G, group)
+    if fmt != "asym4":
+        return _quantize_symmetric(wg, code_bits(fmt))
     zero = np.float32(0.0)
     # 1. range of the group, widened to include zero
     lo = np.minimum(wg.min(axis=2), zero)                       # [N][G] fp32
@@ -214,6 +253,25 @@ def quantize_groupwise(w, group: int):
     r = np.rint(wg / s[:, :, None]).astype(np.int32)
     q = np.clip(r + z[:, :, None], 0, 15).astype(np.uint8)
     return (q.reshape(N, K), np.ascontiguousarray(s_bits.T), np.ascontiguousarray(z.T.astype(np.uint8)))
+
+
+def _quantize_symmetric(wg, bits: int):
+    """Symmetric groupwise round-to-nearest of wg [N][G][group] with b-bit codes:
+    s = max|w| / (2**(b-1) - 1), q = clamp(rint(w / s), -2**(b-1), 2**(b-1) - 1),
+    stored as q + 2**(b-1)."""
+    N, G, group = wg.shape
+    qmax = (1 << (bits - 1)) - 1
+    off = qmax + 1
+    # 1. the group's largest magnitude (exact in fp32)
+    amax = np.abs(wg).max(axis=2)
+    # 2. scale: fp32 amax / qmax rounded once to fp16; zero -> smallest subnormal
+    s_bits = f32_to_f16_bits(amax / np.float32(qmax))
+    s_bits = np.where(s_bits == 0, F16_MIN_SUBNORMAL_BITS, s_bits).astype(np.uint16)
+    s = f16_bits_to_f32(s_bits)
+    # 3. codes: round(w / s) in the signed range, offset to unsigned
+    q = np.clip(np.rint(wg / s[:, :, None]).astype(np.int32), -off, qmax) + off
+    zeros = np.full((G, N), off, dtype=np.uint8)
+    return (q.astype(np.uint8).reshape(N, G * group), np.ascontiguousarray(s_bits.T), zeros)
 
 
 def dequantize(codes, scale_bits, zeros, group: int) -> np.ndarray:
@@ -250,7 +308,12 @@ def dequantize(codes, scale_bits, zeros, group: int) -> np.ndarray:
 #   scales: fp16 bits [T][N][GPC] (group g = GPC*t + e is element e).
 #   zeros: u32 words [T][N*GPC/8]; the GPC zero-points of row n in column t are
 #   nibbles GPC*(n % (8/GPC)) + e of word n // (8/GPC).
-#   At group 128 (GPC = 1) these are the plain [G][N] and [G][N/8] layouts.
+#   At group 128 (GPC = 1) these are the plain [G][N] and [G][N/8] layouts;
+#   group 256 uses the same plain layouts, one slot per group, and column t
+#   reads slot t // 2.
+#   8-bit codes (sym8) are two 4-bit planes, each in the qweight layout above:
+#   the low nibbles of every code first (N*K/2 bytes), then the high nibbles.
+#   The symmetric formats store no zero words.
 # ---------------------------------------------------------------------------
 
 
@@ -274,9 +337,12 @@ def _device_nibble_index(N: int, K: int) -> np.ndarray:
     return dword * 8 + p
 
 
-def pack_device(codes) -> np.ndarray:
-    """codes u8 [N][K] -> packed qweight bytes (uint8, N*K/2) in the device layout."""
+def pack_device(codes, fmt: str = "asym4") -> np.ndarray:
+    """codes u8 [N][K] -> packed qweight bytes (uint8, N*K/2 or N*K for sym8) in the
+    device layout."""
     codes = np.asarray(codes, dtype=np.uint8)
+    if code_bits(fmt) == 8:
+        return np.concatenate([pack_device(codes & np.uint8(0xF)), pack_device(codes >> np.uint8(4))])
     N, K = codes.shape
     if N % 8 or K % 32:
         raise ValueError("N % 8 == 0 and K % 32 == 0 required")
@@ -286,9 +352,12 @@ def pack_device(codes) -> np.ndarray:
     return (nib[0::2] | (nib[1::2] << 4)).astype(np.uint8)
 
 
-def unpack_device(qweight, N: int, K: int) -> np.ndarray:
+def unpack_device(qweight, N: int, K: int, fmt: str = "asym4") -> np.ndarray:
     """Inverse of pack_device: packed bytes -> codes u8 [N][K]."""
     qb = np.asarray(qweight, dtype=np.uint8).ravel()
+    if code_bits(fmt) == 8:
+        half = N * K // 2
+        return unpack_device(qb[:half], N, K) | (unpack_device(qb[half:], N, K) << np.uint8(4))
     nib = np.empty(2 * qb.size, dtype=np.uint8)
     nib[0::2] = qb & 0xF
     nib[1::2] = qb >> 4
@@ -314,9 +383,15 @@ def unpack_zeros(words, G: int, N: int) -> np.ndarray:
     return out.reshape(G, N)
 
 
+def _gpc(group: int) -> int:
+    """Metadata slots per 128-weight column (group 256: one slot per two columns)."""
+    return max(1, 128 // group)
+
+
 def _padded_groups(G: int, group: int) -> int:
-    """Group slots of the per-column metadata layout: T columns of 128/group groups."""
-    gpc = 128 // group
+    """Group slots of the per-column metadata layout: T columns of 128/group groups
+    (group 256: exactly G slots)."""
+    gpc = _gpc(group)
     return -(-G // gpc) * gpc
 
 
@@ -324,7 +399,7 @@ def pack_scales_device(scale_bits, group: int) -> np.ndarray:
     """scale bits [G][N] -> device order [T][N][GPC] (uint16), unused slots 0."""
     s = np.asarray(scale_bits, dtype=np.uint16)
     G, N = s.shape
-    gpc = 128 // group
+    gpc = _gpc(group)
     Gp = _padded_groups(G, group)
     full = np.zeros((Gp, N), dtype=np.uint16)
     full[:G] = s
@@ -338,7 +413,7 @@ def pack_zeros_device(zeros, group: int) -> np.ndarray:
     n*GPC + e within the column, eight nibbles per little-endian word."""
     z = np.asarray(zeros, dtype=np.uint32)
     G, N = z.shape
-    gpc = 128 // group
+    gpc = _gpc(group)
     Gp = _padded_groups(G, group)
     full = np.zeros((Gp, N), dtype=np.uint32)
     full[:G] = z
@@ -350,17 +425,18 @@ def pack_zeros_device(zeros, group: int) -> np.ndarray:
     return word
 
 
-def device_meta_bytes(N: int, K: int, group: int):
+def device_meta_bytes(N: int, K: int, group: int, fmt: str = "asym4"):
     """(scales, zeros) byte counts of the per-column metadata layout."""
     Gp = _padded_groups(K // group, group)
-    return 2 * Gp * N, Gp * N // 2
+    return 2 * Gp * N, Gp * N // 2 if fmt == "asym4" else 0
 
 
-def quantize_and_pack(w, group: int):
-    """Full offline step: (qweight bytes, device scales, device zero words, codes, scale bits, zeros)."""
-    codes, s_bits, zeros = quantize_groupwise(w, group)
-    return (pack_device(codes), pack_scales_device(s_bits, group), pack_zeros_device(zeros, group),
-            codes, s_bits, zeros)
+def quantize_and_pack(w, group: int, fmt: str = "asym4"):
+    """Full offline step: (qweight bytes, device scales, device zero words or None,
+    codes, scale bits, zeros)."""
+    codes, s_bits, zeros = quantize_groupwise(w, group, fmt)
+    zdev = pack_zeros_device(zeros, group) if fmt == "asym4" else None
+    return (pack_device(codes, fmt), pack_scales_device(s_bits, group), zdev, codes, s_bits, zeros)
 
 
 # ---------------------------------------------------------------------------

@@ -386,3 +386,177 @@ def test_device_metadata_layout_by_hand():
     s128 = np.arange(3 * 16, dtype=np.uint16).reshape(3, 16)
     assert np.array_equal(ref.pack_scales_device(s128, 128).reshape(3, 16), s128)
     assert ref.device_meta_bytes(8, 160, 32) == (2 * 8 * 8, 8 * 8 // 2)
+
+
+# ---------------------------------------------------------------------------
+# Symmetric formats (sym4, sym8 = W8A16) and group 256
+# ---------------------------------------------------------------------------
+
+SYM = [("sym4", 7), ("sym8", 127)]
+
+
+@pytest.mark.parametrize("fmt,qmax", SYM)
+@pytest.mark.parametrize("group", [32, 128, 256])
+def test_symmetric_codes_are_nearest_signed_grid_points(fmt, qmax, group):
+    """Brute force over every signed code: the chosen one is a nearest grid
+    point q*s, q in [-qmax-1, qmax]; the zero is the fixed offset qmax+1."""
+    rng = np.random.default_rng(qmax + group)
+    w = (rng.standard_t(5, size=(12, 2 * group)) * 0.03).astype(np.float32)
+    w[2] = np.abs(w[2])
+    w[3, :group] = -0.125
+    codes, s_bits, zeros = ref.quantize_groupwise(w, group, fmt)
+    N, K = w.shape
+    G = K // group
+    assert np.all(zeros == qmax + 1)
+    s = ref.f16_bits_to_f64(s_bits).T
+    # the scale: max|w| / qmax in fp32, rounded to fp16 (checked through numpy's own fp16)
+    amax = np.abs(w.reshape(N, G, group)).max(2)
+    want_s = (amax / np.float32(qmax)).astype(np.float16).astype(np.float64)
+    assert np.array_equal(s, want_s)
+    grid = np.arange(-qmax - 1, qmax + 1)[None, None, None, :] * s[:, :, None, None]
+    w64 = w.astype(np.float64).reshape(N, G, group)
+    dist = np.abs(w64[..., None] - grid)
+    got = np.take_along_axis(dist, codes.reshape(N, G, group, 1).astype(np.int64), axis=-1)[..., 0]
+    assert np.all(got <= dist.min(-1) + 2.0 ** -20 * np.abs(w64) + 1e-30)
+    # nothing reaches the clamp: |w| <= max|w| ~ qmax * s
+    assert codes.min() >= 1
+
+
+@pytest.mark.parametrize("fmt,qmax", SYM)
+def test_symmetric_is_odd(fmt, qmax):
+    """Round half to even is odd-symmetric and the range is |w|: negating the
+    weights negates the rebuilt weights exactly."""
+    rng = np.random.default_rng(7)
+    w = (rng.standard_normal((16, 512)) * 0.05).astype(np.float32)
+    a = ref.dequantize(*ref.quantize_groupwise(w, 64, fmt), 64)
+    b = ref.dequantize(*ref.quantize_groupwise(-w, 64, fmt), 64)
+    assert np.array_equal(a, -b)
+
+
+@pytest.mark.parametrize("fmt,qmax", SYM)
+def test_symmetric_ties_round_to_even(fmt, qmax):
+    s = 2.0 ** -5
+    j = np.arange(-qmax, qmax)                     # (j + 1/2) s strictly inside [-qmax, qmax] s
+    vals = np.concatenate([[qmax * s], (j + 0.5) * s])
+    K = 256
+    vals = np.concatenate([vals, np.zeros(-vals.size % K)]) if vals.size <= K else vals
+    w = vals.astype(np.float32)[None, :]
+    w = np.tile(w, (8, 1))
+    group = w.shape[1] if w.shape[1] in (32, 64, 128, 256) else 256
+    codes, s_bits, zeros = ref.quantize_groupwise(w, group, fmt)
+    assert ref.f16_bits_to_f64(s_bits)[0, 0] == s
+    d = codes[0, 1:1 + j.size].astype(np.int64) - (qmax + 1)
+    assert np.array_equal(d, np.where(j % 2 == 0, j, j + 1))
+
+
+@pytest.mark.parametrize("fmt,qmax", SYM)
+@pytest.mark.parametrize("group", [32, 256])
+def test_symmetric_lattice_weights_are_reproduced_exactly(fmt, qmax, group):
+    rng = np.random.default_rng(300 + qmax + group)
+    N, G = 24, 3
+    q = rng.integers(-qmax, qmax + 1, size=(N, G, group))
+    q[:, :, 0] = np.where(rng.random((N, G)) < 0.5, qmax, -qmax)     # |q| = qmax present
+    e = rng.integers(-18, -3, size=(N, G))
+    s = np.ldexp(1.0, e)
+    W = (q * s[:, :, None]).reshape(N, G * group).astype(np.float32)
+    codes, s_bits, zeros = ref.quantize_groupwise(W, group, fmt)
+    assert np.array_equal(codes.reshape(N, G, group).astype(np.int64) - (qmax + 1), q)
+    assert np.array_equal(ref.f16_bits_to_f64(s_bits).T, s)
+    assert np.array_equal(ref.dequantize(codes, s_bits, zeros, group), W.astype(np.float64))
+
+
+@pytest.mark.parametrize("fmt,qmax", SYM)
+def test_symmetric_round_trip_within_half_scale(fmt, qmax):
+    rng = np.random.default_rng(11)
+    w = (rng.standard_normal((32, 1024)) * 0.02).astype(np.float32)
+    codes, s_bits, zeros = ref.quantize_groupwise(w, 128, fmt)
+    err = np.abs(w.astype(np.float64) - ref.dequantize(codes, s_bits, zeros, 128))
+    s = np.repeat(ref.f16_bits_to_f64(s_bits).T, 128, axis=1)
+    assert np.all(err <= 0.5 * s + 2.0 ** -24 * np.abs(w))
+
+
+def test_symmetric_degenerate_groups():
+    w = np.zeros((8, 64), dtype=np.float32)
+    w[1, :32] = 1e-12
+    w[2, :32] = -0.5
+    for fmt, qmax in SYM:
+        codes, s_bits, zeros = ref.quantize_groupwise(w, 32, fmt)
+        assert s_bits[0, 0] == 0x0001 and np.all(codes[0] == qmax + 1)    # all-zero group: q = 0
+        assert s_bits[0, 1] == 0x0001 and np.all(codes[1, :32] == qmax + 1)
+        assert np.all(codes[2, :32] == 1)                                  # -max|w| -> -qmax
+        w_hat = ref.dequantize(codes, s_bits, zeros, 32)
+        assert np.all(w_hat[0] == 0.0) and np.all(w_hat[1] == 0.0)
+
+
+def test_int8_per_tensor_matches_integer_search():
+    """The pages' per-tensor symmetric INT8 (one group spanning a row here):
+    every code is the integer nearest to w/s, found by a search over all 256."""
+    rng = np.random.default_rng(5)
+    w = rng.standard_normal((4, 256)).astype(np.float32)
+    codes, s_bits, zeros = ref.quantize_groupwise(w, 256, "sym8")
+    s = ref.f16_bits_to_f64(s_bits)[0]
+    for n in range(4):
+        cand = np.arange(-128, 128)
+        best = cand[np.argmin(np.abs(w[n][:, None].astype(np.float64) - cand[None, :] * s[n]), axis=1)]
+        assert np.array_equal(codes[n].astype(np.int64) - 128, best)
+
+
+def test_format_byte_accounting():
+    for N, K, g in [(4096, 4096, 128), (5120, 13824, 256), (8192, 28672, 32)]:
+        for fmt in ref.FORMATS:
+            q, s, z = ref.packed_bytes(N, K, g, fmt)
+            assert (q + s + z) * 8 == N * K * ref.format_bits_per_weight(g, fmt)
+    assert ref.format_bits_per_weight(128, "asym4") == 4.15625
+    assert ref.format_bits_per_weight(128, "sym4") == 4.125
+    assert ref.format_bits_per_weight(256, "sym8") == 8.0625
+    assert ref.format_bits_per_weight(256, "asym4") == 4 + 20 / 256
+    assert ref.packed_bytes(64, 512, 256, "sym8") == (64 * 512, 2 * 2 * 64, 0)
+    assert ref.device_meta_bytes(64, 512, 256, "sym4") == (2 * 2 * 64, 0)
+
+
+def test_group256_metadata_is_the_plain_layout():
+    G, N = 3, 16
+    s_bits = np.arange(1, G * N + 1, dtype=np.uint16).reshape(G, N)
+    z = (np.arange(G * N, dtype=np.uint8).reshape(G, N) * 5) % 16
+    assert np.array_equal(ref.pack_scales_device(s_bits, 256).reshape(G, N), s_bits)
+    assert np.array_equal(ref.pack_zeros_device(z, 256), ref.pack_zeros(z))
+    assert ref.device_meta_bytes(N, 768, 256) == (2 * G * N, G * N // 2)
+
+
+def test_group256_groups_span_two_columns():
+    """A group of 256 straddles two 128-weight columns: its range and scale come
+    from both halves (a group-128 quantisation of the same row differs)."""
+    w = np.zeros((8, 256), dtype=np.float32)
+    w[:, :128] = 0.01
+    w[:, 128:] = -1.5
+    c256, s256, z256 = ref.quantize_groupwise(w, 256)
+    c128, s128, z128 = ref.quantize_groupwise(w, 128)
+    assert s256.shape == (1, 8) and s128.shape == (2, 8)
+    assert ref.f16_bits_to_f64(s256[0, 0]) == ref.f16_bits_to_f64(ref.f32_to_f16_bits(np.float32(1.51) / np.float32(15)))
+    lo, hi = -1.5, 0.01
+    s = float(ref.f16_bits_to_f64(s256[0, 0]))
+    assert z256[0, 0] == int(np.clip(np.rint(np.float32(-lo) / np.float32(s)), 0, 15))
+    # the small half is lost inside the wide group (w_hat = 0), kept at group 128
+    w_hat256 = ref.dequantize(c256, s256, z256, 256)
+    w_hat128 = ref.dequantize(c128, s128, z128, 128)
+    assert np.all(w_hat256[:, :128] == 0.0)
+    assert np.all(np.abs(w_hat128[:, :128] - 0.01) < 1e-5)
+
+
+@pytest.mark.parametrize("N,K", [(72, 64), (200, 96), (16, 256)])
+def test_sym8_planes_round_trip_and_order(N, K):
+    rng = np.random.default_rng(N * K)
+    codes = rng.integers(0, 256, size=(N, K), dtype=np.uint8)
+    packed = ref.pack_device(codes, "sym8")
+    assert packed.size == N * K
+    assert np.array_equal(ref.unpack_device(packed, N, K, "sym8"), codes)
+    # plane 0 is the 4-bit layout of the low nibbles, plane 1 of the high nibbles
+    assert np.array_equal(packed[:N * K // 2], ref.pack_device(codes & 0xF))
+    one = np.zeros((N, K), dtype=np.uint8)
+    one[N - 1, K - 1] = 0xA5
+    p1 = ref.pack_device(one, "sym8")
+    nz = np.nonzero(p1)[0]
+    assert len(nz) == 2 and nz[1] - nz[0] == N * K // 2
+    # the same nibble position in both planes: 0x5 (low nibble) in plane 0, 0xA in plane 1
+    lo, hi = int(p1[nz[0]]), int(p1[nz[1]])
+    assert (lo, hi) in ((0x05, 0x0A), (0x50, 0xA0))
