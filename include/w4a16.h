@@ -2,7 +2,7 @@
  * w4a16.h - C ABI of the MI355X (gfx950) W4A16 weight-only linear layer.
  *
  * The operation. Weights are stored as 4-bit integer codes with one fp16 scale
- * and one 4-bit zero-point per group of 32, 64 or 128 consecutive input
+ * and one 4-bit zero-point per group of 32, 64, 128 or 256 consecutive input
  * channels; the kernels unpack and rescale the codes just before the multiply,
  * while the activations stay 16-bit and the accumulation is fp32
  * ("Weight-Only Quantisation", klaylearn glossary, definition; "Weight-Only
@@ -15,6 +15,17 @@
  *     q  = clamp(rint(w / s) + z, 0, 15)                rint: ties to even
  *   dequantise:   w_hat[n][k] = s[g][n] * (q[n][k] - z[g][n])
  *   product:      y[m][n] = sum_k x[m][k] * w_hat[n][k]
+ *
+ * Two symmetric formats share the kernels (w4a16_format): codes without a
+ * stored zero-point, 4-bit (SYM4) or 8-bit (SYM8, weight-only INT8: W8A16),
+ *     s = fp16_rne(max|w| / qmax), 0 -> 2^-24         qmax = 7 or 127
+ *     q = clamp(rint(w / s), -qmax-1, qmax) + qmax + 1   (stored code, unsigned)
+ *     w_hat = s * (q - (qmax + 1))
+ * (the symmetric INT8 scheme of the instagit comparison page, "INT8:
+ * Symmetric Integer Quantization", applied per group as the "Classic blocks"
+ * row of the GGUF table in "Quantization Is Not a Zip File" does; INT4 or
+ * INT8 weights under 16-bit activations: "Weight-Only Quantisation",
+ * definition). Group 256 is the super-block size of that table's K-quant row.
  *
  * Rounding to the nearest grid point of w / scale follows "Quantization Is Not
  * a Zip File" (zhuai.tech), section 3; the per-group scale ("block locality")
@@ -45,7 +56,12 @@
  *                                   of column t's words (slots past K hold 0)
  *            For K % 128 == 0 both have the canonical sizes 2*G*N and G*N/2
  *            bytes (G = K/group), and at group 128 they are exactly [G][N]
- *            and [G][N/8].
+ *            and [G][N/8]. Group 256 (K % 256 == 0) uses the same [G][N] and
+ *            [G][N/8] layouts, one slot per group: column t reads slot t/2.
+ *   SYM4     qweight as above (codes q + 8), scales as above, no zeros.
+ *   SYM8     qweight N*K bytes: two 4-bit planes in the layout above, the low
+ *            nibbles of every code in bytes [0, N*K/2), the high nibbles in
+ *            [N*K/2, N*K); scales as above, no zeros.
  *   x        fp16 or bf16 [M][K], row-major
  *   y        same type as x, [M][N], row-major; fp32 accumulation, rounded
  *            once to the output type (round to nearest even)
@@ -62,10 +78,15 @@
  * device query that failed).
  *
  * Preconditions shared by the compute calls:
- *   1 <= M <= 2^24, M*K < 2^34, N >= 8, N % 8 == 0, group in {32, 64, 128},
- *   K >= group, K % group == 0; pointers non-NULL and 16-byte aligned; y does not overlap
- *   any input; the current device is a gfx950 (w4a16_device_supported).
+ *   1 <= M <= 2^24, M*K < 2^34, N >= 8, N % 8 == 0, group in {32, 64, 128, 256},
+ *   K >= group, K % group == 0; pointers non-NULL and 16-byte aligned (zeros
+ *   is not read, and may be NULL, for the symmetric formats); y does not
+ *   overlap any input; the current device is a gfx950 (w4a16_device_supported).
  *   Weights given to w4a16_pack are finite with |w| < 2^18.
+ *
+ * Every call without a format argument works on W4A16_FMT_ASYM4; its `_fmt`
+ * twin takes the format as the argument after `group` and is otherwise the
+ * same call.
  */
 #ifndef W4A16_H
 #define W4A16_H
@@ -92,6 +113,12 @@ typedef enum {
     W4A16_BF16 = 1
 } w4a16_dtype;
 
+typedef enum {
+    W4A16_FMT_ASYM4 = 0,   /* 4-bit codes, fp16 scale and 4-bit zero-point per group */
+    W4A16_FMT_SYM4 = 1,    /* 4-bit codes q + 8, fp16 scale per group, no zero-points */
+    W4A16_FMT_SYM8 = 2     /* 8-bit codes q + 128 (two 4-bit planes), fp16 scale per group: W8A16 */
+} w4a16_format;
+
 /* Human-readable name of a status code (static string, never NULL). */
 const char *w4a16_status_string(int status);
 
@@ -107,13 +134,19 @@ w4a16_status w4a16_device_supported(int device);
 
 /* Byte sizes of the packed buffers for an N x K weight matrix: qweight
  * N*K/2, scales 2*T*N*(128/group), zeros T*N*(128/group)/2 with
- * T = ceil(K/128). For K % 128 == 0 these are 2*G*N and G*N/2: 4 + 20/group
+ * T = ceil(K/128) (group 256: 2*G*N and G*N/2). For K % 128 == 0 these are 2*G*N and G*N/2: 4 + 20/group
  * bits per weight, the 4.156 bits/weight at group 128 of "Weight-Only
  * Quantization Explained", "The memory arithmetic". Host-only; any
  * out-pointer may be NULL. */
 w4a16_status w4a16_packed_bytes(int64_t N, int64_t K, int32_t group,
                                 size_t *qweight_bytes, size_t *scales_bytes,
                                 size_t *zeros_bytes);
+/* Per format: qweight N*K/2 bytes (N*K for SYM8), scales as above, zeros 0
+ * bytes for the symmetric formats. SYM4 stores 4 + 16/group bits per weight,
+ * SYM8 8 + 16/group. */
+w4a16_status w4a16_packed_bytes_fmt(int64_t N, int64_t K, int32_t group, int32_t fmt,
+                                    size_t *qweight_bytes, size_t *scales_bytes,
+                                    size_t *zeros_bytes);
 
 /* Workspace bytes a w4a16_gemv / w4a16_gemm / w4a16_linear call of this shape
  * needs. Host-only. The current kernels reduce inside each workgroup and need
@@ -127,6 +160,10 @@ w4a16_status w4a16_workspace_bytes(int64_t M, int64_t N, int64_t K, int32_t grou
  * Bit-exact with the quantiser defined above (IEEE fp32, no reciprocal). */
 w4a16_status w4a16_pack(const float *w, int64_t N, int64_t K, int32_t group,
                         void *qweight, void *scales, void *zeros, void *stream);
+/* Same in any format: the symmetric quantiser above for SYM4 / SYM8 (zeros
+ * not written, may be NULL). */
+w4a16_status w4a16_pack_fmt(const float *w, int64_t N, int64_t K, int32_t group, int32_t fmt,
+                            void *qweight, void *scales, void *zeros, void *stream);
 
 /* Inverse view of the packed data in canonical form, for tests and tools:
  * codes uint8 [N][K], scales fp16 bits [G][N], zeros uint8 [G][N]. */
@@ -134,6 +171,12 @@ w4a16_status w4a16_unpack(const void *qweight, const void *scales, const void *z
                           int64_t N, int64_t K, int32_t group,
                           uint8_t *codes, uint16_t *scales_out, uint8_t *zeros_out,
                           void *stream);
+/* Same in any format: codes are the stored unsigned codes (0..255 for SYM8);
+ * zeros_out receives the fixed zero (8 or 128) of a symmetric format. */
+w4a16_status w4a16_unpack_fmt(const void *qweight, const void *scales, const void *zeros,
+                              int64_t N, int64_t K, int32_t group, int32_t fmt,
+                              uint8_t *codes, uint16_t *scales_out, uint8_t *zeros_out,
+                              void *stream);
 
 /* Decode GEMV: y [M][N] = x [M][K] . w_hat^T for small M (1 <= M <= 8).
  * One pass over the packed weights: 128-bit loads, in-register unpack, fp16
@@ -145,6 +188,10 @@ w4a16_status w4a16_gemv(const void *x, int32_t dtype, const void *qweight,
                         const void *scales, const void *zeros, void *y,
                         int64_t M, int64_t N, int64_t K, int32_t group,
                         void *workspace, size_t workspace_bytes, void *stream);
+w4a16_status w4a16_gemv_fmt(const void *x, int32_t dtype, const void *qweight,
+                            const void *scales, const void *zeros, void *y,
+                            int64_t M, int64_t N, int64_t K, int32_t group, int32_t fmt,
+                            void *workspace, size_t workspace_bytes, void *stream);
 
 /* Matrix-core GEMM for any M >= 1 (M*K < 2^34). M <= 256: the packed weights
  * stream through registers as in the GEMV, and each unpacked dword feeds one
@@ -158,6 +205,10 @@ w4a16_status w4a16_gemm(const void *x, int32_t dtype, const void *qweight,
                         const void *scales, const void *zeros, void *y,
                         int64_t M, int64_t N, int64_t K, int32_t group,
                         void *workspace, size_t workspace_bytes, void *stream);
+w4a16_status w4a16_gemm_fmt(const void *x, int32_t dtype, const void *qweight,
+                            const void *scales, const void *zeros, void *y,
+                            int64_t M, int64_t N, int64_t K, int32_t group, int32_t fmt,
+                            void *workspace, size_t workspace_bytes, void *stream);
 
 /* Default path: dispatches on M between w4a16_gemv (small-batch decode, where
  * the weight stream is the bottleneck) and w4a16_gemm (larger batches and
@@ -167,6 +218,10 @@ w4a16_status w4a16_linear(const void *x, int32_t dtype, const void *qweight,
                           const void *scales, const void *zeros, void *y,
                           int64_t M, int64_t N, int64_t K, int32_t group,
                           void *workspace, size_t workspace_bytes, void *stream);
+w4a16_status w4a16_linear_fmt(const void *x, int32_t dtype, const void *qweight,
+                              const void *scales, const void *zeros, void *y,
+                              int64_t M, int64_t N, int64_t K, int32_t group, int32_t fmt,
+                              void *workspace, size_t workspace_bytes, void *stream);
 
 /* Several independent linear layers of the same M, K, group and activation
  * type in one launch: y[p] = x[p] . w_hat[p]^T for p < count (1..8), problem p
@@ -186,6 +241,12 @@ w4a16_status w4a16_linear_group(int32_t count, const void *const *x, int32_t dty
                                 const void *const *zeros, void *const *y, int64_t M,
                                 const int64_t *N, int64_t K, int32_t group,
                                 void *workspace, size_t workspace_bytes, void *stream);
+/* Same, every problem in format `fmt` (zeros may be NULL for the symmetric formats). */
+w4a16_status w4a16_linear_group_fmt(int32_t count, const void *const *x, int32_t dtype,
+                                    const void *const *qweight, const void *const *scales,
+                                    const void *const *zeros, void *const *y, int64_t M,
+                                    const int64_t *N, int64_t K, int32_t group, int32_t fmt,
+                                    void *workspace, size_t workspace_bytes, void *stream);
 
 /* Largest M that w4a16_linear may send to the GEMV kernel. */
 int32_t w4a16_gemv_max_m(void);

@@ -13,33 +13,35 @@ def lib():
     return w4
 
 
-def oracle_pack(w: np.ndarray, group: int):
-    codes, s_bits, zeros = ref.quantize_groupwise(w, group)
+def oracle_pack(w: np.ndarray, group: int, fmt: str = "asym4"):
+    codes, s_bits, zeros = ref.quantize_groupwise(w, group, fmt)
     return {
         "codes": codes,
         "s_bits": s_bits,
         "zeros": zeros,
-        "qweight": ref.pack_device(codes),
+        "fmt": fmt,
+        "qweight": ref.pack_device(codes, fmt),
         "scales_dev": ref.pack_scales_device(s_bits, group).ravel(),
-        "zeros_dev": ref.pack_zeros_device(zeros, group).ravel(),
+        "zeros_dev": ref.pack_zeros_device(zeros, group).ravel() if fmt == "asym4" else None,
     }
 
 
-def gpu_pack(w: np.ndarray, group: int):
+def gpu_pack(w: np.ndarray, group: int, fmt: str = "asym4"):
     import torch
     wt = torch.from_numpy(w).cuda()
-    pw = lib().pack(wt, group)
+    pw = lib().pack(wt, group, fmt)
     torch.cuda.synchronize()
     del wt
     return pw
 
 
-def prepared(key, make_w, group):
+def prepared(key, make_w, group, fmt: str = "asym4"):
     """Weights, oracle quantisation and the GPU-packed weight, cached per key."""
+    key = (key, fmt) if fmt != "asym4" else key
     if key not in _CACHE:
         w = make_w()
-        o = oracle_pack(w, group)
-        pw = gpu_pack(w, group)
+        o = oracle_pack(w, group, fmt)
+        pw = gpu_pack(w, group, fmt)
         _CACHE[key] = (w, o, pw)
     return _CACHE[key]
 

@@ -137,3 +137,29 @@ def test_product_path_never_touches_the_oracle():
                 text = open(os.path.join(dirpath, f)).read()
                 assert "oracle" not in text.lower().replace("oracle/", ""), f
                 assert "w4a16_ref" not in text, f
+
+
+@pytest.mark.parametrize("N,K,group", [(4096, 4096, 128), (72, 768, 256), (5120, 13824, 256), (72, 160, 32)])
+def test_packed_bytes_formats(w4, N, K, group):
+    slots = K // 256 if group == 256 else -(-K // 128) * (128 // group)
+    assert w4.packed_bytes(N, K, group, "asym4") == (N * K // 2, 2 * slots * N, slots * N // 2)
+    assert w4.packed_bytes(N, K, group, "sym4") == (N * K // 2, 2 * slots * N, 0)
+    assert w4.packed_bytes(N, K, group, "sym8") == (N * K, 2 * slots * N, 0)
+    assert w4.packed_bytes(N, K, group) == w4.packed_bytes(N, K, group, "asym4")
+
+
+def test_format_arguments_validated(w4):
+    lib = w4.raw()
+    q, s, z = ctypes.c_size_t(), ctypes.c_size_t(), ctypes.c_size_t()
+    assert lib.w4a16_packed_bytes_fmt(64, 256, 128, 3, ctypes.byref(q), ctypes.byref(s), ctypes.byref(z)) == 1
+    assert lib.w4a16_packed_bytes_fmt(64, 384, 256, 1, ctypes.byref(q), ctypes.byref(s), ctypes.byref(z)) == 1
+    fake = ctypes.c_void_p(1 << 20)
+    y = ctypes.c_void_p(1 << 30)
+    # unknown format
+    assert lib.w4a16_gemm_fmt(fake, 0, fake, fake, fake, y, 1, 64, 256, 128, 3, None, 0, None) == 1
+    assert lib.w4a16_pack_fmt(fake, 64, 256, 128, -1, fake, fake, fake, None) == 1
+    # the zero-point format needs its zeros; K % 256 for group 256
+    assert lib.w4a16_linear_fmt(fake, 0, fake, fake, None, y, 1, 64, 256, 128, 0, None, 0, None) == 1
+    assert lib.w4a16_gemv_fmt(fake, 0, fake, fake, None, y, 1, 64, 384, 256, 1, None, 0, None) == 1
+    with pytest.raises(ValueError):
+        w4.packed_bytes(64, 256, 128, "int3")

@@ -1,0 +1,153 @@
+"""GPU parity of the weight-format variants: symmetric 4-bit (sym4), symmetric
+8-bit (sym8, W8A16) and group 256 (all three formats). The packed bytes,
+scales and canonical view are bit-identical to the oracle's; every product is
+within 2e-3 * sum|x * w_hat| + 1e-5 (+ the output rounding) of the fp64
+oracle, on each kernel (GEMV, small-batch matrix-core, tiled matrix-core)."""
+import numpy as np
+import pytest
+
+import workloads as wl
+from oracle import w4a16_ref as ref
+from tests import helpers as H
+
+pytestmark = pytest.mark.gpu
+
+FORMATS = ["asym4", "sym4", "sym8"]
+
+# (N, K, group): ragged N (N % 16 = 8), partial last column (K % 128 = 32 / 64),
+# group 256 with an odd number of groups, several tiles of the large-M kernel
+SHAPES = [(72, 160, 32), (136, 320, 64), (328, 640, 128), (264, 768, 256), (1000, 1024, 256),
+          (520, 2048, 128)]
+
+
+def _prep(N, K, group, fmt):
+    return H.prepared(("fmt", N, K, group), lambda: wl.random_weights(N * 3 + K + group, N, K), group, fmt)
+
+
+def _check_packed(o, pw):
+    import torch
+    torch.cuda.synchronize()
+    assert np.array_equal(pw.qweight.cpu().numpy(), o["qweight"]), "qweight differs"
+    s = pw.scales.cpu().view(torch.int16).numpy().view(np.uint16)
+    assert np.array_equal(s, o["scales_dev"]), "scales differ"
+    if o["zeros_dev"] is None:
+        assert pw.zeros is None
+    else:
+        assert np.array_equal(pw.zeros.cpu().numpy().view(np.uint32), o["zeros_dev"]), "zeros differ"
+    codes, s_out, z_out = H.lib().unpack(pw)
+    torch.cuda.synchronize()
+    assert np.array_equal(codes.cpu().numpy(), o["codes"])
+    assert np.array_equal(s_out.cpu().numpy().view(np.uint16), o["s_bits"])
+    assert np.array_equal(z_out.cpu().numpy(), o["zeros"])
+
+
+@pytest.mark.parametrize("fmt", FORMATS)
+@pytest.mark.parametrize("N,K,group", SHAPES)
+def test_pack_formats_bit_exact(N, K, group, fmt):
+    w, o, pw = _prep(N, K, group, fmt)
+    _check_packed(o, pw)
+    q, s, z = H.lib().packed_bytes(N, K, group, fmt)
+    assert (q, s, z) == (o["qweight"].size, 2 * o["scales_dev"].size,
+                         0 if o["zeros_dev"] is None else 4 * o["zeros_dev"].size)
+
+
+@pytest.mark.parametrize("fmt", ["sym4", "sym8"])
+def test_pack_symmetric_edges(fmt):
+    N, K, group = 16, 256, 64
+    s = 2.0 ** -5
+    qmax = 7 if fmt == "sym4" else 127
+    j = np.arange(-qmax, qmax)[: group - 1]
+    row = np.zeros(K, dtype=np.float64)
+    row[0] = qmax * s                                    # max|w| = qmax * s: scale exactly s
+    row[1:1 + j.size] = (j + 0.5) * s                    # exact ties inside the first group
+    w = np.tile(row.astype(np.float32), (N, 1))
+    w[1] = 0.0                                           # all-zero row: scale 2^-24, code qmax + 1
+    w[2] = -1e-12                                        # scale underflows fp16
+    w[3, :group] = np.float32(-2.0 ** 17)                # near the documented |w| bound
+    w[4] = np.float32(1.5e-39)                           # fp32 subnormals
+    o = H.oracle_pack(w, group, fmt)
+    _check_packed(o, H.gpu_pack(w, group, fmt))
+
+
+def _run(kernel, x_bits, dtype, pw):
+    import torch
+    fn = {"gemv": H.lib().gemv, "gemm": H.lib().gemm, "linear": H.lib().linear}[kernel]
+    y = fn(H.to_device_bits(x_bits, dtype), pw)
+    torch.cuda.synchronize()
+    return y
+
+
+@pytest.mark.parametrize("fmt", FORMATS)
+@pytest.mark.parametrize("N,K,group", SHAPES)
+@pytest.mark.parametrize("dtype", ["f16", "bf16"])
+@pytest.mark.parametrize("kernel,M", [("gemv", 1), ("gemv", 3), ("gemm", 1), ("gemm", 17), ("gemm", 100),
+                                      ("gemm", 300), ("linear", 2)])
+def test_format_products_match_oracle(N, K, group, fmt, dtype, kernel, M):
+    w, o, pw = _prep(N, K, group, fmt)
+    x = wl.random_activations(N + K + M + len(fmt), M, K, dtype)
+    y = _run(kernel, x, dtype, pw)
+    assert y.shape == (M, N)
+    H.check_against_oracle(y, x, dtype, o, group)
+
+
+@pytest.mark.parametrize("fmt", ["sym4", "sym8"])
+@pytest.mark.parametrize("dtype", ["f16", "bf16"])
+@pytest.mark.parametrize("M", [1, 4, 40, 300])
+def test_format_one_hot_is_exact(fmt, dtype, M):
+    """Row m of x = e_{k_m}: y[m][n] == round(w_hat[n][k_m]) bit for bit, on
+    every kernel M reaches (GEMV for M = 1 and 4, small-batch and tiled GEMM)."""
+    import torch
+    N, K, group = 264, 768, 256
+    w, o, pw = _prep(N, K, group, fmt)
+    w_hat = ref.dequantize(o["codes"], o["s_bits"], o["zeros"], group)
+    ks = (np.arange(M) * 7919 + 5) % K
+    ks[0], ks[-1] = 0, K - 1
+    x32 = np.zeros((M, K), dtype=np.float32)
+    x32[np.arange(M), ks] = 1.0
+    want = ref.out_round_bits(w_hat[:, ks].T, dtype)
+    kernels = ["gemm", "linear"] + (["gemv"] if M <= 8 else [])
+    for kernel in kernels:
+        y = _run(kernel, wl.to_16bit(x32, dtype), dtype, pw)
+        got = y.cpu().view(torch.int16).numpy().view(np.uint16)
+        assert np.array_equal(got, want), kernel
+
+
+@pytest.mark.parametrize("fmt", ["sym4", "sym8"])
+@pytest.mark.parametrize("M", [1, 16, 40])
+def test_format_grouped_launch_matches_single(fmt, M):
+    import torch
+    K, group = 1024, 128
+    Ns = (1000, 136)
+    pws, os_ = [], []
+    for i, N in enumerate(Ns):
+        w, o, pw = H.prepared(("fmt-group", N, K, group), lambda N=N: wl.random_weights(400 + N, N, K), group, fmt)
+        pws.append(pw)
+        os_.append(o)
+    x = wl.random_activations(17 + M, M, K, "bf16")
+    xd = H.to_device_bits(x, "bf16")
+    ys = H.lib().linear_group([xd, xd], pws)
+    torch.cuda.synchronize()
+    for y, pw, o in zip(ys, pws, os_):
+        single = H.lib().gemm(xd, pw)
+        torch.cuda.synchronize()
+        assert torch.equal(y.view(torch.int16), single.view(torch.int16))
+        H.check_against_oracle(y, x, "bf16", o, group)
+
+
+@pytest.mark.slow
+@pytest.mark.parametrize("fmt", ["sym4", "sym8"])
+def test_format_full_size_decode_and_prefill(fmt):
+    """The 4096 x 4096 decode matrix (group 128) at M = 1 and 16 in full, and the
+    5120 x 13824 prefill matrix at M = 2048 on sampled columns."""
+    w, o, pw = H.prepared(("fmt-full", 1), lambda: wl.weights(1, 0), 128, fmt)
+    for M, dtype in ((1, "f16"), (16, "f16")):
+        x = wl.activations(1, 0, M) if M == 1 else wl.random_activations(99, M, 4096, dtype)
+        H.check_against_oracle(_run("linear", x, dtype, pw), x, dtype, o, 128)
+    H.drop((("fmt-full", 1), fmt))
+    w, o, pw = H.prepared(("fmt-full", 4), lambda: wl.weights(4, 0), 128, fmt)
+    N = w.shape[0]
+    cols = np.unique(np.concatenate([np.arange(16), N - 16 + np.arange(16),
+                                     np.random.default_rng(3).choice(N, 96, replace=False)]))
+    x = wl.activations(4, 0, 2048)
+    H.check_against_oracle(_run("linear", x, "bf16", pw), x, "bf16", o, 128, cols=cols)
+    H.drop((("fmt-full", 4), fmt))

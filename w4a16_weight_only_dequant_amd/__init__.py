@@ -3,6 +3,6 @@
 The compute lives in libw4a16.so (hand-written HIP kernels behind a C ABI,
 include/w4a16.h); this package is its thin Python binding.
 """
-from ._lib import (EXPORTED, LIB_PATH, PackedWeight, W4A16Error, Workspace, device_supported,  # noqa: F401
+from ._lib import (EXPORTED, FORMATS, LIB_PATH, PackedWeight, W4A16Error, Workspace, device_supported,  # noqa: F401
                    gemm, gemv, gemv_max_m, linear, linear_group, linear_kernel, pack, packed_bytes, raw, unpack,
                    workspace_bytes)

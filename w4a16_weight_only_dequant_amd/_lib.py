@@ -19,6 +19,9 @@ LIB_PATH = os.environ.get("W4A16_LIB") or os.path.join(_HERE, "libw4a16.so")
 W4A16_OK = 0
 W4A16_F16 = 0
 W4A16_BF16 = 1
+# weight formats (w4a16_format): 4-bit codes + fp16 scale + 4-bit zero-point per
+# group; symmetric 4-bit codes; symmetric 8-bit codes (W8A16)
+FORMATS = {"asym4": 0, "sym4": 1, "sym8": 2}
 
 if not os.path.exists(LIB_PATH):
     raise ImportError(
@@ -50,6 +53,15 @@ _SIGS = {
     "w4a16_linear": (ctypes.c_int, [_vp, _i32, _vp, _vp, _vp, _vp, _i64, _i64, _i64, _i32, _vp, _sz, _vp]),
     "w4a16_linear_group": (ctypes.c_int, [_i32, _vpp, _i32, _vpp, _vpp, _vpp, _vpp, _i64, _i64p, _i64, _i32,
                                           _vp, _sz, _vp]),
+    "w4a16_packed_bytes_fmt": (ctypes.c_int, [_i64, _i64, _i32, _i32, _szp, _szp, _szp]),
+    "w4a16_pack_fmt": (ctypes.c_int, [_vp, _i64, _i64, _i32, _i32, _vp, _vp, _vp, _vp]),
+    "w4a16_unpack_fmt": (ctypes.c_int, [_vp, _vp, _vp, _i64, _i64, _i32, _i32, _vp, _vp, _vp, _vp]),
+    "w4a16_gemv_fmt": (ctypes.c_int, [_vp, _i32, _vp, _vp, _vp, _vp, _i64, _i64, _i64, _i32, _i32, _vp, _sz, _vp]),
+    "w4a16_gemm_fmt": (ctypes.c_int, [_vp, _i32, _vp, _vp, _vp, _vp, _i64, _i64, _i64, _i32, _i32, _vp, _sz, _vp]),
+    "w4a16_linear_fmt": (ctypes.c_int, [_vp, _i32, _vp, _vp, _vp, _vp, _i64, _i64, _i64, _i32, _i32, _vp, _sz,
+                                        _vp]),
+    "w4a16_linear_group_fmt": (ctypes.c_int, [_i32, _vpp, _i32, _vpp, _vpp, _vpp, _vpp, _i64, _i64p, _i64, _i32,
+                                              _i32, _vp, _sz, _vp]),
 }
 
 EXPORTED = tuple(_SIGS)
@@ -90,10 +102,17 @@ def _dtype_code(t: torch.Tensor) -> int:
     raise TypeError(f"activations must be float16 or bfloat16, got {t.dtype}")
 
 
-def packed_bytes(N: int, K: int, group: int):
+def _fmt_code(fmt: str) -> int:
+    try:
+        return FORMATS[fmt]
+    except KeyError:
+        raise ValueError(f"unknown weight format {fmt!r}; one of {sorted(FORMATS)}") from None
+
+
+def packed_bytes(N: int, K: int, group: int, fmt: str = "asym4"):
     q, s, z = _sz(), _sz(), _sz()
-    _check("w4a16_packed_bytes", _lib.w4a16_packed_bytes(N, K, group, ctypes.byref(q), ctypes.byref(s),
-                                                         ctypes.byref(z)))
+    _check("w4a16_packed_bytes_fmt", _lib.w4a16_packed_bytes_fmt(N, K, group, _fmt_code(fmt), ctypes.byref(q),
+                                                                 ctypes.byref(s), ctypes.byref(z)))
     return q.value, s.value, z.value
 
 
@@ -126,45 +145,51 @@ def linear_kernel(M: int, N: int, K: int, group: int, dtype=torch.float16) -> st
 
 
 class PackedWeight:
-    """Packed W4A16 weight of an N x K linear layer, resident in device memory."""
+    """Packed weight of an N x K linear layer, resident in device memory."""
 
-    def __init__(self, qweight, scales, zeros, N, K, group):
-        self.qweight = qweight    # uint8 [N*K/2], device layout
-        self.scales = scales      # float16, per 128-weight column: [T][N][128/group]
-        self.zeros = zeros        # int32, per column: [T][N*128/group/8] (4-bit zero-points)
-        self.N, self.K, self.group = N, K, group
+    def __init__(self, qweight, scales, zeros, N, K, group, fmt="asym4"):
+        self.qweight = qweight    # uint8 [N*K/2] (sym8: [N*K], two planes), device layout
+        self.scales = scales      # float16, per 128-weight column: [T][N][128/group] (group 256: [G][N])
+        self.zeros = zeros        # int32 zero-point words (asym4), None for the symmetric formats
+        self.N, self.K, self.group, self.fmt = N, K, group, fmt
 
     def nbytes(self) -> int:
-        return self.qweight.numel() + 2 * self.scales.numel() + 4 * self.zeros.numel()
+        z = 4 * self.zeros.numel() if self.zeros is not None else 0
+        return self.qweight.numel() + 2 * self.scales.numel() + z
+
+    def zeros_ptr(self):
+        return self.zeros.data_ptr() if self.zeros is not None else None
 
 
-def pack(w: torch.Tensor, group: int, stream=None) -> PackedWeight:
-    """Quantise fp32 weights [N][K] (device) and pack them (w4a16_pack)."""
+def pack(w: torch.Tensor, group: int, fmt: str = "asym4", stream=None) -> PackedWeight:
+    """Quantise fp32 weights [N][K] (device) and pack them (w4a16_pack_fmt)."""
     if w.dtype != torch.float32 or w.dim() != 2 or not w.is_cuda:
         raise TypeError("w must be a 2-D float32 CUDA tensor [N][K]")
     w = w.contiguous()
     N, K = w.shape
-    qb, sb, zb = packed_bytes(N, K, group)
+    qb, sb, zb = packed_bytes(N, K, group, fmt)
     dev = w.device
     qweight = torch.empty(qb, dtype=torch.uint8, device=dev)
     scales = torch.empty(sb // 2, dtype=torch.float16, device=dev)
-    zeros = torch.empty(zb // 4, dtype=torch.int32, device=dev)
-    _check("w4a16_pack", _lib.w4a16_pack(w.data_ptr(), N, K, group, qweight.data_ptr(), scales.data_ptr(),
-                                         zeros.data_ptr(), _stream_ptr(stream)))
-    return PackedWeight(qweight, scales, zeros, N, K, group)
+    zeros = torch.empty(zb // 4, dtype=torch.int32, device=dev) if zb else None
+    _check("w4a16_pack_fmt", _lib.w4a16_pack_fmt(w.data_ptr(), N, K, group, _fmt_code(fmt), qweight.data_ptr(),
+                                                 scales.data_ptr(), zeros.data_ptr() if zeros is not None else None,
+                                                 _stream_ptr(stream)))
+    return PackedWeight(qweight, scales, zeros, N, K, group, fmt)
 
 
 def unpack(pw: PackedWeight, stream=None):
-    """Canonical view (codes u8 [N][K], scale bits int16 [G][N], zeros u8 [G][N])."""
+    """Canonical view (codes u8 [N][K], scale bits int16 [G][N], zeros u8 [G][N];
+    the symmetric formats report their fixed zero, 8 or 128)."""
     N, K, group = pw.N, pw.K, pw.group
     G = K // group
     dev = pw.qweight.device
     codes = torch.empty((N, K), dtype=torch.uint8, device=dev)
     s_out = torch.empty((G, N), dtype=torch.int16, device=dev)
     z_out = torch.empty((G, N), dtype=torch.uint8, device=dev)
-    _check("w4a16_unpack", _lib.w4a16_unpack(pw.qweight.data_ptr(), pw.scales.data_ptr(), pw.zeros.data_ptr(),
-                                             N, K, group, codes.data_ptr(), s_out.data_ptr(),
-                                             z_out.data_ptr(), _stream_ptr(stream)))
+    _check("w4a16_unpack_fmt", _lib.w4a16_unpack_fmt(pw.qweight.data_ptr(), pw.scales.data_ptr(), pw.zeros_ptr(),
+                                                     N, K, group, _fmt_code(pw.fmt), codes.data_ptr(),
+                                                     s_out.data_ptr(), z_out.data_ptr(), _stream_ptr(stream)))
     return codes, s_out, z_out
 
 
@@ -208,9 +233,10 @@ def _call(fn_name: str, x: torch.Tensor, pw: PackedWeight, out=None, workspace=N
     ws = (workspace or _default_workspace(x.device)).get(nbytes)
     ws_ptr = ws.data_ptr() if ws is not None else None
     ws_len = ws.numel() if ws is not None else 0
+    fn_name = fn_name + "_fmt"
     fn = getattr(_lib, fn_name)
     _check(fn_name, fn(x.data_ptr(), _dtype_code(x), pw.qweight.data_ptr(), pw.scales.data_ptr(),
-                       pw.zeros.data_ptr(), y.data_ptr(), M, pw.N, pw.K, pw.group, ws_ptr, ws_len,
+                       pw.zeros_ptr(), y.data_ptr(), M, pw.N, pw.K, pw.group, _fmt_code(pw.fmt), ws_ptr, ws_len,
                        _stream_ptr(stream)))
     return y
 
@@ -226,7 +252,8 @@ def gemm(x, pw, out=None, workspace=None, stream=None):
 
 
 def linear_group(xs, pws, outs=None, workspace=None, stream=None):
-    """Several layers of the same M, K, group and type in one launch (w4a16_linear_group).
+    """Several layers of the same M, K, group, format and type in one launch
+    (w4a16_linear_group_fmt).
 
     xs: list of CUDA tensors [M][K] (entries may be the same tensor); pws: list of
     PackedWeight; returns the list of outputs [M][N_p]."""
@@ -238,18 +265,19 @@ def linear_group(xs, pws, outs=None, workspace=None, stream=None):
     for x, pw in zip(xs, pws):
         if x.dim() != 2 or not x.is_cuda or x.shape != (M, K) or x.dtype != xs[0].dtype:
             raise ValueError("every x must be a CUDA tensor [M][K] of one type")
-        if pw.K != K or pw.group != group:
-            raise ValueError("every weight must share K and group")
+        if pw.K != K or pw.group != group or pw.fmt != pws[0].fmt:
+            raise ValueError("every weight must share K, group and format")
     ys = outs if outs is not None else [torch.empty((M, pw.N), dtype=xs[0].dtype, device=xs[0].device)
                                         for pw in pws]
     arr = lambda vals: (ctypes.c_void_p * count)(*vals)  # noqa: E731
     nbytes = workspace_bytes(M, max(pw.N for pw in pws), K, group)
     ws = (workspace or _default_workspace(xs[0].device)).get(nbytes)
-    _check("w4a16_linear_group", _lib.w4a16_linear_group(
+    zeros = arr([p.zeros_ptr() for p in pws]) if pws[0].zeros is not None else None
+    _check("w4a16_linear_group_fmt", _lib.w4a16_linear_group_fmt(
         count, arr([x.data_ptr() for x in xs]), _dtype_code(xs[0]), arr([p.qweight.data_ptr() for p in pws]),
-        arr([p.scales.data_ptr() for p in pws]), arr([p.zeros.data_ptr() for p in pws]),
+        arr([p.scales.data_ptr() for p in pws]), zeros,
         arr([y.data_ptr() for y in ys]), M, (ctypes.c_int64 * count)(*[p.N for p in pws]), K, group,
-        ws.data_ptr() if ws is not None else None, ws.numel() if ws is not None else 0, _stream_ptr(stream)))
+        _fmt_code(pws[0].fmt), ws.data_ptr() if ws is not None else None, ws.numel() if ws is not None else 0, _stream_ptr(stream)))
     return ys
 
 

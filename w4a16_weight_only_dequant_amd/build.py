@@ -11,7 +11,8 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 OUT = os.path.join(HERE, "libw4a16.so")
 BUILD_DIR = os.path.join(ROOT, "_build")
-SOURCES = ["api.hip", "pack.hip", "gemv.hip", "gemm.hip", "prefill.hip"]
+SOURCES = ["api.hip", "pack.hip", "gemv.hip", "gemv_sym4.hip", "gemv_sym8.hip", "gemm.hip", "gemm_sym4.hip",
+           "gemm_sym8.hip", "prefill.hip", "prefill_sym4.hip", "prefill_sym8.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = [
@@ -34,7 +35,7 @@ def _run(cmd):
     return r
 
 
-def build(verbose: bool = False, jobs: int = 4, out: str = OUT, extra_flags=(), build_dir: str = BUILD_DIR) -> str:
+def build(verbose: bool = False, jobs: int = 8, out: str = OUT, extra_flags=(), build_dir: str = BUILD_DIR) -> str:
     """Compile every HIP source for gfx950 and link libw4a16.so (next to this file by default)."""
     os.makedirs(build_dir, exist_ok=True)
     objs = []

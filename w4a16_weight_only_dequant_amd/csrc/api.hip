@@ -39,7 +39,7 @@ int gemv_max_m() {
 bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
 bool shape_ok(int64_t N, int64_t K, int32_t group) {
-    if (group != 32 && group != 64 && group != 128) return false;
+    if (group != 32 && group != 64 && group != 128 && group != 256) return false;
     if (N < 8 || N % 8 != 0) return false;
     if (K < group || K % group != 0) return false;
     // 32-bit index limits of the kernels
@@ -47,15 +47,17 @@ bool shape_ok(int64_t N, int64_t K, int32_t group) {
     return true;
 }
 
-// Byte sizes of the packed buffers: codes, then scales and zero-points per
-// 128-weight column (128/group slots per column; a short last column keeps its
-// unused slots).
-void meta_bytes(int64_t N, int64_t K, int32_t group, size_t *q, size_t *sb, size_t *zb) {
-    const int64_t gpc = 128 / group;
-    const int64_t T = (K / 32 + 3) / 4;
-    *q = (size_t)(N * K / 2);
-    *sb = (size_t)(2 * T * N * gpc);
-    *zb = (size_t)(T * N * gpc / 2);
+bool fmt_ok(int32_t fmt) { return fmt == W4A16_FMT_ASYM4 || fmt == W4A16_FMT_SYM4 || fmt == W4A16_FMT_SYM8; }
+
+// Byte sizes of the packed buffers: codes (one 4-bit plane, two for 8-bit
+// codes), then scales and zero-points per 128-weight column (128/group slots
+// per column; a short last column keeps its unused slots), or per group of
+// 256. The symmetric formats store no zero-points.
+void meta_bytes(int64_t N, int64_t K, int32_t group, int32_t fmt, size_t *q, size_t *sb, size_t *zb) {
+    const int64_t slots = group == 256 ? K / 256 : (K / 32 + 3) / 4 * (128 / group);
+    *q = (size_t)(N * K / 2) * (fmt == W4A16_FMT_SYM8 ? 2 : 1);
+    *sb = (size_t)(2 * slots * N);
+    *zb = fmt == W4A16_FMT_ASYM4 ? (size_t)(slots * N / 2) : 0;
 }
 
 struct Range {
@@ -73,19 +75,22 @@ w4a16_status check_device() {
     return w4a16_device_supported(dev);
 }
 
-// Argument checks shared by gemv / gemm / linear.
+// Argument checks shared by gemv / gemm / linear. The symmetric formats do
+// not read `zeros` (it may be NULL).
 w4a16_status check_linear(const void *x, int32_t dtype, const void *qweight, const void *scales,
                           const void *zeros, void *y, int64_t M, int64_t N, int64_t K, int32_t group,
-                          void *workspace, size_t workspace_bytes, size_t need) {
-    if (!x || !qweight || !scales || !zeros || !y) return W4A16_ERR_INVALID_ARG;
+                          int32_t fmt, void *workspace, size_t workspace_bytes, size_t need) {
+    if (!fmt_ok(fmt)) return W4A16_ERR_INVALID_ARG;
+    const bool zp = fmt == W4A16_FMT_ASYM4;
+    if (!x || !qweight || !scales || (zp && !zeros) || !y) return W4A16_ERR_INVALID_ARG;
     if (dtype != W4A16_F16 && dtype != W4A16_BF16) return W4A16_ERR_INVALID_ARG;
     if (M < 1 || M > (1LL << 24) || !shape_ok(N, K, group)) return W4A16_ERR_INVALID_ARG;
     if (M * K >= (1LL << 34)) return W4A16_ERR_INVALID_ARG;   // 32-bit activation indices (in 16-byte units)
-    if (!aligned16(x) || !aligned16(qweight) || !aligned16(scales) || !aligned16(zeros) ||
+    if (!aligned16(x) || !aligned16(qweight) || !aligned16(scales) || (zp && !aligned16(zeros)) ||
         !aligned16(y))
         return W4A16_ERR_INVALID_ARG;
     size_t qb, sb, zb;
-    meta_bytes(N, K, group, &qb, &sb, &zb);
+    meta_bytes(N, K, group, fmt, &qb, &sb, &zb);
     const Range ry = range_of(y, (size_t)(M * N * 2));
     if (overlap(ry, range_of(x, (size_t)(M * K * 2))) || overlap(ry, range_of(qweight, qb)) ||
         overlap(ry, range_of(scales, sb)) || overlap(ry, range_of(zeros, zb)))
@@ -154,6 +159,7 @@ int w4a16_layout_version(void) { return W4A16_LAYOUT_VERSION; }
 int32_t w4a16_gemv_max_m(void) { return gemv_max_m(); }
 
 int32_t w4a16_linear_kernel(int64_t M, int64_t N, int64_t K, int32_t group, int32_t dtype) {
+    // the same choice for every weight format
     if (M < 1 || M > (1LL << 24) || !shape_ok(N, K, group) || (dtype != W4A16_F16 && dtype != W4A16_BF16))
         return -1;
     if (prefer_gemv(M, N, K, group, dtype)) return 0;
@@ -176,9 +182,14 @@ w4a16_status w4a16_device_supported(int device) {
 
 w4a16_status w4a16_packed_bytes(int64_t N, int64_t K, int32_t group, size_t *qweight_bytes,
                                 size_t *scales_bytes, size_t *zeros_bytes) {
-    if (!shape_ok(N, K, group)) return W4A16_ERR_INVALID_ARG;
+    return w4a16_packed_bytes_fmt(N, K, group, W4A16_FMT_ASYM4, qweight_bytes, scales_bytes, zeros_bytes);
+}
+
+w4a16_status w4a16_packed_bytes_fmt(int64_t N, int64_t K, int32_t group, int32_t fmt, size_t *qweight_bytes,
+                                    size_t *scales_bytes, size_t *zeros_bytes) {
+    if (!shape_ok(N, K, group) || !fmt_ok(fmt)) return W4A16_ERR_INVALID_ARG;
     size_t q, sb, zb;
-    meta_bytes(N, K, group, &q, &sb, &zb);
+    meta_bytes(N, K, group, fmt, &q, &sb, &zb);
     if (qweight_bytes) *qweight_bytes = q;
     if (scales_bytes) *scales_bytes = sb;
     if (zeros_bytes) *zeros_bytes = zb;
@@ -193,13 +204,20 @@ w4a16_status w4a16_workspace_bytes(int64_t M, int64_t N, int64_t K, int32_t grou
 
 w4a16_status w4a16_pack(const float *w, int64_t N, int64_t K, int32_t group, void *qweight,
                         void *scales, void *zeros, void *stream) {
-    if (!w || !qweight || !scales || !zeros || !shape_ok(N, K, group)) return W4A16_ERR_INVALID_ARG;
-    if (!aligned16(w) || !aligned16(qweight) || !aligned16(scales) || !aligned16(zeros))
+    return w4a16_pack_fmt(w, N, K, group, W4A16_FMT_ASYM4, qweight, scales, zeros, stream);
+}
+
+w4a16_status w4a16_pack_fmt(const float *w, int64_t N, int64_t K, int32_t group, int32_t fmt, void *qweight,
+                            void *scales, void *zeros, void *stream) {
+    if (!fmt_ok(fmt)) return W4A16_ERR_INVALID_ARG;
+    const bool zp = fmt == W4A16_FMT_ASYM4;
+    if (!w || !qweight || !scales || (zp && !zeros) || !shape_ok(N, K, group)) return W4A16_ERR_INVALID_ARG;
+    if (!aligned16(w) || !aligned16(qweight) || !aligned16(scales) || (zp && !aligned16(zeros)))
         return W4A16_ERR_INVALID_ARG;
     if (((K / 32 + 3) / 4) * N > (1LL << 31)) return W4A16_ERR_INVALID_ARG;
     w4a16_status st = check_device();
     if (st != W4A16_OK) return st;
-    hipError_t e = launch_pack(w, (int)N, (int)K, group, qweight, scales, zeros,
+    hipError_t e = launch_pack(w, (int)N, (int)K, group, fmt, qweight, scales, zeros,
                                reinterpret_cast<hipStream_t>(stream));
     return e == hipSuccess ? W4A16_OK : W4A16_ERR_HIP;
 }
@@ -207,60 +225,86 @@ w4a16_status w4a16_pack(const float *w, int64_t N, int64_t K, int32_t group, voi
 w4a16_status w4a16_unpack(const void *qweight, const void *scales, const void *zeros, int64_t N,
                           int64_t K, int32_t group, uint8_t *codes, uint16_t *scales_out,
                           uint8_t *zeros_out, void *stream) {
-    if (!qweight || !scales || !zeros || !codes || !scales_out || !zeros_out ||
+    return w4a16_unpack_fmt(qweight, scales, zeros, N, K, group, W4A16_FMT_ASYM4, codes, scales_out, zeros_out,
+                            stream);
+}
+
+w4a16_status w4a16_unpack_fmt(const void *qweight, const void *scales, const void *zeros, int64_t N,
+                              int64_t K, int32_t group, int32_t fmt, uint8_t *codes, uint16_t *scales_out,
+                              uint8_t *zeros_out, void *stream) {
+    if (!fmt_ok(fmt)) return W4A16_ERR_INVALID_ARG;
+    const bool zp = fmt == W4A16_FMT_ASYM4;
+    if (!qweight || !scales || (zp && !zeros) || !codes || !scales_out || !zeros_out ||
         !shape_ok(N, K, group))
         return W4A16_ERR_INVALID_ARG;
     if (!aligned16(qweight) || !aligned16(codes)) return W4A16_ERR_INVALID_ARG;
     w4a16_status st = check_device();
     if (st != W4A16_OK) return st;
-    hipError_t e = launch_unpack(qweight, scales, zeros, (int)N, (int)K, group, codes, scales_out,
+    hipError_t e = launch_unpack(qweight, scales, zeros, (int)N, (int)K, group, fmt, codes, scales_out,
                                  zeros_out, reinterpret_cast<hipStream_t>(stream));
     return e == hipSuccess ? W4A16_OK : W4A16_ERR_HIP;
 }
 
-w4a16_status w4a16_gemv(const void *x, int32_t dtype, const void *qweight, const void *scales,
-                        const void *zeros, void *y, int64_t M, int64_t N, int64_t K, int32_t group,
-                        void *workspace, size_t workspace_bytes, void *stream) {
+w4a16_status w4a16_gemv_fmt(const void *x, int32_t dtype, const void *qweight, const void *scales,
+                            const void *zeros, void *y, int64_t M, int64_t N, int64_t K, int32_t group, int32_t fmt,
+                            void *workspace, size_t workspace_bytes, void *stream) {
     (void)workspace;
     (void)workspace_bytes;
     if (M > 8) return W4A16_ERR_INVALID_ARG;
-    w4a16_status st = check_linear(x, dtype, qweight, scales, zeros, y, M, N, K, group, nullptr, 0, 0);
+    w4a16_status st = check_linear(x, dtype, qweight, scales, zeros, y, M, N, K, group, fmt, nullptr, 0, 0);
     if (st != W4A16_OK) return st;
     st = check_device();
     if (st != W4A16_OK) return st;
     if (!gemv_fits(M, N, K, group, dtype)) return W4A16_ERR_INVALID_ARG;
     GemvPlan plan = gemv_plan(M, N, K, group);
     hipError_t e = launch_gemv(x, dtype == W4A16_BF16, qweight, scales, zeros, y, (int)M, (int)N,
-                               (int)K, group, plan, reinterpret_cast<hipStream_t>(stream));
+                               (int)K, group, fmt, plan, reinterpret_cast<hipStream_t>(stream));
     return e == hipSuccess ? W4A16_OK : W4A16_ERR_HIP;
 }
 
-w4a16_status w4a16_gemm(const void *x, int32_t dtype, const void *qweight, const void *scales,
+w4a16_status w4a16_gemv(const void *x, int32_t dtype, const void *qweight, const void *scales,
                         const void *zeros, void *y, int64_t M, int64_t N, int64_t K, int32_t group,
                         void *workspace, size_t workspace_bytes, void *stream) {
+    return w4a16_gemv_fmt(x, dtype, qweight, scales, zeros, y, M, N, K, group, W4A16_FMT_ASYM4, workspace,
+                          workspace_bytes, stream);
+}
+
+w4a16_status w4a16_gemm_fmt(const void *x, int32_t dtype, const void *qweight, const void *scales,
+                            const void *zeros, void *y, int64_t M, int64_t N, int64_t K, int32_t group, int32_t fmt,
+                            void *workspace, size_t workspace_bytes, void *stream) {
     const size_t need = (M >= 1 && M <= (1LL << 24) && shape_ok(N, K, group))
                             ? gemm_need(M, N, K, group) : 0;
-    w4a16_status st = check_linear(x, dtype, qweight, scales, zeros, y, M, N, K, group, workspace,
+    w4a16_status st = check_linear(x, dtype, qweight, scales, zeros, y, M, N, K, group, fmt, workspace,
                                    workspace_bytes, need);
     if (st != W4A16_OK) return st;
     st = check_device();
     if (st != W4A16_OK) return st;
     GemmPlan plan = gemm_plan(M, N, K, group);
     hipError_t e = launch_gemm(x, dtype == W4A16_BF16, qweight, scales, zeros, y, (int)M, (int)N,
-                               (int)K, group, plan, reinterpret_cast<hipStream_t>(stream));
+                               (int)K, group, fmt, plan, reinterpret_cast<hipStream_t>(stream));
     return e == hipSuccess ? W4A16_OK : W4A16_ERR_HIP;
 }
 
-w4a16_status w4a16_linear_group(int32_t count, const void *const *x, int32_t dtype, const void *const *qweight,
-                                const void *const *scales, const void *const *zeros, void *const *y, int64_t M,
-                                const int64_t *N, int64_t K, int32_t group, void *workspace,
-                                size_t workspace_bytes, void *stream) {
-    if (count < 1 || count > kMaxGroup || !x || !qweight || !scales || !zeros || !y || !N)
+w4a16_status w4a16_gemm(const void *x, int32_t dtype, const void *qweight, const void *scales,
+                        const void *zeros, void *y, int64_t M, int64_t N, int64_t K, int32_t group,
+                        void *workspace, size_t workspace_bytes, void *stream) {
+    return w4a16_gemm_fmt(x, dtype, qweight, scales, zeros, y, M, N, K, group, W4A16_FMT_ASYM4, workspace,
+                          workspace_bytes, stream);
+}
+
+w4a16_status w4a16_linear_group_fmt(int32_t count, const void *const *x, int32_t dtype,
+                                    const void *const *qweight, const void *const *scales,
+                                    const void *const *zeros, void *const *y, int64_t M, const int64_t *N,
+                                    int64_t K, int32_t group, int32_t fmt, void *workspace, size_t workspace_bytes,
+                                    void *stream) {
+    const bool zp = fmt == W4A16_FMT_ASYM4;
+    if (count < 1 || count > kMaxGroup || !x || !qweight || !scales || (zp && !zeros) || !y || !N)
         return W4A16_ERR_INVALID_ARG;
+    auto zero_ptr = [&](int p) -> const void * { return zp ? zeros[p] : nullptr; };
     int64_t n_total = 0;
     for (int p = 0; p < count; ++p) {
-        const w4a16_status st = check_linear(x[p], dtype, qweight[p], scales[p], zeros[p], y[p], M, N[p], K,
-                                             group, workspace, workspace_bytes, 0);
+        const w4a16_status st = check_linear(x[p], dtype, qweight[p], scales[p], zero_ptr(p), y[p], M, N[p], K,
+                                             group, fmt, workspace, workspace_bytes, 0);
         if (st != W4A16_OK) return st;
         n_total += N[p];
     }
@@ -270,9 +314,9 @@ w4a16_status w4a16_linear_group(int32_t count, const void *const *x, int32_t dty
         for (int q = 0; q < count; ++q) {
             if (q == p) continue;
             size_t qb, sb, zb;
-            meta_bytes(N[q], K, group, &qb, &sb, &zb);
+            meta_bytes(N[q], K, group, fmt, &qb, &sb, &zb);
             if (overlap(ry, range_of(x[q], (size_t)(M * K * 2))) || overlap(ry, range_of(qweight[q], qb)) ||
-                overlap(ry, range_of(scales[q], sb)) || overlap(ry, range_of(zeros[q], zb)) ||
+                overlap(ry, range_of(scales[q], sb)) || (zp && overlap(ry, range_of(zeros[q], zb))) ||
                 overlap(ry, range_of(y[q], (size_t)(M * N[q] * 2))))
                 return W4A16_ERR_INVALID_ARG;
         }
@@ -282,8 +326,8 @@ w4a16_status w4a16_linear_group(int32_t count, const void *const *x, int32_t dty
     const GemmPlan plan = gemm_plan(M, n_total, K, group);
     if (plan.kind != 0) {   // large M: one tiled launch per problem
         for (int p = 0; p < count; ++p) {
-            st = w4a16_gemm(x[p], dtype, qweight[p], scales[p], zeros[p], y[p], M, N[p], K, group, workspace,
-                            workspace_bytes, stream);
+            st = w4a16_gemm_fmt(x[p], dtype, qweight[p], scales[p], zero_ptr(p), y[p], M, N[p], K, group, fmt,
+                                workspace, workspace_bytes, stream);
             if (st != W4A16_OK) return st;
         }
         return W4A16_OK;
@@ -294,23 +338,38 @@ w4a16_status w4a16_linear_group(int32_t count, const void *const *x, int32_t dty
         tab.x[p] = x[p];
         tab.qweight[p] = qweight[p];
         tab.scales[p] = scales[p];
-        tab.zeros[p] = zeros[p];
+        tab.zeros[p] = zero_ptr(p);
         tab.y[p] = y[p];
         tab.N[p] = (int)N[p];
     }
-    hipError_t e = launch_gemm_group(tab, dtype == W4A16_BF16, (int)M, (int)K, group, plan,
+    hipError_t e = launch_gemm_group(tab, dtype == W4A16_BF16, (int)M, (int)K, group, fmt, plan,
                                      reinterpret_cast<hipStream_t>(stream));
     return e == hipSuccess ? W4A16_OK : W4A16_ERR_HIP;
+}
+
+w4a16_status w4a16_linear_group(int32_t count, const void *const *x, int32_t dtype, const void *const *qweight,
+                                const void *const *scales, const void *const *zeros, void *const *y, int64_t M,
+                                const int64_t *N, int64_t K, int32_t group, void *workspace,
+                                size_t workspace_bytes, void *stream) {
+    return w4a16_linear_group_fmt(count, x, dtype, qweight, scales, zeros, y, M, N, K, group, W4A16_FMT_ASYM4,
+                                  workspace, workspace_bytes, stream);
+}
+
+w4a16_status w4a16_linear_fmt(const void *x, int32_t dtype, const void *qweight, const void *scales,
+                              const void *zeros, void *y, int64_t M, int64_t N, int64_t K, int32_t group,
+                              int32_t fmt, void *workspace, size_t workspace_bytes, void *stream) {
+    if (prefer_gemv(M, N, K, group, dtype))
+        return w4a16_gemv_fmt(x, dtype, qweight, scales, zeros, y, M, N, K, group, fmt, workspace,
+                              workspace_bytes, stream);
+    return w4a16_gemm_fmt(x, dtype, qweight, scales, zeros, y, M, N, K, group, fmt, workspace,
+                          workspace_bytes, stream);
 }
 
 w4a16_status w4a16_linear(const void *x, int32_t dtype, const void *qweight, const void *scales,
                           const void *zeros, void *y, int64_t M, int64_t N, int64_t K, int32_t group,
                           void *workspace, size_t workspace_bytes, void *stream) {
-    if (prefer_gemv(M, N, K, group, dtype))
-        return w4a16_gemv(x, dtype, qweight, scales, zeros, y, M, N, K, group, workspace,
-                          workspace_bytes, stream);
-    return w4a16_gemm(x, dtype, qweight, scales, zeros, y, M, N, K, group, workspace,
-                      workspace_bytes, stream);
+    return w4a16_linear_fmt(x, dtype, qweight, scales, zeros, y, M, N, K, group, W4A16_FMT_ASYM4, workspace,
+                            workspace_bytes, stream);
 }
 
 }  // extern "C"

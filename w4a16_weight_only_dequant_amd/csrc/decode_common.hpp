@@ -26,13 +26,27 @@ __device__ inline uint32_t vconst(uint32_t c) {
 
 __device__ inline uint32_t and_or(uint32_t a, uint32_t mask, uint32_t bits) { return (a & mask) | bits; }
 
+// f16_magic16 / bf16_magic16 are the same magic numbers times 16 (exponent
+// + 4): (d & 0x000F000F) | magic16 is (16384 + 16 q) in fp16, (2048 + 16 q)
+// in bf16, the high nibble of an 8-bit code already weighted by 16.
 struct UnpackConsts {
-    uint32_t lo_mask, hi_mask, f16_magic, bf16_magic;
+    uint32_t lo_mask, hi_mask, f16_magic, bf16_magic, f16_magic16, bf16_magic16;
 };
 
 __device__ inline UnpackConsts unpack_consts() {
-    return UnpackConsts{vconst(0x000F000Fu), vconst(0x00F000F0u), vconst(0x64006400u), vconst(0x43004300u)};
+    return UnpackConsts{vconst(0x000F000Fu), vconst(0x00F000F0u), vconst(0x64006400u),
+                        vconst(0x43004300u), vconst(0x74007400u), vconst(0x45004500u)};
 }
+
+// Weight formats (compile-time kernel parameter): kAsym4 reads a 4-bit
+// zero-point per group, kSym4 and kSym8 have the fixed zero 8 / 128 and no
+// zero-point loads; kSym8 codes are two 4-bit planes (low nibbles, then high
+// nibbles), each in the packed layout of the 4-bit formats.
+template <int FMT> struct FormatTraits {
+    static constexpr bool has_zeros = FMT == kAsym4;
+    static constexpr bool two_planes = FMT == kSym8;
+    static constexpr uint32_t fixed_zero = FMT == kSym8 ? 128u : 8u;
+};
 
 // One dword (8 codes of one k-slice, even k in the low half-word) -> four
 // fp16 pairs (k0,k1) (k2,k3) (k4,k5) (k6,k7) holding q - z exactly.
@@ -54,12 +68,69 @@ __device__ inline void unpack_f16(uint32_t d, uint32_t z, const UnpackConsts &uc
     t[3] = __builtin_bit_cast(uint32_t, __builtin_elementwise_fma(h3, sixteenth, b));
 }
 
+// Two dwords of the two planes of 8-bit codes c = lo + 16 hi (the same
+// k-slice) -> four fp16 pairs holding c - 128 exactly. Pairs (k0,k1): from
+// 1024 + lo and 16384 + 16 hi, (16384 + 16 hi - 17536) + (1024 + lo); pairs
+// (k2,k3): from 1024 + 16 lo and 16384 + 256 hi, both scaled by 1/16 in two
+// fmas. Every intermediate is an integer below 2048 in magnitude, so exact.
+__device__ inline void unpack_f16_s8(uint32_t dl, uint32_t dh, const UnpackConsts &uc, uint32_t (&t)[4]) {
+    const half2_t c0 = {(_Float16)-17536.0f, (_Float16)-17536.0f};
+    const half2_t c1 = {(_Float16)-1216.0f, (_Float16)-1216.0f};
+    const half2_t sixteenth = {(_Float16)0.0625f, (_Float16)0.0625f};
+    const uint32_t dl8 = dl >> 8, dh8 = dh >> 8;
+    auto even = [&](uint32_t a, uint32_t b) {
+        const half2_t l = __builtin_bit_cast(half2_t, and_or(a, uc.lo_mask, uc.f16_magic));
+        const half2_t h = __builtin_bit_cast(half2_t, and_or(b, uc.lo_mask, uc.f16_magic16));
+        return __builtin_bit_cast(uint32_t, (h + c0) + l);
+    };
+    auto odd = [&](uint32_t a, uint32_t b) {
+        const half2_t l = __builtin_bit_cast(half2_t, and_or(a, uc.hi_mask, uc.f16_magic));
+        const half2_t h = __builtin_bit_cast(half2_t, and_or(b, uc.hi_mask, uc.f16_magic16));
+        return __builtin_bit_cast(uint32_t, __builtin_elementwise_fma(
+                                                l, sixteenth, __builtin_elementwise_fma(h, sixteenth, c1)));
+    };
+    t[0] = even(dl, dh);
+    t[1] = odd(dl, dh);
+    t[2] = even(dl8, dh8);
+    t[3] = odd(dl8, dh8);
+}
+
+// The fp16 operands of one k-slice of a format: exact (code - zero) pairs.
+template <int FMT>
+__device__ inline void unpack_f16_fmt(uint32_t d, uint32_t dh, uint32_t z, const UnpackConsts &uc,
+                                      uint32_t (&t)[4]) {
+    if constexpr (FormatTraits<FMT>::two_planes)
+        unpack_f16_s8(d, dh, uc, t);
+    else
+        unpack_f16(d, z, uc, t);
+}
+
 // One dword -> four bf16 pairs holding 128 + q (exact: 7 mantissa bits).
 __device__ inline void unpack_bf16_magic(uint32_t d, const UnpackConsts &uc, uint32_t (&t)[4]) {
     t[0] = and_or(d, uc.lo_mask, uc.bf16_magic);
     t[1] = and_or(d >> 4, uc.lo_mask, uc.bf16_magic);
     t[2] = and_or(d >> 8, uc.lo_mask, uc.bf16_magic);
     t[3] = and_or(d >> 12, uc.lo_mask, uc.bf16_magic);
+}
+
+// The high-nibble plane of 8-bit codes -> four bf16 pairs holding
+// 16 (128 + hi) = 2048 + 16 hi (exact: 16 times an 8-bit integer).
+__device__ inline void unpack_bf16_magic16(uint32_t d, const UnpackConsts &uc, uint32_t (&t)[4]) {
+    t[0] = and_or(d, uc.lo_mask, uc.bf16_magic16);
+    t[1] = and_or(d >> 4, uc.lo_mask, uc.bf16_magic16);
+    t[2] = and_or(d >> 8, uc.lo_mask, uc.bf16_magic16);
+    t[3] = and_or(d >> 12, uc.lo_mask, uc.bf16_magic16);
+}
+
+// Offset that the bf16 magic operands of a format add per activation: a dot
+// product of x with them equals sum x (code - z) + bias(z) * sum x, where
+// bias = 128 + z for 4-bit codes and 128 + 16 * 128 + 128 = 2304 for 8-bit ones.
+template <int FMT>
+__device__ inline float bf16_magic_bias(uint32_t z) {
+    if constexpr (FormatTraits<FMT>::two_planes)
+        return 2304.0f;
+    else
+        return (float)(128u + z);
 }
 
 // The K-slice of one wave, in columns [t_begin, t_end); t_full ends the run of

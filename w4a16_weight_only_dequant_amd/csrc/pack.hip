@@ -1,11 +1,15 @@
 // Offline quantise + pack, and the inverse view used by tests and tools.
 //
-// Quantiser: groupwise asymmetric round-to-nearest. The rounding step
-// q = round(w / scale) is the naive quantiser of "Quantization Is Not a Zip
-// File" (section 3), applied per group of 32/64/128 weights ("Block
-// locality", same section); the zero-point and (q - zero) * scale
-// reconstruction follow the asymmetric example of the instagit comparison
-// page ("Practical Code Examples"). Every step is IEEE fp32 so that the integer
+// Quantiser: groupwise round-to-nearest. The rounding step q = round(w /
+// scale) is the naive quantiser of "Quantization Is Not a Zip File" (section
+// 3), applied per group of 32/64/128 weights ("Block locality", same section)
+// or of 256 (the K-quant super-block size in that page's table of GGUF
+// names). The zero-point format (asym4) follows the asymmetric example of the
+// instagit comparison page ("Practical Code Examples"): range [min, max]
+// including zero, (q - zero) * scale. The symmetric formats (sym4, sym8 =
+// W8A16) follow its symmetric INT8 scheme ("INT8: Symmetric Integer
+// Quantization"): scale max|w| / qmax, codes clamped to the signed range,
+// stored offset by qmax + 1 so that they are unsigned. Every step is IEEE fp32 so that the integer
 // codes are reproducible bit for bit: min/max are exact, the two divisions are
 // correctly rounded (never a reciprocal multiply), rint rounds half to even,
 // and the fp16 scale conversion is round-to-nearest-even with subnormals.
@@ -14,83 +18,98 @@
 namespace w4a16 {
 namespace {
 
-// One thread per (row n, column t of 128 weights): quantises the column's
-// 128/GROUP groups of row n, writes their codes, scales and zero-points.
-template <int GROUP>
+// One thread per (row n, span u of K): a span is one 128-weight column for
+// groups of at most 128 weights (its 128/GROUP groups), one group of 256
+// otherwise. The thread quantises its groups of row n in two passes over the
+// fp32 weights (range, then codes) and writes their codes, scales and, for
+// the zero-point format, zero-points.
+template <int GROUP, int FMT>
 __global__ __launch_bounds__(256) void pack_kernel(const float *__restrict__ w, int N, int K,
                                                    uint32_t *__restrict__ qweight,
                                                    uint16_t *__restrict__ scales,
                                                    uint32_t *__restrict__ zeros) {
+    using FT = FormatTraits<FMT>;
+    constexpr int SPAN = GROUP > kColumn ? GROUP : kColumn;
+    constexpr int GPS = SPAN / GROUP;       // groups per span (4, 2, 1, 1)
     constexpr int CPG = GROUP / kChunk;     // chunks per group
-    constexpr int GPC = kColumn / GROUP;    // groups per column
-    const int C = K / kChunk;
-    const int T = (C + kColChunks - 1) / kColChunks;
+    constexpr int QMAX = FMT == kSym8 ? 127 : 7;   // symmetric: codes q + QMAX + 1, q in [-QMAX-1, QMAX]
+    const int U = (K + SPAN - 1) / SPAN;
     const int G = K / GROUP;
-    const int64_t tid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;   // (t, n), n fastest
-    const bool active = tid < (int64_t)T * N;
+    const int64_t tid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;   // (u, n), n fastest
+    const bool active = tid < (int64_t)U * N;
     const int n = active ? (int)(tid % N) : 0;
-    const int t = active ? (int)(tid / N) : 0;
+    const int u = active ? (int)(tid / N) : 0;
+    const int64_t plane = (int64_t)N * K / 8;   // dwords of one 4-bit plane
 
-    uint32_t znib = 0;   // the GPC zero-points of (t, n), 4 bits each
-#pragma unroll
-    for (int e = 0; e < GPC; ++e) {
-        const int g = t * GPC + e;
+    uint32_t znib = 0;   // the GPS zero-points of (u, n), 4 bits each
+    for (int e = 0; e < GPS; ++e) {
+        const int g = u * GPS + e;
         const bool real = active && g < G;
-        float vals[GROUP];
-        float lo = 0.0f, hi = 0.0f;   // the range always contains zero
+        const float4 *src = reinterpret_cast<const float4 *>(w + (int64_t)n * K + (int64_t)(real ? g : 0) * GROUP);
+        // 1. range: [min(0, min w), max(0, max w)] or max|w|
+        float lo = 0.0f, hi = 0.0f, amax = 0.0f;
         if (real) {
-            const float4 *src = reinterpret_cast<const float4 *>(w + (int64_t)n * K + (int64_t)g * GROUP);
-#pragma unroll
             for (int i = 0; i < GROUP / 4; ++i) {
                 const float4 v = src[i];
-                vals[4 * i + 0] = v.x;
-                vals[4 * i + 1] = v.y;
-                vals[4 * i + 2] = v.z;
-                vals[4 * i + 3] = v.w;
+                lo = fminf(fminf(fminf(lo, v.x), fminf(v.y, v.z)), v.w);
+                hi = fmaxf(fmaxf(fmaxf(hi, v.x), fmaxf(v.y, v.z)), v.w);
             }
-#pragma unroll
-            for (int i = 0; i < GROUP; ++i) {
-                lo = fminf(lo, vals[i]);
-                hi = fmaxf(hi, vals[i]);
-            }
+            amax = fmaxf(-lo, hi);
         }
-        const float s32 = (hi - lo) / 15.0f;
+        // 2. scale, rounded once to fp16 (zero -> smallest positive fp16, 2^-24)
+        const float s32 = FT::has_zeros ? (hi - lo) / 15.0f : amax / (float)QMAX;
         uint16_t sbits = f32_to_f16_bits(s32);
-        if (sbits == 0) sbits = 1;                           // smallest positive fp16, 2^-24
+        if (sbits == 0) sbits = 1;
         const float sc = (float)__builtin_bit_cast(_Float16, sbits);
-        int z = (int)rintf(-lo / sc);
-        z = z < 0 ? 0 : (z > 15 ? 15 : z);
+        int z = 0;
+        if constexpr (FT::has_zeros) {
+            z = (int)rintf(-lo / sc);
+            z = z < 0 ? 0 : (z > 15 ? 15 : z);
+        }
+        // 3. codes, one dword (8 consecutive k) at a time
         if (real) {
-#pragma unroll
             for (int c = 0; c < CPG; ++c) {
 #pragma unroll
                 for (int d = 0; d < 4; ++d) {
-                    uint32_t word = 0;
+                    const float4 a = src[c * 8 + d * 2], b = src[c * 8 + d * 2 + 1];
+                    const float v[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
+                    uint32_t word = 0, word_hi = 0;
 #pragma unroll
                     for (int i = 0; i < 8; ++i) {
-                        int q = (int)rintf(vals[c * 32 + d * 8 + i] / sc) + z;
-                        q = q < 0 ? 0 : (q > 15 ? 15 : q);
+                        int q = (int)rintf(v[i] / sc);
+                        if constexpr (FT::has_zeros) {
+                            q += z;
+                            q = q < 0 ? 0 : (q > 15 ? 15 : q);
+                        } else {
+                            q = q < -QMAX - 1 ? -QMAX - 1 : (q > QMAX ? QMAX : q);
+                            q += QMAX + 1;
+                        }
                         const int p = (i >> 1) + 4 * (i & 1);   // even k low half, odd k high half
-                        word |= (uint32_t)q << (4 * p);
+                        word |= (uint32_t)(q & 0xF) << (4 * p);
+                        word_hi |= (uint32_t)(q >> 4) << (4 * p);
                     }
-                    qweight[dword_offset(n, g * CPG + c, d, N, K)] = word;
+                    const int64_t off = dword_offset(n, g * CPG + c, d, N, K);
+                    qweight[off] = word;
+                    if constexpr (FT::two_planes) qweight[plane + off] = word_hi;
                 }
             }
         }
-        if (active) scales[((int64_t)t * N + n) * GPC + e] = real ? sbits : (uint16_t)0;
+        if (active) scales[((int64_t)u * N + n) * GPS + e] = real ? sbits : (uint16_t)0;
         znib |= (real ? (uint32_t)z : 0u) << (4 * e);
     }
-    // zeros: word (t, i) holds the nibbles of rows 8/GPC*i .. 8/GPC*i + 8/GPC-1;
-    // N % 8 == 0 and tid runs n fastest, so those rows sit in neighbouring lanes
-    constexpr int RPW = 8 / GPC;    // rows per zero word
-    uint32_t zw = active ? znib << (4 * GPC * (n % RPW)) : 0u;
+    if constexpr (FT::has_zeros) {
+        // zeros: word (u, i) holds the nibbles of rows 8/GPS*i .. 8/GPS*i + 8/GPS-1;
+        // N % 8 == 0 and tid runs n fastest, so those rows sit in neighbouring lanes
+        constexpr int RPW = 8 / GPS;    // rows per zero word
+        uint32_t zw = active ? znib << (4 * GPS * (n % RPW)) : 0u;
 #pragma unroll
-    for (int off = 1; off < RPW; off <<= 1) zw |= __shfl_xor(zw, off, 64);
-    if (active && n % RPW == 0) zeros[(int64_t)t * (N / RPW) + n / RPW] = zw;
+        for (int off = 1; off < RPW; off <<= 1) zw |= __shfl_xor(zw, off, 64);
+        if (active && n % RPW == 0) zeros[(int64_t)u * (N / RPW) + n / RPW] = zw;
+    }
 }
 
 __global__ __launch_bounds__(256) void unpack_codes_kernel(const uint32_t *__restrict__ qweight,
-                                                           int N, int K,
+                                                           int N, int K, int planes,
                                                            uint8_t *__restrict__ codes) {
     // one thread per (n, 8-weight dword) in canonical order
     const int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
@@ -101,64 +120,88 @@ __global__ __launch_bounds__(256) void unpack_codes_kernel(const uint32_t *__res
     const int c = kd / 4, j = kd % 4;
     const int64_t dword = dword_offset(n, c, j, N, K);
     const uint32_t word = qweight[dword];
+    const uint32_t word_hi = planes == 2 ? qweight[(int64_t)N * KD + dword] : 0u;   // 8-bit codes: high nibbles
     uint8_t out[8];
 #pragma unroll
-    for (int i = 0; i < 8; ++i) out[i] = (word >> (4 * ((i >> 1) + 4 * (i & 1)))) & 0xF;
+    for (int i = 0; i < 8; ++i) {
+        const int p = 4 * ((i >> 1) + 4 * (i & 1));
+        out[i] = ((word >> p) & 0xF) | (((word_hi >> p) & 0xF) << 4);
+    }
     uint2 packed;
     packed.x = out[0] | (out[1] << 8) | (out[2] << 16) | ((uint32_t)out[3] << 24);
     packed.y = out[4] | (out[5] << 8) | (out[6] << 16) | ((uint32_t)out[7] << 24);
     *reinterpret_cast<uint2 *>(codes + (int64_t)n * K + 8 * kd) = packed;
 }
 
+// fixed_zero: 0 when the zero-points are read from `zeros`, else the
+// symmetric formats' fixed zero (8 or 128), written for every group.
 template <int GROUP>
 __global__ __launch_bounds__(256) void unpack_meta_kernel(const uint16_t *__restrict__ scales,
                                                           const uint32_t *__restrict__ zeros,
-                                                          int N, int G, uint16_t *__restrict__ s_out,
+                                                          int N, int G, int fixed_zero, uint16_t *__restrict__ s_out,
                                                           uint8_t *__restrict__ z_out) {
-    constexpr int GPC = kColumn / GROUP;
+    constexpr int GPS = GROUP < kColumn ? kColumn / GROUP : 1;   // metadata slots per span
     const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;   // canonical (g, n)
     if (i >= (int64_t)G * N) return;
     const int g = (int)(i / N), n = (int)(i % N);
-    const int t = g / GPC, e = g % GPC;
-    s_out[i] = scales[((int64_t)t * N + n) * GPC + e];
-    const int64_t nib = (int64_t)t * N * GPC + (int64_t)n * GPC + e;
+    const int t = g / GPS, e = g % GPS;
+    s_out[i] = scales[((int64_t)t * N + n) * GPS + e];
+    if (fixed_zero) {
+        z_out[i] = (uint8_t)fixed_zero;
+        return;
+    }
+    const int64_t nib = (int64_t)t * N * GPS + (int64_t)n * GPS + e;
     z_out[i] = (zeros[nib / 8] >> (4 * (nib % 8))) & 0xF;
 }
 
-}  // namespace
-
-hipError_t launch_pack(const float *w, int N, int K, int group, void *qweight, void *scales,
-                       void *zeros, hipStream_t stream) {
-    const int64_t total = ceil_div(K / kChunk, kColChunks) * N;   // (column, row) pairs
+template <int FMT>
+hipError_t launch_pack_fmt(const float *w, int N, int K, int group, uint32_t *q, uint16_t *s, uint32_t *z,
+                           hipStream_t stream) {
+    const int span = group > kColumn ? group : kColumn;
+    const int64_t total = ceil_div(K, span) * N;   // (span, row) pairs
     const dim3 block(256);
     const dim3 grid((unsigned)ceil_div(total, 256));
-    auto *q = reinterpret_cast<uint32_t *>(qweight);
-    auto *s = reinterpret_cast<uint16_t *>(scales);
-    auto *z = reinterpret_cast<uint32_t *>(zeros);
     switch (group) {
-        case 32: hipLaunchKernelGGL(pack_kernel<32>, grid, block, 0, stream, w, N, K, q, s, z); break;
-        case 64: hipLaunchKernelGGL(pack_kernel<64>, grid, block, 0, stream, w, N, K, q, s, z); break;
-        default: hipLaunchKernelGGL(pack_kernel<128>, grid, block, 0, stream, w, N, K, q, s, z); break;
+        case 32: hipLaunchKernelGGL((pack_kernel<32, FMT>), grid, block, 0, stream, w, N, K, q, s, z); break;
+        case 64: hipLaunchKernelGGL((pack_kernel<64, FMT>), grid, block, 0, stream, w, N, K, q, s, z); break;
+        case 128: hipLaunchKernelGGL((pack_kernel<128, FMT>), grid, block, 0, stream, w, N, K, q, s, z); break;
+        default: hipLaunchKernelGGL((pack_kernel<256, FMT>), grid, block, 0, stream, w, N, K, q, s, z); break;
     }
     return hipGetLastError();
 }
 
+}  // namespace
+
+hipError_t launch_pack(const float *w, int N, int K, int group, int fmt, void *qweight, void *scales,
+                       void *zeros, hipStream_t stream) {
+    auto *q = reinterpret_cast<uint32_t *>(qweight);
+    auto *s = reinterpret_cast<uint16_t *>(scales);
+    auto *z = reinterpret_cast<uint32_t *>(zeros);
+    switch (fmt) {
+        case kSym4: return launch_pack_fmt<kSym4>(w, N, K, group, q, s, z, stream);
+        case kSym8: return launch_pack_fmt<kSym8>(w, N, K, group, q, s, z, stream);
+        default: return launch_pack_fmt<kAsym4>(w, N, K, group, q, s, z, stream);
+    }
+}
+
 hipError_t launch_unpack(const void *qweight, const void *scales, const void *zeros, int N, int K,
-                         int group, uint8_t *codes, uint16_t *scales_out, uint8_t *zeros_out,
+                         int group, int fmt, uint8_t *codes, uint16_t *scales_out, uint8_t *zeros_out,
                          hipStream_t stream) {
     const int64_t nd = (int64_t)N * (K / 8);
     hipLaunchKernelGGL(unpack_codes_kernel, dim3((unsigned)ceil_div(nd, 256)), dim3(256), 0, stream,
-                       reinterpret_cast<const uint32_t *>(qweight), N, K, codes);
+                       reinterpret_cast<const uint32_t *>(qweight), N, K, fmt == kSym8 ? 2 : 1, codes);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     const int G = K / group;
+    const int fz = fmt == kSym8 ? 128 : (fmt == kSym4 ? 8 : 0);
     const dim3 grid((unsigned)ceil_div((int64_t)G * N, 256));
     auto *sc = reinterpret_cast<const uint16_t *>(scales);
     auto *zp = reinterpret_cast<const uint32_t *>(zeros);
     switch (group) {
-        case 32: hipLaunchKernelGGL(unpack_meta_kernel<32>, grid, dim3(256), 0, stream, sc, zp, N, G, scales_out, zeros_out); break;
-        case 64: hipLaunchKernelGGL(unpack_meta_kernel<64>, grid, dim3(256), 0, stream, sc, zp, N, G, scales_out, zeros_out); break;
-        default: hipLaunchKernelGGL(unpack_meta_kernel<128>, grid, dim3(256), 0, stream, sc, zp, N, G, scales_out, zeros_out); break;
+        case 32: hipLaunchKernelGGL(unpack_meta_kernel<32>, grid, dim3(256), 0, stream, sc, zp, N, G, fz, scales_out, zeros_out); break;
+        case 64: hipLaunchKernelGGL(unpack_meta_kernel<64>, grid, dim3(256), 0, stream, sc, zp, N, G, fz, scales_out, zeros_out); break;
+        case 128: hipLaunchKernelGGL(unpack_meta_kernel<128>, grid, dim3(256), 0, stream, sc, zp, N, G, fz, scales_out, zeros_out); break;
+        default: hipLaunchKernelGGL(unpack_meta_kernel<256>, grid, dim3(256), 0, stream, sc, zp, N, G, fz, scales_out, zeros_out); break;
     }
     return hipGetLastError();
 }

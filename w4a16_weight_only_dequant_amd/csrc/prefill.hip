@@ -1,374 +1,10 @@
-// Matrix-core GEMM of the W4A16 linear layer for larger batches and prefill
-// (M above the small-batch kernels' range): y[m][n] = sum_k x[m][k] * w_hat[n][k].
-//
-// At prefill the same packed weights serve many tokens, so the layer turns
-// compute bound and the dequantisation sits on the critical path of a dense
-// matrix product ("Weight-Only Quantisation", the FAQ answers on batch size
-// and on where the time goes; "Weight-Only Quantization Explained", the
-// section on where the method stops paying). Each workgroup therefore
-// rebuilds its weight tile once, in LDS, as 16-bit values w_hat = s*(q - z)
-// (one rounding from the exact product), and feeds the matrix cores from
-// there ("Weight-Only Quantisation": the low-bit weights are turned back into
-// 16-bit values right before the multiply).
-//
-// Tiling (gfx950, wave64): a workgroup computes a BM x BN tile of y with
-// WM x WN waves (4, or 8 for the 256 x 256 tile: two per SIMD), each owning a
-// (BM/WM) x (BN/WN) sub-tile as 32x32 blocks of
-// v_mfma_f32_32x32x16 accumulators (fp32). K advances in steps of 64 through
-// two LDS buffers: while the waves multiply out of one buffer they write the
-// next step's activations and dequantised weights into the other, and the
-// global loads for the step after that are already in flight. Both LDS tiles
-// are [row][64 k] 16-bit with the eight 16-byte units of a row XOR-swizzled
-// (swz below), so the MFMA operand reads (32 rows, same k) and the tile writes
-// are free of bank conflicts. The packed weights arrive one 128-weight
-// column at a time (16-byte records, one KiB per 16 rows) and serve two steps.
-#include <stdlib.h>
-
-#include "decode_common.hpp"
+// Tiled matrix-core path (large M), host side: the tile choice and the
+// dispatch over the weight formats. The kernel is in prefill_kernel.hpp; each
+// weight format is compiled in its own translation unit (this one: the 4-bit
+// zero-point format; prefill_sym4.hip, prefill_sym8.hip).
+#include "prefill_kernel.hpp"
 
 namespace w4a16 {
-namespace {
-
-typedef _Float16 h8_t __attribute__((ext_vector_type(8)));
-typedef __bf16 b8_t __attribute__((ext_vector_type(8)));
-typedef float f16_t __attribute__((ext_vector_type(16)));
-typedef float float2_t __attribute__((ext_vector_type(2)));
-
-constexpr int kStepK = 64;                    // k per LDS step
-struct Plain { static constexpr bool value = false; };
-struct Masked { static constexpr bool value = true; };
-constexpr Plain kPlain{};
-constexpr Masked kMasked{};
-constexpr int kUnits = kStepK / 8;            // 16-byte units per tile row
-
-template <bool BF>
-__device__ inline f16_t mfma32x32x16(const uint4 &a, const uint4 &b, f16_t c) {
-    if constexpr (BF)
-        return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(b8_t, a), __builtin_bit_cast(b8_t, b),
-                                                        c, 0, 0, 0);
-    else
-        return __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(h8_t, a), __builtin_bit_cast(h8_t, b),
-                                                       c, 0, 0, 0);
-}
-
-// Unit u of tile row `row` sits at position u ^ f(row), f(row) = (row % 8) ^
-// ((row / 8) % 2). Any 8 consecutive rows get 8 different positions, and so
-// do the 8 even (or odd) rows of any aligned 16: 16-byte accesses of 8 or 16
-// lanes at a time that walk down the rows hit all banks once whether the LDS
-// serves 128 or 256 bytes per cycle.
-__device__ inline int swz(int row, int unit) { return row * kUnits + (unit ^ (row & 7) ^ ((row >> 3) & 1)); }
-
-// One dword of codes (k = 0..7 of a slice, even k in the low half-word) ->
-// eight bf16 values s*(q - z) in k order. The magic-number unpack gives the
-// exact fp16 values 1024 + q (low nibble of a byte) and 1024 + 16 q (high
-// nibble); one fma with an fp16 operand (v_fma_mix_f32) then forms
-// s*(1024+q) - s*(1024+z) = s*(q - z), or (s/16)*(1024+16q) - s*(64+z), where
-// every product and both constants are exact in fp32 (at most 22 significant
-// bits), so the fma returns s*(q - z) exactly (15 significant bits at most) and
-// the conversion to bf16 is its one rounding, to nearest even.
-struct DequantBf16 {
-    float s, c_lo, s16, c_hi;   // s, -s*(1024+z), s/16, -s*(64+z)
-};
-__device__ inline DequantBf16 dequant_bf16_consts(float s, uint32_t z) {
-    return DequantBf16{s, -s * (float)(1024u + z), s * 0.0625f, -s * (float)(64u + z)};
-}
-__device__ inline uint4 dequant_bf16(uint32_t d, const DequantBf16 &c, const UnpackConsts &uc) {
-    const uint32_t d8 = d >> 8;
-    const half2_t h0 = __builtin_bit_cast(half2_t, and_or(d, uc.lo_mask, uc.f16_magic));    // k0, k1
-    const half2_t h1 = __builtin_bit_cast(half2_t, and_or(d, uc.hi_mask, uc.f16_magic));    // k2, k3 (x16)
-    const half2_t h2 = __builtin_bit_cast(half2_t, and_or(d8, uc.lo_mask, uc.f16_magic));   // k4, k5
-    const half2_t h3 = __builtin_bit_cast(half2_t, and_or(d8, uc.hi_mask, uc.f16_magic));   // k6, k7 (x16)
-    auto lo = [&](_Float16 h) { return fmaf(c.s, (float)h, c.c_lo); };
-    auto hi = [&](_Float16 h) { return fmaf(c.s16, (float)h, c.c_hi); };
-    auto pk = [](float a, float b) {
-        return __builtin_bit_cast(uint32_t, __builtin_convertvector(float2_t{a, b}, bf162_t));
-    };
-    return make_uint4(pk(lo(h0.x), lo(h0.y)), pk(hi(h1.x), hi(h1.y)), pk(lo(h2.x), lo(h2.y)),
-                      pk(hi(h3.x), hi(h3.y)));
-}
-
-// Same for fp16: exact (q - z) pairs, then one fp16 multiply by s.
-__device__ inline uint4 dequant_f16(uint32_t d, uint32_t z, _Float16 sh, const UnpackConsts &uc) {
-    uint32_t t[4];
-    unpack_f16(d, z, uc, t);
-    const half2_t s2 = {sh, sh};
-    uint32_t o[4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) o[i] = __builtin_bit_cast(uint32_t, __builtin_bit_cast(half2_t, t[i]) * s2);
-    return make_uint4(o[0], o[1], o[2], o[3]);
-}
-
-template <int BM, int BN, int WM, int WN, int GROUP, bool BF>
-__global__ __launch_bounds__(64 * WM * WN) __attribute__((amdgpu_waves_per_eu(WM * WN / 4, WM * WN / 4))) void prefill_kernel(
-    const uint16_t *__restrict__ x, const uint4 *__restrict__ qw, const uint16_t *__restrict__ scales,
-    const uint32_t *__restrict__ zeros, uint16_t *__restrict__ y, int M, int N, int K, int m_tiles,
-    int n_tiles) {
-    constexpr int NT = 64 * WM * WN;                 // threads
-    constexpr int TM = BM / WM / 32, TN = BN / WN / 32;   // 32x32 blocks per wave
-    constexpr int RB = BN / kRowBlock;               // row blocks per tile
-    constexpr int WREC = RB * 64 / NT;               // packed records per thread per column
-    constexpr int XREC = BM * kUnits / NT;           // activation units per thread per step
-    constexpr int CPG = GROUP / kChunk;
-    constexpr int GPC = kColumn / GROUP;
-    static_assert(RB * 64 % NT == 0 && BM * kUnits % NT == 0, "tile / thread mismatch");
-
-    extern __shared__ __align__(16) unsigned char smem[];
-    uint4 *xs = reinterpret_cast<uint4 *>(smem);                        // [2][BM][8]
-    uint4 *ws = reinterpret_cast<uint4 *>(smem) + 2 * BM * kUnits;      // [2][BN][8]
-
-    const int tid = threadIdx.x;
-    const int lane = tid & 63;
-    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const int wm = wave / WN, wn = wave % WN;
-
-    // tile index; consecutive ids walk M first, so the M tiles that share a
-    // weight tile run side by side. Workgroups are dealt to the eight XCDs
-    // round-robin: remap so each XCD gets a contiguous range of ids (and
-    // keeps the shared weight tile in its own L2).
-    const int tiles = m_tiles * n_tiles;
-    int id = blockIdx.x;
-    if (tiles % 8 == 0) id = (id % 8) * (tiles / 8) + id / 8;
-    const int mt = id % m_tiles, nt = id / m_tiles;
-    const int m0 = mt * BM, n0 = nt * BN;
-
-    const int C = K / kChunk;
-    const int T = (C + kColChunks - 1) / kColChunks;
-    const int steps = (C + 1) / 2;                   // 64-k steps (the last may hold one chunk)
-    const int nblocks = (N + kRowBlock - 1) / kRowBlock;
-
-    // ---- weight records of this thread: row block i * waves + wave of the
-    // tile, record = lane (d = lane / 16, r = lane % 16: dword d of the
-    // column's four chunks of row r). Offsets are 32-bit element indices.
-    const int d = lane >> 4, r = lane & 15;
-    uint32_t woff[WREC], wstep[WREC], soff[WREC], zoff[WREC];
-    int zshift[WREC], wrow[WREC], wrows[WREC];
-#pragma unroll
-    for (int i = 0; i < WREC; ++i) {
-        const int rb = i * (NT / 64) + wave;
-        const int b = min(n0 / kRowBlock + rb, nblocks - 1);   // past the last block: repeat it (not stored)
-        const int rows = min(kRowBlock, N - b * kRowBlock);
-        const int rl = r < rows ? r : r - rows;                 // lanes past a short block re-read a valid row
-        const int n = b * kRowBlock + rl;
-        wrows[i] = rows;
-        woff[i] = (uint32_t)b * (uint32_t)(K / 2) + (uint32_t)(d * rows + rl);    // uint4 index, column 0 (a block is K/2 uint4)
-        wstep[i] = (uint32_t)(kColChunks * rows);                                 // uint4 per column
-        soff[i] = (uint32_t)n;                                                    // ColScales index, column 0
-        zoff[i] = (uint32_t)(n * GPC) / 8;
-        zshift[i] = 4 * ((n * GPC) % 8);
-        wrow[i] = rb * kRowBlock + r;                                             // LDS row
-    }
-    const uint32_t zstep = (uint32_t)(N * GPC / 8);
-    const ColScales<GPC> *scol = reinterpret_cast<const ColScales<GPC> *>(scales);
-    const int t_full = C / kColChunks;   // columns with all four chunks
-    struct WCol {
-        uint4 rec[WREC];
-        ColScales<GPC> sc[WREC];
-        uint32_t zw[WREC];
-    };
-    auto load_wcol = [&](int t, WCol &u) __attribute__((always_inline)) {
-#pragma unroll
-        for (int i = 0; i < WREC; ++i) {
-            if (t < t_full) {
-                u.rec[i] = qw[woff[i] + (uint32_t)t * wstep[i]];
-            } else {   // partial last column: nc dwords per (d, row), missing chunks are zero codes
-                const int nc = C - t * kColChunks;
-                const int rl = r < wrows[i] ? r : r - wrows[i];
-                const uint32_t blk = woff[i] - (uint32_t)(d * wrows[i] + rl);   // row block base, uint4
-                const uint32_t *col = reinterpret_cast<const uint32_t *>(qw + blk) + (size_t)t * wrows[i] * 16 +
-                                      (size_t)(d * wrows[i] + rl) * nc;
-                uint32_t v[4];
-#pragma unroll
-                for (int j = 0; j < kColChunks; ++j) v[j] = j < nc ? col[j] : 0u;
-                u.rec[i] = make_uint4(v[0], v[1], v[2], v[3]);
-            }
-            u.sc[i] = scol[soff[i] + (uint32_t)t * (uint32_t)N];
-            u.zw[i] = zeros[zoff[i] + (uint32_t)t * zstep];
-        }
-    };
-    // dequantise half h (chunks 2h, 2h+1) of weight record i into LDS;
-    // chunks past K (partial last column) have zero codes and zero scale
-    const UnpackConsts uc = unpack_consts();
-    auto store_w_rec = [&](const WCol &u, int i, int h, uint4 *wbuf) __attribute__((always_inline)) {
-#pragma unroll
-        for (int jj = 0; jj < 2; ++jj) {
-            const uint32_t dw = h ? (jj ? u.rec[i].w : u.rec[i].z) : (jj ? u.rec[i].y : u.rec[i].x);
-            const int e = (2 * h + jj) / CPG;
-            const uint32_t z = (u.zw[i] >> (zshift[i] + 4 * e)) & 0xFu;
-            const float s = u.sc[i].get(e);
-            uint4 v;
-            if constexpr (BF)
-                v = dequant_bf16(dw, dequant_bf16_consts(s, z), uc);
-            else
-                v = dequant_f16(dw, z, (_Float16)s, uc);
-            wbuf[swz(wrow[i], 4 * jj + d)] = v;
-        }
-    };
-
-    // ---- activation units of this thread: tile row (i * NT + tid) / 8, unit
-    // tid % 8 of the step; units past K read as zero
-    const uint4 *xg = reinterpret_cast<const uint4 *>(x);
-    const int xu = tid % kUnits;
-    uint32_t xoff[XREC];
-#pragma unroll
-    for (int i = 0; i < XREC; ++i) {
-        const int row = (i * NT + tid) / kUnits;
-        xoff[i] = (uint32_t)min(m0 + row, M - 1) * (uint32_t)(K / 8) + (uint32_t)xu;   // rows past M repeat the last
-    }
-    const int k8_total = K / 8;
-    // Steps that may reach past K (the partial last column) zero those units:
-    // the address is clamped into the row and the value masked, so the load
-    // stays unconditional (no branch splits the interleaved step).
-    auto load_x_unit = [&](int i, int step_idx, auto masked) __attribute__((always_inline)) {
-        if constexpr (!decltype(masked)::value) return xg[xoff[i] + (uint32_t)(step_idx * kUnits)];
-        const int k8 = step_idx * kUnits + xu;
-        uint4 v = xg[xoff[i] + (uint32_t)(min(k8, k8_total - 1) - xu)];
-        const uint32_t keep = 0u - (uint32_t)(k8 < k8_total);
-        v.x &= keep;
-        v.y &= keep;
-        v.z &= keep;
-        v.w &= keep;
-        return v;
-    };
-    uint4 xv[XREC];
-
-    f16_t acc[TM][TN];
-#pragma unroll
-    for (int a = 0; a < TM; ++a)
-#pragma unroll
-        for (int b = 0; b < TN; ++b)
-#pragma unroll
-            for (int v = 0; v < 16; ++v) acc[a][b][v] = 0.0f;
-
-    // One 64-k step out of LDS (4 sub-steps of 16 k), with the operands of
-    // the next step written into the other buffer in between: sub-step kk
-    // also dequantises weight record kk (both of its chunks of half h) and
-    // moves every fourth activation unit from registers to LDS, reloading the
-    // register with the unit of the step after (x_next). Fragment reads run
-    // one sub-step ahead of the MFMAs that use them.
-    auto step = [&](const uint4 *xb, const uint4 *wb, const WCol &u, int h, uint4 *wdst, uint4 *xdst,
-                    int x_next, auto masked) __attribute__((always_inline)) {
-        const int rsel = lane & 31, khalf = lane >> 5;
-        uint4 af[2][TM], bfr[2][TN];
-        auto read = [&](int kk, uint4 (&a_)[TM], uint4 (&b_)[TN]) __attribute__((always_inline)) {
-#pragma unroll
-            for (int a = 0; a < TM; ++a) a_[a] = xb[swz(wm * (BM / WM) + 32 * a + rsel, 2 * kk + khalf)];
-#pragma unroll
-            for (int b = 0; b < TN; ++b) b_[b] = wb[swz(wn * (BN / WN) + 32 * b + rsel, 2 * kk + khalf)];
-        };
-        // one wave per SIMD: fragment reads run one sub-step ahead; two waves
-        // per SIMD: read just before use (the other wave covers the latency,
-        // and the registers are needed for its accumulators)
-        constexpr bool kAhead = WM * WN == 4;
-        read(0, af[0], bfr[0]);
-#pragma unroll
-        for (int kk = 0; kk < kStepK / 16; ++kk) {
-            if constexpr (kAhead) {
-                if (kk + 1 < kStepK / 16) read(kk + 1, af[(kk + 1) & 1], bfr[(kk + 1) & 1]);
-            } else if (kk > 0) {
-                read(kk, af[kk & 1], bfr[kk & 1]);
-            }
-            if (kk < WREC) store_w_rec(u, kk, h, wdst);
-#pragma unroll
-            for (int i = kk; i < XREC; i += kStepK / 16) {
-                xdst[swz((i * NT + tid) / kUnits, xu)] = xv[i];
-                xv[i] = load_x_unit(i, x_next, masked);
-            }
-#pragma unroll
-            for (int a = 0; a < TM; ++a)
-#pragma unroll
-                for (int b = 0; b < TN; ++b)
-                    acc[a][b] = mfma32x32x16<BF>(af[kk & 1][a], bfr[kk & 1][b], acc[a][b]);
-        }
-    };
-
-    // ---- main loop over the full columns: iteration t multiplies steps 2t
-    // (buffer 0) and 2t+1 (buffer 1) and writes steps 2t+1 and 2t+2. Loads
-    // past the end of K are clamped to valid addresses; what they bring is
-    // written into a buffer that is never multiplied.
-    uint4 *xs0 = xs, *xs1 = xs + BM * kUnits, *ws0 = ws, *ws1 = ws + BN * kUnits;
-    WCol wcur, wnext;
-    load_wcol(0, wcur);
-#pragma unroll
-    for (int i = 0; i < XREC; ++i) xv[i] = load_x_unit(i, 0, kMasked);
-    load_wcol(min(1, T - 1), wnext);
-#pragma unroll
-    for (int i = 0; i < WREC; ++i) store_w_rec(wcur, i, 0, ws0);
-#pragma unroll
-    for (int i = 0; i < XREC; ++i) {
-        xs0[swz((i * NT + tid) / kUnits, xu)] = xv[i];
-        xv[i] = load_x_unit(i, min(1, steps - 1), kMasked);
-    }
-    __syncthreads();
-    // (the activation loads of the last full column reach the steps after it:
-    // those are the masked ones)
-    auto column = [&](int t, auto masked) __attribute__((always_inline)) {
-        step(xs0, ws0, wcur, 1, ws1, xs1, min(2 * t + 2, steps - 1), masked);
-        __syncthreads();
-        wcur = wnext;
-        load_wcol(min(t + 2, T - 1), wnext);
-        step(xs1, ws1, wcur, 0, ws0, xs0, min(2 * t + 3, steps - 1), masked);
-        __syncthreads();
-    };
-    for (int t = 0; t + 1 < t_full; ++t) column(t, kPlain);
-    if (t_full > 0) column(t_full - 1, kMasked);
-    // the partial last column (K % 128 != 0): one or two more steps; its
-    // missing chunks have zero codes and zero activations
-    if (t_full < T) {
-        const int s0 = 2 * t_full;
-        const bool two = s0 + 1 < steps;
-        step(xs0, ws0, wcur, 1, ws1, xs1, min(s0 + 2, steps - 1), kMasked);
-        __syncthreads();
-        if (two) step(xs1, ws1, wcur, 0, ws0, xs0, min(s0 + 2, steps - 1), kMasked);
-    }
-
-    // ---- epilogue: lane holds rows (v/4)*8 + (lane/32)*4 + v%4 of column lane%32
-#pragma unroll
-    for (int a = 0; a < TM; ++a)
-#pragma unroll
-        for (int b = 0; b < TN; ++b) {
-            const int n = n0 + wn * (BN / WN) + 32 * b + (lane & 31);
-            if (n >= N) continue;
-#pragma unroll
-            for (int v = 0; v < 16; ++v) {
-                const int m = m0 + wm * (BM / WM) + 32 * a + (v / 4) * 8 + (lane >> 5) * 4 + (v % 4);
-                if (m < M)
-                    y[(int64_t)m * N + n] = BF ? f32_to_bf16_bits(acc[a][b][v]) : f32_to_f16_bits(acc[a][b][v]);
-            }
-        }
-}
-
-template <int BM, int BN, int WM, int WN, int GROUP, bool BF>
-hipError_t launch_tile(const void *x, const void *qw, const void *sc, const void *zp, void *y, int M, int N,
-                       int K, hipStream_t stream) {
-    auto kern = prefill_kernel<BM, BN, WM, WN, GROUP, BF>;
-    const size_t lds = (size_t)2 * (BM + BN) * kUnits * 16;
-    static bool attr_set = false;   // per instantiation; the attribute is per function
-    if (!attr_set) {
-        hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(kern),
-                                           hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
-        if (e != hipSuccess) return e;
-        attr_set = true;
-    }
-    const int m_tiles = (int)ceil_div(M, BM), n_tiles = (int)ceil_div(N, BN);
-    hipLaunchKernelGGL(kern, dim3((unsigned)(m_tiles * n_tiles)), dim3(64 * WM * WN), lds, stream,
-                       reinterpret_cast<const uint16_t *>(x), reinterpret_cast<const uint4 *>(qw),
-                       reinterpret_cast<const uint16_t *>(sc), reinterpret_cast<const uint32_t *>(zp),
-                       reinterpret_cast<uint16_t *>(y), M, N, K, m_tiles, n_tiles);
-    return hipGetLastError();
-}
-
-template <int GROUP, bool BF>
-hipError_t launch_group(int tile, const void *x, const void *qw, const void *sc, const void *zp, void *y, int M,
-                        int N, int K, hipStream_t stream) {
-    switch (tile) {
-        case kTile64x256: return launch_tile<64, 256, 1, 4, GROUP, BF>(x, qw, sc, zp, y, M, N, K, stream);
-        case kTile128x256: return launch_tile<128, 256, 2, 2, GROUP, BF>(x, qw, sc, zp, y, M, N, K, stream);
-        case kTile256x256w8: return launch_tile<256, 256, 2, 4, GROUP, BF>(x, qw, sc, zp, y, M, N, K, stream);
-        default: return launch_tile<256, 256, 2, 2, GROUP, BF>(x, qw, sc, zp, y, M, N, K, stream);
-    }
-}
-
-}  // namespace
 
 int prefill_tile(int64_t M, int64_t N) {
     static const int forced = [] {
@@ -399,19 +35,15 @@ int prefill_tile(int64_t M, int64_t N) {
 }
 
 hipError_t launch_prefill(const void *x, bool bf16, const void *qweight, const void *scales, const void *zeros,
-                          void *y, int M, int N, int K, int group, const GemmPlan &plan, hipStream_t stream) {
-    if (bf16) {
-        switch (group) {
-            case 32: return launch_group<32, true>(plan.tile, x, qweight, scales, zeros, y, M, N, K, stream);
-            case 64: return launch_group<64, true>(plan.tile, x, qweight, scales, zeros, y, M, N, K, stream);
-            default: return launch_group<128, true>(plan.tile, x, qweight, scales, zeros, y, M, N, K, stream);
-        }
-    }
-    switch (group) {
-        case 32: return launch_group<32, false>(plan.tile, x, qweight, scales, zeros, y, M, N, K, stream);
-        case 64: return launch_group<64, false>(plan.tile, x, qweight, scales, zeros, y, M, N, K, stream);
-        default: return launch_group<128, false>(plan.tile, x, qweight, scales, zeros, y, M, N, K, stream);
+                          void *y, int M, int N, int K, int group, int fmt, const GemmPlan &plan, hipStream_t stream) {
+    switch (fmt) {
+        case kSym4: return launch_prefill_fmt<kSym4>(x, bf16, qweight, scales, zeros, y, M, N, K, group, plan, stream);
+        case kSym8: return launch_prefill_fmt<kSym8>(x, bf16, qweight, scales, zeros, y, M, N, K, group, plan, stream);
+        default: return launch_prefill_fmt<kAsym4>(x, bf16, qweight, scales, zeros, y, M, N, K, group, plan, stream);
     }
 }
+
+template hipError_t launch_prefill_fmt<kAsym4>(const void *, bool, const void *, const void *, const void *, void *,
+                                               int, int, int, int, const GemmPlan &, hipStream_t);
 
 }  // namespace w4a16

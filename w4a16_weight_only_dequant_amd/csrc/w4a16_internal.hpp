@@ -33,6 +33,9 @@ __host__ __device__ inline int64_t dword_offset(int n, int c, int d, int N, int 
            (int64_t)r * nc + j;
 }
 
+// Weight formats (the values of w4a16_format in the public header).
+enum { kAsym4 = 0, kSym4 = 1, kSym8 = 2 };
+
 typedef _Float16 half2_t __attribute__((ext_vector_type(2)));
 typedef __bf16 bf162_t __attribute__((ext_vector_type(2)));
 
@@ -79,24 +82,46 @@ struct GroupTable {
     int first[kMaxGroup + 1];   // first workgroup of each problem (set by the launcher)
     int count;
 };
-hipError_t launch_gemm_group(const GroupTable &tab, bool bf16, int M, int K, int group, const GemmPlan &plan,
-                             hipStream_t stream);
+// Launchers. `group` is 32, 64, 128 or 256; `fmt` one of kAsym4, kSym4,
+// kSym8 (zeros is not read by the symmetric formats).
+hipError_t launch_gemm_group(const GroupTable &tab, bool bf16, int M, int K, int group, int fmt,
+                             const GemmPlan &plan, hipStream_t stream);
 
-hipError_t launch_pack(const float *w, int N, int K, int group, void *qweight,
+hipError_t launch_pack(const float *w, int N, int K, int group, int fmt, void *qweight,
                        void *scales, void *zeros, hipStream_t stream);
 hipError_t launch_unpack(const void *qweight, const void *scales, const void *zeros,
-                         int N, int K, int group, uint8_t *codes, uint16_t *scales_out,
+                         int N, int K, int group, int fmt, uint8_t *codes, uint16_t *scales_out,
                          uint8_t *zeros_out, hipStream_t stream);
 hipError_t launch_gemv(const void *x, bool bf16, const void *qweight, const void *scales,
-                       const void *zeros, void *y, int M, int N, int K, int group,
+                       const void *zeros, void *y, int M, int N, int K, int group, int fmt,
                        const GemvPlan &plan, hipStream_t stream);
 hipError_t launch_gemm(const void *x, bool bf16, const void *qweight, const void *scales,
-                       const void *zeros, void *y, int M, int N, int K, int group,
+                       const void *zeros, void *y, int M, int N, int K, int group, int fmt,
                        const GemmPlan &plan, hipStream_t stream);
 hipError_t launch_prefill(const void *x, bool bf16, const void *qweight, const void *scales,
-                          const void *zeros, void *y, int M, int N, int K, int group,
+                          const void *zeros, void *y, int M, int N, int K, int group, int fmt,
                           const GemmPlan &plan, hipStream_t stream);
 int prefill_tile(int64_t M, int64_t N);
+
+// The kernels of one format, each compiled in a translation unit of its own.
+#define W4A16_LINEAR_PARAMS const void *x, bool bf16, const void *qweight, const void *scales, const void *zeros, \
+                            void *y, int M, int N, int K, int group
+template <int FMT> hipError_t launch_gemv_fmt(W4A16_LINEAR_PARAMS, const GemvPlan &plan, hipStream_t stream);
+template <int FMT> hipError_t launch_skinny_fmt(W4A16_LINEAR_PARAMS, const GemmPlan &plan, hipStream_t stream);
+template <int FMT> hipError_t launch_prefill_fmt(W4A16_LINEAR_PARAMS, const GemmPlan &plan, hipStream_t stream);
+template <int FMT>
+hipError_t launch_skinny_group_fmt(const GroupTable &tab, bool bf16, int M, int K, int group, const GemmPlan &plan,
+                                   hipStream_t stream);
+#define W4A16_EXTERN_FMT(F)                                                                              \
+    extern template hipError_t launch_gemv_fmt<F>(W4A16_LINEAR_PARAMS, const GemvPlan &, hipStream_t);   \
+    extern template hipError_t launch_skinny_fmt<F>(W4A16_LINEAR_PARAMS, const GemmPlan &, hipStream_t); \
+    extern template hipError_t launch_prefill_fmt<F>(W4A16_LINEAR_PARAMS, const GemmPlan &, hipStream_t); \
+    extern template hipError_t launch_skinny_group_fmt<F>(const GroupTable &, bool, int, int, int,        \
+                                                          const GemmPlan &, hipStream_t);
+W4A16_EXTERN_FMT(kAsym4)
+W4A16_EXTERN_FMT(kSym4)
+W4A16_EXTERN_FMT(kSym8)
+#undef W4A16_EXTERN_FMT
 
 __device__ inline uint16_t f32_to_f16_bits(float v) {
     _Float16 h = (_Float16)v;
