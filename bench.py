@@ -19,7 +19,10 @@ kernel's own rate: algorithmic bytes of its launches over their average
 duration from HIP events on the launch stream. `prefill` carries the M = 2048
 GEMM's TFLOP/s against the dense bf16 MFMA peak. `grouped_step` times the same
 seven layers with q/k/v and gate/up each in one launch (w4a16_linear_group);
-`value` stays the seven-launch step. `cpu_baseline` times the CPU
+`value` stays the seven-launch step. `formats` repeats the decode step and
+the prefill GEMM with the weights in the other formats (symmetric 4-bit,
+symmetric 8-bit = W8A16, group 256), each against its own bytes and flops.
+`cpu_baseline` times the CPU
 oracle (dequantise + fp64 product) on a bounded sample of the headline workload.
 """
 from __future__ import annotations
@@ -41,10 +44,12 @@ WORKLOAD_IDS = {"gemv_4096": 1, "decode_13b_layer": 2, "fused_qkv": 3, "prefill"
 
 # sources each kernel is built from (for matching stored counter results)
 KERNEL_SOURCES = {
-    "gemv": ["gemv.hip", "decode_common.hpp", "w4a16_internal.hpp"],
-    "skinny": ["gemm.hip", "decode_common.hpp", "w4a16_internal.hpp"],
-    "prefill": ["prefill.hip", "decode_common.hpp", "w4a16_internal.hpp"],
+    "gemv": ["gemv.hip", "gemv_kernel.hpp", "decode_common.hpp", "w4a16_internal.hpp"],
+    "skinny": ["gemm.hip", "gemm_kernel.hpp", "decode_common.hpp", "w4a16_internal.hpp"],
+    "prefill": ["prefill.hip", "prefill_kernel.hpp", "decode_common.hpp", "w4a16_internal.hpp"],
 }
+# weight-format variants measured beside the headline (format, group)
+FORMAT_LEGS = [("sym4", 128), ("sym8", 128), ("asym4", 256)]
 
 
 def parse():
@@ -57,6 +62,7 @@ def parse():
     p.add_argument("--no-prefill", action="store_true", help="skip the M=2048 prefill leg")
     p.add_argument("--prefill-reps", type=int, default=60)
     p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--no-formats", action="store_true", help="skip the weight-format legs")
     p.add_argument("--cpu-seconds", type=float, default=15.0)
     p.add_argument("--copy-calibration", action="store_true",
                    help="also run an elementwise kernel that reads and writes 256 MiB (counter scaling)")
@@ -71,9 +77,13 @@ def kernel_source_hash(kind):
     return h.hexdigest()[:16]
 
 
-def algorithmic_bytes(M, N, K, group):
+def algorithmic_bytes(M, N, K, group, fmt="asym4"):
+    """Codes (4 or 8 bits per weight), fp16 scales, 4-bit zero-points (asym4
+    only), activations read and outputs written."""
     G = K // group
-    return N * K // 2 + 2 * G * N + G * N // 2 + 2 * M * K + 2 * M * N
+    codes = N * K if fmt == "sym8" else N * K // 2
+    zeros = G * N // 2 if fmt == "asym4" else 0
+    return codes + 2 * G * N + zeros + 2 * M * K + 2 * M * N
 
 
 def kernel_kind(w4, M, N, K, group, dtype):
@@ -98,7 +108,7 @@ class Workload:
     """Packed weights, activations and outputs of one configuration, with
     enough rotated copies of the weights to defeat the 256 MB MALL."""
 
-    def __init__(self, cfg_id, M, dev):
+    def __init__(self, cfg_id, M, dev, fmt="asym4", group=None):
         import numpy as np
         import torch
 
@@ -106,13 +116,14 @@ class Workload:
         import workloads as wl
         self.w4, self.torch = w4, torch
         self.cfg = wl.WORKLOADS[cfg_id]
-        self.M, self.group, self.dtype = M, self.cfg.group, self.cfg.dtype
+        self.M, self.group, self.dtype = M, group or self.cfg.group, self.cfg.dtype
+        self.fmt = fmt
         tdt = torch.float16 if self.dtype == "f16" else torch.bfloat16
         self.mats = list(self.cfg.matrices)
         packed, self.xs, self.ys = [], [], []
         for mi, mat in enumerate(self.mats):
             w = torch.from_numpy(wl.weights(cfg_id, mi)).to(dev)
-            packed.append(w4.pack(w, self.group))
+            packed.append(w4.pack(w, self.group, fmt))
             del w
             xb = wl.activations(cfg_id, mi, M)
             self.xs.append(torch.from_numpy(xb.view(np.int16)).to(dev).view(tdt))
@@ -122,10 +133,11 @@ class Workload:
         self.copies = max(1, -(-3 * MALL_BYTES // set_bytes))
         self.sets = [packed]
         for _ in range(self.copies - 1):
-            self.sets.append([w4.PackedWeight(p.qweight.clone(), p.scales.clone(), p.zeros.clone(), p.N, p.K,
-                                              p.group) for p in packed])
+            self.sets.append([w4.PackedWeight(p.qweight.clone(), p.scales.clone(),
+                                              p.zeros.clone() if p.zeros is not None else None, p.N, p.K,
+                                              p.group, p.fmt) for p in packed])
         self.ws = w4.Workspace(dev)
-        self.bytes = [algorithmic_bytes(M, m.N, m.K, self.group) for m in self.mats]
+        self.bytes = [algorithmic_bytes(M, m.N, m.K, self.group, fmt) for m in self.mats]
         self.flops = [2 * M * m.N * m.K for m in self.mats]
 
     def launch(self, c, j):
@@ -243,6 +255,53 @@ def cpu_oracle_baseline(cfg_id, M, seconds):
                       f"{done_bytes / 1e6:.0f} MB of the workload's algorithmic bytes in {t_cpu:.1f} s"}
 
 
+def time_steps(wk, steps, warmup):
+    """Wall time per step of replaying the step graphs (weights rotated over copies)."""
+    torch = wk.torch
+    for i in range(warmup):
+        wk.step_graphs[i % wk.copies].replay()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(steps):
+        wk.step_graphs[i % wk.copies].replay()
+    torch.cuda.synchronize()
+    return (time.perf_counter() - t0) * 1e3 / steps
+
+
+def format_legs(dev, cfg_id, M, steps, warmup, prefill_reps):
+    """The decode step and the prefill GEMM in each weight-format variant: step
+    GB/s over its own algorithmic bytes, per-kernel rates against the peaks."""
+    import workloads as wl
+    torch = __import__("torch")
+    legs = []
+    for fmt, group in FORMAT_LEGS:
+        wk = Workload(cfg_id, M, dev, fmt, group)
+        wk.graphs(dev)
+        ms = time_steps(wk, steps, warmup)
+        per = wk.per_kernel_ms(max(1, steps // (wk.copies * 4)))
+        kernel_gbs = sum(wk.bytes) / (sum(per) * 1e-3) / 1e9
+        leg = {"format": fmt, "group": group, "bits_per_weight": round(8 * (sum(wk.bytes) - sum(
+                   2 * M * (m.N + m.K) for m in wk.mats)) / sum(m.N * m.K for m in wk.mats), 4),
+               "ms_per_step": round(ms, 5), "value": round(sum(wk.bytes) / (ms * 1e-3) / 1e9, 1), "unit": "GB/s",
+               "decode_kernels": {"achieved": round(kernel_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                                  "frac": round(kernel_gbs / HBM_PEAK_GBS, 4),
+                                  "us": {m.name: round(per[j] * 1e3, 2) for j, m in enumerate(wk.mats)}}}
+        del wk
+        torch.cuda.empty_cache()
+        pcfg = WORKLOAD_IDS["prefill"]
+        pk = Workload(pcfg, wl.WORKLOADS[pcfg].ms[0], dev, fmt, group)
+        pk.graphs(dev)
+        pms = pk.per_kernel_ms(max(1, prefill_reps // pk.copies))
+        tf = pk.flops[0] / (pms[0] * 1e-3) / 1e12
+        leg["prefill"] = {"M": pk.M, "kernel_us": round(pms[0] * 1e3, 2), "achieved": round(tf, 1),
+                          "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                          "frac": round(tf / MFMA_BF16_PEAK_TFLOPS, 4)}
+        del pk
+        torch.cuda.empty_cache()
+        legs.append(leg)
+    return legs
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -352,6 +411,10 @@ def main():
         del pk
         torch.cuda.empty_cache()
 
+    formats = None
+    if not args.no_formats:
+        formats = format_legs(dev, cfg_id, M, max(20, args.steps // 2), args.warmup, args.prefill_reps // 2)
+
     if args.copy_calibration:
         # an elementwise kernel of known traffic (reads 256 MiB, writes 256 MiB):
         # counter bytes of this launch give the scale factor for the others
@@ -389,6 +452,7 @@ def main():
         "roofline": roof,
         "grouped_step": grouped,
         "prefill": prefill,
+        "formats": formats,
         "cpu_baseline": cpu,
     }
     print(json.dumps(out))

@@ -34,7 +34,7 @@
 namespace w4a16 {
 namespace {
 
-constexpr int kMaxWaves = 16;
+constexpr int kMaxWaves = kGemvMaxWaves;
 #ifndef W4A16_GEMV_PREFETCH
 #define W4A16_GEMV_PREFETCH 6
 #endif
@@ -58,7 +58,7 @@ __host__ __device__ inline size_t wave_lds_bytes(int MT, int xcols, bool bf16, i
 }
 
 template <int GROUP, int MT, bool BF, int FMT>
-__global__ __launch_bounds__(1024) __attribute__((amdgpu_waves_per_eu(1, 4))) void gemv_kernel(
+__global__ __launch_bounds__(64 * kMaxWaves) __attribute__((amdgpu_waves_per_eu(1, 4))) void gemv_kernel(
     const uint16_t *__restrict__ x, const uint4 *__restrict__ qw, const uint4 *__restrict__ qw_hi,
     const uint16_t *__restrict__ scales, const uint32_t *__restrict__ zeros, uint16_t *__restrict__ y, int N,
     int K, int xcols, int mshift) {

@@ -53,8 +53,14 @@ GemvPlan gemv_plan(int64_t M, int64_t N, int64_t K, int32_t group);
 // Dynamic LDS of one GEMV workgroup (per-wave activations, bf16 sums, metadata).
 size_t gemv_lds_bytes(int64_t M, int64_t K, bool bf16, int waves, int group);
 int gemv_xcols(int64_t K, int waves);
+// Most waves of one GEMV workgroup (they split K); the launch bound, and so
+// the register budget of a wave, follows from it.
+#ifndef W4A16_GEMV_MAX_WAVES
+#define W4A16_GEMV_MAX_WAVES 16
+#endif
+constexpr int kGemvMaxWaves = W4A16_GEMV_MAX_WAVES;
 // Static LDS of one GEMV workgroup (cross-wave reduction buffer).
-constexpr size_t kGemvStaticLds = 16 * 8 * 16 * sizeof(float);
+constexpr size_t kGemvStaticLds = kGemvMaxWaves * 8 * 16 * sizeof(float);
 
 // Plan for the matrix-core kernels: kind 0 streams the weights through
 // registers for M <= kSkinnyMaxM (16-row MFMA tiles of activations, one per
