@@ -36,6 +36,11 @@ What it computes, and where the method is stated:
   codes are stored offset by 2**(b-1), so the shared reconstruction
   s * (code - zero) holds with a fixed zero of 8 or 128 that is never stored.
 
+* The quality report (MSE, SNR, cosine, max error) of the error-analysis
+  routine the instagit page lists, and AWQ's run-time half (activations
+  multiplied by the reciprocal of the factors the weights were scaled up by),
+  both at the end of this module.
+
 Readings where the pages are silent (each also listed in the design notes):
   * range includes zero: lo = min(0, min w), hi = max(0, max w);
   * scale s = fp16_rne((hi - lo) / 15) computed in fp32; a zero scale becomes
@@ -498,3 +503,70 @@ def error_ratio(y_gpu, y_ref, a, out_dtype: str | None = None) -> np.ndarray:
     if out_dtype is not None:
         budget = budget + out_half_ulp(np.maximum(np.abs(y_gpu), np.abs(y_ref)), out_dtype)
     return np.abs(y_gpu - y_ref) / budget
+
+
+# ---------------------------------------------------------------------------
+# Quantisation quality. The instagit comparison page ("Implementation
+# Architecture": the error-analysis routine) reports four figures for a
+# quantised tensor: mean squared error, signal-to-noise ratio in dB, cosine
+# similarity and the largest error. Its formulas are not printed; these are the
+# standard definitions, over the flattened matrix, in fp64:
+#   MSE  = sum (w - w_hat)^2 / (N K)
+#   SNR  = 10 log10( sum w^2 / sum (w - w_hat)^2 )      (+inf when exact)
+#   cos  = sum w w_hat / sqrt(sum w^2 * sum w_hat^2)   (1 when both are zero)
+#   max  = max |w - w_hat|
+# ---------------------------------------------------------------------------
+
+
+def quant_error_sums(w, w_hat):
+    """(sum d^2, sum w^2, sum w_hat^2, sum w w_hat, max |d|) with d = w - w_hat, fp64."""
+    w = np.asarray(w, dtype=np.float32).astype(np.float64)
+    h = np.asarray(w_hat, dtype=np.float64)
+    d = w - h
+    return (float(np.sum(d * d)), float(np.sum(w * w)), float(np.sum(h * h)), float(np.sum(w * h)),
+            float(np.max(np.abs(d), initial=0.0)))
+
+
+def quant_error_stats(sums, count: int):
+    """(MSE, SNR dB, cosine, max error) from the five sums over `count` weights."""
+    d2, w2, h2, wh, mx = sums
+    mse = d2 / count
+    snr = np.inf if d2 == 0.0 else (10.0 * np.log10(w2 / d2) if w2 > 0.0 else -np.inf)
+    if w2 == 0.0 and h2 == 0.0:
+        cos = 1.0
+    elif w2 == 0.0 or h2 == 0.0:
+        cos = 0.0
+    else:
+        cos = wh / np.sqrt(w2 * h2)
+    return mse, float(snr), float(cos), mx
+
+
+def quant_error(w, codes, scale_bits, zeros, group: int):
+    """Quality report of one quantised matrix: (MSE, SNR dB, cosine, max error)."""
+    w_hat = dequantize(codes, scale_bits, zeros, group)
+    return quant_error_stats(quant_error_sums(w, w_hat), w_hat.size)
+
+
+# ---------------------------------------------------------------------------
+# AWQ, the deployable half. Salient input channels are scaled up before
+# quantisation and the activations are scaled down to compensate (instagit
+# comparison page, "AWQ: Activation-Aware Weight Quantization"; "Weight-Only
+# Quantisation": deployment stays ordinary groupwise INT4). The choice of the
+# factors needs calibration activations and is not part of this library; the
+# factors a_k > 0 are an input. Offline: w'[n][k] = w[n][k] * a_k (fp32), then
+# the usual quantiser. At run time the activations are multiplied by
+# m_k = 1 / a_k, given as fp32: x'[m][k] = rne16(fp32(x[m][k] * m_k)), one
+# fp32 product rounded once to the activation type, and y = x' w_hat'^T.
+# ---------------------------------------------------------------------------
+
+
+def awq_fold_weights(w, a):
+    """w' = w * a along K (fp32 product): the weights AWQ quantises."""
+    return (np.asarray(w, dtype=np.float32) * np.asarray(a, dtype=np.float32)[None, :]).astype(np.float32)
+
+
+def awq_scale_activations(x_bits, dtype: str, act_mul):
+    """x' bits = rne16(fp32(x * m)) for 16-bit activation bits x [M][K] and fp32 m [K]."""
+    x = act_bits_to_f64(x_bits, dtype).astype(np.float32)       # exact widening
+    prod = x * np.asarray(act_mul, dtype=np.float32)[None, :]     # IEEE fp32 product
+    return f32_to_f16_bits(prod) if dtype == "f16" else f32_to_bf16_bits(prod)

@@ -560,3 +560,95 @@ def test_sym8_planes_round_trip_and_order(N, K):
     # the same nibble position in both planes: 0x5 (low nibble) in plane 0, 0xA in plane 1
     lo, hi = int(p1[nz[0]]), int(p1[nz[1]])
     assert (lo, hi) in ((0x05, 0x0A), (0x50, 0xA0))
+
+
+# ---------------------------------------------------------------------------
+# Quality report and AWQ run-time scaling
+# ---------------------------------------------------------------------------
+
+
+def test_quant_error_matches_hand_computed_perturbation():
+    """Symmetric 4-bit, s = 2^-6: every weight is a grid point k*s plus a known
+    offset e (|e| < s/2, exact binary fraction), one weight per group is 7s so
+    the scale is exactly s; the codes are k and the errors exactly e."""
+    s = Fraction(1, 64)
+    rng = np.random.default_rng(21)
+    N, K, group = 8, 128, 32
+    k = rng.integers(-6, 7, size=(N, K))
+    e_num = rng.integers(-7, 8, size=(N, K))          # e = e_num * s / 16, |e| <= 7s/16 < s/2
+    k[:, ::group] = 7
+    e_num[:, ::group] = 0
+    w_frac = [[k[n, j] * s + e_num[n, j] * s / 16 for j in range(K)] for n in range(N)]
+    w = np.array([[float(v) for v in row] for row in w_frac], dtype=np.float32)
+    codes, s_bits, zeros = ref.quantize_groupwise(w, group, "sym4")
+    assert np.all(ref.f16_bits_to_f64(s_bits) == float(s))
+    assert np.array_equal(codes.astype(np.int64) - 8, k)
+    mse, snr, cos, mx = ref.quant_error(w, codes, s_bits, zeros, group)
+    d2 = sum((e_num[n, j] * s / 16) ** 2 for n in range(N) for j in range(K))
+    w2 = sum(v * v for row in w_frac for v in row)
+    h2 = sum((k[n, j] * s) ** 2 for n in range(N) for j in range(K))
+    wh = sum(w_frac[n][j] * k[n, j] * s for n in range(N) for j in range(K))
+    assert mse == float(d2 / (N * K))
+    assert mx == float(np.abs(e_num).max() * s / 16)
+    assert abs(snr - 10 * np.log10(float(w2 / d2))) < 1e-12
+    assert abs(cos - float(wh) / np.sqrt(float(w2 * h2))) < 1e-15
+
+
+def test_quant_error_special_cases():
+    rng = np.random.default_rng(22)
+    q = rng.integers(0, 16, size=(16, 64))
+    q[:, 0], q[:, 1] = 0, 15
+    W = ((q - 5) * 2.0 ** -8).astype(np.float32)
+    codes, s_bits, zeros = ref.quantize_groupwise(W, 64)
+    mse, snr, cos, mx = ref.quant_error(W, codes, s_bits, zeros, 64)     # lattice weights: exact
+    assert (mse, snr, mx) == (0.0, np.inf, 0.0) and abs(cos - 1.0) < 1e-15
+    z = np.zeros((8, 32), dtype=np.float32)
+    assert ref.quant_error(z, *ref.quantize_groupwise(z, 32), 32) == (0.0, np.inf, 1.0, 0.0)
+    # scaling the weights by 2^e scales the error by 2^e exactly (MSE by 4^e); SNR, cosine unchanged
+    w = (rng.standard_normal((16, 256)) * 0.05).astype(np.float32)
+    a = ref.quant_error(w, *ref.quantize_groupwise(w, 128), 128)
+    b = ref.quant_error(w * np.float32(8), *ref.quantize_groupwise(w * np.float32(8), 128), 128)
+    assert b[0] == a[0] * 64 and b[3] == a[3] * 8
+    assert abs(b[1] - a[1]) < 1e-9 and abs(b[2] - a[2]) < 1e-15
+
+
+def test_awq_activation_rounding_matches_library_conversions():
+    rng = np.random.default_rng(23)
+    M, K = 4, 256
+    m = (rng.uniform(0.05, 4.0, size=K)).astype(np.float32)
+    for dtype in ("f16", "bf16"):
+        x32 = rng.standard_normal((M, K)).astype(np.float32) * 3
+        xb = ref.f32_to_f16_bits(x32) if dtype == "f16" else ref.f32_to_bf16_bits(x32)
+        got = ref.awq_scale_activations(xb, dtype, m)
+        x = ref.act_bits_to_f64(xb, dtype).astype(np.float32)
+        prod = x * m[None, :]
+        if dtype == "f16":
+            want = prod.astype(np.float16).view(np.uint16)
+        else:
+            want = torch.from_numpy(prod).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+        assert np.array_equal(got, want), dtype
+        assert np.array_equal(ref.awq_scale_activations(xb, dtype, np.ones(K, np.float32)), xb)
+
+
+def test_awq_fold_is_exact_for_power_of_two_factors():
+    """Weights scaled up by a_k = 2^e_k and activations by 1/a_k: the product of
+    the quantised folded weights with the scaled activations equals x W^T of the
+    unfolded lattice weights exactly."""
+    rng = np.random.default_rng(24)
+    N, K, group = 16, 128, 32
+    q = rng.integers(0, 16, size=(N, K))
+    q[:, ::group] = 0
+    q[:, 1::group] = 15
+    z = rng.integers(0, 16, size=(N, K // group))
+    s = 2.0 ** rng.integers(-12, -6, size=(N, K // group))
+    Wf = ((q - np.repeat(z, group, 1)) * np.repeat(s, group, 1)).astype(np.float32)   # folded, on the lattice
+    e = rng.integers(-3, 4, size=K)
+    a = np.ldexp(1.0, e).astype(np.float32)
+    W = (Wf / a[None, :]).astype(np.float32)                     # the model's weights
+    assert np.array_equal(ref.awq_fold_weights(W, a), Wf)
+    codes, s_bits, zeros = ref.quantize_groupwise(Wf, group)
+    xb = ref.f32_to_f16_bits((rng.standard_normal((3, K)) * 2).astype(np.float32))
+    xs = ref.awq_scale_activations(xb, "f16", (1.0 / a).astype(np.float32))
+    y, _ = ref.linear_ref_rows(xs, "f16", codes, s_bits, zeros, group)
+    y_direct = ref.f16_bits_to_f64(xb) @ W.astype(np.float64).T
+    assert np.allclose(y, y_direct, rtol=1e-13, atol=1e-300)
