@@ -257,6 +257,49 @@ int32_t w4a16_gemv_max_m(void);
  * Host-only (queries the device's LDS size once). */
 int32_t w4a16_linear_kernel(int64_t M, int64_t N, int64_t K, int32_t group, int32_t dtype);
 
+/* ---- Quality report ----------------------------------------------------
+ * How far the packed weights are from the fp32 weights they were made from:
+ * out[8] (device, fp64) = {MSE, SNR in dB, cosine similarity, max |w - w_hat|,
+ * sum (w - w_hat)^2, sum w^2, sum w_hat^2, sum w*w_hat} over all N*K weights,
+ * w_hat rebuilt from the packed data as the kernels rebuild it. The four
+ * figures are those of the error-analysis routine of the instagit comparison
+ * page ("Implementation Architecture"): MSE = sum d^2 / (N K), SNR =
+ * 10 log10(sum w^2 / sum d^2) (+inf when d = 0), cosine = sum w w_hat /
+ * sqrt(sum w^2 sum w_hat^2) (1 when both are zero). w is the fp32 [N][K]
+ * matrix given to the pack call; workspace (device, caller-owned) holds
+ * per-block partial sums, w4a16_quant_error_workspace_bytes of them; the
+ * partials are folded in a fixed order, so the result is deterministic. */
+w4a16_status w4a16_quant_error_workspace_bytes(int64_t N, int64_t K, int32_t group, size_t *bytes);
+w4a16_status w4a16_quant_error(const float *w, const void *qweight, const void *scales,
+                               const void *zeros, int64_t N, int64_t K, int32_t group, int32_t fmt,
+                               double *out, void *workspace, size_t workspace_bytes, void *stream);
+
+/* ---- AWQ run-time scaling ---------------------------------------------
+ * AWQ scales salient input channels of the weights up before quantisation and
+ * the activations down to compensate (instagit comparison page, "AWQ:
+ * Activation-Aware Weight Quantization"); choosing the factors needs
+ * calibration data and is not done here. The caller quantises
+ * w'[n][k] = w[n][k] * a_k with any pack call and passes act_mul[k] = 1 / a_k
+ * (fp32, device, 16-byte aligned, [K]).
+ *
+ * w4a16_scale_activations: x_out[m][k] = x[m][k] * act_mul[k], the fp32
+ * product rounded once (to nearest even) to x's type. x_out may be x itself.
+ *
+ * w4a16_linear_awq: y = x_out . w_hat'^T. When the GEMV takes the shape
+ * (M <= 8 and the activations fit its LDS) the scaling is folded into the
+ * GEMV's activation staging: one launch, no workspace. Otherwise it runs
+ * w4a16_scale_activations into the workspace (w4a16_awq_workspace_bytes:
+ * M*K*2 rounded up to 256) followed by w4a16_gemm. Either way the result is
+ * the one the same kernel gives for the pre-scaled activations. */
+w4a16_status w4a16_scale_activations(const void *x, int32_t dtype, const float *act_mul, void *x_out,
+                                     int64_t M, int64_t K, void *stream);
+w4a16_status w4a16_awq_workspace_bytes(int64_t M, int64_t N, int64_t K, int32_t group, int32_t dtype,
+                                       size_t *bytes);
+w4a16_status w4a16_linear_awq(const void *x, int32_t dtype, const float *act_mul, const void *qweight,
+                              const void *scales, const void *zeros, void *y, int64_t M, int64_t N,
+                              int64_t K, int32_t group, int32_t fmt, void *workspace,
+                              size_t workspace_bytes, void *stream);
+
 #ifdef __cplusplus
 }
 #endif

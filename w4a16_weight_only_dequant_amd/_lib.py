@@ -62,6 +62,12 @@ _SIGS = {
                                         _vp]),
     "w4a16_linear_group_fmt": (ctypes.c_int, [_i32, _vpp, _i32, _vpp, _vpp, _vpp, _vpp, _i64, _i64p, _i64, _i32,
                                               _i32, _vp, _sz, _vp]),
+    "w4a16_quant_error_workspace_bytes": (ctypes.c_int, [_i64, _i64, _i32, _szp]),
+    "w4a16_quant_error": (ctypes.c_int, [_vp, _vp, _vp, _vp, _i64, _i64, _i32, _i32, _vp, _vp, _sz, _vp]),
+    "w4a16_scale_activations": (ctypes.c_int, [_vp, _i32, _vp, _vp, _i64, _i64, _vp]),
+    "w4a16_awq_workspace_bytes": (ctypes.c_int, [_i64, _i64, _i64, _i32, _i32, _szp]),
+    "w4a16_linear_awq": (ctypes.c_int, [_vp, _i32, _vp, _vp, _vp, _vp, _vp, _i64, _i64, _i64, _i32, _i32, _vp, _sz,
+                                        _vp]),
 }
 
 EXPORTED = tuple(_SIGS)
@@ -284,3 +290,61 @@ def linear_group(xs, pws, outs=None, workspace=None, stream=None):
 def linear(x, pw, out=None, workspace=None, stream=None):
     """Default path, dispatching on M."""
     return _call("w4a16_linear", x, pw, out, workspace, stream)
+
+
+QUALITY_FIELDS = ("mse", "snr_db", "cos", "max_err", "sum_d2", "sum_w2", "sum_h2", "sum_wh")
+
+
+def quant_error(w: torch.Tensor, pw: PackedWeight, stream=None) -> dict:
+    """Quality report of packed weights against the fp32 weights [N][K] (device)
+    they were made from (w4a16_quant_error): MSE, SNR dB, cosine, max error and
+    the fp64 sums behind them."""
+    if w.dtype != torch.float32 or w.dim() != 2 or not w.is_cuda or tuple(w.shape) != (pw.N, pw.K):
+        raise TypeError(f"w must be a float32 CUDA tensor [{pw.N}][{pw.K}]")
+    w = w.contiguous()
+    nb = _sz()
+    _check("w4a16_quant_error_workspace_bytes",
+           _lib.w4a16_quant_error_workspace_bytes(pw.N, pw.K, pw.group, ctypes.byref(nb)))
+    ws = torch.empty(max(nb.value, 16), dtype=torch.uint8, device=w.device)
+    out = torch.empty(8, dtype=torch.float64, device=w.device)
+    _check("w4a16_quant_error", _lib.w4a16_quant_error(
+        w.data_ptr(), pw.qweight.data_ptr(), pw.scales.data_ptr(), pw.zeros_ptr(), pw.N, pw.K, pw.group,
+        _fmt_code(pw.fmt), out.data_ptr(), ws.data_ptr(), ws.numel(), _stream_ptr(stream)))
+    vals = out.cpu().tolist()
+    return dict(zip(QUALITY_FIELDS, vals))
+
+
+def scale_activations(x: torch.Tensor, act_mul: torch.Tensor, out=None, stream=None):
+    """x * act_mul along K, rounded once to x's type (w4a16_scale_activations)."""
+    if x.dim() != 2 or not x.is_cuda:
+        raise ValueError("x must be a CUDA tensor [M][K]")
+    x = x.contiguous()
+    M, K = x.shape
+    if act_mul.dtype != torch.float32 or act_mul.numel() != K or not act_mul.is_cuda:
+        raise TypeError(f"act_mul must be a float32 CUDA tensor [{K}]")
+    y = out if out is not None else torch.empty_like(x)
+    _check("w4a16_scale_activations", _lib.w4a16_scale_activations(
+        x.data_ptr(), _dtype_code(x), act_mul.contiguous().data_ptr(), y.data_ptr(), M, K, _stream_ptr(stream)))
+    return y
+
+
+def linear_awq(x: torch.Tensor, act_mul: torch.Tensor, pw: PackedWeight, out=None, workspace=None, stream=None):
+    """AWQ run-time path: y = (x * act_mul) @ w_hat^T (w4a16_linear_awq); the
+    weights are the quantised w * (1 / act_mul)."""
+    if x.dim() != 2 or x.shape[1] != pw.K or not x.is_cuda:
+        raise ValueError(f"x must be a CUDA tensor [M][{pw.K}]")
+    if act_mul.dtype != torch.float32 or act_mul.numel() != pw.K or not act_mul.is_cuda:
+        raise TypeError(f"act_mul must be a float32 CUDA tensor [{pw.K}]")
+    x = x.contiguous()
+    act_mul = act_mul.contiguous()
+    M = x.shape[0]
+    y = out if out is not None else torch.empty((M, pw.N), dtype=x.dtype, device=x.device)
+    nb = _sz()
+    _check("w4a16_awq_workspace_bytes", _lib.w4a16_awq_workspace_bytes(M, pw.N, pw.K, pw.group, _dtype_code(x),
+                                                                       ctypes.byref(nb)))
+    ws = (workspace or _default_workspace(x.device)).get(nb.value)
+    _check("w4a16_linear_awq", _lib.w4a16_linear_awq(
+        x.data_ptr(), _dtype_code(x), act_mul.data_ptr(), pw.qweight.data_ptr(), pw.scales.data_ptr(),
+        pw.zeros_ptr(), y.data_ptr(), M, pw.N, pw.K, pw.group, _fmt_code(pw.fmt),
+        ws.data_ptr() if ws is not None else None, ws.numel() if ws is not None else 0, _stream_ptr(stream)))
+    return y

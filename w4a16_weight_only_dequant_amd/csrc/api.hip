@@ -258,7 +258,7 @@ w4a16_status w4a16_gemv_fmt(const void *x, int32_t dtype, const void *qweight, c
     if (!gemv_fits(M, N, K, group, dtype)) return W4A16_ERR_INVALID_ARG;
     GemvPlan plan = gemv_plan(M, N, K, group);
     hipError_t e = launch_gemv(x, dtype == W4A16_BF16, qweight, scales, zeros, y, (int)M, (int)N,
-                               (int)K, group, fmt, plan, reinterpret_cast<hipStream_t>(stream));
+                               (int)K, group, fmt, nullptr, plan, reinterpret_cast<hipStream_t>(stream));
     return e == hipSuccess ? W4A16_OK : W4A16_ERR_HIP;
 }
 
@@ -370,6 +370,92 @@ w4a16_status w4a16_linear(const void *x, int32_t dtype, const void *qweight, con
                           void *workspace, size_t workspace_bytes, void *stream) {
     return w4a16_linear_fmt(x, dtype, qweight, scales, zeros, y, M, N, K, group, W4A16_FMT_ASYM4, workspace,
                             workspace_bytes, stream);
+}
+
+w4a16_status w4a16_quant_error_workspace_bytes(int64_t N, int64_t K, int32_t group, size_t *bytes) {
+    if (!bytes || !shape_ok(N, K, group)) return W4A16_ERR_INVALID_ARG;
+    *bytes = quant_error_partial_bytes((int)N);
+    return W4A16_OK;
+}
+
+w4a16_status w4a16_quant_error(const float *w, const void *qweight, const void *scales, const void *zeros,
+                               int64_t N, int64_t K, int32_t group, int32_t fmt, double *out, void *workspace,
+                               size_t workspace_bytes, void *stream) {
+    if (!fmt_ok(fmt) || !shape_ok(N, K, group)) return W4A16_ERR_INVALID_ARG;
+    const bool zp = fmt == W4A16_FMT_ASYM4;
+    if (!w || !qweight || !scales || (zp && !zeros) || !out) return W4A16_ERR_INVALID_ARG;
+    if (!aligned16(w) || !aligned16(qweight) || !aligned16(out)) return W4A16_ERR_INVALID_ARG;
+    const size_t need = quant_error_partial_bytes((int)N);
+    if (!workspace || workspace_bytes < need) return W4A16_ERR_WORKSPACE;
+    if (!aligned16(workspace)) return W4A16_ERR_INVALID_ARG;
+    size_t qb, sb, zb;
+    meta_bytes(N, K, group, fmt, &qb, &sb, &zb);
+    const Range ro = range_of(out, 8 * sizeof(double)), rw = range_of(workspace, need);
+    const Range ins[4] = {range_of(w, (size_t)(N * K * 4)), range_of(qweight, qb), range_of(scales, sb),
+                          range_of(zeros, zb)};
+    for (const Range &r : ins)
+        if (overlap(ro, r) || overlap(rw, r)) return W4A16_ERR_INVALID_ARG;
+    if (overlap(ro, rw)) return W4A16_ERR_INVALID_ARG;
+    w4a16_status st = check_device();
+    if (st != W4A16_OK) return st;
+    hipError_t e = launch_quant_error(w, qweight, scales, zeros, (int)N, (int)K, group, fmt, out,
+                                      reinterpret_cast<double *>(workspace), reinterpret_cast<hipStream_t>(stream));
+    return e == hipSuccess ? W4A16_OK : W4A16_ERR_HIP;
+}
+
+w4a16_status w4a16_scale_activations(const void *x, int32_t dtype, const float *act_mul, void *x_out, int64_t M,
+                                     int64_t K, void *stream) {
+    if (!x || !act_mul || !x_out || M < 1 || M > (1LL << 24) || K < 8 || K % 8 != 0 || K > (1LL << 30))
+        return W4A16_ERR_INVALID_ARG;
+    if (dtype != W4A16_F16 && dtype != W4A16_BF16) return W4A16_ERR_INVALID_ARG;
+    if (!aligned16(x) || !aligned16(act_mul) || !aligned16(x_out)) return W4A16_ERR_INVALID_ARG;
+    const Range ro = range_of(x_out, (size_t)(M * K * 2));
+    if (overlap(ro, range_of(act_mul, (size_t)K * 4))) return W4A16_ERR_INVALID_ARG;
+    if (x != x_out && overlap(ro, range_of(x, (size_t)(M * K * 2)))) return W4A16_ERR_INVALID_ARG;
+    w4a16_status st = check_device();
+    if (st != W4A16_OK) return st;
+    hipError_t e = launch_scale_activations(x, dtype == W4A16_BF16, act_mul, x_out, M, (int)K,
+                                            reinterpret_cast<hipStream_t>(stream));
+    return e == hipSuccess ? W4A16_OK : W4A16_ERR_HIP;
+}
+
+w4a16_status w4a16_awq_workspace_bytes(int64_t M, int64_t N, int64_t K, int32_t group, int32_t dtype,
+                                       size_t *bytes) {
+    if (!bytes || M < 1 || M > (1LL << 24) || !shape_ok(N, K, group) || (dtype != W4A16_F16 && dtype != W4A16_BF16))
+        return W4A16_ERR_INVALID_ARG;
+    *bytes = gemv_fits(M, N, K, group, dtype) ? 0 : align_up((size_t)(M * K * 2), 256);
+    return W4A16_OK;
+}
+
+w4a16_status w4a16_linear_awq(const void *x, int32_t dtype, const float *act_mul, const void *qweight,
+                              const void *scales, const void *zeros, void *y, int64_t M, int64_t N, int64_t K,
+                              int32_t group, int32_t fmt, void *workspace, size_t workspace_bytes, void *stream) {
+    if (!act_mul || !aligned16(act_mul)) return W4A16_ERR_INVALID_ARG;
+    w4a16_status st = check_linear(x, dtype, qweight, scales, zeros, y, M, N, K, group, fmt, nullptr, 0, 0);
+    if (st != W4A16_OK) return st;
+    if (overlap(range_of(y, (size_t)(M * N * 2)), range_of(act_mul, (size_t)K * 4))) return W4A16_ERR_INVALID_ARG;
+    const bool fused = gemv_fits(M, N, K, group, dtype);
+    const size_t need = fused ? 0 : align_up((size_t)(M * K * 2), 256);
+    if (need > 0) {
+        if (!workspace || workspace_bytes < need) return W4A16_ERR_WORKSPACE;
+        if (!aligned16(workspace)) return W4A16_ERR_INVALID_ARG;
+        const Range rw = range_of(workspace, need);
+        if (overlap(rw, range_of(y, (size_t)(M * N * 2))) || overlap(rw, range_of(x, (size_t)(M * K * 2))) ||
+            overlap(rw, range_of(act_mul, (size_t)K * 4)))
+            return W4A16_ERR_INVALID_ARG;
+    }
+    st = check_device();
+    if (st != W4A16_OK) return st;
+    const hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+    if (fused) {   // one launch: the GEMV scales the activations as it stages them
+        const GemvPlan plan = gemv_plan(M, N, K, group);
+        hipError_t e = launch_gemv(x, dtype == W4A16_BF16, qweight, scales, zeros, y, (int)M, (int)N, (int)K, group,
+                                   fmt, act_mul, plan, s);
+        return e == hipSuccess ? W4A16_OK : W4A16_ERR_HIP;
+    }
+    hipError_t e = launch_scale_activations(x, dtype == W4A16_BF16, act_mul, workspace, M, (int)K, s);
+    if (e != hipSuccess) return W4A16_ERR_HIP;
+    return w4a16_gemm_fmt(workspace, dtype, qweight, scales, zeros, y, M, N, K, group, fmt, nullptr, 0, stream);
 }
 
 }  // extern "C"

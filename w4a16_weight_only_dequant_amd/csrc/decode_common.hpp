@@ -14,6 +14,8 @@ namespace w4a16 {
 
 constexpr int kColumn = kChunk * kColChunks;   // 128 weights of K per column
 
+typedef float float2_t __attribute__((ext_vector_type(2)));
+
 // A 32-bit constant materialised in a VGPR. VOP3 instructions (v_and_or_b32)
 // cannot take two literal operands on gfx9, so the masks and magic numbers of
 // the unpack live in registers, which lets (d & mask) | magic issue as one

@@ -40,15 +40,16 @@ GemvPlan gemv_plan(int64_t M, int64_t N, int64_t K, int32_t group) {
 
 hipError_t launch_gemv(const void *x, bool bf16, const void *qweight, const void *scales,
                        const void *zeros, void *y, int M, int N, int K, int group, int fmt,
-                       const GemvPlan &plan, hipStream_t stream) {
+                       const float *act_mul, const GemvPlan &plan, hipStream_t stream) {
+    const float *am = act_mul;
     switch (fmt) {
-        case kSym4: return launch_gemv_fmt<kSym4>(x, bf16, qweight, scales, zeros, y, M, N, K, group, plan, stream);
-        case kSym8: return launch_gemv_fmt<kSym8>(x, bf16, qweight, scales, zeros, y, M, N, K, group, plan, stream);
-        default: return launch_gemv_fmt<kAsym4>(x, bf16, qweight, scales, zeros, y, M, N, K, group, plan, stream);
+        case kSym4: return launch_gemv_fmt<kSym4>(x, bf16, qweight, scales, zeros, y, M, N, K, group, am, plan, stream);
+        case kSym8: return launch_gemv_fmt<kSym8>(x, bf16, qweight, scales, zeros, y, M, N, K, group, am, plan, stream);
+        default: return launch_gemv_fmt<kAsym4>(x, bf16, qweight, scales, zeros, y, M, N, K, group, am, plan, stream);
     }
 }
 
 template hipError_t launch_gemv_fmt<kAsym4>(const void *, bool, const void *, const void *, const void *, void *,
-                                            int, int, int, int, const GemvPlan &, hipStream_t);
+                                            int, int, int, int, const float *, const GemvPlan &, hipStream_t);
 
 }  // namespace w4a16

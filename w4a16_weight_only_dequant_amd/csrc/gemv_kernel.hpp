@@ -50,6 +50,33 @@ __device__ inline float dot_pair(uint32_t w, uint32_t x, float acc) {
                                       __builtin_bit_cast(half2_t, x), acc, false);
 }
 
+// Eight 16-bit activations times eight fp32 multipliers, each product rounded
+// once to the activation type (round to nearest even).
+template <bool BF>
+__device__ inline uint4 scale8(const uint4 &v, const float4 &a, const float4 &b) {
+    const float m[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
+    const uint32_t in[4] = {v.x, v.y, v.z, v.w};
+    uint32_t out[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        float lo, hi;
+        if constexpr (BF) {
+            lo = __builtin_bit_cast(float, in[i] << 16);
+            hi = __builtin_bit_cast(float, in[i] & 0xFFFF0000u);
+        } else {
+            const half2_t h = __builtin_bit_cast(half2_t, in[i]);
+            lo = (float)h.x;
+            hi = (float)h.y;
+        }
+        const float2_t p = {lo * m[2 * i], hi * m[2 * i + 1]};
+        if constexpr (BF)
+            out[i] = __builtin_bit_cast(uint32_t, __builtin_convertvector(p, bf162_t));
+        else
+            out[i] = __builtin_bit_cast(uint32_t, __builtin_convertvector(p, half2_t));
+    }
+    return make_uint4(out[0], out[1], out[2], out[3]);
+}
+
 // LDS bytes of one wave: activations [MT][xcols*128] (16-bit) and, for bf16,
 // their sums over every 8 consecutive k ([MT][xcols*16] fp32).
 __host__ __device__ inline size_t wave_lds_bytes(int MT, int xcols, bool bf16, int group) {
@@ -57,11 +84,13 @@ __host__ __device__ inline size_t wave_lds_bytes(int MT, int xcols, bool bf16, i
     return (size_t)MT * xcols * 256 + (bf16 ? (size_t)MT * xcols * 64 : 0);
 }
 
+// act_mul: NULL, or fp32 multipliers [K] applied to the activations as they
+// are staged (AWQ's run-time scaling: x' = rne16(x * m)).
 template <int GROUP, int MT, bool BF, int FMT>
 __global__ __launch_bounds__(64 * kMaxWaves) __attribute__((amdgpu_waves_per_eu(1, 4))) void gemv_kernel(
     const uint16_t *__restrict__ x, const uint4 *__restrict__ qw, const uint4 *__restrict__ qw_hi,
     const uint16_t *__restrict__ scales, const uint32_t *__restrict__ zeros, uint16_t *__restrict__ y, int N,
-    int K, int xcols, int mshift) {
+    int K, int xcols, int mshift, const float *__restrict__ act_mul) {
     using FT = FormatTraits<FMT>;
     constexpr int CPG = GROUP / kChunk;   // chunks per group (1, 2, 4)
     constexpr int PF0 = MT == 1 ? kPrefetch : (MT == 2 ? 4 : (MT <= 4 ? 3 : 2));
@@ -159,6 +188,18 @@ __global__ __launch_bounds__(64 * kMaxWaves) __attribute__((amdgpu_waves_per_eu(
             xdst(base + 2 * 64 + lane, v2); xdst(base + 3 * 64 + lane, v3);
             xdst(base + 4 * 64 + lane, v4); xdst(base + 5 * 64 + lane, v5);
             xdst(base + 6 * 64 + lane, v6); xdst(base + 7 * 64 + lane, v7);
+        }
+        if (act_mul != nullptr) {
+            // AWQ: scale the staged activations in place (each lane rewrites
+            // the entries it stored; the multiplier loads retire after the
+            // weight prefetch, which the first column waits for anyway)
+            const float4 *mv = reinterpret_cast<const float4 *>(act_mul);
+            for (int i = lane; i < xtotal; i += 64) {
+                const int m = i / per_m, q = i - m * per_m;
+                const int k8 = sl.c_lo * 4 + q;   // 8-activation unit along K
+                uint4 &slot = xw[(size_t)m * xcols * 16 + q];
+                slot = scale8<BF>(slot, mv[2 * k8], mv[2 * k8 + 1]);
+            }
         }
         if constexpr (BF) {
             // sum of every 8 activations (one k-slice of one chunk)
@@ -295,7 +336,7 @@ __global__ __launch_bounds__(64 * kMaxWaves) __attribute__((amdgpu_waves_per_eu(
 
 template <int GROUP, bool BF, int MT, int FMT>
 hipError_t launch_one(const void *x, const void *qw, const void *qw_hi, const void *sc, const void *zp, void *y,
-                      int N, int K, int mshift, const GemvPlan &plan, hipStream_t stream) {
+                      int N, int K, int mshift, const float *am, const GemvPlan &plan, hipStream_t stream) {
     const int xcols = gemv_xcols(K, plan.waves);
     const size_t lds = wave_lds_bytes(MT, xcols, BF, GROUP) * plan.waves;
     auto kern = gemv_kernel<GROUP, MT, BF, FMT>;
@@ -308,22 +349,22 @@ hipError_t launch_one(const void *x, const void *qw, const void *qw_hi, const vo
                        reinterpret_cast<const uint16_t *>(x), reinterpret_cast<const uint4 *>(qw),
                        reinterpret_cast<const uint4 *>(qw_hi), reinterpret_cast<const uint16_t *>(sc),
                        reinterpret_cast<const uint32_t *>(zp), reinterpret_cast<uint16_t *>(y), N, K, xcols,
-                       mshift);
+                       mshift, am);
     return hipGetLastError();
 }
 
 template <int GROUP, bool BF, int FMT>
 hipError_t launch_m(int M, const void *x, const void *qw, const void *qh, const void *sc, const void *zp, void *y,
-                    int N, int K, int ms, const GemvPlan &plan, hipStream_t stream) {
+                    int N, int K, int ms, const float *am, const GemvPlan &plan, hipStream_t stream) {
     switch (M) {
-        case 1: return launch_one<GROUP, BF, 1, FMT>(x, qw, qh, sc, zp, y, N, K, ms, plan, stream);
-        case 2: return launch_one<GROUP, BF, 2, FMT>(x, qw, qh, sc, zp, y, N, K, ms, plan, stream);
-        case 3: return launch_one<GROUP, BF, 3, FMT>(x, qw, qh, sc, zp, y, N, K, ms, plan, stream);
-        case 4: return launch_one<GROUP, BF, 4, FMT>(x, qw, qh, sc, zp, y, N, K, ms, plan, stream);
-        case 5: return launch_one<GROUP, BF, 5, FMT>(x, qw, qh, sc, zp, y, N, K, ms, plan, stream);
-        case 6: return launch_one<GROUP, BF, 6, FMT>(x, qw, qh, sc, zp, y, N, K, ms, plan, stream);
-        case 7: return launch_one<GROUP, BF, 7, FMT>(x, qw, qh, sc, zp, y, N, K, ms, plan, stream);
-        default: return launch_one<GROUP, BF, 8, FMT>(x, qw, qh, sc, zp, y, N, K, ms, plan, stream);
+        case 1: return launch_one<GROUP, BF, 1, FMT>(x, qw, qh, sc, zp, y, N, K, ms, am, plan, stream);
+        case 2: return launch_one<GROUP, BF, 2, FMT>(x, qw, qh, sc, zp, y, N, K, ms, am, plan, stream);
+        case 3: return launch_one<GROUP, BF, 3, FMT>(x, qw, qh, sc, zp, y, N, K, ms, am, plan, stream);
+        case 4: return launch_one<GROUP, BF, 4, FMT>(x, qw, qh, sc, zp, y, N, K, ms, am, plan, stream);
+        case 5: return launch_one<GROUP, BF, 5, FMT>(x, qw, qh, sc, zp, y, N, K, ms, am, plan, stream);
+        case 6: return launch_one<GROUP, BF, 6, FMT>(x, qw, qh, sc, zp, y, N, K, ms, am, plan, stream);
+        case 7: return launch_one<GROUP, BF, 7, FMT>(x, qw, qh, sc, zp, y, N, K, ms, am, plan, stream);
+        default: return launch_one<GROUP, BF, 8, FMT>(x, qw, qh, sc, zp, y, N, K, ms, am, plan, stream);
     }
 }
 
@@ -333,22 +374,23 @@ hipError_t launch_m(int M, const void *x, const void *qw, const void *qh, const 
 // with one metadata slot per two columns (mshift = 1).
 template <int FMT>
 hipError_t launch_gemv_fmt(const void *x, bool bf16, const void *qweight, const void *scales, const void *zeros,
-                           void *y, int M, int N, int K, int group, const GemvPlan &plan, hipStream_t stream) {
+                           void *y, int M, int N, int K, int group, const float *am, const GemvPlan &plan,
+                           hipStream_t stream) {
     const int ms = group == 256 ? 1 : 0;
     const void *qh = FormatTraits<FMT>::two_planes
                          ? static_cast<const void *>(static_cast<const char *>(qweight) + (size_t)N * K / 2)
                          : qweight;
     if (bf16) {
         switch (group) {
-            case 32: return launch_m<32, true, FMT>(M, x, qweight, qh, scales, zeros, y, N, K, ms, plan, stream);
-            case 64: return launch_m<64, true, FMT>(M, x, qweight, qh, scales, zeros, y, N, K, ms, plan, stream);
-            default: return launch_m<128, true, FMT>(M, x, qweight, qh, scales, zeros, y, N, K, ms, plan, stream);
+            case 32: return launch_m<32, true, FMT>(M, x, qweight, qh, scales, zeros, y, N, K, ms, am, plan, stream);
+            case 64: return launch_m<64, true, FMT>(M, x, qweight, qh, scales, zeros, y, N, K, ms, am, plan, stream);
+            default: return launch_m<128, true, FMT>(M, x, qweight, qh, scales, zeros, y, N, K, ms, am, plan, stream);
         }
     }
     switch (group) {
-        case 32: return launch_m<32, false, FMT>(M, x, qweight, qh, scales, zeros, y, N, K, ms, plan, stream);
-        case 64: return launch_m<64, false, FMT>(M, x, qweight, qh, scales, zeros, y, N, K, ms, plan, stream);
-        default: return launch_m<128, false, FMT>(M, x, qweight, qh, scales, zeros, y, N, K, ms, plan, stream);
+        case 32: return launch_m<32, false, FMT>(M, x, qweight, qh, scales, zeros, y, N, K, ms, am, plan, stream);
+        case 64: return launch_m<64, false, FMT>(M, x, qweight, qh, scales, zeros, y, N, K, ms, am, plan, stream);
+        default: return launch_m<128, false, FMT>(M, x, qweight, qh, scales, zeros, y, N, K, ms, am, plan, stream);
     }
 }
 

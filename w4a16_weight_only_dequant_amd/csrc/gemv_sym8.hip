@@ -4,6 +4,6 @@
 namespace w4a16 {
 
 template hipError_t launch_gemv_fmt<kSym8>(const void *, bool, const void *, const void *, const void *, void *,
-                                          int, int, int, int, const GemvPlan &, hipStream_t);
+                                          int, int, int, int, const float *, const GemvPlan &, hipStream_t);
 
 }  // namespace w4a16

@@ -34,7 +34,6 @@ namespace {
 typedef _Float16 h8_t __attribute__((ext_vector_type(8)));
 typedef __bf16 b8_t __attribute__((ext_vector_type(8)));
 typedef float f16_t __attribute__((ext_vector_type(16)));
-typedef float float2_t __attribute__((ext_vector_type(2)));
 
 constexpr int kStepK = 64;                    // k per LDS step
 struct Plain { static constexpr bool value = false; };

@@ -98,9 +98,19 @@ hipError_t launch_pack(const float *w, int N, int K, int group, int fmt, void *q
 hipError_t launch_unpack(const void *qweight, const void *scales, const void *zeros,
                          int N, int K, int group, int fmt, uint8_t *codes, uint16_t *scales_out,
                          uint8_t *zeros_out, hipStream_t stream);
+// Quality report: five fp64 sums per row block into `partial`, then one
+// workgroup folds them in a fixed order into out[8].
+size_t quant_error_partial_bytes(int N);
+hipError_t launch_quant_error(const float *w, const void *qweight, const void *scales, const void *zeros,
+                              int N, int K, int group, int fmt, double *out, double *partial,
+                              hipStream_t stream);
+// x_out[m][k] = rne16(x[m][k] * act_mul[k]).
+hipError_t launch_scale_activations(const void *x, bool bf16, const float *act_mul, void *x_out, int64_t M,
+                                    int K, hipStream_t stream);
+// act_mul: NULL, or fp32 activation multipliers [K] (AWQ's run-time scaling)
 hipError_t launch_gemv(const void *x, bool bf16, const void *qweight, const void *scales,
                        const void *zeros, void *y, int M, int N, int K, int group, int fmt,
-                       const GemvPlan &plan, hipStream_t stream);
+                       const float *act_mul, const GemvPlan &plan, hipStream_t stream);
 hipError_t launch_gemm(const void *x, bool bf16, const void *qweight, const void *scales,
                        const void *zeros, void *y, int M, int N, int K, int group, int fmt,
                        const GemmPlan &plan, hipStream_t stream);
@@ -112,14 +122,16 @@ int prefill_tile(int64_t M, int64_t N);
 // The kernels of one format, each compiled in a translation unit of its own.
 #define W4A16_LINEAR_PARAMS const void *x, bool bf16, const void *qweight, const void *scales, const void *zeros, \
                             void *y, int M, int N, int K, int group
-template <int FMT> hipError_t launch_gemv_fmt(W4A16_LINEAR_PARAMS, const GemvPlan &plan, hipStream_t stream);
+template <int FMT>
+hipError_t launch_gemv_fmt(W4A16_LINEAR_PARAMS, const float *act_mul, const GemvPlan &plan, hipStream_t stream);
 template <int FMT> hipError_t launch_skinny_fmt(W4A16_LINEAR_PARAMS, const GemmPlan &plan, hipStream_t stream);
 template <int FMT> hipError_t launch_prefill_fmt(W4A16_LINEAR_PARAMS, const GemmPlan &plan, hipStream_t stream);
 template <int FMT>
 hipError_t launch_skinny_group_fmt(const GroupTable &tab, bool bf16, int M, int K, int group, const GemmPlan &plan,
                                    hipStream_t stream);
 #define W4A16_EXTERN_FMT(F)                                                                              \
-    extern template hipError_t launch_gemv_fmt<F>(W4A16_LINEAR_PARAMS, const GemvPlan &, hipStream_t);   \
+    extern template hipError_t launch_gemv_fmt<F>(W4A16_LINEAR_PARAMS, const float *, const GemvPlan &,  \
+                                                  hipStream_t);                                         \
     extern template hipError_t launch_skinny_fmt<F>(W4A16_LINEAR_PARAMS, const GemmPlan &, hipStream_t); \
     extern template hipError_t launch_prefill_fmt<F>(W4A16_LINEAR_PARAMS, const GemmPlan &, hipStream_t); \
     extern template hipError_t launch_skinny_group_fmt<F>(const GroupTable &, bool, int, int, int,        \
