@@ -22,6 +22,8 @@ seven layers with q/k/v and gate/up each in one launch (w4a16_linear_group);
 `value` stays the seven-launch step. `formats` repeats the decode step and
 the prefill GEMM with the weights in the other formats (symmetric 4-bit,
 symmetric 8-bit = W8A16, group 256), each against its own bytes and flops.
+`quality` is the quantisation quality report of each matrix (w4a16_quant_error)
+and `awq_step` the decode step through the AWQ run-time path.
 `cpu_baseline` times the CPU
 oracle (dequantise + fp64 product) on a bounded sample of the headline workload.
 """
@@ -158,9 +160,18 @@ class Workload:
 
     def time_grouped(self, dev, groups, steps, warmup):
         """Wall time per step of the grouped step (one HIP graph per weight copy)."""
+        return self.time_fn(dev, lambda c: self.step_grouped(c, groups), steps, warmup)
+
+    def step_awq(self, c, act_mul):
+        """One step through w4a16_linear_awq (activation multipliers per matrix)."""
+        for j in range(len(self.mats)):
+            self.w4.linear_awq(self.xs[j], act_mul[j], self.sets[c][j], out=self.ys[j], workspace=self.ws)
+
+    def time_fn(self, dev, fn, steps, warmup):
+        """Wall time per step of fn(copy) replayed from one HIP graph per weight copy."""
         torch = self.torch
         for c in range(min(2, self.copies)):
-            self.step_grouped(c, groups)
+            fn(c)
         torch.cuda.synchronize()
         cap = torch.cuda.Stream(device=dev)
         graphs = []
@@ -168,7 +179,7 @@ class Workload:
             for c in range(self.copies):
                 g = torch.cuda.CUDAGraph()
                 with torch.cuda.graph(g, stream=cap):
-                    self.step_grouped(c, groups)
+                    fn(c)
                 graphs.append(g)
         torch.cuda.synchronize()
         for i in range(warmup):
@@ -266,6 +277,53 @@ def time_steps(wk, steps, warmup):
         wk.step_graphs[i % wk.copies].replay()
     torch.cuda.synchronize()
     return (time.perf_counter() - t0) * 1e3 / steps
+
+
+def quality_and_awq(dev, cfg_id, M, steps, warmup):
+    """Quality report of every matrix of the workload (w4a16_quant_error: its
+    two kernels timed with HIP events, fp32 weights + packed bytes read), and
+    the decode step through w4a16_linear_awq with 1 % of the input channels
+    scaled by 8 (the GEMV folds the activation scaling into its staging)."""
+    import numpy as np
+    import torch
+
+    import w4a16_weight_only_dequant_amd as w4
+    import workloads as wl
+    cfg = wl.WORKLOADS[cfg_id]
+    report = {}
+    for j, mat in enumerate(cfg.matrices):
+        w = torch.from_numpy(wl.weights(cfg_id, j)).to(dev)
+        pw = w4.pack(w, cfg.group)
+        w4.quant_error(w, pw)
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        reps = 5
+        e0.record()
+        for _ in range(reps):
+            r = w4.quant_error(w, pw)
+        e1.record()
+        torch.cuda.synchronize()
+        us = e0.elapsed_time(e1) * 1e3 / reps   # includes the 64-byte result copy to the host
+        nbytes = mat.N * mat.K * 4 + pw.nbytes()
+        report[mat.name] = {"mse": r["mse"], "snr_db": round(r["snr_db"], 3), "cos": r["cos"],
+                            "max_err": r["max_err"], "us": round(us, 1), "GBs": round(nbytes / us / 1e3, 1)}
+        del w, pw
+    torch.cuda.empty_cache()
+    wk = Workload(cfg_id, M, dev)
+    rng = np.random.default_rng(5)
+    muls = []
+    for m in wk.mats:
+        a = np.ones(m.K, dtype=np.float32)
+        a[rng.choice(m.K, m.K // 100, replace=False)] = 8.0
+        muls.append(torch.from_numpy((1.0 / a).astype(np.float32)).to(dev))
+    plain_ms = wk.time_fn(dev, wk.step, steps, warmup)
+    awq_ms = wk.time_fn(dev, lambda c: wk.step_awq(c, muls), steps, warmup)
+    awq = {"ms_per_step": round(awq_ms, 5), "plain_ms_per_step": round(plain_ms, 5),
+           "value": round(sum(wk.bytes) / (awq_ms * 1e-3) / 1e9, 1), "unit": "GB/s",
+           "note": "decode step through w4a16_linear_awq (activation scaling folded into the GEMV staging)"}
+    del wk
+    torch.cuda.empty_cache()
+    return report, awq
 
 
 def format_legs(dev, cfg_id, M, steps, warmup, prefill_reps):
@@ -411,6 +469,10 @@ def main():
         del pk
         torch.cuda.empty_cache()
 
+    quality, awq = None, None
+    if not args.no_formats and args.workload == "decode_13b_layer":
+        quality, awq = quality_and_awq(dev, cfg_id, M, max(20, args.steps // 2), args.warmup)
+
     formats = None
     if not args.no_formats:
         formats = format_legs(dev, cfg_id, M, max(20, args.steps // 2), args.warmup, args.prefill_reps // 2)
@@ -453,6 +515,8 @@ def main():
         "grouped_step": grouped,
         "prefill": prefill,
         "formats": formats,
+        "quality": quality,
+        "awq_step": awq,
         "cpu_baseline": cpu,
     }
     print(json.dumps(out))
