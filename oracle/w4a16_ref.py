@@ -183,7 +183,7 @@ def bits_per_weight(group: int, scale_bits: int = 16, zero_bits: int = 4, code_b
     return code_bits + (scale_bits + zero_bits) / group
 
 
-FORMATS = ("asym4", "sym4", "sym8")
+FORMATS = ("asym4", "sym4", "sym8", "kq4")
 
 
 def code_bits(fmt: str) -> int:
@@ -194,14 +194,20 @@ def code_bits(fmt: str) -> int:
 
 def format_bits_per_weight(group: int, fmt: str = "asym4") -> float:
     """Storage per weight of a format: the code, the fp16 scale, and the 4-bit
-    zero-point only where the format stores one."""
+    zero-point only where the format stores one. kq4: 4-bit codes plus a 16-byte
+    record per 256 weights (4.5 bits)."""
+    if fmt == "kq4":
+        return 4 + 8 * KQ_RECORD_BYTES / KQ_SUPER
     return bits_per_weight(group, code_bits=code_bits(fmt), zero_bits=4 if fmt == "asym4" else 0)
 
 
 def packed_bytes(N: int, K: int, group: int, fmt: str = "asym4"):
     """(qweight, scales, zeros) algorithmic byte counts: one code per weight, one fp16
-    scale per (group, output column), and for asym4 one 4-bit zero per (group, column)."""
+    scale per (group, output column), and for asym4 one 4-bit zero per (group, column).
+    kq4 (group 256): one 16-byte record per (super-block, column), no zeros."""
     G = K // group
+    if fmt == "kq4":
+        return N * K // 2, KQ_RECORD_BYTES * G * N, 0
     return (N * K * code_bits(fmt)) // 8, 2 * G * N, (G * N) // 2 if fmt == "asym4" else 0
 
 
@@ -235,8 +241,8 @@ def quantize_groupwise(w, group: int, fmt: str = "asym4"):
     N, K = w.shape
     if group not in GROUPS or K % group != 0:
         raise ValueError("group must be 32/64/128/256 and divide K")
-    if fmt not in FORMATS:
-        raise ValueError(f"unknown format {fmt}")
+    if fmt not in FORMATS or fmt == "kq4":
+        raise ValueError(f"unknown format {fmt} (kq4: quantize_kquant)")
     if not np.all(np.isfinite(w)) or np.max(np.abs(w), initial=0.0) >= 2.0 ** 18:
         raise ValueError("weights must be finite with |w| < 2**18")
     G = K // group
@@ -570,3 +576,104 @@ def awq_scale_activations(x_bits, dtype: str, act_mul):
     x = act_bits_to_f64(x_bits, dtype).astype(np.float32)       # exact widening
     prod = x * np.asarray(act_mul, dtype=np.float32)[None, :]     # IEEE fp32 product
     return f32_to_f16_bits(prod) if dtype == "f16" else f32_to_bf16_bits(prod)
+
+
+# ---------------------------------------------------------------------------
+# K-quant-style super-blocks (kq4). "Quantization Is Not a Zip File", "How to
+# read common GGUF quantization names": K-quants keep sub-block scales and
+# minima inside 256-weight super-blocks. The pages give no more than that;
+# the reading used here (listed in the design notes) takes the asymmetric
+# quantiser above per 32-weight sub-block and quantises its scale and minimum
+# a second time, against the super-block's largest:
+#   per sub-block j:  lo = min(0, min w), hi = max(0, max w),
+#                     s_j = (hi - lo) / 15,  mn_j = 0 - lo       (fp32; +0, never -0)
+#   per super-block:  d = fp16(max_j s_j / 63), dmin = fp16(max_j mn_j / 63)
+#                     (0 -> 2**-24)
+#   sc_j = clamp(rint(s_j / d), 0, 63), mq_j = clamp(rint(mn_j / dmin), 0, 63)
+#   S_j = d * sc_j, M_j = dmin * mq_j                             (fp32, exact)
+#   q = clamp(rint((w + M_j) / S_j), 0, 15), and q = 0 where S_j = 0
+#   w_hat = S_j * q - M_j
+# Stored per (super-block u, output column n): a 16-byte record of four
+# little-endian words {d | dmin << 16, sc bits 0-31, sc bits 32-47 | mq bits
+# 0-15 << 16, mq bits 16-47}, where sc and mq are 48-bit fields holding the
+# eight 6-bit values at bits 6j..6j+5; records in [U][N] order (U = K / 256).
+# 4 + 128/256 = 4.5 bits per weight.
+# ---------------------------------------------------------------------------
+
+KQ_SUPER = 256
+KQ_SUB = 32
+KQ_RECORD_BYTES = 16
+
+
+def quantize_kquant(w):
+    """fp32 w [N][K] (K % 256 == 0) -> (codes u8 [N][K], d bits u16 [U][N],
+    dmin bits u16 [U][N], sc u8 [U][8][N], mq u8 [U][8][N])."""
+    w = np.ascontiguousarray(w, dtype=np.float32)
+    N, K = w.shape
+    if K % KQ_SUPER != 0 or K == 0:
+        raise ValueError("K must be a positive multiple of 256")
+    if not np.all(np.isfinite(w)) or np.max(np.abs(w), initial=0.0) >= 2.0 ** 18:
+        raise ValueError("weights must be finite with |w| < 2**18")
+    U = K // KQ_SUPER
+    wb = w.reshape(N, U, KQ_SUPER // KQ_SUB, KQ_SUB)
+    zero = np.float32(0.0)
+    lo = np.minimum(wb.min(axis=3), zero)                       # [N][U][8]
+    hi = np.maximum(wb.max(axis=3), zero)
+    s = (hi - lo) / np.float32(15.0)
+    mn = zero - lo                                               # +0 for a group without negatives
+    d_bits = f32_to_f16_bits(s.max(axis=2) / np.float32(63.0))
+    d_bits = np.where(d_bits == 0, F16_MIN_SUBNORMAL_BITS, d_bits).astype(np.uint16)
+    m_bits = f32_to_f16_bits(mn.max(axis=2) / np.float32(63.0))
+    m_bits = np.where(m_bits == 0, F16_MIN_SUBNORMAL_BITS, m_bits).astype(np.uint16)
+    d = f16_bits_to_f32(d_bits)[:, :, None]
+    dmin = f16_bits_to_f32(m_bits)[:, :, None]
+    sc = np.clip(np.rint(s / d), 0, 63).astype(np.int32)
+    mq = np.clip(np.rint(mn / dmin), 0, 63).astype(np.int32)
+    S = d * sc.astype(np.float32)
+    Mn = dmin * mq.astype(np.float32)
+    num = wb + Mn[..., None]
+    den = np.broadcast_to(S[..., None], num.shape)
+    with np.errstate(divide="ignore", invalid="ignore"):
+        r = np.where(den > 0, np.rint(np.divide(num, den, where=den > 0, out=np.zeros_like(num))), 0.0)
+    q = np.clip(r, 0, 15).astype(np.uint8)
+    return (q.reshape(N, K), np.ascontiguousarray(d_bits.T), np.ascontiguousarray(m_bits.T),
+            np.ascontiguousarray(sc.transpose(1, 2, 0).astype(np.uint8)),
+            np.ascontiguousarray(mq.transpose(1, 2, 0).astype(np.uint8)))
+
+
+def kquant_sub_params(d_bits, m_bits, sc, mq):
+    """(S, M) fp64 [N][K/32]: the effective scale and minimum of every sub-block."""
+    d = f16_bits_to_f64(d_bits).T                                # [N][U]
+    dmin = f16_bits_to_f64(m_bits).T
+    S = d[:, :, None] * np.asarray(sc, dtype=np.float64).transpose(2, 0, 1)
+    M = dmin[:, :, None] * np.asarray(mq, dtype=np.float64).transpose(2, 0, 1)
+    N = S.shape[0]
+    return S.reshape(N, -1), M.reshape(N, -1)
+
+
+def dequantize_kquant(codes, d_bits, m_bits, sc, mq) -> np.ndarray:
+    """w_hat [N][K] = S_j * q - M_j in fp64."""
+    codes = np.asarray(codes, dtype=np.uint8)
+    N, K = codes.shape
+    S, M = kquant_sub_params(d_bits, m_bits, sc, mq)
+    q = codes.reshape(N, K // KQ_SUB, KQ_SUB).astype(np.float64)
+    return (q * S[:, :, None] - M[:, :, None]).reshape(N, K)
+
+
+def pack_kquant_records(d_bits, m_bits, sc, mq) -> np.ndarray:
+    """Super-block records, uint32 [U][N][4] (layout above)."""
+    d_bits = np.asarray(d_bits, dtype=np.uint64)
+    U, N = d_bits.shape
+    sc = np.asarray(sc, dtype=np.uint64)
+    mq = np.asarray(mq, dtype=np.uint64)
+    scf = np.zeros((U, N), dtype=np.uint64)
+    mqf = np.zeros((U, N), dtype=np.uint64)
+    for j in range(KQ_SUPER // KQ_SUB):
+        scf |= sc[:, j, :] << np.uint64(6 * j)
+        mqf |= mq[:, j, :] << np.uint64(6 * j)
+    rec = np.zeros((U, N, 4), dtype=np.uint64)
+    rec[:, :, 0] = d_bits | (np.asarray(m_bits, dtype=np.uint64) << np.uint64(16))
+    rec[:, :, 1] = scf & np.uint64(0xFFFFFFFF)
+    rec[:, :, 2] = (scf >> np.uint64(32)) | ((mqf & np.uint64(0xFFFF)) << np.uint64(16))
+    rec[:, :, 3] = mqf >> np.uint64(16)
+    return rec.astype(np.uint32)

@@ -503,7 +503,7 @@ def test_int8_per_tensor_matches_integer_search():
 
 def test_format_byte_accounting():
     for N, K, g in [(4096, 4096, 128), (5120, 13824, 256), (8192, 28672, 32)]:
-        for fmt in ref.FORMATS:
+        for fmt in ("asym4", "sym4", "sym8"):
             q, s, z = ref.packed_bytes(N, K, g, fmt)
             assert (q + s + z) * 8 == N * K * ref.format_bits_per_weight(g, fmt)
     assert ref.format_bits_per_weight(128, "asym4") == 4.15625
@@ -652,3 +652,84 @@ def test_awq_fold_is_exact_for_power_of_two_factors():
     y, _ = ref.linear_ref_rows(xs, "f16", codes, s_bits, zeros, group)
     y_direct = ref.f16_bits_to_f64(xb) @ W.astype(np.float64).T
     assert np.allclose(y, y_direct, rtol=1e-13, atol=1e-300)
+
+
+# ---------------------------------------------------------------------------
+# K-quant-style super-blocks (kq4)
+# ---------------------------------------------------------------------------
+
+
+def test_kquant_lattice_is_reproduced_exactly():
+    """Sub-blocks built as S_j q - M_j with S_j = d sc_j, M_j = dmin mq_j (d, dmin
+    powers of two, one sc and one mq of 63 per super-block, q spanning 0..15)
+    come back with the same codes, d, dmin, sc, mq and w_hat = w."""
+    rng = np.random.default_rng(31)
+    N, U = 8, 3
+    K = 256 * U
+    d = np.ldexp(1.0, rng.integers(-14, -8, size=(U, N)))
+    dmin = d * np.ldexp(1.0, rng.integers(-3, 4, size=(U, N)))      # dmin <= 8 d
+    sc = rng.integers(1, 64, size=(U, 8, N))
+    sc[:, 0, :] = 63
+    # M_j <= 15 S_j keeps hi = 15 S_j - M_j >= 0 (the range reading); sub-block 0
+    # has sc = mq = 63 so that d and dmin are the super-block's largest / 63
+    cap = np.floor(15 * sc * (d / dmin)[:, None, :]).astype(np.int64)
+    mq = np.minimum(rng.integers(0, 64, size=(U, 8, N)), cap)
+    mq[:, 0, :] = 63
+    S = d[:, None, :] * sc
+    M = dmin[:, None, :] * mq
+    q = rng.integers(0, 16, size=(N, U, 8, 32))
+    q[..., 0], q[..., 1] = 0, 15
+    W = q * S.transpose(2, 0, 1)[..., None] - M.transpose(2, 0, 1)[..., None]
+    W = W.reshape(N, K).astype(np.float32)
+    assert np.array_equal(W.astype(np.float64).reshape(N, U, 8, 32),
+                          q * S.transpose(2, 0, 1)[..., None] - M.transpose(2, 0, 1)[..., None])
+    codes, d_bits, m_bits, sc_o, mq_o = ref.quantize_kquant(W)
+    assert np.array_equal(ref.f16_bits_to_f64(d_bits), d)
+    assert np.array_equal(ref.f16_bits_to_f64(m_bits), dmin)
+    assert np.array_equal(sc_o, sc) and np.array_equal(mq_o, mq)
+    assert np.array_equal(codes.reshape(N, U, 8, 32), q)
+    assert np.array_equal(ref.dequantize_kquant(codes, d_bits, m_bits, sc_o, mq_o), W.astype(np.float64))
+
+
+def test_kquant_codes_are_nearest_given_the_sub_block_parameters():
+    rng = np.random.default_rng(32)
+    w = (rng.standard_t(5, size=(12, 512)) * 0.02).astype(np.float32)
+    w[3] = np.abs(w[3])
+    w[4, :256] = 0.0
+    codes, d_bits, m_bits, sc, mq = ref.quantize_kquant(w)
+    S, M = ref.kquant_sub_params(d_bits, m_bits, sc, mq)
+    N, K = w.shape
+    grid = np.arange(16)[None, None, None, :] * S[:, :, None, None] - M[:, :, None, None]
+    w64 = w.astype(np.float64).reshape(N, K // 32, 32)
+    dist = np.abs(w64[..., None] - grid)
+    got = np.take_along_axis(dist, codes.reshape(N, K // 32, 32, 1).astype(np.int64), axis=-1)[..., 0]
+    assert np.all(got <= dist.min(-1) + 2.0 ** -20 * (np.abs(w64) + M[:, :, None]) + 1e-30)
+    # the all-zero super-block: smallest scales, zero codes, exact zeros
+    assert d_bits[0, 4] == 1 and m_bits[0, 4] == 1
+    assert np.all(codes[4, :256] == 0) and np.all(sc[0, :, 4] == 0) and np.all(mq[0, :, 4] == 0)
+    w_hat = ref.dequantize_kquant(codes, d_bits, m_bits, sc, mq)
+    assert np.all(w_hat[4, :256] == 0.0)
+    # one-signed positive row: no minimum
+    assert np.all(mq[:, :, 3] == 0)
+
+
+def test_kquant_record_layout_by_hand():
+    d_bits = np.array([[0x1234]], dtype=np.uint16)
+    m_bits = np.array([[0xABCD]], dtype=np.uint16)
+    sc = np.array([[[1], [2], [3], [4], [5], [6], [7], [63]]], dtype=np.uint8)
+    mq = np.array([[[63], [0], [0], [0], [0], [0], [0], [1]]], dtype=np.uint8)
+    rec = ref.pack_kquant_records(d_bits, m_bits, sc, mq)
+    scf = sum(v << (6 * j) for j, v in enumerate([1, 2, 3, 4, 5, 6, 7, 63]))
+    mqf = 63 | (1 << 42)
+    assert rec.shape == (1, 1, 4)
+    assert rec[0, 0].tolist() == [0xABCD1234, scf & 0xFFFFFFFF, (scf >> 32) | ((mqf & 0xFFFF) << 16), mqf >> 16]
+    assert rec[0, 0, 2] == 0x003FFC00 | (scf >> 32)   # mq_0 = 63 -> bits 16..21 of word 2
+
+
+def test_kquant_byte_accounting():
+    assert ref.format_bits_per_weight(256, "kq4") == 4.5
+    q, s, z = ref.packed_bytes(5120, 13824, 256, "kq4")
+    assert (q, s, z) == (5120 * 13824 // 2, 16 * 54 * 5120, 0)
+    assert (q + s + z) * 8 == 5120 * 13824 * 4.5
+    with pytest.raises(ValueError):
+        ref.quantize_kquant(np.zeros((8, 128), np.float32))
