@@ -21,7 +21,8 @@ GEMM's TFLOP/s against the dense bf16 MFMA peak. `grouped_step` times the same
 seven layers with q/k/v and gate/up each in one launch (w4a16_linear_group);
 `value` stays the seven-launch step. `formats` repeats the decode step and
 the prefill GEMM with the weights in the other formats (symmetric 4-bit,
-symmetric 8-bit = W8A16, group 256), each against its own bytes and flops.
+symmetric 8-bit = W8A16, group 256, K-quant-style super-blocks), each against
+its own bytes and flops.
 `quality` is the quantisation quality report of each matrix (w4a16_quant_error)
 and `awq_step` the decode step through the AWQ run-time path.
 `cpu_baseline` times the CPU
@@ -51,7 +52,7 @@ KERNEL_SOURCES = {
     "prefill": ["prefill.hip", "prefill_kernel.hpp", "decode_common.hpp", "w4a16_internal.hpp"],
 }
 # weight-format variants measured beside the headline (format, group)
-FORMAT_LEGS = [("sym4", 128), ("sym8", 128), ("asym4", 256)]
+FORMAT_LEGS = [("sym4", 128), ("sym8", 128), ("asym4", 256), ("kq4", 256)]
 
 
 def parse():
@@ -85,7 +86,8 @@ def algorithmic_bytes(M, N, K, group, fmt="asym4"):
     G = K // group
     codes = N * K if fmt == "sym8" else N * K // 2
     zeros = G * N // 2 if fmt == "asym4" else 0
-    return codes + 2 * G * N + zeros + 2 * M * K + 2 * M * N
+    meta = 16 * (K // 256) * N if fmt == "kq4" else 2 * G * N    # kq4: 16-byte super-block records
+    return codes + meta + zeros + 2 * M * K + 2 * M * N
 
 
 def kernel_kind(w4, M, N, K, group, dtype):

@@ -27,6 +27,15 @@
  * INT8 weights under 16-bit activations: "Weight-Only Quantisation",
  * definition). Group 256 is the super-block size of that table's K-quant row.
  *
+ * KQ4, K-quant-style super-blocks ("sub-block scales/minima inside
+ * 256-weight super-blocks", the K-quant row of that table), group = 256:
+ *   per 32-weight sub-block j:  lo, hi as above, s_j = (hi - lo)/15, mn_j = 0 - lo
+ *   per super-block:  d = fp16_rne(max_j s_j / 63), dmin = fp16_rne(max_j mn_j / 63)
+ *                     (0 -> 2^-24)
+ *   sc_j = clamp(rint(s_j/d), 0, 63), mq_j = clamp(rint(mn_j/dmin), 0, 63)
+ *   S_j = d*sc_j, M_j = dmin*mq_j, q = clamp(rint((w + M_j)/S_j), 0, 15) (0 if S_j = 0)
+ *   w_hat = S_j * q - M_j
+ *
  * Rounding to the nearest grid point of w / scale follows "Quantization Is Not
  * a Zip File" (zhuai.tech), section 3; the per-group scale ("block locality")
  * is in the same section; the (q - zero) * scale reconstruction is the
@@ -62,6 +71,11 @@
  *   SYM8     qweight N*K bytes: two 4-bit planes in the layout above, the low
  *            nibbles of every code in bytes [0, N*K/2), the high nibbles in
  *            [N*K/2, N*K); scales as above, no zeros.
+ *   KQ4      qweight as above; `scales` holds one 16-byte record per
+ *            (super-block u, row n) in [K/256][N] order: four little-endian
+ *            words {d | dmin << 16, sc bits 0-31, sc bits 32-47 | mq bits 0-15
+ *            << 16, mq bits 16-47}, sc and mq being 48-bit fields of eight
+ *            6-bit values (sub-block j at bits 6j..6j+5); no zeros. K % 256 == 0.
  *   x        fp16 or bf16 [M][K], row-major
  *   y        same type as x, [M][N], row-major; fp32 accumulation, rounded
  *            once to the output type (round to nearest even)
@@ -116,7 +130,9 @@ typedef enum {
 typedef enum {
     W4A16_FMT_ASYM4 = 0,   /* 4-bit codes, fp16 scale and 4-bit zero-point per group */
     W4A16_FMT_SYM4 = 1,    /* 4-bit codes q + 8, fp16 scale per group, no zero-points */
-    W4A16_FMT_SYM8 = 2     /* 8-bit codes q + 128 (two 4-bit planes), fp16 scale per group: W8A16 */
+    W4A16_FMT_SYM8 = 2,    /* 8-bit codes q + 128 (two 4-bit planes), fp16 scale per group: W8A16 */
+    W4A16_FMT_KQ4 = 3      /* 4-bit codes in 256-weight super-blocks of eight 32-weight sub-blocks with
+                              6-bit scales and minima (K-quant style, 4.5 bits/weight); group 256 */
 } w4a16_format;
 
 /* Human-readable name of a status code (static string, never NULL). */
@@ -141,9 +157,10 @@ w4a16_status w4a16_device_supported(int device);
 w4a16_status w4a16_packed_bytes(int64_t N, int64_t K, int32_t group,
                                 size_t *qweight_bytes, size_t *scales_bytes,
                                 size_t *zeros_bytes);
-/* Per format: qweight N*K/2 bytes (N*K for SYM8), scales as above, zeros 0
- * bytes for the symmetric formats. SYM4 stores 4 + 16/group bits per weight,
- * SYM8 8 + 16/group. */
+/* Per format: qweight N*K/2 bytes (N*K for SYM8), scales as above (KQ4:
+ * 16*(K/256)*N bytes of records), zeros 0 bytes for every format but ASYM4.
+ * SYM4 stores 4 + 16/group bits per weight, SYM8 8 + 16/group, KQ4 4.5. KQ4
+ * with a group other than 256 is W4A16_ERR_INVALID_ARG. */
 w4a16_status w4a16_packed_bytes_fmt(int64_t N, int64_t K, int32_t group, int32_t fmt,
                                     size_t *qweight_bytes, size_t *scales_bytes,
                                     size_t *zeros_bytes);
@@ -172,7 +189,9 @@ w4a16_status w4a16_unpack(const void *qweight, const void *scales, const void *z
                           uint8_t *codes, uint16_t *scales_out, uint8_t *zeros_out,
                           void *stream);
 /* Same in any format: codes are the stored unsigned codes (0..255 for SYM8);
- * zeros_out receives the fixed zero (8 or 128) of a symmetric format. */
+ * zeros_out receives the fixed zero (8 or 128) of a symmetric format. KQ4:
+ * codes only (its records are already in canonical order; scales_out and
+ * zeros_out are not written and may be NULL). */
 w4a16_status w4a16_unpack_fmt(const void *qweight, const void *scales, const void *zeros,
                               int64_t N, int64_t K, int32_t group, int32_t fmt,
                               uint8_t *codes, uint16_t *scales_out, uint8_t *zeros_out,
@@ -293,8 +312,8 @@ w4a16_status w4a16_quant_error(const float *w, const void *qweight, const void *
  * the one the same kernel gives for the pre-scaled activations. */
 w4a16_status w4a16_scale_activations(const void *x, int32_t dtype, const float *act_mul, void *x_out,
                                      int64_t M, int64_t K, void *stream);
-w4a16_status w4a16_awq_workspace_bytes(int64_t M, int64_t N, int64_t K, int32_t group, int32_t dtype,
-                                       size_t *bytes);
+w4a16_status w4a16_awq_workspace_bytes(int64_t M, int64_t N, int64_t K, int32_t group, int32_t fmt,
+                                       int32_t dtype, size_t *bytes);
 w4a16_status w4a16_linear_awq(const void *x, int32_t dtype, const float *act_mul, const void *qweight,
                               const void *scales, const void *zeros, void *y, int64_t M, int64_t N,
                               int64_t K, int32_t group, int32_t fmt, void *workspace,

@@ -14,6 +14,12 @@ def lib():
 
 
 def oracle_pack(w: np.ndarray, group: int, fmt: str = "asym4"):
+    if fmt == "kq4":
+        codes, d_bits, m_bits, sc, mq = ref.quantize_kquant(w)
+        return {"codes": codes, "fmt": fmt, "kq": (d_bits, m_bits, sc, mq),
+                "qweight": ref.pack_device(codes),
+                "records": ref.pack_kquant_records(d_bits, m_bits, sc, mq).ravel(),
+                "zeros_dev": None}
     codes, s_bits, zeros = ref.quantize_groupwise(w, group, fmt)
     return {
         "codes": codes,
@@ -66,7 +72,15 @@ def check_against_oracle(y_gpu, x_bits, dtype, o, group, cols=None):
     y = y_to_f64(y_gpu)
     if cols is not None:
         y = y[:, cols]
-    y_ref, a = ref.linear_ref_rows(x_bits, dtype, o["codes"], o["s_bits"], o["zeros"], group, cols)
+    if o.get("fmt") == "kq4":
+        d_bits, m_bits, sc, mq = o["kq"]
+        codes = o["codes"]
+        if cols is not None:
+            codes, d_bits, m_bits = codes[cols], d_bits[:, cols], m_bits[:, cols]
+            sc, mq = sc[:, :, cols], mq[:, :, cols]
+        y_ref, a = ref.linear_ref(x_bits, dtype, ref.dequantize_kquant(codes, d_bits, m_bits, sc, mq))
+    else:
+        y_ref, a = ref.linear_ref_rows(x_bits, dtype, o["codes"], o["s_bits"], o["zeros"], group, cols)
     r = ref.error_ratio(y, y_ref, a, dtype)
     worst = float(r.max()) if r.size else 0.0
     assert np.all(np.isfinite(y)), "non-finite output"

@@ -1,5 +1,6 @@
 """GPU parity of the weight-format variants: symmetric 4-bit (sym4), symmetric
-8-bit (sym8, W8A16) and group 256 (all three formats). The packed bytes,
+8-bit (sym8, W8A16), group 256 (all three formats) and the K-quant-style
+256-weight super-blocks (kq4). The packed bytes,
 scales and canonical view are bit-identical to the oracle's; every product is
 within 2e-3 * sum|x * w_hat| + 1e-5 (+ the output rounding) of the fp64
 oracle, on each kernel (GEMV, small-batch matrix-core, tiled matrix-core)."""
@@ -151,3 +152,110 @@ def test_format_full_size_decode_and_prefill(fmt):
     x = wl.activations(4, 0, 2048)
     H.check_against_oracle(_run("linear", x, "bf16", pw), x, "bf16", o, 128, cols=cols)
     H.drop((("fmt-full", 4), fmt))
+
+
+# ---------------------------------------------------------------------------
+# K-quant-style super-blocks (kq4, group 256)
+# ---------------------------------------------------------------------------
+
+KQ_SHAPES = [(72, 256), (264, 768), (1000, 1024), (520, 2048)]
+
+
+def _prep_kq(N, K):
+    return H.prepared(("kq", N, K), lambda: wl.random_weights(N * 5 + K, N, K), 256, "kq4")
+
+
+@pytest.mark.parametrize("N,K", KQ_SHAPES)
+def test_kq4_pack_bit_exact(N, K):
+    import torch
+    w, o, pw = _prep_kq(N, K)
+    torch.cuda.synchronize()
+    assert np.array_equal(pw.qweight.cpu().numpy(), o["qweight"]), "codes differ"
+    rec = pw.scales.cpu().view(torch.int32).numpy().view(np.uint32)
+    assert np.array_equal(rec, o["records"]), "super-block records differ"
+    codes, _, _ = H.lib().unpack(pw)
+    torch.cuda.synchronize()
+    assert np.array_equal(codes.cpu().numpy(), o["codes"])
+    assert H.lib().packed_bytes(N, K, 256, "kq4") == (N * K // 2, 16 * (K // 256) * N, 0)
+
+
+def test_kq4_pack_edges():
+    N, K = 24, 512
+    rng = np.random.default_rng(41)
+    w = (rng.standard_normal((N, K)) * 0.05).astype(np.float32)
+    w[0] = 0.0                                    # all-zero super-blocks
+    w[1] = np.abs(w[1])                           # no minimum
+    w[2] = -np.abs(w[2])                          # no positive part
+    w[3, :256] = 1e-12                            # scales underflow fp16
+    w[4, :32] = np.float32(2.0 ** 17)             # one large sub-block
+    w[5, :] = -0.0                                # negative zeros
+    o = H.oracle_pack(w, 256, "kq4")
+    pw = H.gpu_pack(w, 256, "kq4")
+    import torch
+    assert np.array_equal(pw.qweight.cpu().numpy(), o["qweight"])
+    assert np.array_equal(pw.scales.cpu().view(torch.int32).numpy().view(np.uint32), o["records"])
+
+
+@pytest.mark.parametrize("N,K", KQ_SHAPES)
+@pytest.mark.parametrize("dtype", ["f16", "bf16"])
+@pytest.mark.parametrize("kernel,M", [("gemv", 1), ("gemv", 5), ("gemm", 1), ("gemm", 17), ("gemm", 100),
+                                      ("gemm", 300), ("linear", 2)])
+def test_kq4_products_match_oracle(N, K, dtype, kernel, M):
+    w, o, pw = _prep_kq(N, K)
+    x = wl.random_activations(N + K + M + 7, M, K, dtype)
+    y = _run(kernel, x, dtype, pw)
+    H.check_against_oracle(y, x, dtype, o, 256)
+
+
+@pytest.mark.parametrize("dtype", ["f16", "bf16"])
+@pytest.mark.parametrize("M", [1, 4, 40, 300])
+def test_kq4_one_hot(dtype, M):
+    """One-hot rows select one rebuilt weight w_hat = S q - M: every kernel forms
+    it with one fp32 fma and rounds it once more to 16 bit, as the oracle's
+    output rounding does, so the result is bit-exact on all three kernels."""
+    import torch
+    N, K = 264, 768
+    w, o, pw = _prep_kq(N, K)
+    w_hat = ref.dequantize_kquant(o["codes"], *o["kq"])
+    ks = (np.arange(M) * 7919 + 11) % K
+    ks[0], ks[-1] = 0, K - 1
+    x32 = np.zeros((M, K), dtype=np.float32)
+    x32[np.arange(M), ks] = 1.0
+    want = ref.out_round_bits(w_hat[:, ks].T, dtype)
+    kernels = ["gemm", "linear"] + (["gemv"] if M <= 8 else [])
+    for kernel in kernels:
+        y = _run(kernel, wl.to_16bit(x32, dtype), dtype, pw)
+        got = y.cpu().view(torch.int16).numpy().view(np.uint16)
+        assert np.array_equal(got, want), kernel
+
+
+def test_kq4_quality_report():
+    import torch
+    N, K = 520, 2048
+    w, o, pw = _prep_kq(N, K)
+    got = H.lib().quant_error(torch.from_numpy(w).cuda(), pw)
+    w_hat = ref.dequantize_kquant(o["codes"], *o["kq"])
+    sums = ref.quant_error_sums(w, w_hat)
+    mse, snr, cos, mx = ref.quant_error_stats(sums, w_hat.size)
+    assert got["max_err"] == mx
+    assert abs(got["mse"] - mse) <= 1e-12 * mse and abs(got["snr_db"] - snr) <= 1e-9 and abs(got["cos"] - cos) <= 1e-12
+
+
+@pytest.mark.parametrize("M", [1, 16])
+def test_kq4_grouped_launch_matches_single(M):
+    import torch
+    K = 1024
+    pws, os_ = [], []
+    for N in (1000, 136):
+        w, o, pw = H.prepared(("kq-group", N, K), lambda N=N: wl.random_weights(900 + N, N, K), 256, "kq4")
+        pws.append(pw)
+        os_.append(o)
+    x = wl.random_activations(5 + M, M, K, "f16")
+    xd = H.to_device_bits(x, "f16")
+    ys = H.lib().linear_group([xd, xd], pws)
+    torch.cuda.synchronize()
+    for y, pw, o in zip(ys, pws, os_):
+        single = H.lib().gemm(xd, pw)
+        torch.cuda.synchronize()
+        assert torch.equal(y.view(torch.int16), single.view(torch.int16))
+        H.check_against_oracle(y, x, "f16", o, 256)

@@ -20,8 +20,9 @@ W4A16_OK = 0
 W4A16_F16 = 0
 W4A16_BF16 = 1
 # weight formats (w4a16_format): 4-bit codes + fp16 scale + 4-bit zero-point per
-# group; symmetric 4-bit codes; symmetric 8-bit codes (W8A16)
-FORMATS = {"asym4": 0, "sym4": 1, "sym8": 2}
+# group; symmetric 4-bit codes; symmetric 8-bit codes (W8A16); K-quant-style
+# 256-weight super-blocks (group 256)
+FORMATS = {"asym4": 0, "sym4": 1, "sym8": 2, "kq4": 3}
 
 if not os.path.exists(LIB_PATH):
     raise ImportError(
@@ -65,7 +66,7 @@ _SIGS = {
     "w4a16_quant_error_workspace_bytes": (ctypes.c_int, [_i64, _i64, _i32, _szp]),
     "w4a16_quant_error": (ctypes.c_int, [_vp, _vp, _vp, _vp, _i64, _i64, _i32, _i32, _vp, _vp, _sz, _vp]),
     "w4a16_scale_activations": (ctypes.c_int, [_vp, _i32, _vp, _vp, _i64, _i64, _vp]),
-    "w4a16_awq_workspace_bytes": (ctypes.c_int, [_i64, _i64, _i64, _i32, _i32, _szp]),
+    "w4a16_awq_workspace_bytes": (ctypes.c_int, [_i64, _i64, _i64, _i32, _i32, _i32, _szp]),
     "w4a16_linear_awq": (ctypes.c_int, [_vp, _i32, _vp, _vp, _vp, _vp, _vp, _i64, _i64, _i64, _i32, _i32, _vp, _sz,
                                         _vp]),
 }
@@ -155,7 +156,8 @@ class PackedWeight:
 
     def __init__(self, qweight, scales, zeros, N, K, group, fmt="asym4"):
         self.qweight = qweight    # uint8 [N*K/2] (sym8: [N*K], two planes), device layout
-        self.scales = scales      # float16, per 128-weight column: [T][N][128/group] (group 256: [G][N])
+        self.scales = scales      # float16, per 128-weight column: [T][N][128/group] (group 256: [G][N]);
+        #                           kq4: 16-byte super-block records [K/256][N] (viewed as float16)
         self.zeros = zeros        # int32 zero-point words (asym4), None for the symmetric formats
         self.N, self.K, self.group, self.fmt = N, K, group, fmt
 
@@ -191,6 +193,11 @@ def unpack(pw: PackedWeight, stream=None):
     G = K // group
     dev = pw.qweight.device
     codes = torch.empty((N, K), dtype=torch.uint8, device=dev)
+    if pw.fmt == "kq4":   # codes only: the super-block records are already canonical
+        _check("w4a16_unpack_fmt", _lib.w4a16_unpack_fmt(pw.qweight.data_ptr(), pw.scales.data_ptr(), None, N, K,
+                                                         group, _fmt_code(pw.fmt), codes.data_ptr(), None, None,
+                                                         _stream_ptr(stream)))
+        return codes, None, None
     s_out = torch.empty((G, N), dtype=torch.int16, device=dev)
     z_out = torch.empty((G, N), dtype=torch.uint8, device=dev)
     _check("w4a16_unpack_fmt", _lib.w4a16_unpack_fmt(pw.qweight.data_ptr(), pw.scales.data_ptr(), pw.zeros_ptr(),
@@ -340,8 +347,8 @@ def linear_awq(x: torch.Tensor, act_mul: torch.Tensor, pw: PackedWeight, out=Non
     M = x.shape[0]
     y = out if out is not None else torch.empty((M, pw.N), dtype=x.dtype, device=x.device)
     nb = _sz()
-    _check("w4a16_awq_workspace_bytes", _lib.w4a16_awq_workspace_bytes(M, pw.N, pw.K, pw.group, _dtype_code(x),
-                                                                       ctypes.byref(nb)))
+    _check("w4a16_awq_workspace_bytes", _lib.w4a16_awq_workspace_bytes(M, pw.N, pw.K, pw.group, _fmt_code(pw.fmt),
+                                                                       _dtype_code(x), ctypes.byref(nb)))
     ws = (workspace or _default_workspace(x.device)).get(nb.value)
     _check("w4a16_linear_awq", _lib.w4a16_linear_awq(
         x.data_ptr(), _dtype_code(x), act_mul.data_ptr(), pw.qweight.data_ptr(), pw.scales.data_ptr(),

@@ -47,13 +47,23 @@ bool shape_ok(int64_t N, int64_t K, int32_t group) {
     return true;
 }
 
-bool fmt_ok(int32_t fmt) { return fmt == W4A16_FMT_ASYM4 || fmt == W4A16_FMT_SYM4 || fmt == W4A16_FMT_SYM8; }
+bool fmt_ok(int32_t fmt) {
+    return fmt == W4A16_FMT_ASYM4 || fmt == W4A16_FMT_SYM4 || fmt == W4A16_FMT_SYM8 || fmt == W4A16_FMT_KQ4;
+}
+// K-quant super-blocks are 256 weights: that format takes group 256 only
+bool fmt_group_ok(int32_t fmt, int32_t group) { return fmt_ok(fmt) && (fmt != W4A16_FMT_KQ4 || group == 256); }
 
 // Byte sizes of the packed buffers: codes (one 4-bit plane, two for 8-bit
 // codes), then scales and zero-points per 128-weight column (128/group slots
 // per column; a short last column keeps its unused slots), or per group of
 // 256. The symmetric formats store no zero-points.
 void meta_bytes(int64_t N, int64_t K, int32_t group, int32_t fmt, size_t *q, size_t *sb, size_t *zb) {
+    if (fmt == W4A16_FMT_KQ4) {   // one 16-byte record per (super-block, row)
+        *q = (size_t)(N * K / 2);
+        *sb = (size_t)(16 * (K / 256) * N);
+        *zb = 0;
+        return;
+    }
     const int64_t slots = group == 256 ? K / 256 : (K / 32 + 3) / 4 * (128 / group);
     *q = (size_t)(N * K / 2) * (fmt == W4A16_FMT_SYM8 ? 2 : 1);
     *sb = (size_t)(2 * slots * N);
@@ -80,7 +90,7 @@ w4a16_status check_device() {
 w4a16_status check_linear(const void *x, int32_t dtype, const void *qweight, const void *scales,
                           const void *zeros, void *y, int64_t M, int64_t N, int64_t K, int32_t group,
                           int32_t fmt, void *workspace, size_t workspace_bytes, size_t need) {
-    if (!fmt_ok(fmt)) return W4A16_ERR_INVALID_ARG;
+    if (!fmt_group_ok(fmt, group)) return W4A16_ERR_INVALID_ARG;
     const bool zp = fmt == W4A16_FMT_ASYM4;
     if (!x || !qweight || !scales || (zp && !zeros) || !y) return W4A16_ERR_INVALID_ARG;
     if (dtype != W4A16_F16 && dtype != W4A16_BF16) return W4A16_ERR_INVALID_ARG;
@@ -119,19 +129,19 @@ size_t max_lds_per_block() {
 
 // The GEMV stages all activations of the call in LDS; it takes M <= 8 and
 // M * K small enough for one workgroup's LDS.
-bool gemv_fits(int64_t M, int64_t N, int64_t K, int32_t group, int32_t dtype) {
+bool gemv_fits(int64_t M, int64_t N, int64_t K, int32_t group, int32_t dtype, int32_t fmt) {
     if (M < 1 || M > 8) return false;
     const GemvPlan p = gemv_plan(M, N, K, group);
-    return gemv_lds_bytes(M, K, dtype == W4A16_BF16, p.waves, group) + kGemvStaticLds <= max_lds_per_block();
+    return gemv_lds_bytes(M, K, dtype == W4A16_BF16, p.waves, fmt) + kGemvStaticLds <= max_lds_per_block();
 }
 
 // w4a16_linear's choice for M <= gemv_max_m(): the dot-product GEMV for
 // matrices of fewer than 768 row blocks of 16 (its workgroups then hide their
 // latency better), the matrix-core kernel (four row blocks per workgroup) for
 // wider ones; both measured on the decode shapes.
-bool prefer_gemv(int64_t M, int64_t N, int64_t K, int32_t group, int32_t dtype) {
+bool prefer_gemv(int64_t M, int64_t N, int64_t K, int32_t group, int32_t dtype, int32_t fmt) {
     return M >= 1 && M <= gemv_max_m() && ceil_div(N, kRowBlock) < 768 && shape_ok(N, K, group) &&
-           (dtype == W4A16_F16 || dtype == W4A16_BF16) && gemv_fits(M, N, K, group, dtype);
+           (dtype == W4A16_F16 || dtype == W4A16_BF16) && gemv_fits(M, N, K, group, dtype, fmt);
 }
 
 size_t gemm_need(int64_t M, int64_t N, int64_t K, int32_t group) {
@@ -162,7 +172,7 @@ int32_t w4a16_linear_kernel(int64_t M, int64_t N, int64_t K, int32_t group, int3
     // the same choice for every weight format
     if (M < 1 || M > (1LL << 24) || !shape_ok(N, K, group) || (dtype != W4A16_F16 && dtype != W4A16_BF16))
         return -1;
-    if (prefer_gemv(M, N, K, group, dtype)) return 0;
+    if (prefer_gemv(M, N, K, group, dtype, W4A16_FMT_ASYM4)) return 0;
     return gemm_plan(M, N, K, group).kind == 0 ? 1 : 2;
 }
 
@@ -187,7 +197,7 @@ w4a16_status w4a16_packed_bytes(int64_t N, int64_t K, int32_t group, size_t *qwe
 
 w4a16_status w4a16_packed_bytes_fmt(int64_t N, int64_t K, int32_t group, int32_t fmt, size_t *qweight_bytes,
                                     size_t *scales_bytes, size_t *zeros_bytes) {
-    if (!shape_ok(N, K, group) || !fmt_ok(fmt)) return W4A16_ERR_INVALID_ARG;
+    if (!shape_ok(N, K, group) || !fmt_group_ok(fmt, group)) return W4A16_ERR_INVALID_ARG;
     size_t q, sb, zb;
     meta_bytes(N, K, group, fmt, &q, &sb, &zb);
     if (qweight_bytes) *qweight_bytes = q;
@@ -209,7 +219,7 @@ w4a16_status w4a16_pack(const float *w, int64_t N, int64_t K, int32_t group, voi
 
 w4a16_status w4a16_pack_fmt(const float *w, int64_t N, int64_t K, int32_t group, int32_t fmt, void *qweight,
                             void *scales, void *zeros, void *stream) {
-    if (!fmt_ok(fmt)) return W4A16_ERR_INVALID_ARG;
+    if (!fmt_group_ok(fmt, group)) return W4A16_ERR_INVALID_ARG;
     const bool zp = fmt == W4A16_FMT_ASYM4;
     if (!w || !qweight || !scales || (zp && !zeros) || !shape_ok(N, K, group)) return W4A16_ERR_INVALID_ARG;
     if (!aligned16(w) || !aligned16(qweight) || !aligned16(scales) || (zp && !aligned16(zeros)))
@@ -232,9 +242,10 @@ w4a16_status w4a16_unpack(const void *qweight, const void *scales, const void *z
 w4a16_status w4a16_unpack_fmt(const void *qweight, const void *scales, const void *zeros, int64_t N,
                               int64_t K, int32_t group, int32_t fmt, uint8_t *codes, uint16_t *scales_out,
                               uint8_t *zeros_out, void *stream) {
-    if (!fmt_ok(fmt)) return W4A16_ERR_INVALID_ARG;
+    if (!fmt_group_ok(fmt, group)) return W4A16_ERR_INVALID_ARG;
     const bool zp = fmt == W4A16_FMT_ASYM4;
-    if (!qweight || !scales || (zp && !zeros) || !codes || !scales_out || !zeros_out ||
+    const bool meta = fmt != W4A16_FMT_KQ4;   // kq4: codes only (its records are already canonical)
+    if (!qweight || (meta && !scales) || (zp && !zeros) || !codes || (meta && (!scales_out || !zeros_out)) ||
         !shape_ok(N, K, group))
         return W4A16_ERR_INVALID_ARG;
     if (!aligned16(qweight) || !aligned16(codes)) return W4A16_ERR_INVALID_ARG;
@@ -255,7 +266,7 @@ w4a16_status w4a16_gemv_fmt(const void *x, int32_t dtype, const void *qweight, c
     if (st != W4A16_OK) return st;
     st = check_device();
     if (st != W4A16_OK) return st;
-    if (!gemv_fits(M, N, K, group, dtype)) return W4A16_ERR_INVALID_ARG;
+    if (!gemv_fits(M, N, K, group, dtype, fmt)) return W4A16_ERR_INVALID_ARG;
     GemvPlan plan = gemv_plan(M, N, K, group);
     hipError_t e = launch_gemv(x, dtype == W4A16_BF16, qweight, scales, zeros, y, (int)M, (int)N,
                                (int)K, group, fmt, nullptr, plan, reinterpret_cast<hipStream_t>(stream));
@@ -358,7 +369,7 @@ w4a16_status w4a16_linear_group(int32_t count, const void *const *x, int32_t dty
 w4a16_status w4a16_linear_fmt(const void *x, int32_t dtype, const void *qweight, const void *scales,
                               const void *zeros, void *y, int64_t M, int64_t N, int64_t K, int32_t group,
                               int32_t fmt, void *workspace, size_t workspace_bytes, void *stream) {
-    if (prefer_gemv(M, N, K, group, dtype))
+    if (prefer_gemv(M, N, K, group, dtype, fmt))
         return w4a16_gemv_fmt(x, dtype, qweight, scales, zeros, y, M, N, K, group, fmt, workspace,
                               workspace_bytes, stream);
     return w4a16_gemm_fmt(x, dtype, qweight, scales, zeros, y, M, N, K, group, fmt, workspace,
@@ -381,7 +392,7 @@ w4a16_status w4a16_quant_error_workspace_bytes(int64_t N, int64_t K, int32_t gro
 w4a16_status w4a16_quant_error(const float *w, const void *qweight, const void *scales, const void *zeros,
                                int64_t N, int64_t K, int32_t group, int32_t fmt, double *out, void *workspace,
                                size_t workspace_bytes, void *stream) {
-    if (!fmt_ok(fmt) || !shape_ok(N, K, group)) return W4A16_ERR_INVALID_ARG;
+    if (!fmt_group_ok(fmt, group) || !shape_ok(N, K, group)) return W4A16_ERR_INVALID_ARG;
     const bool zp = fmt == W4A16_FMT_ASYM4;
     if (!w || !qweight || !scales || (zp && !zeros) || !out) return W4A16_ERR_INVALID_ARG;
     if (!aligned16(w) || !aligned16(qweight) || !aligned16(out)) return W4A16_ERR_INVALID_ARG;
@@ -419,11 +430,12 @@ w4a16_status w4a16_scale_activations(const void *x, int32_t dtype, const float *
     return e == hipSuccess ? W4A16_OK : W4A16_ERR_HIP;
 }
 
-w4a16_status w4a16_awq_workspace_bytes(int64_t M, int64_t N, int64_t K, int32_t group, int32_t dtype,
+w4a16_status w4a16_awq_workspace_bytes(int64_t M, int64_t N, int64_t K, int32_t group, int32_t fmt, int32_t dtype,
                                        size_t *bytes) {
-    if (!bytes || M < 1 || M > (1LL << 24) || !shape_ok(N, K, group) || (dtype != W4A16_F16 && dtype != W4A16_BF16))
+    if (!bytes || M < 1 || M > (1LL << 24) || !shape_ok(N, K, group) || !fmt_group_ok(fmt, group) ||
+        (dtype != W4A16_F16 && dtype != W4A16_BF16))
         return W4A16_ERR_INVALID_ARG;
-    *bytes = gemv_fits(M, N, K, group, dtype) ? 0 : align_up((size_t)(M * K * 2), 256);
+    *bytes = gemv_fits(M, N, K, group, dtype, fmt) ? 0 : align_up((size_t)(M * K * 2), 256);
     return W4A16_OK;
 }
 
@@ -434,7 +446,7 @@ w4a16_status w4a16_linear_awq(const void *x, int32_t dtype, const float *act_mul
     w4a16_status st = check_linear(x, dtype, qweight, scales, zeros, y, M, N, K, group, fmt, nullptr, 0, 0);
     if (st != W4A16_OK) return st;
     if (overlap(range_of(y, (size_t)(M * N * 2)), range_of(act_mul, (size_t)K * 4))) return W4A16_ERR_INVALID_ARG;
-    const bool fused = gemv_fits(M, N, K, group, dtype);
+    const bool fused = gemv_fits(M, N, K, group, dtype, fmt);
     const size_t need = fused ? 0 : align_up((size_t)(M * K * 2), 256);
     if (need > 0) {
         if (!workspace || workspace_bytes < need) return W4A16_ERR_WORKSPACE;

@@ -44,11 +44,31 @@ __device__ inline UnpackConsts unpack_consts() {
 // zero-point per group, kSym4 and kSym8 have the fixed zero 8 / 128 and no
 // zero-point loads; kSym8 codes are two 4-bit planes (low nibbles, then high
 // nibbles), each in the packed layout of the 4-bit formats.
+// kKq4 (K-quant-style super-blocks) has no zero-point either: the codes are
+// used as they are (zero 0) and each 32-weight chunk takes its own scale S and
+// minimum M from the super-block record (kq_params).
 template <int FMT> struct FormatTraits {
     static constexpr bool has_zeros = FMT == kAsym4;
     static constexpr bool two_planes = FMT == kSym8;
-    static constexpr uint32_t fixed_zero = FMT == kSym8 ? 128u : 8u;
+    static constexpr bool kquant = FMT == kKq4;
+    static constexpr uint32_t fixed_zero = FMT == kSym8 ? 128u : (FMT == kKq4 ? 0u : 8u);
 };
+
+// Sub-block jj (0..7) of a super-block record {d | dmin << 16, 48-bit field
+// of eight 6-bit scales, 48-bit field of eight 6-bit minima}: S = d * sc_jj,
+// M = dmin * mq_jj (fp32 products of an fp16 value and a 6-bit integer: exact).
+struct KqParams {
+    float S, M;
+};
+__device__ inline KqParams kq_params(const uint4 &rec, int jj) {
+    const float d = (float)__builtin_bit_cast(_Float16, (uint16_t)(rec.x & 0xFFFFu));
+    const float dm = (float)__builtin_bit_cast(_Float16, (uint16_t)(rec.x >> 16));
+    const uint64_t scf = (uint64_t)rec.y | ((uint64_t)(rec.z & 0xFFFFu) << 32);
+    const uint64_t mqf = (uint64_t)(rec.z >> 16) | ((uint64_t)rec.w << 16);
+    const uint32_t sc = (uint32_t)(scf >> (6 * jj)) & 63u;
+    const uint32_t mq = (uint32_t)(mqf >> (6 * jj)) & 63u;
+    return KqParams{d * (float)sc, dm * (float)mq};
+}
 
 // One dword (8 codes of one k-slice, even k in the low half-word) -> four
 // fp16 pairs (k0,k1) (k2,k3) (k4,k5) (k6,k7) holding q - z exactly.

@@ -50,6 +50,7 @@ hipError_t launch_gemm(const void *x, bool bf16, const void *qweight, const void
     switch (fmt) {
         case kSym4: return launch_skinny_fmt<kSym4>(x, bf16, qweight, scales, zeros, y, M, N, K, group, plan, stream);
         case kSym8: return launch_skinny_fmt<kSym8>(x, bf16, qweight, scales, zeros, y, M, N, K, group, plan, stream);
+        case kKq4: return launch_skinny_fmt<kKq4>(x, bf16, qweight, scales, zeros, y, M, N, K, group, plan, stream);
         default: return launch_skinny_fmt<kAsym4>(x, bf16, qweight, scales, zeros, y, M, N, K, group, plan, stream);
     }
 }
@@ -59,6 +60,7 @@ hipError_t launch_gemm_group(const GroupTable &tab, bool bf16, int M, int K, int
     switch (fmt) {
         case kSym4: return launch_skinny_group_fmt<kSym4>(tab, bf16, M, K, group, plan, stream);
         case kSym8: return launch_skinny_group_fmt<kSym8>(tab, bf16, M, K, group, plan, stream);
+        case kKq4: return launch_skinny_group_fmt<kKq4>(tab, bf16, M, K, group, plan, stream);
         default: return launch_skinny_group_fmt<kAsym4>(tab, bf16, M, K, group, plan, stream);
     }
 }

@@ -84,6 +84,7 @@ __device__ __forceinline__ void skinny_body(const uint16_t *__restrict__ x, cons
     const uint4 *qw_b[R], *qwh_b[R];
     uint32_t lane_rec[R], col_rec[R];
     const ColScales<GPC> *sc_row[R];
+    const uint4 *kq_row[R];   // kq4: super-block records [K/256][N]
     const uint32_t *zp_row[R];
     int zshift[R];
 #pragma unroll
@@ -97,6 +98,7 @@ __device__ __forceinline__ void skinny_body(const uint16_t *__restrict__ x, cons
         col_rec[i] = (uint32_t)(kColChunks * rows);
         const int n = b * kRowBlock + rl;
         sc_row[i] = reinterpret_cast<const ColScales<GPC> *>(scales) + n;
+        kq_row[i] = reinterpret_cast<const uint4 *>(scales) + n;
         zp_row[i] = zeros + (n * GPC) / 8;
         zshift[i] = 4 * ((n * GPC) % 8);
     }
@@ -104,22 +106,29 @@ __device__ __forceinline__ void skinny_body(const uint16_t *__restrict__ x, cons
     // the 16-row tile past M produce outputs that are never stored)
     const uint4 *xrow = reinterpret_cast<const uint4 *>(x) + (size_t)min(r, M_loc - 1) * (K / 8) + s;
     const UnpackConsts uc = unpack_consts();
-    const uint4 ones = make_uint4(0x3F803F80u, 0x3F803F80u, 0x3F803F80u, 0x3F803F80u);   // bf16 1.0
+    constexpr uint32_t one2 = BF ? 0x3F803F80u : 0x3C003C00u;   // (1.0, 1.0) in the activation type
+    const uint4 ones = make_uint4(one2, one2, one2, one2);
 
     struct Buf {
         uint4 xa[kColChunks];
-        uint4 rec[R], rec_hi[R];
+        uint4 rec[R], rec_hi[R], kq[R];
         ColScales<GPC> sc[R];
         uint32_t zw[R];
+        int par;   // column parity: which half of the super-block (kq4)
     };
     // metadata slot of column t: t >> mshift (group 256: one slot per two columns)
     auto load_meta = [&](int t, Buf &u) {
         const int tm = t >> mshift;
+        u.par = t & 1;
 #pragma unroll
         for (int i = 0; i < R; ++i) {
-            u.sc[i] = sc_row[i][(size_t)tm * N];
-            if constexpr (FT::has_zeros) u.zw[i] = zp_row[i][(size_t)tm * (N * GPC / 8)];
-            else u.zw[i] = 0;
+            if constexpr (FT::kquant) {
+                u.kq[i] = kq_row[i][(size_t)(t >> 1) * N];
+            } else {
+                u.sc[i] = sc_row[i][(size_t)tm * N];
+                if constexpr (FT::has_zeros) u.zw[i] = zp_row[i][(size_t)tm * (N * GPC / 8)];
+                else u.zw[i] = 0;
+            }
         }
     };
     auto load_col = [&](int t, Buf &u) {
@@ -154,6 +163,7 @@ __device__ __forceinline__ void skinny_body(const uint16_t *__restrict__ x, cons
         } else {
             unpack_f16_fmt<FMT>(d, dh, z, uc, w);
             g = mfma16x16x32<BF>(xa, make_uint4(w[0], w[1], w[2], w[3]), g);
+            if constexpr (FT::kquant) sx = mfma16x16x32<BF>(xa, ones, sx);   // sum x for the minimum
         }
     };
     auto zero_of = [&](uint32_t zw, int i, int e) -> uint32_t {
@@ -171,7 +181,30 @@ __device__ __forceinline__ void skinny_body(const uint16_t *__restrict__ x, cons
         g = f4_t{0.0f, 0.0f, 0.0f, 0.0f};
         sx = f4_t{0.0f, 0.0f, 0.0f, 0.0f};
     };
+    // kq4: chunk j is a 32-weight sub-block: acc += S * sum x q - M * sum x
+    auto close_kq = [&](int i, const KqParams &P, f4_t &g, f4_t &sx) {
+#pragma unroll
+        for (int v = 0; v < 4; ++v) {
+            const float gq = BF ? fmaf(-128.0f, sx[v], g[v]) : g[v];   // bf16 operands carry 128 + q
+            acc[i][v] = fmaf(P.S, gq, fmaf(-P.M, sx[v], acc[i][v]));
+        }
+        g = f4_t{0.0f, 0.0f, 0.0f, 0.0f};
+        sx = f4_t{0.0f, 0.0f, 0.0f, 0.0f};
+    };
     auto compute_col = [&](const Buf &u) {
+        if constexpr (FT::kquant) {
+#pragma unroll
+            for (int i = 0; i < R; ++i) {
+                const uint32_t dk[4] = {u.rec[i].x, u.rec[i].y, u.rec[i].z, u.rec[i].w};
+                f4_t g = {0.0f, 0.0f, 0.0f, 0.0f}, sx = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+                for (int j = 0; j < kColChunks; ++j) {
+                    chunk(u.xa[j], dk[j], 0u, 0u, g, sx);
+                    close_kq(i, kq_params(u.kq[i], (u.par << 2) + j), g, sx);
+                }
+            }
+            return;
+        }
 #pragma unroll
         for (int i = 0; i < R; ++i) {
             const uint32_t dws[4] = {u.rec[i].x, u.rec[i].y, u.rec[i].z, u.rec[i].w};
@@ -207,7 +240,7 @@ __device__ __forceinline__ void skinny_body(const uint16_t *__restrict__ x, cons
 
     // the partial last column of K (K % 128 != 0): nc < 4 chunks, each lane's
     // nc dwords are consecutive
-    if (sl.t_end > sl.t_full) {
+    if (!FT::kquant && sl.t_end > sl.t_full) {   // (kq4: K % 256 == 0, every column is full)
         const int tl = sl.t_end - 1;
         const int nc = sl.C - tl * kColChunks;
         Buf u;
@@ -320,6 +353,10 @@ hipError_t launch_skinny_fmt(const void *x, bool bf16, const void *qweight, cons
     const void *qh = FormatTraits<FMT>::two_planes
                          ? static_cast<const void *>(static_cast<const char *>(qweight) + (size_t)N * K / 2)
                          : qweight;
+    if constexpr (FormatTraits<FMT>::kquant) {   // one 32-weight sub-block per chunk
+        return bf16 ? launch_skinny<32, true, FMT>(x, qweight, qh, scales, zeros, y, M, N, K, 0, plan, stream)
+                    : launch_skinny<32, false, FMT>(x, qweight, qh, scales, zeros, y, M, N, K, 0, plan, stream);
+    } else {
     if (bf16) {
         switch (group) {
             case 32: return launch_skinny<32, true, FMT>(x, qweight, qh, scales, zeros, y, M, N, K, ms, plan, stream);
@@ -331,13 +368,17 @@ hipError_t launch_skinny_fmt(const void *x, bool bf16, const void *qweight, cons
         case 32: return launch_skinny<32, false, FMT>(x, qweight, qh, scales, zeros, y, M, N, K, ms, plan, stream);
         case 64: return launch_skinny<64, false, FMT>(x, qweight, qh, scales, zeros, y, M, N, K, ms, plan, stream);
         default: return launch_skinny<128, false, FMT>(x, qweight, qh, scales, zeros, y, M, N, K, ms, plan, stream);
-    }
+    }    }
 }
 
 template <int FMT>
 hipError_t launch_skinny_group_fmt(const GroupTable &tab, bool bf16, int M, int K, int group, const GemmPlan &plan,
                                    hipStream_t stream) {
     const int ms = group == 256 ? 1 : 0;
+    if constexpr (FormatTraits<FMT>::kquant) {
+        return bf16 ? launch_skinny_group<32, true, FMT>(tab, M, K, 0, plan, stream)
+                    : launch_skinny_group<32, false, FMT>(tab, M, K, 0, plan, stream);
+    } else {
     if (bf16) {
         switch (group) {
             case 32: return launch_skinny_group<32, true, FMT>(tab, M, K, ms, plan, stream);
@@ -349,7 +390,7 @@ hipError_t launch_skinny_group_fmt(const GroupTable &tab, bool bf16, int M, int 
         case 32: return launch_skinny_group<32, false, FMT>(tab, M, K, ms, plan, stream);
         case 64: return launch_skinny_group<64, false, FMT>(tab, M, K, ms, plan, stream);
         default: return launch_skinny_group<128, false, FMT>(tab, M, K, ms, plan, stream);
-    }
+    }    }
 }
 
 }  // namespace w4a16

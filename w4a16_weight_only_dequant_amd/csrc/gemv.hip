@@ -11,8 +11,8 @@ int gemv_xcols(int64_t K, int waves) {
     return (int)ceil_div(T, waves);
 }
 
-size_t gemv_lds_bytes(int64_t M, int64_t K, bool bf16, int waves, int group) {
-    return wave_lds_bytes((int)M, gemv_xcols(K, waves), bf16, group) * waves;
+size_t gemv_lds_bytes(int64_t M, int64_t K, bool bf16, int waves, int fmt) {
+    return wave_lds_bytes((int)M, gemv_xcols(K, waves), bf16 || fmt == kKq4) * waves;
 }
 
 GemvPlan gemv_plan(int64_t M, int64_t N, int64_t K, int32_t group) {
@@ -45,6 +45,7 @@ hipError_t launch_gemv(const void *x, bool bf16, const void *qweight, const void
     switch (fmt) {
         case kSym4: return launch_gemv_fmt<kSym4>(x, bf16, qweight, scales, zeros, y, M, N, K, group, am, plan, stream);
         case kSym8: return launch_gemv_fmt<kSym8>(x, bf16, qweight, scales, zeros, y, M, N, K, group, am, plan, stream);
+        case kKq4: return launch_gemv_fmt<kKq4>(x, bf16, qweight, scales, zeros, y, M, N, K, group, am, plan, stream);
         default: return launch_gemv_fmt<kAsym4>(x, bf16, qweight, scales, zeros, y, M, N, K, group, am, plan, stream);
     }
 }

@@ -77,11 +77,11 @@ __device__ inline uint4 scale8(const uint4 &v, const float4 &a, const float4 &b)
     return make_uint4(out[0], out[1], out[2], out[3]);
 }
 
-// LDS bytes of one wave: activations [MT][xcols*128] (16-bit) and, for bf16,
-// their sums over every 8 consecutive k ([MT][xcols*16] fp32).
-__host__ __device__ inline size_t wave_lds_bytes(int MT, int xcols, bool bf16, int group) {
-    (void)group;
-    return (size_t)MT * xcols * 256 + (bf16 ? (size_t)MT * xcols * 64 : 0);
+// LDS bytes of one wave: activations [MT][xcols*128] (16-bit) and, when
+// `sums` (bf16 activations, or super-block minima), their sums over every 8
+// consecutive k ([MT][xcols*16] fp32).
+__host__ __device__ inline size_t wave_lds_bytes(int MT, int xcols, bool sums) {
+    return (size_t)MT * xcols * 256 + (sums ? (size_t)MT * xcols * 64 : 0);
 }
 
 // act_mul: NULL, or fp32 multipliers [K] applied to the activations as they
@@ -94,7 +94,8 @@ __global__ __launch_bounds__(64 * kMaxWaves) __attribute__((amdgpu_waves_per_eu(
     using FT = FormatTraits<FMT>;
     constexpr int CPG = GROUP / kChunk;   // chunks per group (1, 2, 4)
     constexpr int PF0 = MT == 1 ? kPrefetch : (MT == 2 ? 4 : (MT <= 4 ? 3 : 2));
-    constexpr int PF = FormatTraits<FMT>::two_planes ? (PF0 + 1) / 2 : PF0;   // 8-bit: same bytes in flight
+    // 8-bit: the same bytes in flight; kq4: room for the super-block record
+    constexpr int PF = FormatTraits<FMT>::two_planes ? (PF0 + 1) / 2 : (FormatTraits<FMT>::kquant ? PF0 - 1 : PF0);
     extern __shared__ __align__(16) unsigned char smem[];
     __shared__ float red[kMaxWaves][MT][kRowBlock];
 
@@ -113,7 +114,8 @@ __global__ __launch_bounds__(64 * kMaxWaves) __attribute__((amdgpu_waves_per_eu(
     const int nchunks = sl.c_hi - sl.c_lo;
 
     // this wave's LDS region
-    unsigned char *wbase = smem + (size_t)wave * wave_lds_bytes(MT, xcols, BF, GROUP);
+    constexpr bool kSums = BF || FT::kquant;   // sums of every 8 activations are staged
+    unsigned char *wbase = smem + (size_t)wave * wave_lds_bytes(MT, xcols, kSums);
     uint4 *xw = reinterpret_cast<uint4 *>(wbase);                                        // [MT][xcols*16]
     float *xsw = reinterpret_cast<float *>(wbase + (size_t)MT * xcols * 256);           // [MT][xcols*16]
 
@@ -131,16 +133,22 @@ __global__ __launch_bounds__(64 * kMaxWaves) __attribute__((amdgpu_waves_per_eu(
     const uint32_t *zp_row = zeros + (n * GPC) / 8;
     const int zshift = 4 * ((n * GPC) % 8);
 
+    // super-block records (kq4): one per 256 weights of row n, [K/256][N]
+    const uint4 *kq_row = reinterpret_cast<const uint4 *>(scales) + n;
     struct Buf {
-        uint4 rec, rec_hi;
+        uint4 rec, rec_hi, kq;
         ColScales<GPC> sc;
         uint32_t zw;
     };
     auto load_meta = [&](int t, Buf &u) {
-        const int tm = t >> mshift;
-        u.sc = sc_row[(size_t)tm * N];
-        if constexpr (FT::has_zeros) u.zw = zp_row[(size_t)tm * (N * GPC / 8)];
-        else u.zw = 0;
+        if constexpr (FT::kquant) {
+            u.kq = kq_row[(size_t)(t >> 1) * N];
+        } else {
+            const int tm = t >> mshift;
+            u.sc = sc_row[(size_t)tm * N];
+            if constexpr (FT::has_zeros) u.zw = zp_row[(size_t)tm * (N * GPC / 8)];
+            else u.zw = 0;
+        }
     };
     auto load_col = [&](int t, Buf &u) {
         u.rec = qw_b[(uint32_t)t * col_rec + lane_rec];
@@ -201,16 +209,17 @@ __global__ __launch_bounds__(64 * kMaxWaves) __attribute__((amdgpu_waves_per_eu(
                 slot = scale8<BF>(slot, mv[2 * k8], mv[2 * k8 + 1]);
             }
         }
-        if constexpr (BF) {
+        if constexpr (kSums) {
             // sum of every 8 activations (one k-slice of one chunk)
+            constexpr uint32_t one2 = BF ? 0x3F803F80u : 0x3C003C00u;   // (1.0, 1.0)
             for (int i = lane; i < MT * nchunks * 4; i += 64) {
                 const int m = i / (nchunks * 4), q = i - m * (nchunks * 4);
                 const uint4 v = xw[(size_t)m * xcols * 16 + q];
                 float sum = 0.0f;
-                sum = dot_pair<true>(v.x, 0x3F803F80u, sum);
-                sum = dot_pair<true>(v.y, 0x3F803F80u, sum);
-                sum = dot_pair<true>(v.z, 0x3F803F80u, sum);
-                sum = dot_pair<true>(v.w, 0x3F803F80u, sum);
+                sum = dot_pair<BF>(v.x, one2, sum);
+                sum = dot_pair<BF>(v.y, one2, sum);
+                sum = dot_pair<BF>(v.z, one2, sum);
+                sum = dot_pair<BF>(v.w, one2, sum);
                 xsw[(size_t)m * xcols * 16 + q] = sum;
             }
         }
@@ -258,7 +267,34 @@ __global__ __launch_bounds__(64 * kMaxWaves) __attribute__((amdgpu_waves_per_eu(
             p[m] = 0.0f;
         }
     };
+    // kq4: chunk c is one 32-weight sub-block with its own scale S and
+    // minimum M; its contribution is S * sum x q - M * sum x, added to acc
+    auto dword_kq = [&](int c, uint32_t d, const KqParams &P) {
+        uint32_t w[4];
+        if constexpr (BF)
+            unpack_bf16_magic(d, uc, w);
+        else
+            unpack_f16(d, 0u, uc, w);
+        const int q = (c - sl.c_lo) * 4 + s;
+#pragma unroll
+        for (int m = 0; m < MT; ++m) {
+            const uint4 xv = xw[(size_t)m * xcols * 16 + q];
+            const float xs = xsw[(size_t)m * xcols * 16 + q];
+            float t = dot_pair<BF>(w[0], xv.x, 0.0f);
+            t = dot_pair<BF>(w[1], xv.y, t);
+            t = dot_pair<BF>(w[2], xv.z, t);
+            t = dot_pair<BF>(w[3], xv.w, t);
+            if constexpr (BF) t = fmaf(-128.0f, xs, t);   // the magic operands carry 128 + q
+            acc[m] = fmaf(P.S, t, fmaf(-P.M, xs, acc[m]));
+        }
+    };
     auto compute_col = [&](int t, const Buf &u) {
+        if constexpr (FT::kquant) {
+            const uint32_t dk[4] = {u.rec.x, u.rec.y, u.rec.z, u.rec.w};
+#pragma unroll
+            for (int j = 0; j < kColChunks; ++j) dword_kq(t * kColChunks + j, dk[j], kq_params(u.kq, ((t & 1) << 2) + j));
+            return;
+        }
         const uint32_t dws[4] = {u.rec.x, u.rec.y, u.rec.z, u.rec.w};
         const uint32_t dwh[4] = {u.rec_hi.x, u.rec_hi.y, u.rec_hi.z, u.rec_hi.w};
         float p[MT];
@@ -291,7 +327,7 @@ __global__ __launch_bounds__(64 * kMaxWaves) __attribute__((amdgpu_waves_per_eu(
 
     // 3. the partial last column of K (K % 128 != 0): nc < 4 chunks, each
     // lane's nc dwords are consecutive; its metadata has the usual layout
-    if (sl.t_end > sl.t_full) {
+    if (!FT::kquant && sl.t_end > sl.t_full) {   // (kq4: K % 256 == 0, every column is full)
         const int tl = sl.t_end - 1;
         const int nc = sl.C - tl * kColChunks;
         const size_t off = (size_t)tl * rows * 16 + (size_t)s * rows * nc + (size_t)rl * nc;
@@ -338,7 +374,7 @@ template <int GROUP, bool BF, int MT, int FMT>
 hipError_t launch_one(const void *x, const void *qw, const void *qw_hi, const void *sc, const void *zp, void *y,
                       int N, int K, int mshift, const float *am, const GemvPlan &plan, hipStream_t stream) {
     const int xcols = gemv_xcols(K, plan.waves);
-    const size_t lds = wave_lds_bytes(MT, xcols, BF, GROUP) * plan.waves;
+    const size_t lds = wave_lds_bytes(MT, xcols, BF || FormatTraits<FMT>::kquant) * plan.waves;
     auto kern = gemv_kernel<GROUP, MT, BF, FMT>;
     if (lds > 48 * 1024) {
         hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(kern),
@@ -380,6 +416,10 @@ hipError_t launch_gemv_fmt(const void *x, bool bf16, const void *qweight, const 
     const void *qh = FormatTraits<FMT>::two_planes
                          ? static_cast<const void *>(static_cast<const char *>(qweight) + (size_t)N * K / 2)
                          : qweight;
+    if constexpr (FormatTraits<FMT>::kquant) {   // one 32-weight sub-block per chunk
+        return bf16 ? launch_m<32, true, FMT>(M, x, qweight, qh, scales, zeros, y, N, K, 0, am, plan, stream)
+                    : launch_m<32, false, FMT>(M, x, qweight, qh, scales, zeros, y, N, K, 0, am, plan, stream);
+    } else {
     if (bf16) {
         switch (group) {
             case 32: return launch_m<32, true, FMT>(M, x, qweight, qh, scales, zeros, y, N, K, ms, am, plan, stream);
@@ -391,7 +431,7 @@ hipError_t launch_gemv_fmt(const void *x, bool bf16, const void *qweight, const 
         case 32: return launch_m<32, false, FMT>(M, x, qweight, qh, scales, zeros, y, N, K, ms, am, plan, stream);
         case 64: return launch_m<64, false, FMT>(M, x, qweight, qh, scales, zeros, y, N, K, ms, am, plan, stream);
         default: return launch_m<128, false, FMT>(M, x, qweight, qh, scales, zeros, y, N, K, ms, am, plan, stream);
-    }
+    }    }
 }
 
 }  // namespace w4a16

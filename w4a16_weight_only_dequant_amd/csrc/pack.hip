@@ -108,6 +108,69 @@ __global__ __launch_bounds__(256) void pack_kernel(const float *__restrict__ w, 
     }
 }
 
+// K-quant-style super-blocks: one thread per (row n, 256-weight super-block
+// u). Per 32-weight sub-block j: the range [min(0, min w), max(0, max w)]
+// gives s_j = (hi - lo) / 15 and the minimum mn_j = 0 - lo; d and dmin are
+// the largest s_j and mn_j over 63, rounded once to fp16 (0 -> 2^-24); the
+// 6-bit sc_j, mq_j are rint(s_j / d) and rint(mn_j / dmin), clamped; codes
+// are rint((w + M_j) / S_j), clamped to 0..15, with S_j = d sc_j and
+// M_j = dmin mq_j (0 where S_j = 0). Writes the codes and the 16-byte record
+// {d | dmin << 16, 48-bit sc field, 48-bit mq field} at [u][n].
+__global__ __launch_bounds__(256) void pack_kq_kernel(const float *__restrict__ w, int N, int K,
+                                                      uint32_t *__restrict__ qweight, uint4 *__restrict__ rec) {
+    constexpr int SUB = 8;   // sub-blocks per super-block
+    const int U = K / 256;
+    const int64_t tid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;   // (u, n), n fastest
+    if (tid >= (int64_t)U * N) return;
+    const int n = (int)(tid % N), u = (int)(tid / N);
+    const float4 *src = reinterpret_cast<const float4 *>(w + (int64_t)n * K + (int64_t)u * 256);
+    float s[SUB], mn[SUB];
+    float smax = 0.0f, mmax = 0.0f;
+    for (int j = 0; j < SUB; ++j) {
+        float lo = 0.0f, hi = 0.0f;
+        for (int i = 0; i < 8; ++i) {
+            const float4 v = src[j * 8 + i];
+            lo = fminf(fminf(fminf(lo, v.x), fminf(v.y, v.z)), v.w);
+            hi = fmaxf(fmaxf(fmaxf(hi, v.x), fmaxf(v.y, v.z)), v.w);
+        }
+        s[j] = (hi - lo) / 15.0f;
+        mn[j] = 0.0f - lo;
+        smax = fmaxf(smax, s[j]);
+        mmax = fmaxf(mmax, mn[j]);
+    }
+    uint16_t dbits = f32_to_f16_bits(smax / 63.0f), mbits = f32_to_f16_bits(mmax / 63.0f);
+    if (dbits == 0) dbits = 1;
+    if (mbits == 0) mbits = 1;
+    const float d = (float)__builtin_bit_cast(_Float16, dbits), dm = (float)__builtin_bit_cast(_Float16, mbits);
+    uint64_t scf = 0, mqf = 0;
+    for (int j = 0; j < SUB; ++j) {
+        int sc = (int)rintf(s[j] / d), mq = (int)rintf(mn[j] / dm);
+        sc = sc < 0 ? 0 : (sc > 63 ? 63 : sc);
+        mq = mq < 0 ? 0 : (mq > 63 ? 63 : mq);
+        scf |= (uint64_t)sc << (6 * j);
+        mqf |= (uint64_t)mq << (6 * j);
+        const float S = d * (float)sc, M = dm * (float)mq;
+        for (int dd = 0; dd < 4; ++dd) {
+            const float4 a = src[j * 8 + dd * 2], b = src[j * 8 + dd * 2 + 1];
+            const float v[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
+            uint32_t word = 0;
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+                int q = 0;
+                if (S > 0.0f) {
+                    q = (int)rintf((v[i] + M) / S);
+                    q = q < 0 ? 0 : (q > 15 ? 15 : q);
+                }
+                word |= (uint32_t)q << (4 * ((i >> 1) + 4 * (i & 1)));   // even k low half, odd k high half
+            }
+            qweight[dword_offset(n, u * 8 + j, dd, N, K)] = word;
+        }
+    }
+    rec[(int64_t)u * N + n] = make_uint4((uint32_t)dbits | ((uint32_t)mbits << 16), (uint32_t)scf,
+                                         (uint32_t)(scf >> 32) | ((uint32_t)(mqf & 0xFFFFu) << 16),
+                                         (uint32_t)(mqf >> 16));
+}
+
 __global__ __launch_bounds__(256) void unpack_codes_kernel(const uint32_t *__restrict__ qweight,
                                                            int N, int K, int planes,
                                                            uint8_t *__restrict__ codes) {
@@ -177,6 +240,12 @@ hipError_t launch_pack(const float *w, int N, int K, int group, int fmt, void *q
     auto *q = reinterpret_cast<uint32_t *>(qweight);
     auto *s = reinterpret_cast<uint16_t *>(scales);
     auto *z = reinterpret_cast<uint32_t *>(zeros);
+    if (fmt == kKq4) {
+        const int64_t total = (int64_t)(K / 256) * N;
+        hipLaunchKernelGGL(pack_kq_kernel, dim3((unsigned)ceil_div(total, 256)), dim3(256), 0, stream, w, N, K, q,
+                           reinterpret_cast<uint4 *>(scales));
+        return hipGetLastError();
+    }
     switch (fmt) {
         case kSym4: return launch_pack_fmt<kSym4>(w, N, K, group, q, s, z, stream);
         case kSym8: return launch_pack_fmt<kSym8>(w, N, K, group, q, s, z, stream);
@@ -191,7 +260,7 @@ hipError_t launch_unpack(const void *qweight, const void *scales, const void *ze
     hipLaunchKernelGGL(unpack_codes_kernel, dim3((unsigned)ceil_div(nd, 256)), dim3(256), 0, stream,
                        reinterpret_cast<const uint32_t *>(qweight), N, K, fmt == kSym8 ? 2 : 1, codes);
     hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
+    if (e != hipSuccess || fmt == kKq4) return e;   // kq4: its records are already in canonical order
     const int G = K / group;
     const int fz = fmt == kSym8 ? 128 : (fmt == kSym4 ? 8 : 0);
     const dim3 grid((unsigned)ceil_div((int64_t)G * N, 256));

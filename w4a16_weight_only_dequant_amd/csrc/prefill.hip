@@ -39,6 +39,7 @@ hipError_t launch_prefill(const void *x, bool bf16, const void *qweight, const v
     switch (fmt) {
         case kSym4: return launch_prefill_fmt<kSym4>(x, bf16, qweight, scales, zeros, y, M, N, K, group, plan, stream);
         case kSym8: return launch_prefill_fmt<kSym8>(x, bf16, qweight, scales, zeros, y, M, N, K, group, plan, stream);
+        case kKq4: return launch_prefill_fmt<kKq4>(x, bf16, qweight, scales, zeros, y, M, N, K, group, plan, stream);
         default: return launch_prefill_fmt<kAsym4>(x, bf16, qweight, scales, zeros, y, M, N, K, group, plan, stream);
     }
 }

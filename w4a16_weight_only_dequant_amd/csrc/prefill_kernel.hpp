@@ -104,6 +104,25 @@ __device__ inline uint4 dequant_bf16_s8(uint32_t d, uint32_t dh, float s, const 
     return make_uint4(o[0], o[1], o[2], o[3]);
 }
 
+// kq4 sub-block (scale S, minimum M): the exact codes q as fp16 pairs, then
+// w_hat = S q - M by one fp32 fma (rounded once) and one rounding to 16 bit.
+template <bool BF>
+__device__ inline uint4 dequant_kq(uint32_t d, const KqParams &P, const UnpackConsts &uc) {
+    uint32_t t[4];
+    unpack_f16(d, 0u, uc, t);
+    uint32_t o[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const half2_t h = __builtin_bit_cast(half2_t, t[i]);
+        const float2_t v = {fmaf(P.S, (float)h.x, -P.M), fmaf(P.S, (float)h.y, -P.M)};
+        if constexpr (BF)
+            o[i] = __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf162_t));
+        else
+            o[i] = __builtin_bit_cast(uint32_t, __builtin_convertvector(v, half2_t));
+    }
+    return make_uint4(o[0], o[1], o[2], o[3]);
+}
+
 // Same for fp16: exact (code - z) pairs, then one fp16 multiply by s.
 template <int FMT>
 __device__ inline uint4 dequant_f16(uint32_t d, uint32_t dh, uint32_t z, _Float16 sh, const UnpackConsts &uc) {
@@ -181,10 +200,14 @@ __global__ __launch_bounds__(64 * WM * WN) __attribute__((amdgpu_waves_per_eu(WM
     const int t_full = C / kColChunks;   // columns with all four chunks
     struct WCol {
         uint4 rec[WREC], rec_hi[WREC];   // rec_hi: high-nibble plane of 8-bit codes
+        uint4 kq[WREC];                  // kq4: the super-block record of the column's row
         ColScales<GPC> sc[WREC];
         uint32_t zw[WREC];
+        int par;                         // kq4: column parity (half of the super-block)
     };
+    const uint4 *kqrec = reinterpret_cast<const uint4 *>(scales);
     auto load_wcol = [&](int t, WCol &u) __attribute__((always_inline)) {
+        u.par = t & 1;
 #pragma unroll
         for (int i = 0; i < WREC; ++i) {
             if (t < t_full) {
@@ -209,9 +232,13 @@ __global__ __launch_bounds__(64 * WM * WN) __attribute__((amdgpu_waves_per_eu(WM
             }
             // metadata slot of column t: t >> mshift (group 256: one slot per two columns)
             const uint32_t tm = (uint32_t)(t >> mshift);
-            u.sc[i] = scol[soff[i] + tm * (uint32_t)N];
-            if constexpr (FT::has_zeros) u.zw[i] = zeros[zoff[i] + tm * zstep];
-            else u.zw[i] = 0;
+            if constexpr (FT::kquant) {
+                u.kq[i] = kqrec[soff[i] + (uint32_t)(t >> 1) * (uint32_t)N];
+            } else {
+                u.sc[i] = scol[soff[i] + tm * (uint32_t)N];
+                if constexpr (FT::has_zeros) u.zw[i] = zeros[zoff[i] + tm * zstep];
+                else u.zw[i] = 0;
+            }
         }
     };
     // dequantise half h (chunks 2h, 2h+1) of weight record i into LDS;
@@ -225,8 +252,13 @@ __global__ __launch_bounds__(64 * WM * WN) __attribute__((amdgpu_waves_per_eu(WM
             const int e = (2 * h + jj) / CPG;
             uint32_t z = FT::fixed_zero;
             if constexpr (FT::has_zeros) z = (u.zw[i] >> (zshift[i] + 4 * e)) & 0xFu;
-            const float s = u.sc[i].get(e);
             uint4 v;
+            if constexpr (FT::kquant) {
+                v = dequant_kq<BF>(dw, kq_params(u.kq[i], (u.par << 2) + 2 * h + jj), uc);
+                wbuf[swz(wrow[i], 4 * jj + d)] = v;
+                continue;
+            }
+            const float s = u.sc[i].get(e);
             if constexpr (BF && FT::two_planes)
                 v = dequant_bf16_s8(dw, dh, s, uc);
             else if constexpr (BF)
@@ -414,6 +446,10 @@ hipError_t launch_prefill_fmt(const void *x, bool bf16, const void *qweight, con
                          ? static_cast<const void *>(static_cast<const char *>(qweight) + (size_t)N * K / 2)
                          : qweight;
     const int t = plan.tile;
+    if constexpr (FormatTraits<FMT>::kquant) {   // one 32-weight sub-block per chunk
+        return bf16 ? launch_group<32, true, FMT>(t, x, qweight, qh, scales, zeros, y, M, N, K, 0, stream)
+                    : launch_group<32, false, FMT>(t, x, qweight, qh, scales, zeros, y, M, N, K, 0, stream);
+    } else {
     if (bf16) {
         switch (group) {
             case 32: return launch_group<32, true, FMT>(t, x, qweight, qh, scales, zeros, y, M, N, K, ms, stream);
@@ -425,7 +461,7 @@ hipError_t launch_prefill_fmt(const void *x, bool bf16, const void *qweight, con
         case 32: return launch_group<32, false, FMT>(t, x, qweight, qh, scales, zeros, y, M, N, K, ms, stream);
         case 64: return launch_group<64, false, FMT>(t, x, qweight, qh, scales, zeros, y, M, N, K, ms, stream);
         default: return launch_group<128, false, FMT>(t, x, qweight, qh, scales, zeros, y, M, N, K, ms, stream);
-    }
+    }    }
 }
 
 }  // namespace w4a16

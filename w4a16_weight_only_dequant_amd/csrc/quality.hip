@@ -63,7 +63,7 @@ __global__ __launch_bounds__(kQeThreads) void quant_error_partial_kernel(
     const int gpc = kColumn / kgroup;                         // slots per column
     const int mshift = group > kColumn ? 1 : 0;               // group 256: one slot per two columns
     const int64_t plane = (int64_t)N * K / 8;                 // dwords of one 4-bit plane
-    const uint32_t fixed_zero = fmt == kSym8 ? 128u : 8u;
+    const uint32_t fixed_zero = fmt == kSym8 ? 128u : (fmt == kKq4 ? 0u : 8u);
     Sums5 v{0.0, 0.0, 0.0, 0.0, 0.0};
     for (int i = threadIdx.x; i < rows * KD; i += kQeThreads) {
         const int r = i / KD, kd = i % KD;
@@ -72,12 +72,21 @@ __global__ __launch_bounds__(kQeThreads) void quant_error_partial_kernel(
         const int64_t off = dword_offset(n, kd / 4, kd % 4, N, K);
         const uint32_t lo = qw[off];
         const uint32_t hi = fmt == kSym8 ? qw[plane + off] : 0u;
-        const int t = (k0 / kColumn) >> mshift;
-        const int e = (k0 % kColumn) / kgroup;
-        const int64_t slot = ((int64_t)t * N + n) * gpc + e;
-        const double s = (double)(float)__builtin_bit_cast(_Float16, scales[slot]);
+        double s, mn = 0.0;
         uint32_t z = fixed_zero;
-        if (fmt == kAsym4) z = (zeros[slot / 8] >> (4 * (slot % 8))) & 0xFu;
+        if (fmt == kKq4) {   // sub-block (k0 % 256) / 32 of the record [k0 / 256][n]
+            const uint4 rec = reinterpret_cast<const uint4 *>(scales)[(int64_t)(k0 / 256) * N + n];
+            const KqParams P = kq_params(rec, (k0 % 256) / kChunk);
+            s = (double)P.S;
+            mn = (double)P.M;
+            z = 0;
+        } else {
+            const int t = (k0 / kColumn) >> mshift;
+            const int e = (k0 % kColumn) / kgroup;
+            const int64_t slot = ((int64_t)t * N + n) * gpc + e;
+            s = (double)(float)__builtin_bit_cast(_Float16, scales[slot]);
+            if (fmt == kAsym4) z = (zeros[slot / 8] >> (4 * (slot % 8))) & 0xFu;
+        }
         const float4 wa = *reinterpret_cast<const float4 *>(w + (int64_t)n * K + k0);
         const float4 wb = *reinterpret_cast<const float4 *>(w + (int64_t)n * K + k0 + 4);
         const float wv[8] = {wa.x, wa.y, wa.z, wa.w, wb.x, wb.y, wb.z, wb.w};
@@ -85,7 +94,7 @@ __global__ __launch_bounds__(kQeThreads) void quant_error_partial_kernel(
         for (int j = 0; j < 8; ++j) {
             const int p = 4 * ((j >> 1) + 4 * (j & 1));   // even k in the low half-word
             const uint32_t q = ((lo >> p) & 0xFu) | (((hi >> p) & 0xFu) << 4);
-            const double h = s * (double)((int)q - (int)z);
+            const double h = s * (double)((int)q - (int)z) - mn;
             const double x = (double)wv[j];
             const double d = x - h;
             v.d2 = fma(d, d, v.d2);

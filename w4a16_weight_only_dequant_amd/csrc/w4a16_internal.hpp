@@ -34,7 +34,7 @@ __host__ __device__ inline int64_t dword_offset(int n, int c, int d, int N, int 
 }
 
 // Weight formats (the values of w4a16_format in the public header).
-enum { kAsym4 = 0, kSym4 = 1, kSym8 = 2 };
+enum { kAsym4 = 0, kSym4 = 1, kSym8 = 2, kKq4 = 3 };
 
 typedef _Float16 half2_t __attribute__((ext_vector_type(2)));
 typedef __bf16 bf162_t __attribute__((ext_vector_type(2)));
@@ -51,7 +51,7 @@ struct GemvPlan {
 
 GemvPlan gemv_plan(int64_t M, int64_t N, int64_t K, int32_t group);
 // Dynamic LDS of one GEMV workgroup (per-wave activations, bf16 sums, metadata).
-size_t gemv_lds_bytes(int64_t M, int64_t K, bool bf16, int waves, int group);
+size_t gemv_lds_bytes(int64_t M, int64_t K, bool bf16, int waves, int fmt);
 int gemv_xcols(int64_t K, int waves);
 // Most waves of one GEMV workgroup (they split K); the launch bound, and so
 // the register budget of a wave, follows from it.
@@ -89,7 +89,8 @@ struct GroupTable {
     int count;
 };
 // Launchers. `group` is 32, 64, 128 or 256; `fmt` one of kAsym4, kSym4,
-// kSym8 (zeros is not read by the symmetric formats).
+// kSym8, kKq4 (zeros is read by kAsym4 only; kKq4 takes group 256 and its
+// 16-byte super-block records in `scales`).
 hipError_t launch_gemm_group(const GroupTable &tab, bool bf16, int M, int K, int group, int fmt,
                              const GemmPlan &plan, hipStream_t stream);
 
@@ -139,6 +140,7 @@ hipError_t launch_skinny_group_fmt(const GroupTable &tab, bool bf16, int M, int 
 W4A16_EXTERN_FMT(kAsym4)
 W4A16_EXTERN_FMT(kSym4)
 W4A16_EXTERN_FMT(kSym8)
+W4A16_EXTERN_FMT(kKq4)
 #undef W4A16_EXTERN_FMT
 
 __device__ inline uint16_t f32_to_f16_bits(float v) {
