@@ -14,6 +14,15 @@ namespace w4a16 {
 
 constexpr int kColumn = kChunk * kColChunks;   // 128 weights of K per column
 
+// A 16-byte load marked non-temporal: the packed weights of the small-M
+// kernels are read once per call, so they need not displace the activations
+// and metadata in the caches (measured 2-4% faster on the decode shapes).
+typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
+__device__ inline uint4 nt_load(const uint4 *p) {
+    const u32x4_t v = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t *>(p));
+    return make_uint4(v.x, v.y, v.z, v.w);
+}
+
 typedef float float2_t __attribute__((ext_vector_type(2)));
 
 // A 32-bit constant materialised in a VGPR. VOP3 instructions (v_and_or_b32)

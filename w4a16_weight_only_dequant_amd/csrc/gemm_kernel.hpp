@@ -134,8 +134,8 @@ __device__ __forceinline__ void skinny_body(const uint16_t *__restrict__ x, cons
     auto load_col = [&](int t, Buf &u) {
 #pragma unroll
         for (int i = 0; i < R; ++i) {
-            u.rec[i] = qw_b[i][(uint32_t)t * col_rec[i] + lane_rec[i]];
-            if constexpr (FT::two_planes) u.rec_hi[i] = qwh_b[i][(uint32_t)t * col_rec[i] + lane_rec[i]];
+            u.rec[i] = nt_load(&qw_b[i][(uint32_t)t * col_rec[i] + lane_rec[i]]);
+            if constexpr (FT::two_planes) u.rec_hi[i] = nt_load(&qwh_b[i][(uint32_t)t * col_rec[i] + lane_rec[i]]);
         }
 #pragma unroll
         for (int j = 0; j < kColChunks; ++j) u.xa[j] = xrow[(size_t)(t * kColChunks + j) * 4];

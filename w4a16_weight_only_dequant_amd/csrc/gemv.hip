@@ -23,7 +23,7 @@ GemvPlan gemv_plan(int64_t M, int64_t N, int64_t K, int32_t group) {
         return v ? atoi(v) : 0;
     }();
     GemvPlan p{};
-    p.row_blocks = (int)ceil_div(N, kRowBlock);
+    p.row_blocks = (int)ceil_div(N, kGemvRowsPerWg);
     const int64_t columns = ceil_div(K / kChunk, kColChunks);
     // four waves per workgroup measured best for the decode shapes, also for
     // K = 28672 (56 columns per wave); more only for still longer K, never

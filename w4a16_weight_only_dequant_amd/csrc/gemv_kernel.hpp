@@ -35,6 +35,14 @@ namespace w4a16 {
 namespace {
 
 constexpr int kMaxWaves = kGemvMaxWaves;
+// Rows of one workgroup: 16 (a block of the layout; a wave load is one column
+// of it) or 8 (half a block; a wave load covers two columns of those rows).
+// Eight-row workgroups double the workgroup count, which a plain streaming
+// read rewards (35 MB: 12.9 us with 320 workgroups, 7.7 us with 640), but
+// here they split every 256-byte segment of a column between two workgroups
+// and measured 3% faster at 5120 x 5120 and 4-25% slower on the other decode
+// shapes, so 16 is the default.
+constexpr int kRowsPerWg = kGemvRowsPerWg;
 #ifndef W4A16_GEMV_PREFETCH
 #define W4A16_GEMV_PREFETCH 6
 #endif
@@ -97,17 +105,22 @@ __global__ __launch_bounds__(64 * kMaxWaves) __attribute__((amdgpu_waves_per_eu(
     // 8-bit: the same bytes in flight; kq4: room for the super-block record
     constexpr int PF = FormatTraits<FMT>::two_planes ? (PF0 + 1) / 2 : (FormatTraits<FMT>::kquant ? PF0 - 1 : PF0);
     extern __shared__ __align__(16) unsigned char smem[];
-    __shared__ float red[kMaxWaves][MT][kRowBlock];
+    constexpr int RW = kRowsPerWg;          // rows of this workgroup
+    constexpr int CPW = kRowBlock / RW;     // columns covered by one wave load (1 or 2)
+    __shared__ float red[kMaxWaves][MT][RW];
 
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int waves = blockDim.x >> 6;
-    const int r = lane & 15;          // row within the block
-    const int s = lane >> 4;          // dword position: k-slice [8s, 8s+8) of each chunk
-    const int b = blockIdx.x;
-    const int n0 = b * kRowBlock;
-    const int rows = min(kRowBlock, N - n0);
+    const int r = lane % RW;               // row within the workgroup's rows
+    const int s = (lane / RW) & 3;         // dword position: k-slice [8s, 8s+8) of each chunk
+    const int cw = lane / (4 * RW);        // which column of the wave load (0 when CPW = 1)
+    const int n0 = blockIdx.x * RW;        // first row of the workgroup
+    const int b = n0 / kRowBlock;          // its 16-row block of the layout
+    const int rows_b = min(kRowBlock, N - b * kRowBlock);
+    const int rows = min(RW, N - n0);
     const int rl = r < rows ? r : r - rows;   // lanes past a short last block re-read a valid row
+    const int rib = n0 % kRowBlock + rl;       // row within the 16-row block
 
     constexpr int GPC = kColumn / GROUP;   // groups per column (4, 2, 1)
     const Slice sl = wave_slice<GROUP>(K, wave, waves);
@@ -119,11 +132,11 @@ __global__ __launch_bounds__(64 * kMaxWaves) __attribute__((amdgpu_waves_per_eu(
     uint4 *xw = reinterpret_cast<uint4 *>(wbase);                                        // [MT][xcols*16]
     float *xsw = reinterpret_cast<float *>(wbase + (size_t)MT * xcols * 256);           // [MT][xcols*16]
 
-    // weights: block base, full column t at t*4*rows uint4, lane at s*rows + rl
+    // weights: block base, full column t at t*4*rows_b uint4, lane at s*rows_b + rib
     const uint4 *qw_b = qw + (size_t)b * (K / 2);
     const uint4 *qwh_b = qw_hi + (size_t)b * (K / 2);   // 8-bit codes: the high-nibble plane
-    const uint32_t lane_rec = (uint32_t)(s * rows + rl);
-    const uint32_t col_rec = (uint32_t)(kColChunks * rows);
+    const uint32_t lane_rec = (uint32_t)(s * rows_b + rib);
+    const uint32_t col_rec = (uint32_t)(kColChunks * rows_b);
     const UnpackConsts uc = unpack_consts();
     // per-column metadata of row n: GPC scales at (t*N + n)*GPC, GPC zero
     // nibbles starting at nibble (t*N + n)*GPC of the zero words, where t is
@@ -139,6 +152,8 @@ __global__ __launch_bounds__(64 * kMaxWaves) __attribute__((amdgpu_waves_per_eu(
         uint4 rec, rec_hi, kq;
         ColScales<GPC> sc;
         uint32_t zw;
+        int t;       // the lane's column
+        float on;    // 1, or 0 for a lane past the slice's last full column (CPW = 2)
     };
     auto load_meta = [&](int t, Buf &u) {
         if constexpr (FT::kquant) {
@@ -150,9 +165,16 @@ __global__ __launch_bounds__(64 * kMaxWaves) __attribute__((amdgpu_waves_per_eu(
             else u.zw = 0;
         }
     };
-    auto load_col = [&](int t, Buf &u) {
-        u.rec = qw_b[(uint32_t)t * col_rec + lane_rec];
-        if constexpr (FT::two_planes) u.rec_hi = qwh_b[(uint32_t)t * col_rec + lane_rec];
+    // iteration p of the wave covers columns t_begin + CPW p + cw of its slice
+    const int iters = (sl.t_full - sl.t_begin + CPW - 1) / CPW;
+    auto load_col = [&](int p, Buf &u) {
+        const int tc = sl.t_begin + CPW * p + cw;
+        const bool in = CPW == 1 || tc < sl.t_full;
+        const int t = in ? tc : sl.t_full - 1;   // a lane past the last full column re-reads one (weight 0)
+        u.t = t;
+        u.on = in ? 1.0f : 0.0f;
+        u.rec = nt_load(&qw_b[(uint32_t)t * col_rec + lane_rec]);
+        if constexpr (FT::two_planes) u.rec_hi = nt_load(&qwh_b[(uint32_t)t * col_rec + lane_rec]);
         load_meta(t, u);
         // keep the prefetch where it is: the scheduler may not sink these
         // loads towards their use (which would serialise the stream)
@@ -190,7 +212,7 @@ __global__ __launch_bounds__(64 * kMaxWaves) __attribute__((amdgpu_waves_per_eu(
             if (base == 0) {
 #pragma unroll
                 for (int i = 0; i < PF; ++i)
-                    if (sl.t_begin + i < sl.t_full) load_col(sl.t_begin + i, ring[i]);
+                    if (i < iters) load_col(i, ring[i]);
             }
             xdst(base + 0 * 64 + lane, v0); xdst(base + 1 * 64 + lane, v1);
             xdst(base + 2 * 64 + lane, v2); xdst(base + 3 * 64 + lane, v3);
@@ -288,11 +310,17 @@ __global__ __launch_bounds__(64 * kMaxWaves) __attribute__((amdgpu_waves_per_eu(
             acc[m] = fmaf(P.S, t, fmaf(-P.M, xs, acc[m]));
         }
     };
-    auto compute_col = [&](int t, const Buf &u) {
+    auto compute_col = [&](const Buf &u) {
+        const int t = u.t;
         if constexpr (FT::kquant) {
             const uint32_t dk[4] = {u.rec.x, u.rec.y, u.rec.z, u.rec.w};
 #pragma unroll
-            for (int j = 0; j < kColChunks; ++j) dword_kq(t * kColChunks + j, dk[j], kq_params(u.kq, ((t & 1) << 2) + j));
+            for (int j = 0; j < kColChunks; ++j) {
+                KqParams P = kq_params(u.kq, ((t & 1) << 2) + j);
+                P.S *= u.on;
+                P.M *= u.on;
+                dword_kq(t * kColChunks + j, dk[j], P);
+            }
             return;
         }
         const uint32_t dws[4] = {u.rec.x, u.rec.y, u.rec.z, u.rec.w};
@@ -305,7 +333,7 @@ __global__ __launch_bounds__(64 * kMaxWaves) __attribute__((amdgpu_waves_per_eu(
             const int e = j / CPG;
             const uint32_t z = zero_of(u.zw, e);
             dword_dot(t * kColChunks + j, dws[j], dwh[j], z, p);
-            if ((j + 1) % CPG == 0) close_group(u.sc.get(e), p);
+            if ((j + 1) % CPG == 0) close_group(u.sc.get(e) * u.on, p);
         }
     };
 
@@ -313,24 +341,24 @@ __global__ __launch_bounds__(64 * kMaxWaves) __attribute__((amdgpu_waves_per_eu(
     // flight. The ring is indexed by compile-time positions (the loop is
     // unrolled by the ring size), so no register with a load in flight is
     // ever copied, and the loop body has no lane-dependent branch.
-    int t = sl.t_begin;
-    for (; t + PF + 1 <= sl.t_full; t += PF + 1) {
+    int it = 0;
+    for (; it + PF + 1 <= iters; it += PF + 1) {
 #pragma unroll
         for (int i = 0; i <= PF; ++i) {
-            load_col(min(t + i + PF, sl.t_full - 1), ring[(i + PF) % (PF + 1)]);
-            compute_col(t + i, ring[i]);
+            load_col(min(it + i + PF, iters - 1), ring[(i + PF) % (PF + 1)]);
+            compute_col(ring[i]);
         }
     }
 #pragma unroll
     for (int i = 0; i <= PF; ++i)
-        if (t + i < sl.t_full) compute_col(t + i, ring[i]);
+        if (it + i < iters) compute_col(ring[i]);
 
     // 3. the partial last column of K (K % 128 != 0): nc < 4 chunks, each
     // lane's nc dwords are consecutive; its metadata has the usual layout
-    if (!FT::kquant && sl.t_end > sl.t_full) {   // (kq4: K % 256 == 0, every column is full)
+    if (!FT::kquant && sl.t_end > sl.t_full && cw == 0) {   // (kq4: K % 256 == 0, every column is full)
         const int tl = sl.t_end - 1;
         const int nc = sl.C - tl * kColChunks;
-        const size_t off = (size_t)tl * rows * 16 + (size_t)s * rows * nc + (size_t)rl * nc;
+        const size_t off = (size_t)tl * rows_b * 16 + (size_t)s * rows_b * nc + (size_t)rib * nc;
         const uint32_t *col = reinterpret_cast<const uint32_t *>(qw_b) + off;
         const uint32_t *colh = reinterpret_cast<const uint32_t *>(qwh_b) + off;
         Buf u;
@@ -346,22 +374,23 @@ __global__ __launch_bounds__(64 * kMaxWaves) __attribute__((amdgpu_waves_per_eu(
         }
     }
 
-    // 4. reduce: the four k-slice lanes of a row, then the waves (fixed order)
+    // 4. reduce: the lanes of a row (its four k-slices and, when CPW = 2, its
+    // two columns), then the waves (fixed order)
 #pragma unroll
     for (int m = 0; m < MT; ++m) {
         float v = acc[m];
-        v += __shfl_xor(v, 16, 64);
-        v += __shfl_xor(v, 32, 64);
+#pragma unroll
+        for (int off = RW; off < 64; off <<= 1) v += __shfl_xor(v, off, 64);
         acc[m] = v;
     }
-    if (s == 0) {
+    if (lane < RW) {
 #pragma unroll
         for (int m = 0; m < MT; ++m) red[wave][m][r] = acc[m];
     }
     __syncthreads();
-    for (int i = threadIdx.x; i < MT * kRowBlock; i += blockDim.x) {
-        const int m = i / kRowBlock;
-        const int rr = i % kRowBlock;
+    for (int i = threadIdx.x; i < MT * RW; i += blockDim.x) {
+        const int m = i / RW;
+        const int rr = i % RW;
         if (rr < rows) {
             float v = red[0][m][rr];
             for (int w = 1; w < waves; ++w) v += red[w][m][rr];

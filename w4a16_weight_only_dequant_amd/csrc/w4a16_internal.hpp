@@ -42,10 +42,10 @@ typedef __bf16 bf162_t __attribute__((ext_vector_type(2)));
 __host__ __device__ inline int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 __host__ __device__ inline size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
 
-// Host-side plan for one GEMV launch: one workgroup per 16 output rows, each
-// with `waves` waves that split K (no cross-workgroup reduction).
+// Host-side plan for one GEMV launch: one workgroup per kGemvRowsPerWg output
+// rows, each with `waves` waves that split K (no cross-workgroup reduction).
 struct GemvPlan {
-    int row_blocks;   // workgroups = ceil(N / 16)
+    int row_blocks;   // workgroups = ceil(N / kGemvRowsPerWg)
     int waves;        // waves per workgroup (1..16)
 };
 
@@ -56,11 +56,17 @@ int gemv_xcols(int64_t K, int waves);
 // Most waves of one GEMV workgroup (they split K); the launch bound, and so
 // the register budget of a wave, follows from it.
 #ifndef W4A16_GEMV_MAX_WAVES
-#define W4A16_GEMV_MAX_WAVES 16
+#define W4A16_GEMV_MAX_WAVES 8
 #endif
 constexpr int kGemvMaxWaves = W4A16_GEMV_MAX_WAVES;
+// Output rows of one GEMV workgroup: 16 (one block of the layout), or 8 (half
+// a block, two columns per wave load; measured slower on the decode shapes).
+#ifndef W4A16_GEMV_ROWS
+#define W4A16_GEMV_ROWS 16
+#endif
+constexpr int kGemvRowsPerWg = W4A16_GEMV_ROWS;
 // Static LDS of one GEMV workgroup (cross-wave reduction buffer).
-constexpr size_t kGemvStaticLds = kGemvMaxWaves * 8 * 16 * sizeof(float);
+constexpr size_t kGemvStaticLds = kGemvMaxWaves * 8 * kGemvRowsPerWg * sizeof(float);
 
 // Plan for the matrix-core kernels: kind 0 streams the weights through
 // registers for M <= kSkinnyMaxM (16-row MFMA tiles of activations, one per
