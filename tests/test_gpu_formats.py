@@ -17,8 +17,8 @@ FORMATS = ["asym4", "sym4", "sym8"]
 
 # (N, K, group): ragged N (N % 16 = 8), partial last column (K % 128 = 32 / 64),
 # group 256 with an odd number of groups, several tiles of the large-M kernel
-SHAPES = [(72, 160, 32), (136, 320, 64), (328, 640, 128), (264, 768, 256), (1000, 1024, 256),
-          (520, 2048, 128)]
+SHAPES = [(8, 32, 32), (8, 256, 256), (72, 160, 32), (136, 320, 64), (328, 640, 128), (264, 768, 256),
+          (1000, 1024, 256), (520, 2048, 128)]
 
 
 def _prep(N, K, group, fmt):
@@ -158,7 +158,7 @@ def test_format_full_size_decode_and_prefill(fmt):
 # K-quant-style super-blocks (kq4, group 256)
 # ---------------------------------------------------------------------------
 
-KQ_SHAPES = [(72, 256), (264, 768), (1000, 1024), (520, 2048)]
+KQ_SHAPES = [(8, 256), (72, 256), (264, 768), (1000, 1024), (520, 2048)]
 
 
 def _prep_kq(N, K):
@@ -239,6 +239,19 @@ def test_kq4_quality_report():
     mse, snr, cos, mx = ref.quant_error_stats(sums, w_hat.size)
     assert got["max_err"] == mx
     assert abs(got["mse"] - mse) <= 1e-12 * mse and abs(got["snr_db"] - snr) <= 1e-9 and abs(got["cos"] - cos) <= 1e-12
+
+
+@pytest.mark.slow
+@pytest.mark.parametrize("fmt", ["sym8", "kq4"])
+def test_format_full_size_70b_down(fmt):
+    """The 70B down projection (K = 28672, N = 8192) packed as W8A16 and as
+    K-quant super-blocks, M = 1 and 8, every output against the oracle."""
+    group = 256 if fmt == "kq4" else 32
+    w, o, pw = H.prepared(("fmt-full", 5), lambda: wl.weights(5, 0), group, fmt)
+    for M in (1, 8):
+        x = wl.activations(5, 0, M)
+        H.check_against_oracle(_run("linear", x, "f16", pw), x, "f16", o, group)
+    H.drop((("fmt-full", 5), fmt))
 
 
 @pytest.mark.parametrize("M", [1, 16])
