@@ -24,7 +24,11 @@
 // the group's MFMAs accumulate sum x*(q-z) in fp32 and the group scale
 // multiplies that sum. bf16 activations: the dword unpacks to exact bf16
 // (128 + q); a second MFMA against a B of ones gives sum x over the same k,
-// and sum x*(128+q) - (128+z)*sum x = sum x*(q-z), all in fp32.
+// and sum x*(128+q) - (128+z)*sum x = sum x*(q-z), all in fp32. Weight
+// formats (FMT): symmetric codes use a fixed zero; 8-bit codes add a second
+// MFMA per chunk on the high-nibble plane (2048 + 16 hi in bf16); K-quant
+// super-blocks close every chunk with its own scale and minimum
+// (S * sum x q - M * sum x, sum x from the MFMA against ones).
 #pragma once
 
 #include <stdlib.h>

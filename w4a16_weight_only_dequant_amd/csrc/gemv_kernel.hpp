@@ -12,19 +12,23 @@
 // Mapping (gfx950, wave64). A workgroup owns one block of 16 output rows and
 // all of K; its waves split K into slices of 128-weight columns. Lane
 // l = 16 s + r holds, for every column, dword s of the column's four chunks of
-// row r (one 16-byte load per lane; one contiguous KiB per wave), together with
-// row r's scales and zero-points of that column (one small load each, from the
-// per-column metadata layout). The activations of the slice are staged in the
-// wave's own LDS region. The four lanes of a row meet through cross-lane shuffles at
-// the end, the waves through LDS, always in the same order, so results are
-// deterministic and no partial sum leaves the workgroup.
+// row r (one non-temporal 16-byte load per lane; one contiguous KiB per wave),
+// together with row r's scales and zero-points of that column (one small load
+// each, from the per-column metadata layout), prefetched several columns ahead
+// in a register ring. The activations of the slice are staged in the wave's
+// own LDS region (multiplied there by AWQ's per-channel factors when given).
+// The four lanes of a row meet through cross-lane shuffles at the end, the
+// waves through LDS, always in the same order, so results are deterministic
+// and no partial sum leaves the workgroup.
 //
 // fp16 activations: each dword unpacks to four exact (q - z) fp16 pairs and
 // v_dot2_f32_f16 multiplies them with the activation pairs, accumulating in
 // fp32; the group scale multiplies the fp32 group sum. bf16 activations: the
 // dword unpacks to bf16 pairs (128 + q); the sum of x*(128+q) over the
 // dword's 8 weights minus (128 + z) times the sum of those 8 activations is
-// the sum of x*(q - z), both in fp32.
+// the sum of x*(q - z), both in fp32. The other weight formats (FMT) change
+// only the unpack and the per-group terms: a fixed zero (symmetric), a second
+// code plane (8-bit), or a per-chunk scale and minimum (K-quant super-blocks).
 #pragma once
 
 #include <stdlib.h>

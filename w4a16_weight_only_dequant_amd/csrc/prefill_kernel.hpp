@@ -22,6 +22,10 @@
 // (swz below), so the MFMA operand reads (32 rows, same k) and the tile writes
 // are free of bank conflicts. The packed weights arrive one 128-weight
 // column at a time (16-byte records, one KiB per 16 rows) and serve two steps.
+// Weight formats (FMT) differ only in the dequantisation into LDS: a fixed
+// zero (symmetric 4-bit), c - 128 rebuilt from two code planes (8-bit), or
+// S q - M per 32-weight sub-block from the super-block record (K-quant), each
+// formed in fp32 and rounded once to 16 bit.
 #pragma once
 
 #include <stdlib.h>
