@@ -34,6 +34,7 @@ import argparse
 import hashlib
 import json
 import os
+import re
 import sys
 import time
 
@@ -73,10 +74,13 @@ def parse():
 
 
 def kernel_source_hash(kind):
+    """Hash of the code (comments and blank lines stripped) a kernel is built from."""
     h = hashlib.sha256()
     for f in KERNEL_SOURCES[kind]:
-        with open(os.path.join(ROOT, "w4a16_weight_only_dequant_amd", "csrc", f), "rb") as fh:
-            h.update(fh.read())
+        with open(os.path.join(ROOT, "w4a16_weight_only_dequant_amd", "csrc", f)) as fh:
+            text = re.sub(r"/\*.*?\*/", "", fh.read(), flags=re.S)
+        lines = [re.sub(r"//.*", "", line).rstrip() for line in text.splitlines()]
+        h.update("\n".join(line for line in lines if line).encode())
     return h.hexdigest()[:16]
 
 
