@@ -92,11 +92,16 @@
  * device query that failed).
  *
  * Preconditions shared by the compute calls:
- *   1 <= M <= 2^24, M*K < 2^34, N >= 8, N % 8 == 0, group in {32, 64, 128, 256},
+ *   0 <= M <= 2^24, M*K < 2^34, N >= 8, N % 8 == 0, group in {32, 64, 128, 256},
  *   K >= group, K % group == 0; pointers non-NULL and 16-byte aligned (zeros
  *   is not read, and may be NULL, for the symmetric formats); y does not
  *   overlap any input; the current device is a gfx950 (w4a16_device_supported).
  *   Weights given to w4a16_pack are finite with |w| < 2^18.
+ *
+ * Empty batch: with M = 0 the products (gemv, gemm, linear, linear_group,
+ * linear_awq) and w4a16_scale_activations check the shape, type and format
+ * arguments only, read no pointer (all may be NULL), enqueue nothing and
+ * return W4A16_OK; the workspace queries return 0 bytes.
  *
  * Every call without a format argument works on W4A16_FMT_ASYM4; its `_fmt`
  * twin takes the format as the argument after `group` and is otherwise the
@@ -197,7 +202,7 @@ w4a16_status w4a16_unpack_fmt(const void *qweight, const void *scales, const voi
                               uint8_t *codes, uint16_t *scales_out, uint8_t *zeros_out,
                               void *stream);
 
-/* Decode GEMV: y [M][N] = x [M][K] . w_hat^T for small M (1 <= M <= 8).
+/* Decode GEMV: y [M][N] = x [M][K] . w_hat^T for small M (M <= 8).
  * One pass over the packed weights: 128-bit loads, in-register unpack, fp16
  * or bf16 dot products with fp32 accumulation, per-group scale; the waves of
  * a workgroup split K and meet in LDS in a fixed order (deterministic). The
@@ -212,7 +217,7 @@ w4a16_status w4a16_gemv_fmt(const void *x, int32_t dtype, const void *qweight,
                             int64_t M, int64_t N, int64_t K, int32_t group, int32_t fmt,
                             void *workspace, size_t workspace_bytes, void *stream);
 
-/* Matrix-core GEMM for any M >= 1 (M*K < 2^34). M <= 256: the packed weights
+/* Matrix-core GEMM for any M (M*K < 2^34). M <= 256: the packed weights
  * stream through registers as in the GEMV, and each unpacked dword feeds one
  * 16x16x32 MFMA per 16-row tile of x (exact integers q - z, group scale on the
  * fp32 sums; one workgroup per tile and group of row blocks). Larger M:
@@ -272,7 +277,8 @@ int32_t w4a16_gemv_max_m(void);
 
 /* The kernel w4a16_linear picks for this shape on the current device:
  * 0 = decode GEMV, 1 = small-batch matrix-core kernel (M <= 256),
- * 2 = tiled matrix-core GEMM; -1 for arguments w4a16_linear would reject.
+ * 2 = tiled matrix-core GEMM; -1 for M = 0 (no kernel runs) and for
+ * arguments w4a16_linear would reject.
  * Host-only (queries the device's LDS size once). */
 int32_t w4a16_linear_kernel(int64_t M, int64_t N, int64_t K, int32_t group, int32_t dtype);
 

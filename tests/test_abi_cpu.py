@@ -87,7 +87,37 @@ def test_compute_calls_validate_before_device(w4):
     assert lib.w4a16_gemv(fake, 0, fake, fake, fake, fake, 1, 64, 128, 48, None, 0, None) == 1
     assert lib.w4a16_pack(None, 64, 128, 128, fake, fake, fake, None) == 1
     assert lib.w4a16_unpack(fake, fake, fake, 60, 128, 128, fake, fake, fake, None) == 1
-    assert lib.w4a16_workspace_bytes(0, 64, 128, 128, ctypes.byref(ws)) == 1
+    assert lib.w4a16_workspace_bytes(-1, 64, 128, 128, ctypes.byref(ws)) == 1
+
+
+def test_empty_batch_is_a_no_op(w4):
+    """M = 0: the shape, type and format arguments are checked, no pointer is
+    read (all NULL here), nothing is enqueued (no device is needed), OK."""
+    lib = w4.raw()
+    ws = ctypes.c_size_t(7)
+    assert lib.w4a16_workspace_bytes(0, 64, 128, 128, ctypes.byref(ws)) == 0 and ws.value == 0
+    for name in ("w4a16_gemv", "w4a16_gemm", "w4a16_linear"):
+        fn = getattr(lib, name)
+        assert fn(None, 0, None, None, None, None, 0, 64, 128, 128, None, 0, None) == 0, name
+        assert fn(None, 1, None, None, None, None, 0, 64, 256, 32, None, 0, None) == 0, name
+        assert fn(None, 0, None, None, None, None, 0, 60, 128, 128, None, 0, None) == 1, name   # N % 8
+        assert fn(None, 0, None, None, None, None, 0, 64, 128, 48, None, 0, None) == 1, name    # group
+        assert fn(None, 7, None, None, None, None, 0, 64, 128, 128, None, 0, None) == 1, name   # dtype
+        assert fn(None, 0, None, None, None, None, -1, 64, 128, 128, None, 0, None) == 1, name  # M < 0
+        fmt = getattr(lib, name + "_fmt")
+        assert fmt(None, 0, None, None, None, None, 0, 64, 256, 256, 3, None, 0, None) == 0, name
+        assert fmt(None, 0, None, None, None, None, 0, 64, 256, 128, 3, None, 0, None) == 1, name   # kq4 needs 256
+        assert fmt(None, 0, None, None, None, None, 0, 64, 256, 128, 9, None, 0, None) == 1, name   # format
+    assert lib.w4a16_linear_awq(None, 0, None, None, None, None, None, 0, 64, 256, 128, 0, None, 0, None) == 0
+    assert lib.w4a16_linear_awq(None, 0, None, None, None, None, None, 0, 64, 200, 128, 0, None, 0, None) == 1
+    assert lib.w4a16_scale_activations(None, 0, None, None, 0, 64, None) == 0
+    assert lib.w4a16_scale_activations(None, 0, None, None, 0, 60, None) == 1
+    assert lib.w4a16_awq_workspace_bytes(0, 64, 256, 128, 0, 0, ctypes.byref(ws)) == 0 and ws.value == 0
+    Ns = (ctypes.c_int64 * 2)(64, 128)
+    assert lib.w4a16_linear_group(2, None, 0, None, None, None, None, 0, Ns, 128, 128, None, 0, None) == 0
+    bad = (ctypes.c_int64 * 2)(64, 60)
+    assert lib.w4a16_linear_group(2, None, 0, None, None, None, None, 0, bad, 128, 128, None, 0, None) == 1
+    assert lib.w4a16_linear_kernel(0, 64, 128, 128, 0) == -1
 
 
 def test_grouped_call_validates_before_device(w4):

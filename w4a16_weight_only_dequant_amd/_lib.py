@@ -160,6 +160,16 @@ class PackedWeight:
         #                           kq4: 16-byte super-block records [K/256][N] (viewed as float16)
         self.zeros = zeros        # int32 zero-point words (asym4), None for the symmetric formats
         self.N, self.K, self.group, self.fmt = N, K, group, fmt
+        # the kernels index these buffers by the shape alone: check their sizes once here
+        qb, sb, zb = packed_bytes(N, K, group, fmt)
+        parts = [("qweight", qweight, qb), ("scales", scales, sb)] + ([("zeros", zeros, zb)] if zb else [])
+        for name, t, nb in parts:
+            if t is None or not t.is_cuda or not t.is_contiguous():
+                raise ValueError(f"{name} must be a contiguous CUDA tensor")
+            if t.numel() * t.element_size() < nb:
+                raise ValueError(f"{name} holds {t.numel() * t.element_size()} bytes, the layout needs {nb}")
+            if t.device != qweight.device:
+                raise ValueError("qweight, scales and zeros must be on one device")
 
     def nbytes(self) -> int:
         z = 4 * self.zeros.numel() if self.zeros is not None else 0
@@ -236,12 +246,22 @@ def _default_workspace(device) -> Workspace:
     return ws
 
 
+def _output(out, M: int, N: int, x: torch.Tensor) -> torch.Tensor:
+    """`out`, checked to be what the call writes (contiguous [M][N] of x's type
+    and device), or a new tensor."""
+    if out is None:
+        return torch.empty((M, N), dtype=x.dtype, device=x.device)
+    if tuple(out.shape) != (M, N) or out.dtype != x.dtype or out.device != x.device or not out.is_contiguous():
+        raise ValueError(f"out must be a contiguous {x.dtype} tensor [{M}][{N}] on {x.device}")
+    return out
+
+
 def _call(fn_name: str, x: torch.Tensor, pw: PackedWeight, out=None, workspace=None, stream=None):
     if x.dim() != 2 or x.shape[1] != pw.K or not x.is_cuda:
         raise ValueError(f"x must be a CUDA tensor [M][{pw.K}]")
     x = x.contiguous()
     M = x.shape[0]
-    y = out if out is not None else torch.empty((M, pw.N), dtype=x.dtype, device=x.device)
+    y = _output(out, M, pw.N, x)
     nbytes = workspace_bytes(M, pw.N, pw.K, pw.group)
     ws = (workspace or _default_workspace(x.device)).get(nbytes)
     ws_ptr = ws.data_ptr() if ws is not None else None
@@ -280,8 +300,9 @@ def linear_group(xs, pws, outs=None, workspace=None, stream=None):
             raise ValueError("every x must be a CUDA tensor [M][K] of one type")
         if pw.K != K or pw.group != group or pw.fmt != pws[0].fmt:
             raise ValueError("every weight must share K, group and format")
-    ys = outs if outs is not None else [torch.empty((M, pw.N), dtype=xs[0].dtype, device=xs[0].device)
-                                        for pw in pws]
+    if outs is not None and len(outs) != count:
+        raise ValueError("need one output per packed weight")
+    ys = [_output(outs[i] if outs is not None else None, M, pw.N, xs[0]) for i, pw in enumerate(pws)]
     arr = lambda vals: (ctypes.c_void_p * count)(*vals)  # noqa: E731
     nbytes = workspace_bytes(M, max(pw.N for pw in pws), K, group)
     ws = (workspace or _default_workspace(xs[0].device)).get(nbytes)
@@ -329,7 +350,7 @@ def scale_activations(x: torch.Tensor, act_mul: torch.Tensor, out=None, stream=N
     M, K = x.shape
     if act_mul.dtype != torch.float32 or act_mul.numel() != K or not act_mul.is_cuda:
         raise TypeError(f"act_mul must be a float32 CUDA tensor [{K}]")
-    y = out if out is not None else torch.empty_like(x)
+    y = _output(out, M, K, x)
     _check("w4a16_scale_activations", _lib.w4a16_scale_activations(
         x.data_ptr(), _dtype_code(x), act_mul.contiguous().data_ptr(), y.data_ptr(), M, K, _stream_ptr(stream)))
     return y
@@ -345,7 +366,7 @@ def linear_awq(x: torch.Tensor, act_mul: torch.Tensor, pw: PackedWeight, out=Non
     x = x.contiguous()
     act_mul = act_mul.contiguous()
     M = x.shape[0]
-    y = out if out is not None else torch.empty((M, pw.N), dtype=x.dtype, device=x.device)
+    y = _output(out, M, pw.N, x)
     nb = _sz()
     _check("w4a16_awq_workspace_bytes", _lib.w4a16_awq_workspace_bytes(M, pw.N, pw.K, pw.group, _fmt_code(pw.fmt),
                                                                        _dtype_code(x), ctypes.byref(nb)))

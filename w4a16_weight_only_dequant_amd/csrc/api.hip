@@ -86,15 +86,18 @@ w4a16_status check_device() {
 }
 
 // Argument checks shared by gemv / gemm / linear. The symmetric formats do
-// not read `zeros` (it may be NULL).
+// not read `zeros` (it may be NULL). An empty batch (M = 0) checks the shape,
+// type and format arguments only: no pointer is read, and the callers return
+// before anything is enqueued.
 w4a16_status check_linear(const void *x, int32_t dtype, const void *qweight, const void *scales,
                           const void *zeros, void *y, int64_t M, int64_t N, int64_t K, int32_t group,
                           int32_t fmt, void *workspace, size_t workspace_bytes, size_t need) {
     if (!fmt_group_ok(fmt, group)) return W4A16_ERR_INVALID_ARG;
+    if (dtype != W4A16_F16 && dtype != W4A16_BF16) return W4A16_ERR_INVALID_ARG;
+    if (M < 0 || M > (1LL << 24) || !shape_ok(N, K, group)) return W4A16_ERR_INVALID_ARG;
+    if (M == 0) return W4A16_OK;
     const bool zp = fmt == W4A16_FMT_ASYM4;
     if (!x || !qweight || !scales || (zp && !zeros) || !y) return W4A16_ERR_INVALID_ARG;
-    if (dtype != W4A16_F16 && dtype != W4A16_BF16) return W4A16_ERR_INVALID_ARG;
-    if (M < 1 || M > (1LL << 24) || !shape_ok(N, K, group)) return W4A16_ERR_INVALID_ARG;
     if (M * K >= (1LL << 34)) return W4A16_ERR_INVALID_ARG;   // 32-bit activation indices (in 16-byte units)
     if (!aligned16(x) || !aligned16(qweight) || !aligned16(scales) || (zp && !aligned16(zeros)) ||
         !aligned16(y))
@@ -207,8 +210,8 @@ w4a16_status w4a16_packed_bytes_fmt(int64_t N, int64_t K, int32_t group, int32_t
 }
 
 w4a16_status w4a16_workspace_bytes(int64_t M, int64_t N, int64_t K, int32_t group, size_t *bytes) {
-    if (!bytes || M < 1 || M > (1LL << 24) || !shape_ok(N, K, group)) return W4A16_ERR_INVALID_ARG;
-    *bytes = gemm_need(M, N, K, group);
+    if (!bytes || M < 0 || M > (1LL << 24) || !shape_ok(N, K, group)) return W4A16_ERR_INVALID_ARG;
+    *bytes = M == 0 ? 0 : gemm_need(M, N, K, group);
     return W4A16_OK;
 }
 
@@ -263,7 +266,7 @@ w4a16_status w4a16_gemv_fmt(const void *x, int32_t dtype, const void *qweight, c
     (void)workspace_bytes;
     if (M > 8) return W4A16_ERR_INVALID_ARG;
     w4a16_status st = check_linear(x, dtype, qweight, scales, zeros, y, M, N, K, group, fmt, nullptr, 0, 0);
-    if (st != W4A16_OK) return st;
+    if (st != W4A16_OK || M == 0) return st;
     st = check_device();
     if (st != W4A16_OK) return st;
     if (!gemv_fits(M, N, K, group, dtype, fmt)) return W4A16_ERR_INVALID_ARG;
@@ -287,7 +290,7 @@ w4a16_status w4a16_gemm_fmt(const void *x, int32_t dtype, const void *qweight, c
                             ? gemm_need(M, N, K, group) : 0;
     w4a16_status st = check_linear(x, dtype, qweight, scales, zeros, y, M, N, K, group, fmt, workspace,
                                    workspace_bytes, need);
-    if (st != W4A16_OK) return st;
+    if (st != W4A16_OK || M == 0) return st;
     st = check_device();
     if (st != W4A16_OK) return st;
     GemmPlan plan = gemm_plan(M, N, K, group);
@@ -309,8 +312,16 @@ w4a16_status w4a16_linear_group_fmt(int32_t count, const void *const *x, int32_t
                                     int64_t K, int32_t group, int32_t fmt, void *workspace, size_t workspace_bytes,
                                     void *stream) {
     const bool zp = fmt == W4A16_FMT_ASYM4;
-    if (count < 1 || count > kMaxGroup || !x || !qweight || !scales || (zp && !zeros) || !y || !N)
-        return W4A16_ERR_INVALID_ARG;
+    if (count < 1 || count > kMaxGroup || !N) return W4A16_ERR_INVALID_ARG;
+    if (M == 0) {   // empty batch: shapes only
+        for (int p = 0; p < count; ++p) {
+            const w4a16_status st = check_linear(nullptr, dtype, nullptr, nullptr, nullptr, nullptr, 0, N[p], K,
+                                                 group, fmt, nullptr, 0, 0);
+            if (st != W4A16_OK) return st;
+        }
+        return W4A16_OK;
+    }
+    if (!x || !qweight || !scales || (zp && !zeros) || !y) return W4A16_ERR_INVALID_ARG;
     auto zero_ptr = [&](int p) -> const void * { return zp ? zeros[p] : nullptr; };
     int64_t n_total = 0;
     for (int p = 0; p < count; ++p) {
@@ -416,9 +427,10 @@ w4a16_status w4a16_quant_error(const float *w, const void *qweight, const void *
 
 w4a16_status w4a16_scale_activations(const void *x, int32_t dtype, const float *act_mul, void *x_out, int64_t M,
                                      int64_t K, void *stream) {
-    if (!x || !act_mul || !x_out || M < 1 || M > (1LL << 24) || K < 8 || K % 8 != 0 || K > (1LL << 30))
-        return W4A16_ERR_INVALID_ARG;
+    if (M < 0 || M > (1LL << 24) || K < 8 || K % 8 != 0 || K > (1LL << 30)) return W4A16_ERR_INVALID_ARG;
     if (dtype != W4A16_F16 && dtype != W4A16_BF16) return W4A16_ERR_INVALID_ARG;
+    if (M == 0) return W4A16_OK;
+    if (!x || !act_mul || !x_out) return W4A16_ERR_INVALID_ARG;
     if (!aligned16(x) || !aligned16(act_mul) || !aligned16(x_out)) return W4A16_ERR_INVALID_ARG;
     const Range ro = range_of(x_out, (size_t)(M * K * 2));
     if (overlap(ro, range_of(act_mul, (size_t)K * 4))) return W4A16_ERR_INVALID_ARG;
@@ -432,19 +444,19 @@ w4a16_status w4a16_scale_activations(const void *x, int32_t dtype, const float *
 
 w4a16_status w4a16_awq_workspace_bytes(int64_t M, int64_t N, int64_t K, int32_t group, int32_t fmt, int32_t dtype,
                                        size_t *bytes) {
-    if (!bytes || M < 1 || M > (1LL << 24) || !shape_ok(N, K, group) || !fmt_group_ok(fmt, group) ||
+    if (!bytes || M < 0 || M > (1LL << 24) || !shape_ok(N, K, group) || !fmt_group_ok(fmt, group) ||
         (dtype != W4A16_F16 && dtype != W4A16_BF16))
         return W4A16_ERR_INVALID_ARG;
-    *bytes = gemv_fits(M, N, K, group, dtype, fmt) ? 0 : align_up((size_t)(M * K * 2), 256);
+    *bytes = (M == 0 || gemv_fits(M, N, K, group, dtype, fmt)) ? 0 : align_up((size_t)(M * K * 2), 256);
     return W4A16_OK;
 }
 
 w4a16_status w4a16_linear_awq(const void *x, int32_t dtype, const float *act_mul, const void *qweight,
                               const void *scales, const void *zeros, void *y, int64_t M, int64_t N, int64_t K,
                               int32_t group, int32_t fmt, void *workspace, size_t workspace_bytes, void *stream) {
-    if (!act_mul || !aligned16(act_mul)) return W4A16_ERR_INVALID_ARG;
     w4a16_status st = check_linear(x, dtype, qweight, scales, zeros, y, M, N, K, group, fmt, nullptr, 0, 0);
-    if (st != W4A16_OK) return st;
+    if (st != W4A16_OK || M == 0) return st;
+    if (!act_mul || !aligned16(act_mul)) return W4A16_ERR_INVALID_ARG;
     if (overlap(range_of(y, (size_t)(M * N * 2)), range_of(act_mul, (size_t)K * 4))) return W4A16_ERR_INVALID_ARG;
     const bool fused = gemv_fits(M, N, K, group, dtype, fmt);
     const size_t need = fused ? 0 : align_up((size_t)(M * K * 2), 256);
