@@ -32,6 +32,19 @@ def test_library_exports_every_declared_symbol(w4):
     assert set(names) == set(w4.EXPORTED)
 
 
+def test_library_exports_only_the_c_abi(w4):
+    """The dynamic symbol table holds the declared C entry points and nothing
+    else (internal C++ symbols are local to the library)."""
+    import shutil
+    import subprocess
+    nm = shutil.which("nm")
+    if nm is None:
+        pytest.skip("nm is not installed")
+    out = subprocess.run([nm, "-D", "--defined-only", w4.LIB_PATH], capture_output=True, text=True, check=True).stdout
+    exported = {line.split()[-1] for line in out.splitlines() if line.strip()}
+    assert exported == set(_declared())
+
+
 def test_status_strings_and_version(w4):
     lib = w4.raw()
     assert lib.w4a16_layout_version() == 2

@@ -49,7 +49,9 @@ def build(verbose: bool = False, jobs: int = 8, out: str = OUT, extra_flags=(), 
     with ThreadPoolExecutor(max_workers=jobs) as ex:
         list(ex.map(_run, cmds))
     tmp = out + ".tmp"
-    _run([HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC", "-o", tmp, *objs])
+    # export the C ABI only (w4a16_*); internal C++ symbols stay local
+    exports = os.path.join(CSRC, "exports.map")
+    _run([HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC", f"-Wl,--version-script={exports}", "-o", tmp, *objs])
     os.replace(tmp, out)
     if verbose:
         print("built", out)

@@ -116,6 +116,25 @@ w4a16_status check_linear(const void *x, int32_t dtype, const void *qweight, con
     return W4A16_OK;
 }
 
+std::mutex g_attr_mutex;
+}  // namespace
+
+hipError_t w4a16::raise_dyn_lds(const void *kern, size_t bytes, DynLdsAttr &attr) {
+    if (bytes <= 48 * 1024) return hipSuccess;   // within the default limit
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    if (dev < 0 || dev >= kAttrDevices)
+        return hipFuncSetAttribute(kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)bytes);
+    if (attr.set[dev].load(std::memory_order_acquire) >= (int)bytes) return hipSuccess;
+    std::lock_guard<std::mutex> lock(g_attr_mutex);
+    if (attr.set[dev].load(std::memory_order_relaxed) >= (int)bytes) return hipSuccess;
+    e = hipFuncSetAttribute(kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)bytes);
+    if (e == hipSuccess) attr.set[dev].store((int)bytes, std::memory_order_release);
+    return e;
+}
+
+namespace {
 // Largest LDS allocation of one workgroup on the current device (cached per device).
 std::atomic<int> g_max_lds[kMaxDevices];
 size_t max_lds_per_block() {

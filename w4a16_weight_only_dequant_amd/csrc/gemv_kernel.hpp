@@ -409,11 +409,9 @@ hipError_t launch_one(const void *x, const void *qw, const void *qw_hi, const vo
     const int xcols = gemv_xcols(K, plan.waves);
     const size_t lds = wave_lds_bytes(MT, xcols, BF || FormatTraits<FMT>::kquant) * plan.waves;
     auto kern = gemv_kernel<GROUP, MT, BF, FMT>;
-    if (lds > 48 * 1024) {
-        hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(kern),
-                                           hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
-        if (e != hipSuccess) return e;
-    }
+    static DynLdsAttr attr;
+    hipError_t e = raise_dyn_lds(reinterpret_cast<const void *>(kern), lds, attr);
+    if (e != hipSuccess) return e;
     hipLaunchKernelGGL(kern, dim3(plan.row_blocks), dim3(64 * plan.waves), lds, stream,
                        reinterpret_cast<const uint16_t *>(x), reinterpret_cast<const uint4 *>(qw),
                        reinterpret_cast<const uint4 *>(qw_hi), reinterpret_cast<const uint16_t *>(sc),

@@ -411,13 +411,9 @@ hipError_t launch_tile(const void *x, const void *qw, const void *qh, const void
                        int N, int K, int ms, hipStream_t stream) {
     auto kern = prefill_kernel<BM, BN, WM, WN, GROUP, BF, FMT>;
     const size_t lds = (size_t)2 * (BM + BN) * kUnits * 16;
-    static bool attr_set = false;   // per instantiation; the attribute is per function
-    if (!attr_set) {
-        hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(kern),
-                                           hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
-        if (e != hipSuccess) return e;
-        attr_set = true;
-    }
+    static DynLdsAttr attr;
+    hipError_t e = raise_dyn_lds(reinterpret_cast<const void *>(kern), lds, attr);
+    if (e != hipSuccess) return e;
     const int m_tiles = (int)ceil_div(M, BM), n_tiles = (int)ceil_div(N, BN);
     hipLaunchKernelGGL(kern, dim3((unsigned)(m_tiles * n_tiles)), dim3(64 * WM * WN), lds, stream,
                        reinterpret_cast<const uint16_t *>(x), reinterpret_cast<const uint4 *>(qw),

@@ -6,6 +6,8 @@
 #include <stdint.h>
 #include <stddef.h>
 
+#include <atomic>
+
 namespace w4a16 {
 
 // Packed device layout. Rows come in blocks of 16 (the last block may hold
@@ -35,6 +37,18 @@ __host__ __device__ inline int64_t dword_offset(int n, int c, int d, int N, int 
 
 // Weight formats (the values of w4a16_format in the public header).
 enum { kAsym4 = 0, kSym4 = 1, kSym8 = 2, kKq4 = 3 };
+
+// The dynamic-LDS limit of one kernel (hipFuncAttributeMaxDynamicSharedMemorySize)
+// is per kernel and per device. Each launcher keeps one record per kernel;
+// raise_dyn_lds sets the attribute on the current device only when a launch
+// needs more than was set there before (values only grow, under one lock), so
+// steady-state launches make no attribute call and concurrent callers never
+// lower a limit another one relies on.
+constexpr int kAttrDevices = 64;
+struct DynLdsAttr {
+    std::atomic<int> set[kAttrDevices];
+};
+hipError_t raise_dyn_lds(const void *kern, size_t bytes, DynLdsAttr &attr);
 
 typedef _Float16 half2_t __attribute__((ext_vector_type(2)));
 typedef __bf16 bf162_t __attribute__((ext_vector_type(2)));
