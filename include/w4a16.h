@@ -171,10 +171,19 @@ w4a16_status w4a16_packed_bytes_fmt(int64_t N, int64_t K, int32_t group, int32_t
                                     size_t *zeros_bytes);
 
 /* Workspace bytes a w4a16_gemv / w4a16_gemm / w4a16_linear call of this shape
- * needs. Host-only. The current kernels reduce inside each workgroup and need
- * none (0 bytes; the compute calls then accept a NULL workspace); the argument
- * stays in the interface so that a kernel needing scratch memory can be added
- * without changing it. */
+ * needs on the current device. Host-only (queries the device's compute-unit
+ * count once). The decode kernels need none. The tiled GEMM (M > 256) needs
+ * some when its last round of 256 x 256 (or 128 / 64-row) output tiles would
+ * be at most half full on the device's compute units: it then splits the
+ * last two rounds' tiles by K over one workgroup per compute unit
+ * (stream-K), and a tile's two workgroups hand an fp32 partial tile and an
+ * 8-byte flag over through the workspace: BM x 256 x 4 + 8 bytes per compute
+ * unit (about 64 MiB on 256 compute units). With 0 bytes the compute calls
+ * accept a NULL workspace.
+ * The workspace is device memory owned by the caller, 16-byte aligned, and
+ * must not overlap any argument of the call. Its contents need no
+ * initialisation and are meaningless after the call; calls that run at the
+ * same time (other streams) must not share one. */
 w4a16_status w4a16_workspace_bytes(int64_t M, int64_t N, int64_t K, int32_t group,
                                    size_t *bytes);
 
@@ -217,7 +226,8 @@ w4a16_status w4a16_gemv_fmt(const void *x, int32_t dtype, const void *qweight,
                             int64_t M, int64_t N, int64_t K, int32_t group, int32_t fmt,
                             void *workspace, size_t workspace_bytes, void *stream);
 
-/* Matrix-core GEMM for any M (M*K < 2^34). M <= 256: the packed weights
+/* Matrix-core GEMM for any M (M*K < 2^34); the workspace is sized by
+ * w4a16_workspace_bytes (W4A16_ERR_WORKSPACE when it is smaller). M <= 256: the packed weights
  * stream through registers as in the GEMV, and each unpacked dword feeds one
  * 16x16x32 MFMA per 16-row tile of x (exact integers q - z, group scale on the
  * fp32 sums; one workgroup per tile and group of row blocks). Larger M:
@@ -256,8 +266,9 @@ w4a16_status w4a16_linear_fmt(const void *x, int32_t dtype, const void *qweight,
  * of any problem. For M <= 256 all problems run in one launch of the
  * small-batch matrix-core kernel, which pays the fixed cost of a launch (the
  * ramp-up and drain that dominate small decode layers) once; for larger M it
- * enqueues one tiled GEMM per problem. Results are bit-identical to
- * w4a16_gemm on each problem. This fuses the launches, not the math: the
+ * enqueues one tiled GEMM per problem, one after the other, each using the
+ * workspace (which must hold the largest w4a16_workspace_bytes of the
+ * problems). Results are bit-identical to w4a16_gemm on each problem. This fuses the launches, not the math: the
  * pages' dual-output decode variant ("Quantization Is Not a Zip File", section
  * 2, paired gate/up projections) is the special case of two problems sharing x. */
 w4a16_status w4a16_linear_group(int32_t count, const void *const *x, int32_t dtype,
@@ -314,7 +325,8 @@ w4a16_status w4a16_quant_error(const float *w, const void *qweight, const void *
  * (M <= 8 and the activations fit its LDS) the scaling is folded into the
  * GEMV's activation staging: one launch, no workspace. Otherwise it runs
  * w4a16_scale_activations into the workspace (w4a16_awq_workspace_bytes:
- * M*K*2 rounded up to 256) followed by w4a16_gemm. Either way the result is
+ * M*K*2 rounded up to 256, then w4a16_workspace_bytes for the product)
+ * followed by w4a16_gemm. Either way the result is
  * the one the same kernel gives for the pre-scaled activations. */
 w4a16_status w4a16_scale_activations(const void *x, int32_t dtype, const float *act_mul, void *x_out,
                                      int64_t M, int64_t K, void *stream);

@@ -1,0 +1,131 @@
+"""GPU parity of the stream-K schedule of the tiled GEMM: shapes whose tile count
+leaves a partly idle last round on the 256 compute units split the last rounds'
+tiles by columns over 256 workgroups, which hand fp32 partial tiles over
+through the workspace. Outputs within the bar of the oracle (R19), one-hot
+inputs bit-exact, repeat calls and graph replays bit-identical, any workspace
+contents accepted, a short workspace refused."""
+import numpy as np
+import pytest
+
+import workloads as wl
+from oracle import w4a16_ref as ref
+from tests import helpers as H
+
+pytestmark = pytest.mark.gpu
+
+# (M, N, K, group), 256 x 256 tiles: 8 x 33 = 264 tiles (a last round of 8
+# tiles: every workgroup shares tiles), the same with ragged K (a partial last
+# column in the tail segments) and with group 64, and 8 x 97 = 776 tiles (two
+# rounds of whole tiles, then the last 264 tiles split)
+SK_SHAPES = [(2048, 8448, 512, 128), (2048, 8448, 672, 32), (2048, 8448, 1024, 64), (2048, 24832, 512, 128)]
+
+
+def _prep(N, K, group, fmt="asym4"):
+    return H.prepared(("sk", N, K, group), lambda: wl.random_weights(N * 3 + K, N, K), group, fmt)
+
+
+def _cols(N, seed):
+    rng = np.random.default_rng(seed)
+    return np.unique(np.concatenate([np.arange(16), N - 16 + np.arange(16), rng.choice(N, 96, replace=False)]))
+
+
+def _uses_stream_k(M, N, K, group):
+    return H.lib().workspace_bytes(M, N, K, group) > 0
+
+
+@pytest.mark.parametrize("M,N,K,group", SK_SHAPES)
+@pytest.mark.parametrize("dtype", ["f16", "bf16"])
+def test_stream_k_matches_oracle(M, N, K, group, dtype):
+    import torch
+    assert _uses_stream_k(M, N, K, group), "shape expected to take the stream-K split"
+    w, o, pw = _prep(N, K, group)
+    x = wl.random_activations(M + N + K, M, K, dtype)
+    y = H.lib().gemm(H.to_device_bits(x, dtype), pw)
+    torch.cuda.synchronize()
+    H.check_against_oracle(y, x, dtype, o, group, cols=_cols(N, M + K))
+    # every output row of a few columns: each tile's rows, split or whole
+    H.check_against_oracle(y, x, dtype, o, group, cols=np.array([0, 255, 256, N // 2, N - 1]))
+
+
+@pytest.mark.parametrize("fmt", ["sym8", "kq4"])
+def test_stream_k_formats(fmt):
+    import torch
+    M, N, K = 2048, 8448, 512
+    group = 256 if fmt == "kq4" else 128
+    w, o, pw = _prep(N, K, group, fmt)
+    x = wl.random_activations(7, M, K, "bf16")
+    y = H.lib().gemm(H.to_device_bits(x, "bf16"), pw)
+    torch.cuda.synchronize()
+    H.check_against_oracle(y, x, "bf16", o, group, cols=_cols(N, 3))
+
+
+@pytest.mark.parametrize("dtype", ["f16", "bf16"])
+def test_stream_k_one_hot_is_exact(dtype):
+    """One-hot rows: one of the two halves of a split tile holds the selected
+    weight and the other an exact zero, so the sum is round(w_hat) exactly."""
+    import torch
+    M, N, K, group = 2048, 8448, 512, 128
+    w, o, pw = _prep(N, K, group)
+    w_hat = ref.dequantize(o["codes"], o["s_bits"], o["zeros"], group)
+    ks = (np.arange(M) * 7919 + 3) % K
+    x32 = np.zeros((M, K), dtype=np.float32)
+    x32[np.arange(M), ks] = 1.0
+    y = H.lib().gemm(H.to_device_bits(wl.to_16bit(x32, dtype), dtype), pw)
+    torch.cuda.synchronize()
+    got = y.cpu().view(torch.int16).numpy().view(np.uint16)
+    cols = _cols(N, 11)
+    want = ref.out_round_bits(w_hat[cols][:, ks].T, dtype)
+    assert np.array_equal(got[:, cols], want)
+
+
+def test_stream_k_repeatable_any_workspace_and_graph_replay():
+    import torch
+    w4 = H.lib()
+    M, N, K, group = 2048, 8448, 672, 32
+    w, o, pw = _prep(N, K, group)
+    x = H.to_device_bits(wl.random_activations(5, M, K, "bf16"), "bf16")
+    nbytes = w4.workspace_bytes(M, N, K, group)
+    # a workspace full of arbitrary bytes (stale flags included) gives the same result
+    ws_a, ws_b = w4.Workspace("cuda"), w4.Workspace("cuda")
+    buf = ws_b.get(nbytes)
+    buf.copy_(torch.randint(0, 256, buf.shape, dtype=torch.uint8, device="cuda"))
+    y0 = w4.gemm(x, pw, workspace=ws_a)
+    y1 = w4.gemm(x, pw, workspace=ws_b)
+    y2 = w4.gemm(x, pw, workspace=ws_a)
+    torch.cuda.synchronize()
+    assert torch.equal(y0.view(torch.int16), y1.view(torch.int16))
+    assert torch.equal(y0.view(torch.int16), y2.view(torch.int16))
+    # replays of one captured launch (one token): each must wait for its own partials
+    out = torch.empty_like(y0)
+    stream = torch.cuda.Stream()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(stream):
+        w4.gemm(x, pw, out=out, workspace=ws_a)   # warm-up on the capture stream
+        torch.cuda.synchronize()
+        with torch.cuda.graph(graph, stream=stream):
+            w4.gemm(x, pw, out=out, workspace=ws_a)
+    for i in range(3):
+        out.zero_()
+        filler = torch.randn(1 << 20, device="cuda").sum()   # eager work between replays
+        graph.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out.view(torch.int16), y0.view(torch.int16)), f"replay {i}"
+        assert bool(torch.isfinite(filler))
+
+
+def test_stream_k_short_workspace_refused():
+    import torch
+    w4 = H.lib()
+    M, N, K, group = 2048, 8448, 512, 128
+    w, o, pw = _prep(N, K, group)
+    x = H.to_device_bits(wl.random_activations(6, M, K, "f16"), "f16")
+    nbytes = w4.workspace_bytes(M, N, K, group)
+    assert nbytes >= 256 * 256 * 256 * 4
+    short = torch.empty(nbytes - 256, dtype=torch.uint8, device="cuda")
+    y = torch.empty((M, N), dtype=torch.float16, device="cuda")
+    st = w4.raw().w4a16_gemm(x.data_ptr(), 0, pw.qweight.data_ptr(), pw.scales.data_ptr(), pw.zeros_ptr(),
+                             y.data_ptr(), M, N, K, group, short.data_ptr(), short.numel(), None)
+    assert st == 4
+    st = w4.raw().w4a16_gemm(x.data_ptr(), 0, pw.qweight.data_ptr(), pw.scales.data_ptr(), pw.zeros_ptr(),
+                             y.data_ptr(), M, N, K, group, None, 0, None)
+    assert st == 4

@@ -304,7 +304,7 @@ def linear_group(xs, pws, outs=None, workspace=None, stream=None):
         raise ValueError("need one output per packed weight")
     ys = [_output(outs[i] if outs is not None else None, M, pw.N, xs[0]) for i, pw in enumerate(pws)]
     arr = lambda vals: (ctypes.c_void_p * count)(*vals)  # noqa: E731
-    nbytes = workspace_bytes(M, max(pw.N for pw in pws), K, group)
+    nbytes = max(workspace_bytes(M, pw.N, K, group) for pw in pws)
     ws = (workspace or _default_workspace(xs[0].device)).get(nbytes)
     zeros = arr([p.zeros_ptr() for p in pws]) if pws[0].zeros is not None else None
     _check("w4a16_linear_group_fmt", _lib.w4a16_linear_group_fmt(

@@ -108,16 +108,31 @@ w4a16_status check_linear(const void *x, int32_t dtype, const void *qweight, con
     if (overlap(ry, range_of(x, (size_t)(M * K * 2))) || overlap(ry, range_of(qweight, qb)) ||
         overlap(ry, range_of(scales, sb)) || overlap(ry, range_of(zeros, zb)))
         return W4A16_ERR_INVALID_ARG;
-    if (need > 0) {
+    if (need > 0) {   // the kernels write the workspace: it may overlap nothing else
         if (!workspace || workspace_bytes < need) return W4A16_ERR_WORKSPACE;
         if (!aligned16(workspace)) return W4A16_ERR_INVALID_ARG;
-        if (overlap(ry, range_of(workspace, need))) return W4A16_ERR_INVALID_ARG;
+        const Range rw = range_of(workspace, need);
+        if (overlap(ry, rw) || overlap(rw, range_of(x, (size_t)(M * K * 2))) || overlap(rw, range_of(qweight, qb)) ||
+            overlap(rw, range_of(scales, sb)) || overlap(rw, range_of(zeros, zb)))
+            return W4A16_ERR_INVALID_ARG;
     }
     return W4A16_OK;
 }
 
 std::mutex g_attr_mutex;
+std::atomic<int> g_cus[kMaxDevices];
 }  // namespace
+
+int w4a16::device_cu_count() {
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return 0;
+    int v = g_cus[dev].load(std::memory_order_acquire);
+    if (v == 0) {
+        if (hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || v <= 0) return 0;
+        g_cus[dev].store(v, std::memory_order_release);
+    }
+    return v;
+}
 
 hipError_t w4a16::raise_dyn_lds(const void *kern, size_t bytes, DynLdsAttr &attr) {
     if (bytes <= 48 * 1024) return hipSuccess;   // within the default limit
@@ -166,9 +181,10 @@ bool prefer_gemv(int64_t M, int64_t N, int64_t K, int32_t group, int32_t dtype, 
            (dtype == W4A16_F16 || dtype == W4A16_BF16) && gemv_fits(M, N, K, group, dtype, fmt);
 }
 
+// Workspace of a matrix-core call: the stream-K partials and flags of the
+// tiled kernel when its plan splits tiles (0 otherwise).
 size_t gemm_need(int64_t M, int64_t N, int64_t K, int32_t group) {
-    (void)M; (void)N; (void)K; (void)group;
-    return 0;   // no kernel of this library needs scratch memory
+    return prefill_workspace_bytes(gemm_plan(M, N, K, group));
 }
 
 }  // namespace
@@ -313,8 +329,9 @@ w4a16_status w4a16_gemm_fmt(const void *x, int32_t dtype, const void *qweight, c
     st = check_device();
     if (st != W4A16_OK) return st;
     GemmPlan plan = gemm_plan(M, N, K, group);
+    if (prefill_workspace_bytes(plan) > need) return W4A16_ERR_WORKSPACE;   // (the same plan: never)
     hipError_t e = launch_gemm(x, dtype == W4A16_BF16, qweight, scales, zeros, y, (int)M, (int)N,
-                               (int)K, group, fmt, plan, reinterpret_cast<hipStream_t>(stream));
+                               (int)K, group, fmt, plan, workspace, reinterpret_cast<hipStream_t>(stream));
     return e == hipSuccess ? W4A16_OK : W4A16_ERR_HIP;
 }
 
@@ -466,7 +483,8 @@ w4a16_status w4a16_awq_workspace_bytes(int64_t M, int64_t N, int64_t K, int32_t 
     if (!bytes || M < 0 || M > (1LL << 24) || !shape_ok(N, K, group) || !fmt_group_ok(fmt, group) ||
         (dtype != W4A16_F16 && dtype != W4A16_BF16))
         return W4A16_ERR_INVALID_ARG;
-    *bytes = (M == 0 || gemv_fits(M, N, K, group, dtype, fmt)) ? 0 : align_up((size_t)(M * K * 2), 256);
+    *bytes = (M == 0 || gemv_fits(M, N, K, group, dtype, fmt))
+                 ? 0 : align_up((size_t)(M * K * 2), 256) + gemm_need(M, N, K, group);
     return W4A16_OK;
 }
 
@@ -478,7 +496,9 @@ w4a16_status w4a16_linear_awq(const void *x, int32_t dtype, const float *act_mul
     if (!act_mul || !aligned16(act_mul)) return W4A16_ERR_INVALID_ARG;
     if (overlap(range_of(y, (size_t)(M * N * 2)), range_of(act_mul, (size_t)K * 4))) return W4A16_ERR_INVALID_ARG;
     const bool fused = gemv_fits(M, N, K, group, dtype, fmt);
-    const size_t need = fused ? 0 : align_up((size_t)(M * K * 2), 256);
+    // not fused: the scaled activations, then the product's own workspace
+    const size_t xbytes = align_up((size_t)(M * K * 2), 256);
+    const size_t need = fused ? 0 : xbytes + gemm_need(M, N, K, group);
     if (need > 0) {
         if (!workspace || workspace_bytes < need) return W4A16_ERR_WORKSPACE;
         if (!aligned16(workspace)) return W4A16_ERR_INVALID_ARG;
@@ -498,7 +518,8 @@ w4a16_status w4a16_linear_awq(const void *x, int32_t dtype, const float *act_mul
     }
     hipError_t e = launch_scale_activations(x, dtype == W4A16_BF16, act_mul, workspace, M, (int)K, s);
     if (e != hipSuccess) return W4A16_ERR_HIP;
-    return w4a16_gemm_fmt(workspace, dtype, qweight, scales, zeros, y, M, N, K, group, fmt, nullptr, 0, stream);
+    return w4a16_gemm_fmt(workspace, dtype, qweight, scales, zeros, y, M, N, K, group, fmt,
+                          static_cast<char *>(workspace) + xbytes, workspace_bytes - xbytes, stream);
 }
 
 }  // extern "C"

@@ -41,12 +41,15 @@ GemmPlan gemm_plan(int64_t M, int64_t N, int64_t K, int32_t group) {
     }
     p.kind = 1;
     p.tile = prefill_tile(M, N);
+    prefill_stream_k(M, N, K, device_cu_count(), p);
     return p;
 }
 
 hipError_t launch_gemm(const void *x, bool bf16, const void *qweight, const void *scales, const void *zeros,
-                       void *y, int M, int N, int K, int group, int fmt, const GemmPlan &plan, hipStream_t stream) {
-    if (plan.kind != 0) return launch_prefill(x, bf16, qweight, scales, zeros, y, M, N, K, group, fmt, plan, stream);
+                       void *y, int M, int N, int K, int group, int fmt, const GemmPlan &plan, void *workspace,
+                       hipStream_t stream) {
+    if (plan.kind != 0)
+        return launch_prefill(x, bf16, qweight, scales, zeros, y, M, N, K, group, fmt, plan, workspace, stream);
     switch (fmt) {
         case kSym4: return launch_skinny_fmt<kSym4>(x, bf16, qweight, scales, zeros, y, M, N, K, group, plan, stream);
         case kSym8: return launch_skinny_fmt<kSym8>(x, bf16, qweight, scales, zeros, y, M, N, K, group, plan, stream);

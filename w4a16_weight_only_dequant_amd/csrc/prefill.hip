@@ -34,17 +34,57 @@ int prefill_tile(int64_t M, int64_t N) {
     return best;
 }
 
+// Stream-K: with T columns per tile and `tiles` tiles on `cus` compute units,
+// whole-tile scheduling takes ceil(tiles / cus) rounds where tiles / cus would
+// do. When the last round is at most half full, the tiles of the last two
+// rounds are split by columns over exactly `cus` workgroups (each then gets
+// at least one tile's worth, so a tile is shared by at most two of them); the
+// earlier rounds stay whole tiles. Every piece of a split tile costs about
+// what a whole tile's start and end cost (measured ~10 us at K = 5120), so a
+// fuller last round gains nothing (432 tiles of 256 x 256 on 256 CUs:
+// 283 us either way; 264 tiles: 266 -> 185 us). Needs at least 4 columns per
+// tile, so that a split tile still has a head and a tail of some length.
+void prefill_stream_k(int64_t M, int64_t N, int64_t K, int cus, GemmPlan &plan) {
+    static const int enabled = [] {
+        const char *v = getenv("W4A16_PREFILL_SK");
+        return v ? atoi(v) : 1;
+    }();
+    plan.dp_tiles = 0;
+    plan.sk_wgs = 0;
+    const int64_t tiles = ceil_div(M, tile_rows(plan.tile)) * ceil_div(N, kTileCols);
+    const int64_t T = ceil_div(K / kChunk, kColChunks);
+    if (!enabled || cus < 8 || T < 4 || tiles <= cus) return;
+    const int64_t rounds = ceil_div(tiles, cus);
+    const int64_t last = tiles - (rounds - 1) * cus;   // tiles of the last round
+    if (2 * last > cus) return;
+    plan.dp_tiles = (int)((rounds - 2) * cus);
+    plan.sk_wgs = cus;
+}
+
+unsigned long long next_sk_token() {
+    static std::atomic<unsigned long long> counter{0};
+    return counter.fetch_add(1, std::memory_order_relaxed) + 1;
+}
+
+size_t prefill_workspace_bytes(const GemmPlan &plan) {
+    if (plan.kind != 1 || plan.sk_wgs == 0) return 0;
+    const size_t part = (size_t)plan.sk_wgs * tile_rows(plan.tile) * kTileCols * sizeof(float);
+    return part + align_up((size_t)plan.sk_wgs * 8, 256);
+}
+
 hipError_t launch_prefill(const void *x, bool bf16, const void *qweight, const void *scales, const void *zeros,
-                          void *y, int M, int N, int K, int group, int fmt, const GemmPlan &plan, hipStream_t stream) {
+                          void *y, int M, int N, int K, int group, int fmt, const GemmPlan &plan, void *workspace,
+                          hipStream_t stream) {
+    void *ws = workspace;
     switch (fmt) {
-        case kSym4: return launch_prefill_fmt<kSym4>(x, bf16, qweight, scales, zeros, y, M, N, K, group, plan, stream);
-        case kSym8: return launch_prefill_fmt<kSym8>(x, bf16, qweight, scales, zeros, y, M, N, K, group, plan, stream);
-        case kKq4: return launch_prefill_fmt<kKq4>(x, bf16, qweight, scales, zeros, y, M, N, K, group, plan, stream);
-        default: return launch_prefill_fmt<kAsym4>(x, bf16, qweight, scales, zeros, y, M, N, K, group, plan, stream);
+        case kSym4: return launch_prefill_fmt<kSym4>(x, bf16, qweight, scales, zeros, y, M, N, K, group, plan, ws, stream);
+        case kSym8: return launch_prefill_fmt<kSym8>(x, bf16, qweight, scales, zeros, y, M, N, K, group, plan, ws, stream);
+        case kKq4: return launch_prefill_fmt<kKq4>(x, bf16, qweight, scales, zeros, y, M, N, K, group, plan, ws, stream);
+        default: return launch_prefill_fmt<kAsym4>(x, bf16, qweight, scales, zeros, y, M, N, K, group, plan, ws, stream);
     }
 }
 
 template hipError_t launch_prefill_fmt<kAsym4>(const void *, bool, const void *, const void *, const void *, void *,
-                                               int, int, int, int, const GemmPlan &, hipStream_t);
+                                               int, int, int, int, const GemmPlan &, void *, hipStream_t);
 
 }  // namespace w4a16

@@ -143,7 +143,8 @@ template <int BM, int BN, int WM, int WN, int GROUP, bool BF, int FMT>
 __global__ __launch_bounds__(64 * WM * WN) __attribute__((amdgpu_waves_per_eu(WM * WN / 4, WM * WN / 4))) void prefill_kernel(
     const uint16_t *__restrict__ x, const uint4 *__restrict__ qw, const uint4 *__restrict__ qw_hi,
     const uint16_t *__restrict__ scales, const uint32_t *__restrict__ zeros, uint16_t *__restrict__ y, int M,
-    int N, int K, int m_tiles, int n_tiles, int mshift) {
+    int N, int K, int m_tiles, int n_tiles, int mshift, int dp_tiles, int sk_wgs, float4 *__restrict__ partials,
+    unsigned long long *__restrict__ flags, unsigned long long token) {
     using FT = FormatTraits<FMT>;
     constexpr int NT = 64 * WM * WN;                 // threads
     constexpr int TM = BM / WM / 32, TN = BN / WN / 32;   // 32x32 blocks per wave
@@ -155,33 +156,98 @@ __global__ __launch_bounds__(64 * WM * WN) __attribute__((amdgpu_waves_per_eu(WM
     static_assert(RB * 64 % NT == 0 && BM * kUnits % NT == 0, "tile / thread mismatch");
 
     extern __shared__ __align__(16) unsigned char smem[];
-    uint4 *xs = reinterpret_cast<uint4 *>(smem);                        // [2][BM][8]
-    uint4 *ws = reinterpret_cast<uint4 *>(smem) + 2 * BM * kUnits;      // [2][BN][8]
 
-    const int tid = threadIdx.x;
-    const int lane = tid & 63;
-    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int wave = __builtin_amdgcn_readfirstlane((int)threadIdx.x >> 6);
     const int wm = wave / WN, wn = wave % WN;
-
-    // tile index; consecutive ids walk M first, so the M tiles that share a
-    // weight tile run side by side. Workgroups are dealt to the eight XCDs
-    // round-robin: remap so each XCD gets a contiguous range of ids (and
-    // keeps the shared weight tile in its own L2).
-    const int tiles = m_tiles * n_tiles;
-    int id = blockIdx.x;
-    if (tiles % 8 == 0) id = (id % 8) * (tiles / 8) + id / 8;
-    const int mt = id % m_tiles, nt = id / m_tiles;
-    const int m0 = mt * BM, n0 = nt * BN;
 
     const int C = K / kChunk;
     const int T = (C + kColChunks - 1) / kColChunks;
     const int steps = (C + 1) / 2;                   // 64-k steps (the last may hold one chunk)
     const int nblocks = (N + kRowBlock - 1) / kRowBlock;
+    const int t_full = C / kColChunks;               // columns with all four chunks
+
+    // ---- schedule. Tile ids walk M first, so the M tiles that share a
+    // weight tile run side by side. Workgroups are dealt to the eight XCDs
+    // round-robin: ids are remapped so each XCD gets a contiguous range (and
+    // keeps the shared weight tiles in its own L2).
+    // Workgroups below dp_tiles compute one whole tile each. The other sk_wgs
+    // workgroups (stream-K) split the remaining tiles' columns evenly: workgroup
+    // s takes units [s U / sk_wgs, (s+1) U / sk_wgs) of the U = tiles x T
+    // (tile, column) units, at least T of them, so it touches at most three
+    // tiles and a tile is shared by at most two workgroups. It runs its whole
+    // tiles first, then the head (first columns) of its last tile, whose fp32
+    // partial it leaves in `partials` slot s and announces with flags[s] =
+    // token, and last the tail of its first tile, which it finishes with the
+    // partial of workgroup s - 1. A workgroup waits only after producing, and
+    // only for a lower s (dispatched earlier except across an XCD's range
+    // boundary, where the producer never waits before producing), so every
+    // wait ends. The partial is added after the workgroup's own columns, always
+    // in this order, so results do not depend on timing.
+    const int tiles = m_tiles * n_tiles;
+    int ft, lt, fb, le, s_sk = -1;   // first / last tile, first column of the first, end column of the last
+    if ((int)blockIdx.x < dp_tiles) {
+        int id = blockIdx.x;
+        if (dp_tiles % 8 == 0) id = (id % 8) * (dp_tiles / 8) + id / 8;
+        ft = lt = id;
+        fb = 0;
+        le = T;
+    } else {
+        const int b = blockIdx.x - dp_tiles;
+        s_sk = (sk_wgs % 8 == 0) ? (b % 8) * (sk_wgs / 8) + b / 8 : b;
+        const int64_t U = (int64_t)(tiles - dp_tiles) * T;
+        const int64_t lo = (int64_t)s_sk * U / sk_wgs, hi = (int64_t)(s_sk + 1) * U / sk_wgs;
+        ft = (int)(lo / T);
+        lt = (int)((hi - 1) / T);
+        fb = (int)(lo - (int64_t)ft * T);
+        le = (int)(hi - (int64_t)lt * T);
+        ft += dp_tiles;
+        lt += dp_tiles;
+    }
+    // (uniform: keep the schedule in scalar registers)
+    ft = __builtin_amdgcn_readfirstlane(ft);
+    lt = __builtin_amdgcn_readfirstlane(lt);
+    fb = __builtin_amdgcn_readfirstlane(fb);
+    le = __builtin_amdgcn_readfirstlane(le);
+    s_sk = __builtin_amdgcn_readfirstlane(s_sk);
+    const int full_lo = fb == 0 ? ft : ft + 1;     // whole tiles full_lo..full_hi
+    const int full_hi = le == T ? lt : lt - 1;
+    const int n_full = max(0, full_hi - full_lo + 1);
+    const bool has_head = le < T, has_tail = fb > 0;
+    const int n_seg = n_full + (has_head ? 1 : 0) + (has_tail ? 1 : 0);
+
+    const uint32_t zstep = (uint32_t)(N * GPC / 8);
+    const ColScales<GPC> *scol = reinterpret_cast<const ColScales<GPC> *>(scales);
+    const uint4 *kqrec = reinterpret_cast<const uint4 *>(scales);
+    const UnpackConsts uc = unpack_consts();
+    const uint4 *xg = reinterpret_cast<const uint4 *>(x);
+    const int k8_total = K / 8;
+    // LDS: activations [2][BM][8] then weights [2][BN][8] (16-byte units, two buffers)
+    uint4 *xs0 = reinterpret_cast<uint4 *>(smem), *xs1 = xs0 + BM * kUnits;
+    uint4 *ws0 = xs0 + 2 * BM * kUnits, *ws1 = ws0 + BN * kUnits;
+
+    for (int seg = 0; seg < n_seg; ++seg) {
+    // segment seg: a whole tile, the head [0, le) of tile lt, or the tail
+    // [fb, T) of tile ft
+    const int kind = __builtin_amdgcn_readfirstlane(seg < n_full ? 0 : ((seg == n_full && has_head) ? 1 : 2));
+    const int id = __builtin_amdgcn_readfirstlane(kind == 0 ? full_lo + seg : (kind == 1 ? lt : ft));
+    const int tb = kind == 2 ? fb : 0, te = kind == 1 ? le : T;
+    const int mt = __builtin_amdgcn_readfirstlane(id % m_tiles), nt = __builtin_amdgcn_readfirstlane(id / m_tiles);
+    const int m0 = mt * BM, n0 = nt * BN;
+    if (seg > 0) __syncthreads();   // the previous segment's last reads of both LDS buffers are done
+    // The thread's per-segment values (offsets, LDS addresses) derive from a
+    // copy of its index that the compiler cannot see through, so they are
+    // computed per segment instead of being hoisted out of the segment loop
+    // and kept live (spilled) through the hand-over code.
+    int tid_v = (int)threadIdx.x;
+    asm volatile("" : "+v"(tid_v));
+    const int tid = tid_v;
+    const int lane = tid & 63;
+    const int d = lane >> 4, r = lane & 15;
+    const int xu = tid % kUnits;
 
     // ---- weight records of this thread: row block i * waves + wave of the
     // tile, record = lane (d = lane / 16, r = lane % 16: dword d of the
     // column's four chunks of row r). Offsets are 32-bit element indices.
-    const int d = lane >> 4, r = lane & 15;
     uint32_t woff[WREC], wstep[WREC], soff[WREC], zoff[WREC];
     int zshift[WREC], wrow[WREC], wrows[WREC];
 #pragma unroll
@@ -199,9 +265,6 @@ __global__ __launch_bounds__(64 * WM * WN) __attribute__((amdgpu_waves_per_eu(WM
         zshift[i] = 4 * ((n * GPC) % 8);
         wrow[i] = rb * kRowBlock + r;                                             // LDS row
     }
-    const uint32_t zstep = (uint32_t)(N * GPC / 8);
-    const ColScales<GPC> *scol = reinterpret_cast<const ColScales<GPC> *>(scales);
-    const int t_full = C / kColChunks;   // columns with all four chunks
     struct WCol {
         uint4 rec[WREC], rec_hi[WREC];   // rec_hi: high-nibble plane of 8-bit codes
         uint4 kq[WREC];                  // kq4: the super-block record of the column's row
@@ -209,7 +272,6 @@ __global__ __launch_bounds__(64 * WM * WN) __attribute__((amdgpu_waves_per_eu(WM
         uint32_t zw[WREC];
         int par;                         // kq4: column parity (half of the super-block)
     };
-    const uint4 *kqrec = reinterpret_cast<const uint4 *>(scales);
     auto load_wcol = [&](int t, WCol &u) __attribute__((always_inline)) {
         u.par = t & 1;
 #pragma unroll
@@ -247,7 +309,6 @@ __global__ __launch_bounds__(64 * WM * WN) __attribute__((amdgpu_waves_per_eu(WM
     };
     // dequantise half h (chunks 2h, 2h+1) of weight record i into LDS;
     // chunks past K (partial last column) have zero codes and zero scale
-    const UnpackConsts uc = unpack_consts();
     auto store_w_rec = [&](const WCol &u, int i, int h, uint4 *wbuf) __attribute__((always_inline)) {
 #pragma unroll
         for (int jj = 0; jj < 2; ++jj) {
@@ -275,15 +336,12 @@ __global__ __launch_bounds__(64 * WM * WN) __attribute__((amdgpu_waves_per_eu(WM
 
     // ---- activation units of this thread: tile row (i * NT + tid) / 8, unit
     // tid % 8 of the step; units past K read as zero
-    const uint4 *xg = reinterpret_cast<const uint4 *>(x);
-    const int xu = tid % kUnits;
     uint32_t xoff[XREC];
 #pragma unroll
     for (int i = 0; i < XREC; ++i) {
         const int row = (i * NT + tid) / kUnits;
         xoff[i] = (uint32_t)min(m0 + row, M - 1) * (uint32_t)(K / 8) + (uint32_t)xu;   // rows past M repeat the last
     }
-    const int k8_total = K / 8;
     // Steps that may reach past K (the partial last column) zero those units:
     // the address is clamped into the row and the value masked, so the load
     // stays unconditional (no branch splits the interleaved step).
@@ -350,22 +408,22 @@ __global__ __launch_bounds__(64 * WM * WN) __attribute__((amdgpu_waves_per_eu(WM
         }
     };
 
-    // ---- main loop over the full columns: iteration t multiplies steps 2t
-    // (buffer 0) and 2t+1 (buffer 1) and writes steps 2t+1 and 2t+2. Loads
-    // past the end of K are clamped to valid addresses; what they bring is
-    // written into a buffer that is never multiplied.
-    uint4 *xs0 = xs, *xs1 = xs + BM * kUnits, *ws0 = ws, *ws1 = ws + BN * kUnits;
+    // ---- main loop over the segment's full columns [tb, te): iteration t
+    // multiplies steps 2t (buffer 0) and 2t+1 (buffer 1) and writes steps
+    // 2t+1 and 2t+2. Loads past the end of the segment or of K are clamped to
+    // valid addresses; what they bring is written into a buffer that is never
+    // multiplied.
     WCol wcur, wnext;
-    load_wcol(0, wcur);
+    load_wcol(tb, wcur);
 #pragma unroll
-    for (int i = 0; i < XREC; ++i) xv[i] = load_x_unit(i, 0, kMasked);
-    load_wcol(min(1, T - 1), wnext);
+    for (int i = 0; i < XREC; ++i) xv[i] = load_x_unit(i, 2 * tb, kMasked);
+    load_wcol(min(tb + 1, T - 1), wnext);
 #pragma unroll
     for (int i = 0; i < WREC; ++i) store_w_rec(wcur, i, 0, ws0);
 #pragma unroll
     for (int i = 0; i < XREC; ++i) {
         xs0[swz((i * NT + tid) / kUnits, xu)] = xv[i];
-        xv[i] = load_x_unit(i, min(1, steps - 1), kMasked);
+        xv[i] = load_x_unit(i, min(2 * tb + 1, steps - 1), kMasked);
     }
     __syncthreads();
     // (the activation loads of the last full column reach the steps after it:
@@ -378,11 +436,13 @@ __global__ __launch_bounds__(64 * WM * WN) __attribute__((amdgpu_waves_per_eu(WM
         step(xs1, ws1, wcur, 0, ws0, xs0, min(2 * t + 3, steps - 1), masked);
         __syncthreads();
     };
-    for (int t = 0; t + 1 < t_full; ++t) column(t, kPlain);
-    if (t_full > 0) column(t_full - 1, kMasked);
-    // the partial last column (K % 128 != 0): one or two more steps; its
-    // missing chunks have zero codes and zero activations
-    if (t_full < T) {
+    const int te_full = min(te, t_full);
+    for (int t = tb; t + 1 < te_full; ++t) column(t, kPlain);
+    if (te_full > tb) column(te_full - 1, kMasked);
+    // the partial last column (K % 128 != 0; only a segment that ends the
+    // tile's K has it): one or two more steps; its missing chunks have zero
+    // codes and zero activations
+    if (te == T && t_full < T) {
         const int s0 = 2 * t_full;
         const bool two = s0 + 1 < steps;
         step(xs0, ws0, wcur, 1, ws1, xs1, min(s0 + 2, steps - 1), kMasked);
@@ -390,47 +450,148 @@ __global__ __launch_bounds__(64 * WM * WN) __attribute__((amdgpu_waves_per_eu(WM
         if (two) step(xs1, ws1, wcur, 0, ws0, xs0, min(s0 + 2, steps - 1), kMasked);
     }
 
-    // ---- epilogue: lane holds rows (v/4)*8 + (lane/32)*4 + v%4 of column lane%32
+    // ---- stream-K hand-over. Partial slots hold each thread's accumulators
+    // as float4 [TM][TN][4][NT] (coalesced; producer and consumer run the same
+    // tile shape, so thread tid reads back exactly what thread tid wrote).
+    constexpr int kPart = TM * TN * 4;   // float4 per thread
+    if (kind == 1) {
+        float4 *slot = partials + (size_t)s_sk * kPart * NT;
+#pragma unroll
+        for (int a = 0; a < TM; ++a)
+#pragma unroll
+            for (int b = 0; b < TN; ++b)
+#pragma unroll
+                for (int q = 0; q < 4; ++q)
+                    slot[((a * TN + b) * 4 + q) * NT + tid] =
+                        make_float4(acc[a][b][4 * q], acc[a][b][4 * q + 1], acc[a][b][4 * q + 2], acc[a][b][4 * q + 3]);
+        // every wave waits until its stores have reached the L2 (vmcnt(0));
+        // after the barrier one write-back of the L2 (the agent-scope release
+        // of thread 0) makes the whole partial visible to the other XCDs
+        // before the flag, itself a device-coherent store
+        __builtin_amdgcn_s_waitcnt(0x0F70);
+        __syncthreads();
+        if (tid == 0) {
+            __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
+            __hip_atomic_store(&flags[s_sk], token, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        }
+        continue;
+    }
+    if (kind == 2) {
+        if (tid == 0) {
+            // bounded wait (about a second): the producer never waits before
+            // producing, so this ends; the bound only keeps a broken launch
+            // from holding the device. Relaxed polls (device-coherent loads);
+            // the acquire below then orders the partial's loads after them.
+            for (int spin = 0; spin < (1 << 21); ++spin) {
+                if (__hip_atomic_load(&flags[s_sk - 1], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == token) break;
+                __builtin_amdgcn_s_sleep(2);
+            }
+            // invalidates this CU's L1 and this XCD's L2, which all waves of
+            // the workgroup read through: no stale line of the partial is left
+            __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+        }
+        __syncthreads();
+        const float4 *slot = partials + (size_t)(s_sk - 1) * kPart * NT;
+        // one 32x32 block at a time (the scheduling barrier keeps the loads of
+        // all blocks from being hoisted together, which would need another
+        // accumulator's worth of registers)
+#pragma unroll
+        for (int a = 0; a < TM; ++a)
+#pragma unroll
+            for (int b = 0; b < TN; ++b) {
+                float4 p[4];
+#pragma unroll
+                for (int q = 0; q < 4; ++q) p[q] = slot[((a * TN + b) * 4 + q) * NT + tid];
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    acc[a][b][4 * q] += p[q].x;
+                    acc[a][b][4 * q + 1] += p[q].y;
+                    acc[a][b][4 * q + 2] += p[q].z;
+                    acc[a][b][4 * q + 3] += p[q].w;
+                }
+                __builtin_amdgcn_sched_barrier(0);
+            }
+        // the flag of this launch is consumed: clear it, so a replay of the
+        // same launch (same token, e.g. from a graph) waits again
+        if (tid == 0) __hip_atomic_store(&flags[s_sk - 1], 0ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+
+    // ---- epilogue: lane holds rows (v/4)*8 + (lane/32)*4 + v%4 of column
+    // lane%32 of each 32x32 block (a store instruction covers two 64-byte
+    // runs of two rows; measured faster than the transposed layout's 8-byte
+    // stores over 32 rows). Tiles inside the matrix store without per-element
+    // checks (a branch per element splits the accumulators' live ranges and
+    // spills them).
+    const bool inside = m0 + BM <= M && n0 + BN <= N;
 #pragma unroll
     for (int a = 0; a < TM; ++a)
 #pragma unroll
         for (int b = 0; b < TN; ++b) {
             const int n = n0 + wn * (BN / WN) + 32 * b + (lane & 31);
-            if (n >= N) continue;
+            const int mb = m0 + wm * (BM / WM) + 32 * a + (lane >> 5) * 4;
+            uint16_t *yb = y + (int64_t)mb * N + n;
+            if (inside) {
 #pragma unroll
-            for (int v = 0; v < 16; ++v) {
-                const int m = m0 + wm * (BM / WM) + 32 * a + (v / 4) * 8 + (lane >> 5) * 4 + (v % 4);
-                if (m < M)
-                    y[(int64_t)m * N + n] = BF ? f32_to_bf16_bits(acc[a][b][v]) : f32_to_f16_bits(acc[a][b][v]);
+                for (int v = 0; v < 16; ++v)
+                    yb[(int64_t)((v / 4) * 8 + (v % 4)) * N] =
+                        BF ? f32_to_bf16_bits(acc[a][b][v]) : f32_to_f16_bits(acc[a][b][v]);
+            } else if (n < N) {
+#pragma unroll
+                for (int v = 0; v < 16; ++v) {
+                    const int m = mb + (v / 4) * 8 + (v % 4);
+                    if (m < M)
+                        yb[(int64_t)((v / 4) * 8 + (v % 4)) * N] =
+                            BF ? f32_to_bf16_bits(acc[a][b][v]) : f32_to_f16_bits(acc[a][b][v]);
+                }
             }
         }
+    }   // segments
 }
+
+// One tiled launch: dp_tiles whole tiles, then sk_wgs stream-K workgroups
+// (0: every tile whole) with their partials and flags in `ws`.
+struct SkArgs {
+    int dp_tiles, sk_wgs;
+    void *ws;
+};
 
 template <int BM, int BN, int WM, int WN, int GROUP, bool BF, int FMT>
 hipError_t launch_tile(const void *x, const void *qw, const void *qh, const void *sc, const void *zp, void *y, int M,
-                       int N, int K, int ms, hipStream_t stream) {
+                       int N, int K, int ms, const SkArgs &sk, hipStream_t stream) {
+    static_assert(BN == kTileCols, "tile columns");
     auto kern = prefill_kernel<BM, BN, WM, WN, GROUP, BF, FMT>;
     const size_t lds = (size_t)2 * (BM + BN) * kUnits * 16;
     static DynLdsAttr attr;
     hipError_t e = raise_dyn_lds(reinterpret_cast<const void *>(kern), lds, attr);
     if (e != hipSuccess) return e;
     const int m_tiles = (int)ceil_div(M, BM), n_tiles = (int)ceil_div(N, BN);
-    hipLaunchKernelGGL(kern, dim3((unsigned)(m_tiles * n_tiles)), dim3(64 * WM * WN), lds, stream,
+    const int tiles = m_tiles * n_tiles;
+    int dp = tiles, skw = 0;
+    float4 *part = nullptr;
+    unsigned long long *flags = nullptr;
+    if (sk.sk_wgs > 0) {   // the plan guarantees dp_tiles + sk_wgs <= tiles (each share >= one tile)
+        if (sk.ws == nullptr || sk.dp_tiles + sk.sk_wgs > tiles) return hipErrorInvalidValue;
+        dp = sk.dp_tiles;
+        skw = sk.sk_wgs;
+        part = reinterpret_cast<float4 *>(sk.ws);
+        flags = reinterpret_cast<unsigned long long *>(static_cast<char *>(sk.ws) + (size_t)skw * BM * BN * 4);
+    }
+    hipLaunchKernelGGL(kern, dim3((unsigned)(dp + skw)), dim3(64 * WM * WN), lds, stream,
                        reinterpret_cast<const uint16_t *>(x), reinterpret_cast<const uint4 *>(qw),
                        reinterpret_cast<const uint4 *>(qh), reinterpret_cast<const uint16_t *>(sc),
                        reinterpret_cast<const uint32_t *>(zp), reinterpret_cast<uint16_t *>(y), M, N, K, m_tiles,
-                       n_tiles, ms);
+                       n_tiles, ms, dp, skw, part, flags, skw > 0 ? next_sk_token() : 0ull);
     return hipGetLastError();
 }
 
 template <int GROUP, bool BF, int FMT>
 hipError_t launch_group(int tile, const void *x, const void *qw, const void *qh, const void *sc, const void *zp,
-                        void *y, int M, int N, int K, int ms, hipStream_t stream) {
+                        void *y, int M, int N, int K, int ms, const SkArgs &sk, hipStream_t stream) {
     switch (tile) {
-        case kTile64x256: return launch_tile<64, 256, 1, 4, GROUP, BF, FMT>(x, qw, qh, sc, zp, y, M, N, K, ms, stream);
-        case kTile128x256: return launch_tile<128, 256, 2, 2, GROUP, BF, FMT>(x, qw, qh, sc, zp, y, M, N, K, ms, stream);
-        case kTile256x256w8: return launch_tile<256, 256, 2, 4, GROUP, BF, FMT>(x, qw, qh, sc, zp, y, M, N, K, ms, stream);
-        default: return launch_tile<256, 256, 2, 2, GROUP, BF, FMT>(x, qw, qh, sc, zp, y, M, N, K, ms, stream);
+        case kTile64x256: return launch_tile<64, 256, 1, 4, GROUP, BF, FMT>(x, qw, qh, sc, zp, y, M, N, K, ms, sk, stream);
+        case kTile128x256: return launch_tile<128, 256, 2, 2, GROUP, BF, FMT>(x, qw, qh, sc, zp, y, M, N, K, ms, sk, stream);
+        case kTile256x256w8: return launch_tile<256, 256, 2, 4, GROUP, BF, FMT>(x, qw, qh, sc, zp, y, M, N, K, ms, sk, stream);
+        default: return launch_tile<256, 256, 2, 2, GROUP, BF, FMT>(x, qw, qh, sc, zp, y, M, N, K, ms, sk, stream);
     }
 }
 
@@ -440,27 +601,29 @@ hipError_t launch_group(int tile, const void *x, const void *qw, const void *qh,
 // kernels with one metadata slot per two columns (mshift = 1).
 template <int FMT>
 hipError_t launch_prefill_fmt(const void *x, bool bf16, const void *qweight, const void *scales, const void *zeros,
-                              void *y, int M, int N, int K, int group, const GemmPlan &plan, hipStream_t stream) {
+                              void *y, int M, int N, int K, int group, const GemmPlan &plan, void *workspace,
+                              hipStream_t stream) {
+    const SkArgs sk{plan.dp_tiles, plan.sk_wgs, workspace};
     const int ms = group == 256 ? 1 : 0;
     const void *qh = FormatTraits<FMT>::two_planes
                          ? static_cast<const void *>(static_cast<const char *>(qweight) + (size_t)N * K / 2)
                          : qweight;
     const int t = plan.tile;
     if constexpr (FormatTraits<FMT>::kquant) {   // one 32-weight sub-block per chunk
-        return bf16 ? launch_group<32, true, FMT>(t, x, qweight, qh, scales, zeros, y, M, N, K, 0, stream)
-                    : launch_group<32, false, FMT>(t, x, qweight, qh, scales, zeros, y, M, N, K, 0, stream);
+        return bf16 ? launch_group<32, true, FMT>(t, x, qweight, qh, scales, zeros, y, M, N, K, 0, sk, stream)
+                    : launch_group<32, false, FMT>(t, x, qweight, qh, scales, zeros, y, M, N, K, 0, sk, stream);
     } else {
     if (bf16) {
         switch (group) {
-            case 32: return launch_group<32, true, FMT>(t, x, qweight, qh, scales, zeros, y, M, N, K, ms, stream);
-            case 64: return launch_group<64, true, FMT>(t, x, qweight, qh, scales, zeros, y, M, N, K, ms, stream);
-            default: return launch_group<128, true, FMT>(t, x, qweight, qh, scales, zeros, y, M, N, K, ms, stream);
+            case 32: return launch_group<32, true, FMT>(t, x, qweight, qh, scales, zeros, y, M, N, K, ms, sk, stream);
+            case 64: return launch_group<64, true, FMT>(t, x, qweight, qh, scales, zeros, y, M, N, K, ms, sk, stream);
+            default: return launch_group<128, true, FMT>(t, x, qweight, qh, scales, zeros, y, M, N, K, ms, sk, stream);
         }
     }
     switch (group) {
-        case 32: return launch_group<32, false, FMT>(t, x, qweight, qh, scales, zeros, y, M, N, K, ms, stream);
-        case 64: return launch_group<64, false, FMT>(t, x, qweight, qh, scales, zeros, y, M, N, K, ms, stream);
-        default: return launch_group<128, false, FMT>(t, x, qweight, qh, scales, zeros, y, M, N, K, ms, stream);
+        case 32: return launch_group<32, false, FMT>(t, x, qweight, qh, scales, zeros, y, M, N, K, ms, sk, stream);
+        case 64: return launch_group<64, false, FMT>(t, x, qweight, qh, scales, zeros, y, M, N, K, ms, sk, stream);
+        default: return launch_group<128, false, FMT>(t, x, qweight, qh, scales, zeros, y, M, N, K, ms, sk, stream);
     }    }
 }
 

@@ -4,6 +4,6 @@
 namespace w4a16 {
 
 template hipError_t launch_prefill_fmt<kSym4>(const void *, bool, const void *, const void *, const void *, void *,
-                                             int, int, int, int, const GemmPlan &, hipStream_t);
+                                             int, int, int, int, const GemmPlan &, void *, hipStream_t);
 
 }  // namespace w4a16

@@ -92,9 +92,26 @@ struct GemmPlan {
     int waves;         // skinny: waves per workgroup (split K)
     int rows_per_wg;   // skinny: 16-row blocks per workgroup (1, 2, 4)
     int tile;          // tiled: one of kTile*
+    int dp_tiles;      // tiled, stream-K: tiles computed whole, one workgroup each
+    int sk_wgs;        // tiled, stream-K: workgroups sharing the other tiles' columns (0: none)
 };
 
 GemmPlan gemm_plan(int64_t M, int64_t N, int64_t K, int32_t group);
+// Compute units of the current device (cached per device; 0 if unknown).
+int device_cu_count();
+// Tile rows / columns of a tiled kind.
+inline int tile_rows(int tile) { return tile == kTile64x256 ? 64 : (tile == kTile128x256 ? 128 : 256); }
+constexpr int kTileCols = 256;
+// Stream-K split of the tiled GEMM for this shape on `cus` compute units
+// (fills plan.dp_tiles / plan.sk_wgs), and the workspace it needs: one fp32
+// partial tile per stream-K workgroup, then one 8-byte flag each.
+void prefill_stream_k(int64_t M, int64_t N, int64_t K, int cus, GemmPlan &plan);
+size_t prefill_workspace_bytes(const GemmPlan &plan);
+// Stream-K hand-over token: unique per launch in this process (never 0), so
+// flags left in a workspace by other launches never match. A replayed graph
+// reuses its token; the consumers clear every flag they used, so a complete
+// launch leaves all flags at 0.
+unsigned long long next_sk_token();
 
 // Problems of one grouped launch (kernel argument, passed by value).
 constexpr int kMaxGroup = 8;
@@ -132,12 +149,14 @@ hipError_t launch_scale_activations(const void *x, bool bf16, const float *act_m
 hipError_t launch_gemv(const void *x, bool bf16, const void *qweight, const void *scales,
                        const void *zeros, void *y, int M, int N, int K, int group, int fmt,
                        const float *act_mul, const GemvPlan &plan, hipStream_t stream);
+// workspace: prefill_workspace_bytes(plan) bytes (the stream-K partials and
+// flags), may be NULL when that is 0
 hipError_t launch_gemm(const void *x, bool bf16, const void *qweight, const void *scales,
                        const void *zeros, void *y, int M, int N, int K, int group, int fmt,
-                       const GemmPlan &plan, hipStream_t stream);
+                       const GemmPlan &plan, void *workspace, hipStream_t stream);
 hipError_t launch_prefill(const void *x, bool bf16, const void *qweight, const void *scales,
                           const void *zeros, void *y, int M, int N, int K, int group, int fmt,
-                          const GemmPlan &plan, hipStream_t stream);
+                          const GemmPlan &plan, void *workspace, hipStream_t stream);
 int prefill_tile(int64_t M, int64_t N);
 
 // The kernels of one format, each compiled in a translation unit of its own.
@@ -146,7 +165,8 @@ int prefill_tile(int64_t M, int64_t N);
 template <int FMT>
 hipError_t launch_gemv_fmt(W4A16_LINEAR_PARAMS, const float *act_mul, const GemvPlan &plan, hipStream_t stream);
 template <int FMT> hipError_t launch_skinny_fmt(W4A16_LINEAR_PARAMS, const GemmPlan &plan, hipStream_t stream);
-template <int FMT> hipError_t launch_prefill_fmt(W4A16_LINEAR_PARAMS, const GemmPlan &plan, hipStream_t stream);
+template <int FMT>
+hipError_t launch_prefill_fmt(W4A16_LINEAR_PARAMS, const GemmPlan &plan, void *workspace, hipStream_t stream);
 template <int FMT>
 hipError_t launch_skinny_group_fmt(const GroupTable &tab, bool bf16, int M, int K, int group, const GemmPlan &plan,
                                    hipStream_t stream);
@@ -154,7 +174,7 @@ hipError_t launch_skinny_group_fmt(const GroupTable &tab, bool bf16, int M, int 
     extern template hipError_t launch_gemv_fmt<F>(W4A16_LINEAR_PARAMS, const float *, const GemvPlan &,  \
                                                   hipStream_t);                                         \
     extern template hipError_t launch_skinny_fmt<F>(W4A16_LINEAR_PARAMS, const GemmPlan &, hipStream_t); \
-    extern template hipError_t launch_prefill_fmt<F>(W4A16_LINEAR_PARAMS, const GemmPlan &, hipStream_t); \
+    extern template hipError_t launch_prefill_fmt<F>(W4A16_LINEAR_PARAMS, const GemmPlan &, void *, hipStream_t); \
     extern template hipError_t launch_skinny_group_fmt<F>(const GroupTable &, bool, int, int, int,        \
                                                           const GemmPlan &, hipStream_t);
 W4A16_EXTERN_FMT(kAsym4)
