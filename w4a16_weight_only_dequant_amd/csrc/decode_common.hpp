@@ -79,6 +79,34 @@ __device__ inline KqParams kq_params(const uint4 &rec, int jj) {
     return KqParams{d * (float)sc, dm * (float)mq};
 }
 
+// The same for the four sub-blocks of one half (upper: sub-blocks 4-7) of a
+// record, for kernels that take all four at once (the decode GEMV): their
+// fields sit in bits 0-23 of a 32-bit window of each 48-bit field (the upper
+// half's window 24 bits up), so one funnel shift per field and one bit-field
+// extract per sub-block replace the 64-bit shifts. (Kernels that take one
+// sub-block at a time keep kq_params: there the two windows' selects cost
+// registers.)
+struct KqHalf {
+    float d, dm;
+    uint32_t scw, mqw;
+};
+__device__ inline KqHalf kq_half(const uint4 &rec, bool upper) {
+    KqHalf h;
+    h.d = (float)__builtin_bit_cast(_Float16, (uint16_t)(rec.x & 0xFFFFu));
+    h.dm = (float)__builtin_bit_cast(_Float16, (uint16_t)(rec.x >> 16));
+    // scale field: rec.y | rec.z[15:0] << 32; minimum field: rec.z[31:16] | rec.w << 16
+    // (a funnel shift by 0 returns the low word: no select for the scales)
+    h.scw = __builtin_amdgcn_alignbit(rec.z, rec.y, upper ? 24u : 0u);
+    const uint32_t mlo = __builtin_amdgcn_alignbit(rec.w, rec.z, 16), mhi = rec.w >> 8;
+    h.mqw = upper ? mhi : mlo;
+    return h;
+}
+__device__ inline KqParams kq_sub(const KqHalf &h, int j) {
+    const uint32_t sc = (h.scw >> (6 * j)) & 63u;
+    const uint32_t mq = (h.mqw >> (6 * j)) & 63u;
+    return KqParams{h.d * (float)sc, h.dm * (float)mq};
+}
+
 // One dword (8 codes of one k-slice, even k in the low half-word) -> four
 // fp16 pairs (k0,k1) (k2,k3) (k4,k5) (k6,k7) holding q - z exactly.
 // (d & 0x000F000F) | 0x64006400 is (1024+q0, 1024+q1); (d & 0x00F000F0) |
@@ -124,6 +152,15 @@ __device__ inline void unpack_f16_s8(uint32_t dl, uint32_t dh, const UnpackConst
     t[1] = odd(dl, dh);
     t[2] = even(dl8, dh8);
     t[3] = odd(dl8, dh8);
+}
+
+// One dword -> four fp16 pairs holding 1024 + q (exact), in the pair order of
+// unpack_f16: (k0,k1) (k2,k3) (k4,k5) (k6,k7); three shifts and four and_or.
+__device__ inline void unpack_f16_magic(uint32_t d, const UnpackConsts &uc, uint32_t (&t)[4]) {
+    t[0] = and_or(d, uc.lo_mask, uc.f16_magic);
+    t[1] = and_or(d >> 4, uc.lo_mask, uc.f16_magic);
+    t[2] = and_or(d >> 8, uc.lo_mask, uc.f16_magic);
+    t[3] = and_or(d >> 12, uc.lo_mask, uc.f16_magic);
 }
 
 // The fp16 operands of one k-slice of a format: exact (code - zero) pairs.

@@ -201,10 +201,11 @@ __device__ __forceinline__ void skinny_body(const uint16_t *__restrict__ x, cons
             for (int i = 0; i < R; ++i) {
                 const uint32_t dk[4] = {u.rec[i].x, u.rec[i].y, u.rec[i].z, u.rec[i].w};
                 f4_t g = {0.0f, 0.0f, 0.0f, 0.0f}, sx = {0.0f, 0.0f, 0.0f, 0.0f};
+                const KqHalf hf = kq_half(u.kq[i], u.par != 0);
 #pragma unroll
                 for (int j = 0; j < kColChunks; ++j) {
                     chunk(u.xa[j], dk[j], 0u, 0u, g, sx);
-                    close_kq(i, kq_params(u.kq[i], (u.par << 2) + j), g, sx);
+                    close_kq(i, kq_sub(hf, j), g, sx);
                 }
             }
             return;

@@ -295,12 +295,14 @@ __global__ __launch_bounds__(64 * kMaxWaves) __attribute__((amdgpu_waves_per_eu(
     };
     // kq4: chunk c is one 32-weight sub-block with its own scale S and
     // minimum M; its contribution is S * sum x q - M * sum x, added to acc
+    // (both types take the magic operands 128 + q / 1024 + q and remove the
+    // offset with the chunk's activation sum, which the minimum needs anyway)
     auto dword_kq = [&](int c, uint32_t d, const KqParams &P) {
         uint32_t w[4];
         if constexpr (BF)
             unpack_bf16_magic(d, uc, w);
         else
-            unpack_f16(d, 0u, uc, w);
+            unpack_f16_magic(d, uc, w);
         const int q = (c - sl.c_lo) * 4 + s;
 #pragma unroll
         for (int m = 0; m < MT; ++m) {
@@ -310,7 +312,7 @@ __global__ __launch_bounds__(64 * kMaxWaves) __attribute__((amdgpu_waves_per_eu(
             t = dot_pair<BF>(w[1], xv.y, t);
             t = dot_pair<BF>(w[2], xv.z, t);
             t = dot_pair<BF>(w[3], xv.w, t);
-            if constexpr (BF) t = fmaf(-128.0f, xs, t);   // the magic operands carry 128 + q
+            t = fmaf(BF ? -128.0f : -1024.0f, xs, t);   // the magic operands carry 128 + q / 1024 + q
             acc[m] = fmaf(P.S, t, fmaf(-P.M, xs, acc[m]));
         }
     };
@@ -318,11 +320,14 @@ __global__ __launch_bounds__(64 * kMaxWaves) __attribute__((amdgpu_waves_per_eu(
         const int t = u.t;
         if constexpr (FT::kquant) {
             const uint32_t dk[4] = {u.rec.x, u.rec.y, u.rec.z, u.rec.w};
+            const KqHalf hf = kq_half(u.kq, (t & 1) != 0);
 #pragma unroll
             for (int j = 0; j < kColChunks; ++j) {
-                KqParams P = kq_params(u.kq, ((t & 1) << 2) + j);
-                P.S *= u.on;
-                P.M *= u.on;
+                KqParams P = kq_sub(hf, j);
+                if constexpr (CPW > 1) {   // (one column per wave load: every lane is on)
+                    P.S *= u.on;
+                    P.M *= u.on;
+                }
                 dword_kq(t * kColChunks + j, dk[j], P);
             }
             return;

@@ -139,7 +139,10 @@ __device__ inline uint4 dequant_f16(uint32_t d, uint32_t dh, uint32_t z, _Float1
     return make_uint4(o[0], o[1], o[2], o[3]);
 }
 
-template <int BM, int BN, int WM, int WN, int GROUP, bool BF, int FMT>
+// SK: compiled with the stream-K segments; without (every workgroup one whole
+// tile) the segment loop and hand-over code vanish, so the whole-tile
+// launches keep the registers of a plain tiled kernel.
+template <int BM, int BN, int WM, int WN, int GROUP, bool BF, int FMT, bool SK>
 __global__ __launch_bounds__(64 * WM * WN) __attribute__((amdgpu_waves_per_eu(WM * WN / 4, WM * WN / 4))) void prefill_kernel(
     const uint16_t *__restrict__ x, const uint4 *__restrict__ qw, const uint4 *__restrict__ qw_hi,
     const uint16_t *__restrict__ scales, const uint32_t *__restrict__ zeros, uint16_t *__restrict__ y, int M,
@@ -225,7 +228,7 @@ __global__ __launch_bounds__(64 * WM * WN) __attribute__((amdgpu_waves_per_eu(WM
     uint4 *xs0 = reinterpret_cast<uint4 *>(smem), *xs1 = xs0 + BM * kUnits;
     uint4 *ws0 = xs0 + 2 * BM * kUnits, *ws1 = ws0 + BN * kUnits;
 
-    for (int seg = 0; seg < n_seg; ++seg) {
+    for (int seg = 0; seg < (SK ? n_seg : 1); ++seg) {
     // segment seg: a whole tile, the head [0, le) of tile lt, or the tail
     // [fb, T) of tile ft
     const int kind = __builtin_amdgcn_readfirstlane(seg < n_full ? 0 : ((seg == n_full && has_head) ? 1 : 2));
@@ -319,7 +322,7 @@ __global__ __launch_bounds__(64 * WM * WN) __attribute__((amdgpu_waves_per_eu(WM
             if constexpr (FT::has_zeros) z = (u.zw[i] >> (zshift[i] + 4 * e)) & 0xFu;
             uint4 v;
             if constexpr (FT::kquant) {
-                v = dequant_kq<BF>(dw, kq_params(u.kq[i], (u.par << 2) + 2 * h + jj), uc);
+                v = dequant_kq<BF>(dw, kq_sub(kq_half(u.kq[i], u.par != 0), 2 * h + jj), uc);
                 wbuf[swz(wrow[i], 4 * jj + d)] = v;
                 continue;
             }
@@ -454,7 +457,7 @@ __global__ __launch_bounds__(64 * WM * WN) __attribute__((amdgpu_waves_per_eu(WM
     // as float4 [TM][TN][4][NT] (coalesced; producer and consumer run the same
     // tile shape, so thread tid reads back exactly what thread tid wrote).
     constexpr int kPart = TM * TN * 4;   // float4 per thread
-    if (kind == 1) {
+    if (SK && kind == 1) {
         float4 *slot = partials + (size_t)s_sk * kPart * NT;
 #pragma unroll
         for (int a = 0; a < TM; ++a)
@@ -476,7 +479,7 @@ __global__ __launch_bounds__(64 * WM * WN) __attribute__((amdgpu_waves_per_eu(WM
         }
         continue;
     }
-    if (kind == 2) {
+    if (SK && kind == 2) {
         if (tid == 0) {
             // bounded wait (about a second): the producer never waits before
             // producing, so this ends; the bound only keeps a broken launch
@@ -559,10 +562,12 @@ template <int BM, int BN, int WM, int WN, int GROUP, bool BF, int FMT>
 hipError_t launch_tile(const void *x, const void *qw, const void *qh, const void *sc, const void *zp, void *y, int M,
                        int N, int K, int ms, const SkArgs &sk, hipStream_t stream) {
     static_assert(BN == kTileCols, "tile columns");
-    auto kern = prefill_kernel<BM, BN, WM, WN, GROUP, BF, FMT>;
+    const bool split = sk.sk_wgs > 0;
+    auto kern = split ? prefill_kernel<BM, BN, WM, WN, GROUP, BF, FMT, true>
+                      : prefill_kernel<BM, BN, WM, WN, GROUP, BF, FMT, false>;
     const size_t lds = (size_t)2 * (BM + BN) * kUnits * 16;
-    static DynLdsAttr attr;
-    hipError_t e = raise_dyn_lds(reinterpret_cast<const void *>(kern), lds, attr);
+    static DynLdsAttr attr[2];
+    hipError_t e = raise_dyn_lds(reinterpret_cast<const void *>(kern), lds, attr[split ? 1 : 0]);
     if (e != hipSuccess) return e;
     const int m_tiles = (int)ceil_div(M, BM), n_tiles = (int)ceil_div(N, BN);
     const int tiles = m_tiles * n_tiles;
