@@ -59,12 +59,13 @@ FORMAT_LEGS = [("sym4", 128), ("sym8", 128), ("asym4", 256), ("kq4", 256)]
 def parse():
     p = argparse.ArgumentParser()
     p.add_argument("--gpus", type=int, default=1)
-    p.add_argument("--steps", type=int, default=200)
-    p.add_argument("--warmup", type=int, default=20)
+    p.add_argument("--steps", type=int, default=1000)
+    p.add_argument("--warmup", type=int, default=500)
     p.add_argument("--workload", default="decode_13b_layer", choices=list(WORKLOAD_IDS))
     p.add_argument("--m", type=int, default=0, help="batch rows (default: the workload's first M)")
     p.add_argument("--no-prefill", action="store_true", help="skip the M=2048 prefill leg")
-    p.add_argument("--prefill-reps", type=int, default=60)
+    p.add_argument("--prefill-reps", type=int, default=600,
+                   help="prefill launches timed (about 170 ms at M=2048), after a quarter as many untimed")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--no-formats", action="store_true", help="skip the weight-format legs")
     p.add_argument("--cpu-seconds", type=float, default=15.0)
@@ -223,13 +224,17 @@ class Workload:
     def per_kernel_ms(self, reps):
         """Average duration of one launch per matrix: HIP events on the
         replay stream around back-to-back launches (the gap between two
-        dependent launches is included)."""
+        dependent launches is included), after a quarter as many untimed
+        replays: the device's clocks take milliseconds to rise under a new
+        load (M = 2048 prefill: 318 us per launch over the first 7 ms, 280 us
+        sustained)."""
         torch = self.torch
         out = []
         for j in range(len(self.mats)):
             a0 = torch.cuda.Event(enable_timing=True)
             a1 = torch.cuda.Event(enable_timing=True)
-            self.mat_graphs[j].replay()
+            for _ in range(max(1, reps // 4)):
+                self.mat_graphs[j].replay()
             a0.record()
             for _ in range(reps):
                 self.mat_graphs[j].replay()
