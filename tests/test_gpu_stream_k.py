@@ -129,3 +129,26 @@ def test_stream_k_short_workspace_refused():
     st = w4.raw().w4a16_gemm(x.data_ptr(), 0, pw.qweight.data_ptr(), pw.scales.data_ptr(), pw.zeros_ptr(),
                              y.data_ptr(), M, N, K, group, None, 0, None)
     assert st == 4
+
+
+def test_stream_k_through_grouped_and_awq_calls():
+    """The grouped call (large M: one tiled launch per problem, sharing the
+    workspace) and the AWQ path (scaled activations, then the product's own
+    workspace after them) on a split shape match w4a16_gemm bit for bit."""
+    import torch
+    w4 = H.lib()
+    M, K, group = 2048, 512, 128
+    pw_a = _prep(8448, K, group)[2]          # splits (264 tiles)
+    pw_b = H.prepared(("sk-whole", 4096, K, group), lambda: wl.random_weights(41, 4096, K), group)[2]   # whole tiles
+    assert w4.workspace_bytes(M, 8448, K, group) > 0 and w4.workspace_bytes(M, 4096, K, group) == 0
+    x = H.to_device_bits(wl.random_activations(13, M, K, "bf16"), "bf16")
+    ys = w4.linear_group([x, x], [pw_b, pw_a])    # the problem needing a workspace comes second
+    singles = [w4.gemm(x, pw_b), w4.gemm(x, pw_a)]
+    torch.cuda.synchronize()
+    for y, s in zip(ys, singles):
+        assert torch.equal(y.view(torch.int16), s.view(torch.int16))
+    m = torch.full((K,), 0.5, dtype=torch.float32, device="cuda")
+    y_awq = w4.linear_awq(x, m, pw_a)
+    y_pre = w4.gemm(w4.scale_activations(x, m), pw_a)
+    torch.cuda.synchronize()
+    assert torch.equal(y_awq.view(torch.int16), y_pre.view(torch.int16))
