@@ -75,12 +75,13 @@ def parse():
 
 
 def kernel_source_hash(kind):
-    """Hash of the code (comments and blank lines stripped) a kernel is built from."""
+    """Hash of the code a kernel is built from, with comments and all white
+    space removed (edits of comments or layout keep stored counters valid)."""
     h = hashlib.sha256()
     for f in KERNEL_SOURCES[kind]:
         with open(os.path.join(ROOT, "w4a16_weight_only_dequant_amd", "csrc", f)) as fh:
             text = re.sub(r"/\*.*?\*/", "", fh.read(), flags=re.S)
-        lines = [re.sub(r"//.*", "", line).rstrip() for line in text.splitlines()]
+        lines = [re.sub(r"\s+", "", re.sub(r"//.*", "", line)) for line in text.splitlines()]
         h.update("\n".join(line for line in lines if line).encode())
     return h.hexdigest()[:16]
 

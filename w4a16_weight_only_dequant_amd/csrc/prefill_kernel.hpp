@@ -229,325 +229,325 @@ __global__ __launch_bounds__(64 * WM * WN) __attribute__((amdgpu_waves_per_eu(WM
     uint4 *ws0 = xs0 + 2 * BM * kUnits, *ws1 = ws0 + BN * kUnits;
 
     for (int seg = 0; seg < (SK ? n_seg : 1); ++seg) {
-    // segment seg: a whole tile, the head [0, le) of tile lt, or the tail
-    // [fb, T) of tile ft
-    const int kind = __builtin_amdgcn_readfirstlane(seg < n_full ? 0 : ((seg == n_full && has_head) ? 1 : 2));
-    const int id = __builtin_amdgcn_readfirstlane(kind == 0 ? full_lo + seg : (kind == 1 ? lt : ft));
-    const int tb = kind == 2 ? fb : 0, te = kind == 1 ? le : T;
-    const int mt = __builtin_amdgcn_readfirstlane(id % m_tiles), nt = __builtin_amdgcn_readfirstlane(id / m_tiles);
-    const int m0 = mt * BM, n0 = nt * BN;
-    if (seg > 0) __syncthreads();   // the previous segment's last reads of both LDS buffers are done
-    // The thread's per-segment values (offsets, LDS addresses) derive from a
-    // copy of its index that the compiler cannot see through, so they are
-    // computed per segment instead of being hoisted out of the segment loop
-    // and kept live (spilled) through the hand-over code.
-    int tid_v = (int)threadIdx.x;
-    asm volatile("" : "+v"(tid_v));
-    const int tid = tid_v;
-    const int lane = tid & 63;
-    const int d = lane >> 4, r = lane & 15;
-    const int xu = tid % kUnits;
+        // segment seg: a whole tile, the head [0, le) of tile lt, or the tail
+        // [fb, T) of tile ft
+        const int kind = __builtin_amdgcn_readfirstlane(seg < n_full ? 0 : ((seg == n_full && has_head) ? 1 : 2));
+        const int id = __builtin_amdgcn_readfirstlane(kind == 0 ? full_lo + seg : (kind == 1 ? lt : ft));
+        const int tb = kind == 2 ? fb : 0, te = kind == 1 ? le : T;
+        const int mt = __builtin_amdgcn_readfirstlane(id % m_tiles), nt = __builtin_amdgcn_readfirstlane(id / m_tiles);
+        const int m0 = mt * BM, n0 = nt * BN;
+        if (seg > 0) __syncthreads();   // the previous segment's last reads of both LDS buffers are done
+        // The thread's per-segment values (offsets, LDS addresses) derive from a
+        // copy of its index that the compiler cannot see through, so they are
+        // computed per segment instead of being hoisted out of the segment loop
+        // and kept live (spilled) through the hand-over code.
+        int tid_v = (int)threadIdx.x;
+        asm volatile("" : "+v"(tid_v));
+        const int tid = tid_v;
+        const int lane = tid & 63;
+        const int d = lane >> 4, r = lane & 15;
+        const int xu = tid % kUnits;
 
-    // ---- weight records of this thread: row block i * waves + wave of the
-    // tile, record = lane (d = lane / 16, r = lane % 16: dword d of the
-    // column's four chunks of row r). Offsets are 32-bit element indices.
-    uint32_t woff[WREC], wstep[WREC], soff[WREC], zoff[WREC];
-    int zshift[WREC], wrow[WREC], wrows[WREC];
-#pragma unroll
-    for (int i = 0; i < WREC; ++i) {
-        const int rb = i * (NT / 64) + wave;
-        const int b = min(n0 / kRowBlock + rb, nblocks - 1);   // past the last block: repeat it (not stored)
-        const int rows = min(kRowBlock, N - b * kRowBlock);
-        const int rl = r < rows ? r : r - rows;                 // lanes past a short block re-read a valid row
-        const int n = b * kRowBlock + rl;
-        wrows[i] = rows;
-        woff[i] = (uint32_t)b * (uint32_t)(K / 2) + (uint32_t)(d * rows + rl);    // uint4 index, column 0 (a block is K/2 uint4)
-        wstep[i] = (uint32_t)(kColChunks * rows);                                 // uint4 per column
-        soff[i] = (uint32_t)n;                                                    // ColScales index, column 0
-        zoff[i] = (uint32_t)(n * GPC) / 8;
-        zshift[i] = 4 * ((n * GPC) % 8);
-        wrow[i] = rb * kRowBlock + r;                                             // LDS row
-    }
-    struct WCol {
-        uint4 rec[WREC], rec_hi[WREC];   // rec_hi: high-nibble plane of 8-bit codes
-        uint4 kq[WREC];                  // kq4: the super-block record of the column's row
-        ColScales<GPC> sc[WREC];
-        uint32_t zw[WREC];
-        int par;                         // kq4: column parity (half of the super-block)
-    };
-    auto load_wcol = [&](int t, WCol &u) __attribute__((always_inline)) {
-        u.par = t & 1;
+        // ---- weight records of this thread: row block i * waves + wave of the
+        // tile, record = lane (d = lane / 16, r = lane % 16: dword d of the
+        // column's four chunks of row r). Offsets are 32-bit element indices.
+        uint32_t woff[WREC], wstep[WREC], soff[WREC], zoff[WREC];
+        int zshift[WREC], wrow[WREC], wrows[WREC];
 #pragma unroll
         for (int i = 0; i < WREC; ++i) {
-            if (t < t_full) {
-                u.rec[i] = qw[woff[i] + (uint32_t)t * wstep[i]];
-                if constexpr (FT::two_planes) u.rec_hi[i] = qw_hi[woff[i] + (uint32_t)t * wstep[i]];
-            } else {   // partial last column: nc dwords per (d, row), missing chunks are zero codes
-                const int nc = C - t * kColChunks;
-                const int rl = r < wrows[i] ? r : r - wrows[i];
-                const uint32_t blk = woff[i] - (uint32_t)(d * wrows[i] + rl);   // row block base, uint4
-                const size_t off = (size_t)t * wrows[i] * 16 + (size_t)(d * wrows[i] + rl) * nc;
-                const uint32_t *col = reinterpret_cast<const uint32_t *>(qw + blk) + off;
-                uint32_t v[4];
+            const int rb = i * (NT / 64) + wave;
+            const int b = min(n0 / kRowBlock + rb, nblocks - 1);   // past the last block: repeat it (not stored)
+            const int rows = min(kRowBlock, N - b * kRowBlock);
+            const int rl = r < rows ? r : r - rows;                 // lanes past a short block re-read a valid row
+            const int n = b * kRowBlock + rl;
+            wrows[i] = rows;
+            woff[i] = (uint32_t)b * (uint32_t)(K / 2) + (uint32_t)(d * rows + rl);    // uint4 index, column 0 (a block is K/2 uint4)
+            wstep[i] = (uint32_t)(kColChunks * rows);                                 // uint4 per column
+            soff[i] = (uint32_t)n;                                                    // ColScales index, column 0
+            zoff[i] = (uint32_t)(n * GPC) / 8;
+            zshift[i] = 4 * ((n * GPC) % 8);
+            wrow[i] = rb * kRowBlock + r;                                             // LDS row
+        }
+        struct WCol {
+            uint4 rec[WREC], rec_hi[WREC];   // rec_hi: high-nibble plane of 8-bit codes
+            uint4 kq[WREC];                  // kq4: the super-block record of the column's row
+            ColScales<GPC> sc[WREC];
+            uint32_t zw[WREC];
+            int par;                         // kq4: column parity (half of the super-block)
+        };
+        auto load_wcol = [&](int t, WCol &u) __attribute__((always_inline)) {
+            u.par = t & 1;
 #pragma unroll
-                for (int j = 0; j < kColChunks; ++j) v[j] = j < nc ? col[j] : 0u;
-                u.rec[i] = make_uint4(v[0], v[1], v[2], v[3]);
-                if constexpr (FT::two_planes) {
-                    const uint32_t *colh = reinterpret_cast<const uint32_t *>(qw_hi + blk) + off;
+            for (int i = 0; i < WREC; ++i) {
+                if (t < t_full) {
+                    u.rec[i] = qw[woff[i] + (uint32_t)t * wstep[i]];
+                    if constexpr (FT::two_planes) u.rec_hi[i] = qw_hi[woff[i] + (uint32_t)t * wstep[i]];
+                } else {   // partial last column: nc dwords per (d, row), missing chunks are zero codes
+                    const int nc = C - t * kColChunks;
+                    const int rl = r < wrows[i] ? r : r - wrows[i];
+                    const uint32_t blk = woff[i] - (uint32_t)(d * wrows[i] + rl);   // row block base, uint4
+                    const size_t off = (size_t)t * wrows[i] * 16 + (size_t)(d * wrows[i] + rl) * nc;
+                    const uint32_t *col = reinterpret_cast<const uint32_t *>(qw + blk) + off;
+                    uint32_t v[4];
 #pragma unroll
-                    for (int j = 0; j < kColChunks; ++j) v[j] = j < nc ? colh[j] : 0u;
-                    u.rec_hi[i] = make_uint4(v[0], v[1], v[2], v[3]);
+                    for (int j = 0; j < kColChunks; ++j) v[j] = j < nc ? col[j] : 0u;
+                    u.rec[i] = make_uint4(v[0], v[1], v[2], v[3]);
+                    if constexpr (FT::two_planes) {
+                        const uint32_t *colh = reinterpret_cast<const uint32_t *>(qw_hi + blk) + off;
+#pragma unroll
+                        for (int j = 0; j < kColChunks; ++j) v[j] = j < nc ? colh[j] : 0u;
+                        u.rec_hi[i] = make_uint4(v[0], v[1], v[2], v[3]);
+                    }
+                }
+                // metadata slot of column t: t >> mshift (group 256: one slot per two columns)
+                const uint32_t tm = (uint32_t)(t >> mshift);
+                if constexpr (FT::kquant) {
+                    u.kq[i] = kqrec[soff[i] + (uint32_t)(t >> 1) * (uint32_t)N];
+                } else {
+                    u.sc[i] = scol[soff[i] + tm * (uint32_t)N];
+                    if constexpr (FT::has_zeros) u.zw[i] = zeros[zoff[i] + tm * zstep];
+                    else u.zw[i] = 0;
                 }
             }
-            // metadata slot of column t: t >> mshift (group 256: one slot per two columns)
-            const uint32_t tm = (uint32_t)(t >> mshift);
-            if constexpr (FT::kquant) {
-                u.kq[i] = kqrec[soff[i] + (uint32_t)(t >> 1) * (uint32_t)N];
-            } else {
-                u.sc[i] = scol[soff[i] + tm * (uint32_t)N];
-                if constexpr (FT::has_zeros) u.zw[i] = zeros[zoff[i] + tm * zstep];
-                else u.zw[i] = 0;
-            }
-        }
-    };
-    // dequantise half h (chunks 2h, 2h+1) of weight record i into LDS;
-    // chunks past K (partial last column) have zero codes and zero scale
-    auto store_w_rec = [&](const WCol &u, int i, int h, uint4 *wbuf) __attribute__((always_inline)) {
-#pragma unroll
-        for (int jj = 0; jj < 2; ++jj) {
-            const uint32_t dw = h ? (jj ? u.rec[i].w : u.rec[i].z) : (jj ? u.rec[i].y : u.rec[i].x);
-            const uint32_t dh = h ? (jj ? u.rec_hi[i].w : u.rec_hi[i].z) : (jj ? u.rec_hi[i].y : u.rec_hi[i].x);
-            const int e = (2 * h + jj) / CPG;
-            uint32_t z = FT::fixed_zero;
-            if constexpr (FT::has_zeros) z = (u.zw[i] >> (zshift[i] + 4 * e)) & 0xFu;
-            uint4 v;
-            if constexpr (FT::kquant) {
-                v = dequant_kq<BF>(dw, kq_sub(kq_half(u.kq[i], u.par != 0), 2 * h + jj), uc);
-                wbuf[swz(wrow[i], 4 * jj + d)] = v;
-                continue;
-            }
-            const float s = u.sc[i].get(e);
-            if constexpr (BF && FT::two_planes)
-                v = dequant_bf16_s8(dw, dh, s, uc);
-            else if constexpr (BF)
-                v = dequant_bf16(dw, dequant_bf16_consts(s, z), uc);
-            else
-                v = dequant_f16<FMT>(dw, dh, z, (_Float16)s, uc);
-            wbuf[swz(wrow[i], 4 * jj + d)] = v;
-        }
-    };
-
-    // ---- activation units of this thread: tile row (i * NT + tid) / 8, unit
-    // tid % 8 of the step; units past K read as zero
-    uint32_t xoff[XREC];
-#pragma unroll
-    for (int i = 0; i < XREC; ++i) {
-        const int row = (i * NT + tid) / kUnits;
-        xoff[i] = (uint32_t)min(m0 + row, M - 1) * (uint32_t)(K / 8) + (uint32_t)xu;   // rows past M repeat the last
-    }
-    // Steps that may reach past K (the partial last column) zero those units:
-    // the address is clamped into the row and the value masked, so the load
-    // stays unconditional (no branch splits the interleaved step).
-    auto load_x_unit = [&](int i, int step_idx, auto masked) __attribute__((always_inline)) {
-        if constexpr (!decltype(masked)::value) return xg[xoff[i] + (uint32_t)(step_idx * kUnits)];
-        const int k8 = step_idx * kUnits + xu;
-        uint4 v = xg[xoff[i] + (uint32_t)(min(k8, k8_total - 1) - xu)];
-        const uint32_t keep = 0u - (uint32_t)(k8 < k8_total);
-        v.x &= keep;
-        v.y &= keep;
-        v.z &= keep;
-        v.w &= keep;
-        return v;
-    };
-    uint4 xv[XREC];
-
-    f16_t acc[TM][TN];
-#pragma unroll
-    for (int a = 0; a < TM; ++a)
-#pragma unroll
-        for (int b = 0; b < TN; ++b)
-#pragma unroll
-            for (int v = 0; v < 16; ++v) acc[a][b][v] = 0.0f;
-
-    // One 64-k step out of LDS (4 sub-steps of 16 k), with the operands of
-    // the next step written into the other buffer in between: sub-step kk
-    // also dequantises weight record kk (both of its chunks of half h) and
-    // moves every fourth activation unit from registers to LDS, reloading the
-    // register with the unit of the step after (x_next). Fragment reads run
-    // one sub-step ahead of the MFMAs that use them.
-    auto step = [&](const uint4 *xb, const uint4 *wb, const WCol &u, int h, uint4 *wdst, uint4 *xdst,
-                    int x_next, auto masked) __attribute__((always_inline)) {
-        const int rsel = lane & 31, khalf = lane >> 5;
-        uint4 af[2][TM], bfr[2][TN];
-        auto read = [&](int kk, uint4 (&a_)[TM], uint4 (&b_)[TN]) __attribute__((always_inline)) {
-#pragma unroll
-            for (int a = 0; a < TM; ++a) a_[a] = xb[swz(wm * (BM / WM) + 32 * a + rsel, 2 * kk + khalf)];
-#pragma unroll
-            for (int b = 0; b < TN; ++b) b_[b] = wb[swz(wn * (BN / WN) + 32 * b + rsel, 2 * kk + khalf)];
         };
-        // one wave per SIMD: fragment reads run one sub-step ahead; two waves
-        // per SIMD: read just before use (the other wave covers the latency,
-        // and the registers are needed for its accumulators)
-        constexpr bool kAhead = WM * WN == 4;
-        read(0, af[0], bfr[0]);
+        // dequantise half h (chunks 2h, 2h+1) of weight record i into LDS;
+        // chunks past K (partial last column) have zero codes and zero scale
+        auto store_w_rec = [&](const WCol &u, int i, int h, uint4 *wbuf) __attribute__((always_inline)) {
 #pragma unroll
-        for (int kk = 0; kk < kStepK / 16; ++kk) {
-            if constexpr (kAhead) {
-                if (kk + 1 < kStepK / 16) read(kk + 1, af[(kk + 1) & 1], bfr[(kk + 1) & 1]);
-            } else if (kk > 0) {
-                read(kk, af[kk & 1], bfr[kk & 1]);
+            for (int jj = 0; jj < 2; ++jj) {
+                const uint32_t dw = h ? (jj ? u.rec[i].w : u.rec[i].z) : (jj ? u.rec[i].y : u.rec[i].x);
+                const uint32_t dh = h ? (jj ? u.rec_hi[i].w : u.rec_hi[i].z) : (jj ? u.rec_hi[i].y : u.rec_hi[i].x);
+                const int e = (2 * h + jj) / CPG;
+                uint32_t z = FT::fixed_zero;
+                if constexpr (FT::has_zeros) z = (u.zw[i] >> (zshift[i] + 4 * e)) & 0xFu;
+                uint4 v;
+                if constexpr (FT::kquant) {
+                    v = dequant_kq<BF>(dw, kq_sub(kq_half(u.kq[i], u.par != 0), 2 * h + jj), uc);
+                    wbuf[swz(wrow[i], 4 * jj + d)] = v;
+                    continue;
+                }
+                const float s = u.sc[i].get(e);
+                if constexpr (BF && FT::two_planes)
+                    v = dequant_bf16_s8(dw, dh, s, uc);
+                else if constexpr (BF)
+                    v = dequant_bf16(dw, dequant_bf16_consts(s, z), uc);
+                else
+                    v = dequant_f16<FMT>(dw, dh, z, (_Float16)s, uc);
+                wbuf[swz(wrow[i], 4 * jj + d)] = v;
             }
-            if (kk < WREC) store_w_rec(u, kk, h, wdst);
+        };
+
+        // ---- activation units of this thread: tile row (i * NT + tid) / 8, unit
+        // tid % 8 of the step; units past K read as zero
+        uint32_t xoff[XREC];
 #pragma unroll
-            for (int i = kk; i < XREC; i += kStepK / 16) {
-                xdst[swz((i * NT + tid) / kUnits, xu)] = xv[i];
-                xv[i] = load_x_unit(i, x_next, masked);
-            }
-#pragma unroll
-            for (int a = 0; a < TM; ++a)
-#pragma unroll
-                for (int b = 0; b < TN; ++b)
-                    acc[a][b] = mfma32x32x16<BF>(af[kk & 1][a], bfr[kk & 1][b], acc[a][b]);
+        for (int i = 0; i < XREC; ++i) {
+            const int row = (i * NT + tid) / kUnits;
+            xoff[i] = (uint32_t)min(m0 + row, M - 1) * (uint32_t)(K / 8) + (uint32_t)xu;   // rows past M repeat the last
         }
-    };
+        // Steps that may reach past K (the partial last column) zero those units:
+        // the address is clamped into the row and the value masked, so the load
+        // stays unconditional (no branch splits the interleaved step).
+        auto load_x_unit = [&](int i, int step_idx, auto masked) __attribute__((always_inline)) {
+            if constexpr (!decltype(masked)::value) return xg[xoff[i] + (uint32_t)(step_idx * kUnits)];
+            const int k8 = step_idx * kUnits + xu;
+            uint4 v = xg[xoff[i] + (uint32_t)(min(k8, k8_total - 1) - xu)];
+            const uint32_t keep = 0u - (uint32_t)(k8 < k8_total);
+            v.x &= keep;
+            v.y &= keep;
+            v.z &= keep;
+            v.w &= keep;
+            return v;
+        };
+        uint4 xv[XREC];
 
-    // ---- main loop over the segment's full columns [tb, te): iteration t
-    // multiplies steps 2t (buffer 0) and 2t+1 (buffer 1) and writes steps
-    // 2t+1 and 2t+2. Loads past the end of the segment or of K are clamped to
-    // valid addresses; what they bring is written into a buffer that is never
-    // multiplied.
-    WCol wcur, wnext;
-    load_wcol(tb, wcur);
-#pragma unroll
-    for (int i = 0; i < XREC; ++i) xv[i] = load_x_unit(i, 2 * tb, kMasked);
-    load_wcol(min(tb + 1, T - 1), wnext);
-#pragma unroll
-    for (int i = 0; i < WREC; ++i) store_w_rec(wcur, i, 0, ws0);
-#pragma unroll
-    for (int i = 0; i < XREC; ++i) {
-        xs0[swz((i * NT + tid) / kUnits, xu)] = xv[i];
-        xv[i] = load_x_unit(i, min(2 * tb + 1, steps - 1), kMasked);
-    }
-    __syncthreads();
-    // (the activation loads of the last full column reach the steps after it:
-    // those are the masked ones)
-    auto column = [&](int t, auto masked) __attribute__((always_inline)) {
-        step(xs0, ws0, wcur, 1, ws1, xs1, min(2 * t + 2, steps - 1), masked);
-        __syncthreads();
-        wcur = wnext;
-        load_wcol(min(t + 2, T - 1), wnext);
-        step(xs1, ws1, wcur, 0, ws0, xs0, min(2 * t + 3, steps - 1), masked);
-        __syncthreads();
-    };
-    const int te_full = min(te, t_full);
-    for (int t = tb; t + 1 < te_full; ++t) column(t, kPlain);
-    if (te_full > tb) column(te_full - 1, kMasked);
-    // the partial last column (K % 128 != 0; only a segment that ends the
-    // tile's K has it): one or two more steps; its missing chunks have zero
-    // codes and zero activations
-    if (te == T && t_full < T) {
-        const int s0 = 2 * t_full;
-        const bool two = s0 + 1 < steps;
-        step(xs0, ws0, wcur, 1, ws1, xs1, min(s0 + 2, steps - 1), kMasked);
-        __syncthreads();
-        if (two) step(xs1, ws1, wcur, 0, ws0, xs0, min(s0 + 2, steps - 1), kMasked);
-    }
-
-    // ---- stream-K hand-over. Partial slots hold each thread's accumulators
-    // as float4 [TM][TN][4][NT] (coalesced; producer and consumer run the same
-    // tile shape, so thread tid reads back exactly what thread tid wrote).
-    constexpr int kPart = TM * TN * 4;   // float4 per thread
-    if (SK && kind == 1) {
-        float4 *slot = partials + (size_t)s_sk * kPart * NT;
+        f16_t acc[TM][TN];
 #pragma unroll
         for (int a = 0; a < TM; ++a)
 #pragma unroll
             for (int b = 0; b < TN; ++b)
 #pragma unroll
-                for (int q = 0; q < 4; ++q)
-                    slot[((a * TN + b) * 4 + q) * NT + tid] =
-                        make_float4(acc[a][b][4 * q], acc[a][b][4 * q + 1], acc[a][b][4 * q + 2], acc[a][b][4 * q + 3]);
-        // every wave waits until its stores have reached the L2 (vmcnt(0));
-        // after the barrier one write-back of the L2 (the agent-scope release
-        // of thread 0) makes the whole partial visible to the other XCDs
-        // before the flag, itself a device-coherent store
-        __builtin_amdgcn_s_waitcnt(0x0F70);
-        __syncthreads();
-        if (tid == 0) {
-            __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
-            __hip_atomic_store(&flags[s_sk], token, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        }
-        continue;
-    }
-    if (SK && kind == 2) {
-        if (tid == 0) {
-            // bounded wait (about a second): the producer never waits before
-            // producing, so this ends; the bound only keeps a broken launch
-            // from holding the device. Relaxed polls (device-coherent loads);
-            // the acquire below then orders the partial's loads after them.
-            for (int spin = 0; spin < (1 << 21); ++spin) {
-                if (__hip_atomic_load(&flags[s_sk - 1], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == token) break;
-                __builtin_amdgcn_s_sleep(2);
+                for (int v = 0; v < 16; ++v) acc[a][b][v] = 0.0f;
+
+        // One 64-k step out of LDS (4 sub-steps of 16 k), with the operands of
+        // the next step written into the other buffer in between: sub-step kk
+        // also dequantises weight record kk (both of its chunks of half h) and
+        // moves every fourth activation unit from registers to LDS, reloading the
+        // register with the unit of the step after (x_next). Fragment reads run
+        // one sub-step ahead of the MFMAs that use them.
+        auto step = [&](const uint4 *xb, const uint4 *wb, const WCol &u, int h, uint4 *wdst, uint4 *xdst,
+                        int x_next, auto masked) __attribute__((always_inline)) {
+            const int rsel = lane & 31, khalf = lane >> 5;
+            uint4 af[2][TM], bfr[2][TN];
+            auto read = [&](int kk, uint4 (&a_)[TM], uint4 (&b_)[TN]) __attribute__((always_inline)) {
+#pragma unroll
+                for (int a = 0; a < TM; ++a) a_[a] = xb[swz(wm * (BM / WM) + 32 * a + rsel, 2 * kk + khalf)];
+#pragma unroll
+                for (int b = 0; b < TN; ++b) b_[b] = wb[swz(wn * (BN / WN) + 32 * b + rsel, 2 * kk + khalf)];
+            };
+            // one wave per SIMD: fragment reads run one sub-step ahead; two waves
+            // per SIMD: read just before use (the other wave covers the latency,
+            // and the registers are needed for its accumulators)
+            constexpr bool kAhead = WM * WN == 4;
+            read(0, af[0], bfr[0]);
+#pragma unroll
+            for (int kk = 0; kk < kStepK / 16; ++kk) {
+                if constexpr (kAhead) {
+                    if (kk + 1 < kStepK / 16) read(kk + 1, af[(kk + 1) & 1], bfr[(kk + 1) & 1]);
+                } else if (kk > 0) {
+                    read(kk, af[kk & 1], bfr[kk & 1]);
+                }
+                if (kk < WREC) store_w_rec(u, kk, h, wdst);
+#pragma unroll
+                for (int i = kk; i < XREC; i += kStepK / 16) {
+                    xdst[swz((i * NT + tid) / kUnits, xu)] = xv[i];
+                    xv[i] = load_x_unit(i, x_next, masked);
+                }
+#pragma unroll
+                for (int a = 0; a < TM; ++a)
+#pragma unroll
+                    for (int b = 0; b < TN; ++b)
+                        acc[a][b] = mfma32x32x16<BF>(af[kk & 1][a], bfr[kk & 1][b], acc[a][b]);
             }
-            // invalidates this CU's L1 and this XCD's L2, which all waves of
-            // the workgroup read through: no stale line of the partial is left
-            __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+        };
+
+        // ---- main loop over the segment's full columns [tb, te): iteration t
+        // multiplies steps 2t (buffer 0) and 2t+1 (buffer 1) and writes steps
+        // 2t+1 and 2t+2. Loads past the end of the segment or of K are clamped to
+        // valid addresses; what they bring is written into a buffer that is never
+        // multiplied.
+        WCol wcur, wnext;
+        load_wcol(tb, wcur);
+#pragma unroll
+        for (int i = 0; i < XREC; ++i) xv[i] = load_x_unit(i, 2 * tb, kMasked);
+        load_wcol(min(tb + 1, T - 1), wnext);
+#pragma unroll
+        for (int i = 0; i < WREC; ++i) store_w_rec(wcur, i, 0, ws0);
+#pragma unroll
+        for (int i = 0; i < XREC; ++i) {
+            xs0[swz((i * NT + tid) / kUnits, xu)] = xv[i];
+            xv[i] = load_x_unit(i, min(2 * tb + 1, steps - 1), kMasked);
         }
         __syncthreads();
-        const float4 *slot = partials + (size_t)(s_sk - 1) * kPart * NT;
-        // one 32x32 block at a time (the scheduling barrier keeps the loads of
-        // all blocks from being hoisted together, which would need another
-        // accumulator's worth of registers)
+        // (the activation loads of the last full column reach the steps after it:
+        // those are the masked ones)
+        auto column = [&](int t, auto masked) __attribute__((always_inline)) {
+            step(xs0, ws0, wcur, 1, ws1, xs1, min(2 * t + 2, steps - 1), masked);
+            __syncthreads();
+            wcur = wnext;
+            load_wcol(min(t + 2, T - 1), wnext);
+            step(xs1, ws1, wcur, 0, ws0, xs0, min(2 * t + 3, steps - 1), masked);
+            __syncthreads();
+        };
+        const int te_full = min(te, t_full);
+        for (int t = tb; t + 1 < te_full; ++t) column(t, kPlain);
+        if (te_full > tb) column(te_full - 1, kMasked);
+        // the partial last column (K % 128 != 0; only a segment that ends the
+        // tile's K has it): one or two more steps; its missing chunks have zero
+        // codes and zero activations
+        if (te == T && t_full < T) {
+            const int s0 = 2 * t_full;
+            const bool two = s0 + 1 < steps;
+            step(xs0, ws0, wcur, 1, ws1, xs1, min(s0 + 2, steps - 1), kMasked);
+            __syncthreads();
+            if (two) step(xs1, ws1, wcur, 0, ws0, xs0, min(s0 + 2, steps - 1), kMasked);
+        }
+
+        // ---- stream-K hand-over. Partial slots hold each thread's accumulators
+        // as float4 [TM][TN][4][NT] (coalesced; producer and consumer run the same
+        // tile shape, so thread tid reads back exactly what thread tid wrote).
+        constexpr int kPart = TM * TN * 4;   // float4 per thread
+        if (SK && kind == 1) {
+            float4 *slot = partials + (size_t)s_sk * kPart * NT;
+#pragma unroll
+            for (int a = 0; a < TM; ++a)
+#pragma unroll
+                for (int b = 0; b < TN; ++b)
+#pragma unroll
+                    for (int q = 0; q < 4; ++q)
+                        slot[((a * TN + b) * 4 + q) * NT + tid] =
+                            make_float4(acc[a][b][4 * q], acc[a][b][4 * q + 1], acc[a][b][4 * q + 2], acc[a][b][4 * q + 3]);
+            // every wave waits until its stores have reached the L2 (vmcnt(0));
+            // after the barrier one write-back of the L2 (the agent-scope release
+            // of thread 0) makes the whole partial visible to the other XCDs
+            // before the flag, itself a device-coherent store
+            __builtin_amdgcn_s_waitcnt(0x0F70);
+            __syncthreads();
+            if (tid == 0) {
+                __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
+                __hip_atomic_store(&flags[s_sk], token, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            }
+            continue;
+        }
+        if (SK && kind == 2) {
+            if (tid == 0) {
+                // bounded wait (about a second): the producer never waits before
+                // producing, so this ends; the bound only keeps a broken launch
+                // from holding the device. Relaxed polls (device-coherent loads);
+                // the acquire below then orders the partial's loads after them.
+                for (int spin = 0; spin < (1 << 21); ++spin) {
+                    if (__hip_atomic_load(&flags[s_sk - 1], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == token) break;
+                    __builtin_amdgcn_s_sleep(2);
+                }
+                // invalidates this CU's L1 and this XCD's L2, which all waves of
+                // the workgroup read through: no stale line of the partial is left
+                __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+            }
+            __syncthreads();
+            const float4 *slot = partials + (size_t)(s_sk - 1) * kPart * NT;
+            // one 32x32 block at a time (the scheduling barrier keeps the loads of
+            // all blocks from being hoisted together, which would need another
+            // accumulator's worth of registers)
+#pragma unroll
+            for (int a = 0; a < TM; ++a)
+#pragma unroll
+                for (int b = 0; b < TN; ++b) {
+                    float4 p[4];
+#pragma unroll
+                    for (int q = 0; q < 4; ++q) p[q] = slot[((a * TN + b) * 4 + q) * NT + tid];
+#pragma unroll
+                    for (int q = 0; q < 4; ++q) {
+                        acc[a][b][4 * q] += p[q].x;
+                        acc[a][b][4 * q + 1] += p[q].y;
+                        acc[a][b][4 * q + 2] += p[q].z;
+                        acc[a][b][4 * q + 3] += p[q].w;
+                    }
+                    __builtin_amdgcn_sched_barrier(0);
+                }
+            // the flag of this launch is consumed: clear it, so a replay of the
+            // same launch (same token, e.g. from a graph) waits again
+            if (tid == 0) __hip_atomic_store(&flags[s_sk - 1], 0ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        }
+
+        // ---- epilogue: lane holds rows (v/4)*8 + (lane/32)*4 + v%4 of column
+        // lane%32 of each 32x32 block (a store instruction covers two 64-byte
+        // runs of two rows; measured faster than the transposed layout's 8-byte
+        // stores over 32 rows). Tiles inside the matrix store without per-element
+        // checks (a branch per element splits the accumulators' live ranges and
+        // spills them).
+        const bool inside = m0 + BM <= M && n0 + BN <= N;
 #pragma unroll
         for (int a = 0; a < TM; ++a)
 #pragma unroll
             for (int b = 0; b < TN; ++b) {
-                float4 p[4];
+                const int n = n0 + wn * (BN / WN) + 32 * b + (lane & 31);
+                const int mb = m0 + wm * (BM / WM) + 32 * a + (lane >> 5) * 4;
+                uint16_t *yb = y + (int64_t)mb * N + n;
+                if (inside) {
 #pragma unroll
-                for (int q = 0; q < 4; ++q) p[q] = slot[((a * TN + b) * 4 + q) * NT + tid];
-#pragma unroll
-                for (int q = 0; q < 4; ++q) {
-                    acc[a][b][4 * q] += p[q].x;
-                    acc[a][b][4 * q + 1] += p[q].y;
-                    acc[a][b][4 * q + 2] += p[q].z;
-                    acc[a][b][4 * q + 3] += p[q].w;
-                }
-                __builtin_amdgcn_sched_barrier(0);
-            }
-        // the flag of this launch is consumed: clear it, so a replay of the
-        // same launch (same token, e.g. from a graph) waits again
-        if (tid == 0) __hip_atomic_store(&flags[s_sk - 1], 0ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    }
-
-    // ---- epilogue: lane holds rows (v/4)*8 + (lane/32)*4 + v%4 of column
-    // lane%32 of each 32x32 block (a store instruction covers two 64-byte
-    // runs of two rows; measured faster than the transposed layout's 8-byte
-    // stores over 32 rows). Tiles inside the matrix store without per-element
-    // checks (a branch per element splits the accumulators' live ranges and
-    // spills them).
-    const bool inside = m0 + BM <= M && n0 + BN <= N;
-#pragma unroll
-    for (int a = 0; a < TM; ++a)
-#pragma unroll
-        for (int b = 0; b < TN; ++b) {
-            const int n = n0 + wn * (BN / WN) + 32 * b + (lane & 31);
-            const int mb = m0 + wm * (BM / WM) + 32 * a + (lane >> 5) * 4;
-            uint16_t *yb = y + (int64_t)mb * N + n;
-            if (inside) {
-#pragma unroll
-                for (int v = 0; v < 16; ++v)
-                    yb[(int64_t)((v / 4) * 8 + (v % 4)) * N] =
-                        BF ? f32_to_bf16_bits(acc[a][b][v]) : f32_to_f16_bits(acc[a][b][v]);
-            } else if (n < N) {
-#pragma unroll
-                for (int v = 0; v < 16; ++v) {
-                    const int m = mb + (v / 4) * 8 + (v % 4);
-                    if (m < M)
+                    for (int v = 0; v < 16; ++v)
                         yb[(int64_t)((v / 4) * 8 + (v % 4)) * N] =
                             BF ? f32_to_bf16_bits(acc[a][b][v]) : f32_to_f16_bits(acc[a][b][v]);
+                } else if (n < N) {
+#pragma unroll
+                    for (int v = 0; v < 16; ++v) {
+                        const int m = mb + (v / 4) * 8 + (v % 4);
+                        if (m < M)
+                            yb[(int64_t)((v / 4) * 8 + (v % 4)) * N] =
+                                BF ? f32_to_bf16_bits(acc[a][b][v]) : f32_to_f16_bits(acc[a][b][v]);
+                    }
                 }
             }
-        }
     }   // segments
 }
 
