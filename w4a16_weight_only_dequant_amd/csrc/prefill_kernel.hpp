@@ -64,20 +64,24 @@ __device__ inline f16_t mfma32x32x16(const uint4 &a, const uint4 &b, f16_t c) {
 __device__ inline int swz(int row, int unit) { return row * kUnits + (unit ^ (row & 7) ^ ((row >> 3) & 1)); }
 
 // One dword of codes (k = 0..7 of a slice, even k in the low half-word) ->
-// eight bf16 values s*(q - z) in k order. The magic-number unpack gives the
+// eight 16-bit values (bf16, or fp16) s*(q - z) in k order. The magic-number unpack gives the
 // exact fp16 values 1024 + q (low nibble of a byte) and 1024 + 16 q (high
 // nibble); one fma with an fp16 operand (v_fma_mix_f32) then forms
 // s*(1024+q) - s*(1024+z) = s*(q - z), or (s/16)*(1024+16q) - s*(64+z), where
 // every product and both constants are exact in fp32 (at most 22 significant
 // bits), so the fma returns s*(q - z) exactly (15 significant bits at most) and
-// the conversion to bf16 is its one rounding, to nearest even.
-struct DequantBf16 {
+// the conversion to bf16 (or fp16: v_cvt_pk_f16_f32) is its one rounding, to
+// nearest even. For fp16 this is the value an fp16 multiply of the exact
+// (q - z) by s gives (one rounding of the same exact product); going through
+// fp32 keeps fewer packed intermediates live than the fp16 route.
+struct DequantConsts {
     float s, c_lo, s16, c_hi;   // s, -s*(1024+z), s/16, -s*(64+z)
 };
-__device__ inline DequantBf16 dequant_bf16_consts(float s, uint32_t z) {
-    return DequantBf16{s, -s * (float)(1024u + z), s * 0.0625f, -s * (float)(64u + z)};
+__device__ inline DequantConsts dequant_consts(float s, uint32_t z) {
+    return DequantConsts{s, -s * (float)(1024u + z), s * 0.0625f, -s * (float)(64u + z)};
 }
-__device__ inline uint4 dequant_bf16(uint32_t d, const DequantBf16 &c, const UnpackConsts &uc) {
+template <bool BF>
+__device__ inline uint4 dequant_16(uint32_t d, const DequantConsts &c, const UnpackConsts &uc) {
     const uint32_t d8 = d >> 8;
     const half2_t h0 = __builtin_bit_cast(half2_t, and_or(d, uc.lo_mask, uc.f16_magic));    // k0, k1
     const half2_t h1 = __builtin_bit_cast(half2_t, and_or(d, uc.hi_mask, uc.f16_magic));    // k2, k3 (x16)
@@ -86,7 +90,10 @@ __device__ inline uint4 dequant_bf16(uint32_t d, const DequantBf16 &c, const Unp
     auto lo = [&](_Float16 h) { return fmaf(c.s, (float)h, c.c_lo); };
     auto hi = [&](_Float16 h) { return fmaf(c.s16, (float)h, c.c_hi); };
     auto pk = [](float a, float b) {
-        return __builtin_bit_cast(uint32_t, __builtin_convertvector(float2_t{a, b}, bf162_t));
+        if constexpr (BF)
+            return __builtin_bit_cast(uint32_t, __builtin_convertvector(float2_t{a, b}, bf162_t));
+        else
+            return __builtin_bit_cast(uint32_t, __builtin_convertvector(float2_t{a, b}, half2_t));
     };
     return make_uint4(pk(lo(h0.x), lo(h0.y)), pk(hi(h1.x), hi(h1.y)), pk(lo(h2.x), lo(h2.y)),
                       pk(hi(h3.x), hi(h3.y)));
@@ -329,8 +336,13 @@ __global__ __launch_bounds__(64 * WM * WN) __attribute__((amdgpu_waves_per_eu(WM
                 const float s = u.sc[i].get(e);
                 if constexpr (BF && FT::two_planes)
                     v = dequant_bf16_s8(dw, dh, s, uc);
-                else if constexpr (BF)
-                    v = dequant_bf16(dw, dequant_bf16_consts(s, z), uc);
+                else if constexpr (!FT::two_planes && (BF || GROUP >= 128))
+                    // (fp16 through fp32 too at group 128 (and 256), where it is
+                    // faster: M = 2048, N = 13824, K = 5120: 282 against 298 us,
+                    // M = 512: 98 against 106 us; at groups 32 and 64 the packed
+                    // fp16 route, with fewer per-group constants, is faster:
+                    // 282 against 292 us, 92 against 97 us)
+                    v = dequant_16<BF>(dw, dequant_consts(s, z), uc);
                 else
                     v = dequant_f16<FMT>(dw, dh, z, (_Float16)s, uc);
                 wbuf[swz(wrow[i], 4 * jj + d)] = v;
