@@ -152,3 +152,20 @@ def test_stream_k_through_grouped_and_awq_calls():
     y_pre = w4.gemm(w4.scale_activations(x, m), pw_a)
     torch.cuda.synchronize()
     assert torch.equal(y_awq.view(torch.int16), y_pre.view(torch.int16))
+
+
+@pytest.mark.parametrize("N,split", [(12288, True), (12544, False), (16640, True), (36864, True)])
+def test_stream_k_plan_boundaries(N, split):
+    """M = 2048 (256-row tiles, 8 per column of tiles) on 256 compute units:
+    384 tiles (last round exactly half full: split), 392 (just over: whole),
+    520 (one whole round, then the last two split) and 1152 (three whole
+    rounds, then 384 split). Outputs within the bar either way."""
+    import torch
+    M, K, group = 2048, 512, 128
+    assert _uses_stream_k(M, N, K, group) == split
+    w, o, pw = _prep(N, K, group)
+    x = wl.random_activations(N + 5, M, K, "bf16")
+    y = H.lib().linear(H.to_device_bits(x, "bf16"), pw)
+    torch.cuda.synchronize()
+    H.check_against_oracle(y, x, "bf16", o, group, cols=_cols(N, N))
+    H.drop(("sk", N, K, group))
