@@ -169,3 +169,45 @@ def test_stream_k_plan_boundaries(N, split):
     torch.cuda.synchronize()
     H.check_against_oracle(y, x, "bf16", o, group, cols=_cols(N, N))
     H.drop(("sk", N, K, group))
+
+
+def test_concurrent_calls_on_two_streams():
+    """Two host threads, each with its own stream and workspace, run split
+    (stream-K) and decode calls at the same time: every result equals the
+    serial one (per-launch tokens, per-device attribute records and the
+    plan caches are safe to share)."""
+    import threading
+    import torch
+    w4 = H.lib()
+    M, N, K, group = 2048, 8448, 512, 128
+    w, o, pw = _prep(N, K, group)
+    xs = [H.to_device_bits(wl.random_activations(100 + i, M, K, "bf16"), "bf16") for i in range(2)]
+    x1 = [H.to_device_bits(wl.random_activations(200 + i, 1, K, "f16"), "f16") for i in range(2)]
+    want = [w4.gemm(x, pw) for x in xs]
+    want1 = [w4.linear(x, pw) for x in x1]
+    torch.cuda.synchronize()
+    errors = []
+
+    def worker(i):
+        try:
+            stream = torch.cuda.Stream()
+            ws = w4.Workspace("cuda")
+            with torch.cuda.stream(stream):
+                for _ in range(3):
+                    y = w4.gemm(xs[i], pw, workspace=ws, stream=stream)
+                    y1 = w4.linear(x1[i], pw, workspace=ws, stream=stream)
+                    stream.synchronize()
+                    if not torch.equal(y.view(torch.int16), want[i].view(torch.int16)):
+                        errors.append(f"thread {i}: split GEMM differs")
+                    if not torch.equal(y1.view(torch.int16), want1[i].view(torch.int16)):
+                        errors.append(f"thread {i}: decode differs")
+        except Exception as e:   # reported below
+            errors.append(f"thread {i}: {e!r}")
+
+    threads = [threading.Thread(target=worker, args=(i,)) for i in range(2)]
+    for t in threads:
+        t.start()
+    for t in threads:
+        t.join(timeout=60)
+    assert not any(t.is_alive() for t in threads)
+    assert not errors, errors
