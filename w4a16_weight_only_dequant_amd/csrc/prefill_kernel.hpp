@@ -507,25 +507,22 @@ __global__ __launch_bounds__(64 * WM * WN) __attribute__((amdgpu_waves_per_eu(WM
             }
             __syncthreads();
             const float4 *slot = partials + (size_t)(s_sk - 1) * kPart * NT;
-            // one 32x32 block at a time (the scheduling barrier keeps the loads of
-            // all blocks from being hoisted together, which would need another
-            // accumulator's worth of registers)
+            // all 32 loads of the thread's part issue back to back (one round
+            // trip). The fix-up costs more than that: every workgroup reaches it
+            // at about the same time, so the 256 KB partials of all of them are
+            // read together (64 MB on 256 CUs, ~16 us); see the plan's threshold
 #pragma unroll
             for (int a = 0; a < TM; ++a)
 #pragma unroll
-                for (int b = 0; b < TN; ++b) {
-                    float4 p[4];
-#pragma unroll
-                    for (int q = 0; q < 4; ++q) p[q] = slot[((a * TN + b) * 4 + q) * NT + tid];
+                for (int b = 0; b < TN; ++b)
 #pragma unroll
                     for (int q = 0; q < 4; ++q) {
-                        acc[a][b][4 * q] += p[q].x;
-                        acc[a][b][4 * q + 1] += p[q].y;
-                        acc[a][b][4 * q + 2] += p[q].z;
-                        acc[a][b][4 * q + 3] += p[q].w;
+                        const float4 p = slot[((a * TN + b) * 4 + q) * NT + tid];
+                        acc[a][b][4 * q] += p.x;
+                        acc[a][b][4 * q + 1] += p.y;
+                        acc[a][b][4 * q + 2] += p.z;
+                        acc[a][b][4 * q + 3] += p.w;
                     }
-                    __builtin_amdgcn_sched_barrier(0);
-                }
             // the flag of this launch is consumed: clear it, so a replay of the
             // same launch (same token, e.g. from a graph) waits again
             if (tid == 0) __hip_atomic_store(&flags[s_sk - 1], 0ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
