@@ -303,7 +303,7 @@ int32_t w4a16_linear_kernel(int64_t M, int64_t N, int64_t K, int32_t group, int3
  * 10 log10(sum w^2 / sum d^2) (+inf when d = 0), cosine = sum w w_hat /
  * sqrt(sum w^2 sum w_hat^2) (1 when both are zero). w is the fp32 [N][K]
  * matrix given to the pack call; workspace (device, caller-owned) holds
- * per-block partial sums, w4a16_quant_error_workspace_bytes of them; the
+ * per-workgroup partial sums, w4a16_quant_error_workspace_bytes of them; the
  * partials are folded in a fixed order, so the result is deterministic. */
 w4a16_status w4a16_quant_error_workspace_bytes(int64_t N, int64_t K, int32_t group, size_t *bytes);
 w4a16_status w4a16_quant_error(const float *w, const void *qweight, const void *scales,

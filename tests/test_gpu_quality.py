@@ -55,6 +55,31 @@ def test_quant_error_degenerate_matrices():
     _check_report(got, lat, o, group)
 
 
+@pytest.mark.parametrize("N,K,group,fmt", [(16, 4128, 32, "asym4"),      # one row block, 33 one-column slices
+                                            (40, 8288, 32, "sym8"),       # 3 row blocks (one ragged), 65 slices
+                                            (9000, 1280, 256, "sym4")])   # 563 row blocks, 4 slices of 2 or 3 columns
+def test_quant_error_k_slices(N, K, group, fmt):
+    """The report's partial sums are taken per (row block, slice of K's
+    128-weight columns): shapes at both ends of the split, ragged slices
+    included, against the oracle; the device-result form (out=) gives the same
+    numbers, bit-identical on repeat whatever the workspace held before."""
+    import torch
+    w4 = H.lib()
+    w = wl.random_weights(3 * N + K, N, K)
+    o, pw = H.oracle_pack(w, group, fmt), H.gpu_pack(w, group, fmt)
+    wt = torch.from_numpy(np.ascontiguousarray(w)).cuda()
+    got = w4.quant_error(wt, pw)
+    _check_report(got, w, o, group)
+    ws = w4.Workspace("cuda")
+    buf = ws.get(1 << 20)
+    buf.copy_(torch.randint(0, 256, buf.shape, dtype=torch.uint8, device="cuda"))
+    out = torch.full((8,), 7.0, dtype=torch.float64, device="cuda")
+    for _ in range(2):
+        assert w4.quant_error(wt, pw, out=out, workspace=ws) is out
+        torch.cuda.synchronize()
+        assert out.cpu().tolist() == [got[f] for f in w4.QUALITY_FIELDS]
+
+
 @pytest.mark.parametrize("dtype", ["f16", "bf16"])
 @pytest.mark.parametrize("M,K", [(1, 64), (3, 1000 // 8 * 8), (17, 5120), (300, 640)])
 def test_scale_activations_bit_exact(dtype, M, K):

@@ -5,4 +5,4 @@ include/w4a16.h); this package is its thin Python binding.
 """
 from ._lib import (EXPORTED, FORMATS, LIB_PATH, PackedWeight, W4A16Error, Workspace, device_supported,  # noqa: F401
                    gemm, gemv, gemv_max_m, linear, linear_awq, linear_group, linear_kernel, pack, packed_bytes,
-                   quant_error, raw, scale_activations, unpack, workspace_bytes)
+                   QUALITY_FIELDS, quant_error, raw, scale_activations, unpack, workspace_bytes)

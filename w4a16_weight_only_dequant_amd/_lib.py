@@ -219,8 +219,10 @@ def unpack(pw: PackedWeight, stream=None):
 class Workspace:
     """Device workspace handed to the compute calls.
 
-    The calls take a workspace argument sized by w4a16_workspace_bytes; the
-    current kernels need none (0 bytes), so no buffer is allocated then.
+    The calls take a workspace argument sized by w4a16_workspace_bytes: the
+    stream-K split of the tiled GEMM keeps its partial tiles there, and every
+    other launch needs none (0 bytes), so no buffer is allocated then. The
+    buffer only grows; calls that overlap in time need workspaces of their own.
     """
 
     def __init__(self, device=None):
@@ -323,23 +325,30 @@ def linear(x, pw, out=None, workspace=None, stream=None):
 QUALITY_FIELDS = ("mse", "snr_db", "cos", "max_err", "sum_d2", "sum_w2", "sum_h2", "sum_wh")
 
 
-def quant_error(w: torch.Tensor, pw: PackedWeight, stream=None) -> dict:
+def quant_error(w: torch.Tensor, pw: PackedWeight, stream=None, out=None, workspace=None):
     """Quality report of packed weights against the fp32 weights [N][K] (device)
     they were made from (w4a16_quant_error): MSE, SNR dB, cosine, max error and
-    the fp64 sums behind them."""
+    the fp64 sums behind them, as a dict. With `out` (a float64 CUDA tensor of
+    8) the report is written there in QUALITY_FIELDS order and `out` is
+    returned without waiting for it; `workspace` is a Workspace to reuse."""
     if w.dtype != torch.float32 or w.dim() != 2 or not w.is_cuda or tuple(w.shape) != (pw.N, pw.K):
         raise TypeError(f"w must be a float32 CUDA tensor [{pw.N}][{pw.K}]")
     w = w.contiguous()
     nb = _sz()
     _check("w4a16_quant_error_workspace_bytes",
            _lib.w4a16_quant_error_workspace_bytes(pw.N, pw.K, pw.group, ctypes.byref(nb)))
-    ws = torch.empty(max(nb.value, 16), dtype=torch.uint8, device=w.device)
-    out = torch.empty(8, dtype=torch.float64, device=w.device)
+    ws = (workspace or Workspace(w.device)).get(max(nb.value, 16))
+    res = out
+    if res is None:
+        res = torch.empty(8, dtype=torch.float64, device=w.device)
+    elif res.dtype != torch.float64 or res.numel() != 8 or not res.is_contiguous() or res.device != w.device:
+        raise ValueError("out must be a contiguous float64 tensor of 8 on the weights' device")
     _check("w4a16_quant_error", _lib.w4a16_quant_error(
         w.data_ptr(), pw.qweight.data_ptr(), pw.scales.data_ptr(), pw.zeros_ptr(), pw.N, pw.K, pw.group,
-        _fmt_code(pw.fmt), out.data_ptr(), ws.data_ptr(), ws.numel(), _stream_ptr(stream)))
-    vals = out.cpu().tolist()
-    return dict(zip(QUALITY_FIELDS, vals))
+        _fmt_code(pw.fmt), res.data_ptr(), ws.data_ptr(), ws.numel(), _stream_ptr(stream)))
+    if out is not None:
+        return out
+    return dict(zip(QUALITY_FIELDS, res.cpu().tolist()))
 
 
 def scale_activations(x: torch.Tensor, act_mul: torch.Tensor, out=None, stream=None):

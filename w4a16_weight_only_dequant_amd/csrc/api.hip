@@ -432,7 +432,7 @@ w4a16_status w4a16_linear(const void *x, int32_t dtype, const void *qweight, con
 
 w4a16_status w4a16_quant_error_workspace_bytes(int64_t N, int64_t K, int32_t group, size_t *bytes) {
     if (!bytes || !shape_ok(N, K, group)) return W4A16_ERR_INVALID_ARG;
-    *bytes = quant_error_partial_bytes((int)N);
+    *bytes = quant_error_partial_bytes((int)N, (int)K);
     return W4A16_OK;
 }
 
@@ -443,7 +443,7 @@ w4a16_status w4a16_quant_error(const float *w, const void *qweight, const void *
     const bool zp = fmt == W4A16_FMT_ASYM4;
     if (!w || !qweight || !scales || (zp && !zeros) || !out) return W4A16_ERR_INVALID_ARG;
     if (!aligned16(w) || !aligned16(qweight) || !aligned16(out)) return W4A16_ERR_INVALID_ARG;
-    const size_t need = quant_error_partial_bytes((int)N);
+    const size_t need = quant_error_partial_bytes((int)N, (int)K);
     if (!workspace || workspace_bytes < need) return W4A16_ERR_WORKSPACE;
     if (!aligned16(workspace)) return W4A16_ERR_INVALID_ARG;
     size_t qb, sb, zb;

@@ -4,10 +4,10 @@
 // comparison page lists ("Implementation Architecture"): mean squared error,
 // signal-to-noise ratio in dB, cosine similarity and largest error between the
 // fp32 weights and the weights the packed data rebuilds, w_hat = s * (q - z),
-// over the whole matrix, in fp64. One workgroup per 16-row block streams the
-// fp32 weights and the packed codes once and writes five partial sums; one
-// workgroup then folds the partials in a fixed order (deterministic) and
-// derives the four figures.
+// over the whole matrix, in fp64. One workgroup per (16-row block, slice of
+// K's 128-weight columns) streams its share of the fp32 weights and the packed
+// codes once and writes five partial sums; one workgroup then folds the
+// partials in a fixed order (deterministic) and derives the four figures.
 //
 // AWQ's run-time half: the activations are multiplied by per-input-channel
 // fp32 factors (the reciprocals of the factors the weights were scaled up by
@@ -16,6 +16,8 @@
 // folds this into its activation staging; this elementwise kernel serves the
 // other paths.
 #include <math.h>
+
+#include <algorithm>
 
 #include "decode_common.hpp"
 
@@ -28,37 +30,64 @@ struct Sums5 {
     double d2, w2, h2, wh, mx;
 };
 
-__device__ inline void block_reduce(Sums5 &v, double (*sh)[kQeThreads]) {
-    const int t = threadIdx.x;
-    sh[0][t] = v.d2;
-    sh[1][t] = v.w2;
-    sh[2][t] = v.h2;
-    sh[3][t] = v.wh;
-    sh[4][t] = v.mx;
-    __syncthreads();
-    for (int o = kQeThreads / 2; o > 0; o >>= 1) {
-        if (t < o) {
-            sh[0][t] += sh[0][t + o];
-            sh[1][t] += sh[1][t + o];
-            sh[2][t] += sh[2][t + o];
-            sh[3][t] += sh[3][t + o];
-            sh[4][t] = fmax(sh[4][t], sh[4][t + o]);
-        }
-        __syncthreads();
+// Fixed-order reduction of the workgroup's sums into every lane of wave 0:
+// a butterfly inside each wave, then wave 0 adds the waves' totals in order.
+__device__ inline void block_reduce(Sums5 &v, double (*sh)[kQeThreads / 64]) {
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) {
+        v.d2 += __shfl_xor(v.d2, o);
+        v.w2 += __shfl_xor(v.w2, o);
+        v.h2 += __shfl_xor(v.h2, o);
+        v.wh += __shfl_xor(v.wh, o);
+        v.mx = fmax(v.mx, __shfl_xor(v.mx, o));
     }
+    const int wave = threadIdx.x / 64;
+    if (threadIdx.x % 64 == 0) {
+        sh[0][wave] = v.d2;
+        sh[1][wave] = v.w2;
+        sh[2][wave] = v.h2;
+        sh[3][wave] = v.wh;
+        sh[4][wave] = v.mx;
+    }
+    __syncthreads();
     v = Sums5{sh[0][0], sh[1][0], sh[2][0], sh[3][0], sh[4][0]};
+#pragma unroll
+    for (int i = 1; i < kQeThreads / 64; ++i) {
+        v.d2 += sh[0][i];
+        v.w2 += sh[1][i];
+        v.h2 += sh[2][i];
+        v.wh += sh[3][i];
+        v.mx = fmax(v.mx, sh[4][i]);
+    }
 }
 
-// One workgroup per row block b: thread i walks the block's (row, 8-weight
-// dword) pairs, rebuilds the eight weights from the packed layout and
-// accumulates against the fp32 originals.
+// Slices of K per row block: enough workgroups to fill the chip (a row block
+// alone is too little work for the 5120-row matrices), never less than one
+// 128-weight column each.
+#ifndef W4A16_QE_TARGET_WGS
+#define W4A16_QE_TARGET_WGS 2048
+#endif
+constexpr int kQeTargetWgs = W4A16_QE_TARGET_WGS;
+inline int qe_slices(int N, int K) {
+    const int64_t blocks = ceil_div(N, kRowBlock), cols = ceil_div(K, kColumn);
+    return (int)std::max<int64_t>(1, std::min<int64_t>(cols, ceil_div(kQeTargetWgs, blocks)));
+}
+
+// Workgroup g = b * slices + s takes row block b and the columns
+// [s * cols / slices, (s + 1) * cols / slices): thread i walks its (row,
+// 8-weight dword) pairs, rebuilds the eight weights from the packed layout
+// and accumulates against the fp32 originals.
 __global__ __launch_bounds__(kQeThreads) void quant_error_partial_kernel(
     const float *__restrict__ w, const uint32_t *__restrict__ qw, const uint16_t *__restrict__ scales,
-    const uint32_t *__restrict__ zeros, int N, int K, int group, int fmt, double *__restrict__ partial) {
-    __shared__ double sh[5][kQeThreads];
-    const int b = blockIdx.x;
+    const uint32_t *__restrict__ zeros, int N, int K, int group, int fmt, int slices,
+    double *__restrict__ partial) {
+    __shared__ double sh[5][kQeThreads / 64];
+    const int b = blockIdx.x / slices, sl = blockIdx.x % slices;
     const int rows = min(kRowBlock, N - b * kRowBlock);
-    const int KD = K / 8;
+    const int cols = (K + kColumn - 1) / kColumn;
+    const int kd0 = (int)((int64_t)sl * cols / slices) * (kColumn / 8);
+    const int kd1 = min(K / 8, (int)((int64_t)(sl + 1) * cols / slices) * (kColumn / 8));
+    const int KD = kd1 - kd0;
     const int kgroup = group < kColumn ? group : kColumn;     // group of the metadata slot
     const int gpc = kColumn / kgroup;                         // slots per column
     const int mshift = group > kColumn ? 1 : 0;               // group 256: one slot per two columns
@@ -66,7 +95,7 @@ __global__ __launch_bounds__(kQeThreads) void quant_error_partial_kernel(
     const uint32_t fixed_zero = fmt == kSym8 ? 128u : (fmt == kKq4 ? 0u : 8u);
     Sums5 v{0.0, 0.0, 0.0, 0.0, 0.0};
     for (int i = threadIdx.x; i < rows * KD; i += kQeThreads) {
-        const int r = i / KD, kd = i % KD;
+        const int r = i / KD, kd = kd0 + i % KD;
         const int n = b * kRowBlock + r;
         const int k0 = kd * 8;
         const int64_t off = dword_offset(n, kd / 4, kd % 4, N, K);
@@ -106,7 +135,7 @@ __global__ __launch_bounds__(kQeThreads) void quant_error_partial_kernel(
     }
     block_reduce(v, sh);
     if (threadIdx.x == 0) {
-        double *o = partial + (int64_t)b * 5;
+        double *o = partial + (int64_t)blockIdx.x * 5;
         o[0] = v.d2;
         o[1] = v.w2;
         o[2] = v.h2;
@@ -119,7 +148,7 @@ __global__ __launch_bounds__(kQeThreads) void quant_error_partial_kernel(
 __global__ __launch_bounds__(kQeThreads) void quant_error_final_kernel(const double *__restrict__ partial,
                                                                        int blocks, double count,
                                                                        double *__restrict__ out) {
-    __shared__ double sh[5][kQeThreads];
+    __shared__ double sh[5][kQeThreads / 64];
     Sums5 v{0.0, 0.0, 0.0, 0.0, 0.0};
     for (int b = threadIdx.x; b < blocks; b += kQeThreads) {
         const double *p = partial + (int64_t)b * 5;
@@ -183,14 +212,17 @@ __global__ __launch_bounds__(256) void scale_activations_kernel(const uint4 *__r
 
 }  // namespace
 
-size_t quant_error_partial_bytes(int N) { return (size_t)ceil_div(N, kRowBlock) * 5 * sizeof(double); }
+size_t quant_error_partial_bytes(int N, int K) {
+    return (size_t)ceil_div(N, kRowBlock) * qe_slices(N, K) * 5 * sizeof(double);
+}
 
 hipError_t launch_quant_error(const float *w, const void *qweight, const void *scales, const void *zeros, int N,
                               int K, int group, int fmt, double *out, double *partial, hipStream_t stream) {
-    const int blocks = (int)ceil_div(N, kRowBlock);
+    const int slices = qe_slices(N, K);
+    const int blocks = (int)ceil_div(N, kRowBlock) * slices;
     hipLaunchKernelGGL(quant_error_partial_kernel, dim3(blocks), dim3(kQeThreads), 0, stream, w,
                        reinterpret_cast<const uint32_t *>(qweight), reinterpret_cast<const uint16_t *>(scales),
-                       reinterpret_cast<const uint32_t *>(zeros), N, K, group, fmt, partial);
+                       reinterpret_cast<const uint32_t *>(zeros), N, K, group, fmt, slices, partial);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL(quant_error_final_kernel, dim3(1), dim3(kQeThreads), 0, stream, partial, blocks,

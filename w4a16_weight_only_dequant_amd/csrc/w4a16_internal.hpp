@@ -136,9 +136,9 @@ hipError_t launch_pack(const float *w, int N, int K, int group, int fmt, void *q
 hipError_t launch_unpack(const void *qweight, const void *scales, const void *zeros,
                          int N, int K, int group, int fmt, uint8_t *codes, uint16_t *scales_out,
                          uint8_t *zeros_out, hipStream_t stream);
-// Quality report: five fp64 sums per row block into `partial`, then one
-// workgroup folds them in a fixed order into out[8].
-size_t quant_error_partial_bytes(int N);
+// Quality report: five fp64 sums per (row block, slice of K) into `partial`,
+// then one workgroup folds them in a fixed order into out[8].
+size_t quant_error_partial_bytes(int N, int K);
 hipError_t launch_quant_error(const float *w, const void *qweight, const void *scales, const void *zeros,
                               int N, int K, int group, int fmt, double *out, double *partial,
                               hipStream_t stream);
