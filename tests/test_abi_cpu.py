@@ -103,6 +103,19 @@ def test_compute_calls_validate_before_device(w4):
     assert lib.w4a16_workspace_bytes(-1, 64, 128, 128, ctypes.byref(ws)) == 1
 
 
+def test_awq_workspace_must_not_overlap_the_weights(w4):
+    """The unfused AWQ path (M > 8) writes the scaled activations into the
+    workspace: a workspace that overlaps the packed codes, scales or
+    zero-points is refused before the device is touched."""
+    lib = w4.raw()
+    M, N, K, g = 16, 64, 256, 128
+    ws = ctypes.c_size_t(0)
+    assert lib.w4a16_awq_workspace_bytes(M, N, K, g, 0, 0, ctypes.byref(ws)) == 0 and ws.value >= M * K * 2
+    x, m, q, s, z, y = (ctypes.c_void_p(a << 24) for a in (1, 2, 3, 4, 5, 6))   # never dereferenced
+    for at in (q, s, z):
+        assert lib.w4a16_linear_awq(x, 0, m, q, s, z, y, M, N, K, g, 0, at, ws.value, None) == 1
+
+
 def test_empty_batch_is_a_no_op(w4):
     """M = 0: the shape, type and format arguments are checked, no pointer is
     read (all NULL here), nothing is enqueued (no device is needed), OK."""

@@ -503,8 +503,11 @@ w4a16_status w4a16_linear_awq(const void *x, int32_t dtype, const float *act_mul
         if (!workspace || workspace_bytes < need) return W4A16_ERR_WORKSPACE;
         if (!aligned16(workspace)) return W4A16_ERR_INVALID_ARG;
         const Range rw = range_of(workspace, need);
+        size_t qb, sb, zb;
+        meta_bytes(N, K, group, fmt, &qb, &sb, &zb);
         if (overlap(rw, range_of(y, (size_t)(M * N * 2))) || overlap(rw, range_of(x, (size_t)(M * K * 2))) ||
-            overlap(rw, range_of(act_mul, (size_t)K * 4)))
+            overlap(rw, range_of(act_mul, (size_t)K * 4)) || overlap(rw, range_of(qweight, qb)) ||
+            overlap(rw, range_of(scales, sb)) || overlap(rw, range_of(zeros, zb)))
             return W4A16_ERR_INVALID_ARG;
     }
     st = check_device();
