@@ -211,3 +211,36 @@ def test_concurrent_calls_on_two_streams():
         t.join(timeout=60)
     assert not any(t.is_alive() for t in threads)
     assert not errors, errors
+
+
+@pytest.mark.parametrize("M,N,K,group", [(2048, 8448, 512, 128), (2048, 24832, 512, 128), (1024, 8448, 1024, 64),
+                                         (2048, 4096, 512, 128), (1, 1024, 8192, 128), (8, 5120, 2048, 32)])
+def test_workspace_bytes_are_enough_and_nothing_beyond_is_written(M, N, K, group):
+    """Every product call succeeds with exactly w4a16_workspace_bytes of
+    workspace, writes nothing past it (a guard region after it keeps its
+    pattern), gives the same output as with a generous workspace, and is
+    refused with one byte less."""
+    import torch
+    w4 = H.lib()
+    w, o, pw = _prep(N, K, group)
+    x = H.to_device_bits(wl.random_activations(M + 3, M, K, "bf16"), "bf16")
+    nbytes = w4.workspace_bytes(M, N, K, group)
+    guard = 1 << 16
+    buf = torch.full((nbytes + guard,), 0xA5, dtype=torch.uint8, device="cuda")
+    big = torch.zeros(nbytes + (1 << 20), dtype=torch.uint8, device="cuda")
+    calls = ["w4a16_gemm", "w4a16_linear"] + (["w4a16_gemv"] if M <= 8 else [])
+    for fn in calls:
+        y = torch.empty((M, N), dtype=torch.bfloat16, device="cuda")
+        y_ref = torch.empty_like(y)
+        args = (x.data_ptr(), 1, pw.qweight.data_ptr(), pw.scales.data_ptr(), pw.zeros_ptr())
+        shape = (M, N, K, group)
+        st = getattr(w4.raw(), fn)(*args, y.data_ptr(), *shape, buf.data_ptr() if nbytes else None, nbytes, None)
+        assert st == 0, (fn, st)
+        assert getattr(w4.raw(), fn)(*args, y_ref.data_ptr(), *shape, big.data_ptr(), big.numel(), None) == 0
+        torch.cuda.synchronize()
+        assert bool((buf[nbytes:] == 0xA5).all()), f"{fn} wrote past its workspace"
+        assert torch.equal(y.view(torch.int16), y_ref.view(torch.int16)), fn
+        if nbytes:
+            assert getattr(w4.raw(), fn)(*args, y.data_ptr(), *shape, buf.data_ptr(), nbytes - 1, None) == 4, fn
+    H.check_against_oracle(y, wl.random_activations(M + 3, M, K, "bf16"), "bf16", o, group, cols=_cols(N, 5))
+    H.drop(("sk", N, K, group))
