@@ -15,9 +15,12 @@ pytestmark = pytest.mark.gpu
 
 # (M, N, K, group), 256 x 256 tiles: 8 x 33 = 264 tiles (a last round of 8
 # tiles: every workgroup shares tiles), the same with ragged K (a partial last
-# column in the tail segments) and with group 64, and 8 x 97 = 776 tiles (two
-# rounds of whole tiles, then the last 264 tiles split)
-SK_SHAPES = [(2048, 8448, 512, 128), (2048, 8448, 672, 32), (2048, 8448, 1024, 64), (2048, 24832, 512, 128)]
+# column in the tail segments), with group 64, with group 256 (one metadata
+# slot per two columns) and with ragged M (the last tile row holds 208 rows),
+# and 8 x 97 = 776 tiles (two rounds of whole tiles, then the last 264 tiles
+# split)
+SK_SHAPES = [(2048, 8448, 512, 128), (2048, 8448, 672, 32), (2048, 8448, 1024, 64), (2048, 8448, 1024, 256),
+             (2000, 8448, 512, 128), (2048, 24832, 512, 128)]
 
 
 def _prep(N, K, group, fmt="asym4"):
