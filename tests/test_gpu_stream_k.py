@@ -247,3 +247,18 @@ def test_workspace_bytes_are_enough_and_nothing_beyond_is_written(M, N, K, group
             assert getattr(w4.raw(), fn)(*args, y.data_ptr(), *shape, buf.data_ptr(), nbytes - 1, None) == 4, fn
     H.check_against_oracle(y, wl.random_activations(M + 3, M, K, "bf16"), "bf16", o, group, cols=_cols(N, 5))
     H.drop(("sk", N, K, group))
+
+
+def test_stream_k_full_size_ffn_shape():
+    """M = 2048, N = 11008, K = 4096 (a 7B-style FFN width: 344 tiles, the last
+    two rounds split): long segments of 32-column tiles, every row of 160
+    sampled columns against the oracle."""
+    import torch
+    M, N, K, group = 2048, 11008, 4096, 128
+    assert _uses_stream_k(M, N, K, group)
+    w, o, pw = _prep(N, K, group)
+    x = wl.random_activations(77, M, K, "bf16")
+    y = H.lib().linear(H.to_device_bits(x, "bf16"), pw)
+    torch.cuda.synchronize()
+    H.check_against_oracle(y, x, "bf16", o, group, cols=np.unique(np.concatenate([_cols(N, 8), N - 256 + np.arange(32)])))
+    H.drop(("sk", N, K, group))
