@@ -48,7 +48,7 @@ WORKLOAD_IDS = {"gemv_4096": 1, "decode_13b_layer": 2, "fused_qkv": 3, "prefill"
 
 # sources each kernel is built from (for matching stored counter results)
 KERNEL_SOURCES = {
-    "gemv": ["gemv.hip", "gemv_kernel.hpp", "decode_common.hpp", "w4a16_internal.hpp"],
+    "gemv": ["decode.hip", "decode_kernel.hpp", "decode_common.hpp", "w4a16_internal.hpp"],
     "skinny": ["gemm.hip", "gemm_kernel.hpp", "decode_common.hpp", "w4a16_internal.hpp"],
     "prefill": ["prefill.hip", "prefill_kernel.hpp", "decode_common.hpp", "w4a16_internal.hpp"],
 }

@@ -58,21 +58,20 @@
  *            the high half-word. A full column of a full block is one
  *            contiguous KiB in which the 16 bytes at 256d + 16r are dword d of
  *            the column's four chunks of row r.
- *   scales   fp16 [T][N][128/group] the group scales of row n in column t, in
- *                                   k order (slots past K hold 0)
- *   zeros    uint32 [T][N*128/group/8]  4-bit zero-points in the same order:
- *                                   entry (t, n, e) is nibble (n*128/group + e)
- *                                   of column t's words (slots past K hold 0)
- *            For K % 128 == 0 both have the canonical sizes 2*G*N and G*N/2
- *            bytes (G = K/group), and at group 128 they are exactly [G][N]
- *            and [G][N/8]. Group 256 (K % 256 == 0) uses the same [G][N] and
- *            [G][N/8] layouts, one slot per group: column t reads slot t/2.
+ *   scales   fp16 [N][G8]           row n's group scales in k order, G = K/group
+ *                                   and G8 = G rounded up to a multiple of 8
+ *                                   (slots g >= G hold 0): one row's scales
+ *                                   along K are contiguous
+ *   zeros    uint32 [N][G8/8]       4-bit zero-points: group g of row n is
+ *                                   bits 4*(g%8) .. 4*(g%8)+3 of word n*G8/8 + g/8
+ *                                   (slots g >= G hold 0)
+ *            With G % 8 == 0 the sizes are the canonical 2*G*N and G*N/2 bytes.
  *   SYM4     qweight as above (codes q + 8), scales as above, no zeros.
  *   SYM8     qweight N*K bytes: two 4-bit planes in the layout above, the low
  *            nibbles of every code in bytes [0, N*K/2), the high nibbles in
  *            [N*K/2, N*K); scales as above, no zeros.
  *   KQ4      qweight as above; `scales` holds one 16-byte record per
- *            (super-block u, row n) in [K/256][N] order: four little-endian
+ *            (row n, super-block u) in [N][K/256] order: four little-endian
  *            words {d | dmin << 16, sc bits 0-31, sc bits 32-47 | mq bits 0-15
  *            << 16, mq bits 16-47}, sc and mq being 48-bit fields of eight
  *            6-bit values (sub-block j at bits 6j..6j+5); no zeros. K % 256 == 0.
@@ -117,7 +116,7 @@
 extern "C" {
 #endif
 
-#define W4A16_LAYOUT_VERSION 2
+#define W4A16_LAYOUT_VERSION 3
 
 typedef enum {
     W4A16_OK = 0,
@@ -154,8 +153,8 @@ int w4a16_layout_version(void);
 w4a16_status w4a16_device_supported(int device);
 
 /* Byte sizes of the packed buffers for an N x K weight matrix: qweight
- * N*K/2, scales 2*T*N*(128/group), zeros T*N*(128/group)/2 with
- * T = ceil(K/128) (group 256: 2*G*N and G*N/2). For K % 128 == 0 these are 2*G*N and G*N/2: 4 + 20/group
+ * N*K/2, scales 2*G8*N, zeros G8*N/2 (G8 = K/group rounded up to a multiple
+ * of 8). With (K/group) % 8 == 0 these are 2*G*N and G*N/2: 4 + 20/group
  * bits per weight, the 4.156 bits/weight at group 128 of "Weight-Only
  * Quantization Explained", "The memory arithmetic". Host-only; any
  * out-pointer may be NULL. */
@@ -212,11 +211,18 @@ w4a16_status w4a16_unpack_fmt(const void *qweight, const void *scales, const voi
                               void *stream);
 
 /* Decode GEMV: y [M][N] = x [M][K] . w_hat^T for small M (M <= 8).
- * One pass over the packed weights: 128-bit loads, in-register unpack, fp16
- * or bf16 dot products with fp32 accumulation, per-group scale; the waves of
- * a workgroup split K and meet in LDS in a fixed order (deterministic). The
- * activations are staged in LDS: returns W4A16_ERR_INVALID_ARG for M > 8 or
- * when M*K does not fit (w4a16_gemm has no such limit). */
+ * One pass over the packed weights: one workgroup per 16-row block holds all
+ * of K (up to 16 waves of eight or sixteen 128-weight columns each),
+ * 128-bit loads, in-register unpack, packed fp16 / bf16 dot products with
+ * fp32 accumulation, the group scale and zero-point applied once per group;
+ * the waves meet in LDS in a fixed order (deterministic). Range: the
+ * activations and metadata it stages in LDS fit 160 KiB, which bounds K by
+ *            M = 1    M = 2    M = 3..4   M = 5..8
+ *   g 32     32768    22528    12288      6144
+ *   g 64     32768    28672    15360      7168
+ *   g 128+   32768    32768    16384      8192
+ * Outside it, and for M > 8, W4A16_ERR_INVALID_ARG (w4a16_gemm and
+ * w4a16_linear have no such limit). */
 w4a16_status w4a16_gemv(const void *x, int32_t dtype, const void *qweight,
                         const void *scales, const void *zeros, void *y,
                         int64_t M, int64_t N, int64_t K, int32_t group,
@@ -322,7 +328,7 @@ w4a16_status w4a16_quant_error(const float *w, const void *qweight, const void *
  * product rounded once (to nearest even) to x's type. x_out may be x itself.
  *
  * w4a16_linear_awq: y = x_out . w_hat'^T. When the GEMV takes the shape
- * (M <= 8 and the activations fit its LDS) the scaling is folded into the
+ * (M <= 8, K within its range above and K <= 16384) the scaling is folded into the
  * GEMV's activation staging: one launch, no workspace. Otherwise it runs
  * w4a16_scale_activations into the workspace (w4a16_awq_workspace_bytes:
  * M*K*2 rounded up to 256, then w4a16_workspace_bytes for the product)

@@ -314,14 +314,13 @@ def dequantize(codes, scale_bits, zeros, group: int) -> np.ndarray:
 #   So for a full column the 16 rows x 4 dword positions form one contiguous
 #   KiB in which the 16 bytes at d*256 + r*16 are dword d of the column's four
 #   chunks of row r. Dwords are little-endian.
-#   Metadata per column (GPC = 128/group groups per column, T = ceil(C/4)
-#   columns; a short last column keeps its unused group slots, filled with 0):
-#   scales: fp16 bits [T][N][GPC] (group g = GPC*t + e is element e).
-#   zeros: u32 words [T][N*GPC/8]; the GPC zero-points of row n in column t are
-#   nibbles GPC*(n % (8/GPC)) + e of word n // (8/GPC).
-#   At group 128 (GPC = 1) these are the plain [G][N] and [G][N/8] layouts;
-#   group 256 uses the same plain layouts, one slot per group, and column t
-#   reads slot t // 2.
+#   Metadata (layout 3), one row after another so that a row's metadata for a
+#   run of K is contiguous: G = K/group groups per row, padded to G8 (the next
+#   multiple of 8; padded slots hold 0).
+#   scales: fp16 bits [N][G8] (group g of row n is element n*G8 + g).
+#   zeros: u32 words [N][G8/8]; group g of row n is nibble g % 8 of word
+#   n*(G8/8) + g // 8 (little-endian words, nibble i at bits 4i..4i+3).
+#   K-quant super-block records: [N][K/256] of 16 bytes.
 #   8-bit codes (sym8) are two 4-bit planes, each in the qweight layout above:
 #   the low nibbles of every code first (N*K/2 bytes), then the high nibbles.
 #   The symmetric formats store no zero words.
@@ -394,52 +393,39 @@ def unpack_zeros(words, G: int, N: int) -> np.ndarray:
     return out.reshape(G, N)
 
 
-def _gpc(group: int) -> int:
-    """Metadata slots per 128-weight column (group 256: one slot per two columns)."""
-    return max(1, 128 // group)
-
-
-def _padded_groups(G: int, group: int) -> int:
-    """Group slots of the per-column metadata layout: T columns of 128/group groups
-    (group 256: exactly G slots)."""
-    gpc = _gpc(group)
-    return -(-G // gpc) * gpc
+def padded_groups(G: int) -> int:
+    """G8: metadata slots per row, the group count rounded up to a multiple of 8."""
+    return -(-G // 8) * 8
 
 
 def pack_scales_device(scale_bits, group: int) -> np.ndarray:
-    """scale bits [G][N] -> device order [T][N][GPC] (uint16), unused slots 0."""
+    """scale bits [G][N] -> device order [N][G8] (uint16), padded slots 0."""
     s = np.asarray(scale_bits, dtype=np.uint16)
     G, N = s.shape
-    gpc = _gpc(group)
-    Gp = _padded_groups(G, group)
-    full = np.zeros((Gp, N), dtype=np.uint16)
-    full[:G] = s
-    return np.ascontiguousarray(full.reshape(Gp // gpc, gpc, N).transpose(0, 2, 1))
+    out = np.zeros((N, padded_groups(G)), dtype=np.uint16)
+    out[:, :G] = s.T
+    return out
 
 
 def pack_zeros_device(zeros, group: int) -> np.ndarray:
-    """zero-points u8 [G][N] -> device words [T][N*GPC/8] (uint32), unused slots 0.
-
-    The GPC nibbles of (column t, row n) are consecutive: nibble index
-    n*GPC + e within the column, eight nibbles per little-endian word."""
+    """zero-points u8 [G][N] -> device words [N][G8/8] (uint32), padded slots 0:
+    group g of row n is nibble g % 8 of word g // 8 of the row."""
     z = np.asarray(zeros, dtype=np.uint32)
     G, N = z.shape
-    gpc = _gpc(group)
-    Gp = _padded_groups(G, group)
-    full = np.zeros((Gp, N), dtype=np.uint32)
-    full[:G] = z
-    nib = full.reshape(Gp // gpc, gpc, N).transpose(0, 2, 1).reshape(Gp // gpc, N * gpc)
-    nib = nib.reshape(Gp // gpc, N * gpc // 8, 8)
-    word = np.zeros(nib.shape[:2], dtype=np.uint32)
-    for t in range(8):
-        word |= nib[:, :, t] << np.uint32(4 * t)
+    G8 = padded_groups(G)
+    full = np.zeros((N, G8), dtype=np.uint32)
+    full[:, :G] = z.T
+    nib = full.reshape(N, G8 // 8, 8)
+    word = np.zeros((N, G8 // 8), dtype=np.uint32)
+    for i in range(8):
+        word |= nib[:, :, i] << np.uint32(4 * i)
     return word
 
 
 def device_meta_bytes(N: int, K: int, group: int, fmt: str = "asym4"):
-    """(scales, zeros) byte counts of the per-column metadata layout."""
-    Gp = _padded_groups(K // group, group)
-    return 2 * Gp * N, Gp * N // 2 if fmt == "asym4" else 0
+    """(scales, zeros) byte counts of the device metadata layout."""
+    G8 = padded_groups(K // group)
+    return 2 * G8 * N, G8 * N // 2 if fmt == "asym4" else 0
 
 
 def quantize_and_pack(w, group: int, fmt: str = "asym4"):
@@ -596,7 +582,8 @@ def awq_scale_activations(x_bits, dtype: str, act_mul):
 # Stored per (super-block u, output column n): a 16-byte record of four
 # little-endian words {d | dmin << 16, sc bits 0-31, sc bits 32-47 | mq bits
 # 0-15 << 16, mq bits 16-47}, where sc and mq are 48-bit fields holding the
-# eight 6-bit values at bits 6j..6j+5; records in [U][N] order (U = K / 256).
+# eight 6-bit values at bits 6j..6j+5; canonical records in [U][N] order
+# (U = K / 256); the device keeps each row's records together, [N][U].
 # 4 + 128/256 = 4.5 bits per weight.
 # ---------------------------------------------------------------------------
 
@@ -658,6 +645,12 @@ def dequantize_kquant(codes, d_bits, m_bits, sc, mq) -> np.ndarray:
     S, M = kquant_sub_params(d_bits, m_bits, sc, mq)
     q = codes.reshape(N, K // KQ_SUB, KQ_SUB).astype(np.float64)
     return (q * S[:, :, None] - M[:, :, None]).reshape(N, K)
+
+
+def pack_kquant_device(d_bits, m_bits, sc, mq) -> np.ndarray:
+    """Super-block records in device order, uint32 [N][U][4] (one row's records
+    contiguous along K)."""
+    return np.ascontiguousarray(pack_kquant_records(d_bits, m_bits, sc, mq).transpose(1, 0, 2))
 
 
 def pack_kquant_records(d_bits, m_bits, sc, mq) -> np.ndarray:

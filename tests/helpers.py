@@ -18,7 +18,7 @@ def oracle_pack(w: np.ndarray, group: int, fmt: str = "asym4"):
         codes, d_bits, m_bits, sc, mq = ref.quantize_kquant(w)
         return {"codes": codes, "fmt": fmt, "kq": (d_bits, m_bits, sc, mq),
                 "qweight": ref.pack_device(codes),
-                "records": ref.pack_kquant_records(d_bits, m_bits, sc, mq).ravel(),
+                "records": ref.pack_kquant_device(d_bits, m_bits, sc, mq).ravel(),
                 "zeros_dev": None}
     codes, s_bits, zeros = ref.quantize_groupwise(w, group, fmt)
     return {

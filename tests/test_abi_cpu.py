@@ -47,7 +47,7 @@ def test_library_exports_only_the_c_abi(w4):
 
 def test_status_strings_and_version(w4):
     lib = w4.raw()
-    assert lib.w4a16_layout_version() == 2
+    assert lib.w4a16_layout_version() == 3
     for code in range(5):
         assert lib.w4a16_status_string(code)
     assert lib.w4a16_status_string(99) == b"unknown status"
@@ -59,10 +59,11 @@ def test_packed_bytes_closed_form(w4, N, K, group):
     G = K // group
     q, s, z = w4.packed_bytes(N, K, group)
     assert q == N * K // 2
-    # metadata per 128-weight column: 128/group slots; exact 2GN / GN/2 when K % 128 == 0
-    slots = -(-K // 128) * (128 // group)
+    # metadata row-major, each row's G groups padded to a multiple of 8 slots;
+    # exactly 2GN / GN/2 when G % 8 == 0
+    slots = -(-G // 8) * 8
     assert (s, z) == (2 * slots * N, slots * N // 2)
-    if K % 128 == 0:
+    if G % 8 == 0:
         assert (s, z) == (2 * G * N, G * N // 2)
 
 
@@ -197,7 +198,7 @@ def test_product_path_never_touches_the_oracle():
 
 @pytest.mark.parametrize("N,K,group", [(4096, 4096, 128), (72, 768, 256), (5120, 13824, 256), (72, 160, 32)])
 def test_packed_bytes_formats(w4, N, K, group):
-    slots = K // 256 if group == 256 else -(-K // 128) * (128 // group)
+    slots = -(-(K // group) // 8) * 8
     assert w4.packed_bytes(N, K, group, "asym4") == (N * K // 2, 2 * slots * N, slots * N // 2)
     assert w4.packed_bytes(N, K, group, "sym4") == (N * K // 2, 2 * slots * N, 0)
     assert w4.packed_bytes(N, K, group, "sym8") == (N * K, 2 * slots * N, 0)

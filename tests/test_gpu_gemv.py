@@ -17,25 +17,48 @@ def _run(fn, x_bits, dtype, pw):
     return y
 
 
+def _dec_lds_per_wave(mt, ncol, group):
+    """LDS bytes of one decode wave (4-bit zero-point format): activations,
+    activation sums, the 16 rows' scales and zero-point words, 16 spare bytes."""
+    upc = 1 if group >= 128 else 128 // group
+    meta_row = ncol if group >= 256 else ncol * (128 // group) * 2
+    zwords = (ncol // 2 + 7) // 8 if group >= 256 else (ncol * (128 // group) + 7) // 8
+    return mt * ncol * 256 + mt * ncol * upc * 32 + 16 * meta_row + 16 * zwords * 4 + 16
+
+
 def gemv_accepts(M, K, dtype, group=32):
-    """The GEMV stages activations and group metadata in one workgroup's LDS
-    (160 KiB on gfx950); conservative bound incl. the per-wave rounding of slices."""
-    lds = M * K * 2 * (1.0 + (64 / 256 if dtype == "bf16" else 0.0)) + (K // group) * 40 + 16 * 1024
-    return M <= 8 and lds <= 150 * 1024
+    """The decode kernel's range: M <= 8 and all of K in one workgroup of at
+    most 16 waves (8 columns of 128 weights per wave, or 16 for one or two
+    activation rows), its LDS within gfx950's 160 KiB per workgroup."""
+    if not 1 <= M <= 8:
+        return False
+    T = -(-(K // 32) // 4)
+    mt = 1 if M <= 1 else 2 if M <= 2 else 4 if M <= 4 else 8
+    if -(-T // 8) <= 16:
+        ncol = 8
+    elif mt <= 2 and -(-T // 16) <= 16:
+        ncol = 16
+    else:
+        return False
+    return -(-T // ncol) * _dec_lds_per_wave(mt, ncol, group) <= 160 * 1024
 
 
 SMALL = [(8, 32, 32), (72, 64, 32), (200, 96, 32), (136, 256, 64), (64, 384, 128), (328, 640, 128),
-         (1000, 1024, 64), (4104, 4096, 128), (520, 8192, 32)]
+         (1000, 1024, 64), (4104, 4096, 128), (520, 8192, 32), (40, 160, 32), (24, 1120, 32),
+         (48, 16384, 128), (24, 32768, 64)]
 
 
 @pytest.mark.parametrize("N,K,group", SMALL)
 @pytest.mark.parametrize("dtype", ["f16", "bf16"])
 @pytest.mark.parametrize("M", [1, 2, 3, 8])
 def test_gemv_small_shapes(N, K, group, dtype, M):
-    if not gemv_accepts(M, K, dtype, group):
-        pytest.skip("activations of this call exceed the GEMV's LDS stage")
     w, o, pw = H.prepared(("small", N, K, group), lambda: wl.random_weights(N + K, N, K), group)
     x = wl.random_activations(N * 31 + K + M, M, K, dtype)
+    if not gemv_accepts(M, K, dtype, group):
+        # outside the decode kernel's range: an invalid-argument error, no launch
+        with pytest.raises(H.lib().W4A16Error):
+            _run(H.lib().gemv, x, dtype, pw)
+        return
     y = _run(H.lib().gemv, x, dtype, pw)
     assert y.shape == (M, N)
     H.check_against_oracle(y, x, dtype, o, group)

@@ -365,27 +365,33 @@ def test_zero_packing_by_hand():
 
 
 def test_device_metadata_layout_by_hand():
-    # group 32: 4 groups per column; N = 8 rows, K = 160 -> G = 5 groups, 2 columns
+    # row-major metadata, each row padded to a multiple of 8 groups:
+    # group 32, N = 8 rows, K = 160 -> G = 5 groups, G8 = 8 slots per row
     G, N = 5, 8
-    s_bits = (np.arange(G * N, dtype=np.uint16).reshape(G, N) + 1)
-    z = (np.arange(G * N, dtype=np.uint8).reshape(G, N) % 16)
+    s_bits = (np.arange(G * N, dtype=np.uint16).reshape(G, N) + 1)   # s_bits[g, n] = 1 + 8 g + n
+    z = (np.arange(G * N, dtype=np.uint8).reshape(G, N) % 16)         # z[g, n] = (8 g + n) % 16
     ds = ref.pack_scales_device(s_bits, 32)
-    assert ds.shape == (2, 8, 4)
-    assert ds[0, 3].tolist() == [s_bits[0, 3], s_bits[1, 3], s_bits[2, 3], s_bits[3, 3]]
-    assert ds[1, 7].tolist() == [s_bits[4, 7], 0, 0, 0]
+    assert ds.shape == (8, 8)
+    # row 3: groups 0..4 are 1 + 3, 9 + 3, 17 + 3, 25 + 3, 33 + 3, then three padded zeros
+    assert ds[3].tolist() == [4, 12, 20, 28, 36, 0, 0, 0]
+    assert ds[7].tolist() == [8, 16, 24, 32, 40, 0, 0, 0]
     dz = ref.pack_zeros_device(z, 32)
-    assert dz.shape == (2, 4)
-    # column 0, rows 2 and 3 share word 1: nibbles (row 2: groups 0..3, row 3: groups 0..3)
-    want = 0
-    for e, (row, g) in enumerate([(2, 0), (2, 1), (2, 2), (2, 3), (3, 0), (3, 1), (3, 2), (3, 3)]):
-        want |= int(z[g, row]) << (4 * e)
-    assert int(dz[0, 1]) == want
-    # group 128 keeps the canonical [G][N] / [G][N/8] forms
-    z128 = (np.arange(3 * 16, dtype=np.uint8).reshape(3, 16) % 16)
-    assert np.array_equal(ref.pack_zeros_device(z128, 128), ref.pack_zeros(z128))
-    s128 = np.arange(3 * 16, dtype=np.uint16).reshape(3, 16)
-    assert np.array_equal(ref.pack_scales_device(s128, 128).reshape(3, 16), s128)
+    assert dz.shape == (8, 1)
+    # row 2: z = 2, 10, 18 % 16 = 2, 26 % 16 = 10, 34 % 16 = 2 in nibbles 0..4
+    assert int(dz[2, 0]) == 0x0002A2A2
+    # row 7: 7, 15, 23 % 16 = 7, 31 % 16 = 15, 39 % 16 = 7
+    assert int(dz[7, 0]) == 0x0007F7F7
     assert ref.device_meta_bytes(8, 160, 32) == (2 * 8 * 8, 8 * 8 // 2)
+    # group 128, K = 1280 -> G = 10 groups, G8 = 16: row n's 16 slots start at 32 n bytes
+    s10 = np.arange(10 * 16, dtype=np.uint16).reshape(10, 16)
+    d10 = ref.pack_scales_device(s10, 128)
+    assert d10.shape == (16, 16) and d10[5, 9] == s10[9, 5] and d10[5, 10] == 0
+    z10 = (np.arange(10 * 16, dtype=np.uint8).reshape(10, 16) % 16)
+    w10 = ref.pack_zeros_device(z10, 128)
+    assert w10.shape == (16, 2)
+    # row 1, groups 8 and 9 (z = (16 g + 1) % 16 = 1) in nibbles 0 and 1 of word 1
+    assert int(w10[1, 1]) == 0x00000011
+    assert ref.device_meta_bytes(16, 1280, 128) == (2 * 16 * 16, 16 * 16 // 2)
 
 
 # ---------------------------------------------------------------------------
@@ -511,16 +517,20 @@ def test_format_byte_accounting():
     assert ref.format_bits_per_weight(256, "sym8") == 8.0625
     assert ref.format_bits_per_weight(256, "asym4") == 4 + 20 / 256
     assert ref.packed_bytes(64, 512, 256, "sym8") == (64 * 512, 2 * 2 * 64, 0)
-    assert ref.device_meta_bytes(64, 512, 256, "sym4") == (2 * 2 * 64, 0)
+    assert ref.device_meta_bytes(64, 512, 256, "sym4") == (2 * 8 * 64, 0)
 
 
-def test_group256_metadata_is_the_plain_layout():
+def test_group256_metadata_layout():
     G, N = 3, 16
     s_bits = np.arange(1, G * N + 1, dtype=np.uint16).reshape(G, N)
     z = (np.arange(G * N, dtype=np.uint8).reshape(G, N) * 5) % 16
-    assert np.array_equal(ref.pack_scales_device(s_bits, 256).reshape(G, N), s_bits)
-    assert np.array_equal(ref.pack_zeros_device(z, 256), ref.pack_zeros(z))
-    assert ref.device_meta_bytes(N, 768, 256) == (2 * G * N, G * N // 2)
+    ds = ref.pack_scales_device(s_bits, 256)
+    assert ds.shape == (N, 8)
+    assert np.array_equal(ds[:, :G], s_bits.T) and not ds[:, G:].any()
+    dz = ref.pack_zeros_device(z, 256)
+    # row 4: z = (5 * (16 g + 4)) % 16 = 4 for g = 0, 1, 2
+    assert dz.shape == (N, 1) and int(dz[4, 0]) == 0x444
+    assert ref.device_meta_bytes(N, 768, 256) == (2 * 8 * N, 8 * N // 2)
 
 
 def test_group256_groups_span_two_columns():

@@ -12,7 +12,7 @@ CSRC = os.path.join(HERE, "csrc")
 OUT = os.path.join(HERE, "libw4a16.so")
 BUILD_DIR = os.path.join(ROOT, "_build")
 SOURCES = ["api.hip", "pack.hip", "quality.hip",
-           "gemv.hip", "gemv_sym4.hip", "gemv_sym8.hip", "gemv_kq4.hip",
+           "decode.hip", "decode_sym4.hip", "decode_sym8.hip", "decode_kq4.hip",
            "gemm.hip", "gemm_sym4.hip", "gemm_sym8.hip", "gemm_kq4.hip",
            "prefill.hip", "prefill_sym4.hip", "prefill_sym8.hip", "prefill_kq4.hip"]
 

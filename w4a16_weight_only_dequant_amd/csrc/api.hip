@@ -18,23 +18,9 @@ constexpr int kMaxDevices = 64;
 // 0 = not queried yet, 1 = gfx950, 2 = other device
 std::atomic<int> g_device_kind[kMaxDevices];
 
-int env_int(const char *name, int fallback) {
-    const char *v = std::getenv(name);
-    if (!v || !*v) return fallback;
-    char *end = nullptr;
-    long r = std::strtol(v, &end, 10);
-    return (end && *end == 0) ? (int)r : fallback;
-}
-
-// Largest M routed to the GEMV kernel by w4a16_linear (the GEMV kernel itself
-// accepts M <= 8). Measured: from M = 2 on the matrix-core kernel is faster.
-int gemv_max_m() {
-    static const int v = [] {
-        int m = env_int("W4A16_GEMV_MAX_M", 1);
-        return m < 0 ? 0 : (m > 8 ? 8 : m);
-    }();
-    return v;
-}
+// Largest M routed to the decode kernel by w4a16_linear (the decode kernel
+// itself accepts M <= 8): from M = 2 on the matrix-core kernel measured faster.
+int gemv_max_m() { return 1; }
 
 bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
@@ -54,20 +40,20 @@ bool fmt_ok(int32_t fmt) {
 bool fmt_group_ok(int32_t fmt, int32_t group) { return fmt_ok(fmt) && (fmt != W4A16_FMT_KQ4 || group == 256); }
 
 // Byte sizes of the packed buffers: codes (one 4-bit plane, two for 8-bit
-// codes), then scales and zero-points per 128-weight column (128/group slots
-// per column; a short last column keeps its unused slots), or per group of
-// 256. The symmetric formats store no zero-points.
+// codes), then scales and zero-points row-major, each row's groups padded to
+// a multiple of 8 (G8 slots); K-quant: one 16-byte record per (row,
+// super-block). The symmetric formats store no zero-points.
 void meta_bytes(int64_t N, int64_t K, int32_t group, int32_t fmt, size_t *q, size_t *sb, size_t *zb) {
-    if (fmt == W4A16_FMT_KQ4) {   // one 16-byte record per (super-block, row)
+    if (fmt == W4A16_FMT_KQ4) {   // one 16-byte record per (row, super-block)
         *q = (size_t)(N * K / 2);
         *sb = (size_t)(16 * (K / 256) * N);
         *zb = 0;
         return;
     }
-    const int64_t slots = group == 256 ? K / 256 : (K / 32 + 3) / 4 * (128 / group);
+    const int64_t G8 = (K / group + 7) / 8 * 8;
     *q = (size_t)(N * K / 2) * (fmt == W4A16_FMT_SYM8 ? 2 : 1);
-    *sb = (size_t)(2 * slots * N);
-    *zb = fmt == W4A16_FMT_ASYM4 ? (size_t)(slots * N / 2) : 0;
+    *sb = (size_t)(2 * G8 * N);
+    *zb = fmt == W4A16_FMT_ASYM4 ? (size_t)(G8 * N / 2) : 0;
 }
 
 struct Range {
@@ -123,6 +109,19 @@ std::mutex g_attr_mutex;
 std::atomic<int> g_cus[kMaxDevices];
 }  // namespace
 
+int w4a16::tuning_knob(const char *name, int fallback) {
+#ifdef W4A16_TUNING_KNOBS
+    const char *v = std::getenv(name);
+    if (!v || !*v) return fallback;
+    char *end = nullptr;
+    const long r = std::strtol(v, &end, 10);
+    return (end && *end == 0) ? (int)r : fallback;
+#else
+    (void)name;
+    return fallback;
+#endif
+}
+
 int w4a16::device_cu_count() {
     int dev = 0;
     if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return 0;
@@ -164,21 +163,20 @@ size_t max_lds_per_block() {
     return (size_t)v;
 }
 
-// The GEMV stages all activations of the call in LDS; it takes M <= 8 and
-// M * K small enough for one workgroup's LDS.
-bool gemv_fits(int64_t M, int64_t N, int64_t K, int32_t group, int32_t dtype, int32_t fmt) {
-    if (M < 1 || M > 8) return false;
-    const GemvPlan p = gemv_plan(M, N, K, group);
-    return gemv_lds_bytes(M, K, dtype == W4A16_BF16, p.waves, fmt) + kGemvStaticLds <= max_lds_per_block();
+// The decode kernel takes M <= 8 and K up to 32768 (16384 from M = 3 on, or
+// with AWQ scaling), within one workgroup's LDS.
+bool decode_fits(int64_t M, int64_t N, int64_t K, int32_t group, int32_t fmt, bool awq) {
+    if (M < 1 || M > kDecodeMaxM) return false;
+    const DecodePlan p = decode_plan(M, N, K, group, fmt, awq);
+    return p.ok && p.lds <= max_lds_per_block();
 }
 
-// w4a16_linear's choice for M <= gemv_max_m(): the dot-product GEMV for
-// matrices of fewer than 768 row blocks of 16 (its workgroups then hide their
-// latency better), the matrix-core kernel (four row blocks per workgroup) for
-// wider ones; both measured on the decode shapes.
+// w4a16_linear's choice: the decode kernel at M <= gemv_max_m() (M = 1;
+// measured faster than the matrix-core kernel on every decode shape), the
+// matrix-core kernels otherwise.
 bool prefer_gemv(int64_t M, int64_t N, int64_t K, int32_t group, int32_t dtype, int32_t fmt) {
-    return M >= 1 && M <= gemv_max_m() && ceil_div(N, kRowBlock) < 768 && shape_ok(N, K, group) &&
-           (dtype == W4A16_F16 || dtype == W4A16_BF16) && gemv_fits(M, N, K, group, dtype, fmt);
+    return M >= 1 && M <= gemv_max_m() && shape_ok(N, K, group) && (dtype == W4A16_F16 || dtype == W4A16_BF16) &&
+           decode_fits(M, N, K, group, fmt, false);
 }
 
 // Workspace of a matrix-core call: the stream-K partials and flags of the
@@ -299,15 +297,15 @@ w4a16_status w4a16_gemv_fmt(const void *x, int32_t dtype, const void *qweight, c
                             void *workspace, size_t workspace_bytes, void *stream) {
     (void)workspace;
     (void)workspace_bytes;
-    if (M > 8) return W4A16_ERR_INVALID_ARG;
+    if (M > kDecodeMaxM) return W4A16_ERR_INVALID_ARG;
     w4a16_status st = check_linear(x, dtype, qweight, scales, zeros, y, M, N, K, group, fmt, nullptr, 0, 0);
     if (st != W4A16_OK || M == 0) return st;
     st = check_device();
     if (st != W4A16_OK) return st;
-    if (!gemv_fits(M, N, K, group, dtype, fmt)) return W4A16_ERR_INVALID_ARG;
-    GemvPlan plan = gemv_plan(M, N, K, group);
-    hipError_t e = launch_gemv(x, dtype == W4A16_BF16, qweight, scales, zeros, y, (int)M, (int)N,
-                               (int)K, group, fmt, nullptr, plan, reinterpret_cast<hipStream_t>(stream));
+    if (!decode_fits(M, N, K, group, fmt, false)) return W4A16_ERR_INVALID_ARG;
+    const DecodePlan plan = decode_plan(M, N, K, group, fmt, false);
+    hipError_t e = launch_decode(x, dtype == W4A16_BF16, qweight, scales, zeros, y, (int)M, (int)N, (int)K, group,
+                                 fmt, nullptr, plan, reinterpret_cast<hipStream_t>(stream));
     return e == hipSuccess ? W4A16_OK : W4A16_ERR_HIP;
 }
 
@@ -483,7 +481,8 @@ w4a16_status w4a16_awq_workspace_bytes(int64_t M, int64_t N, int64_t K, int32_t 
     if (!bytes || M < 0 || M > (1LL << 24) || !shape_ok(N, K, group) || !fmt_group_ok(fmt, group) ||
         (dtype != W4A16_F16 && dtype != W4A16_BF16))
         return W4A16_ERR_INVALID_ARG;
-    *bytes = (M == 0 || gemv_fits(M, N, K, group, dtype, fmt))
+    (void)dtype;
+    *bytes = (M == 0 || decode_fits(M, N, K, group, fmt, true))
                  ? 0 : align_up((size_t)(M * K * 2), 256) + gemm_need(M, N, K, group);
     return W4A16_OK;
 }
@@ -495,7 +494,7 @@ w4a16_status w4a16_linear_awq(const void *x, int32_t dtype, const float *act_mul
     if (st != W4A16_OK || M == 0) return st;
     if (!act_mul || !aligned16(act_mul)) return W4A16_ERR_INVALID_ARG;
     if (overlap(range_of(y, (size_t)(M * N * 2)), range_of(act_mul, (size_t)K * 4))) return W4A16_ERR_INVALID_ARG;
-    const bool fused = gemv_fits(M, N, K, group, dtype, fmt);
+    const bool fused = decode_fits(M, N, K, group, fmt, true);
     // not fused: the scaled activations, then the product's own workspace
     const size_t xbytes = align_up((size_t)(M * K * 2), 256);
     const size_t need = fused ? 0 : xbytes + gemm_need(M, N, K, group);
@@ -513,10 +512,10 @@ w4a16_status w4a16_linear_awq(const void *x, int32_t dtype, const float *act_mul
     st = check_device();
     if (st != W4A16_OK) return st;
     const hipStream_t s = reinterpret_cast<hipStream_t>(stream);
-    if (fused) {   // one launch: the GEMV scales the activations as it stages them
-        const GemvPlan plan = gemv_plan(M, N, K, group);
-        hipError_t e = launch_gemv(x, dtype == W4A16_BF16, qweight, scales, zeros, y, (int)M, (int)N, (int)K, group,
-                                   fmt, act_mul, plan, s);
+    if (fused) {   // one launch: the decode kernel scales the activations as it loads them
+        const DecodePlan plan = decode_plan(M, N, K, group, fmt, true);
+        hipError_t e = launch_decode(x, dtype == W4A16_BF16, qweight, scales, zeros, y, (int)M, (int)N, (int)K,
+                                     group, fmt, act_mul, plan, s);
         return e == hipSuccess ? W4A16_OK : W4A16_ERR_HIP;
     }
     hipError_t e = launch_scale_activations(x, dtype == W4A16_BF16, act_mul, workspace, M, (int)K, s);

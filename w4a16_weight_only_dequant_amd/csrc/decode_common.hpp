@@ -201,6 +201,33 @@ __device__ inline float bf16_magic_bias(uint32_t z) {
         return (float)(128u + z);
 }
 
+// Eight 16-bit activations times eight fp32 multipliers, each product rounded
+// once to the activation type (round to nearest even).
+template <bool BF>
+__device__ inline uint4 scale8(const uint4 &v, const float4 &a, const float4 &b) {
+    const float m[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
+    const uint32_t in[4] = {v.x, v.y, v.z, v.w};
+    uint32_t out[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        float lo, hi;
+        if constexpr (BF) {
+            lo = __builtin_bit_cast(float, in[i] << 16);
+            hi = __builtin_bit_cast(float, in[i] & 0xFFFF0000u);
+        } else {
+            const half2_t h = __builtin_bit_cast(half2_t, in[i]);
+            lo = (float)h.x;
+            hi = (float)h.y;
+        }
+        const float2_t p = {lo * m[2 * i], hi * m[2 * i + 1]};
+        if constexpr (BF)
+            out[i] = __builtin_bit_cast(uint32_t, __builtin_convertvector(p, bf162_t));
+        else
+            out[i] = __builtin_bit_cast(uint32_t, __builtin_convertvector(p, half2_t));
+    }
+    return make_uint4(out[0], out[1], out[2], out[3]);
+}
+
 // The K-slice of one wave, in columns [t_begin, t_end); t_full ends the run of
 // full (4-chunk) columns; the last column of K may be partial.
 struct Slice {

@@ -1,0 +1,9 @@
+// Decode kernels of one weight format (kSym4); see decode_kernel.hpp.
+#include "decode_kernel.hpp"
+
+namespace w4a16 {
+
+template hipError_t launch_decode_fmt<kSym4>(const void *, bool, const void *, const void *, const void *, void *,
+                                            int, int, int, int, const float *, const DecodePlan &, hipStream_t);
+
+}  // namespace w4a16

@@ -7,18 +7,9 @@
 namespace w4a16 {
 
 GemmPlan gemm_plan(int64_t M, int64_t N, int64_t K, int32_t group) {
-    static const int forced_waves = [] {
-        const char *v = getenv("W4A16_SKINNY_WAVES");
-        return v ? atoi(v) : 0;
-    }();
-    static const int forced_r = [] {
-        const char *v = getenv("W4A16_SKINNY_R");
-        return v ? atoi(v) : 0;
-    }();
-    static const int skinny_max = [] {
-        const char *v = getenv("W4A16_SKINNY_MAX_M");
-        return v ? atoi(v) : kSkinnyMaxM;
-    }();
+    static const int forced_waves = tuning_knob("W4A16_SKINNY_WAVES", 0);
+    static const int forced_r = tuning_knob("W4A16_SKINNY_R", 0);
+    static const int skinny_max = tuning_knob("W4A16_SKINNY_MAX_M", kSkinnyMaxM);
     GemmPlan p{};
     if (M <= skinny_max) {
         p.kind = 0;

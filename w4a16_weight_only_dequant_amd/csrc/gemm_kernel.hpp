@@ -87,10 +87,9 @@ __device__ __forceinline__ void skinny_body(const uint16_t *__restrict__ x, cons
     // row; a workgroup past the last block repeats the last one (not stored)
     const uint4 *qw_b[R], *qwh_b[R];
     uint32_t lane_rec[R], col_rec[R];
-    const ColScales<GPC> *sc_row[R];
-    const uint4 *kq_row[R];   // kq4: super-block records [K/256][N]
-    const uint32_t *zp_row[R];
-    int zshift[R];
+    const ColScales<GPC> *sc_row[R];   // the row's scales, in units of one column's GPC values
+    const uint4 *kq_row[R];            // kq4: the row's super-block records
+    const uint32_t *zp_row[R];         // the row's zero-point words
 #pragma unroll
     for (int i = 0; i < R; ++i) {
         const int b = min(wg * R + i, nblocks - 1);
@@ -101,10 +100,10 @@ __device__ __forceinline__ void skinny_body(const uint16_t *__restrict__ x, cons
         lane_rec[i] = (uint32_t)(s * rows + rl);
         col_rec[i] = (uint32_t)(kColChunks * rows);
         const int n = b * kRowBlock + rl;
-        sc_row[i] = reinterpret_cast<const ColScales<GPC> *>(scales) + n;
-        kq_row[i] = reinterpret_cast<const uint4 *>(scales) + n;
-        zp_row[i] = zeros + (n * GPC) / 8;
-        zshift[i] = 4 * ((n * GPC) % 8);
+        const int G8 = meta_slots(K, GROUP << mshift);   // (group 256 runs these kernels with mshift = 1)
+        sc_row[i] = reinterpret_cast<const ColScales<GPC> *>(scales + (size_t)n * G8);
+        kq_row[i] = reinterpret_cast<const uint4 *>(scales) + (size_t)n * (K / 256);
+        zp_row[i] = zeros + (size_t)n * (G8 / 8);
     }
     // A operand rows: lane row r, clamped to the last real row of x (rows of
     // the 16-row tile past M produce outputs that are never stored)
@@ -120,17 +119,18 @@ __device__ __forceinline__ void skinny_body(const uint16_t *__restrict__ x, cons
         uint32_t zw[R];
         int par;   // column parity: which half of the super-block (kq4)
     };
-    // metadata slot of column t: t >> mshift (group 256: one slot per two columns)
+    // metadata slot of column t: t >> mshift (group 256: one slot per two
+    // columns); its zero-points come pre-shifted to bit 0
     auto load_meta = [&](int t, Buf &u) {
         const int tm = t >> mshift;
         u.par = t & 1;
 #pragma unroll
         for (int i = 0; i < R; ++i) {
             if constexpr (FT::kquant) {
-                u.kq[i] = kq_row[i][(size_t)(t >> 1) * N];
+                u.kq[i] = kq_row[i][t >> 1];
             } else {
-                u.sc[i] = sc_row[i][(size_t)tm * N];
-                if constexpr (FT::has_zeros) u.zw[i] = zp_row[i][(size_t)tm * (N * GPC / 8)];
+                u.sc[i] = sc_row[i][tm];
+                if constexpr (FT::has_zeros) u.zw[i] = zp_row[i][(tm * GPC) >> 3] >> (4 * ((tm * GPC) & 7));
                 else u.zw[i] = 0;
             }
         }
@@ -171,7 +171,8 @@ __device__ __forceinline__ void skinny_body(const uint16_t *__restrict__ x, cons
         }
     };
     auto zero_of = [&](uint32_t zw, int i, int e) -> uint32_t {
-        if constexpr (FT::has_zeros) return (zw >> (zshift[i] + 4 * e)) & 0xFu;
+        (void)i;
+        if constexpr (FT::has_zeros) return (zw >> (4 * e)) & 0xFu;
         else return FT::fixed_zero;
     };
     auto close_group = [&](int i, float sc, uint32_t z, f4_t &g, f4_t &sx) {

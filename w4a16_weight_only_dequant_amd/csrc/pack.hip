@@ -18,44 +18,41 @@
 namespace w4a16 {
 namespace {
 
-// One thread per (row n, span u of K): a span is one 128-weight column for
-// groups of at most 128 weights (its 128/GROUP groups), one group of 256
-// otherwise. The thread quantises its groups of row n in two passes over the
-// fp32 weights (range, then codes) and writes their codes, scales and, for
-// the zero-point format, zero-points.
+// One thread per (row n, run w of eight consecutive groups): it quantises
+// the run's groups of row n in two passes over the fp32 weights (range, then
+// codes), writes their codes, the eight scales (one 16-byte store: scales are
+// [N][G8], G8 = K / GROUP rounded up to a multiple of 8, padded slots 0) and,
+// for the zero-point format, the eight zero-points as one word of [N][G8 / 8].
 template <int GROUP, int FMT>
 __global__ __launch_bounds__(256) void pack_kernel(const float *__restrict__ w, int N, int K,
                                                    uint32_t *__restrict__ qweight,
                                                    uint16_t *__restrict__ scales,
                                                    uint32_t *__restrict__ zeros) {
     using FT = FormatTraits<FMT>;
-    constexpr int SPAN = GROUP > kColumn ? GROUP : kColumn;
-    constexpr int GPS = SPAN / GROUP;       // groups per span (4, 2, 1, 1)
     constexpr int CPG = GROUP / kChunk;     // chunks per group
     constexpr int QMAX = FMT == kSym8 ? 127 : 7;   // symmetric: codes q + QMAX + 1, q in [-QMAX-1, QMAX]
-    const int U = (K + SPAN - 1) / SPAN;
     const int G = K / GROUP;
-    const int64_t tid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;   // (u, n), n fastest
-    const bool active = tid < (int64_t)U * N;
-    const int n = active ? (int)(tid % N) : 0;
-    const int u = active ? (int)(tid / N) : 0;
+    const int W = (G + 7) / 8;              // runs of eight groups per row
+    const int64_t tid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;   // (n, run), run fastest
+    if (tid >= (int64_t)W * N) return;
+    const int n = (int)(tid / W);
+    const int run = (int)(tid % W);
     const int64_t plane = (int64_t)N * K / 8;   // dwords of one 4-bit plane
 
-    uint32_t znib = 0;   // the GPS zero-points of (u, n), 4 bits each
-    for (int e = 0; e < GPS; ++e) {
-        const int g = u * GPS + e;
-        const bool real = active && g < G;
-        const float4 *src = reinterpret_cast<const float4 *>(w + (int64_t)n * K + (int64_t)(real ? g : 0) * GROUP);
+    uint32_t sw[4] = {0u, 0u, 0u, 0u};   // the run's eight scales, two per word
+    uint32_t zw = 0;                     // and zero-points, 4 bits each
+    for (int e = 0; e < 8; ++e) {
+        const int g = run * 8 + e;
+        if (g >= G) break;   // padded slots stay 0
+        const float4 *src = reinterpret_cast<const float4 *>(w + (int64_t)n * K + (int64_t)g * GROUP);
         // 1. range: [min(0, min w), max(0, max w)] or max|w|
-        float lo = 0.0f, hi = 0.0f, amax = 0.0f;
-        if (real) {
-            for (int i = 0; i < GROUP / 4; ++i) {
-                const float4 v = src[i];
-                lo = fminf(fminf(fminf(lo, v.x), fminf(v.y, v.z)), v.w);
-                hi = fmaxf(fmaxf(fmaxf(hi, v.x), fmaxf(v.y, v.z)), v.w);
-            }
-            amax = fmaxf(-lo, hi);
+        float lo = 0.0f, hi = 0.0f;
+        for (int i = 0; i < GROUP / 4; ++i) {
+            const float4 v = src[i];
+            lo = fminf(fminf(fminf(lo, v.x), fminf(v.y, v.z)), v.w);
+            hi = fmaxf(fmaxf(fmaxf(hi, v.x), fmaxf(v.y, v.z)), v.w);
         }
+        const float amax = fmaxf(-lo, hi);
         // 2. scale, rounded once to fp16 (zero -> smallest positive fp16, 2^-24)
         const float s32 = FT::has_zeros ? (hi - lo) / 15.0f : amax / (float)QMAX;
         uint16_t sbits = f32_to_f16_bits(s32);
@@ -67,45 +64,37 @@ __global__ __launch_bounds__(256) void pack_kernel(const float *__restrict__ w, 
             z = z < 0 ? 0 : (z > 15 ? 15 : z);
         }
         // 3. codes, one dword (8 consecutive k) at a time
-        if (real) {
-            for (int c = 0; c < CPG; ++c) {
+        for (int c = 0; c < CPG; ++c) {
 #pragma unroll
-                for (int d = 0; d < 4; ++d) {
-                    const float4 a = src[c * 8 + d * 2], b = src[c * 8 + d * 2 + 1];
-                    const float v[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
-                    uint32_t word = 0, word_hi = 0;
+            for (int d = 0; d < 4; ++d) {
+                const float4 a = src[c * 8 + d * 2], b = src[c * 8 + d * 2 + 1];
+                const float v[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
+                uint32_t word = 0, word_hi = 0;
 #pragma unroll
-                    for (int i = 0; i < 8; ++i) {
-                        int q = (int)rintf(v[i] / sc);
-                        if constexpr (FT::has_zeros) {
-                            q += z;
-                            q = q < 0 ? 0 : (q > 15 ? 15 : q);
-                        } else {
-                            q = q < -QMAX - 1 ? -QMAX - 1 : (q > QMAX ? QMAX : q);
-                            q += QMAX + 1;
-                        }
-                        const int p = (i >> 1) + 4 * (i & 1);   // even k low half, odd k high half
-                        word |= (uint32_t)(q & 0xF) << (4 * p);
-                        word_hi |= (uint32_t)(q >> 4) << (4 * p);
+                for (int i = 0; i < 8; ++i) {
+                    int q = (int)rintf(v[i] / sc);
+                    if constexpr (FT::has_zeros) {
+                        q += z;
+                        q = q < 0 ? 0 : (q > 15 ? 15 : q);
+                    } else {
+                        q = q < -QMAX - 1 ? -QMAX - 1 : (q > QMAX ? QMAX : q);
+                        q += QMAX + 1;
                     }
-                    const int64_t off = dword_offset(n, g * CPG + c, d, N, K);
-                    qweight[off] = word;
-                    if constexpr (FT::two_planes) qweight[plane + off] = word_hi;
+                    const int p = (i >> 1) + 4 * (i & 1);   // even k low half, odd k high half
+                    word |= (uint32_t)(q & 0xF) << (4 * p);
+                    word_hi |= (uint32_t)(q >> 4) << (4 * p);
                 }
+                const int64_t off = dword_offset(n, g * CPG + c, d, N, K);
+                qweight[off] = word;
+                if constexpr (FT::two_planes) qweight[plane + off] = word_hi;
             }
         }
-        if (active) scales[((int64_t)u * N + n) * GPS + e] = real ? sbits : (uint16_t)0;
-        znib |= (real ? (uint32_t)z : 0u) << (4 * e);
+        sw[e >> 1] |= (uint32_t)sbits << (16 * (e & 1));
+        zw |= (uint32_t)z << (4 * e);
     }
-    if constexpr (FT::has_zeros) {
-        // zeros: word (u, i) holds the nibbles of rows 8/GPS*i .. 8/GPS*i + 8/GPS-1;
-        // N % 8 == 0 and tid runs n fastest, so those rows sit in neighbouring lanes
-        constexpr int RPW = 8 / GPS;    // rows per zero word
-        uint32_t zw = active ? znib << (4 * GPS * (n % RPW)) : 0u;
-#pragma unroll
-        for (int off = 1; off < RPW; off <<= 1) zw |= __shfl_xor(zw, off, 64);
-        if (active && n % RPW == 0) zeros[(int64_t)u * (N / RPW) + n / RPW] = zw;
-    }
+    const int64_t G8 = (int64_t)W * 8;
+    *reinterpret_cast<uint4 *>(scales + (int64_t)n * G8 + (int64_t)run * 8) = make_uint4(sw[0], sw[1], sw[2], sw[3]);
+    if constexpr (FT::has_zeros) zeros[(int64_t)n * W + run] = zw;
 }
 
 // K-quant-style super-blocks: one thread per (row n, 256-weight super-block
@@ -115,7 +104,7 @@ __global__ __launch_bounds__(256) void pack_kernel(const float *__restrict__ w, 
 // 6-bit sc_j, mq_j are rint(s_j / d) and rint(mn_j / dmin), clamped; codes
 // are rint((w + M_j) / S_j), clamped to 0..15, with S_j = d sc_j and
 // M_j = dmin mq_j (0 where S_j = 0). Writes the codes and the 16-byte record
-// {d | dmin << 16, 48-bit sc field, 48-bit mq field} at [u][n].
+// {d | dmin << 16, 48-bit sc field, 48-bit mq field} at [n][u].
 __global__ __launch_bounds__(256) void pack_kq_kernel(const float *__restrict__ w, int N, int K,
                                                       uint32_t *__restrict__ qweight, uint4 *__restrict__ rec) {
     constexpr int SUB = 8;   // sub-blocks per super-block
@@ -166,7 +155,7 @@ __global__ __launch_bounds__(256) void pack_kq_kernel(const float *__restrict__ 
             qweight[dword_offset(n, u * 8 + j, dd, N, K)] = word;
         }
     }
-    rec[(int64_t)u * N + n] = make_uint4((uint32_t)dbits | ((uint32_t)mbits << 16), (uint32_t)scf,
+    rec[(int64_t)n * U + u] = make_uint4((uint32_t)dbits | ((uint32_t)mbits << 16), (uint32_t)scf,
                                          (uint32_t)(scf >> 32) | ((uint32_t)(mqf & 0xFFFFu) << 16),
                                          (uint32_t)(mqf >> 16));
 }
@@ -196,32 +185,29 @@ __global__ __launch_bounds__(256) void unpack_codes_kernel(const uint32_t *__res
     *reinterpret_cast<uint2 *>(codes + (int64_t)n * K + 8 * kd) = packed;
 }
 
-// fixed_zero: 0 when the zero-points are read from `zeros`, else the
-// symmetric formats' fixed zero (8 or 128), written for every group.
-template <int GROUP>
+// Metadata [N][G8] / [N][G8 / 8] -> canonical [G][N] scale bits and
+// zero-points. fixed_zero: 0 when the zero-points are read from `zeros`, else
+// the symmetric formats' fixed zero (8 or 128), written for every group.
 __global__ __launch_bounds__(256) void unpack_meta_kernel(const uint16_t *__restrict__ scales,
                                                           const uint32_t *__restrict__ zeros,
                                                           int N, int G, int fixed_zero, uint16_t *__restrict__ s_out,
                                                           uint8_t *__restrict__ z_out) {
-    constexpr int GPS = GROUP < kColumn ? kColumn / GROUP : 1;   // metadata slots per span
     const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;   // canonical (g, n)
     if (i >= (int64_t)G * N) return;
     const int g = (int)(i / N), n = (int)(i % N);
-    const int t = g / GPS, e = g % GPS;
-    s_out[i] = scales[((int64_t)t * N + n) * GPS + e];
+    const int64_t G8 = (int64_t)(G + 7) / 8 * 8;
+    s_out[i] = scales[(int64_t)n * G8 + g];
     if (fixed_zero) {
         z_out[i] = (uint8_t)fixed_zero;
         return;
     }
-    const int64_t nib = (int64_t)t * N * GPS + (int64_t)n * GPS + e;
-    z_out[i] = (zeros[nib / 8] >> (4 * (nib % 8))) & 0xF;
+    z_out[i] = (zeros[(int64_t)n * (G8 / 8) + g / 8] >> (4 * (g % 8))) & 0xF;
 }
 
 template <int FMT>
 hipError_t launch_pack_fmt(const float *w, int N, int K, int group, uint32_t *q, uint16_t *s, uint32_t *z,
                            hipStream_t stream) {
-    const int span = group > kColumn ? group : kColumn;
-    const int64_t total = ceil_div(K, span) * N;   // (span, row) pairs
+    const int64_t total = ceil_div(K / group, 8) * N;   // (row, run of eight groups)
     const dim3 block(256);
     const dim3 grid((unsigned)ceil_div(total, 256));
     switch (group) {
@@ -264,14 +250,8 @@ hipError_t launch_unpack(const void *qweight, const void *scales, const void *ze
     const int G = K / group;
     const int fz = fmt == kSym8 ? 128 : (fmt == kSym4 ? 8 : 0);
     const dim3 grid((unsigned)ceil_div((int64_t)G * N, 256));
-    auto *sc = reinterpret_cast<const uint16_t *>(scales);
-    auto *zp = reinterpret_cast<const uint32_t *>(zeros);
-    switch (group) {
-        case 32: hipLaunchKernelGGL(unpack_meta_kernel<32>, grid, dim3(256), 0, stream, sc, zp, N, G, fz, scales_out, zeros_out); break;
-        case 64: hipLaunchKernelGGL(unpack_meta_kernel<64>, grid, dim3(256), 0, stream, sc, zp, N, G, fz, scales_out, zeros_out); break;
-        case 128: hipLaunchKernelGGL(unpack_meta_kernel<128>, grid, dim3(256), 0, stream, sc, zp, N, G, fz, scales_out, zeros_out); break;
-        default: hipLaunchKernelGGL(unpack_meta_kernel<256>, grid, dim3(256), 0, stream, sc, zp, N, G, fz, scales_out, zeros_out); break;
-    }
+    hipLaunchKernelGGL(unpack_meta_kernel, grid, dim3(256), 0, stream, reinterpret_cast<const uint16_t *>(scales),
+                       reinterpret_cast<const uint32_t *>(zeros), N, G, fz, scales_out, zeros_out);
     return hipGetLastError();
 }
 

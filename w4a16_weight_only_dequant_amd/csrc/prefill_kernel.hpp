@@ -225,7 +225,7 @@ __global__ __launch_bounds__(64 * WM * WN) __attribute__((amdgpu_waves_per_eu(WM
     const bool has_head = le < T, has_tail = fb > 0;
     const int n_seg = n_full + (has_head ? 1 : 0) + (has_tail ? 1 : 0);
 
-    const uint32_t zstep = (uint32_t)(N * GPC / 8);
+    const int G8 = meta_slots(K, GROUP << mshift);   // metadata slots per row (group 256: mshift = 1)
     const ColScales<GPC> *scol = reinterpret_cast<const ColScales<GPC> *>(scales);
     const uint4 *kqrec = reinterpret_cast<const uint4 *>(scales);
     const UnpackConsts uc = unpack_consts();
@@ -259,7 +259,7 @@ __global__ __launch_bounds__(64 * WM * WN) __attribute__((amdgpu_waves_per_eu(WM
         // tile, record = lane (d = lane / 16, r = lane % 16: dword d of the
         // column's four chunks of row r). Offsets are 32-bit element indices.
         uint32_t woff[WREC], wstep[WREC], soff[WREC], zoff[WREC];
-        int zshift[WREC], wrow[WREC], wrows[WREC];
+        int wrow[WREC], wrows[WREC];
 #pragma unroll
         for (int i = 0; i < WREC; ++i) {
             const int rb = i * (NT / 64) + wave;
@@ -270,9 +270,10 @@ __global__ __launch_bounds__(64 * WM * WN) __attribute__((amdgpu_waves_per_eu(WM
             wrows[i] = rows;
             woff[i] = (uint32_t)b * (uint32_t)(K / 2) + (uint32_t)(d * rows + rl);    // uint4 index, column 0 (a block is K/2 uint4)
             wstep[i] = (uint32_t)(kColChunks * rows);                                 // uint4 per column
-            soff[i] = (uint32_t)n;                                                    // ColScales index, column 0
-            zoff[i] = (uint32_t)(n * GPC) / 8;
-            zshift[i] = 4 * ((n * GPC) % 8);
+            // the row's metadata: ColScales index of its first column (kq4: its
+            // first super-block record) and its first zero-point word
+            soff[i] = FT::kquant ? (uint32_t)n * (uint32_t)(K / 256) : (uint32_t)n * (uint32_t)(G8 / GPC);
+            zoff[i] = (uint32_t)n * (uint32_t)(G8 / 8);
             wrow[i] = rb * kRowBlock + r;                                             // LDS row
         }
         struct WCol {
@@ -306,14 +307,17 @@ __global__ __launch_bounds__(64 * WM * WN) __attribute__((amdgpu_waves_per_eu(WM
                         u.rec_hi[i] = make_uint4(v[0], v[1], v[2], v[3]);
                     }
                 }
-                // metadata slot of column t: t >> mshift (group 256: one slot per two columns)
+                // metadata slot of column t: t >> mshift (group 256: one slot per
+                // two columns); its zero-points come pre-shifted to bit 0
                 const uint32_t tm = (uint32_t)(t >> mshift);
                 if constexpr (FT::kquant) {
-                    u.kq[i] = kqrec[soff[i] + (uint32_t)(t >> 1) * (uint32_t)N];
+                    u.kq[i] = kqrec[soff[i] + (uint32_t)(t >> 1)];
                 } else {
-                    u.sc[i] = scol[soff[i] + tm * (uint32_t)N];
-                    if constexpr (FT::has_zeros) u.zw[i] = zeros[zoff[i] + tm * zstep];
-                    else u.zw[i] = 0;
+                    u.sc[i] = scol[soff[i] + tm];
+                    if constexpr (FT::has_zeros)
+                        u.zw[i] = zeros[zoff[i] + ((tm * GPC) >> 3)] >> (4 * ((tm * GPC) & 7));
+                    else
+                        u.zw[i] = 0;
                 }
             }
         };
@@ -326,7 +330,7 @@ __global__ __launch_bounds__(64 * WM * WN) __attribute__((amdgpu_waves_per_eu(WM
                 const uint32_t dh = h ? (jj ? u.rec_hi[i].w : u.rec_hi[i].z) : (jj ? u.rec_hi[i].y : u.rec_hi[i].x);
                 const int e = (2 * h + jj) / CPG;
                 uint32_t z = FT::fixed_zero;
-                if constexpr (FT::has_zeros) z = (u.zw[i] >> (zshift[i] + 4 * e)) & 0xFu;
+                if constexpr (FT::has_zeros) z = (u.zw[i] >> (4 * e)) & 0xFu;
                 uint4 v;
                 if constexpr (FT::kquant) {
                     v = dequant_kq<BF>(dw, kq_sub(kq_half(u.kq[i], u.par != 0), 2 * h + jj), uc);

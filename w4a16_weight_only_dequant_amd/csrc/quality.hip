@@ -88,9 +88,7 @@ __global__ __launch_bounds__(kQeThreads) void quant_error_partial_kernel(
     const int kd0 = (int)((int64_t)sl * cols / slices) * (kColumn / 8);
     const int kd1 = min(K / 8, (int)((int64_t)(sl + 1) * cols / slices) * (kColumn / 8));
     const int KD = kd1 - kd0;
-    const int kgroup = group < kColumn ? group : kColumn;     // group of the metadata slot
-    const int gpc = kColumn / kgroup;                         // slots per column
-    const int mshift = group > kColumn ? 1 : 0;               // group 256: one slot per two columns
+    const int G8 = meta_slots(K, group);                      // metadata slots per row
     const int64_t plane = (int64_t)N * K / 8;                 // dwords of one 4-bit plane
     const uint32_t fixed_zero = fmt == kSym8 ? 128u : (fmt == kKq4 ? 0u : 8u);
     Sums5 v{0.0, 0.0, 0.0, 0.0, 0.0};
@@ -103,18 +101,16 @@ __global__ __launch_bounds__(kQeThreads) void quant_error_partial_kernel(
         const uint32_t hi = fmt == kSym8 ? qw[plane + off] : 0u;
         double s, mn = 0.0;
         uint32_t z = fixed_zero;
-        if (fmt == kKq4) {   // sub-block (k0 % 256) / 32 of the record [k0 / 256][n]
-            const uint4 rec = reinterpret_cast<const uint4 *>(scales)[(int64_t)(k0 / 256) * N + n];
+        if (fmt == kKq4) {   // sub-block (k0 % 256) / 32 of the record [n][k0 / 256]
+            const uint4 rec = reinterpret_cast<const uint4 *>(scales)[(int64_t)n * (K / 256) + k0 / 256];
             const KqParams P = kq_params(rec, (k0 % 256) / kChunk);
             s = (double)P.S;
             mn = (double)P.M;
             z = 0;
         } else {
-            const int t = (k0 / kColumn) >> mshift;
-            const int e = (k0 % kColumn) / kgroup;
-            const int64_t slot = ((int64_t)t * N + n) * gpc + e;
-            s = (double)(float)__builtin_bit_cast(_Float16, scales[slot]);
-            if (fmt == kAsym4) z = (zeros[slot / 8] >> (4 * (slot % 8))) & 0xFu;
+            const int g = k0 / group;
+            s = (double)(float)__builtin_bit_cast(_Float16, scales[(int64_t)n * G8 + g]);
+            if (fmt == kAsym4) z = (zeros[(int64_t)n * (G8 / 8) + g / 8] >> (4 * (g % 8))) & 0xFu;
         }
         const float4 wa = *reinterpret_cast<const float4 *>(w + (int64_t)n * K + k0);
         const float4 wb = *reinterpret_cast<const float4 *>(w + (int64_t)n * K + k0 + 4);

@@ -25,6 +25,13 @@ constexpr int kRowBlock = 16;
 constexpr int kChunk = 32;
 constexpr int kColChunks = 4;
 
+// Metadata (layout 3): row-major, so that one row's metadata along K is
+// contiguous. G8 = K / group rounded up to a multiple of 8. Scales [N][G8]
+// fp16; zero-points [N][G8 / 8] words of eight 4-bit values (group g of a row
+// in bits 4 (g % 8) of the row's word g / 8); K-quant super-block records
+// [N][K / 256] of 16 bytes. Padded slots hold 0.
+__host__ __device__ inline int meta_slots(int K, int group) { return ((K / group) + 7) & ~7; }
+
 __host__ __device__ inline int64_t dword_offset(int n, int c, int d, int N, int K) {
     const int b = n / kRowBlock, r = n % kRowBlock;
     const int rows_b = (N - b * kRowBlock) < kRowBlock ? (N - b * kRowBlock) : kRowBlock;
@@ -34,6 +41,12 @@ __host__ __device__ inline int64_t dword_offset(int n, int c, int d, int N, int 
     return (int64_t)b * kRowBlock * (K / 8) + (int64_t)t * rows_b * 16 + (int64_t)d * rows_b * nc +
            (int64_t)r * nc + j;
 }
+
+// Development-only overrides of the launch plans (tiles, waves, splits):
+// read from the environment only in a build compiled with
+// -DW4A16_TUNING_KNOBS; the shipped library's dispatch is fixed and the
+// fallback is returned.
+int tuning_knob(const char *name, int fallback);
 
 // Weight formats (the values of w4a16_format in the public header).
 enum { kAsym4 = 0, kSym4 = 1, kSym8 = 2, kKq4 = 3 };
@@ -56,31 +69,17 @@ typedef __bf16 bf162_t __attribute__((ext_vector_type(2)));
 __host__ __device__ inline int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 __host__ __device__ inline size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
 
-// Host-side plan for one GEMV launch: one workgroup per kGemvRowsPerWg output
-// rows, each with `waves` waves that split K (no cross-workgroup reduction).
-struct GemvPlan {
-    int row_blocks;   // workgroups = ceil(N / kGemvRowsPerWg)
-    int waves;        // waves per workgroup (1..16)
+// Host-side plan for one decode launch (M <= kDecodeMaxM): one workgroup per
+// 16-row block, `waves` waves of `ncol` 128-weight columns each (all of K),
+// `mt` activation rows held. ok is false when the shape is outside the
+// kernel's range (K above 16384 or 32768, see decode_plan).
+constexpr int kDecodeMaxM = 8;
+struct DecodePlan {
+    int mt, ncol, waves;
+    size_t lds;   // dynamic LDS bytes of one workgroup
+    bool ok;
 };
-
-GemvPlan gemv_plan(int64_t M, int64_t N, int64_t K, int32_t group);
-// Dynamic LDS of one GEMV workgroup (per-wave activations, bf16 sums, metadata).
-size_t gemv_lds_bytes(int64_t M, int64_t K, bool bf16, int waves, int fmt);
-int gemv_xcols(int64_t K, int waves);
-// Most waves of one GEMV workgroup (they split K); the launch bound, and so
-// the register budget of a wave, follows from it.
-#ifndef W4A16_GEMV_MAX_WAVES
-#define W4A16_GEMV_MAX_WAVES 8
-#endif
-constexpr int kGemvMaxWaves = W4A16_GEMV_MAX_WAVES;
-// Output rows of one GEMV workgroup: 16 (one block of the layout), or 8 (half
-// a block, two columns per wave load; measured slower on the decode shapes).
-#ifndef W4A16_GEMV_ROWS
-#define W4A16_GEMV_ROWS 16
-#endif
-constexpr int kGemvRowsPerWg = W4A16_GEMV_ROWS;
-// Static LDS of one GEMV workgroup (cross-wave reduction buffer).
-constexpr size_t kGemvStaticLds = kGemvMaxWaves * 8 * kGemvRowsPerWg * sizeof(float);
+DecodePlan decode_plan(int64_t M, int64_t N, int64_t K, int32_t group, int fmt, bool awq);
 
 // Plan for the matrix-core kernels: kind 0 streams the weights through
 // registers for M <= kSkinnyMaxM (16-row MFMA tiles of activations, one per
@@ -146,9 +145,9 @@ hipError_t launch_quant_error(const float *w, const void *qweight, const void *s
 hipError_t launch_scale_activations(const void *x, bool bf16, const float *act_mul, void *x_out, int64_t M,
                                     int K, hipStream_t stream);
 // act_mul: NULL, or fp32 activation multipliers [K] (AWQ's run-time scaling)
-hipError_t launch_gemv(const void *x, bool bf16, const void *qweight, const void *scales,
-                       const void *zeros, void *y, int M, int N, int K, int group, int fmt,
-                       const float *act_mul, const GemvPlan &plan, hipStream_t stream);
+hipError_t launch_decode(const void *x, bool bf16, const void *qweight, const void *scales,
+                         const void *zeros, void *y, int M, int N, int K, int group, int fmt,
+                         const float *act_mul, const DecodePlan &plan, hipStream_t stream);
 // workspace: prefill_workspace_bytes(plan) bytes (the stream-K partials and
 // flags), may be NULL when that is 0
 hipError_t launch_gemm(const void *x, bool bf16, const void *qweight, const void *scales,
@@ -163,7 +162,7 @@ int prefill_tile(int64_t M, int64_t N);
 #define W4A16_LINEAR_PARAMS const void *x, bool bf16, const void *qweight, const void *scales, const void *zeros, \
                             void *y, int M, int N, int K, int group
 template <int FMT>
-hipError_t launch_gemv_fmt(W4A16_LINEAR_PARAMS, const float *act_mul, const GemvPlan &plan, hipStream_t stream);
+hipError_t launch_decode_fmt(W4A16_LINEAR_PARAMS, const float *act_mul, const DecodePlan &plan, hipStream_t stream);
 template <int FMT> hipError_t launch_skinny_fmt(W4A16_LINEAR_PARAMS, const GemmPlan &plan, hipStream_t stream);
 template <int FMT>
 hipError_t launch_prefill_fmt(W4A16_LINEAR_PARAMS, const GemmPlan &plan, void *workspace, hipStream_t stream);
@@ -171,8 +170,8 @@ template <int FMT>
 hipError_t launch_skinny_group_fmt(const GroupTable &tab, bool bf16, int M, int K, int group, const GemmPlan &plan,
                                    hipStream_t stream);
 #define W4A16_EXTERN_FMT(F)                                                                              \
-    extern template hipError_t launch_gemv_fmt<F>(W4A16_LINEAR_PARAMS, const float *, const GemvPlan &,  \
-                                                  hipStream_t);                                         \
+    extern template hipError_t launch_decode_fmt<F>(W4A16_LINEAR_PARAMS, const float *, const DecodePlan &, \
+                                                    hipStream_t);                                         \
     extern template hipError_t launch_skinny_fmt<F>(W4A16_LINEAR_PARAMS, const GemmPlan &, hipStream_t); \
     extern template hipError_t launch_prefill_fmt<F>(W4A16_LINEAR_PARAMS, const GemmPlan &, void *, hipStream_t); \
     extern template hipError_t launch_skinny_group_fmt<F>(const GroupTable &, bool, int, int, int,        \
