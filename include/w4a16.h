@@ -88,7 +88,8 @@
  * Errors: every function returns a w4a16_status. Argument checks happen
  * before anything is enqueued, and a failed check leaves every buffer
  * untouched. W4A16_ERR_HIP reports a HIP runtime error (launch failure or a
- * device query that failed).
+ * device query that failed) or a kernel error of an earlier call (see
+ * w4a16_init).
  *
  * Preconditions shared by the compute calls:
  *   0 <= M <= 2^24, M*K < 2^34, N >= 8, N % 8 == 0, group in {32, 64, 128, 256},
@@ -145,6 +146,20 @@ const char *w4a16_status_string(int status);
 /* Layout version of the packed format this library reads and writes. */
 int w4a16_layout_version(void);
 
+/* One-time set-up of `device` (a gfx950) for this library, safe to call again
+ * and from several threads: the device check and, once per process, a
+ * 256-byte block of pinned host memory mapped into every device (the kernel
+ * error word below). Every compute call runs it on its device on first use;
+ * call it at start-up to keep that allocation out of later calls.
+ * Kernel errors: when the bounded wait of a stream-K hand-over (see
+ * w4a16_workspace_bytes) runs out, which a correct launch never lets happen,
+ * the waiting workgroup writes its whole output tile as NaN and sets the
+ * process's error word; the next compute call (any entry point, any device)
+ * clears it and returns W4A16_ERR_HIP before enqueuing anything.
+ * W4A16_ERR_UNSUPPORTED for a device other than a gfx950, W4A16_ERR_HIP when
+ * a runtime call fails. */
+w4a16_status w4a16_init(int device);
+
 /* W4A16_OK when `device` is a gfx950 (the only target of these kernels),
  * W4A16_ERR_UNSUPPORTED for any other device, W4A16_ERR_HIP if the query fails.
  * The four "support" states of "Quantization Is Not a Zip File" (section 8)
@@ -181,7 +196,9 @@ w4a16_status w4a16_packed_bytes_fmt(int64_t N, int64_t K, int32_t group, int32_t
  * accept a NULL workspace.
  * The workspace is device memory owned by the caller, 16-byte aligned, and
  * must not overlap any argument of the call. Its contents need no
- * initialisation and are meaningless after the call; calls that run at the
+ * initialisation (each launch marks its hand-overs with a 64-bit token mixed
+ * from a random per-process seed, which earlier contents match only by a
+ * 2^-64 chance) and are meaningless after the call; calls that run at the
  * same time (other streams) must not share one. */
 w4a16_status w4a16_workspace_bytes(int64_t M, int64_t N, int64_t K, int32_t group,
                                    size_t *bytes);
@@ -342,6 +359,17 @@ w4a16_status w4a16_linear_awq(const void *x, int32_t dtype, const float *act_mul
                               const void *scales, const void *zeros, void *y, int64_t M, int64_t N,
                               int64_t K, int32_t group, int32_t fmt, void *workspace,
                               size_t workspace_bytes, void *stream);
+
+/* Testing hook, for the tests of the kernel error path only: w4a16_gemm_fmt
+ * on a shape whose plan splits tiles by stream-K (W4A16_ERR_INVALID_ARG
+ * otherwise, nothing enqueued), except that the waiting workgroups wait for a
+ * token no producer writes and give up after a few microseconds. Every
+ * kernel ends normally; the split tiles of y are NaN, every other tile is what
+ * w4a16_gemm_fmt writes, and the error word is set (see w4a16_init). */
+w4a16_status w4a16_testing_gemm_expire(const void *x, int32_t dtype, const void *qweight,
+                                       const void *scales, const void *zeros, void *y, int64_t M,
+                                       int64_t N, int64_t K, int32_t group, int32_t fmt,
+                                       void *workspace, size_t workspace_bytes, void *stream);
 
 #ifdef __cplusplus
 }

@@ -116,6 +116,119 @@ def test_stream_k_repeatable_any_workspace_and_graph_replay():
         assert bool(torch.isfinite(filler))
 
 
+def test_stream_k_workspace_holding_small_integers():
+    """A workspace whose every 8-byte word holds a small integer (what ids,
+    positions or a launch counter would leave there) gives the result of a
+    clean one: the hand-over tokens are 64-bit mixes of a random seed, so no
+    stale word passes for a flag."""
+    import torch
+    w4 = H.lib()
+    M, N, K, group = 2048, 8448, 512, 128
+    w, o, pw = _prep(N, K, group)
+    x = H.to_device_bits(wl.random_activations(9, M, K, "f16"), "f16")
+    nbytes = w4.workspace_bytes(M, N, K, group)
+    want = w4.gemm(x, pw, workspace=w4.Workspace("cuda"))
+    for base in (0, 1, 1 << 20):
+        ws = w4.Workspace("cuda")
+        buf = ws.get(nbytes)
+        words = buf[: buf.numel() // 8 * 8].view(torch.int64)
+        words.copy_(torch.arange(base, base + words.numel(), dtype=torch.int64, device="cuda"))
+        for _ in range(3):
+            y = w4.gemm(x, pw, workspace=ws)
+            torch.cuda.synchronize()
+            assert torch.equal(y.view(torch.int16), want.view(torch.int16)), base
+
+
+def test_stream_k_wait_expiry_poisons_tiles_and_reports():
+    """The testing hook makes every waiting workgroup's bounded wait run out
+    (its token is never written): all kernels end, each split tile of y is NaN
+    as a whole, every other output equals the normal call, and the next compute
+    call, whichever it is, returns W4A16_ERR_HIP once; the one after runs."""
+    import torch
+    w4 = H.lib()
+    raw = w4.raw()
+    M, N, K, group = 2048, 8448, 512, 128
+    w, o, pw = _prep(N, K, group)
+    x = H.to_device_bits(wl.random_activations(8, M, K, "bf16"), "bf16")
+    nbytes = w4.workspace_bytes(M, N, K, group)
+    ws = torch.zeros(nbytes, dtype=torch.uint8, device="cuda")
+    want = w4.gemm(x, pw)
+    torch.cuda.synchronize()
+    y = torch.zeros_like(want)
+    head = (x.data_ptr(), 1, pw.qweight.data_ptr(), pw.scales.data_ptr(), pw.zeros_ptr())
+    assert raw.w4a16_testing_gemm_expire(*head, y.data_ptr(), M, N, K, group, 0, ws.data_ptr(), nbytes, None) == 0
+    torch.cuda.synchronize()
+    nan = torch.isnan(y.float())
+    # tiles are 64, 128 or 256 rows by 256 columns: every 64 x 256 block is all NaN or none
+    per_block = nan.view(M // 64, 64, N // 256, 256).sum(dim=(1, 3))
+    assert bool(((per_block == 0) | (per_block == 64 * 256)).all())
+    assert int(per_block.count_nonzero()) > 0
+    assert torch.equal(y.view(torch.int16)[~nan], want.view(torch.int16)[~nan])
+    # the error is reported by the next call (here an unrelated decode call) and then cleared
+    x1 = H.to_device_bits(wl.random_activations(3, 1, K, "bf16"), "bf16")
+    y1 = torch.zeros((1, N), dtype=torch.bfloat16, device="cuda")
+    st = raw.w4a16_linear(x1.data_ptr(), 1, *head[2:], y1.data_ptr(), 1, N, K, group, None, 0, None)
+    assert st == 3, st   # W4A16_ERR_HIP, nothing enqueued
+    torch.cuda.synchronize()
+    assert not bool(y1.float().abs().sum())
+    y2 = torch.zeros_like(want)
+    assert raw.w4a16_gemm(*head, y2.data_ptr(), M, N, K, group, ws.data_ptr(), nbytes, None) == 0
+    torch.cuda.synchronize()
+    assert torch.equal(y2.view(torch.int16), want.view(torch.int16))
+
+
+def test_testing_hook_refuses_shapes_without_a_split():
+    import torch
+    w4 = H.lib()
+    M, N, K, group = 256, 8448, 512, 128
+    assert w4.workspace_bytes(M, N, K, group) == 0
+    w, o, pw = _prep(N, K, group)
+    x = H.to_device_bits(wl.random_activations(4, M, K, "f16"), "f16")
+    y = torch.full((M, N), 3.0, dtype=torch.float16, device="cuda")
+    st = w4.raw().w4a16_testing_gemm_expire(x.data_ptr(), 0, pw.qweight.data_ptr(), pw.scales.data_ptr(),
+                                            pw.zeros_ptr(), y.data_ptr(), M, N, K, group, 0, None, 0, None)
+    assert st == 1   # W4A16_ERR_INVALID_ARG
+    torch.cuda.synchronize()
+    assert bool((y == 3.0).all())
+
+
+def test_default_workspace_is_per_stream():
+    """Calls on two streams without an explicit workspace run at the same
+    time on workspaces of their own: every result equals the serial one."""
+    import threading
+    import torch
+    w4 = H.lib()
+    M, N, K, group = 2048, 8448, 512, 128
+    w, o, pw = _prep(N, K, group)
+    xs = [H.to_device_bits(wl.random_activations(300 + i, M, K, "f16"), "f16") for i in range(2)]
+    want = [w4.gemm(x, pw) for x in xs]
+    torch.cuda.synchronize()
+    streams = [torch.cuda.Stream() for _ in range(2)]
+    errors = []
+
+    def worker(i):
+        try:
+            with torch.cuda.stream(streams[i]):
+                for _ in range(4):
+                    y = w4.gemm(xs[i], pw)
+                    streams[i].synchronize()
+                    if not torch.equal(y.view(torch.int16), want[i].view(torch.int16)):
+                        errors.append(f"stream {i}: split GEMM differs")
+        except Exception as e:   # reported below
+            errors.append(f"stream {i}: {e!r}")
+
+    threads = [threading.Thread(target=worker, args=(i,)) for i in range(2)]
+    for t in threads:
+        t.start()
+    for t in threads:
+        t.join(timeout=60)
+    assert not any(t.is_alive() for t in threads)
+    assert not errors, errors
+    from w4a16_weight_only_dequant_amd import _lib
+    keys = {k for k in _lib._workspaces if k[1] in (s.cuda_stream for s in streams)}
+    assert len(keys) == 2
+
+
 def test_stream_k_short_workspace_refused():
     import torch
     w4 = H.lib()

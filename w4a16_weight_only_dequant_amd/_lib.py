@@ -9,6 +9,7 @@ from __future__ import annotations
 
 import ctypes
 import os
+import threading
 
 import torch
 
@@ -45,6 +46,7 @@ _SIGS = {
     "w4a16_gemv_max_m": (_i32, []),
     "w4a16_linear_kernel": (_i32, [_i64, _i64, _i64, _i32, _i32]),
     "w4a16_device_supported": (ctypes.c_int, [ctypes.c_int]),
+    "w4a16_init": (ctypes.c_int, [ctypes.c_int]),
     "w4a16_packed_bytes": (ctypes.c_int, [_i64, _i64, _i32, _szp, _szp, _szp]),
     "w4a16_workspace_bytes": (ctypes.c_int, [_i64, _i64, _i64, _i32, _szp]),
     "w4a16_pack": (ctypes.c_int, [_vp, _i64, _i64, _i32, _vp, _vp, _vp, _vp]),
@@ -69,6 +71,8 @@ _SIGS = {
     "w4a16_awq_workspace_bytes": (ctypes.c_int, [_i64, _i64, _i64, _i32, _i32, _i32, _szp]),
     "w4a16_linear_awq": (ctypes.c_int, [_vp, _i32, _vp, _vp, _vp, _vp, _vp, _i64, _i64, _i64, _i32, _i32, _vp, _sz,
                                         _vp]),
+    "w4a16_testing_gemm_expire": (ctypes.c_int, [_vp, _i32, _vp, _vp, _vp, _vp, _i64, _i64, _i64, _i32, _i32, _vp,
+                                                 _sz, _vp]),
 }
 
 EXPORTED = tuple(_SIGS)
@@ -127,6 +131,11 @@ def workspace_bytes(M: int, N: int, K: int, group: int) -> int:
     b = _sz()
     _check("w4a16_workspace_bytes", _lib.w4a16_workspace_bytes(M, N, K, group, ctypes.byref(b)))
     return b.value
+
+
+def init(device: int = 0):
+    """One-time set-up of a device (w4a16_init); the compute calls run it on first use."""
+    _check("w4a16_init", _lib.w4a16_init(device))
 
 
 def device_supported(device: int = 0) -> bool:
@@ -223,28 +232,40 @@ class Workspace:
     stream-K split of the tiled GEMM keeps its partial tiles there, and every
     other launch needs none (0 bytes), so no buffer is allocated then. The
     buffer only grows; calls that overlap in time need workspaces of their own.
+    A buffer used on a stream other than the one it was allocated on is
+    recorded on that stream, so that the caching allocator does not hand its
+    memory out again before the work queued there is done.
     """
 
     def __init__(self, device=None):
         self.device = torch.device(device) if device is not None else torch.device("cuda")
         self.buf = None
+        self._alloc_stream = None
 
-    def get(self, nbytes: int):
+    def get(self, nbytes: int, stream=None):
         if nbytes == 0:
             return None
         if self.buf is None or self.buf.numel() < nbytes:
+            # the old buffer (if any) was recorded on every stream that used it
             self.buf = torch.zeros(max(nbytes, 1 << 20), dtype=torch.uint8, device=self.device)
+            self._alloc_stream = torch.cuda.current_stream(self.device)
+        if stream is not None and stream != self._alloc_stream:
+            self.buf.record_stream(stream)
         return self.buf
 
 
 _workspaces = {}
+_workspaces_lock = threading.Lock()
 
 
-def _default_workspace(device) -> Workspace:
-    key = (device.type, device.index)
-    ws = _workspaces.get(key)
-    if ws is None:
-        ws = _workspaces[key] = Workspace(device)
+def _default_workspace(device, stream) -> Workspace:
+    """One default workspace per (device, stream): calls on different streams
+    may run at the same time and must not share partial tiles and flags."""
+    key = (device.index, stream.cuda_stream)
+    with _workspaces_lock:
+        ws = _workspaces.get(key)
+        if ws is None:
+            ws = _workspaces[key] = Workspace(device)
     return ws
 
 
@@ -265,7 +286,8 @@ def _call(fn_name: str, x: torch.Tensor, pw: PackedWeight, out=None, workspace=N
     M = x.shape[0]
     y = _output(out, M, pw.N, x)
     nbytes = workspace_bytes(M, pw.N, pw.K, pw.group)
-    ws = (workspace or _default_workspace(x.device)).get(nbytes)
+    strm = stream if stream is not None else torch.cuda.current_stream(x.device)
+    ws = (workspace or _default_workspace(x.device, strm)).get(nbytes, strm)
     ws_ptr = ws.data_ptr() if ws is not None else None
     ws_len = ws.numel() if ws is not None else 0
     fn_name = fn_name + "_fmt"
@@ -307,7 +329,8 @@ def linear_group(xs, pws, outs=None, workspace=None, stream=None):
     ys = [_output(outs[i] if outs is not None else None, M, pw.N, xs[0]) for i, pw in enumerate(pws)]
     arr = lambda vals: (ctypes.c_void_p * count)(*vals)  # noqa: E731
     nbytes = max(workspace_bytes(M, pw.N, K, group) for pw in pws)
-    ws = (workspace or _default_workspace(xs[0].device)).get(nbytes)
+    strm = stream if stream is not None else torch.cuda.current_stream(xs[0].device)
+    ws = (workspace or _default_workspace(xs[0].device, strm)).get(nbytes, strm)
     zeros = arr([p.zeros_ptr() for p in pws]) if pws[0].zeros is not None else None
     _check("w4a16_linear_group_fmt", _lib.w4a16_linear_group_fmt(
         count, arr([x.data_ptr() for x in xs]), _dtype_code(xs[0]), arr([p.qweight.data_ptr() for p in pws]),
@@ -379,7 +402,8 @@ def linear_awq(x: torch.Tensor, act_mul: torch.Tensor, pw: PackedWeight, out=Non
     nb = _sz()
     _check("w4a16_awq_workspace_bytes", _lib.w4a16_awq_workspace_bytes(M, pw.N, pw.K, pw.group, _fmt_code(pw.fmt),
                                                                        _dtype_code(x), ctypes.byref(nb)))
-    ws = (workspace or _default_workspace(x.device)).get(nb.value)
+    strm = stream if stream is not None else torch.cuda.current_stream(x.device)
+    ws = (workspace or _default_workspace(x.device, strm)).get(nb.value, strm)
     _check("w4a16_linear_awq", _lib.w4a16_linear_awq(
         x.data_ptr(), _dtype_code(x), act_mul.data_ptr(), pw.qweight.data_ptr(), pw.scales.data_ptr(),
         pw.zeros_ptr(), y.data_ptr(), M, pw.N, pw.K, pw.group, _fmt_code(pw.fmt),

@@ -65,10 +65,51 @@ Range range_of(const void *p, size_t bytes) {
     return Range{lo, lo + bytes};
 }
 
+// Process-wide kernel error word: pinned host memory, mapped into every
+// device's address space and coherent (kernels write it with system-scope
+// stores, the host reads it without a copy). Allocated once by the first
+// w4a16_init; g_err_dev holds its address on each initialised device.
+std::mutex g_init_mu;
+unsigned int *g_err_host = nullptr;
+std::atomic<unsigned int *> g_err_dev[kMaxDevices];
+std::atomic<int> g_ready[kMaxDevices];   // 1 once w4a16_init succeeded on the device
+
+w4a16_status init_device(int dev) {
+    if (dev < 0 || dev >= kMaxDevices) return W4A16_ERR_INVALID_ARG;
+    if (g_ready[dev].load(std::memory_order_acquire)) return W4A16_OK;
+    std::lock_guard<std::mutex> lock(g_init_mu);
+    if (g_ready[dev].load(std::memory_order_acquire)) return W4A16_OK;
+    if (g_err_host == nullptr) {
+        void *p = nullptr;
+        if (hipHostMalloc(&p, 256, hipHostMallocMapped | hipHostMallocPortable | hipHostMallocCoherent) != hipSuccess)
+            return W4A16_ERR_HIP;
+        std::memset(p, 0, 256);
+        g_err_host = static_cast<unsigned int *>(p);
+    }
+    void *d = nullptr;
+    if (hipHostGetDevicePointer(&d, g_err_host, 0) != hipSuccess) return W4A16_ERR_HIP;
+    g_err_dev[dev].store(static_cast<unsigned int *>(d), std::memory_order_release);
+    g_ready[dev].store(1, std::memory_order_release);
+    return W4A16_OK;
+}
+
+// A kernel error recorded since the last call (a stream-K wait that ran out):
+// taken once, reported as W4A16_ERR_HIP by the call that finds it.
+bool take_kernel_error() {
+    unsigned int *p = g_err_host;
+    return p != nullptr && __atomic_exchange_n(p, 0u, __ATOMIC_SEQ_CST) != 0u;
+}
+
+// The device check of every compute call: a gfx950, set up (w4a16_init on
+// first use), and no kernel error pending.
 w4a16_status check_device() {
     int dev = 0;
     if (hipGetDevice(&dev) != hipSuccess) return W4A16_ERR_HIP;
-    return w4a16_device_supported(dev);
+    w4a16_status st = w4a16_device_supported(dev);
+    if (st != W4A16_OK) return st;
+    st = init_device(dev);
+    if (st != W4A16_OK) return st;
+    return take_kernel_error() ? W4A16_ERR_HIP : W4A16_OK;
 }
 
 // Argument checks shared by gemv / gemm / linear. The symmetric formats do
@@ -202,6 +243,17 @@ const char *w4a16_status_string(int status) {
 
 int w4a16_layout_version(void) { return W4A16_LAYOUT_VERSION; }
 
+w4a16_status w4a16_init(int device) {
+    w4a16_status st = w4a16_device_supported(device);
+    if (st != W4A16_OK) return st;
+    int cur = 0;
+    if (hipGetDevice(&cur) != hipSuccess) return W4A16_ERR_HIP;
+    if (cur != device && hipSetDevice(device) != hipSuccess) return W4A16_ERR_HIP;
+    st = init_device(device);
+    if (cur != device && hipSetDevice(cur) != hipSuccess) return W4A16_ERR_HIP;
+    return st;
+}
+
 int32_t w4a16_gemv_max_m(void) { return gemv_max_m(); }
 
 int32_t w4a16_linear_kernel(int64_t M, int64_t N, int64_t K, int32_t group, int32_t dtype) {
@@ -330,6 +382,23 @@ w4a16_status w4a16_gemm_fmt(const void *x, int32_t dtype, const void *qweight, c
     if (prefill_workspace_bytes(plan) > need) return W4A16_ERR_WORKSPACE;   // (the same plan: never)
     hipError_t e = launch_gemm(x, dtype == W4A16_BF16, qweight, scales, zeros, y, (int)M, (int)N,
                                (int)K, group, fmt, plan, workspace, reinterpret_cast<hipStream_t>(stream));
+    return e == hipSuccess ? W4A16_OK : W4A16_ERR_HIP;
+}
+
+w4a16_status w4a16_testing_gemm_expire(const void *x, int32_t dtype, const void *qweight, const void *scales,
+                                       const void *zeros, void *y, int64_t M, int64_t N, int64_t K, int32_t group,
+                                       int32_t fmt, void *workspace, size_t workspace_bytes, void *stream) {
+    const size_t need = (M >= 1 && M <= (1LL << 24) && shape_ok(N, K, group)) ? gemm_need(M, N, K, group) : 0;
+    if (need == 0) return W4A16_ERR_INVALID_ARG;   // no stream-K split for this shape
+    w4a16_status st = check_linear(x, dtype, qweight, scales, zeros, y, M, N, K, group, fmt, workspace,
+                                   workspace_bytes, need);
+    if (st != W4A16_OK) return st;
+    st = check_device();
+    if (st != W4A16_OK) return st;
+    GemmPlan plan = gemm_plan(M, N, K, group);
+    plan.sk_expire_test = 1;
+    hipError_t e = launch_gemm(x, dtype == W4A16_BF16, qweight, scales, zeros, y, (int)M, (int)N, (int)K, group,
+                               fmt, plan, workspace, reinterpret_cast<hipStream_t>(stream));
     return e == hipSuccess ? W4A16_OK : W4A16_ERR_HIP;
 }
 
@@ -525,3 +594,9 @@ w4a16_status w4a16_linear_awq(const void *x, int32_t dtype, const float *act_mul
 }
 
 }  // extern "C"
+
+unsigned int *w4a16::kernel_error_word() {
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return nullptr;
+    return g_err_dev[dev].load(std::memory_order_acquire);
+}

@@ -2,6 +2,9 @@
 // dispatch over the weight formats. The kernel is in prefill_kernel.hpp; each
 // weight format is compiled in its own translation unit (this one: the 4-bit
 // zero-point format; prefill_sym4.hip, prefill_sym8.hip).
+#include <chrono>
+#include <random>
+
 #include "prefill_kernel.hpp"
 
 namespace w4a16 {
@@ -55,9 +58,28 @@ void prefill_stream_k(int64_t M, int64_t N, int64_t K, int cus, GemmPlan &plan) 
     plan.sk_wgs = cus;
 }
 
+// splitmix64's output function (Steele, Lea and Flood, "Fast splittable
+// pseudorandom number generators", 2014): a bijection of 64-bit words, so
+// distinct counter values give distinct tokens.
+static unsigned long long mix64(unsigned long long z) {
+    z = (z ^ (z >> 30)) * 0xBF58476D1CE4E5B9ull;
+    z = (z ^ (z >> 27)) * 0x94D049BB133111EBull;
+    return z ^ (z >> 31);
+}
+
+static unsigned long long token_seed() {
+    std::random_device rd;
+    unsigned long long s = ((unsigned long long)rd() << 32) ^ rd();
+    s ^= (unsigned long long)std::chrono::steady_clock::now().time_since_epoch().count();
+    return s;
+}
+
 unsigned long long next_sk_token() {
+    static const unsigned long long seed = token_seed();
     static std::atomic<unsigned long long> counter{0};
-    return counter.fetch_add(1, std::memory_order_relaxed) + 1;
+    const unsigned long long c = counter.fetch_add(1, std::memory_order_relaxed);
+    const unsigned long long t = mix64(seed + c * 0x9E3779B97F4A7C15ull);
+    return t != 0 ? t : 0x9E3779B97F4A7C15ull;   // 0 marks an empty flag
 }
 
 size_t prefill_workspace_bytes(const GemmPlan &plan) {

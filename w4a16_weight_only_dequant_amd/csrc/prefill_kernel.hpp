@@ -154,7 +154,8 @@ __global__ __launch_bounds__(64 * WM * WN) __attribute__((amdgpu_waves_per_eu(WM
     const uint16_t *__restrict__ x, const uint4 *__restrict__ qw, const uint4 *__restrict__ qw_hi,
     const uint16_t *__restrict__ scales, const uint32_t *__restrict__ zeros, uint16_t *__restrict__ y, int M,
     int N, int K, int m_tiles, int n_tiles, int mshift, int dp_tiles, int sk_wgs, float4 *__restrict__ partials,
-    unsigned long long *__restrict__ flags, unsigned long long token) {
+    unsigned long long *__restrict__ flags, unsigned long long token, unsigned long long wait_token,
+    unsigned int *__restrict__ err) {
     using FT = FormatTraits<FMT>;
     constexpr int NT = 64 * WM * WN;                 // threads
     constexpr int TM = BM / WM / 32, TN = BN / WN / 32;   // 32x32 blocks per wave
@@ -496,20 +497,37 @@ __global__ __launch_bounds__(64 * WM * WN) __attribute__((amdgpu_waves_per_eu(WM
             continue;
         }
         if (SK && kind == 2) {
+            __shared__ float sk_poison;
             if (tid == 0) {
                 // bounded wait (about a second): the producer never waits before
                 // producing, so this ends; the bound only keeps a broken launch
                 // from holding the device. Relaxed polls (device-coherent loads);
                 // the acquire below then orders the partial's loads after them.
-                for (int spin = 0; spin < (1 << 21); ++spin) {
-                    if (__hip_atomic_load(&flags[s_sk - 1], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == token) break;
+                // (a launch testing the expiry waits for another token, briefly)
+                const int spin_limit = wait_token == token ? (1 << 21) : 64;
+                int ready = 0;
+                for (int spin = 0; spin < spin_limit; ++spin) {
+                    if (__hip_atomic_load(&flags[s_sk - 1], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == wait_token) {
+                        ready = 1;
+                        break;
+                    }
                     __builtin_amdgcn_s_sleep(2);
                 }
+                // the wait ran out: the tile is written as NaN (the partial gets a
+                // NaN term) and the process's error word (host memory) is set, so
+                // the failure shows both in the output and in the status of the
+                // next call
+                if (!ready && err != nullptr) {
+                    __hip_atomic_store(err, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+                    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "");
+                }
+                sk_poison = ready ? 0.0f : __builtin_nanf("");
                 // invalidates this CU's L1 and this XCD's L2, which all waves of
                 // the workgroup read through: no stale line of the partial is left
                 __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
             }
             __syncthreads();
+            const float poison = sk_poison;
             const float4 *slot = partials + (size_t)(s_sk - 1) * kPart * NT;
             // all 32 loads of the thread's part issue back to back (one round
             // trip). The fix-up costs more than that: every workgroup reaches it
@@ -522,10 +540,10 @@ __global__ __launch_bounds__(64 * WM * WN) __attribute__((amdgpu_waves_per_eu(WM
 #pragma unroll
                     for (int q = 0; q < 4; ++q) {
                         const float4 p = slot[((a * TN + b) * 4 + q) * NT + tid];
-                        acc[a][b][4 * q] += p.x;
-                        acc[a][b][4 * q + 1] += p.y;
-                        acc[a][b][4 * q + 2] += p.z;
-                        acc[a][b][4 * q + 3] += p.w;
+                        acc[a][b][4 * q] += p.x + poison;
+                        acc[a][b][4 * q + 1] += p.y + poison;
+                        acc[a][b][4 * q + 2] += p.z + poison;
+                        acc[a][b][4 * q + 3] += p.w + poison;
                     }
             // the flag of this launch is consumed: clear it, so a replay of the
             // same launch (same token, e.g. from a graph) waits again
@@ -569,6 +587,7 @@ __global__ __launch_bounds__(64 * WM * WN) __attribute__((amdgpu_waves_per_eu(WM
 struct SkArgs {
     int dp_tiles, sk_wgs;
     void *ws;
+    bool expire_test;   // consumers wait for a token no producer writes (tests the expiry path)
 };
 
 template <int BM, int BN, int WM, int WN, int GROUP, bool BF, int FMT>
@@ -594,11 +613,16 @@ hipError_t launch_tile(const void *x, const void *qw, const void *qh, const void
         part = reinterpret_cast<float4 *>(sk.ws);
         flags = reinterpret_cast<unsigned long long *>(static_cast<char *>(sk.ws) + (size_t)skw * BM * BN * 4);
     }
+    // consumers wait for the token their producer writes; a launch that tests
+    // the expiry of the wait gives them one no producer writes and a short bound
+    const unsigned long long token = skw > 0 ? next_sk_token() : 0ull;
+    const unsigned long long wait_token = sk.expire_test ? token ^ 0xA5A5A5A5A5A5A5A5ull : token;
+    unsigned int *err = skw > 0 ? kernel_error_word() : nullptr;
     hipLaunchKernelGGL(kern, dim3((unsigned)(dp + skw)), dim3(64 * WM * WN), lds, stream,
                        reinterpret_cast<const uint16_t *>(x), reinterpret_cast<const uint4 *>(qw),
                        reinterpret_cast<const uint4 *>(qh), reinterpret_cast<const uint16_t *>(sc),
                        reinterpret_cast<const uint32_t *>(zp), reinterpret_cast<uint16_t *>(y), M, N, K, m_tiles,
-                       n_tiles, ms, dp, skw, part, flags, skw > 0 ? next_sk_token() : 0ull);
+                       n_tiles, ms, dp, skw, part, flags, token, wait_token, err);
     return hipGetLastError();
 }
 
@@ -621,7 +645,7 @@ template <int FMT>
 hipError_t launch_prefill_fmt(const void *x, bool bf16, const void *qweight, const void *scales, const void *zeros,
                               void *y, int M, int N, int K, int group, const GemmPlan &plan, void *workspace,
                               hipStream_t stream) {
-    const SkArgs sk{plan.dp_tiles, plan.sk_wgs, workspace};
+    const SkArgs sk{plan.dp_tiles, plan.sk_wgs, workspace, plan.sk_expire_test != 0};
     const int ms = group == 256 ? 1 : 0;
     const void *qh = FormatTraits<FMT>::two_planes
                          ? static_cast<const void *>(static_cast<const char *>(qweight) + (size_t)N * K / 2)

@@ -93,6 +93,7 @@ struct GemmPlan {
     int tile;          // tiled: one of kTile*
     int dp_tiles;      // tiled, stream-K: tiles computed whole, one workgroup each
     int sk_wgs;        // tiled, stream-K: workgroups sharing the other tiles' columns (0: none)
+    int sk_expire_test;   // 1: consumers wait for a token no producer writes (exercises the expiry path)
 };
 
 GemmPlan gemm_plan(int64_t M, int64_t N, int64_t K, int32_t group);
@@ -106,11 +107,18 @@ constexpr int kTileCols = 256;
 // partial tile per stream-K workgroup, then one 8-byte flag each.
 void prefill_stream_k(int64_t M, int64_t N, int64_t K, int cus, GemmPlan &plan);
 size_t prefill_workspace_bytes(const GemmPlan &plan);
-// Stream-K hand-over token: unique per launch in this process (never 0), so
-// flags left in a workspace by other launches never match. A replayed graph
-// reuses its token; the consumers clear every flag they used, so a complete
-// launch leaves all flags at 0.
+// Stream-K hand-over token: distinct for every launch in this process and
+// never 0; a 64-bit mix of a random per-process seed and a counter, so that
+// neither flags left by other launches nor whatever the workspace held before
+// (small integers, indices) match it except by a 2^-64 chance. A replayed
+// graph reuses its token; the consumers clear every flag they used, so a
+// complete launch leaves all flags at 0.
 unsigned long long next_sk_token();
+// Process-wide error word in pinned, device-visible host memory (its address
+// on the current device; nullptr before w4a16_init ran on it). A stream-K
+// consumer whose bounded wait runs out writes its tile as NaN and sets the
+// word; the next compute call takes it and returns W4A16_ERR_HIP.
+unsigned int *kernel_error_word();
 
 // Problems of one grouped launch (kernel argument, passed by value).
 constexpr int kMaxGroup = 8;
