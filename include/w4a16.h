@@ -147,10 +147,11 @@ const char *w4a16_status_string(int status);
 int w4a16_layout_version(void);
 
 /* One-time set-up of `device` (a gfx950) for this library, safe to call again
- * and from several threads: the device check and, once per process, a
- * 256-byte block of pinned host memory mapped into every device (the kernel
- * error word below). Every compute call runs it on its device on first use;
- * call it at start-up to keep that allocation out of later calls.
+ * and from several threads: the device check, the device address of the
+ * library's static scratch array (w4a16_linear_noalloc) and, once per
+ * process, a 256-byte block of pinned host memory mapped into every device
+ * (the kernel error word below). Every compute call runs it on its device on
+ * first use; call it at start-up to keep that allocation out of later calls.
  * Kernel errors: when the bounded wait of a stream-K hand-over (see
  * w4a16_workspace_bytes) runs out, which a correct launch never lets happen,
  * the waiting workgroup writes its whole output tile as NaN and sets the
@@ -359,6 +360,24 @@ w4a16_status w4a16_linear_awq(const void *x, int32_t dtype, const float *act_mul
                               const void *scales, const void *zeros, void *y, int64_t M, int64_t N,
                               int64_t K, int32_t group, int32_t fmt, void *workspace,
                               size_t workspace_bytes, void *stream);
+
+/* For callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid it): w4a16_linear_fmt
+ * with no workspace argument. The tiled GEMM's stream-K partials and flags go
+ * to a static device array of W4A16_NOALLOC_SCRATCH_BYTES that each device
+ * holds for the life of the process; the call makes no allocation of any
+ * kind. It needs w4a16_init to have run on the current device
+ * (W4A16_ERR_INVALID_ARG otherwise), and returns W4A16_ERR_WORKSPACE, with
+ * nothing enqueued, for a shape whose plan needs more scratch than that
+ * (none on a device of at most 256 compute units). All calls on one device
+ * share the array, so calls that overlap in time on one device (other
+ * streams, other threads) race and must not be made; consecutive calls are
+ * safe (the array needs no clearing: its stale flags never match a later
+ * launch's token). Everything else is as w4a16_linear_fmt. */
+#define W4A16_NOALLOC_SCRATCH_BYTES ((size_t)(64u << 20) + (4u << 10))
+w4a16_status w4a16_linear_noalloc(const void *x, int32_t dtype, const void *qweight,
+                                  const void *scales, const void *zeros, void *y, int64_t M,
+                                  int64_t N, int64_t K, int32_t group, int32_t fmt, void *stream);
 
 /* Testing hook, for the tests of the kernel error path only: w4a16_gemm_fmt
  * on a shape whose plan splits tiles by stream-K (W4A16_ERR_INVALID_ARG

@@ -71,6 +71,7 @@ _SIGS = {
     "w4a16_awq_workspace_bytes": (ctypes.c_int, [_i64, _i64, _i64, _i32, _i32, _i32, _szp]),
     "w4a16_linear_awq": (ctypes.c_int, [_vp, _i32, _vp, _vp, _vp, _vp, _vp, _i64, _i64, _i64, _i32, _i32, _vp, _sz,
                                         _vp]),
+    "w4a16_linear_noalloc": (ctypes.c_int, [_vp, _i32, _vp, _vp, _vp, _vp, _i64, _i64, _i64, _i32, _i32, _vp]),
     "w4a16_testing_gemm_expire": (ctypes.c_int, [_vp, _i32, _vp, _vp, _vp, _vp, _i64, _i64, _i64, _i32, _i32, _vp,
                                                  _sz, _vp]),
 }
@@ -338,6 +339,21 @@ def linear_group(xs, pws, outs=None, workspace=None, stream=None):
         arr([y.data_ptr() for y in ys]), M, (ctypes.c_int64 * count)(*[p.N for p in pws]), K, group,
         _fmt_code(pws[0].fmt), ws.data_ptr() if ws is not None else None, ws.numel() if ws is not None else 0, _stream_ptr(stream)))
     return ys
+
+
+def linear_noalloc(x, pw, out, stream=None):
+    """w4a16_linear with the library's static scratch for its workspace: the
+    call allocates nothing (out is required; w4a16_init must have run on the
+    device). Calls that overlap in time on one device must not be made."""
+    if x.dim() != 2 or x.shape[1] != pw.K or not x.is_cuda or not x.is_contiguous():
+        raise ValueError(f"x must be a contiguous CUDA tensor [M][{pw.K}]")
+    if out is None:
+        raise ValueError("linear_noalloc writes into a given out tensor")
+    y = _output(out, x.shape[0], pw.N, x)
+    _check("w4a16_linear_noalloc", _lib.w4a16_linear_noalloc(
+        x.data_ptr(), _dtype_code(x), pw.qweight.data_ptr(), pw.scales.data_ptr(), pw.zeros_ptr(), y.data_ptr(),
+        x.shape[0], pw.N, pw.K, pw.group, _fmt_code(pw.fmt), _stream_ptr(stream)))
+    return y
 
 
 def linear(x, pw, out=None, workspace=None, stream=None):

@@ -74,6 +74,15 @@ unsigned int *g_err_host = nullptr;
 std::atomic<unsigned int *> g_err_dev[kMaxDevices];
 std::atomic<int> g_ready[kMaxDevices];   // 1 once w4a16_init succeeded on the device
 
+// Scratch of w4a16_linear_noalloc: the stream-K partial tiles and flags of the
+// tiled GEMM, which need at most (256 x 256 x 4 + 8) bytes per compute unit,
+// 64 MiB + 2 KiB on 256 compute units. Each device holds its own copy for the
+// life of the process. The name is a host-side stand-in: host code uses only
+// the device address that w4a16_init stores in g_scratch.
+constexpr size_t kScratchBytes = W4A16_NOALLOC_SCRATCH_BYTES;
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+std::atomic<void *> g_scratch[kMaxDevices];
+
 w4a16_status init_device(int dev) {
     if (dev < 0 || dev >= kMaxDevices) return W4A16_ERR_INVALID_ARG;
     if (g_ready[dev].load(std::memory_order_acquire)) return W4A16_OK;
@@ -89,6 +98,9 @@ w4a16_status init_device(int dev) {
     void *d = nullptr;
     if (hipHostGetDevicePointer(&d, g_err_host, 0) != hipSuccess) return W4A16_ERR_HIP;
     g_err_dev[dev].store(static_cast<unsigned int *>(d), std::memory_order_release);
+    void *sp = nullptr;
+    if (hipGetSymbolAddress(&sp, HIP_SYMBOL(scratch)) != hipSuccess || sp == nullptr) return W4A16_ERR_HIP;
+    g_scratch[dev].store(sp, std::memory_order_release);
     g_ready[dev].store(1, std::memory_order_release);
     return W4A16_OK;
 }
@@ -470,6 +482,23 @@ w4a16_status w4a16_linear_group_fmt(int32_t count, const void *const *x, int32_t
     hipError_t e = launch_gemm_group(tab, dtype == W4A16_BF16, (int)M, (int)K, group, fmt, plan,
                                      reinterpret_cast<hipStream_t>(stream));
     return e == hipSuccess ? W4A16_OK : W4A16_ERR_HIP;
+}
+
+w4a16_status w4a16_linear_noalloc(const void *x, int32_t dtype, const void *qweight, const void *scales,
+                                  const void *zeros, void *y, int64_t M, int64_t N, int64_t K, int32_t group,
+                                  int32_t fmt, void *stream) {
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return W4A16_ERR_HIP;
+    // the set-up (and its one allocation) must have run on this device
+    if (dev < 0 || dev >= kMaxDevices || !g_ready[dev].load(std::memory_order_acquire))
+        return W4A16_ERR_INVALID_ARG;
+    size_t need = 0;
+    if (M >= 1 && M <= (1LL << 24) && shape_ok(N, K, group) && !prefer_gemv(M, N, K, group, dtype, fmt))
+        need = gemm_need(M, N, K, group);
+    if (need > kScratchBytes) return W4A16_ERR_WORKSPACE;
+    void *ws = need > 0 ? g_scratch[dev].load(std::memory_order_acquire) : nullptr;
+    return w4a16_linear_fmt(x, dtype, qweight, scales, zeros, y, M, N, K, group, fmt, ws,
+                            need > 0 ? kScratchBytes : 0, stream);
 }
 
 w4a16_status w4a16_linear_group(int32_t count, const void *const *x, int32_t dtype, const void *const *qweight,
