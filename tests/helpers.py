@@ -66,9 +66,10 @@ def y_to_f64(y) -> np.ndarray:
     return y.float().cpu().numpy().astype(np.float64)
 
 
-def check_against_oracle(y_gpu, x_bits, dtype, o, group, cols=None):
-    """Assert |y - y_ref| <= 2e-3 * sum|x w_hat| + 1e-5 (+ the one rounding to
-    the output type) element-wise; return the max ratio."""
+def check_against_oracle(y_gpu, x_bits, dtype, o, group, cols=None, quiet=False):
+    """Assert |y - y_ref| <= 2e-3 * sum|x w_hat| + 1e-5 (bf16 outputs: plus
+    half a bf16 ulp, the one rounding to the output type) element-wise; print
+    the max ratio to that bar and to the bare bar, return the former."""
     y = y_to_f64(y_gpu)
     if cols is not None:
         y = y[:, cols]
@@ -83,6 +84,27 @@ def check_against_oracle(y_gpu, x_bits, dtype, o, group, cols=None):
         y_ref, a = ref.linear_ref_rows(x_bits, dtype, o["codes"], o["s_bits"], o["zeros"], group, cols)
     r = ref.error_ratio(y, y_ref, a, dtype)
     worst = float(r.max()) if r.size else 0.0
+    bare = float(ref.error_ratio(y, y_ref, a).max()) if r.size else 0.0
+    if not quiet:
+        print(f"[parity] {y.shape[0]}x{y.shape[1]} outputs: max ratio {worst:.4f} (bare bar {bare:.4f})", flush=True)
     assert np.all(np.isfinite(y)), "non-finite output"
     assert worst <= 1.0, f"max error ratio {worst:.3g} (> 1) at {np.unravel_index(np.argmax(r), r.shape)}"
+    return worst
+
+
+def check_every_output(y_gpu, x_bits, dtype, o, group, chunk=2048):
+    """check_against_oracle over every output column, in chunks of columns
+    (the fp64 product of a full prefill shape is ~1.5e11 MACs)."""
+    N = int(y_gpu.shape[1])
+    worst = bare = 0.0
+    for c0 in range(0, N, chunk):
+        cols = np.arange(c0, min(N, c0 + chunk))
+        y = y_to_f64(y_gpu[:, c0:c0 + len(cols)])
+        y_ref, a = ref.linear_ref_rows(x_bits, dtype, o["codes"], o["s_bits"], o["zeros"], group, cols)
+        r = ref.error_ratio(y, y_ref, a, dtype)
+        assert np.all(np.isfinite(y)), f"non-finite output in columns {c0}.."
+        assert float(r.max()) <= 1.0, f"max error ratio {float(r.max()):.3g} (> 1) in columns {c0}.."
+        worst = max(worst, float(r.max()))
+        bare = max(bare, float(ref.error_ratio(y, y_ref, a).max()))
+    print(f"[parity] every output of {tuple(y_gpu.shape)}: max ratio {worst:.4f} (bare bar {bare:.4f})", flush=True)
     return worst

@@ -137,6 +137,23 @@ def test_gemm_full_size_decode_batches(cfg, mat):
 
 
 @pytest.mark.slow
+@pytest.mark.parametrize("fn", ["gemm", "linear"])
+def test_gemm_full_size_prefill_every_output(fn):
+    """The prefill configuration at its full size (M = 2048, N = 13824,
+    K = 5120, bf16): every one of the 28.3 M outputs against the oracle."""
+    import torch
+    cfg, mat = 4, 0
+    wlc = wl.WORKLOADS[cfg]
+    group = wlc.group
+    w, o, pw = H.prepared((cfg, mat), lambda: wl.weights(cfg, mat), group)
+    M = wlc.ms[0]
+    x = wl.activations(cfg, mat, M)
+    y = getattr(H.lib(), fn)(H.to_device_bits(x, wlc.dtype), pw)
+    torch.cuda.synchronize()
+    H.check_every_output(y, x, wlc.dtype, o, group)
+
+
+@pytest.mark.slow
 def test_gemm_full_size_prefill_sampled_columns():
     """The prefill configuration at its full size: every row, on 320 output
     columns spread over all tiles (first and last tile included)."""

@@ -362,6 +362,20 @@ def test_workspace_bytes_are_enough_and_nothing_beyond_is_written(M, N, K, group
     H.drop(("sk", N, K, group))
 
 
+@pytest.mark.parametrize("dtype", ["f16", "bf16"])
+def test_stream_k_every_output(dtype):
+    """M = 2048, N = 8448, K = 512: 264 tiles, all split over the 256
+    workgroups; every output against the oracle."""
+    import torch
+    M, N, K, group = 2048, 8448, 512, 128
+    assert _uses_stream_k(M, N, K, group)
+    w, o, pw = _prep(N, K, group)
+    x = wl.random_activations(78, M, K, dtype)
+    y = H.lib().linear(H.to_device_bits(x, dtype), pw)
+    torch.cuda.synchronize()
+    H.check_every_output(y, x, dtype, o, group)
+
+
 def test_stream_k_full_size_ffn_shape():
     """M = 2048, N = 11008, K = 4096 (a 7B-style FFN width: 344 tiles, the last
     two rounds split): long segments of 32-column tiles, every row of 160

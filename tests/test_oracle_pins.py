@@ -288,10 +288,48 @@ def test_error_ratio_bar():
     a = np.array([[10.0, 0.0]])
     r = ref.error_ratio(np.array([[1.0 + 0.02001, 1e-5]]), y_ref, a)
     assert np.allclose(r, [[1.0, 1.0]], rtol=1e-9)
-    # with the output rounding: half an ulp of the format at |y| joins the budget
-    r16 = ref.error_ratio(np.array([[1.0 + 0.02001 + 2.0 ** -11]]), np.array([[1.0]]), np.array([[10.0]]), "f16")
+    # fp16 outputs are held to the bare bar; bf16 outputs get half a bf16 ulp at |y|
+    r16 = ref.error_ratio(np.array([[1.0 + 0.02001]]), np.array([[1.0]]), np.array([[10.0]]), "f16")
     rbf = ref.error_ratio(np.array([[1.0 + 0.02001 + 2.0 ** -8]]), np.array([[1.0]]), np.array([[10.0]]), "bf16")
     assert np.allclose(r16, 1.0, rtol=1e-6) and np.allclose(rbf, 1.0, rtol=1e-6)
+
+
+def test_correctly_rounded_fp16_always_meets_the_bare_bar():
+    """For every positive finite fp16 value v (subnormals included), the exact
+    results farthest from v that still round to it (v minus and plus half the
+    gaps to its neighbours), at the tightest budget sum|x*w_hat| = |y|: the
+    rounding alone stays within a quarter of the bare bar, so fp16 needs no
+    rounding term."""
+    bits = np.arange(1, 0x7BFF, dtype=np.uint16)
+    v = bits.view(np.float16).astype(np.float64)
+    up = np.spacing(bits.view(np.float16)).astype(np.float64) / 2
+    down = (v - (bits - 1).view(np.float16).astype(np.float64)) / 2
+    worst = 0.0
+    for y in (v + up, v - down):   # rounding error half a gap either way
+        r = ref.error_ratio(v, y, np.abs(y), "f16")
+        worst = max(worst, float(r.max()))
+    assert worst <= 2.0 ** -11 / 2e-3 + 1e-12 and worst < 0.25
+    # and on random fp64 results rounded by numpy (round to nearest even)
+    rng = np.random.default_rng(3)
+    y = rng.standard_normal(200000) * np.exp2(rng.integers(-26, 15, 200000))
+    r = ref.error_ratio(y.astype(np.float16).astype(np.float64), y, np.abs(y), "f16")
+    assert float(r.max()) < 0.25
+
+
+def test_linear_ref_rows_columns_equal_the_full_product():
+    """linear_ref_rows(cols=...) gives exactly the columns `cols` of
+    linear_ref over the whole dequantised matrix (same fp64 products)."""
+    rng = np.random.default_rng(12)
+    N, K, group, M = 48, 256, 32, 5
+    w = rng.standard_normal((N, K)).astype(np.float32)
+    codes, s_bits, zeros = ref.quantize_groupwise(w, group)
+    x = ref.f32_to_f16_bits(rng.standard_normal((M, K)).astype(np.float32))
+    y_all, a_all = ref.linear_ref(x, "f16", ref.dequantize(codes, s_bits, zeros, group))
+    for cols in (np.array([0]), np.array([N - 1, 3, 17]), np.arange(0, N, 5)):
+        y, a = ref.linear_ref_rows(x, "f16", codes, s_bits, zeros, group, cols)
+        assert np.array_equal(y, y_all[:, cols]) and np.array_equal(a, a_all[:, cols])
+    y, a = ref.linear_ref_rows(x, "f16", codes, s_bits, zeros, group)
+    assert np.array_equal(y, y_all) and np.array_equal(a, a_all)
 
 
 def test_out_half_ulp_fp16_matches_numpy_spacing():
