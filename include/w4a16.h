@@ -316,6 +316,14 @@ int32_t w4a16_gemv_max_m(void);
  * arguments w4a16_linear would reject.
  * Host-only (queries the device's LDS size once). */
 int32_t w4a16_linear_kernel(int64_t M, int64_t N, int64_t K, int32_t group, int32_t dtype);
+/* The same choice for a weight format, with the launch geometry of that
+ * kernel: *workgroups workgroups of *threads threads (either pointer may be
+ * NULL). For profiles and benchmarks: a kernel trace's rows of one shape are
+ * told apart by kernel, grid and workgroup size. Returns the kernel code as
+ * w4a16_linear_kernel, -1 for arguments w4a16_linear_fmt rejects. Host-only
+ * (queries the device's LDS size and compute units once). */
+int32_t w4a16_linear_launch_shape(int64_t M, int64_t N, int64_t K, int32_t group, int32_t dtype,
+                                  int32_t fmt, int64_t *workgroups, int32_t *threads);
 
 /* ---- Quality report ----------------------------------------------------
  * How far the packed weights are from the fp32 weights they were made from:
@@ -378,6 +386,22 @@ w4a16_status w4a16_linear_awq(const void *x, int32_t dtype, const float *act_mul
 w4a16_status w4a16_linear_noalloc(const void *x, int32_t dtype, const void *qweight,
                                   const void *scales, const void *zeros, void *y, int64_t M,
                                   int64_t N, int64_t K, int32_t group, int32_t fmt, void *stream);
+
+/* Measurement helpers of the benchmark, not on the product path.
+ * w4a16_measure_stream_read: reads `bytes` (a multiple of 16) at `src` with
+ * 16-byte loads over `workgroups` workgroups of 256 threads (0: eight per
+ * compute unit), each thread striding the grid with four loads in flight; the
+ * achievable HBM read rate, a ceiling reported beside the kernels. `sink` is
+ * one device word that is written only if the data's fold equals a fixed
+ * constant.
+ * w4a16_measure_copy: dst = src, `bytes` (a multiple of 16, non-overlapping)
+ * with 16-byte loads and stores: a kernel of known traffic (bytes read and
+ * bytes written) that scales a profiler's HBM byte counters.
+ * Both enqueue on `stream`; W4A16_ERR_INVALID_ARG on a bad size, pointer or
+ * alignment. */
+w4a16_status w4a16_measure_stream_read(const void *src, size_t bytes, uint32_t *sink,
+                                       int32_t workgroups, void *stream);
+w4a16_status w4a16_measure_copy(const void *src, void *dst, size_t bytes, void *stream);
 
 /* Testing hook, for the tests of the kernel error path only: w4a16_gemm_fmt
  * on a shape whose plan splits tiles by stream-K (W4A16_ERR_INVALID_ARG

@@ -45,6 +45,7 @@ _SIGS = {
     "w4a16_layout_version": (ctypes.c_int, []),
     "w4a16_gemv_max_m": (_i32, []),
     "w4a16_linear_kernel": (_i32, [_i64, _i64, _i64, _i32, _i32]),
+    "w4a16_linear_launch_shape": (_i32, [_i64, _i64, _i64, _i32, _i32, _i32, _i64p, ctypes.POINTER(_i32)]),
     "w4a16_device_supported": (ctypes.c_int, [ctypes.c_int]),
     "w4a16_init": (ctypes.c_int, [ctypes.c_int]),
     "w4a16_packed_bytes": (ctypes.c_int, [_i64, _i64, _i32, _szp, _szp, _szp]),
@@ -72,6 +73,8 @@ _SIGS = {
     "w4a16_linear_awq": (ctypes.c_int, [_vp, _i32, _vp, _vp, _vp, _vp, _vp, _i64, _i64, _i64, _i32, _i32, _vp, _sz,
                                         _vp]),
     "w4a16_linear_noalloc": (ctypes.c_int, [_vp, _i32, _vp, _vp, _vp, _vp, _i64, _i64, _i64, _i32, _i32, _vp]),
+    "w4a16_measure_stream_read": (ctypes.c_int, [_vp, _sz, _vp, _i32, _vp]),
+    "w4a16_measure_copy": (ctypes.c_int, [_vp, _vp, _sz, _vp]),
     "w4a16_testing_gemm_expire": (ctypes.c_int, [_vp, _i32, _vp, _vp, _vp, _vp, _i64, _i64, _i64, _i32, _i32, _vp,
                                                  _sz, _vp]),
 }
@@ -151,6 +154,16 @@ def gemv_max_m() -> int:
 
 
 LINEAR_KERNELS = ("gemv", "small_batch", "tiled")
+
+
+def linear_launch_shape(M: int, N: int, K: int, group: int, dtype=torch.float16, fmt: str = "asym4"):
+    """(kernel name, workgroups, threads per workgroup) of w4a16_linear's launch."""
+    wg, th = ctypes.c_int64(), _i32()
+    code = int(_lib.w4a16_linear_launch_shape(M, N, K, group, W4A16_BF16 if dtype == torch.bfloat16 else W4A16_F16,
+                                              _fmt_code(fmt), ctypes.byref(wg), ctypes.byref(th)))
+    if code < 0:
+        raise ValueError("w4a16_linear rejects this shape")
+    return LINEAR_KERNELS[code], wg.value, th.value
 
 
 def linear_kernel(M: int, N: int, K: int, group: int, dtype=torch.float16) -> str:

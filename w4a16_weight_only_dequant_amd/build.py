@@ -11,7 +11,7 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 OUT = os.path.join(HERE, "libw4a16.so")
 BUILD_DIR = os.path.join(ROOT, "_build")
-SOURCES = ["api.hip", "pack.hip", "quality.hip",
+SOURCES = ["api.hip", "pack.hip", "quality.hip", "measure.hip",
            "decode.hip", "decode_sym4.hip", "decode_sym8.hip", "decode_kq4.hip",
            "gemm.hip", "gemm_sym4.hip", "gemm_sym8.hip", "gemm_kq4.hip",
            "prefill.hip", "prefill_sym4.hip", "prefill_sym8.hip", "prefill_kq4.hip"]

@@ -276,6 +276,37 @@ int32_t w4a16_linear_kernel(int64_t M, int64_t N, int64_t K, int32_t group, int3
     return gemm_plan(M, N, K, group).kind == 0 ? 1 : 2;
 }
 
+int32_t w4a16_linear_launch_shape(int64_t M, int64_t N, int64_t K, int32_t group, int32_t dtype, int32_t fmt,
+                                  int64_t *workgroups, int32_t *threads) {
+    if (M < 1 || M > (1LL << 24) || !shape_ok(N, K, group) || !fmt_group_ok(fmt, group) ||
+        (dtype != W4A16_F16 && dtype != W4A16_BF16))
+        return -1;
+    int64_t wg = 0;
+    int32_t th = 0;
+    int32_t kind;
+    if (prefer_gemv(M, N, K, group, dtype, fmt)) {
+        const DecodePlan p = decode_plan(M, N, K, group, fmt, false);
+        kind = 0;
+        wg = ceil_div(N, kRowBlock);
+        th = 64 * p.waves;
+    } else {
+        const GemmPlan p = gemm_plan(M, N, K, group);
+        if (p.kind == 0) {
+            kind = 1;
+            wg = ceil_div(ceil_div(N, kRowBlock), p.rows_per_wg) * ceil_div(M, 16);
+            th = 64 * p.waves;
+        } else {
+            kind = 2;
+            wg = p.sk_wgs > 0 ? (int64_t)p.dp_tiles + p.sk_wgs
+                              : ceil_div(M, tile_rows(p.tile)) * ceil_div(N, kTileCols);
+            th = p.tile == kTile256x256w8 ? 512 : 256;
+        }
+    }
+    if (workgroups) *workgroups = wg;
+    if (threads) *threads = th;
+    return kind;
+}
+
 w4a16_status w4a16_device_supported(int device) {
     if (device < 0) return W4A16_ERR_INVALID_ARG;
     if (device < kMaxDevices) {
