@@ -186,8 +186,10 @@ w4a16_status w4a16_packed_bytes_fmt(int64_t N, int64_t K, int32_t group, int32_t
                                     size_t *zeros_bytes);
 
 /* Workspace bytes a w4a16_gemv / w4a16_gemm / w4a16_linear call of this shape
- * needs on the current device. Host-only (queries the device's compute-unit
- * count once). The decode kernels need none. The tiled GEMM (M > 256) needs
+ * needs on the current device, in any weight format. Host-only (queries the
+ * device's compute-unit count once). The decode kernel (M <= 8) needs some
+ * when it splits K: an 8-byte counter per 16-row block (padded to 256 bytes)
+ * and M x 16 fp32 partials per row block and split. The tiled GEMM (M > 256) needs
  * some when its last round of 256 x 256 (or 128 / 64-row) output tiles would
  * be at most half full on the device's compute units: it then splits the
  * last two rounds' tiles by K over one workgroup per compute unit
@@ -203,6 +205,12 @@ w4a16_status w4a16_packed_bytes_fmt(int64_t N, int64_t K, int32_t group, int32_t
  * same time (other streams) must not share one. */
 w4a16_status w4a16_workspace_bytes(int64_t M, int64_t N, int64_t K, int32_t group,
                                    size_t *bytes);
+/* Workspace bytes of a w4a16_linear_group_fmt call (count problems of N[p]
+ * rows each, N a host array): the largest single-call need of any problem,
+ * or, when the call runs one decode launch, the counters of every problem's
+ * row blocks and the partials of those that split. Host-only. */
+w4a16_status w4a16_group_workspace_bytes(int32_t count, int64_t M, const int64_t *N, int64_t K,
+                                         int32_t group, int32_t fmt, size_t *bytes);
 
 /* Quantise and pack: w fp32 [N][K] -> qweight, scales, zeros (layout above).
  * Bit-exact with the quantiser defined above (IEEE fp32, no reciprocal). */
@@ -229,18 +237,18 @@ w4a16_status w4a16_unpack_fmt(const void *qweight, const void *scales, const voi
                               void *stream);
 
 /* Decode GEMV: y [M][N] = x [M][K] . w_hat^T for small M (M <= 8).
- * One pass over the packed weights: one workgroup per 16-row block holds all
- * of K (up to 16 waves of eight or sixteen 128-weight columns each),
+ * One pass over the packed weights: a workgroup per 16-row block and range of
+ * K's 128-weight columns (up to 16 waves of four, eight or sixteen columns),
  * 128-bit loads, in-register unpack, packed fp16 / bf16 dot products with
  * fp32 accumulation, the group scale and zero-point applied once per group;
- * the waves meet in LDS in a fixed order (deterministic). Range: the
- * activations and metadata it stages in LDS fit 160 KiB, which bounds K by
- *            M = 1    M = 2    M = 3..4   M = 5..8
- *   g 32     32768    22528    12288      6144
- *   g 64     32768    28672    15360      7168
- *   g 128+   32768    32768    16384      8192
- * Outside it, and for M > 8, W4A16_ERR_INVALID_ARG (w4a16_gemm and
- * w4a16_linear have no such limit). */
+ * the waves meet in LDS in a fixed order. Split K: when the matrix has few
+ * row blocks for the device's compute units (or K is long), S workgroups
+ * share a row block's K and leave fp32 partials in the workspace
+ * (w4a16_workspace_bytes); the last of them adds the S partials in a fixed
+ * order, so results are deterministic and independent of timing. Range:
+ * M <= 8 and K <= 65536; W4A16_ERR_INVALID_ARG outside it (w4a16_gemm and
+ * w4a16_linear have no such limit), W4A16_ERR_WORKSPACE when the workspace is
+ * smaller than w4a16_workspace_bytes. */
 w4a16_status w4a16_gemv(const void *x, int32_t dtype, const void *qweight,
                         const void *scales, const void *zeros, void *y,
                         int64_t M, int64_t N, int64_t K, int32_t group,
@@ -287,12 +295,14 @@ w4a16_status w4a16_linear_fmt(const void *x, int32_t dtype, const void *qweight,
  * host arrays of `count` entries (device pointers / sizes); x[p] may be the
  * same pointer for several p (q/k/v or gate/up of one token batch). Every
  * problem must pass w4a16_linear's checks, and no y[p] may overlap any buffer
- * of any problem. For M <= 256 all problems run in one launch of the
- * small-batch matrix-core kernel, which pays the fixed cost of a launch (the
- * ramp-up and drain that dominate small decode layers) once; for larger M it
- * enqueues one tiled GEMM per problem, one after the other, each using the
- * workspace (which must hold the largest w4a16_workspace_bytes of the
- * problems). Results are bit-identical to w4a16_gemm on each problem. This fuses the launches, not the math: the
+ * of any problem. The workspace is sized by w4a16_group_workspace_bytes. At
+ * M <= w4a16_gemv_max_m all problems run in one launch of the decode kernel,
+ * each with the split a call on it alone would use; for M up to 256 in one
+ * launch of the small-batch matrix-core kernel; either pays the fixed cost of
+ * a launch (the ramp-up and drain that dominate small decode layers) once.
+ * For larger M it enqueues one tiled GEMM per problem, one after the other,
+ * each using the workspace. Results are bit-identical to w4a16_linear on each
+ * problem. This fuses the launches, not the math: the
  * pages' dual-output decode variant ("Quantization Is Not a Zip File", section
  * 2, paired gate/up projections) is the special case of two problems sharing x. */
 w4a16_status w4a16_linear_group(int32_t count, const void *const *x, int32_t dtype,
@@ -389,11 +399,11 @@ w4a16_status w4a16_linear_noalloc(const void *x, int32_t dtype, const void *qwei
 
 /* Measurement helpers of the benchmark, not on the product path.
  * w4a16_measure_stream_read: reads `bytes` (a multiple of 16) at `src` with
- * 16-byte loads over `workgroups` workgroups of 256 threads (0: eight per
- * compute unit), each thread striding the grid with four loads in flight; the
- * achievable HBM read rate, a ceiling reported beside the kernels. `sink` is
- * one device word that is written only if the data's fold equals a fixed
- * constant.
+ * 16-byte loads, workgroups of 256 threads each reading one contiguous share
+ * with four loads per thread in flight: `workgroups` equal shares, or (0) as
+ * many workgroups as 16 KiB shares; the achievable HBM read rate, a ceiling
+ * reported beside the kernels. `sink` is one device word that is written only
+ * if the data's fold equals a fixed constant.
  * w4a16_measure_copy: dst = src, `bytes` (a multiple of 16, non-overlapping)
  * with 16-byte loads and stores: a kernel of known traffic (bytes read and
  * bytes written) that scales a profiler's HBM byte counters.

@@ -129,7 +129,7 @@ def test_format_grouped_launch_matches_single(fmt, M):
     ys = H.lib().linear_group([xd, xd], pws)
     torch.cuda.synchronize()
     for y, pw, o in zip(ys, pws, os_):
-        single = H.lib().gemm(xd, pw)
+        single = H.lib().linear(xd, pw)
         torch.cuda.synchronize()
         assert torch.equal(y.view(torch.int16), single.view(torch.int16))
         H.check_against_oracle(y, x, "bf16", o, group)
@@ -268,7 +268,7 @@ def test_kq4_grouped_launch_matches_single(M):
     ys = H.lib().linear_group([xd, xd], pws)
     torch.cuda.synchronize()
     for y, pw, o in zip(ys, pws, os_):
-        single = H.lib().gemm(xd, pw)
+        single = H.lib().linear(xd, pw)
         torch.cuda.synchronize()
         assert torch.equal(y.view(torch.int16), single.view(torch.int16))
         H.check_against_oracle(y, x, "f16", o, 256)

@@ -17,35 +17,15 @@ def _run(fn, x_bits, dtype, pw):
     return y
 
 
-def _dec_lds_per_wave(mt, ncol, group):
-    """LDS bytes of one decode wave (4-bit zero-point format): activations,
-    activation sums, the 16 rows' scales and zero-point words, 16 spare bytes."""
-    upc = 1 if group >= 128 else 128 // group
-    meta_row = ncol if group >= 256 else ncol * (128 // group) * 2
-    zwords = (ncol // 2 + 7) // 8 if group >= 256 else (ncol * (128 // group) + 7) // 8
-    return mt * ncol * 256 + mt * ncol * upc * 32 + 16 * meta_row + 16 * zwords * 4 + 16
-
-
 def gemv_accepts(M, K, dtype, group=32):
-    """The decode kernel's range: M <= 8 and all of K in one workgroup of at
-    most 16 waves (8 columns of 128 weights per wave, or 16 for one or two
-    activation rows), its LDS within gfx950's 160 KiB per workgroup."""
-    if not 1 <= M <= 8:
-        return False
-    T = -(-(K // 32) // 4)
-    mt = 1 if M <= 1 else 2 if M <= 2 else 4 if M <= 4 else 8
-    if -(-T // 8) <= 16:
-        ncol = 8
-    elif mt <= 2 and -(-T // 16) <= 16:
-        ncol = 16
-    else:
-        return False
-    return -(-T // ncol) * _dec_lds_per_wave(mt, ncol, group) <= 160 * 1024
+    """The decode kernel's range: M <= 8 and K <= 65536 (it splits K over
+    workgroups until a workgroup's LDS fits)."""
+    return 1 <= M <= 8 and K <= 65536
 
 
 SMALL = [(8, 32, 32), (72, 64, 32), (200, 96, 32), (136, 256, 64), (64, 384, 128), (328, 640, 128),
          (1000, 1024, 64), (4104, 4096, 128), (520, 8192, 32), (40, 160, 32), (24, 1120, 32),
-         (48, 16384, 128), (24, 32768, 64)]
+         (48, 16384, 128), (24, 32768, 64), (16, 65536, 128), (40, 5152, 32), (8, 131072, 128)]
 
 
 @pytest.mark.parametrize("N,K,group", SMALL)
@@ -139,3 +119,76 @@ def test_workspace_reused_across_shapes():
             y = H.lib().gemv(H.to_device_bits(x, "f16"), pw, workspace=ws)
             torch.cuda.synchronize()
             H.check_against_oracle(y, x, "f16", o, group)
+
+
+# (M, N, K, group) whose decode plan splits K over several workgroups per row
+# block (a workgroup's activations and metadata for all of K would pass the
+# LDS), ragged K and a short last row block included
+SPLIT = [(1, 136, 65536, 128), (2, 1032, 28672, 32), (3, 520, 32768, 32), (5, 24, 13824, 64),
+         (8, 40, 16416, 32)]
+
+
+@pytest.mark.parametrize("M,N,K,group", SPLIT)
+@pytest.mark.parametrize("dtype", ["f16", "bf16"])
+def test_split_k_decode_is_deterministic_across_workspaces_and_replays(M, N, K, group, dtype):
+    """Split-K decode: the same bits from a fresh workspace, from one whose
+    counters and partials hold junk (random bytes, then small integers), and
+    from every replay of a captured graph; every output within the bar."""
+    import torch
+    w4 = H.lib()
+    assert w4.workspace_bytes(M, N, K, group) > 0   # the plan splits K
+    w, o, pw = H.prepared(("split", N, K, group), lambda: wl.random_weights(N * 7 + K, N, K), group)
+    for _ in (0,):
+        xb = wl.random_activations(N + 5 * M, M, K, dtype)
+        x = H.to_device_bits(xb, dtype)
+        y0 = w4.gemv(x, pw, workspace=w4.Workspace("cuda"))
+        torch.cuda.synchronize()
+        H.check_against_oracle(y0, xb, dtype, o, group)
+        nbytes = w4.workspace_bytes(M, N, K, group)
+        for fill in ("random", "ints"):
+            ws = w4.Workspace("cuda")
+            buf = ws.get(nbytes)
+            if fill == "random":
+                buf.copy_(torch.randint(0, 256, buf.shape, dtype=torch.uint8, device="cuda"))
+            else:
+                words = buf[: buf.numel() // 8 * 8].view(torch.int64)
+                words.copy_(torch.arange(words.numel(), dtype=torch.int64, device="cuda") % 7)
+            for _ in range(2):
+                y = w4.gemv(x, pw, workspace=ws)
+                torch.cuda.synchronize()
+                assert torch.equal(y.view(torch.int16), y0.view(torch.int16)), fill
+        ws = w4.Workspace("cuda")
+        out = torch.empty_like(y0)
+        stream = torch.cuda.Stream()
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.stream(stream):
+            w4.gemv(x, pw, out=out, workspace=ws, stream=stream)
+            torch.cuda.synchronize()
+            with torch.cuda.graph(graph, stream=stream):
+                w4.gemv(x, pw, out=out, workspace=ws, stream=stream)
+        for i in range(3):
+            out.zero_()
+            filler = torch.randn(1 << 18, device="cuda").sum()
+            graph.replay()
+            torch.cuda.synchronize()
+            assert torch.equal(out.view(torch.int16), y0.view(torch.int16)), f"replay {i}"
+            assert bool(torch.isfinite(filler))
+    H.drop(("split", N, K, group))
+
+
+def test_split_k_decode_short_workspace_refused():
+    import torch
+    w4 = H.lib()
+    N, K, group = 136, 65536, 128
+    w, o, pw = H.prepared(("split", N, K, group), lambda: wl.random_weights(N * 7 + K, N, K), group)
+    x = H.to_device_bits(wl.random_activations(2, 1, K, "f16"), "f16")
+    nbytes = w4.workspace_bytes(1, N, K, group)
+    assert nbytes > 0
+    buf = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+    y = torch.full((1, N), 2.0, dtype=torch.float16, device="cuda")
+    args = (x.data_ptr(), 0, pw.qweight.data_ptr(), pw.scales.data_ptr(), pw.zeros_ptr(), y.data_ptr(), 1, N, K, group)
+    for fn in ("w4a16_gemv", "w4a16_linear"):
+        assert getattr(w4.raw(), fn)(*args, buf.data_ptr(), nbytes - 1, None) == 4, fn   # W4A16_ERR_WORKSPACE
+        assert getattr(w4.raw(), fn)(*args, None, 0, None) == 4, fn
+    torch.cuda.synchronize()
+    assert bool((y == 2.0).all())

@@ -1,6 +1,6 @@
 """GPU parity of the grouped call (w4a16_linear_group): several layers of one
 M, K, group and type in one launch give, for every problem, the bits of
-w4a16_gemm on that problem alone, and stay within the oracle's bar."""
+w4a16_linear on that problem alone, and stay within the oracle's bar."""
 import numpy as np
 import pytest
 
@@ -32,7 +32,7 @@ def test_group_matches_single_calls(dtype, M, shared_x):
     ys = H.lib().linear_group(xs, [pw for _, _, pw in probs])
     torch.cuda.synchronize()
     for p, (w, o, pw) in enumerate(probs):
-        single = H.lib().gemm(xs[p], pw)
+        single = H.lib().linear(xs[p], pw)
         torch.cuda.synchronize()
         assert ys[p].shape == (M, NS[p])
         assert torch.equal(ys[p].view(torch.int16), single.view(torch.int16)), p
@@ -65,7 +65,7 @@ def test_group_decode_layer_set_full_size():
         ys = H.lib().linear_group(xs, [pw for _, _, pw in probs])
         torch.cuda.synchronize()
         for p, (w, o, pw) in enumerate(probs):
-            single = H.lib().gemm(xs[p], pw)
+            single = H.lib().linear(xs[p], pw)
             torch.cuda.synchronize()
             assert torch.equal(ys[p].view(torch.int16), single.view(torch.int16))
             H.check_against_oracle(ys[p], xbits[p], wlc.dtype, o, wlc.group)

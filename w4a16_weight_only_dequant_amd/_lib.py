@@ -50,6 +50,7 @@ _SIGS = {
     "w4a16_init": (ctypes.c_int, [ctypes.c_int]),
     "w4a16_packed_bytes": (ctypes.c_int, [_i64, _i64, _i32, _szp, _szp, _szp]),
     "w4a16_workspace_bytes": (ctypes.c_int, [_i64, _i64, _i64, _i32, _szp]),
+    "w4a16_group_workspace_bytes": (ctypes.c_int, [_i32, _i64, _i64p, _i64, _i32, _i32, _szp]),
     "w4a16_pack": (ctypes.c_int, [_vp, _i64, _i64, _i32, _vp, _vp, _vp, _vp]),
     "w4a16_unpack": (ctypes.c_int, [_vp, _vp, _vp, _i64, _i64, _i32, _vp, _vp, _vp, _vp]),
     "w4a16_gemv": (ctypes.c_int, [_vp, _i32, _vp, _vp, _vp, _vp, _i64, _i64, _i64, _i32, _vp, _sz, _vp]),
@@ -342,7 +343,11 @@ def linear_group(xs, pws, outs=None, workspace=None, stream=None):
         raise ValueError("need one output per packed weight")
     ys = [_output(outs[i] if outs is not None else None, M, pw.N, xs[0]) for i, pw in enumerate(pws)]
     arr = lambda vals: (ctypes.c_void_p * count)(*vals)  # noqa: E731
-    nbytes = max(workspace_bytes(M, pw.N, K, group) for pw in pws)
+    nb = _sz()
+    ns = (ctypes.c_int64 * count)(*[pw.N for pw in pws])
+    _check("w4a16_group_workspace_bytes", _lib.w4a16_group_workspace_bytes(count, M, ns, K, group,
+                                                                           _fmt_code(pws[0].fmt), ctypes.byref(nb)))
+    nbytes = nb.value
     strm = stream if stream is not None else torch.cuda.current_stream(xs[0].device)
     ws = (workspace or _default_workspace(xs[0].device, strm)).get(nbytes, strm)
     zeros = arr([p.zeros_ptr() for p in pws]) if pws[0].zeros is not None else None

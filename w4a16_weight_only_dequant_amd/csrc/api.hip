@@ -2,6 +2,7 @@
 // device check and dispatch on M. Declarations and contracts: include/w4a16.h.
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <atomic>
 #include <cstdlib>
 #include <cstring>
@@ -216,12 +217,38 @@ size_t max_lds_per_block() {
     return (size_t)v;
 }
 
-// The decode kernel takes M <= 8 and K up to 32768 (16384 from M = 3 on, or
-// with AWQ scaling), within one workgroup's LDS.
+// The decode kernel takes M <= 8 and K <= 65536 (its plan splits K until a
+// workgroup's LDS fits).
 bool decode_fits(int64_t M, int64_t N, int64_t K, int32_t group, int32_t fmt, bool awq) {
     if (M < 1 || M > kDecodeMaxM) return false;
     const DecodePlan p = decode_plan(M, N, K, group, fmt, awq);
     return p.ok && p.lds <= max_lds_per_block();
+}
+
+// Workspace of a decode launch over N rows (the split's counters and
+// partials; 0 without a split or outside the kernel's range).
+size_t decode_need(int64_t M, int64_t N, int64_t K, int32_t group, int32_t fmt, bool awq) {
+    if (M < 1 || M > kDecodeMaxM) return 0;
+    const DecodePlan p = decode_plan(M, N, K, group, fmt, awq);
+    return p.ok ? decode_workspace_bytes(p, M, N) : 0;
+}
+// A grouped decode launch: every problem keeps its own plan (0 when a plan
+// does not fit).
+size_t group_decode_need(int count, int64_t M, const int64_t *N, int64_t K, int32_t group, int32_t fmt) {
+    DecodePlan plans[kMaxGroup];
+    int n[kMaxGroup];
+    for (int p = 0; p < count; ++p) {
+        plans[p] = decode_plan(M, N[p], K, group, fmt, false);
+        n[p] = (int)N[p];
+    }
+    return decode_group_workspace_bytes(plans, count, M, n);
+}
+// The same for any weight format (w4a16_workspace_bytes takes none).
+size_t decode_need_any(int64_t M, int64_t N, int64_t K, int32_t group) {
+    size_t need = 0;
+    for (int32_t fmt : {W4A16_FMT_ASYM4, W4A16_FMT_SYM4, W4A16_FMT_SYM8, W4A16_FMT_KQ4})
+        if (fmt_group_ok(fmt, group)) need = std::max(need, decode_need(M, N, K, group, fmt, false));
+    return need;
 }
 
 // w4a16_linear's choice: the decode kernel at M <= gemv_max_m() (M = 1;
@@ -287,7 +314,7 @@ int32_t w4a16_linear_launch_shape(int64_t M, int64_t N, int64_t K, int32_t group
     if (prefer_gemv(M, N, K, group, dtype, fmt)) {
         const DecodePlan p = decode_plan(M, N, K, group, fmt, false);
         kind = 0;
-        wg = ceil_div(N, kRowBlock);
+        wg = ceil_div(N, kRowBlock) * p.splits;
         th = 64 * p.waves;
     } else {
         const GemmPlan p = gemm_plan(M, N, K, group);
@@ -339,7 +366,21 @@ w4a16_status w4a16_packed_bytes_fmt(int64_t N, int64_t K, int32_t group, int32_t
 
 w4a16_status w4a16_workspace_bytes(int64_t M, int64_t N, int64_t K, int32_t group, size_t *bytes) {
     if (!bytes || M < 0 || M > (1LL << 24) || !shape_ok(N, K, group)) return W4A16_ERR_INVALID_ARG;
-    *bytes = M == 0 ? 0 : gemm_need(M, N, K, group);
+    *bytes = M == 0 ? 0 : std::max(gemm_need(M, N, K, group), decode_need_any(M, N, K, group));
+    return W4A16_OK;
+}
+
+w4a16_status w4a16_group_workspace_bytes(int32_t count, int64_t M, const int64_t *N, int64_t K, int32_t group,
+                                         int32_t fmt, size_t *bytes) {
+    if (!bytes || !N || count < 1 || count > kMaxGroup || M < 0 || M > (1LL << 24) || !fmt_group_ok(fmt, group))
+        return W4A16_ERR_INVALID_ARG;
+    size_t need = 0;
+    for (int p = 0; p < count; ++p) {
+        if (!shape_ok(N[p], K, group)) return W4A16_ERR_INVALID_ARG;
+        if (M > 0) need = std::max(need, std::max(gemm_need(M, N[p], K, group), decode_need(M, N[p], K, group, fmt, false)));
+    }
+    if (M > 0 && M <= kDecodeMaxM) need = std::max(need, group_decode_need(count, M, N, K, group, fmt));
+    *bytes = need;
     return W4A16_OK;
 }
 
@@ -390,17 +431,18 @@ w4a16_status w4a16_unpack_fmt(const void *qweight, const void *scales, const voi
 w4a16_status w4a16_gemv_fmt(const void *x, int32_t dtype, const void *qweight, const void *scales,
                             const void *zeros, void *y, int64_t M, int64_t N, int64_t K, int32_t group, int32_t fmt,
                             void *workspace, size_t workspace_bytes, void *stream) {
-    (void)workspace;
-    (void)workspace_bytes;
     if (M > kDecodeMaxM) return W4A16_ERR_INVALID_ARG;
-    w4a16_status st = check_linear(x, dtype, qweight, scales, zeros, y, M, N, K, group, fmt, nullptr, 0, 0);
+    const size_t need = (M >= 1 && shape_ok(N, K, group) && fmt_group_ok(fmt, group))
+                            ? decode_need(M, N, K, group, fmt, false) : 0;
+    w4a16_status st = check_linear(x, dtype, qweight, scales, zeros, y, M, N, K, group, fmt, workspace,
+                                   workspace_bytes, need);
     if (st != W4A16_OK || M == 0) return st;
     st = check_device();
     if (st != W4A16_OK) return st;
     if (!decode_fits(M, N, K, group, fmt, false)) return W4A16_ERR_INVALID_ARG;
     const DecodePlan plan = decode_plan(M, N, K, group, fmt, false);
     hipError_t e = launch_decode(x, dtype == W4A16_BF16, qweight, scales, zeros, y, (int)M, (int)N, (int)K, group,
-                                 fmt, nullptr, plan, reinterpret_cast<hipStream_t>(stream));
+                                 fmt, nullptr, plan, workspace, reinterpret_cast<hipStream_t>(stream));
     return e == hipSuccess ? W4A16_OK : W4A16_ERR_HIP;
 }
 
@@ -471,10 +513,18 @@ w4a16_status w4a16_linear_group_fmt(int32_t count, const void *const *x, int32_t
     auto zero_ptr = [&](int p) -> const void * { return zp ? zeros[p] : nullptr; };
     int64_t n_total = 0;
     for (int p = 0; p < count; ++p) {
-        const w4a16_status st = check_linear(x[p], dtype, qweight[p], scales[p], zero_ptr(p), y[p], M, N[p], K,
-                                             group, fmt, workspace, workspace_bytes, 0);
-        if (st != W4A16_OK) return st;
+        if (!shape_ok(N[p], K, group)) return W4A16_ERR_INVALID_ARG;
         n_total += N[p];
+    }
+    // small batches: one decode launch over every problem's row blocks, each
+    // problem with the plan of a call on it alone (the same bits)
+    bool decode = true;
+    for (int p = 0; p < count; ++p) decode = decode && prefer_gemv(M, N[p], K, group, dtype, fmt);
+    const size_t dec_need = decode ? group_decode_need(count, M, N, K, group, fmt) : 0;
+    for (int p = 0; p < count; ++p) {
+        const w4a16_status st = check_linear(x[p], dtype, qweight[p], scales[p], zero_ptr(p), y[p], M, N[p], K,
+                                             group, fmt, workspace, workspace_bytes, dec_need);
+        if (st != W4A16_OK) return st;
     }
     // no output may overlap any other problem's buffers either
     for (int p = 0; p < count; ++p) {
@@ -491,15 +541,6 @@ w4a16_status w4a16_linear_group_fmt(int32_t count, const void *const *x, int32_t
     }
     w4a16_status st = check_device();
     if (st != W4A16_OK) return st;
-    const GemmPlan plan = gemm_plan(M, n_total, K, group);
-    if (plan.kind != 0) {   // large M: one tiled launch per problem
-        for (int p = 0; p < count; ++p) {
-            st = w4a16_gemm_fmt(x[p], dtype, qweight[p], scales[p], zero_ptr(p), y[p], M, N[p], K, group, fmt,
-                                workspace, workspace_bytes, stream);
-            if (st != W4A16_OK) return st;
-        }
-        return W4A16_OK;
-    }
     GroupTable tab{};
     tab.count = count;
     for (int p = 0; p < count; ++p) {
@@ -509,6 +550,36 @@ w4a16_status w4a16_linear_group_fmt(int32_t count, const void *const *x, int32_t
         tab.zeros[p] = zero_ptr(p);
         tab.y[p] = y[p];
         tab.N[p] = (int)N[p];
+    }
+    if (decode) {
+        DecodePlan plans[kMaxGroup];
+        bool same = true;
+        for (int p = 0; p < count; ++p) {
+            plans[p] = decode_plan(M, N[p], K, group, fmt, false);
+            same = same && plans[p].mt == plans[0].mt && plans[p].ncol == plans[0].ncol;
+        }
+        size_t lds = 0;
+        for (int p = 0; p < count; ++p) lds = std::max(lds, plans[p].lds);
+        if (same && lds <= max_lds_per_block()) {
+            hipError_t e = launch_decode_group(tab, dtype == W4A16_BF16, (int)M, (int)K, group, fmt, plans,
+                                               workspace, reinterpret_cast<hipStream_t>(stream));
+            return e == hipSuccess ? W4A16_OK : W4A16_ERR_HIP;
+        }
+        for (int p = 0; p < count; ++p) {   // plans of different shapes: one launch each
+            st = w4a16_gemv_fmt(x[p], dtype, qweight[p], scales[p], zero_ptr(p), y[p], M, N[p], K, group, fmt,
+                                workspace, workspace_bytes, stream);
+            if (st != W4A16_OK) return st;
+        }
+        return W4A16_OK;
+    }
+    const GemmPlan plan = gemm_plan(M, n_total, K, group);
+    if (plan.kind != 0) {   // large M: one tiled launch per problem
+        for (int p = 0; p < count; ++p) {
+            st = w4a16_gemm_fmt(x[p], dtype, qweight[p], scales[p], zero_ptr(p), y[p], M, N[p], K, group, fmt,
+                                workspace, workspace_bytes, stream);
+            if (st != W4A16_OK) return st;
+        }
+        return W4A16_OK;
     }
     hipError_t e = launch_gemm_group(tab, dtype == W4A16_BF16, (int)M, (int)K, group, fmt, plan,
                                      reinterpret_cast<hipStream_t>(stream));
@@ -524,8 +595,9 @@ w4a16_status w4a16_linear_noalloc(const void *x, int32_t dtype, const void *qwei
     if (dev < 0 || dev >= kMaxDevices || !g_ready[dev].load(std::memory_order_acquire))
         return W4A16_ERR_INVALID_ARG;
     size_t need = 0;
-    if (M >= 1 && M <= (1LL << 24) && shape_ok(N, K, group) && !prefer_gemv(M, N, K, group, dtype, fmt))
-        need = gemm_need(M, N, K, group);
+    if (M >= 1 && M <= (1LL << 24) && shape_ok(N, K, group) && fmt_group_ok(fmt, group))
+        need = prefer_gemv(M, N, K, group, dtype, fmt) ? decode_need(M, N, K, group, fmt, false)
+                                                       : gemm_need(M, N, K, group);
     if (need > kScratchBytes) return W4A16_ERR_WORKSPACE;
     void *ws = need > 0 ? g_scratch[dev].load(std::memory_order_acquire) : nullptr;
     return w4a16_linear_fmt(x, dtype, qweight, scales, zeros, y, M, N, K, group, fmt, ws,
@@ -611,8 +683,9 @@ w4a16_status w4a16_awq_workspace_bytes(int64_t M, int64_t N, int64_t K, int32_t 
         (dtype != W4A16_F16 && dtype != W4A16_BF16))
         return W4A16_ERR_INVALID_ARG;
     (void)dtype;
-    *bytes = (M == 0 || decode_fits(M, N, K, group, fmt, true))
-                 ? 0 : align_up((size_t)(M * K * 2), 256) + gemm_need(M, N, K, group);
+    *bytes = M == 0 ? 0
+             : decode_fits(M, N, K, group, fmt, true) ? decode_need(M, N, K, group, fmt, true)
+                                                      : align_up((size_t)(M * K * 2), 256) + gemm_need(M, N, K, group);
     return W4A16_OK;
 }
 
@@ -626,7 +699,7 @@ w4a16_status w4a16_linear_awq(const void *x, int32_t dtype, const float *act_mul
     const bool fused = decode_fits(M, N, K, group, fmt, true);
     // not fused: the scaled activations, then the product's own workspace
     const size_t xbytes = align_up((size_t)(M * K * 2), 256);
-    const size_t need = fused ? 0 : xbytes + gemm_need(M, N, K, group);
+    const size_t need = fused ? decode_need(M, N, K, group, fmt, true) : xbytes + gemm_need(M, N, K, group);
     if (need > 0) {
         if (!workspace || workspace_bytes < need) return W4A16_ERR_WORKSPACE;
         if (!aligned16(workspace)) return W4A16_ERR_INVALID_ARG;
@@ -644,7 +717,7 @@ w4a16_status w4a16_linear_awq(const void *x, int32_t dtype, const float *act_mul
     if (fused) {   // one launch: the decode kernel scales the activations as it loads them
         const DecodePlan plan = decode_plan(M, N, K, group, fmt, true);
         hipError_t e = launch_decode(x, dtype == W4A16_BF16, qweight, scales, zeros, y, (int)M, (int)N, (int)K,
-                                     group, fmt, act_mul, plan, s);
+                                     group, fmt, act_mul, plan, workspace, s);
         return e == hipSuccess ? W4A16_OK : W4A16_ERR_HIP;
     }
     hipError_t e = launch_scale_activations(x, dtype == W4A16_BF16, act_mul, workspace, M, (int)K, s);

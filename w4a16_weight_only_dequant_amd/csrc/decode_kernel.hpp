@@ -38,13 +38,22 @@
 //   layer one v_mfma_f32_16x16x32 per dword of codes measured about twice the
 //   time of the dot products.
 //
-// Mapping: a workgroup owns one block of 16 output rows and all of K; its
-// waves take consecutive slices of NCOL 128-weight columns. Lane l = 16 s + r
-// loads, per column, dword s of the column's four chunks of row r (one
-// contiguous KiB per wave) and accumulates row r over the k-slices 8s..8s+7
-// of the column's chunks; the four lanes of a row meet by cross-lane moves at
-// the end, the waves through LDS, always in the same order, so results are
-// deterministic and no partial sum leaves the workgroup.
+// Mapping: a workgroup owns one block of 16 output rows and one of S equal
+// ranges of K's columns (S = 1: all of K); its waves take consecutive slices
+// of NCOL 128-weight columns. Lane l = 16 s + r loads, per column, dword s of
+// the column's four chunks of row r (one contiguous KiB per wave) and
+// accumulates row r over the k-slices 8s..8s+7 of the column's chunks; the
+// four lanes of a row meet by cross-lane moves at the end, the waves through
+// LDS, always in the same order.
+// * Split K. A launch needs several workgroups per compute unit to keep the
+//   weight stream going (a row block is 16 rows, so N = 5120 gives only 320
+//   of them for 256 compute units). With S > 1 the S workgroups of a row
+//   block each leave an fp32 partial [M][16] in the workspace and count their
+//   arrival on the block's counter; the last to arrive adds the S partials in
+//   split order (the result does not depend on which one is last) and writes
+//   y. The counter holds the launch's token in its upper 56 bits, so it needs
+//   no initialisation, and the last arrival clears it, so a replayed graph
+//   (same token) counts again from zero.
 //
 // Weight formats (FMT) change the operands and the per-group terms: a fixed
 // zero (symmetric 4-bit), a second code plane (8-bit codes, operands
@@ -52,12 +61,23 @@
 // super-block: S * sum x q - M * sum x.
 #pragma once
 
+#include <algorithm>
+
 #include "decode_common.hpp"
 
 namespace w4a16 {
 namespace {
 
 constexpr int kDecMaxWaves = 16;
+
+// Split of K over the workgroups of a row block (see the mapping above).
+struct DecSplit {
+    int splits;                  // workgroups per row block
+    int cols;                    // columns of K per workgroup (the last range may be shorter)
+    float *part;                 // [blocks][splits][M][16] fp32 partials (splits > 1)
+    unsigned long long *cnt;     // [blocks] arrival counters (splits > 1)
+    unsigned long long token;    // this launch's token in bits 8..63, bits 0..7 zero
+};
 
 template <bool BF>
 __device__ inline float dec_dot2(uint32_t w, uint32_t x, float acc) {
@@ -102,17 +122,21 @@ __host__ __device__ constexpr DecLds dec_lds(int mt, int ncol, int group, int fm
 
 // GROUP: 32, 64, 128 or 256 (K-quant super-blocks: 256, closed per 32-weight
 // chunk). MT: activation rows held (1, 2, 4 or 8; rows m >= M repeat row
-// M - 1 and are never stored). NCOL: columns per wave (8 or 16; 16 for group
-// 256). AWQ: act_mul holds fp32 multipliers [K] applied to the activations as
+// M - 1 and are never stored). NCOL: columns per wave (4, 8 or 16); a
+// workgroup's range of columns (sp.cols) is a multiple of NCOL, so every slice
+// starts at a multiple of NCOL columns and its metadata run at a whole
+// 16-byte part (or, runs of 4 or 8 bytes, at their own alignment). AWQ: act_mul holds fp32 multipliers [K] applied to the activations as
 // they are loaded (AWQ's run-time scaling: x' = rne16(x * m)).
 // Metadata (layout 3): scales [N][G8] fp16 and zero-points [N][G8 / 8] words
 // of eight 4-bit values (group g in bits 4 (g % 8)), G8 = K / group rounded up
 // to a multiple of 8; super-block records [N][K / 256] of 16 bytes.
+// b: the row block, h: the range of K (split), blk: the block's index in the
+// launch's partials and counters.
 template <int GROUP, int MT, bool BF, int FMT, int NCOL, bool AWQ>
-__global__ __launch_bounds__(64 * kDecMaxWaves) void decode_kernel(
+__device__ __forceinline__ void decode_body(
     const uint16_t *__restrict__ x, const uint4 *__restrict__ qw, const uint4 *__restrict__ qw_hi,
     const uint16_t *__restrict__ scales, const uint32_t *__restrict__ zeros, uint16_t *__restrict__ y, int M,
-    int N, int K, const float *__restrict__ act_mul) {
+    int N, int K, const float *__restrict__ act_mul, int b, int h, int blk, const DecSplit &sp) {
     using FT = FormatTraits<FMT>;
     constexpr int GC = GROUP > kColumn ? kColumn : GROUP;   // closing granularity along K (<= a column)
     constexpr int CPG = GC / kChunk;                       // chunks per group (1, 2, 4)
@@ -129,8 +153,8 @@ __global__ __launch_bounds__(64 * kDecMaxWaves) void decode_kernel(
     constexpr int XQ = NCOL / 4;                           // 16-byte activation loads per lane and row
     // small metadata runs (groups 128 and 256) stay in each lane's registers
     constexpr bool MREG = !FT::kquant && MRB <= 32 && ZW <= 2;
-    static_assert(NCOL % 4 == 0 && (MRB % 16 == 0 || (MREG && MRB == 8)),
-                  "a slice covers whole 16-byte metadata parts (or one 8-byte run kept in registers)");
+    static_assert(NCOL % 4 == 0 && (MRB % 16 == 0 || (MREG && MRB <= 8)),
+                  "a slice covers whole 16-byte metadata parts (or a run of at most 8 bytes kept in registers)");
     extern __shared__ __align__(16) unsigned char smem[];
     __shared__ float red[kDecMaxWaves][MT][kRowBlock];
 
@@ -138,17 +162,21 @@ __global__ __launch_bounds__(64 * kDecMaxWaves) void decode_kernel(
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int r = lane & 15;
     const int s = lane >> 4;
-    const int b = blockIdx.x;
     const int rows_b = min(kRowBlock, N - b * kRowBlock);
     const int rl = r < rows_b ? r : r - rows_b;   // lanes past a short last block re-read a valid row
     const int C = K >> 5;                          // chunks along K
     const int T = (C + 3) >> 2;                    // columns (the last may be partial)
-    const int t0 = wave * NCOL;                    // this wave's columns [t0, t0 + NCOL)
-    const int nfull = min(max((C >> 2) - t0, 0), NCOL);
-    const int c_lo = t0 * kColChunks;
-    const int nchunks = max(min((t0 + NCOL) * kColChunks, C) - c_lo, 0);
+    const int t0 = h * sp.cols + wave * NCOL;      // this wave's columns [t0, min(t0 + NCOL, tend))
+    const int tend = min(h * sp.cols + sp.cols, T);
+    // a wave past its range's end (the last range may be shorter) reads valid
+    // memory at the last slice start before T (a multiple of NCOL, as every
+    // slice start is, so its metadata reads stay aligned) and adds nothing
+    const int tb = min(t0, ((T - 1) / NCOL) * NCOL);
+    const int nfull = min(max(min(C >> 2, tend) - t0, 0), NCOL);
+    const int c_lo = tb * kColChunks;
+    const int nchunks = max(min(min(t0 + NCOL, tend) * kColChunks, C) - t0 * kColChunks, 0);
     const int G8 = ((K / GROUP) + 7) & ~7;         // metadata slots per row (scales)
-    const int gs0 = (int)((int64_t)t0 * kColumn / GROUP);   // first group of the slice (K-quant: record)
+    const int gs0 = (int)((int64_t)tb * kColumn / GROUP);   // first group of the slice (K-quant: record)
 
     unsigned char *wl = smem + wave * L.total;
     unsigned char *xl = wl + L.x;                          // [MT][NCOL * 256]
@@ -198,9 +226,11 @@ __global__ __launch_bounds__(64 * kDecMaxWaves) void decode_kernel(
         const int part0 = FT::kquant ? gs0 : gs0 / 8;   // the slice's first part in the row
         const uint32_t *zb = zeros + (size_t)mrow * (G8 / 8);
         if constexpr (MREG) {
-            if constexpr (MRB == 8) {   // an 8-byte run (8-byte aligned)
-                const uint2 v = *reinterpret_cast<const uint2 *>(base + (size_t)min(gs0, G8 - 4) * 2);
+            if constexpr (MRB == 8) {   // an 8-byte run (gs0 is a multiple of 4: aligned)
+                const uint2 v = *reinterpret_cast<const uint2 *>(base + (size_t)gs0 * 2);
                 mreg[0] = make_uint4(v.x, v.y, 0u, 0u);
+            } else if constexpr (MRB == 4) {   // a 4-byte run (gs0 even)
+                mreg[0] = make_uint4(*reinterpret_cast<const uint32_t *>(base + (size_t)gs0 * 2), 0u, 0u, 0u);
             } else {
 #pragma unroll
                 for (int j = 0; j < MPARTS; ++j)
@@ -225,11 +255,11 @@ __global__ __launch_bounds__(64 * kDecMaxWaves) void decode_kernel(
     const unsigned char *qhb = reinterpret_cast<const unsigned char *>(qw_hi) + (size_t)b * 8 * K;
     const uint32_t col_bytes = (uint32_t)rows_b * 64;
     const uint32_t lane_off = nfull > 0 ? (uint32_t)(s * rows_b + rl) * 16u : 0u;
-    const int tlast = min(t0 + max(nfull - 1, 0), T - 1);
+    const int tlast = min(tb + max(nfull - 1, 0), T - 1);
     uint4 rec[NCOL], rech[NCOL];
 #pragma unroll
     for (int p = 0; p < NCOL; ++p) {
-        const uint32_t cb = (uint32_t)min(t0 + p, tlast) * col_bytes;
+        const uint32_t cb = (uint32_t)min(tb + p, tlast) * col_bytes;
         rec[p] = nt_load(reinterpret_cast<const uint4 *>((qb + cb) + lane_off));
         if constexpr (FT::two_planes) rech[p] = nt_load(reinterpret_cast<const uint4 *>((qhb + cb) + lane_off));
         // keep each load where it is: sinking it towards its use would
@@ -338,9 +368,16 @@ __global__ __launch_bounds__(64 * kDecMaxWaves) void decode_kernel(
     };
     const int zoff = gs0 & 7;   // the slice's first zero-point nibble in its first word
     auto zero_of = [&](int g) -> uint32_t {   // g: group within the slice
-        if constexpr (!FT::has_zeros) return 0u;
-        else if constexpr (MREG) return (zreg[(g + zoff) >> 3] >> (4 * ((g + zoff) & 7))) & 0xFu;
-        else return (zrow_l[g >> 3] >> (4 * (g & 7))) & 0xFu;
+        if constexpr (!FT::has_zeros) {
+            return 0u;
+        } else if constexpr (MREG) {
+            // one word: the slice's groups sit at nibbles zoff.. of it; two:
+            // the slice starts a word (zoff = 0), so the index is static
+            if constexpr (ZW <= 1) return (zreg[0] >> (4 * ((g + zoff) & 7))) & 0xFu;
+            else return (zreg[g >> 3] >> (4 * (g & 7))) & 0xFu;
+        } else {
+            return (zrow_l[g >> 3] >> (4 * (g & 7))) & 0xFu;
+        }
     };
     auto scale_of = [&](int g) -> float {     // g: group within the slice
         if constexpr (MREG) {
@@ -349,6 +386,32 @@ __global__ __launch_bounds__(64 * kDecMaxWaves) void decode_kernel(
             return (float)__builtin_bit_cast(_Float16, (uint16_t)(w >> (16 * (g & 1))));
         } else {
             return (float)*reinterpret_cast<const _Float16 *>(mrow_l + g * 2);
+        }
+    };
+    // the same for a group known only at run time (the partial last column):
+    // the register runs are read through selects, not a dynamic index (which
+    // would put them in scratch memory)
+    auto scale_dyn = [&](int g) -> float {
+        if constexpr (MREG) {
+            uint32_t w = 0;
+#pragma unroll
+            for (int q = 0; q < MPARTS; ++q) {
+                w = (g >> 3) == q && (g & 7) < 2 ? mreg[q].x : w;
+                w = (g >> 3) == q && ((g & 7) >> 1) == 1 ? mreg[q].y : w;
+                w = (g >> 3) == q && ((g & 7) >> 1) == 2 ? mreg[q].z : w;
+                w = (g >> 3) == q && ((g & 7) >> 1) == 3 ? mreg[q].w : w;
+            }
+            return (float)__builtin_bit_cast(_Float16, (uint16_t)(w >> (16 * (g & 1))));
+        } else {
+            return scale_of(g);
+        }
+    };
+    auto zero_dyn = [&](int g) -> uint32_t {
+        if constexpr (FT::has_zeros && MREG && ZW > 1) {
+            const uint32_t w = (g >> 3) == 0 ? zreg[0] : zreg[1];
+            return (w >> (4 * (g & 7))) & 0xFu;
+        } else {
+            return zero_of(g);
         }
     };
     // closing unit u of the slice with scale sc, zero-point z; K-quant: S and
@@ -416,7 +479,7 @@ __global__ __launch_bounds__(64 * kDecMaxWaves) void decode_kernel(
     // 6. the partial last column of K (K % 128 != 0, groups 32 and 64): nc < 4
     // chunks, whose nc dwords of a lane are consecutive; its groups are whole
     if constexpr (!FT::kquant && GROUP < kColumn) {
-        if (nfull < NCOL && t0 + nfull == T - 1 && T > (C >> 2)) {
+        if (nfull < NCOL && t0 + nfull == T - 1 && T > (C >> 2) && tend == T) {
             const int tl = T - 1;
             const int nc = C - tl * kColChunks;
             const size_t off = (size_t)tl * rows_b * 16 + (size_t)s * rows_b * nc + (size_t)rl * nc;
@@ -427,7 +490,7 @@ __global__ __launch_bounds__(64 * kDecMaxWaves) void decode_kernel(
                 uint4 xv[MT];
                 load_x(c, xv);
                 chunk(xv, col[j], FT::two_planes ? colh[j] : 0u);
-                if ((j + 1) % CPG == 0 || j == nc - 1) close(c / CPG, scale_of(c / CPG), 0.0f, zero_of(c / CPG), true);
+                if ((j + 1) % CPG == 0 || j == nc - 1) close(c / CPG, scale_dyn(c / CPG), 0.0f, zero_dyn(c / CPG), true);
             }
         }
     }
@@ -447,27 +510,151 @@ __global__ __launch_bounds__(64 * kDecMaxWaves) void decode_kernel(
     }
     __syncthreads();
     const int waves = blockDim.x >> 6;
-    for (int i = threadIdx.x; i < M * kRowBlock; i += blockDim.x) {
+    if (sp.splits == 1) {
+        for (int i = threadIdx.x; i < M * kRowBlock; i += blockDim.x) {
+            const int m = i >> 4, rr = i & 15;
+            if (rr < rows_b) {
+                float v = red[0][m][rr];
+                for (int w = 1; w < waves; ++w) v += red[w][m][rr];
+                y[(int64_t)m * N + b * kRowBlock + rr] = BF ? f32_to_bf16_bits(v) : f32_to_f16_bits(v);
+            }
+        }
+        return;
+    }
+    // split K: this range's partial, then the arrival; the last arrival adds
+    // the S partials in split order and writes y. The partials are written
+    // and read with device-scope atomic accesses (coherent across the XCDs'
+    // L2 caches, which an agent-scope fence would otherwise write back and
+    // invalidate whole, thousands of times per launch): every wave waits for
+    // its stores to complete (vmcnt(0)) before the barrier, the arrival is
+    // counted after it, and the last arrival reads the partials only after its
+    // count returned.
+    const int MR = M * kRowBlock;
+    float *pb = sp.part + (size_t)blk * sp.splits * MR;
+    for (int i = threadIdx.x; i < MR; i += blockDim.x) {
+        const int m = i >> 4, rr = i & 15;
+        float v = red[0][m][rr];
+        for (int w = 1; w < waves; ++w) v += red[w][m][rr];
+        __hip_atomic_store(pb + (size_t)h * MR + i, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+    __shared__ int last;
+    __builtin_amdgcn_s_waitcnt(0x0F70);
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        unsigned long long *c = sp.cnt + blk;
+        unsigned long long old = __hip_atomic_load(c, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        unsigned long long nv;
+        do {
+            nv = (old & ~0xFFull) == sp.token ? old + 1 : (sp.token | 1ull);
+        } while (!__hip_atomic_compare_exchange_strong(c, &old, nv, __ATOMIC_RELAXED, __ATOMIC_RELAXED,
+                                                       __HIP_MEMORY_SCOPE_AGENT));
+        last = (int)(nv & 0xFFull) == sp.splits;
+        // the block is complete: clear its counter (a replay with this token
+        // counts from zero again)
+        if (last) __hip_atomic_store(c, 0ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+    __syncthreads();
+    if (!last) return;
+    for (int i = threadIdx.x; i < MR; i += blockDim.x) {
         const int m = i >> 4, rr = i & 15;
         if (rr < rows_b) {
-            float v = red[0][m][rr];
-            for (int w = 1; w < waves; ++w) v += red[w][m][rr];
+            float v = __hip_atomic_load(pb + i, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            for (int j = 1; j < sp.splits; ++j)
+                v += __hip_atomic_load(pb + (size_t)j * MR + i, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
             y[(int64_t)m * N + b * kRowBlock + rr] = BF ? f32_to_bf16_bits(v) : f32_to_f16_bits(v);
         }
     }
 }
 
+template <int GROUP, int MT, bool BF, int FMT, int NCOL, bool AWQ>
+__global__ __launch_bounds__(64 * kDecMaxWaves) void decode_kernel(
+    const uint16_t *__restrict__ x, const uint4 *__restrict__ qw, const uint4 *__restrict__ qw_hi,
+    const uint16_t *__restrict__ scales, const uint32_t *__restrict__ zeros, uint16_t *__restrict__ y, int M,
+    int N, int K, const float *__restrict__ act_mul, DecSplit sp) {
+    const int id = blockIdx.x;
+    const int b = id / sp.splits, h = id - b * sp.splits;
+    decode_body<GROUP, MT, BF, FMT, NCOL, AWQ>(x, qw, qw_hi, scales, zeros, y, M, N, K, act_mul, b, h, b, sp);
+}
+
+// Several independent problems (same M, K, group, format and type) in one
+// launch: workgroups [first[p], first[p+1]) belong to problem p, which keeps
+// the split of a call on it alone (splits[p] workgroups of cols[p] columns
+// per row block: the same partial sums, so the same bits); its counters and
+// partials start at blk0[p] and part0[p] of the launch's.
+struct DecGroupTable {
+    const void *x[kMaxGroup];
+    const void *qweight[kMaxGroup];
+    const void *scales[kMaxGroup];
+    const void *zeros[kMaxGroup];
+    void *y[kMaxGroup];
+    int N[kMaxGroup];
+    int splits[kMaxGroup];
+    int cols[kMaxGroup];
+    int first[kMaxGroup + 1];
+    int blk0[kMaxGroup];
+    int64_t part0[kMaxGroup];
+    int count;
+};
+
+template <int GROUP, int MT, bool BF, int FMT, int NCOL, bool AWQ>
+__global__ __launch_bounds__(64 * kDecMaxWaves) void decode_group_kernel(DecGroupTable tab, int M, int K,
+                                                                         DecSplit sp) {
+    int p = 0;
+    while (p + 1 < tab.count && (int)blockIdx.x >= tab.first[p + 1]) ++p;   // uniform
+    const int id = (int)blockIdx.x - tab.first[p];
+    const DecSplit spp{tab.splits[p], tab.cols[p], sp.part ? sp.part + tab.part0[p] : nullptr,
+                       sp.cnt ? sp.cnt + tab.blk0[p] : nullptr, sp.token};
+    const int b = id / spp.splits, h = id - b * spp.splits;
+    const uint4 *qw = reinterpret_cast<const uint4 *>(tab.qweight[p]);
+    decode_body<GROUP, MT, BF, FMT, NCOL, AWQ>(
+        reinterpret_cast<const uint16_t *>(tab.x[p]), qw,
+        FormatTraits<FMT>::two_planes ? qw + (size_t)tab.N[p] * (K / 32) : qw,   // second plane (8-bit codes)
+        reinterpret_cast<const uint16_t *>(tab.scales[p]), reinterpret_cast<const uint32_t *>(tab.zeros[p]),
+        reinterpret_cast<uint16_t *>(tab.y[p]), M, tab.N[p], K, nullptr, b, h, b, spp);
+}
+
+// The split's view of the workspace: counters [blocks] (8 bytes each, the
+// array padded to 256 bytes), then partials [blocks][splits][M][16] fp32.
+inline DecSplit dec_split(const DecodePlan &p, void *ws, int blocks) {
+    DecSplit sp{p.splits, p.cols, nullptr, nullptr, 0ull};
+    if (ws != nullptr) {
+        sp.cnt = static_cast<unsigned long long *>(ws);
+        sp.part = reinterpret_cast<float *>(static_cast<char *>(ws) + align_up((size_t)blocks * 8, 256));
+        unsigned long long t = next_sk_token() & ~0xFFull;
+        sp.token = t != 0 ? t : 0x9E3779B97F4A7C00ull;
+    }
+    return sp;
+}
+
+// One launch of the kernel instantiated for (MT, NCOL, AWQ); `grouped` picks
+// the several-problem kernel (its table in `tab`).
 template <int GROUP, int MT, bool BF, int FMT, int NC, bool AWQ>
 hipError_t launch_dec_one(const void *x, const void *qw, const void *qh, const void *sc, const void *zp, void *y,
-                          int M, int N, int K, const float *am, const DecodePlan &p, hipStream_t stream) {
+                          int M, int N, int K, const float *am, const DecodePlan &p, const DecGroupTable *tab,
+                          void *ws, hipStream_t stream) {
     auto kern = decode_kernel<GROUP, MT, BF, FMT, NC, AWQ>;
-    static DynLdsAttr attr;
-    hipError_t e = raise_dyn_lds(reinterpret_cast<const void *>(kern), p.lds, attr);
-    if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(kern, dim3((unsigned)ceil_div(N, kRowBlock)), dim3(64 * p.waves), p.lds, stream,
-                       reinterpret_cast<const uint16_t *>(x), reinterpret_cast<const uint4 *>(qw),
-                       reinterpret_cast<const uint4 *>(qh), reinterpret_cast<const uint16_t *>(sc),
-                       reinterpret_cast<const uint32_t *>(zp), reinterpret_cast<uint16_t *>(y), M, N, K, am);
+    static DynLdsAttr attr[2];
+    if (tab) {   // (the grouped kernel has no activation multipliers)
+        if constexpr (AWQ) {
+            return hipErrorInvalidValue;
+        } else {
+            auto gkern = decode_group_kernel<GROUP, MT, BF, FMT, NC, false>;
+            hipError_t e = raise_dyn_lds(reinterpret_cast<const void *>(gkern), p.lds, attr[1]);
+            if (e != hipSuccess) return e;
+            const int blocks = tab->blk0[tab->count - 1] + (int)ceil_div(tab->N[tab->count - 1], kRowBlock);
+            hipLaunchKernelGGL(gkern, dim3((unsigned)tab->first[tab->count]), dim3(64 * p.waves), p.lds, stream,
+                               *tab, M, K, dec_split(p, ws, blocks));   // (per-problem splits in the table)
+        }
+    } else {
+        hipError_t e = raise_dyn_lds(reinterpret_cast<const void *>(kern), p.lds, attr[0]);
+        if (e != hipSuccess) return e;
+        const int blocks = (int)ceil_div(N, kRowBlock);
+        hipLaunchKernelGGL(kern, dim3((unsigned)(blocks * p.splits)), dim3(64 * p.waves), p.lds, stream,
+                           reinterpret_cast<const uint16_t *>(x), reinterpret_cast<const uint4 *>(qw),
+                           reinterpret_cast<const uint4 *>(qh), reinterpret_cast<const uint16_t *>(sc),
+                           reinterpret_cast<const uint32_t *>(zp), reinterpret_cast<uint16_t *>(y), M, N, K, am,
+                           dec_split(p, ws, blocks));
+    }
     return hipGetLastError();
 }
 
@@ -475,24 +662,53 @@ hipError_t launch_dec_one(const void *x, const void *qw, const void *qh, const v
 // decode_plan chooses
 template <int GROUP, bool BF, int FMT>
 hipError_t launch_dec_group(const void *x, const void *qw, const void *qh, const void *sc, const void *zp, void *y,
-                            int M, int N, int K, const float *am, const DecodePlan &p, hipStream_t stream) {
+                            int M, int N, int K, const float *am, const DecodePlan &p, const DecGroupTable *tab,
+                            void *ws, hipStream_t stream) {
 #define W4A16_DEC(MT_, NC_, AWQ_) \
-    launch_dec_one<GROUP, MT_, BF, FMT, NC_, AWQ_>(x, qw, qh, sc, zp, y, M, N, K, am, p, stream)
+    launch_dec_one<GROUP, MT_, BF, FMT, NC_, AWQ_>(x, qw, qh, sc, zp, y, M, N, K, am, p, tab, ws, stream)
     const bool awq = am != nullptr;
     switch (p.mt * 100 + p.ncol * 2 + (awq ? 1 : 0)) {
+        case 108: return W4A16_DEC(1, 4, false);
+        case 109: return W4A16_DEC(1, 4, true);
         case 116: return W4A16_DEC(1, 8, false);
-        case 132: return W4A16_DEC(1, 16, false);
         case 117: return W4A16_DEC(1, 8, true);
+        case 132: return W4A16_DEC(1, 16, false);
+        case 133: return W4A16_DEC(1, 16, true);
+        case 208: return W4A16_DEC(2, 4, false);
+        case 209: return W4A16_DEC(2, 4, true);
         case 216: return W4A16_DEC(2, 8, false);
-        case 232: return W4A16_DEC(2, 16, false);
         case 217: return W4A16_DEC(2, 8, true);
+        case 232: return W4A16_DEC(2, 16, false);
+        case 233: return W4A16_DEC(2, 16, true);
+        case 408: return W4A16_DEC(4, 4, false);
+        case 409: return W4A16_DEC(4, 4, true);
         case 416: return W4A16_DEC(4, 8, false);
         case 417: return W4A16_DEC(4, 8, true);
+        case 808: return W4A16_DEC(8, 4, false);
+        case 809: return W4A16_DEC(8, 4, true);
         case 816: return W4A16_DEC(8, 8, false);
         case 817: return W4A16_DEC(8, 8, true);
         default: return hipErrorInvalidValue;
     }
 #undef W4A16_DEC
+}
+
+template <bool BF, int FMT>
+hipError_t launch_dec_groups(const void *x, const void *qw, const void *qh, const void *sc, const void *zp, void *y,
+                             int M, int N, int K, int group, const float *am, const DecodePlan &p,
+                             const DecGroupTable *tab, void *ws, hipStream_t stream) {
+#define W4A16_DEC_G(G_) launch_dec_group<G_, BF, FMT>(x, qw, qh, sc, zp, y, M, N, K, am, p, tab, ws, stream)
+    if constexpr (FormatTraits<FMT>::kquant) {
+        return W4A16_DEC_G(256);
+    } else {
+        switch (group) {
+            case 32: return W4A16_DEC_G(32);
+            case 64: return W4A16_DEC_G(64);
+            case 128: return W4A16_DEC_G(128);
+            default: return W4A16_DEC_G(256);
+        }
+    }
+#undef W4A16_DEC_G
 }
 
 }  // namespace
@@ -501,23 +717,62 @@ hipError_t launch_dec_group(const void *x, const void *qw, const void *qh, const
 template <int FMT>
 hipError_t launch_decode_fmt(const void *x, bool bf16, const void *qweight, const void *scales, const void *zeros,
                              void *y, int M, int N, int K, int group, const float *am, const DecodePlan &plan,
-                             hipStream_t stream) {
-    if (!plan.ok) return hipErrorInvalidValue;
+                             void *workspace, hipStream_t stream) {
+    if (!plan.ok || (plan.splits > 1 && workspace == nullptr)) return hipErrorInvalidValue;
     const void *qh = FormatTraits<FMT>::two_planes
                          ? static_cast<const void *>(static_cast<const char *>(qweight) + (size_t)N * K / 2)
                          : qweight;
-#define W4A16_DEC_G(G_, BF_) launch_dec_group<G_, BF_, FMT>(x, qweight, qh, scales, zeros, y, M, N, K, am, plan, stream)
-    if constexpr (FormatTraits<FMT>::kquant) {
-        return bf16 ? W4A16_DEC_G(256, true) : W4A16_DEC_G(256, false);
-    } else {
-        switch (group) {
-            case 32: return bf16 ? W4A16_DEC_G(32, true) : W4A16_DEC_G(32, false);
-            case 64: return bf16 ? W4A16_DEC_G(64, true) : W4A16_DEC_G(64, false);
-            case 128: return bf16 ? W4A16_DEC_G(128, true) : W4A16_DEC_G(128, false);
-            default: return bf16 ? W4A16_DEC_G(256, true) : W4A16_DEC_G(256, false);
+    return bf16 ? launch_dec_groups<true, FMT>(x, qweight, qh, scales, zeros, y, M, N, K, group, am, plan, nullptr,
+                                               workspace, stream)
+                : launch_dec_groups<false, FMT>(x, qweight, qh, scales, zeros, y, M, N, K, group, am, plan, nullptr,
+                                                workspace, stream);
+}
+
+// plans[p]: each problem's own plan (the same mt and ncol for all); the
+// launch runs the most waves and LDS any of them needs. Workspace: counters
+// for every problem's row blocks (padded to 256 bytes), then the partials of
+// the problems that split, in order.
+template <int FMT>
+hipError_t launch_decode_group_fmt(const GroupTable &gt, bool bf16, int M, int K, int group, const DecodePlan *plans,
+                                   void *workspace, hipStream_t stream) {
+    if (gt.count < 1 || gt.count > kMaxGroup) return hipErrorInvalidValue;
+    DecGroupTable tab{};
+    tab.count = gt.count;
+    DecodePlan plan = plans[0];
+    bool split = false;
+    int wgs = 0, blocks = 0;
+    int64_t part = 0;
+    for (int i = 0; i < gt.count; ++i) {
+        const DecodePlan &q = plans[i];
+        if (!q.ok || q.mt != plan.mt || q.ncol != plan.ncol) return hipErrorInvalidValue;
+        plan.waves = std::max(plan.waves, q.waves);
+        plan.lds = std::max(plan.lds, q.lds);
+        tab.x[i] = gt.x[i];
+        tab.qweight[i] = gt.qweight[i];
+        tab.scales[i] = gt.scales[i];
+        tab.zeros[i] = gt.zeros[i];
+        tab.y[i] = gt.y[i];
+        tab.N[i] = gt.N[i];
+        tab.splits[i] = q.splits;
+        tab.cols[i] = q.cols;
+        tab.first[i] = wgs;
+        tab.blk0[i] = blocks;
+        tab.part0[i] = part;
+        const int nb = (int)ceil_div(gt.N[i], kRowBlock);
+        wgs += nb * q.splits;
+        blocks += nb;
+        if (q.splits > 1) {
+            part += (int64_t)nb * q.splits * M * kRowBlock;
+            split = true;
         }
     }
-#undef W4A16_DEC_G
+    if (split && workspace == nullptr) return hipErrorInvalidValue;
+    if (!split) workspace = nullptr;
+    tab.first[gt.count] = wgs;
+    return bf16 ? launch_dec_groups<true, FMT>(nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, M, 0, K, group,
+                                               nullptr, plan, &tab, workspace, stream)
+                : launch_dec_groups<false, FMT>(nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, M, 0, K, group,
+                                                nullptr, plan, &tab, workspace, stream);
 }
 
 }  // namespace w4a16

@@ -4,6 +4,9 @@
 namespace w4a16 {
 
 template hipError_t launch_decode_fmt<kSym4>(const void *, bool, const void *, const void *, const void *, void *,
-                                            int, int, int, int, const float *, const DecodePlan &, hipStream_t);
+                                            int, int, int, int, const float *, const DecodePlan &, void *,
+                                            hipStream_t);
+template hipError_t launch_decode_group_fmt<kSym4>(const GroupTable &, bool, int, int, int, const DecodePlan *, void *,
+                                                  hipStream_t);
 
 }  // namespace w4a16

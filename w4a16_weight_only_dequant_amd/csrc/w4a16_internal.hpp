@@ -69,17 +69,22 @@ typedef __bf16 bf162_t __attribute__((ext_vector_type(2)));
 __host__ __device__ inline int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 __host__ __device__ inline size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
 
-// Host-side plan for one decode launch (M <= kDecodeMaxM): one workgroup per
-// 16-row block, `waves` waves of `ncol` 128-weight columns each (all of K),
-// `mt` activation rows held. ok is false when the shape is outside the
-// kernel's range (K above 16384 or 32768, see decode_plan).
+// Host-side plan for one decode launch (M <= kDecodeMaxM): `splits`
+// workgroups per 16-row block, each over `cols` 128-weight columns of K with
+// `waves` waves of `ncol` columns; `mt` activation rows held. ok is false
+// when the shape is outside the kernel's range (see decode_plan). N: the rows
+// of the launch (all problems of a grouped launch).
 constexpr int kDecodeMaxM = 8;
 struct DecodePlan {
     int mt, ncol, waves;
+    int splits, cols;
     size_t lds;   // dynamic LDS bytes of one workgroup
     bool ok;
 };
 DecodePlan decode_plan(int64_t M, int64_t N, int64_t K, int32_t group, int fmt, bool awq);
+// Workspace of a decode launch over N rows: none without a split; else the
+// blocks' arrival counters (padded to 256 bytes) and fp32 partials.
+size_t decode_workspace_bytes(const DecodePlan &plan, int64_t M, int64_t N);
 
 // Plan for the matrix-core kernels: kind 0 streams the weights through
 // registers for M <= kSkinnyMaxM (16-row MFMA tiles of activations, one per
@@ -152,10 +157,17 @@ hipError_t launch_quant_error(const float *w, const void *qweight, const void *s
 // x_out[m][k] = rne16(x[m][k] * act_mul[k]).
 hipError_t launch_scale_activations(const void *x, bool bf16, const float *act_mul, void *x_out, int64_t M,
                                     int K, hipStream_t stream);
-// act_mul: NULL, or fp32 activation multipliers [K] (AWQ's run-time scaling)
+// act_mul: NULL, or fp32 activation multipliers [K] (AWQ's run-time scaling);
+// workspace: decode_workspace_bytes(plan, M, N) bytes (NULL when that is 0)
 hipError_t launch_decode(const void *x, bool bf16, const void *qweight, const void *scales,
                          const void *zeros, void *y, int M, int N, int K, int group, int fmt,
-                         const float *act_mul, const DecodePlan &plan, hipStream_t stream);
+                         const float *act_mul, const DecodePlan &plan, void *workspace, hipStream_t stream);
+// plans[p]: the plan of a call on problem p alone (decode_plan with its N)
+hipError_t launch_decode_group(const GroupTable &tab, bool bf16, int M, int K, int group, int fmt,
+                               const DecodePlan *plans, void *workspace, hipStream_t stream);
+// Workspace of that grouped launch: every problem's row-block counters, then
+// the partials of the problems that split (0 when none does).
+size_t decode_group_workspace_bytes(const DecodePlan *plans, int count, int64_t M, const int *N);
 // workspace: prefill_workspace_bytes(plan) bytes (the stream-K partials and
 // flags), may be NULL when that is 0
 hipError_t launch_gemm(const void *x, bool bf16, const void *qweight, const void *scales,
@@ -170,7 +182,11 @@ int prefill_tile(int64_t M, int64_t N);
 #define W4A16_LINEAR_PARAMS const void *x, bool bf16, const void *qweight, const void *scales, const void *zeros, \
                             void *y, int M, int N, int K, int group
 template <int FMT>
-hipError_t launch_decode_fmt(W4A16_LINEAR_PARAMS, const float *act_mul, const DecodePlan &plan, hipStream_t stream);
+hipError_t launch_decode_fmt(W4A16_LINEAR_PARAMS, const float *act_mul, const DecodePlan &plan, void *workspace,
+                             hipStream_t stream);
+template <int FMT>
+hipError_t launch_decode_group_fmt(const GroupTable &tab, bool bf16, int M, int K, int group, const DecodePlan *plans,
+                                   void *workspace, hipStream_t stream);
 template <int FMT> hipError_t launch_skinny_fmt(W4A16_LINEAR_PARAMS, const GemmPlan &plan, hipStream_t stream);
 template <int FMT>
 hipError_t launch_prefill_fmt(W4A16_LINEAR_PARAMS, const GemmPlan &plan, void *workspace, hipStream_t stream);
@@ -179,7 +195,9 @@ hipError_t launch_skinny_group_fmt(const GroupTable &tab, bool bf16, int M, int 
                                    hipStream_t stream);
 #define W4A16_EXTERN_FMT(F)                                                                              \
     extern template hipError_t launch_decode_fmt<F>(W4A16_LINEAR_PARAMS, const float *, const DecodePlan &, \
-                                                    hipStream_t);                                         \
+                                                    void *, hipStream_t);                                 \
+    extern template hipError_t launch_decode_group_fmt<F>(const GroupTable &, bool, int, int, int,        \
+                                                          const DecodePlan *, void *, hipStream_t);       \
     extern template hipError_t launch_skinny_fmt<F>(W4A16_LINEAR_PARAMS, const GemmPlan &, hipStream_t); \
     extern template hipError_t launch_prefill_fmt<F>(W4A16_LINEAR_PARAMS, const GemmPlan &, void *, hipStream_t); \
     extern template hipError_t launch_skinny_group_fmt<F>(const GroupTable &, bool, int, int, int,        \
