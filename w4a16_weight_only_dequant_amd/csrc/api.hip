@@ -20,8 +20,9 @@ constexpr int kMaxDevices = 64;
 std::atomic<int> g_device_kind[kMaxDevices];
 
 // Largest M routed to the decode kernel by w4a16_linear (the decode kernel
-// itself accepts M <= 8): from M = 2 on the matrix-core kernel measured faster.
-int gemv_max_m() { return 1; }
+// itself accepts M <= 8): measured faster than the matrix-core kernel up to
+// M = 2 (N = 15360, K = 5120: 11.4 against 14.2 us), slower from M = 4.
+int gemv_max_m() { return 2; }
 
 bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
@@ -251,8 +252,7 @@ size_t decode_need_any(int64_t M, int64_t N, int64_t K, int32_t group) {
     return need;
 }
 
-// w4a16_linear's choice: the decode kernel at M <= gemv_max_m() (M = 1;
-// measured faster than the matrix-core kernel on every decode shape), the
+// w4a16_linear's choice: the decode kernel at M <= gemv_max_m(), the
 // matrix-core kernels otherwise.
 bool prefer_gemv(int64_t M, int64_t N, int64_t K, int32_t group, int32_t dtype, int32_t fmt) {
     return M >= 1 && M <= gemv_max_m() && shape_ok(N, K, group) && (dtype == W4A16_F16 || dtype == W4A16_BF16) &&

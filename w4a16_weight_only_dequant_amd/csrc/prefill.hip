@@ -10,7 +10,7 @@
 namespace w4a16 {
 
 int prefill_tile(int64_t M, int64_t N) {
-    static const int forced = tuning_knob("W4A16_PREFILL_TILE", -1);
+    const int forced = tuning_knob("W4A16_PREFILL_TILE", -1);
     if (forced >= 0 && forced <= kTile256x256w8) return forced;
     // time ~ rounds of workgroups over the 256 CUs x time of one tile; the
     // relative tile times (0.62, 0.67, 1.0 for 64, 128, 256 rows) were
@@ -45,7 +45,7 @@ int prefill_tile(int64_t M, int64_t N) {
 // 283 us either way; 264 tiles: 266 -> 185 us). Needs at least 4 columns per
 // tile, so that a split tile still has a head and a tail of some length.
 void prefill_stream_k(int64_t M, int64_t N, int64_t K, int cus, GemmPlan &plan) {
-    static const int enabled = tuning_knob("W4A16_PREFILL_SK", 1);
+    const int enabled = tuning_knob("W4A16_PREFILL_SK", 1);
     plan.dp_tiles = 0;
     plan.sk_wgs = 0;
     const int64_t tiles = ceil_div(M, tile_rows(plan.tile)) * ceil_div(N, kTileCols);
