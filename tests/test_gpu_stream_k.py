@@ -19,8 +19,8 @@ pytestmark = pytest.mark.gpu
 # slot per two columns) and with ragged M (the last tile row holds 208 rows),
 # and 8 x 97 = 776 tiles (two rounds of whole tiles, then the last 264 tiles
 # split)
-SK_SHAPES = [(2048, 8448, 512, 128), (2048, 8448, 672, 32), (2048, 8448, 1024, 64), (2048, 8448, 1024, 256),
-             (2000, 8448, 512, 128), (2048, 24832, 512, 128)]
+SK_SHAPES = [(2048, 8448, 2048, 128), (2048, 8448, 2080, 32), (2048, 8448, 2048, 64), (2048, 8448, 2048, 256),
+             (2000, 8448, 2048, 128), (2048, 24832, 2048, 128)]
 
 
 def _prep(N, K, group, fmt="asym4"):
@@ -53,7 +53,7 @@ def test_stream_k_matches_oracle(M, N, K, group, dtype):
 @pytest.mark.parametrize("fmt", ["sym8", "kq4"])
 def test_stream_k_formats(fmt):
     import torch
-    M, N, K = 2048, 8448, 512
+    M, N, K = 2048, 8448, 2048
     group = 256 if fmt == "kq4" else 128
     w, o, pw = _prep(N, K, group, fmt)
     x = wl.random_activations(7, M, K, "bf16")
@@ -67,7 +67,7 @@ def test_stream_k_one_hot_is_exact(dtype):
     """One-hot rows: one of the two halves of a split tile holds the selected
     weight and the other an exact zero, so the sum is round(w_hat) exactly."""
     import torch
-    M, N, K, group = 2048, 8448, 512, 128
+    M, N, K, group = 2048, 8448, 2048, 128
     w, o, pw = _prep(N, K, group)
     w_hat = ref.dequantize(o["codes"], o["s_bits"], o["zeros"], group)
     ks = (np.arange(M) * 7919 + 3) % K
@@ -84,7 +84,7 @@ def test_stream_k_one_hot_is_exact(dtype):
 def test_stream_k_repeatable_any_workspace_and_graph_replay():
     import torch
     w4 = H.lib()
-    M, N, K, group = 2048, 8448, 672, 32
+    M, N, K, group = 2048, 8448, 2080, 32
     w, o, pw = _prep(N, K, group)
     x = H.to_device_bits(wl.random_activations(5, M, K, "bf16"), "bf16")
     nbytes = w4.workspace_bytes(M, N, K, group)
@@ -123,7 +123,7 @@ def test_stream_k_workspace_holding_small_integers():
     stale word passes for a flag."""
     import torch
     w4 = H.lib()
-    M, N, K, group = 2048, 8448, 512, 128
+    M, N, K, group = 2048, 8448, 2048, 128
     w, o, pw = _prep(N, K, group)
     x = H.to_device_bits(wl.random_activations(9, M, K, "f16"), "f16")
     nbytes = w4.workspace_bytes(M, N, K, group)
@@ -147,7 +147,7 @@ def test_stream_k_wait_expiry_poisons_tiles_and_reports():
     import torch
     w4 = H.lib()
     raw = w4.raw()
-    M, N, K, group = 2048, 8448, 512, 128
+    M, N, K, group = 2048, 8448, 2048, 128
     w, o, pw = _prep(N, K, group)
     x = H.to_device_bits(wl.random_activations(8, M, K, "bf16"), "bf16")
     nbytes = w4.workspace_bytes(M, N, K, group)
@@ -198,7 +198,7 @@ def test_default_workspace_is_per_stream():
     import threading
     import torch
     w4 = H.lib()
-    M, N, K, group = 2048, 8448, 512, 128
+    M, N, K, group = 2048, 8448, 2048, 128
     w, o, pw = _prep(N, K, group)
     xs = [H.to_device_bits(wl.random_activations(300 + i, M, K, "f16"), "f16") for i in range(2)]
     want = [w4.gemm(x, pw) for x in xs]
@@ -232,7 +232,7 @@ def test_default_workspace_is_per_stream():
 def test_stream_k_short_workspace_refused():
     import torch
     w4 = H.lib()
-    M, N, K, group = 2048, 8448, 512, 128
+    M, N, K, group = 2048, 8448, 2048, 128
     w, o, pw = _prep(N, K, group)
     x = H.to_device_bits(wl.random_activations(6, M, K, "f16"), "f16")
     nbytes = w4.workspace_bytes(M, N, K, group)
@@ -253,7 +253,7 @@ def test_stream_k_through_grouped_and_awq_calls():
     workspace after them) on a split shape match w4a16_gemm bit for bit."""
     import torch
     w4 = H.lib()
-    M, K, group = 2048, 512, 128
+    M, K, group = 2048, 2048, 128
     pw_a = _prep(8448, K, group)[2]          # splits (264 tiles)
     pw_b = H.prepared(("sk-whole", 4096, K, group), lambda: wl.random_weights(41, 4096, K), group)[2]   # whole tiles
     assert w4.workspace_bytes(M, 8448, K, group) > 0 and w4.workspace_bytes(M, 4096, K, group) == 0
@@ -270,14 +270,16 @@ def test_stream_k_through_grouped_and_awq_calls():
     assert torch.equal(y_awq.view(torch.int16), y_pre.view(torch.int16))
 
 
-@pytest.mark.parametrize("N,split", [(12288, True), (12544, False), (16640, True), (36864, True)])
-def test_stream_k_plan_boundaries(N, split):
-    """M = 2048 (256-row tiles, 8 per column of tiles) on 256 compute units:
-    384 tiles (last round exactly half full: split), 392 (just over: whole),
-    520 (one whole round, then the last two split) and 1152 (three whole
-    rounds, then 384 split). Outputs within the bar either way."""
+@pytest.mark.parametrize("N,K,split", [(12288, 2048, True), (12544, 2048, False), (16640, 2048, True),
+                                       (24832, 2048, True), (36864, 2048, False), (12288, 1920, False)])
+def test_stream_k_plan_boundaries(N, K, split):
+    """M = 2048 (256-row tiles, 8 per column of tiles) on 256 compute units,
+    K = 2048 (16 columns): 384 tiles (last round exactly half full: split),
+    392 (just over: whole), 520 (one whole round, then the last two split),
+    776 (four rounds, the last of 8 tiles: split) and 1152 (five rounds:
+    whole); K = 1920 (15 columns: whole). Outputs within the bar either way."""
     import torch
-    M, K, group = 2048, 512, 128
+    M, group = 2048, 128
     assert _uses_stream_k(M, N, K, group) == split
     w, o, pw = _prep(N, K, group)
     x = wl.random_activations(N + 5, M, K, "bf16")
@@ -295,7 +297,7 @@ def test_concurrent_calls_on_two_streams():
     import threading
     import torch
     w4 = H.lib()
-    M, N, K, group = 2048, 8448, 512, 128
+    M, N, K, group = 2048, 8448, 2048, 128
     w, o, pw = _prep(N, K, group)
     xs = [H.to_device_bits(wl.random_activations(100 + i, M, K, "bf16"), "bf16") for i in range(2)]
     x1 = [H.to_device_bits(wl.random_activations(200 + i, 1, K, "f16"), "f16") for i in range(2)]
@@ -329,7 +331,7 @@ def test_concurrent_calls_on_two_streams():
     assert not errors, errors
 
 
-@pytest.mark.parametrize("M,N,K,group", [(2048, 8448, 512, 128), (2048, 24832, 512, 128), (1024, 8448, 1024, 64),
+@pytest.mark.parametrize("M,N,K,group", [(2048, 8448, 2048, 128), (2048, 24832, 2048, 128), (1024, 8448, 2048, 64),
                                          (2048, 4096, 512, 128), (1, 1024, 8192, 128), (8, 5120, 2048, 32)])
 def test_workspace_bytes_are_enough_and_nothing_beyond_is_written(M, N, K, group):
     """Every product call succeeds with exactly w4a16_workspace_bytes of
@@ -367,10 +369,10 @@ def test_workspace_bytes_are_enough_and_nothing_beyond_is_written(M, N, K, group
 
 @pytest.mark.parametrize("dtype", ["f16", "bf16"])
 def test_stream_k_every_output(dtype):
-    """M = 2048, N = 8448, K = 512: 264 tiles, all split over the 256
+    """M = 2048, N = 8448, K = 2048: 264 tiles, all split over the 256
     workgroups; every output against the oracle."""
     import torch
-    M, N, K, group = 2048, 8448, 512, 128
+    M, N, K, group = 2048, 8448, 2048, 128
     assert _uses_stream_k(M, N, K, group)
     w, o, pw = _prep(N, K, group)
     x = wl.random_activations(78, M, K, dtype)

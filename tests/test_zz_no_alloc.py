@@ -42,7 +42,7 @@ def test_noalloc_matches_linear_on_consecutive_calls():
     w4 = H.lib()
     assert w4.raw().w4a16_init(0) == 0
     stream = torch.cuda.Stream()
-    K, group = 512, 128
+    K, group = 2048, 128
     # (M, N): two stream-K splits (the second smaller, ragged M), then a decode
     # call and a small-batch call that use no scratch, then the first again
     cases = [(2048, 8448), (2000, 8448), (1, 8448), (17, 8448), (2048, 8448)]
@@ -67,7 +67,7 @@ def test_noalloc_rejects_bad_arguments_and_writes_nothing():
     import torch
     w4 = H.lib()
     assert w4.raw().w4a16_init(0) == 0
-    K, group = 512, 128
+    K, group = 2048, 128
     w, o, pw = H.prepared(("noalloc", 8448, K, group), lambda: wl.random_weights(77, 8448, K), group)
     x = H.to_device_bits(wl.random_activations(9, 4, K, "bf16"), "bf16")
     y = torch.full((4, pw.N), 5.0, dtype=torch.bfloat16, device="cuda")

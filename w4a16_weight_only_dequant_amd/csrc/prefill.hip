@@ -42,16 +42,20 @@ int prefill_tile(int64_t M, int64_t N) {
 // earlier rounds stay whole tiles. Every piece of a split tile costs about
 // what a whole tile's start and end cost (measured ~10 us at K = 5120), so a
 // fuller last round gains nothing (432 tiles of 256 x 256 on 256 CUs:
-// 283 us either way; 264 tiles: 266 -> 185 us). Needs at least 4 columns per
-// tile, so that a split tile still has a head and a tail of some length.
+// 283 us either way; 264 tiles: 266 -> 185 us). Measured on MI355X it pays
+// from 16 columns per tile (K >= 2048: M = 2048, N = 8448 at K = 2048 102
+// against 117 us, at K = 1024 77 against 65 us) and while the whole-tile rounds
+// are few (at most four: seven rounds at M = 4096, N = 24832, K = 2048: 457
+// against 433 us).
 void prefill_stream_k(int64_t M, int64_t N, int64_t K, int cus, GemmPlan &plan) {
     const int enabled = tuning_knob("W4A16_PREFILL_SK", 1);
     plan.dp_tiles = 0;
     plan.sk_wgs = 0;
     const int64_t tiles = ceil_div(M, tile_rows(plan.tile)) * ceil_div(N, kTileCols);
     const int64_t T = ceil_div(K / kChunk, kColChunks);
-    if (!enabled || cus < 8 || T < 4 || tiles <= cus) return;
+    if (!enabled || cus < 8 || T < 16 || tiles <= cus) return;
     const int64_t rounds = ceil_div(tiles, cus);
+    if (rounds > 4) return;
     const int64_t last = tiles - (rounds - 1) * cus;   // tiles of the last round
     if (2 * last > cus) return;
     plan.dp_tiles = (int)((rounds - 2) * cus);

@@ -153,7 +153,8 @@ template <int BM, int BN, int WM, int WN, int GROUP, bool BF, int FMT, bool SK>
 __global__ __launch_bounds__(64 * WM * WN) __attribute__((amdgpu_waves_per_eu(WM * WN / 4, WM * WN / 4))) void prefill_kernel(
     const uint16_t *__restrict__ x, const uint4 *__restrict__ qw, const uint4 *__restrict__ qw_hi,
     const uint16_t *__restrict__ scales, const uint32_t *__restrict__ zeros, uint16_t *__restrict__ y, int M,
-    int N, int K, int m_tiles, int n_tiles, int mshift, int dp_tiles, int sk_wgs, float4 *__restrict__ partials,
+    int N, int K, int m_tiles, int n_tiles, int mshift, int dp_tiles, int sk_wgs, int raster,
+    float4 *__restrict__ partials,
     unsigned long long *__restrict__ flags, unsigned long long token, unsigned long long wait_token,
     unsigned int *__restrict__ err) {
     using FT = FormatTraits<FMT>;
@@ -198,7 +199,17 @@ __global__ __launch_bounds__(64 * WM * WN) __attribute__((amdgpu_waves_per_eu(WM
     int ft, lt, fb, le, s_sk = -1;   // first / last tile, first column of the first, end column of the last
     if ((int)blockIdx.x < dp_tiles) {
         int id = blockIdx.x;
-        if (dp_tiles % 8 == 0) id = (id % 8) * (dp_tiles / 8) + id / 8;
+        if (raster) {
+            // M bands: XCD j takes the band of m_tiles / 8 M tiles j * band ..
+            // and every N tile, band first, so its activation rows (one band:
+            // 2.6 MB at BM = 256, K = 5120) stay in its L2 and each weight
+            // tile is read once per XCD (raster set only when m_tiles % 8 == 0
+            // and dp_tiles is a multiple of m_tiles)
+            const int band = m_tiles >> 3, xcd = id & 7, l = id >> 3;
+            id = (l / band) * m_tiles + xcd * band + l % band;
+        } else if (dp_tiles % 8 == 0) {
+            id = (id % 8) * (dp_tiles / 8) + id / 8;
+        }
         ft = lt = id;
         fb = 0;
         le = T;
@@ -617,12 +628,13 @@ hipError_t launch_tile(const void *x, const void *qw, const void *qh, const void
     // the expiry of the wait gives them one no producer writes and a short bound
     const unsigned long long token = skw > 0 ? next_sk_token() : 0ull;
     const unsigned long long wait_token = sk.expire_test ? token ^ 0xA5A5A5A5A5A5A5A5ull : token;
+    const int raster = (m_tiles % 8 == 0 && dp % m_tiles == 0 && tuning_knob("W4A16_PREFILL_RASTER", 1) == 1) ? 1 : 0;
     unsigned int *err = skw > 0 ? kernel_error_word() : nullptr;
     hipLaunchKernelGGL(kern, dim3((unsigned)(dp + skw)), dim3(64 * WM * WN), lds, stream,
                        reinterpret_cast<const uint16_t *>(x), reinterpret_cast<const uint4 *>(qw),
                        reinterpret_cast<const uint4 *>(qh), reinterpret_cast<const uint16_t *>(sc),
                        reinterpret_cast<const uint32_t *>(zp), reinterpret_cast<uint16_t *>(y), M, N, K, m_tiles,
-                       n_tiles, ms, dp, skw, part, flags, token, wait_token, err);
+                       n_tiles, ms, dp, skw, raster, part, flags, token, wait_token, err);
     return hipGetLastError();
 }
 
