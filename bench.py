@@ -665,15 +665,21 @@ def counter_pass(out_dir, reps, legs):
 
 
 def _csv_rows(directory, suffix):
+    """Rows of every rocprofv3 CSV file (plain or gzipped) named *suffix under directory."""
+    import gzip
     rows = []
-    for f in sorted(glob.glob(os.path.join(directory, "**", f"*{suffix}"), recursive=True)):
-        with open(f) as fh:
+    files = glob.glob(os.path.join(directory, "**", f"*{suffix}"), recursive=True)
+    files += glob.glob(os.path.join(directory, "**", f"*{suffix}.gz"), recursive=True)
+    for f in sorted(files):
+        with (gzip.open(f, "rt") if f.endswith(".gz") else open(f)) as fh:
             rows.extend(csv.DictReader(fh))
     return rows
 
 
 def _short(name):
+    """Kernel name without return type, namespaces and parameter list."""
     name = name.replace("w4a16::", "").replace("(anonymous namespace)::", "")
+    name = re.sub(r"^void ", "", name)
     return re.sub(r"\(.*$", "", name)[:70]
 
 
@@ -688,11 +694,33 @@ def _int(r, *keys):
     return 0
 
 
+def _template_args(name):
+    m = re.search(r"<(.*)>", name)
+    return [a.strip() for a in m.group(1).split(",")] if m else []
+
+
+def _matches_leg(name, e, group, dtype):
+    """Whether a trace row's kernel is the instantiation a bench entry ran:
+    the 4-bit zero-point format (0) in the leg's group and activation type."""
+    base, args = name.split("<")[0], _template_args(name)
+    bf = "true" if dtype == "bf16" else "false"
+    if base != e["kernel"] or not args:
+        return False
+    if base == "decode_kernel":       # <GROUP, MT, BF, FMT, NCOL, AWQ>
+        return args[0] == str(group) and args[2] == bf and args[3] == "0" and args[5] == "false"
+    if base == "skinny_kernel":       # <GROUP, R, BF, FMT>
+        return args[0] == str(group) and args[2] == bf and args[3] == "0"
+    if base == "prefill_kernel":      # <BM, BN, WM, WN, GROUP, BF, FMT, SK>
+        return args[4] == str(min(group, 128)) and args[5] == bf and args[6] == "0"
+    return False
+
+
 def summarize_trace(directory, bench_json):
     """Kernel trace (rocprofv3 --kernel-trace --output-format csv): launches per
-    (kernel, workgroups, threads) with median / p10 / p90 / mean duration; with
-    a bench.py output line, each group is named by the legs' matrices whose
-    launch geometry it matches, and compared with the bench's per-launch time."""
+    (kernel instantiation, workgroups, threads) with median / p10 / p90 / mean
+    duration; with a bench.py output line, the legs' matrices whose launch
+    (kernel, format, group, type and geometry) a row matches are listed under
+    it with the bench's per-launch time."""
     groups = {}
     for r in _csv_rows(directory, "kernel_trace.csv"):
         name = _short(r["Kernel_Name"])
@@ -702,23 +730,24 @@ def summarize_trace(directory, bench_json):
         grid = _int(r, "Grid_Size_X", "Grid_Size")
         key = (name, grid // max(wg_size, 1), wg_size)
         groups.setdefault(key, []).append((int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3)
-    names = {}
+    entries = []
     if bench_json:
         b = json.loads(open(bench_json).read().strip().splitlines()[-1])
         for leg in b.get("legs", {}).values():
             for M, ents in leg["by_M"].items():
                 for mname, e in ents.items():
-                    names.setdefault((e["kernel"], e["workgroups"], e["threads"]), []).append(
-                        (f"{leg['workload']} M={M} {mname}", e["us"]))
+                    entries.append((f"{leg['workload']} M={M} {mname}", e, leg["group"], leg["dtype"]))
     lines = [f"{'kernel':<62} {'wgs':>6} {'thr':>4} {'n':>6} {'median_us':>10} {'p10':>8} {'p90':>8} {'mean':>8}"]
     for (name, wgs, thr), d in sorted(groups.items(), key=lambda kv: -sum(kv[1])):
         d.sort()
         q = lambda f: d[min(len(d) - 1, int(f * len(d)))]  # noqa: E731
-        lines.append(f"{name:<62} {wgs:>6} {thr:>4} {len(d):>6} {statistics.median(d):>10.2f} {q(0.1):>8.2f} "
+        med = statistics.median(d)
+        lines.append(f"{name:<62} {wgs:>6} {thr:>4} {len(d):>6} {med:>10.2f} {q(0.1):>8.2f} "
                      f"{q(0.9):>8.2f} {statistics.fmean(d):>8.2f}")
-        for label, us in names.get((name.split("<")[0], wgs, thr), []):
-            lines.append(f"    {label}: bench {us:.2f} us per launch (events, dispatch gap included); "
-                         f"trace median {statistics.median(d):.2f} us")
+        for label, e, group, dtype in entries:
+            if e["workgroups"] == wgs and e["threads"] == thr and _matches_leg(name, e, group, dtype):
+                lines.append(f"    {label}: bench {e['us']:.2f} us per launch (events, dispatch gap included), "
+                             f"{e['us'] / med:.3f} x the trace median")
     return "\n".join(lines)
 
 
@@ -741,7 +770,8 @@ def summarize_counters(directories):
                 continue
             did = _int(r, "Dispatch_Id", "Correlation_Id")
             disp.setdefault(did, {"name": name, "c": {}})
-            disp[did]["c"][r["Counter_Name"]] = disp[did]["c"].get(r["Counter_Name"], 0.0) + float(r["Counter_Value"])
+            cn = r["Counter_Name"]
+            disp[did]["c"][cn] = disp[did]["c"].get(cn, 0.0) + float(r["Counter_Value"])
         per[d] = [disp[k] for k in sorted(disp)]
     assert seq is not None, "no counter_pass.json found"
     table = []
@@ -801,7 +831,19 @@ def write_traffic_json(table, scale, command):
             json.dump(doc, fh, indent=1)
 
 
-def print_counter_summary(table, scale):
+def print_counter_summary(table, scale, simds=1024, xcds=8):
+    counters = sorted({c for t in table for c in t["counters"]})
+    for t in table:
+        c = t["counters"]
+        # derived: share of the kernel's cycles the matrix cores were busy,
+        # SQ_VALU_MFMA_BUSY_CYCLES (all SIMDs) / (busy cycles of one XCD x SIMDs);
+        # rocprofv3 reports GRBM_GUI_ACTIVE summed over the XCDs
+        if "SQ_VALU_MFMA_BUSY_CYCLES" in c and c.get("GRBM_GUI_ACTIVE"):
+            c["mfma_busy_pct"] = 100.0 * c["SQ_VALU_MFMA_BUSY_CYCLES"] / (c["GRBM_GUI_ACTIVE"] / xcds * simds)
+        if "SQ_WAIT_ANY" in c and c.get("SQ_BUSY_CYCLES"):
+            c["wait_any_per_busy"] = c["SQ_WAIT_ANY"] / c["SQ_BUSY_CYCLES"]
+        if "SQ_LDS_BANK_CONFLICT" in c and c.get("SQ_INSTS_LDS"):
+            c["lds_conflict_per_inst"] = c["SQ_LDS_BANK_CONFLICT"] / c["SQ_INSTS_LDS"]
     counters = sorted({c for t in table for c in t["counters"]})
     if scale:
         print("counter scale (copy kernel): " + ", ".join(f"{k} x{v:.4f}" for k, v in scale.items()))
@@ -816,7 +858,7 @@ def print_counter_summary(table, scale):
             extra = (f"  {t.get('fetch_bytes', 0) / 1e6:8.2f} {t.get('write_bytes', 0) / 1e6:8.2f} {alg / 1e6:6.2f} "
                      f"{tot / alg:5.3f}")
         print(f"{t['label']:<34} {t['kernel'][:44]:<44} " +
-              " ".join(f"{t['counters'].get(c, float('nan')):>24.1f}" for c in counters) + extra)
+              " ".join(f"{t['counters'].get(c, float('nan')):>24.2f}" for c in counters) + extra)
 
 
 def main():

@@ -223,7 +223,7 @@ size_t max_lds_per_block() {
 bool decode_fits(int64_t M, int64_t N, int64_t K, int32_t group, int32_t fmt, bool awq) {
     if (M < 1 || M > kDecodeMaxM) return false;
     const DecodePlan p = decode_plan(M, N, K, group, fmt, awq);
-    return p.ok && p.lds <= max_lds_per_block();
+    return p.ok && p.lds + decode_static_lds(p) <= max_lds_per_block();
 }
 
 // Workspace of a decode launch over N rows (the split's counters and
@@ -559,7 +559,7 @@ w4a16_status w4a16_linear_group_fmt(int32_t count, const void *const *x, int32_t
             same = same && plans[p].mt == plans[0].mt && plans[p].ncol == plans[0].ncol;
         }
         size_t lds = 0;
-        for (int p = 0; p < count; ++p) lds = std::max(lds, plans[p].lds);
+        for (int p = 0; p < count; ++p) lds = std::max(lds, plans[p].lds + decode_static_lds(plans[p]));
         if (same && lds <= max_lds_per_block()) {
             hipError_t e = launch_decode_group(tab, dtype == W4A16_BF16, (int)M, (int)K, group, fmt, plans,
                                                workspace, reinterpret_cast<hipStream_t>(stream));

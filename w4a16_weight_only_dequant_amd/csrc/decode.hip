@@ -52,7 +52,8 @@ DecodePlan decode_plan(int64_t M, int64_t N, int64_t K, int32_t group, int fmt, 
         const int s_eff = (int)ceil_div(T, cols);
         const int64_t waves = cols / ncol;
         const size_t lds = (size_t)waves * (size_t)dec_lds(mt, ncol, g, fmt).total;
-        if (waves > kDecMaxWaves || lds > (size_t)kDecLdsLimit) {
+        // (the limit holds the dynamic LDS and the kernel's static buffers)
+        if (waves > kDecMaxWaves || lds + (size_t)dec_static_lds(mt) > (size_t)kDecLdsLimit) {
             if (want <= 4) return p;
             continue;
         }
@@ -66,6 +67,8 @@ DecodePlan decode_plan(int64_t M, int64_t N, int64_t K, int32_t group, int fmt, 
         return p;
     }
 }
+
+size_t decode_static_lds(const DecodePlan &plan) { return (size_t)dec_static_lds(plan.mt); }
 
 size_t decode_workspace_bytes(const DecodePlan &plan, int64_t M, int64_t N) {
     if (!plan.ok || plan.splits <= 1) return 0;

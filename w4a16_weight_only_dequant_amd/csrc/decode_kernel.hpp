@@ -104,19 +104,32 @@ __host__ __device__ constexpr int dec_meta_row_bytes(int ncol, int group, int fm
 __host__ __device__ constexpr int dec_zero_words(int ncol, int group, int fmt) {
     return fmt != kAsym4 ? 0 : (group >= 256 ? (ncol / 2 + 7) / 8 : (ncol * (128 / group) + 7) / 8);
 }
+// LDS row strides of the 16 rows' metadata: one row's run plus 16 bytes (scales,
+// records) and plus one word (zero-points), so that the 16 lanes reading the
+// same group of their 16 rows hit 16 different banks (an unpadded run of 64 or
+// 128 bytes would put them on 4 or 2 banks)
+__host__ __device__ constexpr int dec_meta_stride(int ncol, int group, int fmt) {
+    return dec_meta_row_bytes(ncol, group, fmt) + 16;
+}
+__host__ __device__ constexpr int dec_zero_stride(int ncol, int group, int fmt) {
+    return dec_zero_words(ncol, group, fmt) + 1;
+}
 // Per-wave LDS (bytes) for MT activation rows and ncol columns: activations
 // [MT][ncol * 256], activation sums [MT][units][4 slices][2] floats, the 16
-// rows' scales (or records) [16][meta_row_bytes] and zero-points [16][words],
-// and 16 spare bytes.
+// rows' scales (or records) and zero-points at the strides above, and 16 spare
+// bytes.
 struct DecLds {
     int x, sums, meta, zeros, spare, total;
 };
+// Static LDS of a workgroup: the waves' reduction buffer red[kDecMaxWaves][MT][16]
+// floats and the split's arrival flag (rounded up)
+__host__ __device__ constexpr int dec_static_lds(int mt) { return kDecMaxWaves * mt * 16 * 4 + 64; }
 __host__ __device__ constexpr DecLds dec_lds(int mt, int ncol, int group, int fmt) {
     const int upc = fmt == kKq4 ? 4 : (group >= 128 ? 1 : 128 / group);   // closing units per column
     const int x = mt * ncol * 256;
     const int sums = mt * ncol * upc * 4 * 2 * 4;
-    const int meta = 16 * dec_meta_row_bytes(ncol, group, fmt);
-    const int zeros = 16 * dec_zero_words(ncol, group, fmt) * 4;
+    const int meta = 16 * dec_meta_stride(ncol, group, fmt);
+    const int zeros = dec_zero_words(ncol, group, fmt) > 0 ? 16 * dec_zero_stride(ncol, group, fmt) * 4 : 0;
     return DecLds{0, x, x + sums, x + sums + meta, x + sums + meta + zeros, x + sums + meta + zeros + 16};
 }
 
@@ -146,6 +159,8 @@ __device__ __forceinline__ void decode_body(
     constexpr bool HI = !BF && !FT::two_planes;            // fp16 4-bit codes: 16x operands at k2,k3,k6,k7
     constexpr DecLds L = dec_lds(MT, NCOL, GROUP, FMT);
     constexpr int MRB = dec_meta_row_bytes(NCOL, GROUP, FMT);
+    constexpr int MRS = dec_meta_stride(NCOL, GROUP, FMT);  // LDS row stride of the metadata (bytes)
+    constexpr int ZRS = dec_zero_stride(NCOL, GROUP, FMT);  // LDS row stride of the zero-points (words)
     constexpr int MPARTS = (MRB + 15) / 16;                // 16-byte parts of one row's metadata
     constexpr int MJ = (MPARTS + 3) / 4;                   // metadata loads per lane (LDS path)
     constexpr int ZW = dec_zero_words(NCOL, GROUP, FMT);   // zero-point words of one row
@@ -181,8 +196,8 @@ __device__ __forceinline__ void decode_body(
     unsigned char *wl = smem + wave * L.total;
     unsigned char *xl = wl + L.x;                          // [MT][NCOL * 256]
     float *xs = reinterpret_cast<float *>(wl + L.sums);   // [MT][NCOL * UPC][4] of (B, S)
-    unsigned char *ml = wl + L.meta;                       // [16][MRB]      (LDS path)
-    uint32_t *zl = reinterpret_cast<uint32_t *>(wl + L.zeros);   // [16][ZW] (LDS path)
+    unsigned char *ml = wl + L.meta;                       // [16][MRS bytes] (LDS path)
+    uint32_t *zl = reinterpret_cast<uint32_t *>(wl + L.zeros);   // [16][ZRS words] (LDS path)
 
     // 1. activations of the slice, 16 bytes per lane and load (positions past
     // the slice re-read its last unit and are never used)
@@ -279,13 +294,13 @@ __device__ __forceinline__ void decode_body(
 #pragma unroll
         for (int j = 0; j < MJ; ++j) {
             const int part = mp + 4 * j;
-            *reinterpret_cast<uint4 *>(part < MPARTS ? ml + r * MRB + part * 16 : wl + L.spare) = mreg[j];
+            *reinterpret_cast<uint4 *>(part < MPARTS ? ml + r * MRS + part * 16 : wl + L.spare) = mreg[j];
         }
         if constexpr (ZJ > 0) {
 #pragma unroll
             for (int j = 0; j < ZJ; ++j) {
                 const int w = mp + 4 * j;
-                *(w < ZW ? zl + r * ZW + w : reinterpret_cast<uint32_t *>(wl + L.spare)) = zreg[j];
+                *(w < ZW ? zl + r * ZRS + w : reinterpret_cast<uint32_t *>(wl + L.spare)) = zreg[j];
             }
         }
     }
@@ -337,8 +352,8 @@ __device__ __forceinline__ void decode_body(
     // compiler may read the next column's operands early)
     const UnpackConsts uc = unpack_consts();
     const unsigned char *xa = xl + s * 16;
-    const unsigned char *mrow_l = ml + r * MRB;
-    const uint32_t *zrow_l = zl + r * (ZW > 0 ? ZW : 1);
+    const unsigned char *mrow_l = ml + r * MRS;
+    const uint32_t *zrow_l = zl + r * ZRS;
     float acc[MT], lo[MT], hi[MT];
 #pragma unroll
     for (int m = 0; m < MT; ++m) acc[m] = lo[m] = hi[m] = 0.0f;

@@ -82,6 +82,8 @@ struct DecodePlan {
     bool ok;
 };
 DecodePlan decode_plan(int64_t M, int64_t N, int64_t K, int32_t group, int fmt, bool awq);
+// Static LDS of the decode kernel a plan launches (beside plan.lds)
+size_t decode_static_lds(const DecodePlan &plan);
 // Workspace of a decode launch over N rows: none without a split; else the
 // blocks' arrival counters (padded to 256 bytes) and fp32 partials.
 size_t decode_workspace_bytes(const DecodePlan &plan, int64_t M, int64_t N);
