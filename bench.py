@@ -103,6 +103,8 @@ def parse():
     p.add_argument("--summarize-trace", metavar="DIR", default=None)
     p.add_argument("--summarize-counters", metavar="DIR", nargs="+", default=None)
     p.add_argument("--bench-json", default=None, help="a bench.py output line (launch keys of the legs)")
+    p.add_argument("--crossover", action="store_true",
+                   help="time every kernel at M = 1..2048 on two shapes and check the dispatch's choice")
     return p.parse_args()
 
 
@@ -515,6 +517,78 @@ def format_legs(dev, steps, warmup, launches):
     return legs
 
 
+CROSSOVER_MS = (1, 2, 3, 4, 6, 8, 12, 16, 24, 32, 48, 64, 96, 128, 192, 256, 384, 512, 1024, 2048)
+CROSSOVER_SHAPES = ((15360, 5120), (13824, 5120))   # fused QKV and FFN up of the 13B shapes, group 128
+
+
+def time_launches(fn, copies, n):
+    """Microseconds per launch of fn(copy, stream): one graph of n launches
+    rotating over the weight copies, replayed after a 50 ms warm-up, HIP
+    events around the timed replay."""
+    import torch
+    fn(0, None)
+    torch.cuda.synchronize()
+    cap = torch.cuda.Stream()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(cap):
+        with torch.cuda.graph(g, stream=cap):
+            for i in range(n):
+                fn(i % copies, cap)
+    t0 = time.perf_counter()
+    while (time.perf_counter() - t0) * 1e3 < WARM_MS:
+        g.replay()
+        torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    g.replay()
+    e1.record()
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) * 1e3 / n
+
+
+def crossover(dev):
+    """The batch-size crossover between the decode kernel (M <= 8), the
+    small-batch matrix-core kernel and the tiled GEMM: each kernel that takes
+    the shape, timed per launch (cold weights: copies past the MALL) at every
+    M of CROSSOVER_MS on the fused-QKV (15360 x 5120) and FFN-up (13824 x 5120)
+    shapes, fp16 and bf16, and whether w4a16_linear's choice is the fastest
+    (within 3 %)."""
+    import torch
+
+    import w4a16_weight_only_dequant_amd as w4
+    import workloads as wl
+    rows = []
+    for (N, K) in CROSSOVER_SHAPES:
+        w = torch.from_numpy(wl.random_weights(N + K, N, K)).to(dev)
+        pw = w4.pack(w, 128)
+        del w
+        copies = max(1, -(-3 * MALL_BYTES // pw.nbytes()))
+        sets = [pw] + [w4.PackedWeight(pw.qweight.clone(), pw.scales.clone(), pw.zeros.clone(), N, K, 128)
+                       for _ in range(copies - 1)]
+        for dtype in ("f16", "bf16"):
+            tdt = torch.float16 if dtype == "f16" else torch.bfloat16
+            for M in CROSSOVER_MS:
+                x = torch.randn(M, K, device=dev).to(tdt)
+                y = torch.empty(M, N, device=dev, dtype=tdt)
+                kernels = (["gemv"] if M <= 8 else []) + (["small_batch"] if M <= 512 else []) + ["tiled"]
+                times = {}
+                for kname in kernels:
+                    ws = w4.Workspace(dev)
+                    n = 240 if M <= 64 else (120 if M <= 512 else 60)
+                    times[kname] = round(time_launches(
+                        lambda c, st: w4.linear_run(kname, x, sets[c], out=y, workspace=ws, stream=st), copies, n), 2)
+                chosen = w4.linear_kernel(M, N, K, 128, tdt)
+                best = min(times, key=times.get)
+                rows.append({"N": N, "K": K, "dtype": dtype, "M": M, "us": times, "linear_chooses": chosen,
+                             "fastest": best, "chosen_within_3pct": times[chosen] <= 1.03 * times[best]})
+                print(f"N={N} K={K} {dtype} M={M}: " + " ".join(f"{k} {v:.2f}" for k, v in times.items()) +
+                      f" | linear: {chosen}" + ("" if rows[-1]["chosen_within_3pct"] else "  (NOT the fastest)"),
+                      file=sys.stderr, flush=True)
+        del sets, pw
+        torch.cuda.empty_cache()
+    return rows
+
+
 def cpu_model():
     try:
         for line in open("/proc/cpuinfo"):
@@ -893,6 +967,12 @@ def main():
 
     if args.counter_pass:
         counter_pass(args.counter_pass, args.reps, legs_ids)
+        return
+
+    if args.crossover:
+        rows = crossover(dev)
+        print(json.dumps({"crossover": rows, "all_chosen_within_3pct": all(r["chosen_within_3pct"] for r in rows),
+                          "device": device_info(dev)}))
         return
 
     if args.workload:   # one workload's leg only (batch sweeps): no headline, no oracle

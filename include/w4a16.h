@@ -189,7 +189,7 @@ w4a16_status w4a16_packed_bytes_fmt(int64_t N, int64_t K, int32_t group, int32_t
  * needs on the current device, in any weight format. Host-only (queries the
  * device's compute-unit count once). The decode kernel (M <= 8) needs some
  * when it splits K: an 8-byte counter per 16-row block (padded to 256 bytes)
- * and M x 16 fp32 partials per row block and split. The tiled GEMM (M > 256) needs
+ * and M x 16 fp32 partials per row block and split. The tiled GEMM (M > 128) needs
  * some when its last round of 256 x 256 (or 128 / 64-row) output tiles would
  * be at most half full on the device's compute units: it then splits the
  * last two rounds' tiles by K over one workgroup per compute unit
@@ -259,7 +259,7 @@ w4a16_status w4a16_gemv_fmt(const void *x, int32_t dtype, const void *qweight,
                             void *workspace, size_t workspace_bytes, void *stream);
 
 /* Matrix-core GEMM for any M (M*K < 2^34); the workspace is sized by
- * w4a16_workspace_bytes (W4A16_ERR_WORKSPACE when it is smaller). M <= 256: the packed weights
+ * w4a16_workspace_bytes (W4A16_ERR_WORKSPACE when it is smaller). M <= 128: the packed weights
  * stream through registers as in the GEMV, and each unpacked dword feeds one
  * 16x16x32 MFMA per 16-row tile of x (exact integers q - z, group scale on the
  * fp32 sums; one workgroup per tile and group of row blocks). Larger M:
@@ -297,7 +297,7 @@ w4a16_status w4a16_linear_fmt(const void *x, int32_t dtype, const void *qweight,
  * problem must pass w4a16_linear's checks, and no y[p] may overlap any buffer
  * of any problem. The workspace is sized by w4a16_group_workspace_bytes. At
  * M <= w4a16_gemv_max_m all problems run in one launch of the decode kernel,
- * each with the split a call on it alone would use; for M up to 256 in one
+ * each with the split a call on it alone would use; for M up to 128 in one
  * launch of the small-batch matrix-core kernel; either pays the fixed cost of
  * a launch (the ramp-up and drain that dominate small decode layers) once.
  * For larger M it enqueues one tiled GEMM per problem, one after the other,
@@ -317,11 +317,28 @@ w4a16_status w4a16_linear_group_fmt(int32_t count, const void *const *x, int32_t
                                     const int64_t *N, int64_t K, int32_t group, int32_t fmt,
                                     void *workspace, size_t workspace_bytes, void *stream);
 
+/* A kernel run by choice instead of w4a16_linear's dispatch: kernel 0 = the
+ * decode kernel (w4a16_gemv's range), 1 = the small-batch matrix-core kernel,
+ * 2 = the tiled matrix-core GEMM (with its stream-K split where its plan has
+ * one), each at any M it takes; W4A16_ERR_INVALID_ARG for another kernel
+ * number or a shape the kernel does not take. For measuring the dispatch's
+ * crossovers and for callers that pin a kernel. Every other argument and the
+ * results are those of w4a16_linear_fmt (kernel 1 and 2 at M <= 128 and
+ * above give w4a16_gemm_fmt's bits where w4a16_gemm_fmt runs that kernel).
+ * Workspace: w4a16_kernel_workspace_bytes (host-only). */
+w4a16_status w4a16_kernel_workspace_bytes(int32_t kernel, int64_t M, int64_t N, int64_t K,
+                                          int32_t group, int32_t fmt, size_t *bytes);
+w4a16_status w4a16_linear_run_fmt(int32_t kernel, const void *x, int32_t dtype,
+                                  const void *qweight, const void *scales, const void *zeros,
+                                  void *y, int64_t M, int64_t N, int64_t K, int32_t group,
+                                  int32_t fmt, void *workspace, size_t workspace_bytes,
+                                  void *stream);
+
 /* Largest M that w4a16_linear may send to the GEMV kernel. */
 int32_t w4a16_gemv_max_m(void);
 
 /* The kernel w4a16_linear picks for this shape on the current device:
- * 0 = decode GEMV, 1 = small-batch matrix-core kernel (M <= 256),
+ * 0 = decode GEMV, 1 = small-batch matrix-core kernel (M <= 128),
  * 2 = tiled matrix-core GEMM; -1 for M = 0 (no kernel runs) and for
  * arguments w4a16_linear would reject.
  * Host-only (queries the device's LDS size once). */

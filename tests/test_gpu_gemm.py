@@ -1,5 +1,5 @@
 """GPU parity of the matrix-core kernels (w4a16_gemm): the small-batch kernel
-(M <= 256, weights streamed through registers, x in 16-row tiles) and the
+(M <= 128, weights streamed through registers, x in 16-row tiles) and the
 LDS-tiled kernel (larger M, three tile shapes). Every output within
 2e-3 * sum|x * w_hat| + 1e-5 (+ the output rounding) of the fp64 oracle, plus
 exact special cases."""
@@ -25,8 +25,8 @@ def _gemm(x_bits, dtype, pw):
 # last 16-row block (N % 16 = 8) and N not a multiple of the 256-wide tile.
 SHAPES = [(8, 32, 32), (72, 160, 32), (200, 96, 32), (136, 256, 64), (264, 320, 64), (328, 640, 128),
           (1000, 1024, 64), (4104, 4096, 128), (520, 8192, 32)]
-SKINNY_M = [1, 2, 5, 16, 17, 37, 64, 100, 256]
-TILED_M = [257, 300, 520]
+SKINNY_M = [1, 2, 5, 16, 17, 37, 64, 100, 128]
+TILED_M = [129, 256, 300, 520]
 
 
 def _small(N, K, group):
@@ -37,7 +37,7 @@ def _small(N, K, group):
 @pytest.mark.parametrize("dtype", ["f16", "bf16"])
 @pytest.mark.parametrize("M", SKINNY_M + TILED_M)
 def test_gemm_small_shapes(N, K, group, dtype, M):
-    if N * K >= 4096 * 4096 and M in (5, 17, 64, 100, 256, 520):
+    if N * K >= 4096 * 4096 and M in (5, 17, 64, 100, 128, 129, 520):
         pytest.skip("covered by the other batch sizes at this shape")
     w, o, pw = _small(N, K, group)
     x = wl.random_activations(N * 31 + K + M, M, K, dtype)
@@ -116,7 +116,7 @@ def test_linear_dispatch_matches_kernels():
     import torch
     N, K, group = 1000, 1024, 64
     w, o, pw = _small(N, K, group)
-    for M in (1, 2, 3, 16, 17, 256, 257, 300):
+    for M in (1, 2, 3, 16, 17, 128, 129, 300):
         x = H.to_device_bits(wl.random_activations(M, M, K, "f16"), "f16")
         y = H.lib().linear(x, pw)
         ref_fn = H.lib().gemv if H.lib().linear_kernel(M, N, K, group) == "gemv" else H.lib().gemm
@@ -170,3 +170,34 @@ def test_gemm_full_size_prefill_sampled_columns():
     y = _gemm(x, wlc.dtype, pw)
     H.check_against_oracle(y, x, wlc.dtype, o, group, cols=cols)
     H.drop((cfg, mat))
+
+
+@pytest.mark.parametrize("M", [1, 5, 40, 300])
+def test_linear_run_each_kernel(M):
+    """w4a16_linear_run_fmt: every kernel that takes the shape gives a result
+    within the bar of the oracle, the bits of w4a16_linear where the dispatch
+    picks the same kernel; the decode kernel refuses M > 8 and an unknown
+    kernel number is refused."""
+    import torch
+    w4 = H.lib()
+    N, K, group = 520, 2048, 64
+    w, o, pw = H.prepared(("small", N, K, group), lambda: wl.random_weights(N + K, N, K), group)
+    xb = wl.random_activations(M + 77, M, K, "bf16")
+    x = H.to_device_bits(xb, "bf16")
+    y_lin = w4.linear(x, pw)
+    chosen = w4.linear_kernel(M, N, K, group, torch.bfloat16)
+    for kname in (["gemv"] if M <= 8 else []) + ["small_batch", "tiled"]:
+        y = w4.linear_run(kname, x, pw)
+        torch.cuda.synchronize()
+        H.check_against_oracle(y, xb, "bf16", o, group)
+        if kname == chosen:
+            assert torch.equal(y.view(torch.int16), y_lin.view(torch.int16)), kname
+    if M > 8:
+        with pytest.raises(w4.W4A16Error):
+            w4.linear_run("gemv", x, pw)
+    y = torch.full((M, N), 1.0, dtype=torch.bfloat16, device="cuda")
+    st = w4.raw().w4a16_linear_run_fmt(7, x.data_ptr(), 1, pw.qweight.data_ptr(), pw.scales.data_ptr(),
+                                       pw.zeros_ptr(), y.data_ptr(), M, N, K, group, 0, None, 0, None)
+    assert st == 1
+    torch.cuda.synchronize()
+    assert bool((y == 1.0).all())

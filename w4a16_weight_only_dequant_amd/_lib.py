@@ -73,6 +73,9 @@ _SIGS = {
     "w4a16_awq_workspace_bytes": (ctypes.c_int, [_i64, _i64, _i64, _i32, _i32, _i32, _szp]),
     "w4a16_linear_awq": (ctypes.c_int, [_vp, _i32, _vp, _vp, _vp, _vp, _vp, _i64, _i64, _i64, _i32, _i32, _vp, _sz,
                                         _vp]),
+    "w4a16_kernel_workspace_bytes": (ctypes.c_int, [_i32, _i64, _i64, _i64, _i32, _i32, _szp]),
+    "w4a16_linear_run_fmt": (ctypes.c_int, [_i32, _vp, _i32, _vp, _vp, _vp, _vp, _i64, _i64, _i64, _i32, _i32, _vp,
+                                            _sz, _vp]),
     "w4a16_linear_noalloc": (ctypes.c_int, [_vp, _i32, _vp, _vp, _vp, _vp, _i64, _i64, _i64, _i32, _i32, _vp]),
     "w4a16_measure_stream_read": (ctypes.c_int, [_vp, _sz, _vp, _i32, _vp]),
     "w4a16_measure_copy": (ctypes.c_int, [_vp, _vp, _sz, _vp]),
@@ -357,6 +360,27 @@ def linear_group(xs, pws, outs=None, workspace=None, stream=None):
         arr([y.data_ptr() for y in ys]), M, (ctypes.c_int64 * count)(*[p.N for p in pws]), K, group,
         _fmt_code(pws[0].fmt), ws.data_ptr() if ws is not None else None, ws.numel() if ws is not None else 0, _stream_ptr(stream)))
     return ys
+
+
+def linear_run(kernel: str, x, pw, out=None, workspace=None, stream=None):
+    """The named kernel ("gemv", "small_batch" or "tiled") instead of
+    w4a16_linear's dispatch (w4a16_linear_run_fmt)."""
+    code = LINEAR_KERNELS.index(kernel)
+    if x.dim() != 2 or x.shape[1] != pw.K or not x.is_cuda:
+        raise ValueError(f"x must be a CUDA tensor [M][{pw.K}]")
+    x = x.contiguous()
+    M = x.shape[0]
+    y = _output(out, M, pw.N, x)
+    nb = _sz()
+    _check("w4a16_kernel_workspace_bytes", _lib.w4a16_kernel_workspace_bytes(code, M, pw.N, pw.K, pw.group,
+                                                                             _fmt_code(pw.fmt), ctypes.byref(nb)))
+    strm = stream if stream is not None else torch.cuda.current_stream(x.device)
+    ws = (workspace or _default_workspace(x.device, strm)).get(nb.value, strm)
+    _check("w4a16_linear_run_fmt", _lib.w4a16_linear_run_fmt(
+        code, x.data_ptr(), _dtype_code(x), pw.qweight.data_ptr(), pw.scales.data_ptr(), pw.zeros_ptr(),
+        y.data_ptr(), M, pw.N, pw.K, pw.group, _fmt_code(pw.fmt), ws.data_ptr() if ws is not None else None,
+        ws.numel() if ws is not None else 0, _stream_ptr(stream)))
+    return y
 
 
 def linear_noalloc(x, pw, out, stream=None):

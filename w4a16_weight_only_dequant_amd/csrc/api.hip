@@ -453,21 +453,61 @@ w4a16_status w4a16_gemv(const void *x, int32_t dtype, const void *qweight, const
                           workspace_bytes, stream);
 }
 
-w4a16_status w4a16_gemm_fmt(const void *x, int32_t dtype, const void *qweight, const void *scales,
-                            const void *zeros, void *y, int64_t M, int64_t N, int64_t K, int32_t group, int32_t fmt,
-                            void *workspace, size_t workspace_bytes, void *stream) {
+// The matrix-core kernels with a plan of kind `kind` (-1: the dispatch's).
+static w4a16_status run_gemm(int kind, const void *x, int32_t dtype, const void *qweight, const void *scales,
+                      const void *zeros, void *y, int64_t M, int64_t N, int64_t K, int32_t group, int32_t fmt,
+                      void *workspace, size_t workspace_bytes, void *stream) {
     const size_t need = (M >= 1 && M <= (1LL << 24) && shape_ok(N, K, group))
-                            ? gemm_need(M, N, K, group) : 0;
+                            ? prefill_workspace_bytes(gemm_plan(M, N, K, group, kind)) : 0;
     w4a16_status st = check_linear(x, dtype, qweight, scales, zeros, y, M, N, K, group, fmt, workspace,
                                    workspace_bytes, need);
     if (st != W4A16_OK || M == 0) return st;
     st = check_device();
     if (st != W4A16_OK) return st;
-    GemmPlan plan = gemm_plan(M, N, K, group);
+    GemmPlan plan = gemm_plan(M, N, K, group, kind);
     if (prefill_workspace_bytes(plan) > need) return W4A16_ERR_WORKSPACE;   // (the same plan: never)
     hipError_t e = launch_gemm(x, dtype == W4A16_BF16, qweight, scales, zeros, y, (int)M, (int)N,
                                (int)K, group, fmt, plan, workspace, reinterpret_cast<hipStream_t>(stream));
     return e == hipSuccess ? W4A16_OK : W4A16_ERR_HIP;
+}
+
+w4a16_status w4a16_gemm_fmt(const void *x, int32_t dtype, const void *qweight, const void *scales,
+                            const void *zeros, void *y, int64_t M, int64_t N, int64_t K, int32_t group, int32_t fmt,
+                            void *workspace, size_t workspace_bytes, void *stream) {
+    return run_gemm(-1, x, dtype, qweight, scales, zeros, y, M, N, K, group, fmt, workspace, workspace_bytes, stream);
+}
+
+w4a16_status w4a16_kernel_workspace_bytes(int32_t kernel, int64_t M, int64_t N, int64_t K, int32_t group,
+                                          int32_t fmt, size_t *bytes) {
+    if (!bytes || M < 0 || M > (1LL << 24) || !shape_ok(N, K, group) || !fmt_group_ok(fmt, group))
+        return W4A16_ERR_INVALID_ARG;
+    switch (kernel) {
+        case 0:
+            if (M > kDecodeMaxM) return W4A16_ERR_INVALID_ARG;
+            *bytes = M == 0 ? 0 : decode_need(M, N, K, group, fmt, false);
+            return W4A16_OK;
+        case 1:
+        case 2:
+            *bytes = M == 0 ? 0 : prefill_workspace_bytes(gemm_plan(M, N, K, group, kernel - 1));
+            return W4A16_OK;
+        default: return W4A16_ERR_INVALID_ARG;
+    }
+}
+
+w4a16_status w4a16_linear_run_fmt(int32_t kernel, const void *x, int32_t dtype, const void *qweight,
+                                  const void *scales, const void *zeros, void *y, int64_t M, int64_t N, int64_t K,
+                                  int32_t group, int32_t fmt, void *workspace, size_t workspace_bytes,
+                                  void *stream) {
+    switch (kernel) {
+        case 0:
+            return w4a16_gemv_fmt(x, dtype, qweight, scales, zeros, y, M, N, K, group, fmt, workspace,
+                                  workspace_bytes, stream);
+        case 1:
+        case 2:
+            return run_gemm(kernel - 1, x, dtype, qweight, scales, zeros, y, M, N, K, group, fmt, workspace,
+                            workspace_bytes, stream);
+        default: return W4A16_ERR_INVALID_ARG;
+    }
 }
 
 w4a16_status w4a16_testing_gemm_expire(const void *x, int32_t dtype, const void *qweight, const void *scales,

@@ -6,12 +6,12 @@
 
 namespace w4a16 {
 
-GemmPlan gemm_plan(int64_t M, int64_t N, int64_t K, int32_t group) {
+GemmPlan gemm_plan(int64_t M, int64_t N, int64_t K, int32_t group, int kind) {
     const int forced_waves = tuning_knob("W4A16_SKINNY_WAVES", 0);
     const int forced_r = tuning_knob("W4A16_SKINNY_R", 0);
     const int skinny_max = tuning_knob("W4A16_SKINNY_MAX_M", kSkinnyMaxM);
     GemmPlan p{};
-    if (M <= skinny_max) {
+    if (kind == 0 || (kind < 0 && M <= skinny_max)) {
         p.kind = 0;
         const int64_t columns = ceil_div(K / kChunk, kColChunks);
         // waves splitting K: eight (two per SIMD) up to M = 16, where each

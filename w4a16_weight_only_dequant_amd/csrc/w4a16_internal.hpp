@@ -91,7 +91,7 @@ size_t decode_workspace_bytes(const DecodePlan &plan, int64_t M, int64_t N);
 // Plan for the matrix-core kernels: kind 0 streams the weights through
 // registers for M <= kSkinnyMaxM (16-row MFMA tiles of activations, one per
 // workgroup), kind 1 is the LDS-tiled GEMM for everything larger.
-constexpr int kSkinnyMaxM = 256;   // measured crossover to the tiled kernel
+constexpr int kSkinnyMaxM = 128;   // measured crossover to the tiled kernel (M = 128: a tie; 192: 149 against 106 us)
 enum { kTile64x256 = 0, kTile128x256 = 1, kTile256x256 = 2, kTile256x256w8 = 3 };
 struct GemmPlan {
     int kind;          // 0 = skinny, 1 = tiled
@@ -103,7 +103,9 @@ struct GemmPlan {
     int sk_expire_test;   // 1: consumers wait for a token no producer writes (exercises the expiry path)
 };
 
-GemmPlan gemm_plan(int64_t M, int64_t N, int64_t K, int32_t group);
+// kind: -1 the dispatch's choice (small-batch up to kSkinnyMaxM rows), 0 or 1
+// that kind whatever M is
+GemmPlan gemm_plan(int64_t M, int64_t N, int64_t K, int32_t group, int kind = -1);
 // Compute units of the current device (cached per device; 0 if unknown).
 int device_cu_count();
 // Tile rows / columns of a tiled kind.
