@@ -398,7 +398,8 @@ w4a16_status w4a16_linear_awq(const void *x, int32_t dtype, const float *act_mul
 
 /* For callers that cannot allocate device memory (code under HIP graph
  * capture, tight serving loops, harnesses that forbid it): w4a16_linear_fmt
- * with no workspace argument. The tiled GEMM's stream-K partials and flags go
+ * with no workspace argument. The tiled GEMM's stream-K partials and flags
+ * (and the decode kernel's partials and counters where its plan splits K) go
  * to a static device array of W4A16_NOALLOC_SCRATCH_BYTES that each device
  * holds for the life of the process; the call makes no allocation of any
  * kind. It needs w4a16_init to have run on the current device

@@ -117,20 +117,24 @@ __device__ __forceinline__ void skinny_body(const uint16_t *__restrict__ x, cons
         uint4 rec[R], rec_hi[R], kq[R];
         ColScales<GPC> sc[R];
         uint32_t zw[R];
+        int zsh;   // bit offset of the column's first zero-point in zw
         int par;   // column parity: which half of the super-block (kq4)
     };
     // metadata slot of column t: t >> mshift (group 256: one slot per two
-    // columns); its zero-points come pre-shifted to bit 0
+    // columns). The zero-point word is kept as loaded and shifted where it is
+    // used: a shift here would make the wave wait for the load at once, and
+    // (loads complete in order) for every prefetch issued before it.
     auto load_meta = [&](int t, Buf &u) {
         const int tm = t >> mshift;
         u.par = t & 1;
+        u.zsh = 4 * ((tm * GPC) & 7);
 #pragma unroll
         for (int i = 0; i < R; ++i) {
             if constexpr (FT::kquant) {
                 u.kq[i] = kq_row[i][t >> 1];
             } else {
                 u.sc[i] = sc_row[i][tm];
-                if constexpr (FT::has_zeros) u.zw[i] = zp_row[i][(tm * GPC) >> 3] >> (4 * ((tm * GPC) & 7));
+                if constexpr (FT::has_zeros) u.zw[i] = zp_row[i][(tm * GPC) >> 3];
                 else u.zw[i] = 0;
             }
         }
@@ -170,9 +174,8 @@ __device__ __forceinline__ void skinny_body(const uint16_t *__restrict__ x, cons
             if constexpr (FT::kquant) sx = mfma16x16x32<BF>(xa, ones, sx);   // sum x for the minimum
         }
     };
-    auto zero_of = [&](uint32_t zw, int i, int e) -> uint32_t {
-        (void)i;
-        if constexpr (FT::has_zeros) return (zw >> (4 * e)) & 0xFu;
+    auto zero_of = [&](uint32_t zw, int zsh, int e) -> uint32_t {
+        if constexpr (FT::has_zeros) return (zw >> (zsh + 4 * e)) & 0xFu;
         else return FT::fixed_zero;
     };
     auto close_group = [&](int i, float sc, uint32_t z, f4_t &g, f4_t &sx) {
@@ -219,7 +222,7 @@ __device__ __forceinline__ void skinny_body(const uint16_t *__restrict__ x, cons
 #pragma unroll
             for (int j = 0; j < kColChunks; ++j) {
                 const int e = j / CPG;
-                const uint32_t z = zero_of(u.zw[i], i, e);
+                const uint32_t z = zero_of(u.zw[i], u.zsh, e);
                 chunk(u.xa[j], dws[j], dwh[j], z, g, sx);
                 if ((j + 1) % CPG == 0) close_group(i, u.sc[i].get(e), z, g, sx);
             }
@@ -260,7 +263,7 @@ __device__ __forceinline__ void skinny_body(const uint16_t *__restrict__ x, cons
             f4_t g = {0.0f, 0.0f, 0.0f, 0.0f}, sx = {0.0f, 0.0f, 0.0f, 0.0f};
             for (int j = 0; j < nc; ++j) {
                 const int e = j / CPG;
-                const uint32_t z = zero_of(u.zw[i], i, e);
+                const uint32_t z = zero_of(u.zw[i], u.zsh, e);
                 chunk(xrow[(size_t)(tl * kColChunks + j) * 4], col[j], FT::two_planes ? colh[j] : 0u, z, g, sx);
                 if ((j + 1) % CPG == 0 || j == nc - 1) close_group(i, u.sc[i].get(e), z, g, sx);
             }

@@ -297,7 +297,8 @@ __global__ __launch_bounds__(64 * WM * WN) __attribute__((amdgpu_waves_per_eu(WM
             uint4 rec[WREC], rec_hi[WREC];   // rec_hi: high-nibble plane of 8-bit codes
             uint4 kq[WREC];                  // kq4: the super-block record of the column's row
             ColScales<GPC> sc[WREC];
-            uint32_t zw[WREC];
+            uint32_t zw[WREC];               // zero-point words as loaded
+            int zsh;                         // bit offset of the column's first zero-point in zw
             int par;                         // kq4: column parity (half of the super-block)
         };
         // (with `full` known true the column's loads have no branch: whole-tile
@@ -327,14 +328,17 @@ __global__ __launch_bounds__(64 * WM * WN) __attribute__((amdgpu_waves_per_eu(WM
                     }
                 }
                 // metadata slot of column t: t >> mshift (group 256: one slot per
-                // two columns); its zero-points come pre-shifted to bit 0
+                // two columns); the zero-point word is shifted where it is used
+                // (a shift here would wait for the load at once, and for every
+                // load issued before it)
                 const uint32_t tm = (uint32_t)(t >> mshift);
+                u.zsh = (int)(4 * ((tm * GPC) & 7));
                 if constexpr (FT::kquant) {
                     u.kq[i] = kqrec[soff[i] + (uint32_t)(t >> 1)];
                 } else {
                     u.sc[i] = scol[soff[i] + tm];
                     if constexpr (FT::has_zeros)
-                        u.zw[i] = zeros[zoff[i] + ((tm * GPC) >> 3)] >> (4 * ((tm * GPC) & 7));
+                        u.zw[i] = zeros[zoff[i] + ((tm * GPC) >> 3)];
                     else
                         u.zw[i] = 0;
                 }
@@ -349,7 +353,7 @@ __global__ __launch_bounds__(64 * WM * WN) __attribute__((amdgpu_waves_per_eu(WM
                 const uint32_t dh = h ? (jj ? u.rec_hi[i].w : u.rec_hi[i].z) : (jj ? u.rec_hi[i].y : u.rec_hi[i].x);
                 const int e = (2 * h + jj) / CPG;
                 uint32_t z = FT::fixed_zero;
-                if constexpr (FT::has_zeros) z = (u.zw[i] >> (4 * e)) & 0xFu;
+                if constexpr (FT::has_zeros) z = (u.zw[i] >> (u.zsh + 4 * e)) & 0xFu;
                 uint4 v;
                 if constexpr (FT::kquant) {
                     v = dequant_kq<BF>(dw, kq_sub(kq_half(u.kq[i], u.par != 0), 2 * h + jj), uc);
