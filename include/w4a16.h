@@ -189,14 +189,18 @@ w4a16_status w4a16_packed_bytes_fmt(int64_t N, int64_t K, int32_t group, int32_t
  * needs on the current device, in any weight format. Host-only (queries the
  * device's compute-unit count once). The decode kernel (M <= 8) needs some
  * when it splits K: an 8-byte counter per 16-row block (padded to 256 bytes)
- * and M x 16 fp32 partials per row block and split. The tiled GEMM (M > 128) needs
+ * and M x 16 fp32 partials per row block and split. The tiled GEMM (M > 32) needs
  * some when its last round of 256 x 256 (or 128 / 64-row) output tiles would
  * be at most half full on the device's compute units: it then splits the
  * last two rounds' tiles by K over one workgroup per compute unit
  * (stream-K), and a tile's two workgroups hand an fp32 partial tile and an
  * 8-byte flag over through the workspace: BM x 256 x 4 + 8 bytes per compute
- * unit (about 64 MiB on 256 compute units). With 0 bytes the compute calls
- * accept a NULL workspace.
+ * unit (about 64 MiB on 256 compute units). It also needs some when its tiles
+ * fill at most half of the compute units (mid-size batches): each tile's K
+ * is then split over S workgroups (S up to 16), which leave fp32 partial
+ * tiles, the last to arrive adding them in split order: tiles x S x
+ * BM x 256 x 4 bytes plus an 8-byte counter per tile (padded to 256 bytes),
+ * under 64 MiB. With 0 bytes the compute calls accept a NULL workspace.
  * The workspace is device memory owned by the caller, 16-byte aligned, and
  * must not overlap any argument of the call. Its contents need no
  * initialisation (each launch marks its hand-overs with a 64-bit token mixed
@@ -259,7 +263,7 @@ w4a16_status w4a16_gemv_fmt(const void *x, int32_t dtype, const void *qweight,
                             void *workspace, size_t workspace_bytes, void *stream);
 
 /* Matrix-core GEMM for any M (M*K < 2^34); the workspace is sized by
- * w4a16_workspace_bytes (W4A16_ERR_WORKSPACE when it is smaller). M <= 128: the packed weights
+ * w4a16_workspace_bytes (W4A16_ERR_WORKSPACE when it is smaller). M <= 32: the packed weights
  * stream through registers as in the GEMV, and each unpacked dword feeds one
  * 16x16x32 MFMA per 16-row tile of x (exact integers q - z, group scale on the
  * fp32 sums; one workgroup per tile and group of row blocks). Larger M:
@@ -323,7 +327,7 @@ w4a16_status w4a16_linear_group_fmt(int32_t count, const void *const *x, int32_t
  * one), each at any M it takes; W4A16_ERR_INVALID_ARG for another kernel
  * number or a shape the kernel does not take. For measuring the dispatch's
  * crossovers and for callers that pin a kernel. Every other argument and the
- * results are those of w4a16_linear_fmt (kernel 1 and 2 at M <= 128 and
+ * results are those of w4a16_linear_fmt (kernel 1 and 2 at M <= 32 and
  * above give w4a16_gemm_fmt's bits where w4a16_gemm_fmt runs that kernel).
  * Workspace: w4a16_kernel_workspace_bytes (host-only). */
 w4a16_status w4a16_kernel_workspace_bytes(int32_t kernel, int64_t M, int64_t N, int64_t K,
@@ -338,7 +342,7 @@ w4a16_status w4a16_linear_run_fmt(int32_t kernel, const void *x, int32_t dtype,
 int32_t w4a16_gemv_max_m(void);
 
 /* The kernel w4a16_linear picks for this shape on the current device:
- * 0 = decode GEMV, 1 = small-batch matrix-core kernel (M <= 128),
+ * 0 = decode GEMV, 1 = small-batch matrix-core kernel (M <= 32),
  * 2 = tiled matrix-core GEMM; -1 for M = 0 (no kernel runs) and for
  * arguments w4a16_linear would reject.
  * Host-only (queries the device's LDS size once). */

@@ -97,6 +97,12 @@ def check_every_output(y_gpu, x_bits, dtype, o, group, chunk=2048):
     (the fp64 product of a full prefill shape is ~1.5e11 MACs)."""
     N = int(y_gpu.shape[1])
     worst = bare = 0.0
+    if o.get("fmt") == "kq4":   # (super-block records: the sliced oracle of check_against_oracle)
+        for c0 in range(0, N, chunk):
+            cols = np.arange(c0, min(N, c0 + chunk))
+            worst = max(worst, check_against_oracle(y_gpu, x_bits, dtype, o, group, cols=cols, quiet=True))
+        print(f"[parity] every output of {tuple(y_gpu.shape)}: max ratio {worst:.4f}", flush=True)
+        return worst
     for c0 in range(0, N, chunk):
         cols = np.arange(c0, min(N, c0 + chunk))
         y = y_to_f64(y_gpu[:, c0:c0 + len(cols)])

@@ -1,5 +1,5 @@
 """GPU parity of the matrix-core kernels (w4a16_gemm): the small-batch kernel
-(M <= 128, weights streamed through registers, x in 16-row tiles) and the
+(M <= 32, weights streamed through registers, x in 16-row tiles) and the
 LDS-tiled kernel (larger M, three tile shapes). Every output within
 2e-3 * sum|x * w_hat| + 1e-5 (+ the output rounding) of the fp64 oracle, plus
 exact special cases."""
@@ -25,8 +25,8 @@ def _gemm(x_bits, dtype, pw):
 # last 16-row block (N % 16 = 8) and N not a multiple of the 256-wide tile.
 SHAPES = [(8, 32, 32), (72, 160, 32), (200, 96, 32), (136, 256, 64), (264, 320, 64), (328, 640, 128),
           (1000, 1024, 64), (4104, 4096, 128), (520, 8192, 32)]
-SKINNY_M = [1, 2, 5, 16, 17, 37, 64, 100, 128]
-TILED_M = [129, 256, 300, 520]
+SKINNY_M = [1, 2, 5, 16, 17, 32]
+TILED_M = [33, 37, 64, 100, 128, 129, 256, 300, 520]
 
 
 def _small(N, K, group):
@@ -116,7 +116,7 @@ def test_linear_dispatch_matches_kernels():
     import torch
     N, K, group = 1000, 1024, 64
     w, o, pw = _small(N, K, group)
-    for M in (1, 2, 3, 16, 17, 128, 129, 300):
+    for M in (1, 2, 3, 16, 17, 32, 33, 128, 129, 300):
         x = H.to_device_bits(wl.random_activations(M, M, K, "f16"), "f16")
         y = H.lib().linear(x, pw)
         ref_fn = H.lib().gemv if H.lib().linear_kernel(M, N, K, group) == "gemv" else H.lib().gemm

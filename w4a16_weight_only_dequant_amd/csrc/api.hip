@@ -324,8 +324,8 @@ int32_t w4a16_linear_launch_shape(int64_t M, int64_t N, int64_t K, int32_t group
             th = 64 * p.waves;
         } else {
             kind = 2;
-            wg = p.sk_wgs > 0 ? (int64_t)p.dp_tiles + p.sk_wgs
-                              : ceil_div(M, tile_rows(p.tile)) * ceil_div(N, kTileCols);
+            const int64_t tiles = ceil_div(M, tile_rows(p.tile)) * ceil_div(N, kTileCols);
+            wg = p.sk_wgs > 0 ? (int64_t)p.dp_tiles + p.sk_wgs : (p.splits > 1 ? tiles * p.splits : tiles);
             th = p.tile == kTile256x256w8 ? 512 : 256;
         }
     }
@@ -513,8 +513,10 @@ w4a16_status w4a16_linear_run_fmt(int32_t kernel, const void *x, int32_t dtype, 
 w4a16_status w4a16_testing_gemm_expire(const void *x, int32_t dtype, const void *qweight, const void *scales,
                                        const void *zeros, void *y, int64_t M, int64_t N, int64_t K, int32_t group,
                                        int32_t fmt, void *workspace, size_t workspace_bytes, void *stream) {
-    const size_t need = (M >= 1 && M <= (1LL << 24) && shape_ok(N, K, group)) ? gemm_need(M, N, K, group) : 0;
-    if (need == 0) return W4A16_ERR_INVALID_ARG;   // no stream-K split for this shape
+    const bool shape = M >= 1 && M <= (1LL << 24) && shape_ok(N, K, group);
+    const size_t need = shape ? gemm_need(M, N, K, group) : 0;
+    // (only a stream-K plan has waits to expire; a K split does not wait)
+    if (need == 0 || gemm_plan(M, N, K, group).sk_wgs == 0) return W4A16_ERR_INVALID_ARG;
     w4a16_status st = check_linear(x, dtype, qweight, scales, zeros, y, M, N, K, group, fmt, workspace,
                                    workspace_bytes, need);
     if (st != W4A16_OK) return st;

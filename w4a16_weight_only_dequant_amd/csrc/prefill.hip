@@ -2,6 +2,7 @@
 // dispatch over the weight formats. The kernel is in prefill_kernel.hpp; each
 // weight format is compiled in its own translation unit (this one: the 4-bit
 // zero-point format; prefill_sym4.hip, prefill_sym8.hip).
+#include <algorithm>
 #include <chrono>
 #include <random>
 
@@ -47,10 +48,41 @@ int prefill_tile(int64_t M, int64_t N) {
 // against 117 us, at K = 1024 77 against 65 us) and while the whole-tile rounds
 // are few (at most four: seven rounds at M = 4096, N = 24832, K = 2048: 457
 // against 433 us).
+//
+// K split for a grid too small for the device: with at most half as many
+// tiles as compute units (mid-size batches: M = 128, N = 15360 is 120 tiles of
+// 64 x 256), every tile walks all of K on one compute unit while the others
+// idle. Its columns are then split over S workgroups (S = CUs / tiles, at
+// most 16, each range at least 4 columns; S recomputed so that no range is
+// empty); each leaves an fp32 partial tile and the last to arrive adds the S
+// partials in split order (the kernel's split epilogue). Tiles of 4 waves
+// only (the 64- and 128-row tiles that small batches get).
+static void prefill_split_k(int64_t M, int64_t N, int64_t K, int cus, GemmPlan &plan) {
+    plan.splits = 1;
+    plan.split_cols = 0;
+    plan.split_tiles = 0;
+    if (tuning_knob("W4A16_PREFILL_SPLIT", 1) != 1) return;
+    if (plan.tile != kTile64x256 && plan.tile != kTile128x256) return;
+    const int64_t tiles = ceil_div(M, tile_rows(plan.tile)) * ceil_div(N, kTileCols);
+    const int64_t T = ceil_div(K / kChunk, kColChunks);
+    const int64_t slots = (int64_t)cus * tuning_knob("W4A16_PREFILL_SPLIT_PER_CU", 1);   // workgroups to fill
+    if (cus < 8 || 2 * tiles > slots) return;
+    int64_t S = std::min<int64_t>({slots / tiles, T / 4, (int64_t)kMaxTileSplits});
+    if (S < 2) return;
+    const int64_t cols = ceil_div(T, S);
+    S = ceil_div(T, cols);
+    if (S < 2) return;
+    plan.splits = (int)S;
+    plan.split_cols = (int)cols;
+    plan.split_tiles = (int)tiles;
+}
+
 void prefill_stream_k(int64_t M, int64_t N, int64_t K, int cus, GemmPlan &plan) {
     const int enabled = tuning_knob("W4A16_PREFILL_SK", 1);
     plan.dp_tiles = 0;
     plan.sk_wgs = 0;
+    prefill_split_k(M, N, K, cus, plan);
+    if (plan.splits > 1) return;
     const int64_t tiles = ceil_div(M, tile_rows(plan.tile)) * ceil_div(N, kTileCols);
     const int64_t T = ceil_div(K / kChunk, kColChunks);
     if (!enabled || cus < 8 || T < 16 || tiles <= cus) return;
@@ -87,7 +119,11 @@ unsigned long long next_sk_token() {
 }
 
 size_t prefill_workspace_bytes(const GemmPlan &plan) {
-    if (plan.kind != 1 || plan.sk_wgs == 0) return 0;
+    if (plan.kind != 1) return 0;
+    if (plan.splits > 1)   // partial tiles [tiles][splits][rows x 256] fp32, then a counter per tile
+        return (size_t)plan.split_tiles * plan.splits * tile_rows(plan.tile) * kTileCols * sizeof(float) +
+               align_up((size_t)plan.split_tiles * 8, 256);
+    if (plan.sk_wgs == 0) return 0;
     const size_t part = (size_t)plan.sk_wgs * tile_rows(plan.tile) * kTileCols * sizeof(float);
     return part + align_up((size_t)plan.sk_wgs * 8, 256);
 }

@@ -158,8 +158,8 @@ template <int BM, int BN, int WM, int WN, int GROUP, bool BF, int FMT, bool SK>
 __global__ __launch_bounds__(64 * WM * WN) __attribute__((amdgpu_waves_per_eu(WM * WN / 4, WM * WN / 4))) void prefill_kernel(
     const uint16_t *__restrict__ x, const uint4 *__restrict__ qw, const uint4 *__restrict__ qw_hi,
     const uint16_t *__restrict__ scales, const uint32_t *__restrict__ zeros, uint16_t *__restrict__ y, int M,
-    int N, int K, int m_tiles, int n_tiles, int mshift, int dp_tiles, int sk_wgs, int raster,
-    float4 *__restrict__ partials,
+    int N, int K, int m_tiles, int n_tiles, int mshift, int dp_tiles, int sk_wgs, int raster, int splits,
+    int split_cols, float4 *__restrict__ partials,
     unsigned long long *__restrict__ flags, unsigned long long token, unsigned long long wait_token,
     unsigned int *__restrict__ err) {
     using FT = FormatTraits<FMT>;
@@ -202,7 +202,16 @@ __global__ __launch_bounds__(64 * WM * WN) __attribute__((amdgpu_waves_per_eu(WM
     // in this order, so results do not depend on timing.
     const int tiles = m_tiles * n_tiles;
     int ft, lt, fb, le, s_sk = -1;   // first / last tile, first column of the first, end column of the last
-    if ((int)blockIdx.x < dp_tiles) {
+    // K split (4-wave tiles, plan.splits > 1): workgroup id takes columns
+    // [j c, min((j + 1) c, T)) of tile id / S, j = id % S, c = split_cols
+    constexpr bool kCanSplit = SK && WM * WN == 4 && BM <= 128;
+    int piece = -1;
+    if (kCanSplit && splits > 1) {
+        piece = (int)blockIdx.x % splits;
+        ft = lt = (int)blockIdx.x / splits;
+        fb = piece * split_cols;
+        le = min(fb + split_cols, T);
+    } else if ((int)blockIdx.x < dp_tiles) {
         int id = blockIdx.x;
         if (raster) {
             // M bands: XCD j takes the band of m_tiles / 8 M tiles j * band ..
@@ -236,11 +245,13 @@ __global__ __launch_bounds__(64 * WM * WN) __attribute__((amdgpu_waves_per_eu(WM
     fb = __builtin_amdgcn_readfirstlane(fb);
     le = __builtin_amdgcn_readfirstlane(le);
     s_sk = __builtin_amdgcn_readfirstlane(s_sk);
+    piece = __builtin_amdgcn_readfirstlane(piece);
+    const bool split_piece = kCanSplit && piece >= 0;
     const int full_lo = fb == 0 ? ft : ft + 1;     // whole tiles full_lo..full_hi
     const int full_hi = le == T ? lt : lt - 1;
-    const int n_full = max(0, full_hi - full_lo + 1);
-    const bool has_head = le < T, has_tail = fb > 0;
-    const int n_seg = n_full + (has_head ? 1 : 0) + (has_tail ? 1 : 0);
+    const int n_full = split_piece ? 0 : max(0, full_hi - full_lo + 1);
+    const bool has_head = !split_piece && le < T, has_tail = !split_piece && fb > 0;
+    const int n_seg = split_piece ? 1 : n_full + (has_head ? 1 : 0) + (has_tail ? 1 : 0);
 
     const int G8 = meta_slots(K, GROUP << mshift);   // metadata slots per row (group 256: mshift = 1)
     const ColScales<GPC> *scol = reinterpret_cast<const ColScales<GPC> *>(scales);
@@ -255,9 +266,11 @@ __global__ __launch_bounds__(64 * WM * WN) __attribute__((amdgpu_waves_per_eu(WM
     for (int seg = 0; seg < (SK ? n_seg : 1); ++seg) {
         // segment seg: a whole tile, the head [0, le) of tile lt, or the tail
         // [fb, T) of tile ft
-        const int kind = __builtin_amdgcn_readfirstlane(seg < n_full ? 0 : ((seg == n_full && has_head) ? 1 : 2));
+        // (kind 3: a piece [fb, le) of tile ft of the K split)
+        const int kind = __builtin_amdgcn_readfirstlane(
+            split_piece ? 3 : (seg < n_full ? 0 : ((seg == n_full && has_head) ? 1 : 2)));
         const int id = __builtin_amdgcn_readfirstlane(kind == 0 ? full_lo + seg : (kind == 1 ? lt : ft));
-        const int tb = kind == 2 ? fb : 0, te = kind == 1 ? le : T;
+        const int tb = (kind == 2 || kind == 3) ? fb : 0, te = (kind == 1 || kind == 3) ? le : T;
         const int mt = __builtin_amdgcn_readfirstlane(id % m_tiles), nt = __builtin_amdgcn_readfirstlane(id / m_tiles);
         const int m0 = mt * BM, n0 = nt * BN;
         if (seg > 0) __syncthreads();   // the previous segment's last reads of both LDS buffers are done
@@ -510,6 +523,70 @@ __global__ __launch_bounds__(64 * WM * WN) __attribute__((amdgpu_waves_per_eu(WM
             if (two) step(xs1, ws1, wcur, 0, ws0, xs0, min(s0 + 2, steps - 1), kMasked);
         }
 
+        // ---- K split: this piece's fp32 partial into slot (tile, piece), then
+        // the arrival on the tile's counter; the last arrival adds the S
+        // partials in split order (so the result does not depend on which one
+        // is last) and stores the tile. Partials are written and read with
+        // device-scope atomic accesses (coherent across the XCDs' L2 caches
+        // without a fence); every wave waits for its stores to complete before
+        // the barrier, the arrival is counted after it, and the last arrival
+        // reads the partials only after its count returned. The counter holds
+        // the launch's token in bits 8..63, so it needs no initialisation, and
+        // the last arrival clears it, so a replayed graph counts from zero.
+        if constexpr (kCanSplit) {
+            if (kind == 3) {
+                constexpr int kSlot = TM * TN * 16 * NT;   // floats of one partial tile
+                float *pt = reinterpret_cast<float *>(partials) + (size_t)ft * splits * kSlot;
+                float *mine = pt + (size_t)piece * kSlot;
+#pragma unroll
+                for (int a = 0; a < TM; ++a)
+#pragma unroll
+                    for (int b = 0; b < TN; ++b)
+#pragma unroll
+                        for (int v = 0; v < 16; ++v)
+                            __hip_atomic_store(mine + ((a * TN + b) * 16 + v) * NT + tid, acc[a][b][v],
+                                               __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                __shared__ int split_last;
+                __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0)
+                __syncthreads();
+                if (tid == 0) {
+                    unsigned long long *c = flags + ft;
+                    unsigned long long old = __hip_atomic_load(c, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                    unsigned long long nv;
+                    do {
+                        nv = (old & ~0xFFull) == token ? old + 1 : (token | 1ull);
+                    } while (!__hip_atomic_compare_exchange_strong(c, &old, nv, __ATOMIC_RELAXED, __ATOMIC_RELAXED,
+                                                                   __HIP_MEMORY_SCOPE_AGENT));
+                    split_last = (int)(nv & 0xFFull) == splits;
+                    if (split_last) __hip_atomic_store(c, 0ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                }
+                __syncthreads();
+                if (!split_last) continue;
+                // slot by slot, every load of a slot issued before its adds (one
+                // memory round trip per slot); the sum runs in split order
+                auto load_slot = [&](int j, f16_t (&dst)[TM][TN]) __attribute__((always_inline)) {
+                    const float *src = pt + (size_t)j * kSlot + tid;
+#pragma unroll
+                    for (int a = 0; a < TM; ++a)
+#pragma unroll
+                        for (int b = 0; b < TN; ++b)
+#pragma unroll
+                            for (int v = 0; v < 16; ++v)
+                                dst[a][b][v] = __hip_atomic_load(src + ((a * TN + b) * 16 + v) * NT, __ATOMIC_RELAXED,
+                                                                 __HIP_MEMORY_SCOPE_AGENT);
+                };
+                load_slot(0, acc);
+                for (int j = 1; j < splits; ++j) {
+                    f16_t part[TM][TN];
+                    load_slot(j, part);
+#pragma unroll
+                    for (int a = 0; a < TM; ++a)
+#pragma unroll
+                        for (int b = 0; b < TN; ++b) acc[a][b] += part[a][b];
+                }
+            }
+        }
+
         // ---- stream-K hand-over. Partial slots hold each thread's accumulators
         // as float4 [TM][TN][4][NT] (coalesced; producer and consumer run the same
         // tile shape, so thread tid reads back exactly what thread tid wrote).
@@ -626,6 +703,7 @@ __global__ __launch_bounds__(64 * WM * WN) __attribute__((amdgpu_waves_per_eu(WM
 // (0: every tile whole) with their partials and flags in `ws`.
 struct SkArgs {
     int dp_tiles, sk_wgs;
+    int splits, split_cols;   // K split (splits > 1; exclusive with stream-K)
     void *ws;
     bool expire_test;   // consumers wait for a token no producer writes (tests the expiry path)
 };
@@ -634,7 +712,8 @@ template <int BM, int BN, int WM, int WN, int GROUP, bool BF, int FMT>
 hipError_t launch_tile(const void *x, const void *qw, const void *qh, const void *sc, const void *zp, void *y, int M,
                        int N, int K, int ms, const SkArgs &sk, hipStream_t stream) {
     static_assert(BN == kTileCols, "tile columns");
-    const bool split = sk.sk_wgs > 0;
+    const bool ksplit = WM * WN == 4 && BM <= 128 && sk.splits > 1;
+    const bool split = sk.sk_wgs > 0 || ksplit;
     auto kern = split ? prefill_kernel<BM, BN, WM, WN, GROUP, BF, FMT, true>
                       : prefill_kernel<BM, BN, WM, WN, GROUP, BF, FMT, false>;
     const size_t lds = (size_t)2 * (BM + BN) * kUnits * 16;
@@ -643,27 +722,42 @@ hipError_t launch_tile(const void *x, const void *qw, const void *qh, const void
     if (e != hipSuccess) return e;
     const int m_tiles = (int)ceil_div(M, BM), n_tiles = (int)ceil_div(N, BN);
     const int tiles = m_tiles * n_tiles;
-    int dp = tiles, skw = 0;
+    int dp = tiles, skw = 0, splits = 1, grid = tiles;
     float4 *part = nullptr;
     unsigned long long *flags = nullptr;
-    if (sk.sk_wgs > 0) {   // the plan guarantees dp_tiles + sk_wgs <= tiles (each share >= one tile)
+    unsigned long long token = 0ull;
+    if (ksplit) {   // partials [tiles][splits][BM x BN] fp32, then a counter per tile
+        if (sk.ws == nullptr || sk.split_cols < 1 || (int64_t)(sk.splits - 1) * sk.split_cols >= ceil_div(K / kChunk, kColChunks))
+            return hipErrorInvalidValue;
+        splits = sk.splits;
+        dp = 0;
+        grid = tiles * splits;
+        part = reinterpret_cast<float4 *>(sk.ws);
+        flags = reinterpret_cast<unsigned long long *>(static_cast<char *>(sk.ws) +
+                                                       (size_t)tiles * splits * BM * BN * 4);
+        token = next_sk_token() & ~0xFFull;   // the counters keep the arrivals in bits 0..7
+        if (token == 0) token = 0x100ull;
+    } else if (sk.sk_wgs > 0) {   // the plan guarantees dp_tiles + sk_wgs <= tiles (each share >= one tile)
         if (sk.ws == nullptr || sk.dp_tiles + sk.sk_wgs > tiles) return hipErrorInvalidValue;
         dp = sk.dp_tiles;
         skw = sk.sk_wgs;
+        grid = dp + skw;
         part = reinterpret_cast<float4 *>(sk.ws);
         flags = reinterpret_cast<unsigned long long *>(static_cast<char *>(sk.ws) + (size_t)skw * BM * BN * 4);
+        token = next_sk_token();
     }
-    // consumers wait for the token their producer writes; a launch that tests
-    // the expiry of the wait gives them one no producer writes and a short bound
-    const unsigned long long token = skw > 0 ? next_sk_token() : 0ull;
+    // stream-K consumers wait for the token their producer writes; a launch
+    // that tests the expiry of the wait gives them one no producer writes and
+    // a short bound
     const unsigned long long wait_token = sk.expire_test ? token ^ 0xA5A5A5A5A5A5A5A5ull : token;
-    const int raster = (m_tiles % 8 == 0 && dp % m_tiles == 0 && tuning_knob("W4A16_PREFILL_RASTER", 1) == 1) ? 1 : 0;
+    const int raster = (!ksplit && m_tiles % 8 == 0 && dp % m_tiles == 0 &&
+                        tuning_knob("W4A16_PREFILL_RASTER", 1) == 1) ? 1 : 0;
     unsigned int *err = skw > 0 ? kernel_error_word() : nullptr;
-    hipLaunchKernelGGL(kern, dim3((unsigned)(dp + skw)), dim3(64 * WM * WN), lds, stream,
+    hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(64 * WM * WN), lds, stream,
                        reinterpret_cast<const uint16_t *>(x), reinterpret_cast<const uint4 *>(qw),
                        reinterpret_cast<const uint4 *>(qh), reinterpret_cast<const uint16_t *>(sc),
                        reinterpret_cast<const uint32_t *>(zp), reinterpret_cast<uint16_t *>(y), M, N, K, m_tiles,
-                       n_tiles, ms, dp, skw, raster, part, flags, token, wait_token, err);
+                       n_tiles, ms, dp, skw, raster, splits, sk.split_cols, part, flags, token, wait_token, err);
     return hipGetLastError();
 }
 
@@ -686,7 +780,7 @@ template <int FMT>
 hipError_t launch_prefill_fmt(const void *x, bool bf16, const void *qweight, const void *scales, const void *zeros,
                               void *y, int M, int N, int K, int group, const GemmPlan &plan, void *workspace,
                               hipStream_t stream) {
-    const SkArgs sk{plan.dp_tiles, plan.sk_wgs, workspace, plan.sk_expire_test != 0};
+    const SkArgs sk{plan.dp_tiles, plan.sk_wgs, plan.splits, plan.split_cols, workspace, plan.sk_expire_test != 0};
     const int ms = group == 256 ? 1 : 0;
     const void *qh = FormatTraits<FMT>::two_planes
                          ? static_cast<const void *>(static_cast<const char *>(qweight) + (size_t)N * K / 2)

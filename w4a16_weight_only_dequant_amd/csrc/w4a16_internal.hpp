@@ -91,7 +91,9 @@ size_t decode_workspace_bytes(const DecodePlan &plan, int64_t M, int64_t N);
 // Plan for the matrix-core kernels: kind 0 streams the weights through
 // registers for M <= kSkinnyMaxM (16-row MFMA tiles of activations, one per
 // workgroup), kind 1 is the LDS-tiled GEMM for everything larger.
-constexpr int kSkinnyMaxM = 128;   // measured crossover to the tiled kernel (M = 128: a tie; 192: 149 against 106 us)
+// measured crossover to the tiled kernel with its K split (N = 15360, K = 5120,
+// bf16: M = 32 28.9 against 38.6 us, M = 48 41.1 against 38.5 us)
+constexpr int kSkinnyMaxM = 32;
 enum { kTile64x256 = 0, kTile128x256 = 1, kTile256x256 = 2, kTile256x256w8 = 3 };
 struct GemmPlan {
     int kind;          // 0 = skinny, 1 = tiled
@@ -100,6 +102,9 @@ struct GemmPlan {
     int tile;          // tiled: one of kTile*
     int dp_tiles;      // tiled, stream-K: tiles computed whole, one workgroup each
     int sk_wgs;        // tiled, stream-K: workgroups sharing the other tiles' columns (0: none)
+    int splits;        // tiled, K split: workgroups per tile (1: none), each `split_cols` columns of K,
+    int split_cols;    //   over `split_tiles` tiles
+    int split_tiles;
     int sk_expire_test;   // 1: consumers wait for a token no producer writes (exercises the expiry path)
 };
 
@@ -111,9 +116,13 @@ int device_cu_count();
 // Tile rows / columns of a tiled kind.
 inline int tile_rows(int tile) { return tile == kTile64x256 ? 64 : (tile == kTile128x256 ? 128 : 256); }
 constexpr int kTileCols = 256;
+constexpr int kMaxTileSplits = 16;   // K split: workgroups per tile at most
 // Stream-K split of the tiled GEMM for this shape on `cus` compute units
-// (fills plan.dp_tiles / plan.sk_wgs), and the workspace it needs: one fp32
-// partial tile per stream-K workgroup, then one 8-byte flag each.
+// (fills plan.dp_tiles / plan.sk_wgs), or its K split when the tiles fill at
+// most half the compute units (plan.splits / split_cols / split_tiles), and
+// the workspace that needs: stream-K, one fp32 partial tile per stream-K
+// workgroup, then one 8-byte flag each; K split, one fp32 partial tile per
+// (tile, split), then one 8-byte arrival counter per tile.
 void prefill_stream_k(int64_t M, int64_t N, int64_t K, int cus, GemmPlan &plan);
 size_t prefill_workspace_bytes(const GemmPlan &plan);
 // Stream-K hand-over token: distinct for every launch in this process and
