@@ -15,11 +15,12 @@ from tests import helpers as H
 
 pytestmark = pytest.mark.gpu
 
-# (M, N, K, group), 64-row tiles on 256 compute units: 1 x 4 tiles split 4
+# (M, N, K, group) on 256 compute units, 64-row tiles unless stated: 1 x 4 tiles split 4
 # ways; a ragged M, N and K (N % 16 = 8, K % 128 = 32: 68 tiles split 2 ways,
 # the last split holding the partial last column); group 256 (one metadata
 # slot per two columns, 16 tiles split 8 ways); 20 tiles split 6 ways; the
-# mid-batch QKV shape (60 and 120 tiles, split 4 and 2 ways)
+# mid-batch QKV shape (M = 64: 60 tiles of 64 rows split 4 ways; M = 128: 60
+# tiles of 128 rows split 4 ways)
 SPLIT_SHAPES = [(37, 1000, 2048, 64), (200, 4104, 1056, 32), (100, 2048, 4096, 256), (300, 1024, 3072, 128),
                 (64, 15360, 5120, 128), (128, 15360, 5120, 128)]
 

@@ -50,31 +50,53 @@ int prefill_tile(int64_t M, int64_t N) {
 // against 433 us).
 //
 // K split for a grid too small for the device: with at most half as many
-// tiles as compute units (mid-size batches: M = 128, N = 15360 is 120 tiles of
+// tiles as compute units (mid-size batches: M = 64, N = 15360 is 60 tiles of
 // 64 x 256), every tile walks all of K on one compute unit while the others
 // idle. Its columns are then split over S workgroups (S = CUs / tiles, at
 // most 16, each range at least 4 columns; S recomputed so that no range is
 // empty); each leaves an fp32 partial tile and the last to arrive adds the S
 // partials in split order (the kernel's split epilogue). Tiles of 4 waves
-// only (the 64- and 128-row tiles that small batches get).
+// only (64 and 128 rows). Between those two the plan takes the one with less
+// work per workgroup, rows x columns, over its rounds (equal: 128 rows).
+// Measured on MI355X, N = 15360, K = 5120, bf16: M = 64, 64-row tiles split 4
+// ways 37 us (128-row 52); M = 128, 128-row tiles split 4 ways 49 us (64-row
+// split 2 ways 54.5); M = 192 and 256, 128-row tiles split 2 ways 70 / 68 us
+// (64-row whole tiles 78 / 77); a second workgroup per compute unit (twice
+// the splits) was slower everywhere (61 us at M = 64).
+struct TileSplit {
+    int64_t tiles, splits, cols;
+};
+static TileSplit split_of(int tile, int64_t M, int64_t N, int64_t T, int cus) {
+    TileSplit s{ceil_div(M, tile_rows(tile)) * ceil_div(N, kTileCols), 1, T};
+    if (cus < 8 || 2 * s.tiles > cus) return s;
+    int64_t S = std::min<int64_t>({(int64_t)cus / s.tiles, T / 4, (int64_t)kMaxTileSplits});
+    if (S < 2) return s;
+    const int64_t cols = ceil_div(T, S);
+    S = ceil_div(T, cols);
+    if (S < 2) return s;
+    s.splits = S;
+    s.cols = cols;
+    return s;
+}
 static void prefill_split_k(int64_t M, int64_t N, int64_t K, int cus, GemmPlan &plan) {
     plan.splits = 1;
     plan.split_cols = 0;
     plan.split_tiles = 0;
     if (tuning_knob("W4A16_PREFILL_SPLIT", 1) != 1) return;
     if (plan.tile != kTile64x256 && plan.tile != kTile128x256) return;
-    const int64_t tiles = ceil_div(M, tile_rows(plan.tile)) * ceil_div(N, kTileCols);
     const int64_t T = ceil_div(K / kChunk, kColChunks);
-    const int64_t slots = (int64_t)cus * tuning_knob("W4A16_PREFILL_SPLIT_PER_CU", 1);   // workgroups to fill
-    if (cus < 8 || 2 * tiles > slots) return;
-    int64_t S = std::min<int64_t>({slots / tiles, T / 4, (int64_t)kMaxTileSplits});
-    if (S < 2) return;
-    const int64_t cols = ceil_div(T, S);
-    S = ceil_div(T, cols);
-    if (S < 2) return;
-    plan.splits = (int)S;
-    plan.split_cols = (int)cols;
-    plan.split_tiles = (int)tiles;
+    const TileSplit s64 = split_of(kTile64x256, M, N, T, cus), s128 = split_of(kTile128x256, M, N, T, cus);
+    if (s64.splits == 1 && s128.splits == 1) return;
+    auto work = [&](const TileSplit &s, int rows) {
+        return (double)rows * (double)s.cols * (double)ceil_div(s.tiles * s.splits, cus > 0 ? cus : 1);
+    };
+    const bool use128 = work(s128, 128) <= work(s64, 64);
+    const TileSplit &s = use128 ? s128 : s64;
+    plan.tile = use128 ? kTile128x256 : kTile64x256;
+    if (s.splits < 2) return;
+    plan.splits = (int)s.splits;
+    plan.split_cols = (int)s.cols;
+    plan.split_tiles = (int)s.tiles;
 }
 
 void prefill_stream_k(int64_t M, int64_t N, int64_t K, int cus, GemmPlan &plan) {
