@@ -425,6 +425,7 @@ def stream_ceiling(dev, decode_entries):
         us = timed(lambda i: big.data_ptr() + (i % copies) * nb, nb, e["workgroups"], 240)
         out[name] = {"bytes": nb, "workgroups": e["workgroups"], "us": round(us, 3),
                      "GBps": round(nb / us / 1e3, 1), "pct_hbm_peak": round(nb / us / 1e3 / HBM_PEAK_GBS * 100, 2),
+                     "decode_us": e["us"], "read_over_decode": round(us / e["us"], 3),
                      "note": "the same bytes at the decode launch's number of workgroups, launches replayed "
                              "from a graph like the kernel's"}
     del big
@@ -993,7 +994,13 @@ def main():
             continue
         legs[f"c{cfg_id}"] = run_leg(cfg_id, list(wl.WORKLOADS[cfg_id].ms), dev, launches, stash)
         print(f"leg c{cfg_id} done", file=sys.stderr, flush=True)
-    ceiling = stream_ceiling(dev, c2_entries)
+    # the streaming read beside every M = 1 decode launch: the headline set, c1 and c5
+    ceiling_entries = dict(c2_entries)
+    for cid, mat in (("c1", "w"), ("c5", "down")):
+        e = legs.get(cid, {}).get("by_M", {}).get("1", {}).get(mat)
+        if e is not None and e.get("kind") == "gemv":
+            ceiling_entries[f"{cid}_{mat}"] = e
+    ceiling = stream_ceiling(dev, ceiling_entries)
 
     # ---- the dominant kernel of the headline step
     by_kind = {}

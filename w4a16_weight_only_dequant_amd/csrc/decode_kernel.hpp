@@ -225,9 +225,18 @@ __device__ __forceinline__ void decode_body(
     // row l % 16's run (and zero-point words the same way), for LDS. Parts
     // past the end of a row re-read its last one (never used).
     const int mp = lane >> 4;
-    uint4 mreg[MREG ? MPARTS : MJ];
-    uint32_t zreg[MREG ? (ZW > 0 ? ZW : 1) : (ZJ > 0 ? ZJ : 1)];
-    {
+    constexpr int NMR = MREG ? MPARTS : MJ;
+    constexpr int NZR = MREG ? (ZW > 0 ? ZW : 1) : (ZJ > 0 ? ZJ : 1);
+    // (held in one value returned by the loading code: as separate arrays
+    // the compiler kept about 14 more registers live in the large-K kernels)
+    struct MetaRegs {
+        uint4 m[NMR];
+        uint32_t z[NZR];
+    };
+    const MetaRegs meta = [&] {
+        MetaRegs mr;
+        uint4 *mreg = mr.m;
+        uint32_t *zreg = mr.z;
         const int mrow = b * kRowBlock + rl;
         const unsigned char *base;
         int last_part;
@@ -262,7 +271,10 @@ __device__ __forceinline__ void decode_body(
                 for (int j = 0; j < ZJ; ++j) zreg[j] = zb[min(gs0 / 8 + mp + 4 * j, G8 / 8 - 1)];
             }
         }
-    }
+        return mr;
+    }();
+    const uint4 (&mreg)[NMR] = meta.m;
+    const uint32_t (&zreg)[NZR] = meta.z;
 
     // 3. the codes of every column of the slice, all in flight at once (a
     // position past the slice re-reads its last full column: never used)
