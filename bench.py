@@ -103,6 +103,8 @@ def parse():
     p.add_argument("--summarize-trace", metavar="DIR", default=None)
     p.add_argument("--summarize-counters", metavar="DIR", nargs="+", default=None)
     p.add_argument("--bench-json", default=None, help="a bench.py output line (launch keys of the legs)")
+    p.add_argument("--stream-grid", action="store_true",
+                   help="time a plain streaming read of each M = 1 decode matrix's bytes at several grids")
     p.add_argument("--crossover", action="store_true",
                    help="time every kernel at M = 1..2048 on two shapes and check the dispatch's choice")
     return p.parse_args()
@@ -376,17 +378,16 @@ def headline(dev, steps, warmup, launches, stash):
     return step, entries, grouped
 
 
-def stream_ceiling(dev, decode_entries):
-    """A plain 16-byte streaming read: over 2 GiB at eight workgroups per
-    compute unit, and over each decode matrix's bytes (rotated over copies past
-    the MALL) at the decode kernel's number of workgroups."""
+def _stream_reader(dev):
+    """A 2 GiB device buffer and timed(ptr_fn, nbytes, wgs, reps): microseconds
+    per launch of the plain 16-byte streaming read (w4a16_measure_stream_read)
+    of nbytes at ptr_fn(i) with wgs workgroups (0: 16 KiB each)."""
     import torch
 
     import w4a16_weight_only_dequant_amd as w4
     raw = w4.raw()
     sink = torch.zeros(4, dtype=torch.int32, device=dev)
     big = torch.ones(2 << 30, dtype=torch.uint8, device=dev)
-    out = {"kernel": "stream_read_kernel (w4a16_measure_stream_read)"}
 
     def timed(ptr_fn, nbytes, wgs, reps):
         """Microseconds per launch: one graph of `reps` launches, replayed
@@ -411,6 +412,25 @@ def stream_ceiling(dev, decode_entries):
         torch.cuda.synchronize()
         return e0.elapsed_time(e1) * 1e3 / reps
 
+    return timed, big
+
+
+def _rotated(big, nbytes):
+    """(bytes rounded to 4 KiB, ptr_fn): launch i reads copy i % copies of the
+    buffer, with copies x bytes past three times the MALL where the buffer
+    holds that many."""
+    nb = (nbytes + 4095) // 4096 * 4096
+    copies = max(1, min(big.numel() // nb, -(-3 * MALL_BYTES // nb)))
+    return nb, (lambda i: big.data_ptr() + (i % copies) * nb)
+
+
+def stream_ceiling(dev, decode_entries):
+    """A plain 16-byte streaming read: over 2 GiB at eight workgroups per
+    compute unit, and over each decode matrix's bytes (rotated over copies past
+    the MALL) at the decode kernel's number of workgroups."""
+    import torch
+    timed, big = _stream_reader(dev)
+    out = {"kernel": "stream_read_kernel (w4a16_measure_stream_read)"}
     us = timed(lambda i: big.data_ptr(), big.numel(), 0, 20)
     out["2GiB"] = {"bytes": big.numel(), "us": round(us, 1), "GBps": round(big.numel() / us / 1e3, 1),
                    "pct_hbm_peak": round(big.numel() / us / 1e3 / HBM_PEAK_GBS * 100, 2)}
@@ -420,9 +440,8 @@ def stream_ceiling(dev, decode_entries):
         if key in seen:
             continue
         seen.add(key)
-        nb = (e["bytes_algorithmic"] + 4095) // 4096 * 4096
-        copies = max(1, min(big.numel() // nb, -(-3 * MALL_BYTES // nb)))
-        us = timed(lambda i: big.data_ptr() + (i % copies) * nb, nb, e["workgroups"], 240)
+        nb, ptr_fn = _rotated(big, e["bytes_algorithmic"])
+        us = timed(ptr_fn, nb, e["workgroups"], 240)
         out[name] = {"bytes": nb, "workgroups": e["workgroups"], "us": round(us, 3),
                      "GBps": round(nb / us / 1e3, 1), "pct_hbm_peak": round(nb / us / 1e3 / HBM_PEAK_GBS * 100, 2),
                      "decode_us": e["us"], "read_over_decode": round(us / e["us"], 3),
@@ -431,6 +450,34 @@ def stream_ceiling(dev, decode_entries):
     del big
     torch.cuda.empty_cache()
     return out
+
+
+def stream_grid(dev):
+    """The plain streaming read of each M = 1 decode matrix's algorithmic
+    bytes at 256 ... 8192 workgroups and at 16 KiB per workgroup (0): how much
+    the number of workgroups alone moves the rate a read of that size reaches,
+    beside the decode kernel's own grid (profiles/stream_read_vs_grid.txt)."""
+    import torch
+
+    import w4a16_weight_only_dequant_amd as w4
+    import workloads as wl
+    timed, big = _stream_reader(dev)
+    cases = [("c1 w", 1, 0), ("c2 q", 2, 0), ("c2 up", 2, 4), ("c2 down", 2, 6), ("c5 down", 5, 0)]
+    rows = []
+    for label, cfg, mat in cases:
+        wlc = wl.WORKLOADS[cfg]
+        m = wlc.matrices[mat]
+        nbytes = algorithmic_bytes(1, m.N, m.K, wlc.group)
+        nb, ptr_fn = _rotated(big, nbytes)
+        kern, dec_wgs, _ = w4.linear_launch_shape(1, m.N, m.K, wlc.group, torch.float16)
+        for wgs in (256, 320, 512, 864, 1024, 2048, 4096, 8192, 0):
+            us = timed(ptr_fn, nb, wgs, 240)
+            rows.append({"case": label, "N": m.N, "K": m.K, "group": wlc.group, "bytes": nbytes, "workgroups": wgs,
+                         "decode_workgroups": dec_wgs, "us": round(us, 3), "TBps": round(nbytes / us / 1e6, 3)})
+            print(f"{label} {wgs} workgroups: {us:.2f} us", file=sys.stderr, flush=True)
+    del big
+    torch.cuda.empty_cache()
+    return rows
 
 
 def quality_and_awq(dev, steps, warmup):
@@ -968,6 +1015,10 @@ def main():
 
     if args.counter_pass:
         counter_pass(args.counter_pass, args.reps, legs_ids)
+        return
+
+    if args.stream_grid:
+        print(json.dumps({"stream_grid": stream_grid(dev), "device": device_info(dev)}))
         return
 
     if args.crossover:
