@@ -122,6 +122,19 @@ def kernel_source_hash(kind):
     return h.hexdigest()[:16]
 
 
+def decode_variant(kernel, M, N, K, fmt, wgs, threads):
+    """The decode kernel's variant a launch runs, from its geometry: one
+    activation row, 4-bit codes with a scale per group, whole 128-weight
+    columns, one workgroup per row block and sixteen columns per wave (more
+    than eight per wave: waves * 8 < columns) run decode_bcast_kernel (the
+    library's decode plan), otherwise decode_kernel."""
+    cols = K // 128
+    if (kernel == "decode_kernel" and M == 1 and fmt in ("asym4", "sym4") and K % 128 == 0
+            and wgs == -(-N // 16) and (threads // 64) * 8 < cols):
+        return "decode_bcast_kernel"
+    return kernel
+
+
 def algorithmic_bytes(M, N, K, group, fmt="asym4"):
     """Codes (4 or 8 bits per weight), fp16 scales, 4-bit zero-points (asym4
     only), activations read and outputs written."""
@@ -208,8 +221,8 @@ class Workload:
         self.launch_keys = []
         for m in self.mats:
             kname, wg, th = w4.linear_launch_shape(M, m.N, m.K, self.group, self.tdt, fmt)
-            self.launch_keys.append({"kernel": KERNEL_NAMES[kname], "kind": KERNEL_KIND[kname],
-                                     "workgroups": wg, "threads": th})
+            self.launch_keys.append({"kernel": decode_variant(KERNEL_NAMES[kname], M, m.N, m.K, fmt, wg, th),
+                                     "kind": KERNEL_KIND[kname], "workgroups": wg, "threads": th})
 
     def launch(self, c, j):
         self.w4.linear(self.xs[j], self.sets[c][j], out=self.ys[j], workspace=self.ws)
@@ -805,8 +818,8 @@ def _short(name):
     return re.sub(r"\(.*$", "", name)[:70]
 
 
-LIBRARY_KERNELS = ("decode_kernel", "skinny_kernel", "skinny_group_kernel", "prefill_kernel", "copy_kernel",
-                   "stream_read_kernel")
+LIBRARY_KERNELS = ("decode_kernel", "decode_bcast_kernel", "decode_group_kernel", "skinny_kernel",
+                   "skinny_group_kernel", "prefill_kernel", "copy_kernel", "stream_read_kernel")
 
 
 def _int(r, *keys):
@@ -830,6 +843,8 @@ def _matches_leg(name, e, group, dtype):
         return False
     if base == "decode_kernel":       # <GROUP, MT, BF, FMT, NCOL, AWQ>
         return args[0] == str(group) and args[2] == bf and args[3] == "0" and args[5] == "false"
+    if base == "decode_bcast_kernel":  # <GROUP, BF, FMT, NCOL, D>
+        return args[0] == str(group) and args[1] == bf and args[2] == "0"
     if base == "skinny_kernel":       # <GROUP, R, BF, FMT>
         return args[0] == str(group) and args[2] == bf and args[3] == "0"
     if base == "prefill_kernel":      # <BM, BN, WM, WN, GROUP, BF, FMT, SK>

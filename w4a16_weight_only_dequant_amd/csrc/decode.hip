@@ -25,7 +25,6 @@ constexpr int kDecMaxSplits = 32;
 // depend on `awq`: with activation multipliers the kernel sums in the same
 // order, so its result is the plain launch's on the pre-scaled activations.
 DecodePlan decode_plan(int64_t M, int64_t N, int64_t K, int32_t group, int fmt, bool awq) {
-    (void)awq;
     DecodePlan p{};
     p.ok = false;
     if (M < 1 || M > kDecodeMaxM || K <= 0 || N <= 0 || K > 65536) return p;
@@ -63,6 +62,15 @@ DecodePlan decode_plan(int64_t M, int64_t N, int64_t K, int32_t group, int fmt, 
         p.splits = s_eff;
         p.cols = (int)cols;
         p.lds = lds;
+        // one activation row, 4-bit codes with a scale per group, whole
+        // 128-weight columns, sixteen columns per wave (K > 16384): the
+        // variant that keeps the activations in registers, two workgroups per
+        // compute unit (same sums, same order, so the same bits). It is
+        // slower at eight or four columns per wave (K = 5120 and 13824:
+        // 5.7-13.1 against 5.1-10.9 us), where the broadcasts add to the
+        // shorter slices' work.
+        p.bcast = mt == 1 && ncol == 16 && s_eff == 1 && !awq && (fmt == kAsym4 || fmt == kSym4) &&
+                  K % kColumn == 0 && tuning_knob("W4A16_DEC_BCAST", 1) == 1;
         p.ok = true;
         return p;
     }

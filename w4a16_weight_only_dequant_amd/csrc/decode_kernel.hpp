@@ -593,6 +593,307 @@ __device__ __forceinline__ void decode_body(
     }
 }
 
+// One activation row, no split, K a whole number of 128-weight columns, 4-bit
+// codes: the same sums as decode_body in the same order (so the same bits),
+// with less held per wave, so that two workgroups of up to 16 waves fit on a
+// compute unit at once instead of one:
+// * activations stay in registers: lane (s, r) holds slice s of chunks
+//   16 q + r of its wave's slice (q = 0 .. NCOL / 4 - 1), and each chunk's
+//   slice reaches the 16 lanes of row s by a DPP row broadcast (row_newbcast)
+//   from the lane that holds it, instead of being staged through LDS;
+// * the per-group activation sums (the magic-offset and zero-point terms) are
+//   formed in those lanes, combined over a group's lanes by DPP row shifts in
+//   the order decode_body uses, and broadcast the same way;
+// * the codes stream through a ring of D columns per wave: after column p is
+//   used, column p + D is loaded into its registers.
+// LDS holds only the 16 rows' metadata of each wave's slice (groups 32 and
+// 64) and the waves' reduction buffer.
+__host__ __device__ constexpr bool dec_bcast_meta_lds(int ncol, int group, int fmt) {
+    return dec_meta_row_bytes(ncol, group, fmt) > 32 || dec_zero_words(ncol, group, fmt) > 2;
+}
+__host__ __device__ constexpr int dec_bcast_lds(int ncol, int group, int fmt) {
+    return (dec_bcast_meta_lds(ncol, group, fmt)
+                ? 16 * dec_meta_stride(ncol, group, fmt) +
+                      (dec_zero_words(ncol, group, fmt) > 0 ? 16 * dec_zero_stride(ncol, group, fmt) * 4 : 0)
+                : 0) + 16;
+}
+
+// the value of lane j of each row of 16 lanes, in every lane of that row
+template <int J>
+__device__ inline uint32_t row_bcast(uint32_t v) {
+    return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x150 + J, 0xF, 0xF, false);
+}
+template <int J>
+__device__ inline float row_bcast_f(float v) {
+    return __builtin_bit_cast(float, row_bcast<J>(__builtin_bit_cast(uint32_t, v)));
+}
+
+template <int GROUP, bool BF, int FMT, int NCOL, int D>
+__global__ __launch_bounds__(64 * kDecMaxWaves) void decode_bcast_kernel(
+    const uint16_t *__restrict__ x, const uint4 *__restrict__ qw, const uint16_t *__restrict__ scales,
+    const uint32_t *__restrict__ zeros, uint16_t *__restrict__ y, int N, int K) {
+    using FT = FormatTraits<FMT>;
+    static_assert(!FT::two_planes && !FT::kquant, "4-bit codes with a scale (and zero-point) per group");
+    static_assert(NCOL % 4 == 0 && D >= 1 && D <= NCOL, "ring of D columns within a slice of NCOL");
+    constexpr int GC = GROUP > kColumn ? kColumn : GROUP;
+    constexpr int CPG = GC / kChunk;
+    constexpr bool HI = !BF;
+    constexpr int MRB = dec_meta_row_bytes(NCOL, GROUP, FMT);
+    constexpr int MRS = dec_meta_stride(NCOL, GROUP, FMT);
+    constexpr int ZRS = dec_zero_stride(NCOL, GROUP, FMT);
+    constexpr int MPARTS = (MRB + 15) / 16;
+    constexpr int MJ = (MPARTS + 3) / 4;
+    constexpr int ZW = dec_zero_words(NCOL, GROUP, FMT);
+    constexpr int ZJ = (ZW + 3) / 4;
+    constexpr int XQ = NCOL / 4;                 // activation registers (16 chunks each) per lane
+    constexpr bool MREG = !dec_bcast_meta_lds(NCOL, GROUP, FMT);
+    constexpr int LDS = dec_bcast_lds(NCOL, GROUP, FMT);
+    static_assert(MRB % 16 == 0 || (MREG && MRB <= 8), "whole 16-byte metadata parts");
+    extern __shared__ __align__(16) unsigned char smem[];
+    __shared__ float red[kDecMaxWaves][kRowBlock];
+
+    const int b = blockIdx.x;
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int r = lane & 15;
+    const int s = lane >> 4;
+    const int rows_b = min(kRowBlock, N - b * kRowBlock);
+    const int rl = r < rows_b ? r : r - rows_b;
+    const int T = K >> 7;                          // columns (K % 128 == 0)
+    const int t0 = wave * NCOL;
+    const int tb = min(t0, ((T - 1) / NCOL) * NCOL);
+    const int nfull = min(max(T - t0, 0), NCOL);
+    const int nchunks = nfull * kColChunks;
+    const int G8 = ((K / GROUP) + 7) & ~7;
+    const int gs0 = (int)((int64_t)tb * kColumn / GROUP);
+
+    unsigned char *wl = smem + wave * LDS;
+    unsigned char *ml = wl;                                          // [16][MRS bytes] (LDS path)
+    uint32_t *zl = reinterpret_cast<uint32_t *>(wl + 16 * MRS);     // [16][ZRS words] (LDS path)
+    unsigned char *spare = wl + LDS - 16;
+
+    // 1. activations: lane (s, r) loads slice s of chunks 16 q + r of the
+    // slice (chunks past the slice re-read its first one; never used)
+    const uint4 *xsrc = reinterpret_cast<const uint4 *>(x) + (size_t)tb * kColChunks * 4;
+    uint4 xq[XQ];
+#pragma unroll
+    for (int q = 0; q < XQ; ++q) {
+        const int cc = 16 * q + r;
+        xq[q] = xsrc[(cc < nchunks ? cc : 0) * 4 + s];
+    }
+
+    // 2. metadata of the slice (as decode_body: registers for short runs, else LDS rows)
+    const int mp = lane >> 4;
+    constexpr int NMR = MREG ? MPARTS : MJ;
+    constexpr int NZR = MREG ? (ZW > 0 ? ZW : 1) : (ZJ > 0 ? ZJ : 1);
+    struct MetaRegs {
+        uint4 m[NMR];
+        uint32_t z[NZR];
+    };
+    const MetaRegs meta = [&] {
+        MetaRegs mr;
+        uint4 *mreg = mr.m;
+        uint32_t *zreg = mr.z;
+        const int mrow = b * kRowBlock + rl;
+        const unsigned char *base = reinterpret_cast<const unsigned char *>(scales) + (size_t)mrow * G8 * 2;
+        const int last_part = G8 / 8 - 1;
+        const int part0 = gs0 / 8;
+        const uint32_t *zb = zeros + (size_t)mrow * (G8 / 8);
+        if constexpr (MREG) {
+            if constexpr (MRB == 8) {
+                const uint2 v = *reinterpret_cast<const uint2 *>(base + (size_t)gs0 * 2);
+                mreg[0] = make_uint4(v.x, v.y, 0u, 0u);
+            } else if constexpr (MRB == 4) {
+                mreg[0] = make_uint4(*reinterpret_cast<const uint32_t *>(base + (size_t)gs0 * 2), 0u, 0u, 0u);
+            } else {
+#pragma unroll
+                for (int j = 0; j < MPARTS; ++j)
+                    mreg[j] = *reinterpret_cast<const uint4 *>(base + (size_t)min(part0 + j, last_part) * 16);
+            }
+            if constexpr (FT::has_zeros) {
+#pragma unroll
+                for (int j = 0; j < ZW; ++j) zreg[j] = zb[min(gs0 / 8 + j, G8 / 8 - 1)];
+            }
+        } else {
+#pragma unroll
+            for (int j = 0; j < MJ; ++j)
+                mreg[j] = *reinterpret_cast<const uint4 *>(base + (size_t)min(part0 + mp + 4 * j, last_part) * 16);
+            if constexpr (ZJ > 0) {
+#pragma unroll
+                for (int j = 0; j < ZJ; ++j) zreg[j] = zb[min(gs0 / 8 + mp + 4 * j, G8 / 8 - 1)];
+            }
+        }
+        return mr;
+    }();
+    const uint4 (&mreg)[NMR] = meta.m;
+    const uint32_t (&zreg)[NZR] = meta.z;
+
+    // 3. the first D columns of codes
+    const unsigned char *qb = reinterpret_cast<const unsigned char *>(qw) + (size_t)b * 8 * K;
+    const uint32_t col_bytes = (uint32_t)rows_b * 64;
+    const uint32_t lane_off = nfull > 0 ? (uint32_t)(s * rows_b + rl) * 16u : 0u;
+    const int tlast = min(tb + max(nfull - 1, 0), T - 1);
+    uint4 rec[D];
+    auto load_col = [&](int p) -> uint4 {
+        const uint32_t cb = (uint32_t)min(tb + p, tlast) * col_bytes;
+        return nt_load(reinterpret_cast<const uint4 *>((qb + cb) + lane_off));
+    };
+#pragma unroll
+    for (int p = 0; p < D; ++p) {
+        rec[p] = load_col(p);
+        __builtin_amdgcn_sched_barrier(0);
+    }
+
+    // 4. metadata to LDS; the activation sums per closing unit and slice:
+    // lane (s, r) forms them for chunk 16 q + r, the lanes of a unit are
+    // added by row shifts (the unit's sum lands in its last lane)
+    __builtin_amdgcn_s_waitcnt((D & 15) | (7 << 4) | (15 << 8) | ((D >> 4) << 14));
+    if constexpr (!MREG) {
+#pragma unroll
+        for (int j = 0; j < MJ; ++j) {
+            const int part = mp + 4 * j;
+            *reinterpret_cast<uint4 *>(part < MPARTS ? ml + r * MRS + part * 16 : spare) = mreg[j];
+        }
+        if constexpr (ZJ > 0) {
+#pragma unroll
+            for (int j = 0; j < ZJ; ++j) {
+                const int w = mp + 4 * j;
+                *(w < ZW ? zl + r * ZRS + w : reinterpret_cast<uint32_t *>(spare)) = zreg[j];
+            }
+        }
+    }
+    constexpr uint32_t one2 = BF ? 0x3F803F80u : 0x3C003C00u;
+    constexpr float kMagic = BF ? 128.0f : 1024.0f;
+    constexpr float kFixedZ = FT::has_zeros ? 0.0f : (float)FT::fixed_zero;
+    float Bq[XQ], Sq[XQ];
+#pragma unroll
+    for (int q = 0; q < XQ; ++q) {
+        const uint4 v = xq[q];
+        float lo = dec_dot2<BF>(v.z, one2, dec_dot2<BF>(v.x, one2, 0.0f));
+        float hi = dec_dot2<BF>(v.w, one2, dec_dot2<BF>(v.y, one2, 0.0f));
+        if constexpr (CPG >= 2) {
+            lo = dpp_add_shr<1>(lo);
+            hi = dpp_add_shr<1>(hi);
+        }
+        if constexpr (CPG >= 4) {
+            lo = dpp_add_shr<2>(lo);
+            hi = dpp_add_shr<2>(hi);
+        }
+        const float S = lo + hi;
+        Sq[q] = S;
+        if constexpr (HI)
+            Bq[q] = fmaf(kMagic, lo, fmaf(64.0f, hi, kFixedZ * S));
+        else
+            Bq[q] = (kMagic + kFixedZ) * S;
+    }
+    __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+
+    // 5. the columns in order (a column past the slice is computed from copies
+    // and not added)
+    const UnpackConsts uc = unpack_consts();
+    const unsigned char *mrow_l = ml + r * MRS;
+    const uint32_t *zrow_l = zl + r * ZRS;
+    float acc = 0.0f, lo = 0.0f, hi = 0.0f;
+    const int zoff = gs0 & 7;
+    auto zero_of = [&](int g) -> uint32_t {
+        if constexpr (!FT::has_zeros) {
+            return 0u;
+        } else if constexpr (MREG) {
+            if constexpr (ZW <= 1) return (zreg[0] >> (4 * ((g + zoff) & 7))) & 0xFu;
+            else return (zreg[g >> 3] >> (4 * (g & 7))) & 0xFu;
+        } else {
+            return (zrow_l[g >> 3] >> (4 * (g & 7))) & 0xFu;
+        }
+    };
+    auto scale_of = [&](int g) -> float {
+        if constexpr (MREG) {
+            const uint4 v = mreg[g >> 3];
+            const uint32_t w = (g & 7) < 2 ? v.x : ((g & 7) < 4 ? v.y : ((g & 7) < 6 ? v.z : v.w));
+            return (float)__builtin_bit_cast(_Float16, (uint16_t)(w >> (16 * (g & 1))));
+        } else {
+            return (float)*reinterpret_cast<const _Float16 *>(mrow_l + g * 2);
+        }
+    };
+    constexpr float kF = HI ? 0.0625f : 1.0f;
+#pragma unroll
+    for (int p = 0; p < NCOL; ++p) {
+        const bool on = p < nfull;
+        const uint4 cur = rec[p % D];
+        const uint32_t dws[4] = {cur.x, cur.y, cur.z, cur.w};
+#pragma unroll
+        for (int j = 0; j < kColChunks; ++j) {
+            const int cc = p * kColChunks + j;   // chunk within the slice (compile-time)
+            const uint4 xs_q = xq[cc >> 4];
+            uint32_t xv[4];
+            // broadcast slice s of chunk cc from lane cc % 16 of row s
+            switch (cc & 15) {
+#define W4A16_BC(J) case J: xv[0] = row_bcast<J>(xs_q.x); xv[1] = row_bcast<J>(xs_q.y); \
+                            xv[2] = row_bcast<J>(xs_q.z); xv[3] = row_bcast<J>(xs_q.w); break;
+                W4A16_BC(0) W4A16_BC(1) W4A16_BC(2) W4A16_BC(3) W4A16_BC(4) W4A16_BC(5) W4A16_BC(6) W4A16_BC(7)
+                W4A16_BC(8) W4A16_BC(9) W4A16_BC(10) W4A16_BC(11) W4A16_BC(12) W4A16_BC(13) W4A16_BC(14)
+                W4A16_BC(15)
+#undef W4A16_BC
+            }
+            uint32_t w[4];
+            const uint32_t d = dws[j];
+            if constexpr (HI) {
+                const uint32_t d8 = d >> 8;
+                w[0] = and_or(d, uc.lo_mask, uc.f16_magic);
+                w[1] = and_or(d, uc.hi_mask, uc.f16_magic);
+                w[2] = and_or(d8, uc.lo_mask, uc.f16_magic);
+                w[3] = and_or(d8, uc.hi_mask, uc.f16_magic);
+            } else {
+                const uint32_t magic = uc.bf16_magic;
+                w[0] = and_or(d, uc.lo_mask, magic);
+                w[1] = and_or(d >> 4, uc.lo_mask, magic);
+                w[2] = and_or(d >> 8, uc.lo_mask, magic);
+                w[3] = and_or(d >> 12, uc.lo_mask, magic);
+            }
+            lo = dec_dot2<BF>(w[0], xv[0], lo);
+            hi = dec_dot2<BF>(w[1], xv[1], hi);
+            lo = dec_dot2<BF>(w[2], xv[2], lo);
+            hi = dec_dot2<BF>(w[3], xv[3], hi);
+            if ((j + 1) % CPG == 0) {
+                const int u = cc / CPG;                  // closing unit within the slice
+                const int cl = u * CPG + CPG - 1;       // its last chunk: the lane holding its sums
+                float Bv = 0.0f, Sv = 0.0f;
+                switch (cl & 15) {
+#define W4A16_BS(J) case J: Bv = row_bcast_f<J>(Bq[cl >> 4]); Sv = row_bcast_f<J>(Sq[cl >> 4]); break;
+                    W4A16_BS(0) W4A16_BS(1) W4A16_BS(2) W4A16_BS(3) W4A16_BS(4) W4A16_BS(5) W4A16_BS(6)
+                    W4A16_BS(7) W4A16_BS(8) W4A16_BS(9) W4A16_BS(10) W4A16_BS(11) W4A16_BS(12) W4A16_BS(13)
+                    W4A16_BS(14) W4A16_BS(15)
+#undef W4A16_BS
+                }
+                const int g = GROUP > kColumn ? (p >> 1) : u;
+                float part = fmaf(kF, hi, lo) - Bv;
+                if constexpr (FT::has_zeros) part = fmaf(-(float)zero_of(g), Sv, part);
+                const float na = fmaf(scale_of(g), part, acc);
+                acc = on ? na : acc;
+                lo = 0.0f;
+                hi = 0.0f;
+            }
+        }
+        if (p + D < NCOL) {
+            __builtin_amdgcn_sched_barrier(0);
+            rec[p % D] = load_col(p + D);
+            __builtin_amdgcn_sched_barrier(0);
+        }
+    }
+
+    // 6. reduce: the four lanes of a row, then the waves, in a fixed order
+    acc += __shfl_xor(acc, 16, 64);
+    acc += __shfl_xor(acc, 32, 64);
+    if (s == 0) red[wave][r] = acc;
+    __syncthreads();
+    const int waves = blockDim.x >> 6;
+    if (threadIdx.x < kRowBlock && (int)threadIdx.x < rows_b) {
+        const int rr = threadIdx.x;
+        float v = red[0][rr];
+        for (int w2 = 1; w2 < waves; ++w2) v += red[w2][rr];
+        y[b * kRowBlock + rr] = BF ? f32_to_bf16_bits(v) : f32_to_f16_bits(v);
+    }
+}
+
 template <int GROUP, int MT, bool BF, int FMT, int NCOL, bool AWQ>
 __global__ __launch_bounds__(64 * kDecMaxWaves) void decode_kernel(
     const uint16_t *__restrict__ x, const uint4 *__restrict__ qw, const uint4 *__restrict__ qw_hi,
@@ -685,6 +986,26 @@ hipError_t launch_dec_one(const void *x, const void *qw, const void *qh, const v
     return hipGetLastError();
 }
 
+// A launch of decode_bcast_kernel (plan.bcast: sixteen columns per wave): one
+// workgroup per row block, four columns of codes in flight per wave (measured
+// on K = 28672, group 32: 29.6 us, against 32.1 / 32.6 us with six / eight,
+// and 30.8-31.1 us for decode_kernel on the same device).
+template <int GROUP, bool BF, int FMT>
+hipError_t launch_dec_bcast(const void *x, const void *qw, const void *sc, const void *zp, void *y, int N, int K,
+                            const DecodePlan &p, hipStream_t stream) {
+    constexpr int NC = 16, kD = 4;
+    auto kern = decode_bcast_kernel<GROUP, BF, FMT, NC, kD>;
+    const size_t lds = (size_t)p.waves * dec_bcast_lds(NC, GROUP, FMT);
+    static DynLdsAttr attr;
+    hipError_t e = raise_dyn_lds(reinterpret_cast<const void *>(kern), lds, attr);
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(kern, dim3((unsigned)ceil_div(N, kRowBlock)), dim3(64 * p.waves), lds, stream,
+                       reinterpret_cast<const uint16_t *>(x), reinterpret_cast<const uint4 *>(qw),
+                       reinterpret_cast<const uint16_t *>(sc), reinterpret_cast<const uint32_t *>(zp),
+                       reinterpret_cast<uint16_t *>(y), N, K);
+    return hipGetLastError();
+}
+
 // the instantiated (rows, columns per wave, AWQ) combinations: the ones
 // decode_plan chooses
 template <int GROUP, bool BF, int FMT>
@@ -694,6 +1015,12 @@ hipError_t launch_dec_group(const void *x, const void *qw, const void *qh, const
 #define W4A16_DEC(MT_, NC_, AWQ_) \
     launch_dec_one<GROUP, MT_, BF, FMT, NC_, AWQ_>(x, qw, qh, sc, zp, y, M, N, K, am, p, tab, ws, stream)
     const bool awq = am != nullptr;
+    if constexpr (FMT == kAsym4 || FMT == kSym4) {
+        if (p.bcast && tab == nullptr) {   // one activation row, no split, no multipliers, K % 128 == 0
+            if (awq || p.mt != 1 || p.splits != 1 || p.ncol != 16 || K % kColumn != 0) return hipErrorInvalidValue;
+            return launch_dec_bcast<GROUP, BF, FMT>(x, qw, sc, zp, y, N, K, p, stream);
+        }
+    }
     switch (p.mt * 100 + p.ncol * 2 + (awq ? 1 : 0)) {
         case 108: return W4A16_DEC(1, 4, false);
         case 109: return W4A16_DEC(1, 4, true);

@@ -79,6 +79,7 @@ struct DecodePlan {
     int mt, ncol, waves;
     int splits, cols;
     size_t lds;   // dynamic LDS bytes of one workgroup
+    bool bcast;   // single launches: the variant with activations in registers (decode_bcast_kernel)
     bool ok;
 };
 DecodePlan decode_plan(int64_t M, int64_t N, int64_t K, int32_t group, int fmt, bool awq);
