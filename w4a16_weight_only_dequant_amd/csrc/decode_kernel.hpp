@@ -603,7 +603,9 @@ __device__ __forceinline__ void decode_body(
 //   from the lane that holds it, instead of being staged through LDS;
 // * the per-group activation sums (the magic-offset and zero-point terms) are
 //   formed in those lanes, combined over a group's lanes by DPP row shifts in
-//   the order decode_body uses, and broadcast the same way;
+//   the order decode_body uses, and reach the group's close as the DPP
+//   source operand of the subtraction and the fused multiply-add that use
+//   them (no broadcast instruction of their own);
 // * the codes stream through a ring of D columns per wave: after column p is
 //   used, column p + D is loaded into its registers.
 // LDS holds only the 16 rows' metadata of each wave's slice (groups 32 and
@@ -623,9 +625,22 @@ template <int J>
 __device__ inline uint32_t row_bcast(uint32_t v) {
     return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x150 + J, 0xF, 0xF, false);
 }
+// The same broadcast as the DPP source operand of the instruction that uses
+// it (gfx950 VOP2 forms), so it costs no instruction of its own. Each starts
+// with wait states: a VALU write of a register right before a DPP read of it
+// needs them, and the compiler does not look inside these.
+// v - b_J
 template <int J>
-__device__ inline float row_bcast_f(float v) {
-    return __builtin_bit_cast(float, row_bcast<J>(__builtin_bit_cast(uint32_t, v)));
+__device__ inline float sub_rowbcast(float v, float b) {
+    asm("s_nop 4\n\tv_subrev_f32_dpp %0, %1, %0 row_newbcast:%2 row_mask:0xf bank_mask:0xf" : "+v"(v) : "v"(b), "n"(J));
+    return v;
+}
+// v + s_J * (-z), one rounding (fma)
+template <int J>
+__device__ inline float fma_negz_rowbcast(float v, float s, float z) {
+    asm("s_nop 4\n\tv_fmac_f32_dpp %0, %1, -%2 row_newbcast:%3 row_mask:0xf bank_mask:0xf"
+        : "+v"(v) : "v"(s), "v"(z), "n"(J));
+    return v;
 }
 
 template <int GROUP, bool BF, int FMT, int NCOL, int D>
@@ -824,16 +839,6 @@ __global__ __launch_bounds__(64 * kDecMaxWaves) void decode_bcast_kernel(
         for (int j = 0; j < kColChunks; ++j) {
             const int cc = p * kColChunks + j;   // chunk within the slice (compile-time)
             const uint4 xs_q = xq[cc >> 4];
-            uint32_t xv[4];
-            // broadcast slice s of chunk cc from lane cc % 16 of row s
-            switch (cc & 15) {
-#define W4A16_BC(J) case J: xv[0] = row_bcast<J>(xs_q.x); xv[1] = row_bcast<J>(xs_q.y); \
-                            xv[2] = row_bcast<J>(xs_q.z); xv[3] = row_bcast<J>(xs_q.w); break;
-                W4A16_BC(0) W4A16_BC(1) W4A16_BC(2) W4A16_BC(3) W4A16_BC(4) W4A16_BC(5) W4A16_BC(6) W4A16_BC(7)
-                W4A16_BC(8) W4A16_BC(9) W4A16_BC(10) W4A16_BC(11) W4A16_BC(12) W4A16_BC(13) W4A16_BC(14)
-                W4A16_BC(15)
-#undef W4A16_BC
-            }
             uint32_t w[4];
             const uint32_t d = dws[j];
             if constexpr (HI) {
@@ -849,24 +854,34 @@ __global__ __launch_bounds__(64 * kDecMaxWaves) void decode_bcast_kernel(
                 w[2] = and_or(d >> 8, uc.lo_mask, magic);
                 w[3] = and_or(d >> 12, uc.lo_mask, magic);
             }
-            lo = dec_dot2<BF>(w[0], xv[0], lo);
-            hi = dec_dot2<BF>(w[1], xv[1], hi);
-            lo = dec_dot2<BF>(w[2], xv[2], lo);
-            hi = dec_dot2<BF>(w[3], xv[3], hi);
+            // slice s of chunk cc is held by lane cc % 16 of row s
+            switch (cc & 15) {
+#define W4A16_BC(J) case J: \
+                lo = dec_dot2<BF>(w[0], row_bcast<J>(xs_q.x), lo); hi = dec_dot2<BF>(w[1], row_bcast<J>(xs_q.y), hi); \
+                lo = dec_dot2<BF>(w[2], row_bcast<J>(xs_q.z), lo); hi = dec_dot2<BF>(w[3], row_bcast<J>(xs_q.w), hi); \
+                break;
+                W4A16_BC(0) W4A16_BC(1) W4A16_BC(2) W4A16_BC(3) W4A16_BC(4) W4A16_BC(5) W4A16_BC(6) W4A16_BC(7)
+                W4A16_BC(8) W4A16_BC(9) W4A16_BC(10) W4A16_BC(11) W4A16_BC(12) W4A16_BC(13) W4A16_BC(14)
+                W4A16_BC(15)
+#undef W4A16_BC
+            }
             if ((j + 1) % CPG == 0) {
                 const int u = cc / CPG;                  // closing unit within the slice
                 const int cl = u * CPG + CPG - 1;       // its last chunk: the lane holding its sums
-                float Bv = 0.0f, Sv = 0.0f;
+                const int g = GROUP > kColumn ? (p >> 1) : u;
+                float part = fmaf(kF, hi, lo);
+                const float zf = (float)zero_of(g);
                 switch (cl & 15) {
-#define W4A16_BS(J) case J: Bv = row_bcast_f<J>(Bq[cl >> 4]); Sv = row_bcast_f<J>(Sq[cl >> 4]); break;
+#define W4A16_BS(J) case J: \
+                    part = sub_rowbcast<J>(part, Bq[cl >> 4]); \
+                    if constexpr (FT::has_zeros) part = fma_negz_rowbcast<J>(part, Sq[cl >> 4], zf); \
+                    break;
                     W4A16_BS(0) W4A16_BS(1) W4A16_BS(2) W4A16_BS(3) W4A16_BS(4) W4A16_BS(5) W4A16_BS(6)
                     W4A16_BS(7) W4A16_BS(8) W4A16_BS(9) W4A16_BS(10) W4A16_BS(11) W4A16_BS(12) W4A16_BS(13)
                     W4A16_BS(14) W4A16_BS(15)
 #undef W4A16_BS
                 }
-                const int g = GROUP > kColumn ? (p >> 1) : u;
-                float part = fmaf(kF, hi, lo) - Bv;
-                if constexpr (FT::has_zeros) part = fmaf(-(float)zero_of(g), Sv, part);
+                (void)zf;
                 const float na = fmaf(scale_of(g), part, acc);
                 acc = on ? na : acc;
                 lo = 0.0f;
