@@ -627,18 +627,21 @@ __device__ inline uint32_t row_bcast(uint32_t v) {
 }
 // The same broadcast as the DPP source operand of the instruction that uses
 // it (gfx950 VOP2 forms), so it costs no instruction of its own. Each starts
-// with wait states: a VALU write of a register right before a DPP read of it
-// needs them, and the compiler does not look inside these.
+// with wait states (a VALU write of a register right before a DPP read of it
+// needs them, and the compiler does not look inside these), and each is
+// volatile: the compiler takes a plain asm statement for a function of its
+// own lane's inputs and may move it into code that runs with some lanes
+// inactive, where a DPP read returns stale values.
 // v - b_J
 template <int J>
 __device__ inline float sub_rowbcast(float v, float b) {
-    asm("s_nop 4\n\tv_subrev_f32_dpp %0, %1, %0 row_newbcast:%2 row_mask:0xf bank_mask:0xf" : "+v"(v) : "v"(b), "n"(J));
+    asm volatile("s_nop 4\n\tv_subrev_f32_dpp %0, %1, %0 row_newbcast:%2 row_mask:0xf bank_mask:0xf" : "+v"(v) : "v"(b), "n"(J));
     return v;
 }
 // v + s_J * (-z), one rounding (fma)
 template <int J>
 __device__ inline float fma_negz_rowbcast(float v, float s, float z) {
-    asm("s_nop 4\n\tv_fmac_f32_dpp %0, %1, -%2 row_newbcast:%3 row_mask:0xf bank_mask:0xf"
+    asm volatile("s_nop 4\n\tv_fmac_f32_dpp %0, %1, -%2 row_newbcast:%3 row_mask:0xf bank_mask:0xf"
         : "+v"(v) : "v"(s), "v"(z), "n"(J));
     return v;
 }
