@@ -63,6 +63,32 @@ def test_noalloc_matches_linear_on_consecutive_calls():
     assert needs[0] > 0 and needs[1] > 0 and needs[2] == 0 and needs[3] == 0
 
 
+def test_noalloc_decode_long_k_and_split_k():
+    """One activation row: the long-K decode variant (no scratch) and the
+    decode kernel's K split (its partials and counters in the static scratch),
+    in a row, the split twice with a smaller shape between; bit-identical to
+    w4a16_linear_fmt with a workspace and within the bar on every output."""
+    import torch
+    w4 = H.lib()
+    assert w4.raw().w4a16_init(0) == 0
+    stream = torch.cuda.Stream()
+    group = 128
+    cases = [(40, 65536), (264, 24576), (24, 65536), (40, 65536)]
+    needs = []
+    for i, (N, K) in enumerate(cases):
+        w, o, pw = H.prepared(("noalloc_dec", N, K, group), lambda: wl.random_weights(31 * N + K, N, K), group)
+        xb = wl.random_activations(900 + i, 1, K, "bf16")
+        x = H.to_device_bits(xb, "bf16")
+        with torch.cuda.stream(stream):
+            y_ref, nbytes = _ordinary(x, pw, 1, stream)
+            y = _noalloc(x, pw, 1, stream)
+        stream.synchronize()
+        needs.append(nbytes)
+        assert torch.equal(y.view(torch.int16), y_ref.view(torch.int16)), (N, K)
+        H.check_every_output(y, xb, "bf16", o, group)
+    assert needs[0] > 0 and needs[1] == 0 and needs[2] > 0
+
+
 def test_noalloc_rejects_bad_arguments_and_writes_nothing():
     import torch
     w4 = H.lib()
