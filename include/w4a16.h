@@ -245,11 +245,14 @@ w4a16_status w4a16_unpack_fmt(const void *qweight, const void *scales, const voi
  * K's 128-weight columns (up to 16 waves of four, eight or sixteen columns),
  * 128-bit loads, in-register unpack, packed fp16 / bf16 dot products with
  * fp32 accumulation, the group scale and zero-point applied once per group;
- * the waves meet in LDS in a fixed order. Split K: when the matrix has few
- * row blocks for the device's compute units (or K is long), S workgroups
- * share a row block's K and leave fp32 partials in the workspace
- * (w4a16_workspace_bytes); the last of them adds the S partials in a fixed
- * order, so results are deterministic and independent of timing. Range:
+ * the waves meet in LDS in a fixed order. At M = 1 with K > 16384 (4-bit
+ * codes, K a multiple of 128) the activations stay in registers and are
+ * broadcast across lanes, with the same sums in the same order (the same
+ * bits). Split K: only where a workgroup's LDS cannot hold its slice (long K
+ * at the larger M and the smaller groups), S workgroups share a row block's K
+ * and leave fp32 partials in the workspace (w4a16_workspace_bytes); the last
+ * of them adds the S partials in a fixed order, so results are deterministic
+ * and independent of timing. Range:
  * M <= 8 and K <= 65536; W4A16_ERR_INVALID_ARG outside it (w4a16_gemm and
  * w4a16_linear have no such limit), W4A16_ERR_WORKSPACE when the workspace is
  * smaller than w4a16_workspace_bytes. */
